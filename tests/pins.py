@@ -1,0 +1,336 @@
+"""Pins of the fp64 oracle against things other than itself.
+
+Each pin takes ``mutant`` (0 = the oracle; other values build the oracle with
+one planted mistake, see oracle/hs2ref.c) and raises AssertionError when the
+oracle disagrees with the reference the pin names.  test_oracle_pins runs them
+on the oracle; test_oracle_mutants checks every planted mistake fails one.
+"""
+from __future__ import annotations
+
+import math
+from fractions import Fraction
+
+import numpy as np
+
+import oracle
+from long_context_sparse_full_amd import synth
+from tests import refs
+
+rng0 = np.random.default_rng
+
+
+def _small_inputs(kv_dtype, q_dtype, B=2, Tq=3, Hq=8, Hkv=2, N=37, D=16, seed=1, q_std=0.5, q_pos0=None):
+    spec = synth.Spec("pin", 99, B=B, N=N, Tq=Tq, Hq=Hq, Hkv=Hkv, D=D, kv_dtype=kv_dtype, q_dtype=q_dtype,
+                      k=4, window=3, n_sparse=1, needles=2, needle_mode="per_head", q_std=q_std)
+    inp = synth.make_inputs(spec, seed)
+    return spec, inp, (spec.q_pos0 if q_pos0 is None else q_pos0)
+
+
+def _close(a, b, atol, what):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    if a.shape != b.shape:
+        raise AssertionError(f"{what}: shape {a.shape} != {b.shape}")
+    if not np.all(np.isfinite(a)) or not np.allclose(a, b, rtol=0.0, atol=atol):
+        err = np.nanmax(np.abs(a - b)) if np.all(np.isfinite(a)) else float("nan")
+        raise AssertionError(f"{what}: max abs err {err} > {atol}")
+
+
+# --------------------------------------------------------------------- decode
+
+def pin_e4m3fn_table(mutant=0):
+    """All 256 E4M3FN codes against torch.float8_e4m3fn -> float32."""
+    import torch
+    ours = oracle.e4m3fn_table(mutant)
+    theirs = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).float().numpy().astype(np.float64)
+    nan_o, nan_t = np.isnan(ours), np.isnan(theirs)
+    assert np.array_equal(nan_o, nan_t), "NaN codes differ"
+    assert np.array_equal(ours[~nan_o], theirs[~nan_t]), "decoded values differ"
+    assert np.array_equal(np.signbit(ours[~nan_o]), np.signbit(theirs[~nan_t])), "signed zero differs"
+
+
+def pin_bf16_decode(mutant=0):
+    """Every 64th bf16 pattern against torch's bf16 -> float32 cast."""
+    bits = np.arange(0, 65536, 64, dtype=np.uint32).astype(np.uint16)
+    ours = oracle.bf16_decode(bits)
+    theirs = refs.torch_decode(bits)
+    fin = np.isfinite(theirs)
+    assert np.array_equal(np.isnan(ours), np.isnan(theirs))
+    assert np.array_equal(ours[fin], theirs[fin])
+
+
+# ------------------------------------------------------------- full attention
+
+def pin_full_vs_sdpa(mutant=0):
+    """Output and LSE equal float64 SDPA (GQA by repeat_interleave, causal mask
+    offset by q_pos0) for fp32, bf16 and E4M3FN caches."""
+    import torch
+    for kv_dtype, q_dtype, q_pos0 in (("f32", "f32", None), ("bf16", "bf16", 20), ("fp8", "bf16", None)):
+        spec, inp, qp = _small_inputs(kv_dtype, q_dtype, q_pos0=q_pos0)
+        out, lse, _ = oracle.full_attn_scores(inp.q_full, inp.k, inp.v, qp, k_scale=inp.k_scale,
+                                              v_scale=inp.v_scale, mutant=mutant)
+        q = refs.torch_decode(inp.q_full)
+        k = refs.torch_decode(inp.k, inp.k_scale)
+        v = refs.torch_decode(inp.v, inp.v_scale)
+        scale = 1.0 / math.sqrt(spec.D)
+        mask = refs.causal_mask(spec.B, spec.Tq, spec.Hkv, spec.N, qp)
+        _close(out, refs.sdpa(q, k, v, mask, scale), 1e-12, f"{kv_dtype} out")
+        # LSE: torch.logsumexp over the masked logits of each head
+        G = spec.G
+        qt = torch.from_numpy(q).permute(0, 2, 1, 3)
+        kt = torch.from_numpy(k).repeat_interleave(G, 1)
+        logits = scale * qt @ kt.transpose(-1, -2)
+        m = torch.from_numpy(mask).permute(0, 2, 1, 3).repeat_interleave(G, 1)
+        ref_lse = torch.logsumexp(logits.masked_fill(~m, -math.inf), -1).permute(0, 2, 1).numpy()
+        _close(lse, ref_lse, 1e-12, f"{kv_dtype} lse")
+
+
+def pin_scores_vs_sdpa_probs(mutant=0):
+    """Scores equal SDPA's own probabilities (values = identity rows) summed over
+    the query heads sharing each kv head; zero beyond the query position."""
+    spec, inp, qp = _small_inputs("bf16", "bf16", q_pos0=25)
+    _, _, sc = oracle.full_attn_scores(inp.q_full, inp.k, inp.v, qp, mutant=mutant)
+    q = refs.torch_decode(inp.q_full)
+    k = refs.torch_decode(inp.k)
+    P = refs.sdpa_probs(q, k, refs.causal_mask(spec.B, spec.Tq, spec.Hkv, spec.N, qp), 1.0 / math.sqrt(spec.D))
+    ref = P.reshape(spec.B, spec.Tq, spec.Hkv, spec.G, spec.N).sum(3)
+    _close(sc, ref, 1e-12, "scores")
+
+
+def pin_score_mass_is_group_size(mutant=0):
+    """Each unit's scores sum to G (a sum of G probability distributions)."""
+    spec, inp, qp = _small_inputs("f32", "f32", Hq=12, Hkv=3, N=50)
+    _, _, sc = oracle.full_attn_scores(inp.q_full, inp.k, inp.v, qp, mutant=mutant)
+    _close(sc.sum(-1), np.full(sc.shape[:3], spec.G, np.float64), 1e-12, "score mass")
+
+
+def pin_zero_query(mutant=0):
+    """q = 0: uniform attention, so out = mean of v[0..p], scores = G/(p+1),
+    lse = log(p+1)."""
+    spec, inp, qp = _small_inputs("f32", "f32", N=29, Tq=2)
+    q = np.zeros_like(inp.q_full)
+    out, lse, sc = oracle.full_attn_scores(q, inp.k, inp.v, qp, mutant=mutant)
+    v = inp.v.astype(np.float64)
+    for t in range(spec.Tq):
+        p = qp + t
+        for h in range(spec.Hq):
+            g = h // spec.G
+            _close(out[:, t, h], v[:, g, : p + 1].mean(axis=1), 1e-12, "zero-q out")
+            _close(lse[:, t, h], np.full(spec.B, math.log(p + 1)), 1e-12, "zero-q lse")
+        _close(sc[:, t, :, : p + 1], np.full((spec.B, spec.Hkv, p + 1), spec.G / (p + 1)), 1e-14, "zero-q S")
+        _close(sc[:, t, :, p + 1:], 0.0 * sc[:, t, :, p + 1:], 0.0, "zero-q S beyond p")
+
+
+def pin_single_position(mutant=0):
+    """N = 1: out = v_0 exactly, lse = scale * <q, k_0>, scores = G."""
+    spec, inp, qp = _small_inputs("f32", "f32", N=1, Tq=1, D=8)
+    out, lse, sc = oracle.full_attn_scores(inp.q_full, inp.k, inp.v, 0, mutant=mutant)
+    v = inp.v.astype(np.float64)
+    k = inp.k.astype(np.float64)
+    q = inp.q_full.astype(np.float64)
+    for h in range(spec.Hq):
+        g = h // spec.G
+        _close(out[:, 0, h], v[:, g, 0], 0.0, "N=1 out")
+        _close(lse[:, 0, h], (q[:, 0, h] * k[:, g, 0]).sum(-1) / math.sqrt(spec.D), 1e-12, "N=1 lse")
+    _close(sc, np.full(sc.shape, float(spec.G)), 1e-15, "N=1 scores")
+
+
+def pin_key_shift_invariance(mutant=0):
+    """Adding one vector to every key shifts each head's logits by a constant:
+    output and scores are unchanged (softmax shift invariance)."""
+    spec, inp, qp = _small_inputs("f32", "f32")
+    # keys on a 2^-10 grid and a shift on a 2^-4 grid: k + c is exact in float32
+    k1 = (np.round(inp.k * 1024) / 1024).astype(np.float32)
+    c = (np.round(np.random.default_rng(7).standard_normal(spec.D) * 4) / 16).astype(np.float32)
+    k2 = (k1 + c).astype(np.float32)
+    assert np.array_equal(k2.astype(np.float64) - k1.astype(np.float64), np.broadcast_to(c, k1.shape))
+    o1, _, s1 = oracle.full_attn_scores(inp.q_full, k1, inp.v, qp, mutant=mutant)
+    o2, _, s2 = oracle.full_attn_scores(inp.q_full, k2, inp.v, qp, mutant=mutant)
+    _close(o2, o1, 1e-12, "shifted-key out")
+    _close(s2, s1, 1e-12, "shifted-key scores")
+
+
+def pin_position_permutation(mutant=0):
+    """With every position visible (Tq=1, p=N-1), permuting the cache rows
+    permutes the scores and leaves the output unchanged."""
+    spec, inp, qp = _small_inputs("f32", "f32", Tq=1)
+    perm = np.random.default_rng(3).permutation(spec.N)
+    o1, _, s1 = oracle.full_attn_scores(inp.q_full, inp.k, inp.v, qp, mutant=mutant)
+    kp = np.ascontiguousarray(inp.k[:, :, perm])
+    vp = np.ascontiguousarray(inp.v[:, :, perm])
+    o2, _, s2 = oracle.full_attn_scores(inp.q_full, kp, vp, qp, mutant=mutant)
+    _close(o2, o1, 1e-12, "permuted out")
+    _close(s2, s1[..., perm], 1e-14, "permuted scores")
+
+
+# ------------------------------------------------------------------ selection
+
+def _exact_case(rng, N, Tq, ties):
+    """Integer scores (exact in float64) with many ties."""
+    hi = 4 if ties else 10_000
+    return rng.integers(0, hi, size=(1, Tq, 1, N)).astype(np.float64)
+
+
+def pin_select_bruteforce(mutant=0):
+    """Token and block selection equal exhaustive max-mass enumeration with the
+    lexicographically smallest list winning ties (= lower position first)."""
+    rng = np.random.default_rng(11)
+    for case in range(160):
+        N = int(rng.integers(1, 15))
+        Tq = int(rng.integers(1, min(3, N) + 1))
+        qp = N - Tq - int(rng.integers(0, N - Tq + 1))
+        k = int(rng.integers(0, N + 2))
+        W = int(rng.integers(0, 5))
+        bs = int(rng.choice([1, 1, 2, 3]))
+        sc = _exact_case(rng, N, Tq, ties=bool(case % 2))
+        idx, cnt = oracle.select_topk_window(sc, qp, k, W, block_size=bs, max_sel=N, mutant=mutant)
+        for t in range(Tq):
+            want = refs.brute_select([Fraction(int(x)) for x in sc[0, t, 0]], qp + t, k, W, bs)
+            got = list(idx[0, t, 0, : cnt[0, t, 0]])
+            assert got == want, f"case {case}: N={N} p={qp + t} k={k} W={W} bs={bs}: {got} != {want}"
+            assert np.all(idx[0, t, 0, cnt[0, t, 0]:] == -1), "padding must be -1"
+
+
+def pin_select_structure(mutant=0):
+    """Structural facts of the pages' selection on random real scores: the
+    window is always in; entries are unique, ascending and causal; the count is
+    min(k,|C|) + min(W, p+1); k >= |C| selects everything; k = 0 is the window."""
+    rng = np.random.default_rng(5)
+    for _ in range(40):
+        N = int(rng.integers(1, 300))
+        Tq = int(rng.integers(1, 4)) if N >= 4 else 1
+        qp = N - Tq
+        W = int(rng.integers(0, 40))
+        k = int(rng.integers(0, 80))
+        sc = rng.random((2, Tq, 2, N))
+        idx, cnt = oracle.select_topk_window(sc, qp, k, W, max_sel=N, mutant=mutant)
+        for u in np.ndindex(2, Tq, 2):
+            p = qp + u[1]
+            sel = idx[u][: cnt[u]]
+            ncand = max(0, p - W + 1)
+            assert cnt[u] == min(k, ncand) + min(W, p + 1), "count formula"
+            assert np.all(np.diff(sel) > 0), "ascending and unique"
+            assert sel.size == 0 or (sel[0] >= 0 and sel[-1] <= p), "causal"
+            assert set(range(max(0, p - W + 1), p + 1)) <= set(sel.tolist()), "window in"
+            c = sel[sel <= p - W]
+            if k >= ncand:
+                assert np.array_equal(sel, np.arange(p + 1)), "k >= |C| selects all"
+            if k == 0:
+                assert c.size == 0, "k = 0 is only the window"
+            # selected candidates outrank every unselected candidate
+            if 0 < c.size < ncand:
+                row = sc[u][: ncand]
+                rest = np.setdiff1d(np.arange(ncand), c)
+                assert row[c].min() >= row[rest].max(), "top-k property"
+
+
+def pin_select_pages_budget(mutant=0):
+    """The pages' budget: 1024 global + 128 forced recent gives 1152 rows once
+    the context exceeds it; 16 blocks of 64 give the same 1024-token budget."""
+    import json, os
+    here = os.path.dirname(__file__)
+    with open(os.path.join(here, "golden", "pages_constants.json")) as f:
+        pc = json.load(f)
+    k, W, bs = pc["global_tokens"], pc["recent_window"], pc["hysparse_block_tokens"]
+    rng = np.random.default_rng(2)
+    N = 5000
+    sc = rng.random((1, 1, 1, N))
+    idx, cnt = oracle.select_topk_window(sc, N - 1, k, W, max_sel=k + W, mutant=mutant)
+    assert cnt[0, 0, 0] == k + W == pc["selected_rows"]
+    assert np.array_equal(idx[0, 0, 0, -W:], np.arange(N - W, N))
+    nb = pc["global_tokens"] // bs
+    idx, cnt = oracle.select_topk_window(sc, N - 1, nb, W, block_size=bs, max_sel=k + W, mutant=mutant)
+    assert cnt[0, 0, 0] == nb * bs + W
+
+
+def pin_window_competes_alternative(mutant=0):
+    """The alternative reading (window positions also compete): the selection
+    is the top-k over [0, p] united with the window, so k <= |Sel| <= k + W."""
+    rng = np.random.default_rng(9)
+    N, W, k = 200, 16, 40
+    sc = rng.random((1, 1, 1, N))
+    idx, cnt = oracle.select_topk_window(sc, N - 1, k, W, window_competes=True, max_sel=N, mutant=mutant)
+    sel = set(idx[0, 0, 0, : cnt[0, 0, 0]].tolist())
+    top = set(np.argsort(-sc[0, 0, 0], kind="stable")[:k].tolist())
+    assert sel == top | set(range(N - W, N))
+    assert k <= cnt[0, 0, 0] <= k + W
+
+
+# ------------------------------------------------------------- sparse layers
+
+def pin_sparse_equals_full_when_k_covers(mutant=0):
+    """k >= |C|: the selection is every causal position, so sparse attention
+    equals full causal attention (float64 SDPA)."""
+    spec, inp, qp = _small_inputs("bf16", "bf16", Tq=2)
+    _, _, sc = oracle.full_attn_scores(inp.q_full, inp.k, inp.v, qp, mutant=mutant)
+    idx, cnt = oracle.select_topk_window(sc, qp, spec.N, 3, max_sel=spec.N, mutant=mutant)
+    out, _ = oracle.sparse_attn(inp.q_sparse[0], inp.k, inp.v, idx, cnt, mutant=mutant)
+    q = refs.torch_decode(inp.q_sparse[0])
+    ref = refs.sdpa(q, refs.torch_decode(inp.k), refs.torch_decode(inp.v),
+                    refs.causal_mask(spec.B, spec.Tq, spec.Hkv, spec.N, qp), 1.0 / math.sqrt(spec.D))
+    _close(out, ref, 1e-12, "k>=|C| sparse")
+
+
+def pin_sparse_k0_is_sliding_window(mutant=0):
+    """k = 0: only the forced window remains, so sparse attention equals
+    sliding-window attention over the last W positions (float64 SDPA, band mask)."""
+    for W in (1, 5, 11):
+        spec, inp, qp = _small_inputs("fp8", "bf16", Tq=2)
+        _, _, sc = oracle.full_attn_scores(inp.q_full, inp.k, inp.v, qp, k_scale=inp.k_scale,
+                                           v_scale=inp.v_scale, mutant=mutant)
+        idx, cnt = oracle.select_topk_window(sc, qp, 0, W, max_sel=spec.N, mutant=mutant)
+        out, _ = oracle.sparse_attn(inp.q_sparse[0], inp.k, inp.v, idx, cnt, k_scale=inp.k_scale,
+                                    v_scale=inp.v_scale, mutant=mutant)
+        q = refs.torch_decode(inp.q_sparse[0])
+        ref = refs.sdpa(q, refs.torch_decode(inp.k, inp.k_scale), refs.torch_decode(inp.v, inp.v_scale),
+                        refs.band_mask(spec.B, spec.Tq, spec.Hkv, spec.N, qp, W), 1.0 / math.sqrt(spec.D))
+        _close(out, ref, 1e-12, f"k=0 W={W} sparse")
+
+
+def pin_sparse_equals_masked_attention(mutant=0):
+    """Any index list: sparse attention equals full attention with a mask that
+    admits exactly the listed rows (float64 SDPA); lse equals torch.logsumexp."""
+    import torch
+    spec, inp, qp = _small_inputs("f32", "f32", Tq=3, N=41)
+    rng = np.random.default_rng(4)
+    max_sel = 12
+    idx = np.full((spec.B, spec.Tq, spec.Hkv, max_sel), -1, np.int32)
+    cnt = np.zeros((spec.B, spec.Tq, spec.Hkv), np.int32)
+    for u in np.ndindex(spec.B, spec.Tq, spec.Hkv):
+        n = int(rng.integers(1, max_sel + 1))
+        idx[u][:n] = np.sort(rng.choice(spec.N, n, replace=False))
+        cnt[u] = n
+    out, lse = oracle.sparse_attn(inp.q_sparse[0], inp.k, inp.v, idx, cnt, mutant=mutant)
+    mask = refs.index_mask(idx, cnt, spec.N)
+    q, k, v = (refs.torch_decode(x) for x in (inp.q_sparse[0], inp.k, inp.v))
+    scale = 1.0 / math.sqrt(spec.D)
+    _close(out, refs.sdpa(q, k, v, mask, scale), 1e-12, "masked sparse out")
+    G = spec.G
+    logits = scale * torch.from_numpy(q).permute(0, 2, 1, 3) @ torch.from_numpy(k).repeat_interleave(G, 1).transpose(-1, -2)
+    m = torch.from_numpy(mask).permute(0, 2, 1, 3).repeat_interleave(G, 1)
+    ref_lse = torch.logsumexp(logits.masked_fill(~m, -math.inf), -1).permute(0, 2, 1).numpy()
+    _close(lse, ref_lse, 1e-12, "masked sparse lse")
+
+
+# --------------------------------------------------------------------- bridge
+
+def pin_bridge_vs_matmul(mutant=0):
+    """K/V bridge equals a float64 matmul of the torch-decoded bf16 inputs,
+    K heads first then V heads, head-major columns."""
+    rng = np.random.default_rng(8)
+    T, dm, Hkv, D = 6, 48, 2, 8
+    h = synth.to_bf16_bits(rng.standard_normal((T, dm)).astype(np.float32))
+    w = synth.to_bf16_bits(rng.standard_normal((dm, 2 * Hkv * D)).astype(np.float32))
+    K, V = oracle.kv_bridge(h, w, Hkv, D, mutant=mutant)
+    y = refs.torch_decode(h) @ refs.torch_decode(w)
+    _close(K, y[:, : Hkv * D].reshape(T, Hkv, D), 1e-12, "bridge K")
+    _close(V, y[:, Hkv * D:].reshape(T, Hkv, D), 1e-12, "bridge V")
+
+
+ALL_PINS = [
+    pin_e4m3fn_table, pin_bf16_decode, pin_full_vs_sdpa, pin_scores_vs_sdpa_probs,
+    pin_score_mass_is_group_size, pin_zero_query, pin_single_position, pin_key_shift_invariance,
+    pin_position_permutation, pin_select_bruteforce, pin_select_structure, pin_select_pages_budget,
+    pin_window_competes_alternative, pin_sparse_equals_full_when_k_covers,
+    pin_sparse_k0_is_sliding_window, pin_sparse_equals_masked_attention, pin_bridge_vs_matmul,
+]
