@@ -1,0 +1,214 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of the HySparse2 cross-decoder hot path on one MI355X.
+
+One step = full-attention layer over the whole cache (out, lse, scores) ->
+token top-k + forced window -> 3 sparse layers over the shared index list,
+all through the C ABI on the current stream, inputs resident in HBM.
+
+Default workload: decode at 1M context with an FP8 (E4M3FN) cache -- B=1,
+N=1048576, 32 q / 4 kv heads, head_dim 128, k=1024, window=128.  Prints ONE
+JSON line on stdout (progress goes to stderr):
+  value        microseconds per decode step (lower is better)
+  hbm_gbps     algorithmic bytes of the step / step time
+  roofline     the full-layer scan kernel against the 8 TB/s HBM peak, its
+               duration from HIP events on the launch stream
+  cpu_baseline the fp64 oracle on this host's cores, one whole step
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "µs/decode-step (full scan + top-k + 3 sparse layers) & HBM GB/s at 1M ctx"
+HBM_PEAK_GBPS = 8000.0
+SCAN_SRC = os.path.join(ROOT, "long_context_sparse_full_amd", "csrc", "attn.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "full_scan_decode1m_fp8_traffic.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def esize(kv: str) -> int:
+    return {"f32": 4, "bf16": 2, "fp8": 1}[kv]
+
+
+def algorithmic_bytes(spec) -> dict:
+    """What the method itself must move per step (no implementation scratch)."""
+    kv_bytes = 2 * spec.B * spec.Hkv * spec.N * spec.D * esize(spec.kv_dtype)
+    scores = spec.B * spec.Tq * spec.Hkv * spec.N * 4
+    gathered = 2 * spec.B * spec.Tq * spec.Hkv * spec.max_sel * spec.D * esize(spec.kv_dtype)
+    return {"scan_kv": kv_bytes, "scores_write_read": 2 * scores, "gather_per_layer": gathered,
+            "step": kv_bytes + 2 * scores + spec.n_sparse * gathered}
+
+
+def traffic_entry(launch_bytes: int):
+    """HBM bytes per scan launch from the committed rocprofv3 counter summary,
+    only if it was taken on the current kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+        src_hash = hashlib.sha256(open(SCAN_SRC, "rb").read()).hexdigest()
+        if t.get("kernel_src_sha256") != src_hash:
+            return None
+        return int(t["hbm_bytes_per_launch"])
+    except Exception:  # noqa: BLE001
+        return None
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="decode1m_fp8")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no multi-GPU path",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from long_context_sparse_full_amd import hs2, synth
+
+    if not torch.cuda.is_available():
+        log("no GPU visible")
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    spec = synth.config(args.config)
+    if spec.Tq != 1:
+        log("bench.py times decode workloads (Tq = 1)")
+        sys.exit(2)
+    log(f"[bench] generating {spec.name}")
+    t0 = time.time()
+    inp = synth.make_inputs(spec)
+    log(f"[bench] inputs ready in {time.time() - t0:.1f}s")
+
+    def dev(a):
+        t = torch.from_numpy(np.ascontiguousarray(a))
+        return (t.view(torch.bfloat16) if a.dtype == np.uint16 else t).cuda()
+
+    k, v, q = dev(inp.k), dev(inp.v), dev(inp.q_full)
+    ks = dev(inp.k_scale) if inp.k_scale is not None else None
+    vs = dev(inp.v_scale) if inp.v_scale is not None else None
+    qs = [dev(x) for x in inp.q_sparse]
+    B, Tq, Hq, D, Hkv, N = spec.B, spec.Tq, spec.Hq, spec.D, spec.Hkv, spec.N
+    out = torch.empty_like(q)
+    lse = torch.empty((B, Tq, Hq), dtype=torch.float32, device="cuda")
+    scores = torch.empty((B, Tq, Hkv, N), dtype=torch.float32, device="cuda")
+    ws_full = torch.empty(hs2.full_attn_scores_workspace(k, v, Tq, Hq), dtype=torch.uint8, device="cuda")
+    idx = torch.empty((B, Tq, Hkv, spec.max_sel), dtype=torch.int32, device="cuda")
+    cnt = torch.empty((B, Tq, Hkv), dtype=torch.int32, device="cuda")
+    ws_sel = torch.empty(hs2.select_workspace(B, Tq, Hkv, N, 1), dtype=torch.uint8, device="cuda")
+    sp_out = [torch.empty_like(q) for _ in qs]
+    sp_lse = [torch.empty((B, Tq, Hq), dtype=torch.float32, device="cuda") for _ in qs]
+
+    def step():
+        hs2.full_attn_scores(k, v, q, spec.q_pos0, k_scale=ks, v_scale=vs, out=out, lse=lse, scores=scores,
+                             workspace=ws_full)
+        hs2.select_topk_window(scores, spec.q_pos0, spec.k, spec.window, max_sel=spec.max_sel, idx=idx, count=cnt,
+                               workspace=ws_sel)
+        for i, ql in enumerate(qs):
+            hs2.sparse_attn_gather(k, v, ql, idx, cnt, k_scale=ks, v_scale=vs, out=sp_out[i], lse=sp_lse[i])
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - w0) * 1e3 / args.steps
+    ms_step = e0.elapsed_time(e1) / args.steps
+    log(f"[bench] {ms_step * 1e3:.1f} us/step (events), {wall_ms * 1e3:.1f} us/step (wall)")
+
+    # per-kernel durations from HIP events bracketing each launch on its stream
+    hs2.timing_reset()
+    hs2.timing_enable(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    kernels = {}
+    for name in hs2.timing_kernel_names():
+        tot, n = hs2.timing_collect(name)
+        if n:
+            kernels[name] = {"avg_us": round(tot * 1e3 / n, 3), "launches_per_step": n / args.steps}
+    hs2.timing_enable(False)
+    hs2.timing_reset()
+    log(f"[bench] kernels: {json.dumps(kernels)}")
+
+    ab = algorithmic_bytes(spec)
+    scan_us = kernels["full_scan"]["avg_us"]
+    achieved = ab["scan_kv"] / (scan_us * 1e-6) / 1e9
+    roofline = {"kernel": "full_scan", "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                "traffic": traffic_entry(ab["scan_kv"]), "algorithmic_bytes_per_launch": ab["scan_kv"],
+                "avg_launch_us": scan_us}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        threads = len(os.sched_getaffinity(0))
+        os.environ.setdefault("OMP_NUM_THREADS", str(threads))
+        log(f"[bench] oracle step on host ({threads} threads available)")
+        c0 = time.perf_counter()
+        _, _, s_or = oracle.full_attn_scores(inp.q_full, inp.k, inp.v, spec.q_pos0, k_scale=inp.k_scale,
+                                             v_scale=inp.v_scale)
+        c1 = time.perf_counter()
+        idx_or, cnt_or = oracle.select_topk_window(s_or, spec.q_pos0, spec.k, spec.window, max_sel=spec.max_sel)
+        for ql in inp.q_sparse:
+            oracle.sparse_attn(ql, inp.k, inp.v, idx_or, cnt_or, k_scale=inp.k_scale, v_scale=inp.v_scale)
+        c2 = time.perf_counter()
+        units = B * Tq * Hkv
+        cpu = {"value": round((c2 - c0) * 1e6, 1), "unit": "us/decode-step", "cores": min(units, oracle.num_threads()),
+               "kind": "oracle",
+               "sample": f"one whole decode step of {spec.name} (all {units} kv-head units; the oracle "
+                         f"parallelises over units), fp64; full layer {c1 - c0:.2f}s, select+3 sparse {c2 - c1:.2f}s",
+               "threads_available": threads}
+        log(f"[bench] oracle: {c2 - c0:.2f}s per step")
+
+    line = {
+        "metric": METRIC,
+        "value": round(ms_step * 1e3, 2),
+        "unit": "us/decode-step",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"fp8": "fp8e4m3-kv/bf16-q/f32-acc", "bf16": "bf16/f32-acc", "f32": "f32"}[spec.kv_dtype],
+        "data": "synthetic (seeded; planted needle keys)",
+        "config": {"workload": spec.name, "B": B, "context": N, "Tq": Tq, "q_heads": Hq, "kv_heads": Hkv,
+                   "head_dim": D, "kv_dtype": spec.kv_dtype, "top_k": spec.k, "window": spec.window,
+                   "sparse_layers": spec.n_sparse},
+        "hbm_gbps": round(ab["step"] / (ms_step * 1e-3) / 1e9, 1),
+        "algorithmic_bytes_per_step": ab["step"],
+        "wall_us_per_step": round(wall_ms * 1e3, 2),
+        "kernels": kernels,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

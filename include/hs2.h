@@ -1,0 +1,169 @@
+/*
+ * hs2.h -- C ABI of the MI355X (gfx950) HySparse2 cross-decoder attention hot path.
+ *
+ * The method ("HySparse2: Hybrid Sparse Attention with Two-Level KV Sharing",
+ * as described on javabetter.cn "mimo-v3-hysparse2", zgeo.com.cn
+ * "xiaomi-mimo-v3-hysparse2-long-context-geo", aitop.news item 35442 and
+ * siami.tw "xiaomi-mimo-v3-hysparse-2"): each cross-decoder hybrid block is one
+ * full-attention layer followed by several sparse-attention layers
+ * (javabetter.cn, the Cross-Decoder paragraph).  The full layer scans the whole
+ * KV cache and its attention scores pick the tokens (javabetter.cn, first of
+ * the two changes); a token-level top-k is merged with a forced window of the
+ * most recent tokens (zgeo.com.cn, "core principle": 1024 global + 128 recent);
+ * the sparse layers reuse the full layer's KV cache and selection indices
+ * (aitop.news item 35442; javabetter.cn, KV Reuse paragraph); the full layer's
+ * K/V come from a self-decoder hidden state through that layer's own
+ * projection (javabetter.cn, KV Bridging paragraph).
+ *
+ * Conventions shared by every call:
+ *   - All tensor pointers are DEVICE pointers unless stated otherwise; the
+ *     caller allocates and owns every buffer (inputs, outputs, workspace).  The
+ *     library never allocates, frees or retains a pointer beyond the call.
+ *   - Calls are asynchronous on `stream`; results are valid once the stream
+ *     reaches the call.  Calls never synchronise, print or abort.
+ *   - Every call validates its arguments before any launch and returns an
+ *     hs2 status; on failure hs2_last_error() holds a thread-local message.
+ *   - Layouts are dense row-major unless strides are given:
+ *       q, out : [B, Tq, Hq, D]     lse : [B, Tq, Hq] fp32
+ *       scores : [B, Tq, Hkv, N] fp32
+ *       idx    : [B, Tq, Hkv, max_sel] int32, count : [B, Tq, Hkv] int32
+ *     Query head h belongs to KV group g = h / (Hq / Hkv).  Query token t sits
+ *     at cache position p = q_pos0 + t and attends to positions [0, p].
+ *   - Base pointers must be 16-byte aligned; the K/V row stride (stride_n
+ *     times the element size) and the other K/V strides must be multiples of
+ *     16 bytes.
+ *   - Supported: head_dim D in {64, 128}; group size Hq/Hkv <= 16; (q, kv)
+ *     element types (F32, F32), (BF16, BF16), (BF16, FP8_E4M3FN).
+ */
+#ifndef HS2_H
+#define HS2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+struct ihipStream_t;
+typedef struct ihipStream_t* hipStream_t;
+
+#define HS2_ABI_VERSION 1
+
+typedef enum { HS2_F32 = 0, HS2_BF16 = 1, HS2_FP8_E4M3FN = 2 } hs2_dtype;
+
+enum {
+  HS2_OK = 0,
+  HS2_ERR_INVALID_ARG = -1, /* bad shape, pointer, alignment or range          */
+  HS2_ERR_UNSUPPORTED = -2, /* valid but not implemented (D, G, dtype pair)    */
+  HS2_ERR_WORKSPACE = -3,   /* workspace smaller than the *_workspace() figure */
+  HS2_ERR_HIP = -4          /* a HIP launch failed; see hs2_last_error()       */
+};
+
+/* One layer's shared K/V cache.  Element (b, h, n, d) of K is at
+ * k[b*stride_b + h*stride_h + n*stride_n + d] (strides in elements, d
+ * contiguous).  For FP8_E4M3FN caches (OCP E4M3FN codes, as the pages' FP8 KV
+ * cache accounting -- zgeo.com.cn comparison table), k_scale and v_scale hold
+ * one fp32 scale per (b, kv head), index b*Hkv + h, and the cache value is
+ * decode(code) * scale; they are ignored (may be NULL) otherwise.  The
+ * attention calls only read k and v; hs2_kv_bridge writes them. */
+typedef struct {
+  const void* k;
+  const void* v;
+  int32_t dtype; /* hs2_dtype */
+  int64_t stride_b, stride_h, stride_n;
+  const float* k_scale;
+  const float* v_scale;
+  int32_t B, Hkv, N, D;
+} hs2_kv_desc;
+
+int hs2_abi_version(void);
+const char* hs2_status_string(int status);
+/* Message of the calling thread's last failure ("" if none). */
+const char* hs2_last_error(void);
+
+/* Full-attention layer of a hybrid block (javabetter.cn: the full layer looks
+ * at everything from start to end, and its attention scores -- how related the
+ * current token is to each earlier token -- are what the selection uses).
+ * For every (b, t, h), logits s_j = softmax_scale * <q[b,t,h], k[b,g,j]> for
+ * j in [0, p]:
+ *   out[b,t,h]  = sum_j softmax(s)_j * v[b,g,j]    (q's element type, RNE)
+ *   lse[b,t,h]  = log sum_j exp(s_j)               (natural log; may be NULL)
+ *   scores[b,t,g,j] = sum over the query heads h of group g of softmax(s)_j
+ *                     for j <= p, and 0 for p < j < N.
+ * Requires 0 <= q_pos0 and q_pos0 + Tq <= N.  Workspace: at least
+ * hs2_full_attn_scores_workspace(kv, Tq, Hq) bytes, 256-byte aligned, device
+ * memory; its contents on entry are ignored. */
+size_t hs2_full_attn_scores_workspace(const hs2_kv_desc* kv, int32_t Tq, int32_t Hq);
+int hs2_full_attn_scores(const hs2_kv_desc* kv, const void* q, hs2_dtype q_dtype, int32_t Tq,
+                         int32_t Hq, int32_t q_pos0, float softmax_scale, void* out, float* lse,
+                         float* scores, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Token-level top-k with a forced recent window (zgeo.com.cn "core
+ * principle": 1024 global tokens picked and the most recent 128 always kept;
+ * javabetter.cn, the two changes versus HySparse).  For each (b, t, g) with
+ * p = q_pos0 + t: window Wn = [max(0, p-window+1), p]; candidates
+ * C = [0, p-window] (empty when p < window).
+ *   block_size == 1: T = the min(k, |C|) candidates with the largest scores,
+ *     ties to the lower position.
+ *   block_size  > 1: the previous generation's block baseline (zgeo.com.cn
+ *     comparison table: 64-token blocks): aligned blocks of block_size
+ *     positions clipped to C, block mass = sum of its scores (fp64 sum in
+ *     ascending position), the min(k, #blocks) heaviest blocks (ties to the
+ *     lower block), T = their positions; k counts blocks.
+ *   idx[b,t,g,:count] = ascending(T union Wn); idx[b,t,g,count:] = -1.
+ * Scores must be finite and >= 0 (the full layer's scores are).
+ * max_sel >= min(k*block_size + window, N) is required.  Workspace: at least
+ * hs2_select_workspace(B, Tq, Hkv, N) bytes (covers both modes). */
+size_t hs2_select_workspace(int32_t B, int32_t Tq, int32_t Hkv, int32_t N);
+/* Tighter figure for one block_size (what the call actually checks). */
+size_t hs2_select_workspace_for(int32_t B, int32_t Tq, int32_t Hkv, int32_t N, int32_t block_size);
+int hs2_select_topk_window(const float* scores, int32_t B, int32_t Tq, int32_t Hkv, int32_t N,
+                           int32_t q_pos0, int32_t k, int32_t window, int32_t block_size,
+                           int32_t* idx, int32_t* count, int32_t max_sel, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream);
+
+/* Sparse-attention layer with KV reuse (aitop.news item 35442: sparse layers
+ * reuse the previous full-attention layer's KV cache and selection indices;
+ * javabetter.cn: they neither compute nor store K/V).  For every (b, t, h),
+ * g = h / (Hq/Hkv), rows j in idx[b,t,g,0:count[b,t,g]]:
+ *   out[b,t,h] = sum_j softmax_j(softmax_scale * <q[b,t,h], k[b,g,j]>) v[b,g,j]
+ *   lse[b,t,h] = log sum_j exp(...)       (may be NULL)
+ * Every listed index must lie in [0, N) (not checked on the device: the list
+ * is read on the GPU); 0 <= count <= max_sel.  An empty list gives out = 0
+ * and lse = -inf.  No workspace. */
+int hs2_sparse_attn_gather(const hs2_kv_desc* kv, const void* q, hs2_dtype q_dtype, int32_t Tq,
+                           int32_t Hq, float softmax_scale, const int32_t* idx,
+                           const int32_t* count, int32_t max_sel, void* out, float* lse,
+                           hipStream_t stream);
+
+/* KV bridge (javabetter.cn, KV Bridging paragraph: a cross-decoder full layer
+ * computes its K and V from a self-decoder layer's hidden state, with its own
+ * parameters).  y = hidden [T, d_model] (bf16) x w_kv [d_model, 2*Hkv*D]
+ * (bf16), fp32 accumulation; columns [0, Hkv*D) are K heads 0..Hkv-1 and
+ * [Hkv*D, 2*Hkv*D) are V heads, head-major.  The rounded (bf16, RNE) rows are
+ * written into kv_out (a BF16 cache) at batch batch_index, positions
+ * [pos0, pos0 + T).  Requires d_model % 64 == 0. */
+int hs2_kv_bridge(const void* hidden, int32_t T, int32_t d_model, const void* w_kv,
+                  const hs2_kv_desc* kv_out, int32_t batch_index, int32_t pos0, hipStream_t stream);
+
+/* Diagnostic: decode n OCP E4M3FN codes (device array) to fp32 through the
+ * same in-register conversion the attention kernels use.  Lets a test compare
+ * the hardware conversion with the format's definition code by code. */
+int hs2_debug_e4m3fn_to_f32(const uint8_t* codes, float* out, int32_t n, hipStream_t stream);
+
+/* Per-kernel timing with HIP events on the launch stream (off by default).
+ * While enabled, every kernel launch of the library is bracketed by an event
+ * pair on its stream.  hs2_timing_collect synchronises those events and
+ * returns, for launches of the named kernel since the last reset, the summed
+ * milliseconds and the launch count.  Names: see hs2_timing_kernel_name. */
+int hs2_timing_enable(int on);
+int hs2_timing_reset(void);
+int hs2_timing_collect(const char* kernel_name, double* total_ms, int32_t* launches);
+/* i-th kernel name (NULL past the end). */
+const char* hs2_timing_kernel_name(int32_t i);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* HS2_H */

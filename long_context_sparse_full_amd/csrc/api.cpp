@@ -1,0 +1,461 @@
+// C-ABI shim of the HySparse2 cross-decoder hot path: argument validation,
+// workspace planning, dispatch to the gfx950 kernels, per-kernel event timing.
+// Validation never touches the GPU, so every error path runs without a device.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "hs2_internal.hpp"
+
+namespace {
+
+thread_local std::string t_err;
+
+int fail(int status, const std::string& msg) {
+  t_err = msg;
+  return status;
+}
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+int64_t rup(int64_t a, int64_t b) { return cdiv(a, b) * b; }
+size_t a256(size_t x) { return (x + 255) & ~size_t(255); }
+bool al16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int esize(int dt) { return dt == HS2_F32 ? 4 : (dt == HS2_BF16 ? 2 : 1); }
+
+int check_kv(const hs2_kv_desc* kv, const char* what) {
+  const std::string w(what);
+  if (!kv) return fail(HS2_ERR_INVALID_ARG, w + ": kv descriptor is NULL");
+  if (!kv->k || !kv->v) return fail(HS2_ERR_INVALID_ARG, w + ": k or v pointer is NULL");
+  if (kv->B <= 0 || kv->Hkv <= 0 || kv->N <= 0 || kv->D <= 0)
+    return fail(HS2_ERR_INVALID_ARG, w + ": B, Hkv, N and D must be positive");
+  if (kv->dtype != HS2_F32 && kv->dtype != HS2_BF16 && kv->dtype != HS2_FP8_E4M3FN)
+    return fail(HS2_ERR_UNSUPPORTED, w + ": unknown kv dtype " + std::to_string(kv->dtype));
+  if (kv->D != 64 && kv->D != 128)
+    return fail(HS2_ERR_UNSUPPORTED, w + ": head_dim " + std::to_string(kv->D) + " (supported: 64, 128)");
+  if (kv->stride_n < kv->D || kv->stride_h < 0 || kv->stride_b < 0)
+    return fail(HS2_ERR_INVALID_ARG, w + ": strides must satisfy stride_n >= D, stride_h >= 0, stride_b >= 0");
+  const int es = esize(kv->dtype);
+  if (!al16(kv->k) || !al16(kv->v)) return fail(HS2_ERR_INVALID_ARG, w + ": k/v base pointers must be 16-byte aligned");
+  if ((kv->stride_n * es) % 16 || (kv->stride_h * es) % 16 || (kv->stride_b * es) % 16)
+    return fail(HS2_ERR_INVALID_ARG, w + ": k/v strides must be multiples of 16 bytes");
+  if (kv->dtype == HS2_FP8_E4M3FN && (!kv->k_scale || !kv->v_scale))
+    return fail(HS2_ERR_UNSUPPORTED, w + ": FP8_E4M3FN cache needs k_scale and v_scale");
+  return HS2_OK;
+}
+
+int check_q(const hs2_kv_desc* kv, const void* q, int q_dtype, int Tq, int Hq, const char* what) {
+  const std::string w(what);
+  if (!q) return fail(HS2_ERR_INVALID_ARG, w + ": q is NULL");
+  if (Tq <= 0 || Hq <= 0) return fail(HS2_ERR_INVALID_ARG, w + ": Tq and Hq must be positive");
+  if (Hq % kv->Hkv) return fail(HS2_ERR_INVALID_ARG, w + ": Hq must be a multiple of Hkv");
+  if (Hq / kv->Hkv > 16) return fail(HS2_ERR_UNSUPPORTED, w + ": more than 16 query heads per kv head");
+  const bool ok = (q_dtype == HS2_F32 && kv->dtype == HS2_F32) || (q_dtype == HS2_BF16 && kv->dtype == HS2_BF16) ||
+                  (q_dtype == HS2_BF16 && kv->dtype == HS2_FP8_E4M3FN);
+  if (!ok) return fail(HS2_ERR_UNSUPPORTED, w + ": (q, kv) dtype pair not supported");
+  if (!al16(q)) return fail(HS2_ERR_INVALID_ARG, w + ": q must be 16-byte aligned");
+  return HS2_OK;
+}
+
+struct FullPlan {
+  int tpack, n_tpacks, rows, units, nsplit, split_len;
+  int64_t npad;
+  size_t off_ml, off_o, off_lse2, off_logits, total;
+};
+
+// Position splits: about 2048 workgroups in total (8 per CU on 256 CUs), split
+// lengths a multiple of 256 positions (64 on the fp32 path).
+FullPlan plan_full(const hs2_kv_desc* kv, int Tq, int Hq) {
+  FullPlan p{};
+  const int G = Hq / kv->Hkv;
+  const bool f32 = kv->dtype == HS2_F32;
+  p.tpack = f32 ? 1 : std::max(1, std::min(Tq, 16 / G));
+  p.n_tpacks = (int)cdiv(Tq, p.tpack);
+  p.rows = p.tpack * G;
+  p.units = kv->B * p.n_tpacks * kv->Hkv;
+  const int64_t per_unit = std::max<int64_t>(1, 2048 / p.units);
+  const int64_t quantum = f32 ? 64 : 256;
+  p.split_len = (int)rup(cdiv(kv->N, per_unit), quantum);
+  p.nsplit = (int)cdiv(kv->N, p.split_len);
+  p.npad = rup(kv->N, 64);
+  size_t off = 0;
+  p.off_ml = off;
+  off = a256(off + (size_t)p.units * p.nsplit * 16 * 2 * sizeof(float));
+  p.off_o = off;
+  off = a256(off + (size_t)p.units * p.nsplit * 16 * kv->D * sizeof(float));
+  p.off_lse2 = off;
+  off = a256(off + (size_t)p.units * p.rows * sizeof(float));
+  p.off_logits = off;
+  off = a256(off + (size_t)p.units * p.rows * (size_t)p.npad * sizeof(float));
+  p.total = off;
+  return p;
+}
+
+struct SelPlan {
+  int units, nchunks, nblocks_max;
+  size_t off_state, off_ha, off_hb, off_cnt, off_bmass, total;
+};
+
+SelPlan plan_select(int B, int Tq, int Hkv, int N, int block_size) {
+  SelPlan p{};
+  p.units = B * Tq * Hkv;
+  p.nchunks = (int)cdiv(N, hs2::kSelChunk);
+  p.nblocks_max = block_size > 1 ? (int)cdiv(N, block_size) : 0;
+  size_t off = 0;
+  p.off_state = off;
+  off = a256(off + (size_t)p.units * 8 * sizeof(int32_t));
+  if (block_size == 1) {
+    p.off_ha = off;
+    off = a256(off + (size_t)p.units * hs2::kHistBins * sizeof(int32_t));
+    p.off_hb = off;
+    off = a256(off + (size_t)p.units * hs2::kHistBins * sizeof(int32_t));
+    p.off_cnt = off;
+    off = a256(off + (size_t)p.units * p.nchunks * 2 * sizeof(int32_t));
+  } else {
+    p.off_bmass = off;
+    off = a256(off + (size_t)p.units * p.nblocks_max * sizeof(double));
+  }
+  p.total = off;
+  return p;
+}
+
+template <typename T>
+T* at(void* base, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(base) + off);
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(HS2_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+// ---------------------------------------------------------------------------
+// event timing
+// ---------------------------------------------------------------------------
+const char* const kKernelNames[] = {"full_scan",   "combine",     "score",        "select_init",
+                                    "select_hist", "select_find", "select_count", "select_emit",
+                                    "select_block_mass", "select_block_pick", "sparse_gather", "kv_bridge",
+                                    nullptr};
+
+std::mutex g_tmu;
+bool g_timing = false;
+struct TimingRec {
+  const char* name;
+  hipEvent_t a, b;
+};
+std::vector<TimingRec> g_recs;
+std::vector<hipEvent_t> g_pool;
+
+hipEvent_t take_event() {
+  if (!g_pool.empty()) {
+    hipEvent_t e = g_pool.back();
+    g_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+}  // namespace
+
+namespace hs2 {
+TimedLaunch::TimedLaunch(const char* name, hipStream_t s) : name_(name), s_(s), ev0_(nullptr), ev1_(nullptr) {
+  if (!g_timing) return;
+  std::lock_guard<std::mutex> lk(g_tmu);
+  hipEvent_t a = take_event(), b = take_event();
+  if (!a || !b) return;
+  ev0_ = a;
+  ev1_ = b;
+  hipEventRecord(a, s);
+}
+TimedLaunch::~TimedLaunch() {
+  if (!ev0_) return;
+  std::lock_guard<std::mutex> lk(g_tmu);
+  hipEventRecord((hipEvent_t)ev1_, s_);
+  g_recs.push_back(TimingRec{name_, (hipEvent_t)ev0_, (hipEvent_t)ev1_});
+}
+}  // namespace hs2
+
+extern "C" {
+
+int hs2_abi_version(void) { return HS2_ABI_VERSION; }
+
+const char* hs2_status_string(int status) {
+  switch (status) {
+    case HS2_OK: return "ok";
+    case HS2_ERR_INVALID_ARG: return "invalid argument";
+    case HS2_ERR_UNSUPPORTED: return "unsupported";
+    case HS2_ERR_WORKSPACE: return "workspace too small";
+    case HS2_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+const char* hs2_last_error(void) { return t_err.c_str(); }
+
+size_t hs2_full_attn_scores_workspace(const hs2_kv_desc* kv, int32_t Tq, int32_t Hq) {
+  if (!kv || kv->B <= 0 || kv->Hkv <= 0 || kv->N <= 0 || kv->D <= 0 || Tq <= 0 || Hq <= 0 || Hq % kv->Hkv) return 0;
+  return plan_full(kv, Tq, Hq).total;
+}
+
+int hs2_full_attn_scores(const hs2_kv_desc* kv, const void* q, hs2_dtype q_dtype, int32_t Tq, int32_t Hq,
+                         int32_t q_pos0, float softmax_scale, void* out, float* lse, float* scores, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream) {
+  int st = check_kv(kv, "hs2_full_attn_scores");
+  if (st) return st;
+  if ((st = check_q(kv, q, q_dtype, Tq, Hq, "hs2_full_attn_scores"))) return st;
+  if (q_pos0 < 0 || (int64_t)q_pos0 + Tq > kv->N)
+    return fail(HS2_ERR_INVALID_ARG, "hs2_full_attn_scores: need 0 <= q_pos0 and q_pos0 + Tq <= N");
+  if (!out || !scores) return fail(HS2_ERR_INVALID_ARG, "hs2_full_attn_scores: out and scores must not be NULL");
+  if (!al16(out) || !al16(scores) || (lse && ((uintptr_t)lse & 3)))
+    return fail(HS2_ERR_INVALID_ARG, "hs2_full_attn_scores: out/scores must be 16-byte aligned, lse 4-byte");
+  if (!std::isfinite(softmax_scale)) return fail(HS2_ERR_INVALID_ARG, "hs2_full_attn_scores: softmax_scale not finite");
+  const FullPlan pl = plan_full(kv, Tq, Hq);
+  if (!workspace || workspace_bytes < pl.total)
+    return fail(HS2_ERR_WORKSPACE, "hs2_full_attn_scores: workspace needs " + std::to_string(pl.total) + " bytes");
+  if ((uintptr_t)workspace & 255) return fail(HS2_ERR_INVALID_ARG, "hs2_full_attn_scores: workspace must be 256-byte aligned");
+
+  hs2::ScanParams p{};
+  p.k = kv->k;
+  p.v = kv->v;
+  p.sb = kv->stride_b;
+  p.sh = kv->stride_h;
+  p.sn = kv->stride_n;
+  p.k_scale = kv->k_scale;
+  p.v_scale = kv->v_scale;
+  p.B = kv->B;
+  p.Hkv = kv->Hkv;
+  p.N = kv->N;
+  p.D = kv->D;
+  p.G = Hq / kv->Hkv;
+  p.q = q;
+  p.Tq = Tq;
+  p.Hq = Hq;
+  p.q_pos0 = q_pos0;
+  p.scale_log2 = softmax_scale * 1.44269504088896340736f;
+  p.tpack = pl.tpack;
+  p.n_tpacks = pl.n_tpacks;
+  p.rows = pl.rows;
+  p.nsplit = pl.nsplit;
+  p.split_len = pl.split_len;
+  p.part_ml = at<float>(workspace, pl.off_ml);
+  p.part_o = at<float>(workspace, pl.off_o);
+  p.logits = at<float>(workspace, pl.off_logits);
+  p.npad = pl.npad;
+  hipError_t e = hs2::launch_scan(p, kv->dtype, false, true, stream);
+  if (e != hipSuccess) return hip_fail(e, "full_scan launch");
+
+  hs2::CombineParams c{};
+  c.part_ml = p.part_ml;
+  c.part_o = p.part_o;
+  c.nsplit = pl.nsplit;
+  c.rows = pl.rows;
+  c.tpack = pl.tpack;
+  c.n_tpacks = pl.n_tpacks;
+  c.G = p.G;
+  c.Hkv = kv->Hkv;
+  c.Hq = Hq;
+  c.Tq = Tq;
+  c.D = kv->D;
+  c.v_scale = kv->dtype == HS2_FP8_E4M3FN ? kv->v_scale : nullptr;
+  c.out_bf16 = q_dtype == HS2_BF16;
+  c.out = out;
+  c.lse = lse;
+  c.lse2 = at<float>(workspace, pl.off_lse2);
+  if ((e = hs2::launch_combine(c, pl.units, stream)) != hipSuccess) return hip_fail(e, "combine launch");
+
+  hs2::ScoreParams s{};
+  s.logits = p.logits;
+  s.lse2 = c.lse2;
+  s.npad = pl.npad;
+  s.rows = pl.rows;
+  s.tpack = pl.tpack;
+  s.n_tpacks = pl.n_tpacks;
+  s.G = p.G;
+  s.Hkv = kv->Hkv;
+  s.Tq = Tq;
+  s.N = kv->N;
+  s.q_pos0 = q_pos0;
+  s.scores = scores;
+  if ((e = hs2::launch_score(s, pl.units, stream)) != hipSuccess) return hip_fail(e, "score launch");
+  return HS2_OK;
+}
+
+size_t hs2_select_workspace(int32_t B, int32_t Tq, int32_t Hkv, int32_t N) {
+  if (B <= 0 || Tq <= 0 || Hkv <= 0 || N <= 0) return 0;
+  return std::max(plan_select(B, Tq, Hkv, N, 1).total, plan_select(B, Tq, Hkv, N, 2).total);
+}
+
+size_t hs2_select_workspace_for(int32_t B, int32_t Tq, int32_t Hkv, int32_t N, int32_t block_size) {
+  if (B <= 0 || Tq <= 0 || Hkv <= 0 || N <= 0 || block_size < 1) return 0;
+  return plan_select(B, Tq, Hkv, N, block_size).total;
+}
+
+int hs2_select_topk_window(const float* scores, int32_t B, int32_t Tq, int32_t Hkv, int32_t N, int32_t q_pos0,
+                           int32_t k, int32_t window, int32_t block_size, int32_t* idx, int32_t* count,
+                           int32_t max_sel, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!scores || !idx || !count) return fail(HS2_ERR_INVALID_ARG, "hs2_select_topk_window: NULL scores/idx/count");
+  if (B <= 0 || Tq <= 0 || Hkv <= 0 || N <= 0)
+    return fail(HS2_ERR_INVALID_ARG, "hs2_select_topk_window: B, Tq, Hkv, N must be positive");
+  if (q_pos0 < 0 || (int64_t)q_pos0 + Tq > N)
+    return fail(HS2_ERR_INVALID_ARG, "hs2_select_topk_window: need 0 <= q_pos0 and q_pos0 + Tq <= N");
+  if (k < 0 || window < 0 || block_size < 1)
+    return fail(HS2_ERR_INVALID_ARG, "hs2_select_topk_window: need k >= 0, window >= 0, block_size >= 1");
+  const int64_t need_sel = std::min<int64_t>((int64_t)k * block_size + window, N);
+  if (max_sel < need_sel)
+    return fail(HS2_ERR_INVALID_ARG, "hs2_select_topk_window: max_sel must be >= min(k*block_size + window, N) = " +
+                                         std::to_string(need_sel));
+  if (!al16(scores) || ((uintptr_t)idx & 3) || ((uintptr_t)count & 3))
+    return fail(HS2_ERR_INVALID_ARG, "hs2_select_topk_window: scores must be 16-byte aligned, idx/count 4-byte");
+  const SelPlan pl = plan_select(B, Tq, Hkv, N, block_size);
+  if (!workspace || workspace_bytes < pl.total)
+    return fail(HS2_ERR_WORKSPACE, "hs2_select_topk_window: workspace needs " + std::to_string(pl.total) + " bytes");
+  if ((uintptr_t)workspace & 255)
+    return fail(HS2_ERR_INVALID_ARG, "hs2_select_topk_window: workspace must be 256-byte aligned");
+  hs2::SelectParams p{};
+  p.scores = scores;
+  p.units = pl.units;
+  p.Tq = Tq;
+  p.Hkv = Hkv;
+  p.N = N;
+  p.q_pos0 = q_pos0;
+  p.k = k;
+  p.window = window;
+  p.block_size = block_size;
+  p.max_sel = max_sel;
+  p.nchunks = pl.nchunks;
+  p.idx = idx;
+  p.count = count;
+  p.state = at<int32_t>(workspace, pl.off_state);
+  p.hist_a = block_size == 1 ? at<int32_t>(workspace, pl.off_ha) : nullptr;
+  p.hist_b = block_size == 1 ? at<int32_t>(workspace, pl.off_hb) : nullptr;
+  p.cnt = block_size == 1 ? at<int32_t>(workspace, pl.off_cnt) : nullptr;
+  p.bmass = block_size > 1 ? at<double>(workspace, pl.off_bmass) : nullptr;
+  p.nblocks_max = pl.nblocks_max;
+  const hipError_t e = hs2::launch_select(p, stream);
+  if (e != hipSuccess) return hip_fail(e, "select launch");
+  return HS2_OK;
+}
+
+int hs2_sparse_attn_gather(const hs2_kv_desc* kv, const void* q, hs2_dtype q_dtype, int32_t Tq, int32_t Hq,
+                           float softmax_scale, const int32_t* idx, const int32_t* count, int32_t max_sel, void* out,
+                           float* lse, hipStream_t stream) {
+  int st = check_kv(kv, "hs2_sparse_attn_gather");
+  if (st) return st;
+  if ((st = check_q(kv, q, q_dtype, Tq, Hq, "hs2_sparse_attn_gather"))) return st;
+  if (!idx || !count || !out) return fail(HS2_ERR_INVALID_ARG, "hs2_sparse_attn_gather: NULL idx/count/out");
+  if (max_sel <= 0) return fail(HS2_ERR_INVALID_ARG, "hs2_sparse_attn_gather: max_sel must be positive");
+  if (!al16(out) || ((uintptr_t)idx & 3) || ((uintptr_t)count & 3) || (lse && ((uintptr_t)lse & 3)))
+    return fail(HS2_ERR_INVALID_ARG, "hs2_sparse_attn_gather: out must be 16-byte aligned, idx/count/lse 4-byte");
+  if (!std::isfinite(softmax_scale)) return fail(HS2_ERR_INVALID_ARG, "hs2_sparse_attn_gather: softmax_scale not finite");
+  hs2::ScanParams p{};
+  p.k = kv->k;
+  p.v = kv->v;
+  p.sb = kv->stride_b;
+  p.sh = kv->stride_h;
+  p.sn = kv->stride_n;
+  p.k_scale = kv->k_scale;
+  p.v_scale = kv->v_scale;
+  p.B = kv->B;
+  p.Hkv = kv->Hkv;
+  p.N = kv->N;
+  p.D = kv->D;
+  p.G = Hq / kv->Hkv;
+  p.q = q;
+  p.Tq = Tq;
+  p.Hq = Hq;
+  p.q_pos0 = 0;
+  p.scale_log2 = softmax_scale * 1.44269504088896340736f;
+  p.tpack = 1;
+  p.n_tpacks = Tq;
+  p.rows = p.G;
+  p.nsplit = 1;
+  p.idx = idx;
+  p.count = count;
+  p.max_sel = max_sel;
+  p.out = out;
+  p.lse = lse;
+  const hipError_t e = hs2::launch_scan(p, kv->dtype, true, false, stream);
+  if (e != hipSuccess) return hip_fail(e, "sparse_gather launch");
+  return HS2_OK;
+}
+
+int hs2_kv_bridge(const void* hidden, int32_t T, int32_t d_model, const void* w_kv, const hs2_kv_desc* kv_out,
+                  int32_t batch_index, int32_t pos0, hipStream_t stream) {
+  int st = check_kv(kv_out, "hs2_kv_bridge");
+  if (st) return st;
+  if (kv_out->dtype != HS2_BF16) return fail(HS2_ERR_UNSUPPORTED, "hs2_kv_bridge: output cache must be BF16");
+  if (!hidden || !w_kv) return fail(HS2_ERR_INVALID_ARG, "hs2_kv_bridge: NULL hidden or w_kv");
+  if (T <= 0 || d_model <= 0) return fail(HS2_ERR_INVALID_ARG, "hs2_kv_bridge: T and d_model must be positive");
+  if (d_model % 64) return fail(HS2_ERR_UNSUPPORTED, "hs2_kv_bridge: d_model must be a multiple of 64");
+  if (batch_index < 0 || batch_index >= kv_out->B)
+    return fail(HS2_ERR_INVALID_ARG, "hs2_kv_bridge: batch_index out of range");
+  if (pos0 < 0 || (int64_t)pos0 + T > kv_out->N)
+    return fail(HS2_ERR_INVALID_ARG, "hs2_kv_bridge: need 0 <= pos0 and pos0 + T <= N");
+  if (!al16(hidden) || !al16(w_kv)) return fail(HS2_ERR_INVALID_ARG, "hs2_kv_bridge: hidden/w_kv must be 16-byte aligned");
+  const int64_t off = (int64_t)batch_index * kv_out->stride_b + (int64_t)pos0 * kv_out->stride_n;
+  uint16_t* kb = const_cast<uint16_t*>(static_cast<const uint16_t*>(kv_out->k)) + off;
+  uint16_t* vb = const_cast<uint16_t*>(static_cast<const uint16_t*>(kv_out->v)) + off;
+  const hipError_t e = hs2::launch_bridge(static_cast<const uint16_t*>(hidden), T, d_model,
+                                          static_cast<const uint16_t*>(w_kv), kv_out->Hkv, kv_out->D, kb, vb,
+                                          kv_out->stride_n, kv_out->stride_h, stream);
+  if (e != hipSuccess) return hip_fail(e, "kv_bridge launch");
+  return HS2_OK;
+}
+
+int hs2_debug_e4m3fn_to_f32(const uint8_t* codes, float* out, int32_t n, hipStream_t stream) {
+  if (!codes || !out || n <= 0) return fail(HS2_ERR_INVALID_ARG, "hs2_debug_e4m3fn_to_f32: bad arguments");
+  const hipError_t e = hs2::launch_debug_e4m3fn(codes, out, n, stream);
+  if (e != hipSuccess) return hip_fail(e, "debug_e4m3fn launch");
+  return HS2_OK;
+}
+
+int hs2_timing_enable(int on) {
+  std::lock_guard<std::mutex> lk(g_tmu);
+  g_timing = on != 0;
+  return HS2_OK;
+}
+
+int hs2_timing_reset(void) {
+  std::lock_guard<std::mutex> lk(g_tmu);
+  for (auto& r : g_recs) {
+    hipEventSynchronize(r.b);
+    g_pool.push_back(r.a);
+    g_pool.push_back(r.b);
+  }
+  g_recs.clear();
+  return HS2_OK;
+}
+
+int hs2_timing_collect(const char* kernel_name, double* total_ms, int32_t* launches) {
+  if (!kernel_name || !total_ms || !launches) return fail(HS2_ERR_INVALID_ARG, "hs2_timing_collect: NULL argument");
+  std::lock_guard<std::mutex> lk(g_tmu);
+  double tot = 0.0;
+  int32_t n = 0;
+  for (auto& r : g_recs) {
+    if (std::strcmp(r.name, kernel_name) != 0) continue;
+    hipError_t e = hipEventSynchronize(r.b);
+    if (e != hipSuccess) return hip_fail(e, "hs2_timing_collect");
+    float ms = 0.f;
+    e = hipEventElapsedTime(&ms, r.a, r.b);
+    if (e != hipSuccess) return hip_fail(e, "hs2_timing_collect");
+    tot += ms;
+    ++n;
+  }
+  *total_ms = tot;
+  *launches = n;
+  return HS2_OK;
+}
+
+const char* hs2_timing_kernel_name(int32_t i) {
+  const int32_t n = (int32_t)(sizeof(kKernelNames) / sizeof(kKernelNames[0])) - 1;
+  return (i >= 0 && i < n) ? kKernelNames[i] : nullptr;
+}
+
+}  // extern "C"

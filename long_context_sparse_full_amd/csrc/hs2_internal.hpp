@@ -1,0 +1,101 @@
+// Internal declarations shared by the C-ABI shim and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "hs2.h"
+
+namespace hs2 {
+
+// ---------------------------------------------------------------------------
+// full / sparse attention "scan" launches
+// ---------------------------------------------------------------------------
+// A unit is (b, token-pack, kv group g).  Its rows are the query heads of the
+// group for `tpack` consecutive tokens: row r = tl*G + i <-> token
+// t = tp*tpack + tl, head h = g*G + i.  Rows never exceed 16 (one MFMA tile).
+struct ScanParams {
+  const void* k;
+  const void* v;
+  int64_t sb, sh, sn;  // K/V strides, elements
+  const float* k_scale;
+  const float* v_scale;
+  int B, Hkv, N, D, G;
+  const void* q;
+  int Tq, Hq, q_pos0;
+  float scale_log2;  // softmax_scale * log2(e)
+  int tpack;         // tokens per unit
+  int n_tpacks;      // ceil(Tq / tpack)
+  int rows;          // tpack * G
+  int nsplit;        // position splits per unit
+  int split_len;     // positions per split (multiple of 256)
+  float* part_ml;    // [units][nsplit][16][2]   (max, sum) in log2 units
+  float* part_o;     // [units][nsplit][16][D]   unnormalised output
+  float* logits;     // [units][rows][npad]      log2-domain logits (may be null)
+  int64_t npad;
+  // gather (sparse layer) mode: one unit per (b, t, g), tpack = 1
+  const int32_t* idx;
+  const int32_t* count;
+  int max_sel;
+  void* out;         // [B, Tq, Hq, D] in q's element type
+  float* lse;        // [B, Tq, Hq] natural log (nullable)
+};
+
+struct CombineParams {
+  const float* part_ml;
+  const float* part_o;
+  int nsplit, rows, tpack, n_tpacks, G, Hkv, Hq, Tq, D;
+  const float* v_scale;  // FP8 only, [B*Hkv]
+  int out_bf16;
+  void* out;
+  float* lse;    // natural log, nullable
+  float* lse2;   // [units][rows] log2-domain, for the score pass
+};
+
+struct ScoreParams {
+  const float* logits;
+  const float* lse2;
+  int64_t npad;
+  int rows, tpack, n_tpacks, G, Hkv, Tq, N, q_pos0;
+  float* scores;  // [B, Tq, Hkv, N]
+};
+
+// ---------------------------------------------------------------------------
+// selection
+// ---------------------------------------------------------------------------
+constexpr int kSelChunk = 4096;  // candidates per workgroup in the select passes
+constexpr int kHistBins = 4096;  // 12-bit digits
+
+struct SelectParams {
+  const float* scores;  // [units][N]
+  int units, Tq, Hkv, N, q_pos0, k, window, block_size, max_sel, nchunks;
+  int32_t* idx;
+  int32_t* count;
+  int32_t* state;   // [units][8]
+  int32_t* hist_a;  // [units][4096]
+  int32_t* hist_b;  // [units][4096]
+  int32_t* cnt;     // [units][nchunks][2]
+  double* bmass;    // [units][nblocks_max] (block mode)
+  int nblocks_max;
+};
+
+// launchers (return hipError_t of the launch)
+hipError_t launch_scan(const ScanParams& p, int kv_dtype, bool gather, bool write_logits, hipStream_t s);
+hipError_t launch_combine(const CombineParams& p, int units, hipStream_t s);
+hipError_t launch_score(const ScoreParams& p, int units, hipStream_t s);
+hipError_t launch_select(const SelectParams& p, hipStream_t s);
+hipError_t launch_bridge(const uint16_t* hidden, int T, int dm, const uint16_t* w, int Hkv, int D,
+                         uint16_t* k_out, uint16_t* v_out, int64_t sn, int64_t sh, hipStream_t s);
+hipError_t launch_debug_e4m3fn(const uint8_t* codes, float* out, int n, hipStream_t s);
+
+// timing hooks used by the launchers
+struct TimedLaunch {
+  TimedLaunch(const char* name, hipStream_t s);
+  ~TimedLaunch();
+  const char* name_;
+  hipStream_t s_;
+  void* ev0_;
+  void* ev1_;
+};
+
+}  // namespace hs2

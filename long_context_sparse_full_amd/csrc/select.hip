@@ -1,0 +1,380 @@
+// Selection kernels of the HySparse2 cross-decoder hot path (gfx950).
+//
+// Token mode: the k highest-scoring positions of C = [0, p - window] (ties to
+// the lower position) united with the forced window [p - window + 1, p], in
+// ascending order (zgeo.com.cn "xiaomi-mimo-v3-hysparse2-long-context-geo",
+// "core principle": 1024 global tokens plus the 128 most recent kept by force;
+// javabetter.cn "mimo-v3-hysparse2", the two changes versus HySparse).
+//
+// The k-th largest score is found exactly by a radix select over the 32-bit
+// patterns of the non-negative fp32 scores (their unsigned order is their
+// numeric order): digits of 12, 12 and 8 bits, each pass a histogram of the
+// keys that share the digits found so far.  Histograms use integer atomics
+// only, so every count -- and therefore the selection -- is deterministic.
+// The emit pass keeps every key above the threshold and the lowest-positioned
+// keys equal to it, compacted in ascending position order.
+//
+// Block mode (block_size > 1) is the previous generation's 64-token block
+// selection (zgeo.com.cn comparison table): block mass = fp64 sum of its
+// scores over C in ascending position, heaviest blocks first, ties to the
+// lower block.
+#include "hs2_internal.hpp"
+
+namespace hs2 {
+namespace {
+
+enum { ST_MODE = 0, ST_PREFIX = 1, ST_NEED = 2, ST_NCAND = 3, ST_TAKE = 4, ST_P = 5 };
+enum { MODE_RADIX = 0, MODE_ALL = 1, MODE_NONE = 2 };
+
+__device__ __forceinline__ uint32_t score_key(float s) {
+  const uint32_t u = __float_as_uint(s);
+  return u == 0x80000000u ? 0u : u;  // -0 orders as +0
+}
+
+template <typename T>
+__device__ __forceinline__ T block_exclusive_scan(T v, T* sm, T& total) {
+  // 256 threads; sm has >= 256 + 8 slots
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  T x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const T y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) sm[256 + wave] = x;
+  __syncthreads();
+  T wbase = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const T s = sm[256 + w];
+    if (w < wave) wbase += s;
+    tot += s;
+  }
+  __syncthreads();
+  total = tot;
+  return wbase + x - v;
+}
+
+__global__ void __launch_bounds__(256) sel_init(SelectParams P) {
+  const int u = blockIdx.x;
+  const int t = (u / P.Hkv) % P.Tq;
+  const int p = P.q_pos0 + t;
+  const int ncand = max(0, p - P.window + 1);
+  int take;
+  if (P.block_size == 1) {
+    take = min(P.k, ncand);
+  } else {
+    const int nb = ncand > 0 ? (ncand - 1) / P.block_size + 1 : 0;
+    take = min(P.k, nb);
+  }
+  if (threadIdx.x == 0) {
+    int32_t* st = P.state + (int64_t)u * 8;
+    st[ST_MODE] = (take == 0) ? MODE_NONE : ((P.block_size == 1 && take == ncand) ? MODE_ALL : MODE_RADIX);
+    st[ST_PREFIX] = 0;
+    st[ST_NEED] = take;
+    st[ST_NCAND] = ncand;
+    st[ST_TAKE] = take;
+    st[ST_P] = p;
+  }
+  if (P.block_size == 1) {
+    int32_t* ha = P.hist_a + (int64_t)u * kHistBins;
+    int32_t* hb = P.hist_b + (int64_t)u * kHistBins;
+    for (int i = threadIdx.x; i < kHistBins; i += 256) {
+      ha[i] = 0;
+      hb[i] = 0;
+    }
+  }
+}
+
+// PASS 0: bits 31..20, PASS 1: bits 19..8 (keys matching bits 31..20),
+// PASS 2: bits 7..0 (keys matching bits 31..8)
+template <int PASS>
+__global__ void __launch_bounds__(256) sel_hist(SelectParams P) {
+  constexpr int SHIFT = PASS == 0 ? 20 : (PASS == 1 ? 8 : 0);
+  constexpr int BINS = PASS == 2 ? 256 : 4096;
+  constexpr uint32_t MATCH = PASS == 0 ? 0u : (PASS == 1 ? 0xFFF00000u : 0xFFFFFF00u);
+  __shared__ int32_t h[BINS];
+  const int u = blockIdx.y, chunk = blockIdx.x;
+  const int32_t* st = P.state + (int64_t)u * 8;
+  if (st[ST_MODE] != MODE_RADIX) return;
+  const int ncand = st[ST_NCAND];
+  const int base = chunk * kSelChunk;
+  if (base >= ncand) return;
+  const int end = min(base + kSelChunk, ncand);
+  const uint32_t prefix = (uint32_t)st[ST_PREFIX];
+  for (int i = threadIdx.x; i < BINS; i += 256) h[i] = 0;
+  __syncthreads();
+  const float* s = P.scores + (int64_t)u * P.N;
+  for (int j = base + threadIdx.x; j < end; j += 256) {
+    const uint32_t key = score_key(s[j]);
+    if ((key & MATCH) == prefix) atomicAdd(&h[(key >> SHIFT) & (BINS - 1)], 1);
+  }
+  __syncthreads();
+  int32_t* gh = (PASS == 1 ? P.hist_b : P.hist_a) + (int64_t)u * kHistBins;
+  for (int i = threadIdx.x; i < BINS; i += 256)
+    if (h[i]) atomicAdd(&gh[i], h[i]);
+}
+
+template <int PASS>
+__global__ void __launch_bounds__(256) sel_find(SelectParams P) {
+  constexpr int SHIFT = PASS == 0 ? 20 : (PASS == 1 ? 8 : 0);
+  constexpr int BINS = PASS == 2 ? 256 : 4096;
+  constexpr int BPT = BINS / 256;
+  __shared__ int32_t sm[264];
+  __shared__ int32_t s_digit, s_above;
+  const int u = blockIdx.x;
+  int32_t* st = P.state + (int64_t)u * 8;
+  if (st[ST_MODE] != MODE_RADIX) return;
+  const int need = st[ST_NEED];
+  int32_t* gh = (PASS == 1 ? P.hist_b : P.hist_a) + (int64_t)u * kHistBins;
+  // thread T owns digits [BINS - (T+1)*BPT, BINS - T*BPT): thread 0 has the top ones
+  const int T = threadIdx.x;
+  const int hi_d = BINS - T * BPT - 1;
+  int32_t c[BPT];
+  int32_t mine = 0;
+#pragma unroll
+  for (int e = 0; e < BPT; ++e) {
+    c[e] = gh[hi_d - e];
+    mine += c[e];
+  }
+  int32_t total;
+  const int32_t above = block_exclusive_scan<int32_t>(mine, sm, total);
+  if (above < need && need <= above + mine) {
+    int32_t a = above;
+#pragma unroll
+    for (int e = 0; e < BPT; ++e) {
+      if (a < need && need <= a + c[e]) {
+        s_digit = hi_d - e;
+        s_above = a;
+      }
+      a += c[e];
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    st[ST_PREFIX] = (int32_t)((uint32_t)st[ST_PREFIX] | ((uint32_t)s_digit << SHIFT));
+    st[ST_NEED] = need - s_above;
+  }
+  if (PASS == 1) {  // pass 2 accumulates into hist_a again
+    int32_t* ha = P.hist_a + (int64_t)u * kHistBins;
+    for (int i = threadIdx.x; i < 256; i += 256) ha[i] = 0;
+  }
+}
+
+// per chunk: keys above the threshold and keys equal to it
+__global__ void __launch_bounds__(256) sel_count(SelectParams P) {
+  __shared__ int32_t sm[264];
+  const int u = blockIdx.y, chunk = blockIdx.x;
+  const int32_t* st = P.state + (int64_t)u * 8;
+  if (st[ST_MODE] != MODE_RADIX) return;
+  const int ncand = st[ST_NCAND];
+  const int base = chunk * kSelChunk;
+  if (base >= ncand) return;
+  const int end = min(base + kSelChunk, ncand);
+  const uint32_t tau = (uint32_t)st[ST_PREFIX];
+  const float* s = P.scores + (int64_t)u * P.N;
+  int32_t gt = 0, eq = 0;
+  for (int j = base + threadIdx.x; j < end; j += 256) {
+    const uint32_t key = score_key(s[j]);
+    gt += key > tau;
+    eq += key == tau;
+  }
+  int32_t tgt, teq;
+  block_exclusive_scan<int32_t>(gt, sm, tgt);
+  block_exclusive_scan<int32_t>(eq, sm, teq);
+  if (threadIdx.x == 0) {
+    P.cnt[((int64_t)u * P.nchunks + chunk) * 2] = tgt;
+    P.cnt[((int64_t)u * P.nchunks + chunk) * 2 + 1] = teq;
+  }
+}
+
+__global__ void __launch_bounds__(256) sel_emit(SelectParams P) {
+  __shared__ int32_t sm[264];
+  const int u = blockIdx.y, chunk = blockIdx.x;
+  const int32_t* st = P.state + (int64_t)u * 8;
+  const int mode = st[ST_MODE];
+  const int ncand = st[ST_NCAND];
+  const int take = st[ST_TAKE];
+  const int p = st[ST_P];
+  int32_t* out = P.idx + (int64_t)u * P.max_sel;
+
+  if (chunk == 0) {  // forced window, count and padding
+    const int wlo = max(0, p - P.window + 1);
+    const int nw = p - wlo + 1;
+    for (int i = threadIdx.x; i < nw; i += 256) out[take + i] = wlo + i;
+    for (int i = take + nw + threadIdx.x; i < P.max_sel; i += 256) out[i] = -1;
+    if (threadIdx.x == 0) P.count[u] = take + nw;
+  }
+  if (mode == MODE_NONE) return;
+  const int base = chunk * kSelChunk;
+  if (base >= ncand) return;
+  const int end = min(base + kSelChunk, ncand);
+  if (mode == MODE_ALL) {
+    for (int j = base + threadIdx.x; j < end; j += 256) out[j] = j;
+    return;
+  }
+  const uint32_t tau = (uint32_t)st[ST_PREFIX];
+  const int need = st[ST_NEED];
+  // selected count and equal-key count of all earlier chunks
+  int32_t eq_before = 0, sel_before = 0;
+  for (int c0 = 0; c0 < chunk; c0 += 256) {
+    const int c = c0 + threadIdx.x;
+    int32_t gt = 0, eq = 0;
+    if (c < chunk) {
+      gt = P.cnt[((int64_t)u * P.nchunks + c) * 2];
+      eq = P.cnt[((int64_t)u * P.nchunks + c) * 2 + 1];
+    }
+    int32_t eq_tot;
+    const int32_t eqb = eq_before + block_exclusive_scan<int32_t>(eq, sm, eq_tot);
+    const int32_t sel = gt + max(0, min(need - eqb, eq));
+    int32_t sel_tot;
+    block_exclusive_scan<int32_t>(sel, sm, sel_tot);
+    eq_before += eq_tot;
+    sel_before += sel_tot;
+  }
+  // this chunk: thread owns 16 consecutive positions
+  const int j0 = base + threadIdx.x * 16;
+  const float* s = P.scores + (int64_t)u * P.N;
+  uint32_t keys[16];
+  int32_t my_eq = 0;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const int j = j0 + e;
+    keys[e] = (j < end) ? score_key(s[j]) : 0u;
+    my_eq += (j < end) && keys[e] == tau;
+  }
+  int32_t teq;
+  int32_t eq_rank = eq_before + block_exclusive_scan<int32_t>(my_eq, sm, teq);
+  uint32_t selmask = 0;
+  int32_t my_sel = 0;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const int j = j0 + e;
+    bool take_it = false;
+    if (j < end) {
+      if (keys[e] > tau) {
+        take_it = true;
+      } else if (keys[e] == tau) {
+        take_it = eq_rank < need;
+        ++eq_rank;
+      }
+    }
+    selmask |= (uint32_t)take_it << e;
+    my_sel += take_it;
+  }
+  int32_t tsel;
+  int32_t slot = sel_before + block_exclusive_scan<int32_t>(my_sel, sm, tsel);
+#pragma unroll
+  for (int e = 0; e < 16; ++e)
+    if (selmask >> e & 1u) {
+      if (slot < take) out[slot] = j0 + e;  // never past this unit's budget
+      ++slot;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// block baseline
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) sel_block_mass(SelectParams P) {
+  const int u = blockIdx.y;
+  const int beta = blockIdx.x * 256 + threadIdx.x;
+  const int32_t* st = P.state + (int64_t)u * 8;
+  const int ncand = st[ST_NCAND];
+  const int nb = ncand > 0 ? (ncand - 1) / P.block_size + 1 : 0;
+  if (beta >= nb) return;
+  const float* s = P.scores + (int64_t)u * P.N;
+  const int lo = beta * P.block_size;
+  const int hi = min(lo + P.block_size, ncand);
+  double m = 0.0;
+  for (int j = lo; j < hi; ++j) m += (double)s[j];
+  P.bmass[(int64_t)u * P.nblocks_max + beta] = m;
+}
+
+__global__ void __launch_bounds__(256) sel_block_pick(SelectParams P) {
+  __shared__ double s_m[256];
+  __shared__ int s_b[256];
+  __shared__ int32_t sm[264];
+  const int u = blockIdx.x;
+  const int32_t* st = P.state + (int64_t)u * 8;
+  const int ncand = st[ST_NCAND];
+  const int take = st[ST_TAKE];
+  const int p = st[ST_P];
+  const int nb = ncand > 0 ? (ncand - 1) / P.block_size + 1 : 0;
+  double* bm = P.bmass + (int64_t)u * P.nblocks_max;
+  int32_t* out = P.idx + (int64_t)u * P.max_sel;
+  // take rounds of (mass desc, block asc) argmax; a taken block's mass becomes -1
+  for (int round = 0; round < take; ++round) {
+    double best = -1.0;
+    int bb = 0x7fffffff;
+    for (int beta = threadIdx.x; beta < nb; beta += 256) {
+      const double m = bm[beta];
+      if (m > best || (m == best && beta < bb)) {
+        best = m;
+        bb = beta;
+      }
+    }
+    s_m[threadIdx.x] = best;
+    s_b[threadIdx.x] = bb;
+    __syncthreads();
+    for (int o = 128; o > 0; o >>= 1) {
+      if (threadIdx.x < o) {
+        const double m2 = s_m[threadIdx.x + o];
+        const int b2 = s_b[threadIdx.x + o];
+        if (m2 > s_m[threadIdx.x] || (m2 == s_m[threadIdx.x] && b2 < s_b[threadIdx.x])) {
+          s_m[threadIdx.x] = m2;
+          s_b[threadIdx.x] = b2;
+        }
+      }
+      __syncthreads();
+    }
+    if (threadIdx.x == 0) bm[s_b[0]] = -1.0;
+    __syncthreads();
+  }
+  // ascending emit of the taken blocks' candidate positions
+  int32_t written = 0;
+  for (int b0 = 0; b0 < nb; b0 += 256) {
+    const int beta = b0 + threadIdx.x;
+    int32_t n = 0;
+    if (beta < nb && bm[beta] == -1.0) n = min(beta * P.block_size + P.block_size, ncand) - beta * P.block_size;
+    int32_t tot;
+    const int32_t off = written + block_exclusive_scan<int32_t>(n, sm, tot);
+    for (int e = 0; e < n && off + e < P.max_sel; ++e) out[off + e] = beta * P.block_size + e;
+    written += tot;
+  }
+  const int wlo = max(0, p - P.window + 1);
+  const int nw = p - wlo + 1;
+  for (int i = threadIdx.x; i < nw && written + i < P.max_sel; i += 256) out[written + i] = wlo + i;
+  for (int i = written + nw + threadIdx.x; i < P.max_sel; i += 256) out[i] = -1;
+  if (threadIdx.x == 0) P.count[u] = written + nw;
+}
+
+}  // namespace
+
+hipError_t launch_select(const SelectParams& p, hipStream_t s) {
+  const dim3 grid_c(p.nchunks, p.units);
+  hipError_t e;
+#define HS2_L(name, kern, grid)                                   \
+  do {                                                            \
+    TimedLaunch tl_(name, s);                                     \
+    hipLaunchKernelGGL(kern, grid, dim3(256), 0, s, p);           \
+    if ((e = hipGetLastError()) != hipSuccess) return e;          \
+  } while (0)
+  HS2_L("select_init", sel_init, dim3(p.units));
+  if (p.block_size == 1) {
+    HS2_L("select_hist", sel_hist<0>, grid_c);
+    HS2_L("select_find", sel_find<0>, dim3(p.units));
+    HS2_L("select_hist", sel_hist<1>, grid_c);
+    HS2_L("select_find", sel_find<1>, dim3(p.units));
+    HS2_L("select_hist", sel_hist<2>, grid_c);
+    HS2_L("select_find", sel_find<2>, dim3(p.units));
+    HS2_L("select_count", sel_count, grid_c);
+    HS2_L("select_emit", sel_emit, grid_c);
+  } else {
+    HS2_L("select_block_mass", sel_block_mass, dim3((p.nblocks_max + 255) / 256, p.units));
+    HS2_L("select_block_pick", sel_block_pick, dim3(p.units));
+  }
+#undef HS2_L
+  return hipSuccess;
+}
+
+}  // namespace hs2

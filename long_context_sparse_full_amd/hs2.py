@@ -1,0 +1,237 @@
+"""Python binding of libhs2.so (C ABI in include/hs2.h).
+
+Argument marshalling only: every step of the hot path runs in the library's
+gfx950 kernels.  Tensors are torch CUDA (HIP) tensors; each call passes
+``tensor.data_ptr()`` and the current torch stream.  Importing this module
+loads the library and raises ImportError when it has not been built (run
+``python -m long_context_sparse_full_amd.build``); there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libhs2.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"libhs2.so not found at {LIB_PATH}: build it with "
+                      "`python -m long_context_sparse_full_amd.build` (no fallback exists)")
+_lib = ctypes.CDLL(LIB_PATH)
+
+F32, BF16, FP8_E4M3FN = 0, 1, 2
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
+
+
+class KVDesc(ctypes.Structure):
+    _fields_ = [
+        ("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("dtype", ctypes.c_int32),
+        ("stride_b", ctypes.c_int64), ("stride_h", ctypes.c_int64), ("stride_n", ctypes.c_int64),
+        ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
+        ("B", ctypes.c_int32), ("Hkv", ctypes.c_int32), ("N", ctypes.c_int32), ("D", ctypes.c_int32),
+    ]
+
+
+_vp, _i32, _f32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+_KVP = ctypes.POINTER(KVDesc)
+
+
+def _sig(name, res, args):
+    f = getattr(_lib, name)
+    f.restype = res
+    f.argtypes = args
+    return f
+
+
+_abi_version = _sig("hs2_abi_version", ctypes.c_int, [])
+_status_string = _sig("hs2_status_string", ctypes.c_char_p, [ctypes.c_int])
+_last_error = _sig("hs2_last_error", ctypes.c_char_p, [])
+_full_ws = _sig("hs2_full_attn_scores_workspace", _sz, [_KVP, _i32, _i32])
+_full = _sig("hs2_full_attn_scores", ctypes.c_int,
+             [_KVP, _vp, _i32, _i32, _i32, _i32, _f32, _vp, _vp, _vp, _vp, _sz, _vp])
+_sel_ws = _sig("hs2_select_workspace", _sz, [_i32, _i32, _i32, _i32])
+_sel_ws_for = _sig("hs2_select_workspace_for", _sz, [_i32, _i32, _i32, _i32, _i32])
+_select = _sig("hs2_select_topk_window", ctypes.c_int,
+               [_vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _i32, _vp, _sz, _vp])
+_sparse = _sig("hs2_sparse_attn_gather", ctypes.c_int,
+               [_KVP, _vp, _i32, _i32, _i32, _f32, _vp, _vp, _i32, _vp, _vp, _vp])
+_bridge = _sig("hs2_kv_bridge", ctypes.c_int, [_vp, _i32, _i32, _vp, _KVP, _i32, _i32, _vp])
+_dbg_e4m3 = _sig("hs2_debug_e4m3fn_to_f32", ctypes.c_int, [_vp, _vp, _i32, _vp])
+_t_enable = _sig("hs2_timing_enable", ctypes.c_int, [ctypes.c_int])
+_t_reset = _sig("hs2_timing_reset", ctypes.c_int, [])
+_t_collect = _sig("hs2_timing_collect", ctypes.c_int,
+                  [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int32)])
+_t_name = _sig("hs2_timing_kernel_name", ctypes.c_char_p, [_i32])
+
+EXPORTED = [
+    "hs2_abi_version", "hs2_status_string", "hs2_last_error", "hs2_full_attn_scores_workspace",
+    "hs2_full_attn_scores", "hs2_select_workspace", "hs2_select_workspace_for", "hs2_select_topk_window",
+    "hs2_sparse_attn_gather", "hs2_kv_bridge", "hs2_debug_e4m3fn_to_f32", "hs2_timing_enable",
+    "hs2_timing_reset", "hs2_timing_collect", "hs2_timing_kernel_name",
+]
+
+
+class HS2Error(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = _last_error().decode(errors="replace")
+        super().__init__(f"{where}: {_status_string(status).decode()} ({status}): {msg}")
+
+
+def _check(status: int, where: str):
+    if status != OK:
+        raise HS2Error(status, where)
+
+
+def abi_version() -> int:
+    return int(_abi_version())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return FP8_E4M3FN
+    raise TypeError(f"unsupported element type {t.dtype}")
+
+
+def kv_desc(k: torch.Tensor, v: torch.Tensor, k_scale=None, v_scale=None) -> KVDesc:
+    """Descriptor of a [B, Hkv, N, D] cache (uint8/float8_e4m3fn caches need scales)."""
+    if k.shape != v.shape or k.dim() != 4 or k.stride() != v.stride() or k.dtype != v.dtype:
+        raise ValueError("k and v must be [B, Hkv, N, D] tensors of one dtype and layout")
+    if k.stride(3) != 1:
+        raise ValueError("head_dim must be contiguous")
+    B, H, N, D = k.shape
+    code = _dtype_code(k)
+    ks = vs = None
+    if code == FP8_E4M3FN:
+        if k_scale is None or v_scale is None:
+            ks = vs = None
+        else:
+            ks = k_scale.data_ptr()
+            vs = v_scale.data_ptr()
+    return KVDesc(k.data_ptr(), v.data_ptr(), code, k.stride(0), k.stride(1), k.stride(2), ks, vs, B, H, N, D)
+
+
+def full_attn_scores_workspace(k, v, Tq: int, Hq: int) -> int:
+    d = kv_desc(k, v)
+    return int(_full_ws(ctypes.byref(d), Tq, Hq))
+
+
+def full_attn_scores(k, v, q, q_pos0: int, softmax_scale: float | None = None, k_scale=None, v_scale=None,
+                     out=None, lse=None, scores=None, workspace=None, want_lse: bool = True):
+    """Full-attention layer: returns (out [B,Tq,Hq,D], lse [B,Tq,Hq] or None, scores [B,Tq,Hkv,N])."""
+    d = kv_desc(k, v, k_scale, v_scale)
+    B, Tq, Hq, D = q.shape
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(D)
+    dev = q.device
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Tq, Hq), dtype=torch.float32, device=dev)
+    if scores is None:
+        scores = torch.empty((B, Tq, d.Hkv, d.N), dtype=torch.float32, device=dev)
+    need = int(_full_ws(ctypes.byref(d), Tq, Hq))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    st = _full(ctypes.byref(d), q.data_ptr(), _dtype_code(q), Tq, Hq, int(q_pos0), float(softmax_scale),
+               out.data_ptr(), None if lse is None else lse.data_ptr(), scores.data_ptr(),
+               workspace.data_ptr(), workspace.numel(), _stream())
+    _check(st, "hs2_full_attn_scores")
+    return out, lse, scores
+
+
+def select_workspace(B, Tq, Hkv, N, block_size: int | None = None) -> int:
+    if block_size is None:
+        return int(_sel_ws(B, Tq, Hkv, N))
+    return int(_sel_ws_for(B, Tq, Hkv, N, block_size))
+
+
+def select_topk_window(scores, q_pos0: int, k: int, window: int, block_size: int = 1, max_sel: int | None = None,
+                       idx=None, count=None, workspace=None):
+    """Top-k (token or block) + forced window: returns (idx int32, count int32)."""
+    B, Tq, Hkv, N = scores.shape
+    if max_sel is None:
+        max_sel = min(N, k * block_size + window)
+    dev = scores.device
+    if idx is None:
+        idx = torch.empty((B, Tq, Hkv, max_sel), dtype=torch.int32, device=dev)
+    if count is None:
+        count = torch.empty((B, Tq, Hkv), dtype=torch.int32, device=dev)
+    if workspace is None:
+        workspace = torch.empty(max(select_workspace(B, Tq, Hkv, N, block_size), 256), dtype=torch.uint8, device=dev)
+    st = _select(scores.data_ptr(), B, Tq, Hkv, N, int(q_pos0), int(k), int(window), int(block_size),
+                 idx.data_ptr(), count.data_ptr(), int(max_sel), workspace.data_ptr(), workspace.numel(), _stream())
+    _check(st, "hs2_select_topk_window")
+    return idx, count
+
+
+def sparse_attn_gather(k, v, q, idx, count, softmax_scale: float | None = None, k_scale=None, v_scale=None,
+                       out=None, lse=None, want_lse: bool = True):
+    """Sparse layer over the shared index list: returns (out, lse or None)."""
+    d = kv_desc(k, v, k_scale, v_scale)
+    B, Tq, Hq, D = q.shape
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Tq, Hq), dtype=torch.float32, device=q.device)
+    st = _sparse(ctypes.byref(d), q.data_ptr(), _dtype_code(q), Tq, Hq, float(softmax_scale), idx.data_ptr(),
+                 count.data_ptr(), idx.shape[-1], out.data_ptr(), None if lse is None else lse.data_ptr(), _stream())
+    _check(st, "hs2_sparse_attn_gather")
+    return out, lse
+
+
+def kv_bridge(hidden, w_kv, k_cache, v_cache, batch_index: int, pos0: int):
+    """Project bf16 hidden states [T, d_model] with w_kv [d_model, 2*Hkv*D] into the bf16 cache rows."""
+    d = kv_desc(k_cache, v_cache)
+    T, dm = hidden.shape
+    st = _bridge(hidden.data_ptr(), T, dm, w_kv.data_ptr(), ctypes.byref(d), int(batch_index), int(pos0), _stream())
+    _check(st, "hs2_kv_bridge")
+
+
+def debug_e4m3fn_to_f32(codes: torch.Tensor) -> torch.Tensor:
+    out = torch.empty(codes.numel(), dtype=torch.float32, device=codes.device)
+    _check(_dbg_e4m3(codes.data_ptr(), out.data_ptr(), codes.numel(), _stream()), "hs2_debug_e4m3fn_to_f32")
+    return out
+
+
+def timing_enable(on: bool = True):
+    _check(_t_enable(int(bool(on))), "hs2_timing_enable")
+
+
+def timing_reset():
+    _check(_t_reset(), "hs2_timing_reset")
+
+
+def timing_collect(name: str):
+    ms = ctypes.c_double()
+    n = ctypes.c_int32()
+    _check(_t_collect(name.encode(), ctypes.byref(ms), ctypes.byref(n)), "hs2_timing_collect")
+    return ms.value, n.value
+
+
+def timing_kernel_names():
+    out, i = [], 0
+    while True:
+        s = _t_name(i)
+        if s is None:
+            return out
+        out.append(s.decode())
+        i += 1
+
+
+def raw_call(name: str):
+    """The underlying ctypes function of an exported symbol (for tests of the C ABI)."""
+    return getattr(_lib, name)

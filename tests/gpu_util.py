@@ -1,0 +1,147 @@
+"""Helpers shared by the GPU parity tests, smoke() and bench.py: moving the
+generator's host arrays to the device, running the hot path through the C ABI,
+and the parity criteria (tolerances are stated here, once)."""
+from __future__ import annotations
+
+import math
+import sys
+
+import numpy as np
+import torch
+
+# ---- tolerances --------------------------------------------------------------
+# Outputs of the full and sparse layers, max-abs against the fp64 oracle on the
+# same (dequantised) inputs: 1e-5 for fp32, 1e-2 for bf16 / FP8 caches.
+O_TOL = {"f32": 1e-5, "bf16": 1e-2, "fp8": 1e-2}
+# LSE (natural log), max-abs: fp32 logits on every path.
+LSE_TOL = {"f32": 1e-5, "bf16": 1e-4, "fp8": 1e-4}
+# Scores: |dS| <= S_ABS + S_REL * S_oracle.  fp32 logits (exact bf16/fp8
+# products, fp32 sums) and an fp32 log-sum-exp give ~1e-6 relative error.
+S_REL, S_ABS = 2e-5, 1e-9
+# Selection: bit-exact indices where the oracle's score gap at the k-th
+# boundary exceeds GAP; elsewhere the selected score mass must agree to MASS.
+GAP, MASS = 1e-4, 1e-4
+
+
+def log(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def dev(a: np.ndarray) -> torch.Tensor:
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if a.dtype == np.uint16:
+        t = t.view(torch.bfloat16)
+    return t.cuda()
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    if t.dtype == torch.bfloat16:
+        t = t.float()
+    return t.cpu().numpy()
+
+
+class DeviceBlock:
+    """One hybrid block's inputs on the device."""
+
+    def __init__(self, inp):
+        self.inp = inp
+        self.k = dev(inp.k)
+        self.v = dev(inp.v)
+        self.ks = dev(inp.k_scale) if inp.k_scale is not None else None
+        self.vs = dev(inp.v_scale) if inp.v_scale is not None else None
+        self.q = dev(inp.q_full)
+        self.qs = [dev(x) for x in inp.q_sparse]
+
+
+def run_block(hs2, blk: DeviceBlock, spec, k=None, window=None, block_size=1, layers=None):
+    """full -> select -> sparse layers on the GPU; returns host arrays."""
+    k = spec.k if k is None else k
+    window = spec.window if window is None else window
+    out, lse, sc = hs2.full_attn_scores(blk.k, blk.v, blk.q, spec.q_pos0, k_scale=blk.ks, v_scale=blk.vs)
+    max_sel = min(spec.N, k * block_size + window)
+    idx, cnt = hs2.select_topk_window(sc, spec.q_pos0, k, window, block_size=block_size, max_sel=max_sel)
+    sp = []
+    for q in (blk.qs if layers is None else blk.qs[:layers]):
+        o, l = hs2.sparse_attn_gather(blk.k, blk.v, q, idx, cnt, k_scale=blk.ks, v_scale=blk.vs)
+        sp.append((host(o), host(l)))
+    torch.cuda.synchronize()
+    return dict(out=host(out), lse=host(lse), scores=host(sc), idx=host(idx), count=host(cnt), sparse=sp)
+
+
+def max_abs(a, b) -> float:
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    if a.size == 0:
+        return 0.0
+    return float(np.max(np.abs(a - b)))
+
+
+def assert_close(got, want, tol, what):
+    err = max_abs(got, want)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite values"
+    assert err <= tol, f"{what}: max-abs error {err:.3e} > {tol:.1e}"
+    return err
+
+
+def assert_scores(got, want, what="scores"):
+    got = np.asarray(got, np.float64)
+    want = np.asarray(want, np.float64)
+    bound = S_ABS + S_REL * np.abs(want)
+    bad = np.abs(got - want) > bound
+    if bad.any():
+        i = np.unravel_index(np.argmax(np.abs(got - want) - bound), got.shape)
+        raise AssertionError(f"{what}: {int(bad.sum())} entries outside |dS| <= {S_ABS:g} + {S_REL:g}*S; "
+                             f"worst at {i}: got {got[i]:.9e} want {want[i]:.9e}")
+    rel = np.max(np.abs(got - want) / (S_ABS + np.abs(want)))
+    return float(rel)
+
+
+def check_structure(idx, count, q_pos0, k, window, N, block_size=1):
+    """Window always in, ascending, unique, causal, exact count, -1 padding."""
+    B, Tq, Hkv, max_sel = idx.shape
+    for u in np.ndindex(B, Tq, Hkv):
+        p = q_pos0 + u[1]
+        n = int(count[u])
+        sel = idx[u][:n]
+        ncand = max(0, p - window + 1)
+        if block_size == 1:
+            want_n = min(k, ncand) + min(window, p + 1)
+            assert n == want_n, f"count {n} != {want_n} at {u}"
+        assert np.all(idx[u][n:] == -1), f"padding at {u}"
+        assert np.all(np.diff(sel) > 0), f"not ascending/unique at {u}"
+        assert n == 0 or (sel[0] >= 0 and sel[-1] <= p), f"not causal at {u}"
+        wlo = max(0, p - window + 1)
+        nw = p - wlo + 1
+        assert np.array_equal(sel[n - nw:] if nw else sel[:0], np.arange(wlo, p + 1)), f"window missing at {u}"
+
+
+def check_selection_vs_oracle(idx, count, idx_or, count_or, scores_or, q_pos0, k, window):
+    """North-star criterion per (b, t, g): bit-exact where the oracle's gap at the
+    k-th boundary exceeds GAP, else equal selected mass within MASS.  Returns
+    (units checked bit-exact, units checked by mass, worst mass difference)."""
+    B, Tq, Hkv, _ = idx.shape
+    exact = by_mass = 0
+    worst = 0.0
+    for u in np.ndindex(B, Tq, Hkv):
+        p = q_pos0 + u[1]
+        ncand = max(0, p - window + 1)
+        s = scores_or[u][:ncand]
+        if k <= 0 or k >= ncand:
+            gap = math.inf
+        else:
+            top = np.sort(s)[::-1]
+            gap = top[k - 1] - top[k]
+        g_sel = idx[u][: count[u]]
+        o_sel = idx_or[u][: count_or[u]]
+        if gap > GAP:
+            assert np.array_equal(g_sel, o_sel), f"index set differs at {u} although gap {gap:.2e} > {GAP}"
+            exact += 1
+        else:
+            gm = s[g_sel[g_sel < ncand]].sum()
+            om = s[o_sel[o_sel < ncand]].sum()
+            d = abs(gm - om)
+            worst = max(worst, d)
+            assert d <= MASS, f"selected mass differs by {d:.2e} at {u} (gap {gap:.2e})"
+            by_mass += 1
+    return exact, by_mass, worst

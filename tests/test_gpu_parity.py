@@ -1,0 +1,262 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle on the same
+seeded inputs: full layer (out, lse, scores), selection, sparse layers; small
+shapes spanning several tiles with ragged tails and edge cases."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from long_context_sparse_full_amd import synth
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def hs2():
+    from long_context_sparse_full_amd import hs2 as mod
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return mod
+
+
+def small_spec(kv, D=128, G=8, Hkv=2, B=2, N=1000, Tq=1, k=64, window=16, q_std=None, needles=8, mode="uniform"):
+    qd = "f32" if kv == "f32" else "bf16"
+    if q_std is None:
+        q_std = 1.0 if kv == "f32" else 1.0 / math.sqrt(D)
+    return synth.Spec(f"small-{kv}", 90, B=B, N=N, Tq=Tq, Hq=G * Hkv, Hkv=Hkv, D=D, kv_dtype=kv, q_dtype=qd, k=k,
+                      window=window, n_sparse=2, needles=needles, needle_mode=mode, q_std=q_std)
+
+
+def oracle_full(inp, spec):
+    return oracle.full_attn_scores(inp.q_full, inp.k, inp.v, spec.q_pos0, k_scale=inp.k_scale, v_scale=inp.v_scale)
+
+
+def test_e4m3fn_hardware_decode_matches_definition(hs2):
+    codes = torch.arange(256, dtype=torch.uint8, device="cuda")
+    got = gu.host(hs2.debug_e4m3fn_to_f32(codes)).astype(np.float64)
+    want = oracle.e4m3fn_table()
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], want[~nan])
+
+
+CASES = [
+    # kv, D, G, Hkv, B, N, Tq
+    ("f32", 64, 4, 2, 1, 300, 8),
+    ("f32", 128, 8, 1, 2, 97, 1),
+    ("f32", 64, 16, 1, 1, 1, 1),
+    ("bf16", 128, 8, 2, 2, 1000, 1),
+    ("bf16", 128, 8, 2, 1, 4097, 1),
+    ("bf16", 128, 4, 2, 2, 777, 3),
+    ("bf16", 64, 8, 2, 1, 600, 2),
+    ("bf16", 128, 16, 1, 1, 33, 1),
+    ("bf16", 128, 8, 1, 1, 1, 1),
+    ("fp8", 128, 8, 2, 2, 1000, 1),
+    ("fp8", 128, 8, 4, 1, 5000, 1),
+    ("fp8", 64, 4, 2, 1, 513, 4),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "-".join(map(str, c)))
+def test_full_layer_parity(hs2, case):
+    kv, D, G, Hkv, B, N, Tq = case
+    spec = small_spec(kv, D=D, G=G, Hkv=Hkv, B=B, N=N, Tq=Tq, needles=min(8, max(0, N - 16)))
+    gu.log(f"full-layer parity {case}")
+    inp = synth.make_inputs(spec, seed=1234)
+    blk = gu.DeviceBlock(inp)
+    out, lse, sc = hs2.full_attn_scores(blk.k, blk.v, blk.q, spec.q_pos0, k_scale=blk.ks, v_scale=blk.vs)
+    torch.cuda.synchronize()
+    o_or, l_or, s_or = oracle_full(inp, spec)
+    e_o = gu.assert_close(gu.host(out), o_or, gu.O_TOL[kv], "out")
+    e_l = gu.assert_close(gu.host(lse), l_or, gu.LSE_TOL[kv], "lse")
+    e_s = gu.assert_scores(gu.host(sc), s_or)
+    gu.log(f"  max|dO|={e_o:.2e} max|dLSE|={e_l:.2e} max rel dS={e_s:.2e}")
+
+
+def test_full_layer_q_pos0_before_end(hs2):
+    spec = small_spec("bf16", N=900, Tq=2)
+    inp = synth.make_inputs(spec, seed=7)
+    blk = gu.DeviceBlock(inp)
+    qp = 500
+    out, lse, sc = hs2.full_attn_scores(blk.k, blk.v, blk.q, qp)
+    torch.cuda.synchronize()
+    o_or, l_or, s_or = oracle.full_attn_scores(inp.q_full, inp.k, inp.v, qp)
+    gu.assert_close(gu.host(out), o_or, gu.O_TOL["bf16"], "out")
+    gu.assert_close(gu.host(lse), l_or, gu.LSE_TOL["bf16"], "lse")
+    gu.assert_scores(gu.host(sc), s_or)
+    assert np.all(gu.host(sc)[..., qp + 2:] == 0.0)
+
+
+# ---------------------------------------------------------------- selection
+
+def _select_both(hs2, scores_np, q_pos0, k, window, block_size=1):
+    s = torch.from_numpy(np.ascontiguousarray(scores_np, np.float32)).cuda()
+    N = scores_np.shape[-1]
+    max_sel = min(N, k * block_size + window)
+    idx, cnt = hs2.select_topk_window(s, q_pos0, k, window, block_size=block_size, max_sel=max_sel)
+    torch.cuda.synchronize()
+    idx_or, cnt_or = oracle.select_topk_window(scores_np.astype(np.float32).astype(np.float64), q_pos0, k, window,
+                                               block_size=block_size, max_sel=max_sel)
+    return gu.host(idx), gu.host(cnt), idx_or, cnt_or
+
+
+SEL_CASES = [
+    # B, Tq, Hkv, N, k, window, block_size, kind
+    (1, 1, 4, 70000, 1024, 128, 1, "random"),
+    (2, 3, 2, 9000, 300, 32, 1, "random"),
+    (1, 2, 2, 5000, 100, 8, 1, "ties"),
+    (1, 1, 1, 4096, 512, 64, 1, "allequal"),
+    (1, 1, 1, 3000, 0, 16, 1, "random"),
+    (1, 1, 1, 3000, 5000, 16, 1, "random"),
+    (1, 4, 1, 100, 10, 128, 1, "random"),      # p < window for every query
+    (1, 1, 2, 5000, 40, 0, 1, "random"),       # no window
+    (1, 1, 1, 1, 5, 3, 1, "random"),
+    (2, 2, 2, 20000, 16, 128, 64, "random"),   # block baseline
+    (1, 1, 1, 6000, 7, 5, 64, "blockties"),
+    (1, 1, 1, 3000, 100, 16, 64, "random"),    # k blocks cover everything
+    (1, 1, 1, 50000, 1024, 128, 1, "tiny"),    # exercises the low digits
+]
+
+
+@pytest.mark.parametrize("case", SEL_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_select_bit_exact_on_identical_scores(hs2, case):
+    B, Tq, Hkv, N, k, W, bs, kind = case
+    gu.log(f"select {case}")
+    rng = np.random.default_rng(N + k)
+    if kind == "random":
+        sc = rng.random((B, Tq, Hkv, N)).astype(np.float32) * 1e-3
+    elif kind == "ties":
+        sc = (rng.integers(0, 6, (B, Tq, Hkv, N)) / 64.0).astype(np.float32)
+    elif kind == "allequal":
+        sc = np.full((B, Tq, Hkv, N), 1.0 / N, np.float32)
+    elif kind == "blockties":
+        sc = np.zeros((B, Tq, Hkv, N), np.float32)
+        sc[..., ::64] = 0.5  # every block has the same mass
+    else:  # "tiny": values that differ only in the lowest mantissa bits
+        base = np.float32(3e-6)
+        sc = (base + rng.integers(0, 300, (B, Tq, Hkv, N)).astype(np.float32) * np.float32(2.0 ** -42)).astype(np.float32)
+    qp = N - Tq
+    idx, cnt, idx_or, cnt_or = _select_both(hs2, sc, qp, k, W, bs)
+    assert np.array_equal(cnt, cnt_or), "counts differ"
+    assert np.array_equal(idx, idx_or), "index lists differ"
+    gu.check_structure(idx, cnt, qp, k, W, N, bs)
+
+
+def test_select_deterministic(hs2):
+    rng = np.random.default_rng(3)
+    sc = (rng.integers(0, 50, (1, 1, 4, 300000)) / 977.0).astype(np.float32)
+    a = _select_both(hs2, sc, 300000 - 1, 1024, 128)
+    b = _select_both(hs2, sc, 300000 - 1, 1024, 128)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[0], a[2])
+
+
+# ------------------------------------------------------------ sparse layers
+
+@pytest.mark.parametrize("kv,D,G", [("f32", 64, 4), ("bf16", 128, 8), ("fp8", 128, 8), ("bf16", 64, 16)])
+def test_sparse_parity_on_gpu_selection(hs2, kv, D, G):
+    spec = small_spec(kv, D=D, G=G, Hkv=2, B=2, N=3000, Tq=2, k=200, window=32)
+    gu.log(f"sparse parity {kv} D={D} G={G}")
+    inp = synth.make_inputs(spec, seed=99)
+    blk = gu.DeviceBlock(inp)
+    res = gu.run_block(hs2, blk, spec)
+    for layer, (o, l) in enumerate(res["sparse"]):
+        o_or, l_or = oracle.sparse_attn(inp.q_sparse[layer], inp.k, inp.v, res["idx"], res["count"],
+                                        k_scale=inp.k_scale, v_scale=inp.v_scale)
+        gu.assert_close(o, o_or, gu.O_TOL[kv], f"sparse layer {layer} out")
+        gu.assert_close(l, l_or, gu.LSE_TOL[kv], f"sparse layer {layer} lse")
+
+
+def test_sparse_random_lists_and_empty(hs2):
+    spec = small_spec("bf16", B=1, N=4000, Tq=5)
+    inp = synth.make_inputs(spec, seed=5)
+    blk = gu.DeviceBlock(inp)
+    rng = np.random.default_rng(0)
+    max_sel = 700
+    idx = np.full((1, 5, 2, max_sel), -1, np.int32)
+    cnt = np.zeros((1, 5, 2), np.int32)
+    for u, n in zip(np.ndindex(1, 5, 2), [0, 1, 31, 32, 33, 255, 256, 257, 699, 700]):
+        idx[u][:n] = np.sort(rng.choice(4000, n, replace=False))
+        cnt[u] = n
+    o, l = hs2.sparse_attn_gather(blk.k, blk.v, blk.qs[0], gu.dev(idx), gu.dev(cnt))
+    torch.cuda.synchronize()
+    o_or, l_or = oracle.sparse_attn(inp.q_sparse[0], inp.k, inp.v, idx, cnt)
+    o, l = gu.host(o), gu.host(l)
+    empty = cnt == 0
+    assert np.all(o[0, 0, :8] == 0.0) and np.all(np.isneginf(l[0, 0, :8]))
+    gu.assert_close(o, o_or, gu.O_TOL["bf16"], "out")
+    fin = ~np.isinf(l_or)
+    gu.assert_close(l[fin], l_or[fin], gu.LSE_TOL["bf16"], "lse")
+    assert empty.sum() == 1
+
+
+def test_sparse_equals_full_when_k_covers_and_swa_when_k0(hs2):
+    spec = small_spec("bf16", B=1, N=1500, Tq=1, Hkv=2)
+    inp = synth.make_inputs(spec, seed=17)
+    blk = gu.DeviceBlock(inp)
+    full_o, _, sc = hs2.full_attn_scores(blk.k, blk.v, blk.q, spec.q_pos0)
+    idx, cnt = hs2.select_topk_window(sc, spec.q_pos0, spec.N, spec.window, max_sel=spec.N)
+    o, _ = hs2.sparse_attn_gather(blk.k, blk.v, blk.q, idx, cnt)
+    torch.cuda.synchronize()
+    assert np.array_equal(gu.host(idx)[0, 0, 0], np.arange(spec.N))
+    gu.assert_close(gu.host(o), gu.host(full_o), 2e-3, "k>=|C| sparse vs full")
+    idx0, cnt0 = hs2.select_topk_window(sc, spec.q_pos0, 0, 128, max_sel=128)
+    o0, _ = hs2.sparse_attn_gather(blk.k, blk.v, blk.q, idx0, cnt0)
+    torch.cuda.synchronize()
+    assert np.array_equal(gu.host(idx0)[0, 0, 1], np.arange(spec.N - 128, spec.N))
+    o_or, _ = oracle.sparse_attn(inp.q_full, inp.k, inp.v, gu.host(idx0), gu.host(cnt0))
+    gu.assert_close(gu.host(o0), o_or, gu.O_TOL["bf16"], "k=0 sliding window")
+
+
+# ---------------------------------------------------- planted-gap variants
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8", "f32"])
+def test_planted_gap_indices_bit_exact(hs2, kv):
+    """Exactly k strong needles per (b, g): the k-th boundary has a wide gap,
+    so the GPU's index set must equal the oracle's bit for bit."""
+    k = 12
+    spec = small_spec(kv, B=2, N=2048, Tq=1, Hkv=2, G=8 if kv != "f32" else 4, D=128 if kv != "f32" else 64,
+                      k=k, window=32, needles=k, mode="per_head")
+    inp = synth.make_inputs(spec, seed=4242)
+    blk = gu.DeviceBlock(inp)
+    res = gu.run_block(hs2, blk, spec)
+    _, _, s_or = oracle_full(inp, spec)
+    idx_or, cnt_or = oracle.select_topk_window(s_or, spec.q_pos0, k, spec.window, max_sel=spec.max_sel)
+    exact, by_mass, _ = gu.check_selection_vs_oracle(res["idx"], res["count"], idx_or, cnt_or, s_or, spec.q_pos0, k,
+                                                     spec.window)
+    assert by_mass == 0 and exact == spec.B * spec.Hkv, "planted gaps must put every unit on the bit-exact branch"
+    # the needles are what was picked
+    for b in range(spec.B):
+        for g in range(spec.Hkv):
+            sel = set(res["idx"][b, 0, g, :k].tolist())
+            assert sel == set(inp.needle_pos[b, g].tolist())
+
+
+def test_full_path_bitwise_deterministic(hs2):
+    spec = small_spec("fp8", B=1, N=20000, Hkv=4)
+    inp = synth.make_inputs(spec, seed=8)
+    blk = gu.DeviceBlock(inp)
+    a = gu.run_block(hs2, blk, spec)
+    b = gu.run_block(hs2, blk, spec)
+    for key in ("out", "lse", "scores", "idx", "count"):
+        assert np.array_equal(a[key], b[key]), key
+    for (oa, la), (ob, lb) in zip(a["sparse"], b["sparse"]):
+        assert np.array_equal(oa, ob) and np.array_equal(la, lb)
+
+
+def test_strided_cache_view(hs2):
+    """A cache that is a view into a longer buffer (padded rows, extra heads)."""
+    spec = small_spec("bf16", B=1, N=700, Hkv=2)
+    inp = synth.make_inputs(spec, seed=21)
+    big_k = torch.zeros((1, 3, 800, 136), dtype=torch.bfloat16, device="cuda")
+    big_v = torch.zeros_like(big_k)
+    big_k[:, :2, :700, :128] = gu.dev(inp.k)
+    big_v[:, :2, :700, :128] = gu.dev(inp.v)
+    k = big_k[:, :2, :700, :128]
+    v = big_v[:, :2, :700, :128]
+    out, lse, sc = hs2.full_attn_scores(k, v, gu.dev(inp.q_full), spec.q_pos0)
+    torch.cuda.synchronize()
+    o_or, l_or, s_or = oracle_full(inp, spec)
+    gu.assert_close(gu.host(out), o_or, gu.O_TOL["bf16"], "out")
+    gu.assert_scores(gu.host(sc), s_or)
