@@ -74,6 +74,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="decode1m_fp8")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no multi-GPU path",
@@ -89,6 +91,22 @@ def main():
         log("no GPU visible")
         sys.exit(1)
     torch.cuda.set_device(0)
+    if args.copy_probe:
+        # a plain copy of known size: its FETCH_SIZE / WRITE_SIZE readings give
+        # the scale that turns those counters into HBM bytes
+        n = 1 << 30
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for i in range(4):
+            c0.record()
+            dst.copy_(src)
+            c1.record()
+            torch.cuda.synchronize()
+            log(f"[copy-probe] {n} B read + {n} B written in {c0.elapsed_time(c1):.3f} ms "
+                f"({2 * n / c0.elapsed_time(c1) / 1e6:.1f} GB/s)")
+        print(json.dumps({"copy_probe_bytes": n, "ms": c0.elapsed_time(c1)}), flush=True)
+        return
     spec = synth.config(args.config)
     if spec.Tq != 1:
         log("bench.py times decode workloads (Tq = 1)")

@@ -152,6 +152,14 @@ int hs2_kv_bridge(const void* hidden, int32_t T, int32_t d_model, const void* w_
  * the hardware conversion with the format's definition code by code. */
 int hs2_debug_e4m3fn_to_f32(const uint8_t* codes, float* out, int32_t n, hipStream_t stream);
 
+/* Diagnostic: streaming-read probe.  Reads `bytes` (a multiple of 16) of the
+ * 16-byte aligned device buffer `buf` once with 16-byte non-temporal loads
+ * from `blocks` workgroups of 256 threads, and writes one word per thread to
+ * `out` (blocks*256 uint32).  Its duration (kernel "stream_read") gives the
+ * HBM read bandwidth this GPU actually sustains, the ceiling the scan is
+ * compared with. */
+int hs2_debug_stream_read(const void* buf, size_t bytes, uint32_t* out, int32_t blocks, hipStream_t stream);
+
 /* Per-kernel timing with HIP events on the launch stream (off by default).
  * While enabled, every kernel launch of the library is bracketed by an event
  * pair on its stream.  hs2_timing_collect synchronises those events and

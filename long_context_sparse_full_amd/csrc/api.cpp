@@ -45,6 +45,8 @@ int check_kv(const hs2_kv_desc* kv, const char* what) {
   if (!al16(kv->k) || !al16(kv->v)) return fail(HS2_ERR_INVALID_ARG, w + ": k/v base pointers must be 16-byte aligned");
   if ((kv->stride_n * es) % 16 || (kv->stride_h * es) % 16 || (kv->stride_b * es) % 16)
     return fail(HS2_ERR_INVALID_ARG, w + ": k/v strides must be multiples of 16 bytes");
+  if (kv->stride_n * es > (int64_t(1) << 24))
+    return fail(HS2_ERR_UNSUPPORTED, w + ": k/v row stride above 16 MiB");
   if (kv->dtype == HS2_FP8_E4M3FN && (!kv->k_scale || !kv->v_scale))
     return fail(HS2_ERR_UNSUPPORTED, w + ": FP8_E4M3FN cache needs k_scale and v_scale");
   return HS2_OK;
@@ -66,11 +68,14 @@ int check_q(const hs2_kv_desc* kv, const void* q, int q_dtype, int Tq, int Hq, c
 struct FullPlan {
   int tpack, n_tpacks, rows, units, nsplit, split_len;
   int64_t npad;
-  size_t off_ml, off_o, off_lse2, off_logits, total;
+  size_t off_ml, off_o, off_lse2, off_lg16, off_lgmax, total;
 };
 
-// Position splits: about 2048 workgroups in total (8 per CU on 256 CUs), split
-// lengths a multiple of 256 positions (64 on the fp32 path).
+// Position splits: about HS2_SCAN_TARGET_WGS workgroups in total (4 per CU on
+// 256 CUs), split lengths a multiple of 256 positions (64 on the fp32 path).
+#ifndef HS2_SCAN_TARGET_WGS
+#define HS2_SCAN_TARGET_WGS 1024
+#endif
 FullPlan plan_full(const hs2_kv_desc* kv, int Tq, int Hq) {
   FullPlan p{};
   const int G = Hq / kv->Hkv;
@@ -79,7 +84,7 @@ FullPlan plan_full(const hs2_kv_desc* kv, int Tq, int Hq) {
   p.n_tpacks = (int)cdiv(Tq, p.tpack);
   p.rows = p.tpack * G;
   p.units = kv->B * p.n_tpacks * kv->Hkv;
-  const int64_t per_unit = std::max<int64_t>(1, 2048 / p.units);
+  const int64_t per_unit = std::max<int64_t>(1, HS2_SCAN_TARGET_WGS / p.units);
   const int64_t quantum = f32 ? 64 : 256;
   p.split_len = (int)rup(cdiv(kv->N, per_unit), quantum);
   p.nsplit = (int)cdiv(kv->N, p.split_len);
@@ -91,15 +96,17 @@ FullPlan plan_full(const hs2_kv_desc* kv, int Tq, int Hq) {
   off = a256(off + (size_t)p.units * p.nsplit * 16 * kv->D * sizeof(float));
   p.off_lse2 = off;
   off = a256(off + (size_t)p.units * p.rows * sizeof(float));
-  p.off_logits = off;
-  off = a256(off + (size_t)p.units * p.rows * (size_t)p.npad * sizeof(float));
+  p.off_lg16 = off;
+  off = a256(off + (size_t)p.units * p.rows * (size_t)p.npad * sizeof(uint16_t));
+  p.off_lgmax = off;
+  off = a256(off + (size_t)p.units * p.rows * (size_t)(p.npad / 32) * sizeof(float));
   p.total = off;
   return p;
 }
 
 struct SelPlan {
   int units, nchunks, nblocks_max;
-  size_t off_state, off_ha, off_hb, off_cnt, off_bmass, total;
+  size_t off_state, off_hist, off_cnt, off_bmass, total;
 };
 
 SelPlan plan_select(int B, int Tq, int Hkv, int N, int block_size) {
@@ -109,12 +116,10 @@ SelPlan plan_select(int B, int Tq, int Hkv, int N, int block_size) {
   p.nblocks_max = block_size > 1 ? (int)cdiv(N, block_size) : 0;
   size_t off = 0;
   p.off_state = off;
-  off = a256(off + (size_t)p.units * 8 * sizeof(int32_t));
+  off = a256(off + (size_t)p.units * 16 * sizeof(int32_t));
   if (block_size == 1) {
-    p.off_ha = off;
-    off = a256(off + (size_t)p.units * hs2::kHistBins * sizeof(int32_t));
-    p.off_hb = off;
-    off = a256(off + (size_t)p.units * hs2::kHistBins * sizeof(int32_t));
+    p.off_hist = off;
+    off = a256(off + (size_t)p.units * 3 * hs2::kHistBins * sizeof(int32_t));
     p.off_cnt = off;
     off = a256(off + (size_t)p.units * p.nchunks * 2 * sizeof(int32_t));
   } else {
@@ -138,8 +143,8 @@ int hip_fail(hipError_t e, const char* what) {
 // event timing
 // ---------------------------------------------------------------------------
 const char* const kKernelNames[] = {"full_scan",   "combine",     "score",        "select_init",
-                                    "select_hist", "select_find", "select_count", "select_emit",
-                                    "select_block_mass", "select_block_pick", "sparse_gather", "kv_bridge",
+                                    "select_hist", "select_count", "select_emit",
+                                    "select_block_mass", "select_block_pick", "sparse_gather", "kv_bridge", "stream_read",
                                     nullptr};
 
 std::mutex g_tmu;
@@ -246,7 +251,8 @@ int hs2_full_attn_scores(const hs2_kv_desc* kv, const void* q, hs2_dtype q_dtype
   p.split_len = pl.split_len;
   p.part_ml = at<float>(workspace, pl.off_ml);
   p.part_o = at<float>(workspace, pl.off_o);
-  p.logits = at<float>(workspace, pl.off_logits);
+  p.lg16 = at<uint16_t>(workspace, pl.off_lg16);
+  p.lgmax = at<float>(workspace, pl.off_lgmax);
   p.npad = pl.npad;
   hipError_t e = hs2::launch_scan(p, kv->dtype, false, true, stream);
   if (e != hipSuccess) return hip_fail(e, "full_scan launch");
@@ -271,7 +277,8 @@ int hs2_full_attn_scores(const hs2_kv_desc* kv, const void* q, hs2_dtype q_dtype
   if ((e = hs2::launch_combine(c, pl.units, stream)) != hipSuccess) return hip_fail(e, "combine launch");
 
   hs2::ScoreParams s{};
-  s.logits = p.logits;
+  s.lg16 = p.lg16;
+  s.lgmax = p.lgmax;
   s.lse2 = c.lse2;
   s.npad = pl.npad;
   s.rows = pl.rows;
@@ -333,8 +340,7 @@ int hs2_select_topk_window(const float* scores, int32_t B, int32_t Tq, int32_t H
   p.idx = idx;
   p.count = count;
   p.state = at<int32_t>(workspace, pl.off_state);
-  p.hist_a = block_size == 1 ? at<int32_t>(workspace, pl.off_ha) : nullptr;
-  p.hist_b = block_size == 1 ? at<int32_t>(workspace, pl.off_hb) : nullptr;
+  p.hist = block_size == 1 ? at<int32_t>(workspace, pl.off_hist) : nullptr;
   p.cnt = block_size == 1 ? at<int32_t>(workspace, pl.off_cnt) : nullptr;
   p.bmass = block_size > 1 ? at<double>(workspace, pl.off_bmass) : nullptr;
   p.nblocks_max = pl.nblocks_max;
@@ -413,6 +419,14 @@ int hs2_debug_e4m3fn_to_f32(const uint8_t* codes, float* out, int32_t n, hipStre
   if (!codes || !out || n <= 0) return fail(HS2_ERR_INVALID_ARG, "hs2_debug_e4m3fn_to_f32: bad arguments");
   const hipError_t e = hs2::launch_debug_e4m3fn(codes, out, n, stream);
   if (e != hipSuccess) return hip_fail(e, "debug_e4m3fn launch");
+  return HS2_OK;
+}
+
+int hs2_debug_stream_read(const void* buf, size_t bytes, uint32_t* out, int32_t blocks, hipStream_t stream) {
+  if (!buf || !out || bytes < 16 || blocks <= 0 || !al16(buf))
+    return fail(HS2_ERR_INVALID_ARG, "hs2_debug_stream_read: bad arguments");
+  const hipError_t e = hs2::launch_stream_read(buf, bytes, out, blocks, stream);
+  if (e != hipSuccess) return hip_fail(e, "stream_read launch");
   return HS2_OK;
 }
 

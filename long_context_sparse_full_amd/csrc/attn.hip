@@ -29,6 +29,17 @@ typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
+// Compile-time tuning of the full-layer scan (fixed for gfx950; see the design notes).
+#ifndef HS2_SCAN_NT
+#define HS2_SCAN_NT 0  // non-temporal K/V loads in the streaming scan (measured slower on gfx950)
+#endif
+#ifndef HS2_SCAN_INTERLEAVE
+#define HS2_SCAN_INTERLEAVE 1  // split s takes workgroup tiles s, s+nsplit, ... (all splits sweep together)
+#endif
+#ifndef HS2_SCAN_MIN_WAVES
+#define HS2_SCAN_MIN_WAVES 1  // occupancy floor handed to the register allocator
+#endif
+
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLn2 = 0.693147180559945309f;
 
@@ -40,11 +51,10 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
 }
 
 // four E4M3FN codes (bytes 0..3 of w) -> two dwords of bf16 pairs (exact)
+// (one v_cvt_scalef32_pk_bf16_fp8 per pair, scale 1.0: every E4M3FN value is a bf16 value)
 __device__ __forceinline__ void e4m3x4_to_bf16(uint32_t w, uint32_t& lo, uint32_t& hi) {
-  const f32x2_t a = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
-  const f32x2_t b = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
-  lo = pack_bf16(a.x, a.y);
-  hi = pack_bf16(b.x, b.y);
+  lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+  hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
 }
 
 __device__ __forceinline__ f32x4_t mfma_bf16(u32x4_t a, u32x4_t b, f32x4_t c) {
@@ -53,6 +63,17 @@ __device__ __forceinline__ f32x4_t mfma_bf16(u32x4_t a, u32x4_t b, f32x4_t c) {
 }
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// 16-bit code of a log2-domain logit x below its tile maximum m:
+// round((m - x) * 2^12), saturated; 65535 stands for "at least 16 below m" and
+// decodes to a zero contribution.  Step 2^-12 bounds the relative error of
+// 2^x by 2^-13 * ln 2 < 8.5e-5.
+constexpr float kCodeScale = 4096.f;
+constexpr float kCodeInv = 1.f / 4096.f;
+__device__ __forceinline__ uint32_t logit_code(float m, float x) {
+  const float d = (m - x) * kCodeScale;  // >= 0; +inf when x = -inf
+  return d < 65534.5f ? (uint32_t)__builtin_rintf(d) : 65535u;
+}
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
@@ -73,216 +94,204 @@ __device__ __forceinline__ int dmap(int c, int g4) {
 // ---------------------------------------------------------------------------
 // MFMA scan (bf16 query; bf16 or E4M3FN cache)
 // ---------------------------------------------------------------------------
-template <bool FP8, int D, bool GATHER, bool WRITE_LOGITS, int WAVES>
-__global__ void __launch_bounds__(WAVES * 64) scan_mfma(ScanParams P) {
-  constexpr int NC = D / 32;  // QK MFMAs per 16-position half
-  constexpr int VE = D / 16;  // V elements per lane per row = PV MFMA tiles
-  __shared__ float sm_m[WAVES][16];
-  __shared__ float sm_l[WAVES][16];
-  __shared__ float sm_o[WAVES][16][D + 1];
+// Raw (undecoded) K/V bytes of one 32-position tile, as this lane loads them:
+// K rows j0+16*hh+(lane%16) in the MFMA A layout, 16 bytes per load starting at
+// byte 16*g4 (then +64 per further load); V rows j0+16*(kk>>2)+4*g4+(kk&3),
+// VE elements from element VE*(lane%16).
+template <bool FP8, int D>
+struct RawTile {
+  static constexpr int NC = D / 32;
+  static constexpr int VE = D / 16;
+  static constexpr int KW = FP8 ? NC / 2 : NC;      // 16-byte K loads per 16-position half
+  static constexpr int VW = FP8 ? VE / 4 : VE / 2;  // dwords of one V row slice
+  u32x4_t k[2][KW];
+  uint32_t v[8][VW];
+};
 
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int r = lane & 15;   // query row (MFMA N index) / V column group
-  const int g4 = lane >> 4;  // lane group
-  const int unit = blockIdx.y;
-  const int split = blockIdx.x;
-  const int g = unit % P.Hkv;
-  const int tp = (unit / P.Hkv) % P.n_tpacks;
-  const int b = unit / (P.Hkv * P.n_tpacks);
-  const int tl = r / P.G;
-  const int hi = r - tl * P.G;
-  const int t = tp * P.tpack + tl;
-  const bool row_ok = (r < P.rows) && (t < P.Tq);
-  const int h = g * P.G + hi;
-
-  int j_begin, j_end, p_row, p_max;
-  const int32_t* list = nullptr;
-  if constexpr (GATHER) {
-    list = P.idx + (int64_t)unit * P.max_sel;
-    j_begin = 0;
-    j_end = min(max(P.count[unit], 0), P.max_sel);
-    p_row = row_ok ? 0x7fffffff : -1;
-    p_max = j_end - 1;
+template <typename T, bool NT>
+__device__ __forceinline__ T ld(const char* p) {
+  if constexpr (NT) {
+    return __builtin_nontemporal_load((const T*)p);
   } else {
-    const int t_last = min(tp * P.tpack + P.tpack, P.Tq) - 1;
-    p_max = P.q_pos0 + t_last;
-    j_begin = split * P.split_len;
-    j_end = min(j_begin + P.split_len, p_max + 1);
-    p_row = row_ok ? P.q_pos0 + t : -1;
+    return *(const T*)p;
   }
-  const int jlim = min(p_row, j_end - 1);
+}
 
-  // query fragments (MFMA B operand of QK^T): row r, head-dim slice dmap(c, g4)
-  u32x4_t qf[NC];
-  {
-    const uint16_t* qb = (const uint16_t*)P.q + (((int64_t)b * P.Tq + (row_ok ? t : 0)) * P.Hq + (row_ok ? h : 0)) * D;
+template <typename T>
+__device__ __forceinline__ void ldv(uint32_t* dst, const char* p, bool nt) {
+  if constexpr (sizeof(T) == 16) {
+    const u32x4_t w = nt ? ld<u32x4_t, true>(p) : ld<u32x4_t, false>(p);
+    dst[0] = w.x; dst[1] = w.y; dst[2] = w.z; dst[3] = w.w;
+  } else if constexpr (sizeof(T) == 8) {
+    const u32x2_t w = nt ? ld<u32x2_t, true>(p) : ld<u32x2_t, false>(p);
+    dst[0] = w.x; dst[1] = w.y;
+  } else {
+    dst[0] = nt ? ld<uint32_t, true>(p) : ld<uint32_t, false>(p);
+  }
+}
+
+// Loads of one tile from per-lane row addresses: kptr[hh] / vptr[kk] point at
+// this lane's first byte of the row.
+template <bool FP8, int D, bool NT>
+__device__ __forceinline__ void load_tile(RawTile<FP8, D>& R, const char* const kptr[2], const char* const vptr[8]) {
+  using RT = RawTile<FP8, D>;
+  constexpr int VB = RT::VW * 4;  // bytes per V row slice
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      qf[c] = row_ok ? *(const u32x4_t*)(qb + dmap<FP8, D>(c, g4)) : u32x4_t{0u, 0u, 0u, 0u};
+  for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+    for (int c = 0; c < RT::KW; ++c) R.k[hh][c] = ld<u32x4_t, NT>(kptr[hh] + 64 * c);
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) {
+    if constexpr (VB == 16) ldv<u32x4_t>(R.v[kk], vptr[kk], NT);
+    else if constexpr (VB == 8) ldv<u32x2_t>(R.v[kk], vptr[kk], NT);
+    else ldv<uint32_t>(R.v[kk], vptr[kk], NT);
+  }
+}
+
+// Online-softmax state of one wave: row r = lane % 16; the 4 lanes of a row
+// (lane groups g4) agree on m and hold partial sums l and output slices.
+template <int D>
+struct WaveState {
+  float m, l;
+  f32x4_t o[D / 16];
+};
+
+// One 32-position tile: decode, QK^T, mask (only when the tile crosses the
+// causal / range limit), logits, online softmax, PV.  Positions of this lane's
+// logits: j0 + 16*hh + 4*g4 + ii.
+template <bool FP8, int D, bool WRITE_LOGITS>
+__device__ __forceinline__ void compute_tile(const RawTile<FP8, D>& R, const u32x4_t (&qf)[D / 32], float cs, int j0,
+                                             int jlim, bool need_mask, int g4, uint16_t* lg, float* lgm,
+                                             WaveState<D>& S) {
+  constexpr int NC = D / 32, VE = D / 16;
+  u32x4_t kf[2][NC];
+  uint32_t vd[8][VE / 2];
+  if constexpr (!FP8) {
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int c = 0; c < NC; ++c) kf[hh][c] = R.k[hh][c];
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk)
+#pragma unroll
+      for (int w = 0; w < VE / 2; ++w) vd[kk][w] = R.v[kk][w];
+  } else {
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int ii = 0; ii < NC / 2; ++ii) {
+        const u32x4_t raw = R.k[hh][ii];
+        uint32_t a0, a1, a2, a3, b0, b1, b2, b3;
+        e4m3x4_to_bf16(raw.x, a0, a1);
+        e4m3x4_to_bf16(raw.y, a2, a3);
+        e4m3x4_to_bf16(raw.z, b0, b1);
+        e4m3x4_to_bf16(raw.w, b2, b3);
+        kf[hh][2 * ii] = u32x4_t{a0, a1, a2, a3};
+        kf[hh][2 * ii + 1] = u32x4_t{b0, b1, b2, b3};
+      }
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      e4m3x4_to_bf16(R.v[kk][0], vd[kk][0], vd[kk][1]);
+      if constexpr (VE == 8) e4m3x4_to_bf16(R.v[kk][1], vd[kk][2], vd[kk][3]);
     }
   }
-  const int64_t kvoff = (int64_t)b * P.sb + (int64_t)g * P.sh;
-  float cs = P.scale_log2;
-  if constexpr (FP8) cs *= P.k_scale[b * P.Hkv + g];
 
-  float m_run = kNegInf, l_run = 0.f;
-  f32x4_t oacc[VE];
+  // logits S^T[position][row]
+  f32x4_t s[2];
 #pragma unroll
-  for (int dt = 0; dt < VE; ++dt) oacc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  for (int j0 = j_begin + wave * 32; j0 < j_end; j0 += WAVES * 32) {
-    // ---- cache rows touched by this lane
-    int krow[2], vrow[8];
-    if constexpr (GATHER) {
-      const int myrow = min(max(list[min(j0 + (lane & 31), j_end - 1)], 0), P.N - 1);
+  for (int hh = 0; hh < 2; ++hh) {
+    s[hh] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) krow[hh] = __shfl(myrow, 16 * hh + r);
+    for (int c = 0; c < NC; ++c) s[hh] = mfma_bf16(kf[hh][c], qf[c], s[hh]);
+  }
+  float x[2][4];
 #pragma unroll
-      for (int kk = 0; kk < 8; ++kk) vrow[kk] = __shfl(myrow, 16 * (kk >> 2) + 4 * g4 + (kk & 3));
-    } else {
+  for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) krow[hh] = min(j0 + 16 * hh + r, p_max);
+    for (int ii = 0; ii < 4; ++ii) x[hh][ii] = s[hh][ii] * cs;
+  if (need_mask) {
 #pragma unroll
-      for (int kk = 0; kk < 8; ++kk) vrow[kk] = min(j0 + 16 * (kk >> 2) + 4 * g4 + (kk & 3), p_max);
-    }
-
-    // ---- K rows in the MFMA A layout: row = position (lane % 16), 8 head-dim elements
-    u32x4_t kf[2][NC];
-    if constexpr (!FP8) {
-      const uint16_t* kb = (const uint16_t*)P.k + kvoff;
+    for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
+      for (int ii = 0; ii < 4; ++ii)
+        if (j0 + 16 * hh + 4 * g4 + ii > jlim) x[hh][ii] = kNegInf;
+  }
+  float tmax = kNegInf;
 #pragma unroll
-        for (int c = 0; c < NC; ++c)
-          kf[hh][c] = *(const u32x4_t*)(kb + (int64_t)krow[hh] * P.sn + dmap<FP8, D>(c, g4));
-    } else {
-      const uint8_t* kb = (const uint8_t*)P.k + kvoff;
+  for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) tmax = fmaxf(tmax, x[hh][ii]);
+  tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+  tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+  if constexpr (WRITE_LOGITS) {
+    if (lg) {  // lg -> this row's code at position j0 + 4*g4; lgm -> this row's tile maxima
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
-#pragma unroll
-        for (int ii = 0; ii < NC / 2; ++ii) {
-          const u32x4_t raw = *(const u32x4_t*)(kb + (int64_t)krow[hh] * P.sn + 64 * ii + 16 * g4);
-          uint32_t a0, a1, a2, a3, b0, b1, b2, b3;
-          e4m3x4_to_bf16(raw.x, a0, a1);
-          e4m3x4_to_bf16(raw.y, a2, a3);
-          e4m3x4_to_bf16(raw.z, b0, b1);
-          e4m3x4_to_bf16(raw.w, b2, b3);
-          kf[hh][2 * ii] = u32x4_t{a0, a1, a2, a3};
-          kf[hh][2 * ii + 1] = u32x4_t{b0, b1, b2, b3};
-        }
+        const uint32_t c0 = logit_code(tmax, x[hh][0]), c1 = logit_code(tmax, x[hh][1]);
+        const uint32_t c2 = logit_code(tmax, x[hh][2]), c3 = logit_code(tmax, x[hh][3]);
+        *(u32x2_t*)(lg + 16 * hh) = u32x2_t{c0 | (c1 << 16), c2 | (c3 << 16)};
       }
-    }
-
-    // ---- V rows: lane holds VE consecutive head-dim elements (VE*r ..) of 8 rows
-    uint32_t vd[8][VE / 2];
-    if constexpr (!FP8) {
-      const uint16_t* vb = (const uint16_t*)P.v + kvoff + VE * r;
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
-        if constexpr (VE == 8) {
-          const u32x4_t w = *(const u32x4_t*)(vb + (int64_t)vrow[kk] * P.sn);
-          vd[kk][0] = w.x; vd[kk][1] = w.y; vd[kk][2] = w.z; vd[kk][3] = w.w;
-        } else {
-          const u32x2_t w = *(const u32x2_t*)(vb + (int64_t)vrow[kk] * P.sn);
-          vd[kk][0] = w.x; vd[kk][1] = w.y;
-        }
-      }
-    } else {
-      const uint8_t* vb = (const uint8_t*)P.v + kvoff + VE * r;
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
-        if constexpr (VE == 8) {
-          const u32x2_t w = *(const u32x2_t*)(vb + (int64_t)vrow[kk] * P.sn);
-          e4m3x4_to_bf16(w.x, vd[kk][0], vd[kk][1]);
-          e4m3x4_to_bf16(w.y, vd[kk][2], vd[kk][3]);
-        } else {
-          const uint32_t w = *(const uint32_t*)(vb + (int64_t)vrow[kk] * P.sn);
-          e4m3x4_to_bf16(w, vd[kk][0], vd[kk][1]);
-        }
-      }
-    }
-
-    // ---- logits S^T[position][row]: lane holds row r at positions j0+16hh+4g4+ii
-    f32x4_t s[2];
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      s[hh] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int c = 0; c < NC; ++c) s[hh] = mfma_bf16(kf[hh][c], qf[c], s[hh]);
-    }
-    float x[2][4];
-    float tmax = kNegInf;
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        const int j = j0 + 16 * hh + 4 * g4 + ii;
-        const float xv = (j <= jlim) ? s[hh][ii] * cs : kNegInf;
-        x[hh][ii] = xv;
-        tmax = fmaxf(tmax, xv);
-      }
-    if constexpr (WRITE_LOGITS) {
-      if (row_ok) {
-        float* lg = P.logits + ((int64_t)unit * P.rows + r) * P.npad + j0 + 4 * g4;
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-          *(f32x4_t*)(lg + 16 * hh) = f32x4_t{x[hh][0], x[hh][1], x[hh][2], x[hh][3]};
-      }
-    }
-
-    // ---- online softmax (log2 domain); the 4 lanes of one row agree on m
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    const float m_new = fmaxf(m_run, tmax);
-    const float alpha = (m_new == m_run) ? 1.f : exp2_fast(m_run - m_new);
-    const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-    float pr[2][4];
-    float psum = 0.f;
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        pr[hh][ii] = exp2_fast(x[hh][ii] - m_use);
-        psum += pr[hh][ii];
-      }
-    l_run = l_run * alpha + psum;
-    if (__any(alpha != 1.f)) {
-#pragma unroll
-      for (int dt = 0; dt < VE; ++dt) oacc[dt] *= alpha;
-    }
-    m_run = m_new;
-
-    // ---- PV: O^T[d][row] += V^T[d][pos] P^T[pos][row]
-    // P^T operand: k-slot kk of lane group g4 <-> position 16*(kk>>2) + 4*g4 + (kk&3)
-    const u32x4_t pf = u32x4_t{pack_bf16(pr[0][0], pr[0][1]), pack_bf16(pr[0][2], pr[0][3]),
-                               pack_bf16(pr[1][0], pr[1][1]), pack_bf16(pr[1][2], pr[1][3])};
-#pragma unroll
-    for (int dt = 0; dt < VE; ++dt) {
-      const int w = dt >> 1;
-      u32x4_t va;
-#pragma unroll
-      for (int q2 = 0; q2 < 4; ++q2) {
-        const uint32_t e0 = vd[2 * q2][w], e1 = vd[2 * q2 + 1][w];
-        va[q2] = (dt & 1) ? ((e0 >> 16) | (e1 & 0xffff0000u)) : ((e0 & 0xffffu) | (e1 << 16));
-      }
-      oacc[dt] = mfma_bf16(va, pf, oacc[dt]);
+      if (g4 == 0) lgm[j0 >> 5] = tmax;
     }
   }
 
-  // ---- merge the waves of this workgroup
+  // online softmax in the log2 domain
+  const float m_new = fmaxf(S.m, tmax);
+  const float alpha = (m_new == S.m) ? 1.f : exp2_fast(S.m - m_new);
+  const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+  float pr[2][4];
+  float psum = 0.f;
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      pr[hh][ii] = exp2_fast(x[hh][ii] - m_use);
+      psum += pr[hh][ii];
+    }
+  S.l = S.l * alpha + psum;
+  if (__any(alpha != 1.f)) {
+#pragma unroll
+    for (int dt = 0; dt < VE; ++dt) S.o[dt] *= alpha;
+  }
+  S.m = m_new;
+
+  // PV: O^T[d][row] += V^T[d][pos] P^T[pos][row]; k-slot kk of lane group g4
+  // is position 16*(kk>>2) + 4*g4 + (kk&3), for P and V alike
+  const u32x4_t pf = u32x4_t{pack_bf16(pr[0][0], pr[0][1]), pack_bf16(pr[0][2], pr[0][3]),
+                             pack_bf16(pr[1][0], pr[1][1]), pack_bf16(pr[1][2], pr[1][3])};
+#pragma unroll
+  for (int dt = 0; dt < VE; ++dt) {
+    const int w = dt >> 1;
+    u32x4_t va;
+#pragma unroll
+    for (int q2 = 0; q2 < 4; ++q2) {
+      const uint32_t e0 = vd[2 * q2][w], e1 = vd[2 * q2 + 1][w];
+      va[q2] = (dt & 1) ? __builtin_amdgcn_perm(e1, e0, 0x07060302u) : __builtin_amdgcn_perm(e1, e0, 0x05040100u);
+    }
+    S.o[dt] = mfma_bf16(va, pf, S.o[dt]);
+  }
+}
+
+// Merge the waves of a workgroup through LDS and emit, per row, either the
+// split partial (max, sum, output) or the final normalised output and LSE.
+template <bool FP8, int D, bool GATHER, int WAVES>
+__device__ __forceinline__ void merge_and_store(const ScanParams& P, WaveState<D>& S, int unit, int split, int b, int g,
+                                                int wave, int r, int g4, float (*sm_m)[16], float (*sm_l)[16],
+                                                float (*sm_o)[16][D + 1]) {
+  constexpr int VE = D / 16;
+  float l_run = S.l;
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
+  __syncthreads();
   if (g4 == 0) {
-    sm_m[wave][r] = m_run;
+    sm_m[wave][r] = S.m;
     sm_l[wave][r] = l_run;
   }
 #pragma unroll
   for (int dt = 0; dt < VE; ++dt)
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii) sm_o[wave][r][VE * (4 * g4 + ii) + dt] = oacc[dt][ii];
+    for (int ii = 0; ii < 4; ++ii) sm_o[wave][r][VE * (4 * g4 + ii) + dt] = S.o[dt][ii];
   __syncthreads();
-
   for (int e = threadIdx.x; e < P.rows * D; e += WAVES * 64) {
     const int rr = e / D, d = e - rr * D;
     float M = kNegInf;
@@ -297,8 +306,7 @@ __global__ void __launch_bounds__(WAVES * 64) scan_mfma(ScanParams P) {
       O += sm_o[w][rr][d] * f;
     }
     if constexpr (GATHER) {
-      // unit = (b, t, g); rows = G heads of token t
-      const int tt = (unit / P.Hkv) % P.Tq;
+      const int tt = (unit / P.Hkv) % P.Tq;  // unit = (b, t, g); rows = heads of token t
       const int hh = g * P.G + rr;
       float o = (L > 0.f) ? O / L : 0.f;
       if constexpr (FP8) o *= P.v_scale[b * P.Hkv + g];
@@ -314,6 +322,201 @@ __global__ void __launch_bounds__(WAVES * 64) scan_mfma(ScanParams P) {
       }
     }
   }
+}
+
+// Query fragments (MFMA B operand of QK^T): row r, head-dim slice dmap(c, g4).
+template <bool FP8, int D>
+__device__ __forceinline__ void load_q(u32x4_t (&qf)[D / 32], const ScanParams& P, int b, int t, int h, bool row_ok,
+                                       int g4) {
+  const uint16_t* qb = (const uint16_t*)P.q + (((int64_t)b * P.Tq + (row_ok ? t : 0)) * P.Hq + (row_ok ? h : 0)) * D;
+#pragma unroll
+  for (int c = 0; c < D / 32; ++c) qf[c] = row_ok ? *(const u32x4_t*)(qb + dmap<FP8, D>(c, g4)) : u32x4_t{0u, 0u, 0u, 0u};
+}
+
+// Full layer: one workgroup per (position split, unit); waves take interleaved
+// 32-position tiles and prefetch the next tile while computing this one.
+// Tile bases are wave-uniform (scalar registers); each lane adds a fixed
+// 32-bit offset, so interior tiles need no per-lane address arithmetic.
+template <bool FP8, int D, bool WRITE_LOGITS, int WAVES>
+__global__ void __launch_bounds__(WAVES * 64, HS2_SCAN_MIN_WAVES) scan_full(ScanParams P) {
+  constexpr int VE = D / 16, NC = D / 32, EB = FP8 ? 1 : 2;
+  constexpr int STEP = WAVES * 32;
+  __shared__ float sm_m[WAVES][16];
+  __shared__ float sm_l[WAVES][16];
+  __shared__ float sm_o[WAVES][16][D + 1];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane & 15, g4 = lane >> 4;
+  const int unit = blockIdx.y, split = blockIdx.x;
+  const int g = unit % P.Hkv;
+  const int tp = (unit / P.Hkv) % P.n_tpacks;
+  const int b = unit / (P.Hkv * P.n_tpacks);
+  const int tl = r / P.G;
+  const int t = tp * P.tpack + tl;
+  const bool row_ok = (r < P.rows) && (t < P.Tq);
+  const int h = g * P.G + (r - tl * P.G);
+
+  const int p_max = P.q_pos0 + min(tp * P.tpack + P.tpack, P.Tq) - 1;
+#if HS2_SCAN_INTERLEAVE
+  // workgroup tile w = STEP positions; this split owns tiles split, split+nsplit, ...
+  const int j_begin = split * STEP;
+  const int j_end = p_max + 1;
+  const int jstride = P.nsplit * STEP;
+#else
+  const int j_begin = split * P.split_len;
+  const int j_end = min(j_begin + P.split_len, p_max + 1);
+  const int jstride = STEP;
+#endif
+  const int jlim = min(row_ok ? P.q_pos0 + t : -1, j_end - 1);
+  // tiles ending at or before j_nomask need no masking for any valid row
+  const int j_nomask = min(P.q_pos0 + tp * P.tpack, j_end - 1);
+
+  u32x4_t qf[NC];
+  load_q<FP8, D>(qf, P, b, t, h, row_ok, g4);
+  const int64_t kvoff = ((int64_t)b * P.sb + (int64_t)g * P.sh) * EB;
+  const char* kb = (const char*)P.k + kvoff;
+  const char* vb = (const char*)P.v + kvoff;
+  const int64_t snb = P.sn * EB;
+  float cs = P.scale_log2;
+  if constexpr (FP8) cs *= P.k_scale[b * P.Hkv + g];
+  uint16_t* lg_row = nullptr;
+  float* lgm_row = nullptr;
+  if constexpr (WRITE_LOGITS) {
+    if (row_ok) {
+      lg_row = P.lg16 + ((int64_t)unit * P.rows + r) * P.npad + 4 * g4;
+      lgm_row = P.lgmax + ((int64_t)unit * P.rows + r) * (P.npad >> 5);
+    }
+  }
+
+  // per-lane offsets (bytes) of this lane's K and V rows relative to the tile base
+  uint32_t koff[2], voff[8];
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) koff[hh] = (uint32_t)((16 * hh + r) * snb) + 16u * g4;
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk)
+    voff[kk] = (uint32_t)((16 * (kk >> 2) + 4 * g4 + (kk & 3)) * snb) + (uint32_t)(VE * r * EB);
+
+  WaveState<D> S;
+  S.m = kNegInf;
+  S.l = 0.f;
+#pragma unroll
+  for (int dt = 0; dt < VE; ++dt) S.o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  auto load = [&](RawTile<FP8, D>& R, int j0) {
+    const char* kp[2];
+    const char* vp[8];
+    if (j0 + 31 <= p_max) {
+      const char* tk = kb + (int64_t)j0 * snb;
+      const char* tv = vb + (int64_t)j0 * snb;
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) kp[hh] = tk + koff[hh];
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) vp[kk] = tv + voff[kk];
+    } else {  // tail tile: rows past the last position repeat it
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) kp[hh] = kb + (int64_t)min(j0 + 16 * hh + r, p_max) * snb + 16 * g4;
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk)
+        vp[kk] = vb + (int64_t)min(j0 + 16 * (kk >> 2) + 4 * g4 + (kk & 3), p_max) * snb + VE * r * EB;
+    }
+    load_tile<FP8, D, HS2_SCAN_NT != 0>(R, kp, vp);
+  };
+  auto compute = [&](const RawTile<FP8, D>& R, int j0) {
+    compute_tile<FP8, D, WRITE_LOGITS>(R, qf, cs, j0, jlim, j0 + 31 > j_nomask, g4,
+                                       WRITE_LOGITS && lg_row ? lg_row + j0 : nullptr, lgm_row, S);
+  };
+
+  RawTile<FP8, D> A, B;
+  int j0 = j_begin + wave * 32;
+  if (j0 < j_end) load(A, j0);
+  while (j0 < j_end) {  // ping-pong: load tile n+1 while computing tile n
+    const int j1 = j0 + jstride;
+    if (j1 < j_end) load(B, j1);
+    compute(A, j0);
+    if (j1 >= j_end) break;
+    const int j2 = j1 + jstride;
+    if (j2 < j_end) load(A, j2);
+    compute(B, j1);
+    j0 = j2;
+  }
+  merge_and_store<FP8, D, false, WAVES>(P, S, unit, split, b, g, wave, r, g4, sm_m, sm_l, sm_o);
+}
+
+constexpr int kGatherIdxCap = 2048;  // index-list entries staged in LDS at a time
+
+// Sparse layer: one workgroup per (b, t, g) over its whole index list (staged
+// in LDS), final output written directly.
+template <bool FP8, int D, int WAVES>
+__global__ void __launch_bounds__(WAVES * 64) scan_gather(ScanParams P) {
+  constexpr int VE = D / 16, NC = D / 32, EB = FP8 ? 1 : 2;
+  constexpr int STEP = WAVES * 32;
+  __shared__ float sm_m[WAVES][16];
+  __shared__ float sm_l[WAVES][16];
+  __shared__ float sm_o[WAVES][16][D + 1];
+  __shared__ int s_idx[kGatherIdxCap];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane & 15, g4 = lane >> 4;
+  const int unit = blockIdx.y;  // (b, t, g)
+  const int g = unit % P.Hkv;
+  const int t = (unit / P.Hkv) % P.Tq;
+  const int b = unit / (P.Hkv * P.Tq);
+  const bool row_ok = r < P.G;
+  const int h = g * P.G + r;
+  const int32_t* list = P.idx + (int64_t)unit * P.max_sel;
+  const int n = min(max(P.count[unit], 0), P.max_sel);
+
+  u32x4_t qf[NC];
+  load_q<FP8, D>(qf, P, b, t, h, row_ok, g4);
+  const int64_t kvoff = ((int64_t)b * P.sb + (int64_t)g * P.sh) * EB;
+  const char* kb = (const char*)P.k + kvoff + 16 * g4;
+  const char* vb = (const char*)P.v + kvoff + VE * r * EB;
+  const int64_t snb = P.sn * EB;
+  float cs = P.scale_log2;
+  if constexpr (FP8) cs *= P.k_scale[b * P.Hkv + g];
+
+  WaveState<D> S;
+  S.m = kNegInf;
+  S.l = 0.f;
+#pragma unroll
+  for (int dt = 0; dt < VE; ++dt) S.o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  for (int base = 0; base < n; base += kGatherIdxCap) {
+    const int nb = min(kGatherIdxCap, n - base);
+    __syncthreads();
+    for (int i = threadIdx.x; i < nb; i += WAVES * 64) s_idx[i] = min(max(list[base + i], 0), P.N - 1);
+    __syncthreads();
+    const int jl = base + nb - 1;
+    auto load = [&](RawTile<FP8, D>& R, int j0) {
+      const char* kp[2];
+      const char* vp[8];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) kp[hh] = kb + (int64_t)s_idx[min(j0 - base + 16 * hh + r, nb - 1)] * snb;
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk)
+        vp[kk] = vb + (int64_t)s_idx[min(j0 - base + 16 * (kk >> 2) + 4 * g4 + (kk & 3), nb - 1)] * snb;
+      load_tile<FP8, D, false>(R, kp, vp);
+    };
+    auto compute = [&](const RawTile<FP8, D>& R, int j0) {
+      compute_tile<FP8, D, false>(R, qf, cs, j0, jl, j0 + 31 > jl, g4, nullptr, nullptr, S);
+    };
+    RawTile<FP8, D> A, B;
+    int j0 = base + wave * 32;
+    if (j0 < base + nb) load(A, j0);
+    while (j0 < base + nb) {
+      const int j1 = j0 + STEP;
+      if (j1 < base + nb) load(B, j1);
+      compute(A, j0);
+      if (j1 >= base + nb) break;
+      const int j2 = j1 + STEP;
+      if (j2 < base + nb) load(A, j2);
+      compute(B, j1);
+      j0 = j2;
+    }
+  }
+  merge_and_store<FP8, D, true, WAVES>(P, S, unit, 0, b, g, wave, r, g4, sm_m, sm_l, sm_o);
 }
 
 // ---------------------------------------------------------------------------
@@ -386,11 +589,23 @@ __global__ void __launch_bounds__(256) scan_f32(ScanParams P) {
       tmax = fmaxf(tmax, x[s]);
     }
     if constexpr (WRITE_LOGITS) {
+      // per aligned 32-position half: positions c, c+16 (half 0) and c+32, c+48 (half 1)
+      float hm0 = fmaxf(x[0], x[1]), hm1 = fmaxf(x[2], x[3]);
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) {
+        hm0 = fmaxf(hm0, __shfl_xor(hm0, o));
+        hm1 = fmaxf(hm1, __shfl_xor(hm1, o));
+      }
       if (r < R) {
-        float* lg = P.logits + ((int64_t)unit * P.rows + r) * P.npad + j0;
+        uint16_t* lg = P.lg16 + ((int64_t)unit * P.rows + r) * P.npad + j0;
+        float* lgm = P.lgmax + ((int64_t)unit * P.rows + r) * (P.npad >> 5) + (j0 >> 5);
 #pragma unroll
         for (int s = 0; s < 4; ++s)
-          if (c + 16 * s < nt) lg[c + 16 * s] = x[s];
+          if (c + 16 * s < nt) lg[c + 16 * s] = (uint16_t)logit_code(s < 2 ? hm0 : hm1, x[s]);
+        if (c == 0) {
+          lgm[0] = hm0;
+          if (nt > 32) lgm[1] = hm1;
+        }
       }
     }
 #pragma unroll
@@ -451,8 +666,32 @@ __global__ void __launch_bounds__(256) scan_f32(ScanParams P) {
 // ---------------------------------------------------------------------------
 // combine split partials -> output, LSE (natural) and log2 LSE for scores
 // ---------------------------------------------------------------------------
-__global__ void combine(CombineParams P) {
-  const int unit = blockIdx.x, r = blockIdx.y, d = threadIdx.x;
+constexpr int kMaxSplits = 2048;
+
+__device__ __forceinline__ float block_reduce_256(float v, float* red, bool is_max) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float y = __shfl_xor(v, o);
+    v = is_max ? fmaxf(v, y) : v + y;
+  }
+  __syncthreads();
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  float t = red[0];
+#pragma unroll
+  for (int w = 1; w < 4; ++w) t = is_max ? fmaxf(t, red[w]) : t + red[w];
+  return t;
+}
+
+// grid (unit, row, head-dim chunk of 32): every workgroup recomputes the split
+// weights 2^(m_s - M) into LDS, then 8 groups of 32 threads sum interleaved
+// splits with 4 independent accumulators each (many loads in flight).
+__global__ void __launch_bounds__(256) combine(CombineParams P) {
+  __shared__ float sw[kMaxSplits];
+  __shared__ float red[8];
+  __shared__ float part[256];
+  const int unit = blockIdx.x, r = blockIdx.y, tid = threadIdx.x;
   const int g = unit % P.Hkv;
   const int tp = (unit / P.Hkv) % P.n_tpacks;
   const int b = unit / (P.Hkv * P.n_tpacks);
@@ -461,16 +700,36 @@ __global__ void combine(CombineParams P) {
   if (t >= P.Tq) return;
   const int h = g * P.G + i;
   const float* ml = P.part_ml + ((int64_t)unit * P.nsplit * 16 + r) * 2;
-  const float* po = P.part_o + ((int64_t)unit * P.nsplit * 16 + r) * P.D + d;
-  float M = kNegInf;
-  for (int s = 0; s < P.nsplit; ++s) M = fmaxf(M, ml[s * 32]);
+  float m = kNegInf;
+  for (int s = tid; s < P.nsplit; s += 256) m = fmaxf(m, ml[s * 32]);
+  const float M = block_reduce_256(m, red, true);
   const float Ms = (M == kNegInf) ? 0.f : M;
-  float L = 0.f, O = 0.f;
-  for (int s = 0; s < P.nsplit; ++s) {
-    const float f = exp2f(ml[s * 32] - Ms);
-    L += ml[s * 32 + 1] * f;
-    O += po[(int64_t)s * 16 * P.D] * f;
+  float l = 0.f;
+  for (int s = tid; s < P.nsplit; s += 256) {
+    const float w = exp2f(ml[s * 32] - Ms);
+    sw[s] = w;
+    l += ml[s * 32 + 1] * w;
   }
+  const float L = block_reduce_256(l, red, false);  // its barriers also publish sw
+  const int dl = tid & 31, pp = tid >> 5;
+  const int d = blockIdx.z * 32 + dl;
+  const float* po = P.part_o + ((int64_t)unit * P.nsplit * 16 + r) * P.D + d;
+  const int64_t sstride = (int64_t)16 * P.D;
+  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+  int s = pp;
+  for (; s + 24 < P.nsplit; s += 32) {
+    a0 += sw[s] * po[s * sstride];
+    a1 += sw[s + 8] * po[(s + 8) * sstride];
+    a2 += sw[s + 16] * po[(s + 16) * sstride];
+    a3 += sw[s + 24] * po[(s + 24) * sstride];
+  }
+  for (; s < P.nsplit; s += 8) a0 += sw[s] * po[s * sstride];
+  part[tid] = (a0 + a1) + (a2 + a3);
+  __syncthreads();
+  if (pp != 0) return;
+  float O = 0.f;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) O += part[q * 32 + dl];
   float o = (L > 0.f) ? O / L : 0.f;
   if (P.v_scale) o *= P.v_scale[b * P.Hkv + g];
   const int64_t orow = ((int64_t)b * P.Tq + t) * P.Hq + h;
@@ -502,11 +761,13 @@ __global__ void __launch_bounds__(256) score(ScoreParams P) {
     float s[4] = {0.f, 0.f, 0.f, 0.f};
     if (j4 <= p) {
       for (int i = 0; i < P.G; ++i) {
-        const int r = tl * P.G + i;
-        const float l2 = P.lse2[(int64_t)unit * P.rows + r];
-        const f32x4_t x = *(const f32x4_t*)(P.logits + ((int64_t)unit * P.rows + r) * P.npad + j4);
+        const int64_t row = (int64_t)unit * P.rows + tl * P.G + i;
+        const float c = P.lgmax[row * (P.npad >> 5) + (j4 >> 5)] - P.lse2[row];
+        const u32x2_t w = *(const u32x2_t*)(P.lg16 + row * P.npad + j4);
+        const uint32_t code[4] = {w.x & 0xffffu, w.x >> 16, w.y & 0xffffu, w.y >> 16};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) s[e] += exp2f(x[e] - l2);
+        for (int e = 0; e < 4; ++e)
+          s[e] += (code[e] == 65535u) ? 0.f : exp2f(c - (float)code[e] * kCodeInv);
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e)
@@ -521,6 +782,21 @@ __global__ void __launch_bounds__(256) score(ScoreParams P) {
   }
 }
 
+// Streaming-read probe: every byte of buf read once with 16-byte non-temporal
+// loads, grid-stride; one xor word per thread (out: blocks*256 words).
+__global__ void __launch_bounds__(256) stream_read(const u32x4_t* __restrict__ buf, int64_t n16, uint32_t* out) {
+  uint32_t acc = 0;
+  const int64_t stride = (int64_t)gridDim.x * 256 * 4;
+  for (int64_t i = (int64_t)blockIdx.x * 1024 + threadIdx.x; i < n16; i += stride) {
+    u32x4_t v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = (i + 256 * u < n16) ? __builtin_nontemporal_load(buf + i + 256 * u) : u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  out[(int64_t)blockIdx.x * 256 + threadIdx.x] = acc;
+}
+
 __global__ void debug_e4m3fn(const uint8_t* codes, float* out, int n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i * 4 >= n) return;
@@ -533,10 +809,17 @@ __global__ void debug_e4m3fn(const uint8_t* codes, float* out, int n) {
   for (int e = 0; e < 4 && i * 4 + e < n; ++e) out[i * 4 + e] = v[e];
 }
 
-template <bool FP8, int D, bool GATHER, bool WL, int WAVES>
-hipError_t go_mfma(const ScanParams& p, dim3 grid, hipStream_t s, const char* name) {
-  TimedLaunch tl(name, s);
-  hipLaunchKernelGGL((scan_mfma<FP8, D, GATHER, WL, WAVES>), grid, dim3(WAVES * 64), 0, s, p);
+template <bool FP8, int D, bool WL, int WAVES>
+hipError_t go_full(const ScanParams& p, dim3 grid, hipStream_t s) {
+  TimedLaunch tl("full_scan", s);
+  hipLaunchKernelGGL((scan_full<FP8, D, WL, WAVES>), grid, dim3(WAVES * 64), 0, s, p);
+  return hipGetLastError();
+}
+
+template <bool FP8, int D, int WAVES>
+hipError_t go_gather(const ScanParams& p, dim3 grid, hipStream_t s) {
+  TimedLaunch tl("sparse_gather", s);
+  hipLaunchKernelGGL((scan_gather<FP8, D, WAVES>), grid, dim3(WAVES * 64), 0, s, p);
   return hipGetLastError();
 }
 
@@ -549,7 +832,10 @@ hipError_t go_f32(const ScanParams& p, dim3 grid, hipStream_t s, const char* nam
 
 }  // namespace
 
-constexpr int kScanWaves = 4;
+#ifndef HS2_SCAN_WAVES
+#define HS2_SCAN_WAVES 4
+#endif
+constexpr int kScanWaves = HS2_SCAN_WAVES;
 constexpr int kGatherWaves = 8;
 
 hipError_t launch_scan(const ScanParams& p, int kv_dtype, bool gather, bool write_logits, hipStream_t s) {
@@ -565,11 +851,11 @@ hipError_t launch_scan(const ScanParams& p, int kv_dtype, bool gather, bool writ
     return write_logits ? go_f32<64, false, true>(p, grid, s, name) : go_f32<64, false, false>(p, grid, s, name);
   }
   const bool fp8 = kv_dtype == HS2_FP8_E4M3FN;
-#define HS2_GO(F8, DD)                                                                         \
-  do {                                                                                         \
-    if (gather) return go_mfma<F8, DD, true, false, kGatherWaves>(p, grid, s, name);           \
-    if (write_logits) return go_mfma<F8, DD, false, true, kScanWaves>(p, grid, s, name);       \
-    return go_mfma<F8, DD, false, false, kScanWaves>(p, grid, s, name);                        \
+#define HS2_GO(F8, DD)                                                                  \
+  do {                                                                                  \
+    if (gather) return go_gather<F8, DD, kGatherWaves>(p, grid, s);                     \
+    if (write_logits) return go_full<F8, DD, true, kScanWaves>(p, grid, s);             \
+    return go_full<F8, DD, false, kScanWaves>(p, grid, s);                              \
   } while (0)
   if (fp8) {
     if (p.D == 128) HS2_GO(true, 128);
@@ -582,7 +868,7 @@ hipError_t launch_scan(const ScanParams& p, int kv_dtype, bool gather, bool writ
 
 hipError_t launch_combine(const CombineParams& p, int units, hipStream_t s) {
   TimedLaunch tl("combine", s);
-  hipLaunchKernelGGL(combine, dim3(units, p.rows), dim3(p.D), 0, s, p);
+  hipLaunchKernelGGL(combine, dim3(units, p.rows, p.D / 32), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
@@ -590,6 +876,12 @@ hipError_t launch_score(const ScoreParams& p, int units, hipStream_t s) {
   TimedLaunch tl("score", s);
   const int blocks = (p.N + 1023) / 1024;
   hipLaunchKernelGGL(score, dim3(blocks, units), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* out, int blocks, hipStream_t s) {
+  TimedLaunch tl("stream_read", s);
+  hipLaunchKernelGGL(stream_read, dim3(blocks), dim3(256), 0, s, (const u32x4_t*)buf, (int64_t)(bytes / 16), out);
   return hipGetLastError();
 }
 

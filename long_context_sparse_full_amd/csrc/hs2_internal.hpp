@@ -31,7 +31,10 @@ struct ScanParams {
   int split_len;     // positions per split (multiple of 256)
   float* part_ml;    // [units][nsplit][16][2]   (max, sum) in log2 units
   float* part_o;     // [units][nsplit][16][D]   unnormalised output
-  float* logits;     // [units][rows][npad]      log2-domain logits (may be null)
+  // per-head logits for the score pass, 16-bit log-domain code relative to the
+  // row's maximum over each aligned 32-position tile (see the score kernel)
+  uint16_t* lg16;    // [units][rows][npad]  code = round((tile max - x) * 4096), 65535 = below range
+  float* lgmax;      // [units][rows][npad/32] tile maxima (log2 domain)
   int64_t npad;
   // gather (sparse layer) mode: one unit per (b, t, g), tpack = 1
   const int32_t* idx;
@@ -53,7 +56,8 @@ struct CombineParams {
 };
 
 struct ScoreParams {
-  const float* logits;
+  const uint16_t* lg16;
+  const float* lgmax;
   const float* lse2;
   int64_t npad;
   int rows, tpack, n_tpacks, G, Hkv, Tq, N, q_pos0;
@@ -63,7 +67,7 @@ struct ScoreParams {
 // ---------------------------------------------------------------------------
 // selection
 // ---------------------------------------------------------------------------
-constexpr int kSelChunk = 4096;  // candidates per workgroup in the select passes
+constexpr int kSelChunk = 16384;  // candidates per workgroup in the select passes
 constexpr int kHistBins = 4096;  // 12-bit digits
 
 struct SelectParams {
@@ -71,9 +75,8 @@ struct SelectParams {
   int units, Tq, Hkv, N, q_pos0, k, window, block_size, max_sel, nchunks;
   int32_t* idx;
   int32_t* count;
-  int32_t* state;   // [units][8]
-  int32_t* hist_a;  // [units][4096]
-  int32_t* hist_b;  // [units][4096]
+  int32_t* state;   // [units][16]
+  int32_t* hist;    // [units][3][4096] digit histograms of the three passes
   int32_t* cnt;     // [units][nchunks][2]
   double* bmass;    // [units][nblocks_max] (block mode)
   int nblocks_max;
@@ -87,6 +90,7 @@ hipError_t launch_select(const SelectParams& p, hipStream_t s);
 hipError_t launch_bridge(const uint16_t* hidden, int T, int dm, const uint16_t* w, int Hkv, int D,
                          uint16_t* k_out, uint16_t* v_out, int64_t sn, int64_t sh, hipStream_t s);
 hipError_t launch_debug_e4m3fn(const uint8_t* codes, float* out, int n, hipStream_t s);
+hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* out, int blocks, hipStream_t s);
 
 // timing hooks used by the launchers
 struct TimedLaunch {

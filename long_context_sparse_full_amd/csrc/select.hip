@@ -23,7 +23,10 @@
 namespace hs2 {
 namespace {
 
-enum { ST_MODE = 0, ST_PREFIX = 1, ST_NEED = 2, ST_NCAND = 3, ST_TAKE = 4, ST_P = 5 };
+// per-unit state; each pass reads the slots of the previous kernel and writes
+// its own, so no kernel reads a slot that a sibling workgroup is writing
+enum { ST_MODE = 0, ST_NCAND = 1, ST_TAKE = 2, ST_P = 3, ST_PREFIX1 = 4, ST_NEED1 = 5,
+       ST_PREFIX2 = 6, ST_NEED2 = 7, ST_TAU = 8, ST_NEED3 = 9, ST_WORDS = 16 };
 enum { MODE_RADIX = 0, MODE_ALL = 1, MODE_NONE = 2 };
 
 __device__ __forceinline__ uint32_t score_key(float s) {
@@ -68,66 +71,34 @@ __global__ void __launch_bounds__(256) sel_init(SelectParams P) {
     take = min(P.k, nb);
   }
   if (threadIdx.x == 0) {
-    int32_t* st = P.state + (int64_t)u * 8;
+    int32_t* st = P.state + (int64_t)u * ST_WORDS;
     st[ST_MODE] = (take == 0) ? MODE_NONE : ((P.block_size == 1 && take == ncand) ? MODE_ALL : MODE_RADIX);
-    st[ST_PREFIX] = 0;
-    st[ST_NEED] = take;
     st[ST_NCAND] = ncand;
     st[ST_TAKE] = take;
     st[ST_P] = p;
   }
   if (P.block_size == 1) {
-    int32_t* ha = P.hist_a + (int64_t)u * kHistBins;
-    int32_t* hb = P.hist_b + (int64_t)u * kHistBins;
-    for (int i = threadIdx.x; i < kHistBins; i += 256) {
-      ha[i] = 0;
-      hb[i] = 0;
-    }
+    int32_t* h = P.hist + (int64_t)u * 3 * kHistBins;
+    for (int i = threadIdx.x; i < 3 * kHistBins; i += 256) h[i] = 0;
   }
 }
 
-// PASS 0: bits 31..20, PASS 1: bits 19..8 (keys matching bits 31..20),
-// PASS 2: bits 7..0 (keys matching bits 31..8)
+// digits: pass 0 = bits 31..20, pass 1 = bits 19..8, pass 2 = bits 7..0
 template <int PASS>
-__global__ void __launch_bounds__(256) sel_hist(SelectParams P) {
-  constexpr int SHIFT = PASS == 0 ? 20 : (PASS == 1 ? 8 : 0);
-  constexpr int BINS = PASS == 2 ? 256 : 4096;
-  constexpr uint32_t MATCH = PASS == 0 ? 0u : (PASS == 1 ? 0xFFF00000u : 0xFFFFFF00u);
-  __shared__ int32_t h[BINS];
-  const int u = blockIdx.y, chunk = blockIdx.x;
-  const int32_t* st = P.state + (int64_t)u * 8;
-  if (st[ST_MODE] != MODE_RADIX) return;
-  const int ncand = st[ST_NCAND];
-  const int base = chunk * kSelChunk;
-  if (base >= ncand) return;
-  const int end = min(base + kSelChunk, ncand);
-  const uint32_t prefix = (uint32_t)st[ST_PREFIX];
-  for (int i = threadIdx.x; i < BINS; i += 256) h[i] = 0;
-  __syncthreads();
-  const float* s = P.scores + (int64_t)u * P.N;
-  for (int j = base + threadIdx.x; j < end; j += 256) {
-    const uint32_t key = score_key(s[j]);
-    if ((key & MATCH) == prefix) atomicAdd(&h[(key >> SHIFT) & (BINS - 1)], 1);
-  }
-  __syncthreads();
-  int32_t* gh = (PASS == 1 ? P.hist_b : P.hist_a) + (int64_t)u * kHistBins;
-  for (int i = threadIdx.x; i < BINS; i += 256)
-    if (h[i]) atomicAdd(&gh[i], h[i]);
-}
+struct Digit {
+  static constexpr int SHIFT = PASS == 0 ? 20 : (PASS == 1 ? 8 : 0);
+  static constexpr int BINS = PASS == 2 ? 256 : 4096;
+  static constexpr uint32_t MATCH = PASS == 0 ? 0u : (PASS == 1 ? 0xFFF00000u : 0xFFFFFF00u);
+};
 
+// Whole-block search of a digit histogram (counts of the keys that share the
+// digits found so far): the digit d* holding the need-th largest key, and the
+// number of keys in higher digits.  Thread T owns the BINS/256 digits just
+// below BINS - T*BINS/256, so a forward scan over threads runs from the top.
 template <int PASS>
-__global__ void __launch_bounds__(256) sel_find(SelectParams P) {
-  constexpr int SHIFT = PASS == 0 ? 20 : (PASS == 1 ? 8 : 0);
-  constexpr int BINS = PASS == 2 ? 256 : 4096;
-  constexpr int BPT = BINS / 256;
-  __shared__ int32_t sm[264];
+__device__ void find_digit(const int32_t* gh, int need, int32_t* sm, int& digit, int& above_out) {
+  constexpr int BINS = Digit<PASS>::BINS, BPT = BINS / 256;
   __shared__ int32_t s_digit, s_above;
-  const int u = blockIdx.x;
-  int32_t* st = P.state + (int64_t)u * 8;
-  if (st[ST_MODE] != MODE_RADIX) return;
-  const int need = st[ST_NEED];
-  int32_t* gh = (PASS == 1 ? P.hist_b : P.hist_a) + (int64_t)u * kHistBins;
-  // thread T owns digits [BINS - (T+1)*BPT, BINS - T*BPT): thread 0 has the top ones
   const int T = threadIdx.x;
   const int hi_d = BINS - T * BPT - 1;
   int32_t c[BPT];
@@ -151,34 +122,99 @@ __global__ void __launch_bounds__(256) sel_find(SelectParams P) {
     }
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    st[ST_PREFIX] = (int32_t)((uint32_t)st[ST_PREFIX] | ((uint32_t)s_digit << SHIFT));
-    st[ST_NEED] = need - s_above;
-  }
-  if (PASS == 1) {  // pass 2 accumulates into hist_a again
-    int32_t* ha = P.hist_a + (int64_t)u * kHistBins;
-    for (int i = threadIdx.x; i < 256; i += 256) ha[i] = 0;
+  digit = s_digit;
+  above_out = s_above;
+  __syncthreads();
+}
+
+// Positions [base, end) of one unit's candidates, 64 per thread in 16 rounds
+// of 4 consecutive keys (16-byte loads when the row allows them).
+template <typename F>
+__device__ __forceinline__ void for_each_key(const float* s, int base, int end, bool vec_ok, F&& f) {
+#pragma unroll 4
+  for (int i = 0; i < kSelChunk / 1024; ++i) {
+    const int j = base + 4 * (threadIdx.x + 256 * i);
+    if (j >= end) break;
+    if (vec_ok && j + 3 < end) {
+      const float4 v = *(const float4*)(s + j);
+      f(j, score_key(v.x));
+      f(j + 1, score_key(v.y));
+      f(j + 2, score_key(v.z));
+      f(j + 3, score_key(v.w));
+    } else {
+      for (int e = 0; e < 4 && j + e < end; ++e) f(j + e, score_key(s[j + e]));
+    }
   }
 }
 
-// per chunk: keys above the threshold and keys equal to it
-__global__ void __launch_bounds__(256) sel_count(SelectParams P) {
+// PASS 0 histograms all candidates; PASS 1 and 2 first settle the previous
+// digit (every workgroup computes it; chunk 0 records it) and histogram the
+// keys that share the digits found so far.
+template <int PASS>
+__global__ void __launch_bounds__(256) sel_hist(SelectParams P) {
+  using DG = Digit<PASS>;
+  __shared__ int32_t h[DG::BINS];
   __shared__ int32_t sm[264];
   const int u = blockIdx.y, chunk = blockIdx.x;
-  const int32_t* st = P.state + (int64_t)u * 8;
+  int32_t* st = P.state + (int64_t)u * ST_WORDS;
   if (st[ST_MODE] != MODE_RADIX) return;
   const int ncand = st[ST_NCAND];
   const int base = chunk * kSelChunk;
   if (base >= ncand) return;
   const int end = min(base + kSelChunk, ncand);
-  const uint32_t tau = (uint32_t)st[ST_PREFIX];
+  int32_t* hist = P.hist + (int64_t)u * 3 * kHistBins;
+  uint32_t prefix = 0;
+  if constexpr (PASS > 0) {
+    // the previous pass's digit; inputs are what the kernel before wrote
+    uint32_t prev = PASS == 1 ? 0u : (uint32_t)st[ST_PREFIX1];
+    int need = PASS == 1 ? st[ST_TAKE] : st[ST_NEED1];
+    int d, above;
+    find_digit<PASS - 1>(hist + (PASS - 1) * kHistBins, need, sm, d, above);
+    prefix = prev | ((uint32_t)d << Digit<PASS - 1>::SHIFT);
+    need -= above;
+    if (chunk == 0 && threadIdx.x == 0) {
+      st[PASS == 1 ? ST_PREFIX1 : ST_PREFIX2] = (int32_t)prefix;
+      st[PASS == 1 ? ST_NEED1 : ST_NEED2] = need;
+    }
+  }
+  for (int i = threadIdx.x; i < DG::BINS; i += 256) h[i] = 0;
+  __syncthreads();
+  const float* s = P.scores + (int64_t)u * P.N;
+  const bool vec_ok = (P.N & 3) == 0;
+  for_each_key(s, base, end, vec_ok, [&](int, uint32_t key) {
+    if ((key & DG::MATCH) == prefix) atomicAdd(&h[(key >> DG::SHIFT) & (DG::BINS - 1)], 1);
+  });
+  __syncthreads();
+  int32_t* gh = hist + PASS * kHistBins;
+  for (int i = threadIdx.x; i < DG::BINS; i += 256)
+    if (h[i]) atomicAdd(&gh[i], h[i]);
+}
+
+// settles the last digit (threshold tau and how many keys equal to it are
+// taken), then counts, per chunk, keys above tau and keys equal to it
+__global__ void __launch_bounds__(256) sel_count(SelectParams P) {
+  __shared__ int32_t sm[264];
+  const int u = blockIdx.y, chunk = blockIdx.x;
+  int32_t* st = P.state + (int64_t)u * ST_WORDS;
+  if (st[ST_MODE] != MODE_RADIX) return;
+  const int ncand = st[ST_NCAND];
+  const int base = chunk * kSelChunk;
+  if (base >= ncand) return;
+  const int end = min(base + kSelChunk, ncand);
+  int d, above;
+  const int need2 = st[ST_NEED2];
+  find_digit<2>(P.hist + ((int64_t)u * 3 + 2) * kHistBins, need2, sm, d, above);
+  const uint32_t tau = (uint32_t)st[ST_PREFIX2] | (uint32_t)d;
+  if (chunk == 0 && threadIdx.x == 0) {
+    st[ST_TAU] = (int32_t)tau;
+    st[ST_NEED3] = need2 - above;
+  }
   const float* s = P.scores + (int64_t)u * P.N;
   int32_t gt = 0, eq = 0;
-  for (int j = base + threadIdx.x; j < end; j += 256) {
-    const uint32_t key = score_key(s[j]);
+  for_each_key(s, base, end, (P.N & 3) == 0, [&](int, uint32_t key) {
     gt += key > tau;
     eq += key == tau;
-  }
+  });
   int32_t tgt, teq;
   block_exclusive_scan<int32_t>(gt, sm, tgt);
   block_exclusive_scan<int32_t>(eq, sm, teq);
@@ -188,17 +224,19 @@ __global__ void __launch_bounds__(256) sel_count(SelectParams P) {
   }
 }
 
+// Ascending compaction: every key above tau, and the lowest-positioned keys
+// equal to tau, then (chunk 0) the forced window, the count and the padding.
 __global__ void __launch_bounds__(256) sel_emit(SelectParams P) {
   __shared__ int32_t sm[264];
   const int u = blockIdx.y, chunk = blockIdx.x;
-  const int32_t* st = P.state + (int64_t)u * 8;
+  const int32_t* st = P.state + (int64_t)u * ST_WORDS;
   const int mode = st[ST_MODE];
   const int ncand = st[ST_NCAND];
   const int take = st[ST_TAKE];
   const int p = st[ST_P];
   int32_t* out = P.idx + (int64_t)u * P.max_sel;
 
-  if (chunk == 0) {  // forced window, count and padding
+  if (chunk == 0) {
     const int wlo = max(0, p - P.window + 1);
     const int nw = p - wlo + 1;
     for (int i = threadIdx.x; i < nw; i += 256) out[take + i] = wlo + i;
@@ -213,9 +251,9 @@ __global__ void __launch_bounds__(256) sel_emit(SelectParams P) {
     for (int j = base + threadIdx.x; j < end; j += 256) out[j] = j;
     return;
   }
-  const uint32_t tau = (uint32_t)st[ST_PREFIX];
-  const int need = st[ST_NEED];
-  // selected count and equal-key count of all earlier chunks
+  const uint32_t tau = (uint32_t)st[ST_TAU];
+  const int need = st[ST_NEED3];
+  // selected and equal-key counts of all earlier chunks
   int32_t eq_before = 0, sel_before = 0;
   for (int c0 = 0; c0 < chunk; c0 += 256) {
     const int c = c0 + threadIdx.x;
@@ -232,44 +270,49 @@ __global__ void __launch_bounds__(256) sel_emit(SelectParams P) {
     eq_before += eq_tot;
     sel_before += sel_tot;
   }
-  // this chunk: thread owns 16 consecutive positions
-  const int j0 = base + threadIdx.x * 16;
   const float* s = P.scores + (int64_t)u * P.N;
-  uint32_t keys[16];
-  int32_t my_eq = 0;
+  int32_t eq_rank = eq_before, slot = sel_before;
+  // 4 rounds of 4096 positions; a thread owns 16 consecutive ones per round
+  for (int rb = base; rb < end; rb += 4096) {
+    const int j0 = rb + threadIdx.x * 16;
+    uint32_t keys[16];
+    int32_t my_eq = 0;
 #pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    const int j = j0 + e;
-    keys[e] = (j < end) ? score_key(s[j]) : 0u;
-    my_eq += (j < end) && keys[e] == tau;
-  }
-  int32_t teq;
-  int32_t eq_rank = eq_before + block_exclusive_scan<int32_t>(my_eq, sm, teq);
-  uint32_t selmask = 0;
-  int32_t my_sel = 0;
+    for (int e = 0; e < 16; ++e) {
+      const int j = j0 + e;
+      keys[e] = (j < end) ? score_key(s[j]) : 0u;
+      my_eq += (j < end) && keys[e] == tau;
+    }
+    int32_t teq;
+    int32_t r_eq = eq_rank + block_exclusive_scan<int32_t>(my_eq, sm, teq);
+    uint32_t selmask = 0;
+    int32_t my_sel = 0;
 #pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    const int j = j0 + e;
-    bool take_it = false;
-    if (j < end) {
-      if (keys[e] > tau) {
-        take_it = true;
-      } else if (keys[e] == tau) {
-        take_it = eq_rank < need;
-        ++eq_rank;
+    for (int e = 0; e < 16; ++e) {
+      const int j = j0 + e;
+      bool take_it = false;
+      if (j < end) {
+        if (keys[e] > tau) {
+          take_it = true;
+        } else if (keys[e] == tau) {
+          take_it = r_eq < need;
+          ++r_eq;
+        }
       }
+      selmask |= (uint32_t)take_it << e;
+      my_sel += take_it;
     }
-    selmask |= (uint32_t)take_it << e;
-    my_sel += take_it;
-  }
-  int32_t tsel;
-  int32_t slot = sel_before + block_exclusive_scan<int32_t>(my_sel, sm, tsel);
+    int32_t tsel;
+    int32_t sl = slot + block_exclusive_scan<int32_t>(my_sel, sm, tsel);
 #pragma unroll
-  for (int e = 0; e < 16; ++e)
-    if (selmask >> e & 1u) {
-      if (slot < take) out[slot] = j0 + e;  // never past this unit's budget
-      ++slot;
-    }
+    for (int e = 0; e < 16; ++e)
+      if (selmask >> e & 1u) {
+        if (sl < take) out[sl] = j0 + e;  // never past this unit's budget
+        ++sl;
+      }
+    eq_rank += teq;
+    slot += tsel;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -278,7 +321,7 @@ __global__ void __launch_bounds__(256) sel_emit(SelectParams P) {
 __global__ void __launch_bounds__(256) sel_block_mass(SelectParams P) {
   const int u = blockIdx.y;
   const int beta = blockIdx.x * 256 + threadIdx.x;
-  const int32_t* st = P.state + (int64_t)u * 8;
+  const int32_t* st = P.state + (int64_t)u * ST_WORDS;
   const int ncand = st[ST_NCAND];
   const int nb = ncand > 0 ? (ncand - 1) / P.block_size + 1 : 0;
   if (beta >= nb) return;
@@ -295,7 +338,7 @@ __global__ void __launch_bounds__(256) sel_block_pick(SelectParams P) {
   __shared__ int s_b[256];
   __shared__ int32_t sm[264];
   const int u = blockIdx.x;
-  const int32_t* st = P.state + (int64_t)u * 8;
+  const int32_t* st = P.state + (int64_t)u * ST_WORDS;
   const int ncand = st[ST_NCAND];
   const int take = st[ST_TAKE];
   const int p = st[ST_P];
@@ -362,11 +405,8 @@ hipError_t launch_select(const SelectParams& p, hipStream_t s) {
   HS2_L("select_init", sel_init, dim3(p.units));
   if (p.block_size == 1) {
     HS2_L("select_hist", sel_hist<0>, grid_c);
-    HS2_L("select_find", sel_find<0>, dim3(p.units));
     HS2_L("select_hist", sel_hist<1>, grid_c);
-    HS2_L("select_find", sel_find<1>, dim3(p.units));
     HS2_L("select_hist", sel_hist<2>, grid_c);
-    HS2_L("select_find", sel_find<2>, dim3(p.units));
     HS2_L("select_count", sel_count, grid_c);
     HS2_L("select_emit", sel_emit, grid_c);
   } else {

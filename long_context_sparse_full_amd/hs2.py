@@ -60,6 +60,7 @@ _sparse = _sig("hs2_sparse_attn_gather", ctypes.c_int,
                [_KVP, _vp, _i32, _i32, _i32, _f32, _vp, _vp, _i32, _vp, _vp, _vp])
 _bridge = _sig("hs2_kv_bridge", ctypes.c_int, [_vp, _i32, _i32, _vp, _KVP, _i32, _i32, _vp])
 _dbg_e4m3 = _sig("hs2_debug_e4m3fn_to_f32", ctypes.c_int, [_vp, _vp, _i32, _vp])
+_dbg_stream = _sig("hs2_debug_stream_read", ctypes.c_int, [_vp, _sz, _vp, _i32, _vp])
 _t_enable = _sig("hs2_timing_enable", ctypes.c_int, [ctypes.c_int])
 _t_reset = _sig("hs2_timing_reset", ctypes.c_int, [])
 _t_collect = _sig("hs2_timing_collect", ctypes.c_int,
@@ -69,7 +70,8 @@ _t_name = _sig("hs2_timing_kernel_name", ctypes.c_char_p, [_i32])
 EXPORTED = [
     "hs2_abi_version", "hs2_status_string", "hs2_last_error", "hs2_full_attn_scores_workspace",
     "hs2_full_attn_scores", "hs2_select_workspace", "hs2_select_workspace_for", "hs2_select_topk_window",
-    "hs2_sparse_attn_gather", "hs2_kv_bridge", "hs2_debug_e4m3fn_to_f32", "hs2_timing_enable",
+    "hs2_sparse_attn_gather", "hs2_kv_bridge", "hs2_debug_e4m3fn_to_f32", "hs2_debug_stream_read",
+    "hs2_timing_enable",
     "hs2_timing_reset", "hs2_timing_collect", "hs2_timing_kernel_name",
 ]
 
@@ -204,6 +206,15 @@ def kv_bridge(hidden, w_kv, k_cache, v_cache, batch_index: int, pos0: int):
 def debug_e4m3fn_to_f32(codes: torch.Tensor) -> torch.Tensor:
     out = torch.empty(codes.numel(), dtype=torch.float32, device=codes.device)
     _check(_dbg_e4m3(codes.data_ptr(), out.data_ptr(), codes.numel(), _stream()), "hs2_debug_e4m3fn_to_f32")
+    return out
+
+
+def debug_stream_read(buf: torch.Tensor, blocks: int = 2048) -> torch.Tensor:
+    """Read every byte of buf once (streaming probe); returns the per-thread xor words."""
+    out = torch.empty(blocks * 256, dtype=torch.int32, device=buf.device)
+    nbytes = buf.numel() * buf.element_size()
+    _check(_dbg_stream(buf.data_ptr(), nbytes - nbytes % 16, out.data_ptr(), blocks, _stream()),
+           "hs2_debug_stream_read")
     return out
 
 

@@ -128,8 +128,9 @@ def test_full_attn_validation(hs2, case, want):
 def test_workspace_figures(hs2):
     d = desc(hs2, N=1 << 20, H=4)
     ws = hs2._full_ws(ctypes.byref(d), 1, 32)
-    # logits scratch: 4 kv heads x 8 rows x 2^20 positions x 4 B, plus split partials
-    assert 4 * 8 * (1 << 20) * 4 <= ws < 4 * 8 * (1 << 20) * 4 + (64 << 20)
+    # logit codes: 4 kv heads x 8 rows x 2^20 positions x 2 B, tile maxima (1/16 of that), split partials
+    codes = 4 * 8 * (1 << 20) * 2
+    assert codes + codes // 16 <= ws < codes + codes // 16 + (32 << 20)
     assert hs2._sel_ws(1, 1, 4, 1 << 20) >= hs2._sel_ws_for(1, 1, 4, 1 << 20, 1)
     assert hs2._sel_ws_for(1, 512, 4, 131072, 64) > 0
     assert hs2._full_ws(None, 1, 32) == 0

@@ -71,7 +71,7 @@ def test_full_layer_parity(hs2, case):
     o_or, l_or, s_or = oracle_full(inp, spec)
     e_o = gu.assert_close(gu.host(out), o_or, gu.O_TOL[kv], "out")
     e_l = gu.assert_close(gu.host(lse), l_or, gu.LSE_TOL[kv], "lse")
-    e_s = gu.assert_scores(gu.host(sc), s_or)
+    e_s = gu.assert_scores(gu.host(sc), s_or, G=G)
     gu.log(f"  max|dO|={e_o:.2e} max|dLSE|={e_l:.2e} max rel dS={e_s:.2e}")
 
 
@@ -85,7 +85,7 @@ def test_full_layer_q_pos0_before_end(hs2):
     o_or, l_or, s_or = oracle.full_attn_scores(inp.q_full, inp.k, inp.v, qp)
     gu.assert_close(gu.host(out), o_or, gu.O_TOL["bf16"], "out")
     gu.assert_close(gu.host(lse), l_or, gu.LSE_TOL["bf16"], "lse")
-    gu.assert_scores(gu.host(sc), s_or)
+    gu.assert_scores(gu.host(sc), s_or, G=spec.G)
     assert np.all(gu.host(sc)[..., qp + 2:] == 0.0)
 
 
@@ -259,4 +259,4 @@ def test_strided_cache_view(hs2):
     torch.cuda.synchronize()
     o_or, l_or, s_or = oracle_full(inp, spec)
     gu.assert_close(gu.host(out), o_or, gu.O_TOL["bf16"], "out")
-    gu.assert_scores(gu.host(sc), s_or)
+    gu.assert_scores(gu.host(sc), s_or, G=spec.G)
