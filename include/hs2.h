@@ -137,6 +137,20 @@ int hs2_sparse_attn_gather(const hs2_kv_desc* kv, const void* q, hs2_dtype q_dty
                            const int32_t* count, int32_t max_sel, void* out, float* lse,
                            hipStream_t stream);
 
+/* The same sparse layer with a caller workspace: each (b, t, g) list is cut
+ * into slices of 128 entries, one workgroup per slice, and the last slice to
+ * finish merges the partials -- many more workgroups at small batch.  The
+ * workspace (device, 256-byte aligned, at least hs2_sparse_attn_workspace()
+ * bytes) holds per-(b, t, g) arrival counters that MUST be zero before the
+ * first call on it (e.g. zero-filled at allocation); every call leaves them
+ * zero again.  Calls that share a workspace must be ordered on one stream.
+ * fp32 caches take the workspace-free path. */
+size_t hs2_sparse_attn_workspace(int32_t B, int32_t Tq, int32_t Hkv, int32_t D, int32_t max_sel);
+int hs2_sparse_attn_gather_ws(const hs2_kv_desc* kv, const void* q, hs2_dtype q_dtype, int32_t Tq,
+                              int32_t Hq, float softmax_scale, const int32_t* idx,
+                              const int32_t* count, int32_t max_sel, void* out, float* lse,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* KV bridge (javabetter.cn, KV Bridging paragraph: a cross-decoder full layer
  * computes its K and V from a self-decoder layer's hidden state, with its own
  * parameters).  y = hidden [T, d_model] (bf16) x w_kv [d_model, 2*Hkv*D]

@@ -121,7 +121,7 @@ SelPlan plan_select(int B, int Tq, int Hkv, int N, int block_size) {
     p.off_hist = off;
     off = a256(off + (size_t)p.units * 3 * hs2::kHistBins * sizeof(int32_t));
     p.off_cnt = off;
-    off = a256(off + (size_t)p.units * p.nchunks * 2 * sizeof(int32_t));
+    off = a256(off + (size_t)p.units * p.nchunks * 258 * sizeof(int32_t));
   } else {
     p.off_bmass = off;
     off = a256(off + (size_t)p.units * p.nblocks_max * sizeof(double));
@@ -143,7 +143,7 @@ int hip_fail(hipError_t e, const char* what) {
 // event timing
 // ---------------------------------------------------------------------------
 const char* const kKernelNames[] = {"full_scan",   "combine",     "score",        "select_init",
-                                    "select_hist", "select_count", "select_emit",
+                                    "select_hist", "select_emit",
                                     "select_block_mass", "select_block_pick", "sparse_gather", "kv_bridge", "stream_read",
                                     nullptr};
 
@@ -388,6 +388,92 @@ int hs2_sparse_attn_gather(const hs2_kv_desc* kv, const void* q, hs2_dtype q_dty
   p.out = out;
   p.lse = lse;
   const hipError_t e = hs2::launch_scan(p, kv->dtype, true, false, stream);
+  if (e != hipSuccess) return hip_fail(e, "sparse_gather launch");
+  return HS2_OK;
+}
+
+namespace {
+struct GatherPlan {
+  int nsplit, slice;
+  size_t off_ml, off_o, off_cnt, total;
+};
+// slices of 128 list slots (one 32-row tile per wave of a 4-wave workgroup)
+GatherPlan plan_gather(int units, int max_sel, int D) {
+  GatherPlan g{};
+  g.slice = 128;
+  g.nsplit = (int)cdiv(max_sel, g.slice);
+  if (g.nsplit > 32) {  // long lists: about 32 slices of a multiple of 128 slots, at most 2048
+    g.slice = (int)std::min<int64_t>(rup(cdiv(max_sel, 32), 128), 2048);
+    g.nsplit = (int)cdiv(max_sel, g.slice);
+  }
+  size_t off = 0;
+  g.off_cnt = off;
+  off = a256(off + (size_t)units * sizeof(int32_t));
+  g.off_ml = off;
+  off = a256(off + (size_t)units * g.nsplit * 16 * 2 * sizeof(float));
+  g.off_o = off;
+  off = a256(off + (size_t)units * g.nsplit * 16 * D * sizeof(float));
+  g.total = off;
+  return g;
+}
+}  // namespace
+
+size_t hs2_sparse_attn_workspace(int32_t B, int32_t Tq, int32_t Hkv, int32_t D, int32_t max_sel) {
+  if (B <= 0 || Tq <= 0 || Hkv <= 0 || D <= 0 || max_sel <= 0) return 0;
+  return plan_gather(B * Tq * Hkv, max_sel, D).total;
+}
+
+int hs2_sparse_attn_gather_ws(const hs2_kv_desc* kv, const void* q, hs2_dtype q_dtype, int32_t Tq, int32_t Hq,
+                              float softmax_scale, const int32_t* idx, const int32_t* count, int32_t max_sel,
+                              void* out, float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int st = check_kv(kv, "hs2_sparse_attn_gather_ws");
+  if (st) return st;
+  if ((st = check_q(kv, q, q_dtype, Tq, Hq, "hs2_sparse_attn_gather_ws"))) return st;
+  if (!idx || !count || !out) return fail(HS2_ERR_INVALID_ARG, "hs2_sparse_attn_gather_ws: NULL idx/count/out");
+  if (max_sel <= 0) return fail(HS2_ERR_INVALID_ARG, "hs2_sparse_attn_gather_ws: max_sel must be positive");
+  if (!al16(out) || ((uintptr_t)idx & 3) || ((uintptr_t)count & 3) || (lse && ((uintptr_t)lse & 3)))
+    return fail(HS2_ERR_INVALID_ARG, "hs2_sparse_attn_gather_ws: out must be 16-byte aligned, idx/count/lse 4-byte");
+  if (!std::isfinite(softmax_scale))
+    return fail(HS2_ERR_INVALID_ARG, "hs2_sparse_attn_gather_ws: softmax_scale not finite");
+  if (kv->dtype == HS2_F32)  // the fp32 path has no split form; it needs no workspace
+    return hs2_sparse_attn_gather(kv, q, q_dtype, Tq, Hq, softmax_scale, idx, count, max_sel, out, lse, stream);
+  const int units = kv->B * Tq * kv->Hkv;
+  const GatherPlan gp = plan_gather(units, max_sel, kv->D);
+  if (!workspace || workspace_bytes < gp.total)
+    return fail(HS2_ERR_WORKSPACE, "hs2_sparse_attn_gather_ws: workspace needs " + std::to_string(gp.total) + " bytes");
+  if ((uintptr_t)workspace & 255)
+    return fail(HS2_ERR_INVALID_ARG, "hs2_sparse_attn_gather_ws: workspace must be 256-byte aligned");
+  hs2::ScanParams p{};
+  p.k = kv->k;
+  p.v = kv->v;
+  p.sb = kv->stride_b;
+  p.sh = kv->stride_h;
+  p.sn = kv->stride_n;
+  p.k_scale = kv->k_scale;
+  p.v_scale = kv->v_scale;
+  p.B = kv->B;
+  p.Hkv = kv->Hkv;
+  p.N = kv->N;
+  p.D = kv->D;
+  p.G = Hq / kv->Hkv;
+  p.q = q;
+  p.Tq = Tq;
+  p.Hq = Hq;
+  p.scale_log2 = softmax_scale * 1.44269504088896340736f;
+  p.tpack = 1;
+  p.n_tpacks = Tq;
+  p.rows = p.G;
+  p.nsplit = gp.nsplit;
+  p.split_len = gp.slice;
+  p.part_ml = at<float>(workspace, gp.off_ml);
+  p.part_o = at<float>(workspace, gp.off_o);
+  p.gcounter = at<int32_t>(workspace, gp.off_cnt);
+  p.idx = idx;
+  p.count = count;
+  p.max_sel = max_sel;
+  p.out = out;
+  p.lse = lse;
+  const hipError_t e = hs2::launch_gather_split(p, kv->dtype, stream);
   if (e != hipSuccess) return hip_fail(e, "sparse_gather launch");
   return HS2_OK;
 }

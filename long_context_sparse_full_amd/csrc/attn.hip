@@ -502,21 +502,144 @@ __global__ void __launch_bounds__(WAVES * 64) scan_gather(ScanParams P) {
     auto compute = [&](const RawTile<FP8, D>& R, int j0) {
       compute_tile<FP8, D, false>(R, qf, cs, j0, jl, j0 + 31 > jl, g4, nullptr, nullptr, S);
     };
-    RawTile<FP8, D> A, B;
+    const int jend = base + nb;
     int j0 = base + wave * 32;
-    if (j0 < base + nb) load(A, j0);
-    while (j0 < base + nb) {
-      const int j1 = j0 + STEP;
-      if (j1 < base + nb) load(B, j1);
+    if constexpr (!FP8 && D == 128) {  // 64-register tiles: two-tile ping-pong
+      RawTile<FP8, D> A, B;
+      if (j0 < jend) load(A, j0);
+      while (j0 < jend) {
+        if (j0 + STEP < jend) load(B, j0 + STEP);
+        compute(A, j0);
+        j0 += STEP;
+        if (j0 >= jend) break;
+        if (j0 + STEP < jend) load(A, j0 + STEP);
+        compute(B, j0);
+        j0 += STEP;
+      }
+    } else {
+    // three-tile register ring: two tiles of loads in flight while one is computed
+    RawTile<FP8, D> A, B, C;
+    if (j0 < jend) load(A, j0);
+    if (j0 + STEP < jend) load(B, j0 + STEP);
+    while (j0 < jend) {
+      if (j0 + 2 * STEP < jend) load(C, j0 + 2 * STEP);
       compute(A, j0);
-      if (j1 >= base + nb) break;
-      const int j2 = j1 + STEP;
-      if (j2 < base + nb) load(A, j2);
-      compute(B, j1);
-      j0 = j2;
+      j0 += STEP;
+      if (j0 >= jend) break;
+      if (j0 + 2 * STEP < jend) load(A, j0 + 2 * STEP);
+      compute(B, j0);
+      j0 += STEP;
+      if (j0 >= jend) break;
+      if (j0 + 2 * STEP < jend) load(B, j0 + 2 * STEP);
+      compute(C, j0);
+      j0 += STEP;
+    }
     }
   }
   merge_and_store<FP8, D, true, WAVES>(P, S, unit, 0, b, g, wave, r, g4, sm_m, sm_l, sm_o);
+}
+
+// Sparse layer, split form: the index list of each (b, t, g) is cut into
+// gsplit slices of gslice slots; one workgroup per slice (one 32-row tile per
+// wave when gslice = 128) writes a partial (max, sum, output); the workgroup
+// that finishes last for its (b, t, g) -- a device-scope counter, fenced on
+// both sides -- merges the partials, writes the output and re-arms the counter.
+template <bool FP8, int D, int WAVES>
+__global__ void __launch_bounds__(WAVES * 64) scan_gather_split(ScanParams P) {
+  constexpr int VE = D / 16, NC = D / 32, EB = FP8 ? 1 : 2;
+  constexpr int STEP = WAVES * 32;
+  __shared__ float sm_m[WAVES][16];
+  __shared__ float sm_l[WAVES][16];
+  __shared__ float sm_o[WAVES][16][D + 1];
+  __shared__ int s_idx[kGatherIdxCap];
+  __shared__ int s_last;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane & 15, g4 = lane >> 4;
+  const int unit = blockIdx.y, split = blockIdx.x;  // unit = (b, t, g)
+  const int g = unit % P.Hkv;
+  const int t = (unit / P.Hkv) % P.Tq;
+  const int b = unit / (P.Hkv * P.Tq);
+  const bool row_ok = r < P.G;
+  const int h = g * P.G + r;
+  const int32_t* list = P.idx + (int64_t)unit * P.max_sel;
+  const int n = min(max(P.count[unit], 0), P.max_sel);
+  const int lo = split * P.split_len;  // gslice
+  const int hi = min(lo + P.split_len, n);
+
+  u32x4_t qf[NC];
+  load_q<FP8, D>(qf, P, b, t, h, row_ok, g4);
+  const int64_t kvoff = ((int64_t)b * P.sb + (int64_t)g * P.sh) * EB;
+  const char* kb = (const char*)P.k + kvoff + 16 * g4;
+  const char* vb = (const char*)P.v + kvoff + VE * r * EB;
+  const int64_t snb = P.sn * EB;
+  float cs = P.scale_log2;
+  if constexpr (FP8) cs *= P.k_scale[b * P.Hkv + g];
+
+  WaveState<D> S;
+  S.m = kNegInf;
+  S.l = 0.f;
+#pragma unroll
+  for (int dt = 0; dt < VE; ++dt) S.o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int nb = max(0, hi - lo);  // <= gslice <= kGatherIdxCap
+  for (int i = threadIdx.x; i < nb; i += WAVES * 64) s_idx[i] = min(max(list[lo + i], 0), P.N - 1);
+  __syncthreads();
+  if (nb > 0) {
+    const int jl = lo + nb - 1;
+    auto load = [&](RawTile<FP8, D>& R, int j0) {
+      const char* kp[2];
+      const char* vp[8];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) kp[hh] = kb + (int64_t)s_idx[min(j0 - lo + 16 * hh + r, nb - 1)] * snb;
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk)
+        vp[kk] = vb + (int64_t)s_idx[min(j0 - lo + 16 * (kk >> 2) + 4 * g4 + (kk & 3), nb - 1)] * snb;
+      load_tile<FP8, D, false>(R, kp, vp);
+    };
+    RawTile<FP8, D> A, B;
+    int j0 = lo + wave * 32;
+    if (j0 < hi) load(A, j0);
+    while (j0 < hi) {
+      const int j1 = j0 + STEP;
+      if (j1 < hi) load(B, j1);
+      compute_tile<FP8, D, false>(A, qf, cs, j0, jl, j0 + 31 > jl, g4, nullptr, nullptr, S);
+      if (j1 >= hi) break;
+      const int j2 = j1 + STEP;
+      if (j2 < hi) load(A, j2);
+      compute_tile<FP8, D, false>(B, qf, cs, j1, jl, j1 + 31 > jl, g4, nullptr, nullptr, S);
+      j0 = j2;
+    }
+  }
+  // partial of this slice (rows = G heads), same layout as the full-layer splits
+  merge_and_store<FP8, D, false, WAVES>(P, S, unit, split, b, g, wave, r, g4, sm_m, sm_l, sm_o);
+
+  __threadfence();  // release the partial device-wide
+  __syncthreads();
+  if (threadIdx.x == 0) s_last = (atomicAdd(&P.gcounter[unit], 1) == P.nsplit - 1);
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();  // acquire the other slices' partials
+  for (int e = threadIdx.x; e < P.G * D; e += WAVES * 64) {
+    const int rr = e / D, d = e - rr * D;
+    const int64_t pb = (int64_t)unit * P.nsplit * 16 + rr;
+    float M = kNegInf;
+    for (int sp = 0; sp < P.nsplit; ++sp) M = fmaxf(M, P.part_ml[(pb + sp * 16) * 2]);
+    const float Ms = (M == kNegInf) ? 0.f : M;
+    float L = 0.f, O = 0.f;
+    for (int sp = 0; sp < P.nsplit; ++sp) {
+      const float f = exp2_fast(P.part_ml[(pb + sp * 16) * 2] - Ms);
+      L += P.part_ml[(pb + sp * 16) * 2 + 1] * f;
+      O += P.part_o[(pb + sp * 16) * D + d] * f;
+    }
+    float o = (L > 0.f) ? O / L : 0.f;
+    if constexpr (FP8) o *= P.v_scale[b * P.Hkv + g];
+    const int64_t orow = ((int64_t)b * P.Tq + t) * P.Hq + g * P.G + rr;
+    ((__bf16*)P.out)[orow * D + d] = (__bf16)o;
+    if (d == 0 && P.lse) P.lse[orow] = (L > 0.f) ? (M + log2f(L)) * kLn2 : kNegInf;
+  }
+  if (threadIdx.x == 0) P.gcounter[unit] = 0;  // re-armed for the next call
 }
 
 // ---------------------------------------------------------------------------
@@ -817,6 +940,13 @@ hipError_t go_full(const ScanParams& p, dim3 grid, hipStream_t s) {
 }
 
 template <bool FP8, int D, int WAVES>
+hipError_t go_gather_split(const ScanParams& p, dim3 grid, hipStream_t s) {
+  TimedLaunch tl("sparse_gather", s);
+  hipLaunchKernelGGL((scan_gather_split<FP8, D, WAVES>), grid, dim3(WAVES * 64), 0, s, p);
+  return hipGetLastError();
+}
+
+template <bool FP8, int D, int WAVES>
 hipError_t go_gather(const ScanParams& p, dim3 grid, hipStream_t s) {
   TimedLaunch tl("sparse_gather", s);
   hipLaunchKernelGGL((scan_gather<FP8, D, WAVES>), grid, dim3(WAVES * 64), 0, s, p);
@@ -864,6 +994,13 @@ hipError_t launch_scan(const ScanParams& p, int kv_dtype, bool gather, bool writ
   if (p.D == 128) HS2_GO(false, 128);
   HS2_GO(false, 64);
 #undef HS2_GO
+}
+
+hipError_t launch_gather_split(const ScanParams& p, int kv_dtype, hipStream_t s) {
+  const dim3 grid(p.nsplit, p.B * p.Tq * p.Hkv);
+  if (kv_dtype == HS2_FP8_E4M3FN)
+    return p.D == 128 ? go_gather_split<true, 128, 4>(p, grid, s) : go_gather_split<true, 64, 4>(p, grid, s);
+  return p.D == 128 ? go_gather_split<false, 128, 4>(p, grid, s) : go_gather_split<false, 64, 4>(p, grid, s);
 }
 
 hipError_t launch_combine(const CombineParams& p, int units, hipStream_t s) {

@@ -42,6 +42,7 @@ struct ScanParams {
   int max_sel;
   void* out;         // [B, Tq, Hq, D] in q's element type
   float* lse;        // [B, Tq, Hq] natural log (nullable)
+  int32_t* gcounter; // split gather: per-(b, t, g) arrival counters (zero between calls)
 };
 
 struct CombineParams {
@@ -77,13 +78,14 @@ struct SelectParams {
   int32_t* count;
   int32_t* state;   // [units][16]
   int32_t* hist;    // [units][3][4096] digit histograms of the three passes
-  int32_t* cnt;     // [units][nchunks][2]
+  int32_t* cnt;     // [units][nchunks][258]: keys above the 24-bit prefix, suffix sums of the last digit
   double* bmass;    // [units][nblocks_max] (block mode)
   int nblocks_max;
 };
 
 // launchers (return hipError_t of the launch)
 hipError_t launch_scan(const ScanParams& p, int kv_dtype, bool gather, bool write_logits, hipStream_t s);
+hipError_t launch_gather_split(const ScanParams& p, int kv_dtype, hipStream_t s);
 hipError_t launch_combine(const CombineParams& p, int units, hipStream_t s);
 hipError_t launch_score(const ScoreParams& p, int units, hipStream_t s);
 hipError_t launch_select(const SelectParams& p, hipStream_t s);

@@ -26,7 +26,7 @@ namespace {
 // per-unit state; each pass reads the slots of the previous kernel and writes
 // its own, so no kernel reads a slot that a sibling workgroup is writing
 enum { ST_MODE = 0, ST_NCAND = 1, ST_TAKE = 2, ST_P = 3, ST_PREFIX1 = 4, ST_NEED1 = 5,
-       ST_PREFIX2 = 6, ST_NEED2 = 7, ST_TAU = 8, ST_NEED3 = 9, ST_WORDS = 16 };
+       ST_PREFIX2 = 6, ST_NEED2 = 7, ST_WORDS = 16 };
 enum { MODE_RADIX = 0, MODE_ALL = 1, MODE_NONE = 2 };
 
 __device__ __forceinline__ uint32_t score_key(float s) {
@@ -127,29 +127,81 @@ __device__ void find_digit(const int32_t* gh, int need, int32_t* sm, int& digit,
   __syncthreads();
 }
 
-// Positions [base, end) of one unit's candidates, 64 per thread in 16 rounds
-// of 4 consecutive keys (16-byte loads when the row allows them).
-template <typename F>
-__device__ __forceinline__ void for_each_key(const float* s, int base, int end, bool vec_ok, F&& f) {
-#pragma unroll 4
-  for (int i = 0; i < kSelChunk / 1024; ++i) {
+// The 64 candidate keys of this thread in one chunk, all loads issued at once:
+// positions base + 4*(tid + 256*i) + e, i < 16, e < 4 (coalesced 16-byte
+// loads when the row allows them).  Keys of positions >= end are flagged.
+constexpr int kKeysPerThread = kSelChunk / 256;
+struct ChunkKeys {
+  uint32_t key[kKeysPerThread];
+  uint64_t valid;  // bit 4*i + e
+};
+
+__device__ __forceinline__ void load_keys(const float* s, int base, int end, bool vec_ok, ChunkKeys& K) {
+  K.valid = 0;
+#pragma unroll
+  for (int i = 0; i < kKeysPerThread / 4; ++i) {
     const int j = base + 4 * (threadIdx.x + 256 * i);
-    if (j >= end) break;
     if (vec_ok && j + 3 < end) {
       const float4 v = *(const float4*)(s + j);
-      f(j, score_key(v.x));
-      f(j + 1, score_key(v.y));
-      f(j + 2, score_key(v.z));
-      f(j + 3, score_key(v.w));
+      K.key[4 * i] = score_key(v.x);
+      K.key[4 * i + 1] = score_key(v.y);
+      K.key[4 * i + 2] = score_key(v.z);
+      K.key[4 * i + 3] = score_key(v.w);
+      K.valid |= (uint64_t)0xF << (4 * i);
     } else {
-      for (int e = 0; e < 4 && j + e < end; ++e) f(j + e, score_key(s[j + e]));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool ok = j + e < end;
+        K.key[4 * i + e] = ok ? score_key(s[j + e]) : 0u;
+        K.valid |= (uint64_t)ok << (4 * i + e);
+      }
     }
   }
 }
 
+// LDS histogram of one digit over the keys that match `prefix`.  PASS 0 keys
+// cluster in a few bins (the scores of one row share exponent and leading
+// mantissa bits), so each thread first counts its two most recent bins in
+// registers and only spills the others to the (contended) LDS atomics.
+template <int PASS>
+__device__ __forceinline__ void hist_keys(const ChunkKeys& K, uint32_t prefix, int32_t* h) {
+  using DG = Digit<PASS>;
+  if constexpr (PASS == 0) {
+    uint32_t b1 = 0xffffffffu, b2 = 0xffffffffu;
+    int32_t c1 = 0, c2 = 0;
+#pragma unroll
+    for (int i = 0; i < kKeysPerThread; ++i) {
+      if (!(K.valid >> i & 1)) continue;
+      const uint32_t bin = K.key[i] >> DG::SHIFT;
+      if (bin == b1) {
+        ++c1;
+      } else if (bin == b2) {
+        ++c2;
+      } else if (c1 == 0) {
+        b1 = bin;
+        c1 = 1;
+      } else if (c2 == 0) {
+        b2 = bin;
+        c2 = 1;
+      } else {
+        atomicAdd(&h[bin], 1);
+      }
+    }
+    if (c1) atomicAdd(&h[b1], c1);
+    if (c2) atomicAdd(&h[b2], c2);
+  } else {
+#pragma unroll
+    for (int i = 0; i < kKeysPerThread; ++i)
+      if ((K.valid >> i & 1) && (K.key[i] & DG::MATCH) == prefix) atomicAdd(&h[(K.key[i] >> DG::SHIFT) & (DG::BINS - 1)], 1);
+  }
+}
+
 // PASS 0 histograms all candidates; PASS 1 and 2 first settle the previous
-// digit (every workgroup computes it; chunk 0 records it) and histogram the
-// keys that share the digits found so far.
+// digit (every workgroup computes it while its loads are in flight; chunk 0
+// records it) and histogram the keys that share the digits found so far.
+// PASS 2 also stores, per chunk, the count of keys above the 24-bit prefix and
+// the suffix sums of its 256-bin histogram, from which the emit pass gets every
+// chunk's counts above and equal to the final threshold.
 template <int PASS>
 __global__ void __launch_bounds__(256) sel_hist(SelectParams P) {
   using DG = Digit<PASS>;
@@ -162,11 +214,13 @@ __global__ void __launch_bounds__(256) sel_hist(SelectParams P) {
   const int base = chunk * kSelChunk;
   if (base >= ncand) return;
   const int end = min(base + kSelChunk, ncand);
+  ChunkKeys K;
+  load_keys(P.scores + (int64_t)u * P.N, base, end, (P.N & 3) == 0, K);
   int32_t* hist = P.hist + (int64_t)u * 3 * kHistBins;
   uint32_t prefix = 0;
   if constexpr (PASS > 0) {
     // the previous pass's digit; inputs are what the kernel before wrote
-    uint32_t prev = PASS == 1 ? 0u : (uint32_t)st[ST_PREFIX1];
+    const uint32_t prev = PASS == 1 ? 0u : (uint32_t)st[ST_PREFIX1];
     int need = PASS == 1 ? st[ST_TAKE] : st[ST_NEED1];
     int d, above;
     find_digit<PASS - 1>(hist + (PASS - 1) * kHistBins, need, sm, d, above);
@@ -179,53 +233,33 @@ __global__ void __launch_bounds__(256) sel_hist(SelectParams P) {
   }
   for (int i = threadIdx.x; i < DG::BINS; i += 256) h[i] = 0;
   __syncthreads();
-  const float* s = P.scores + (int64_t)u * P.N;
-  const bool vec_ok = (P.N & 3) == 0;
-  for_each_key(s, base, end, vec_ok, [&](int, uint32_t key) {
-    if ((key & DG::MATCH) == prefix) atomicAdd(&h[(key >> DG::SHIFT) & (DG::BINS - 1)], 1);
-  });
+  hist_keys<PASS>(K, prefix, h);
   __syncthreads();
   int32_t* gh = hist + PASS * kHistBins;
   for (int i = threadIdx.x; i < DG::BINS; i += 256)
     if (h[i]) atomicAdd(&gh[i], h[i]);
-}
-
-// settles the last digit (threshold tau and how many keys equal to it are
-// taken), then counts, per chunk, keys above tau and keys equal to it
-__global__ void __launch_bounds__(256) sel_count(SelectParams P) {
-  __shared__ int32_t sm[264];
-  const int u = blockIdx.y, chunk = blockIdx.x;
-  int32_t* st = P.state + (int64_t)u * ST_WORDS;
-  if (st[ST_MODE] != MODE_RADIX) return;
-  const int ncand = st[ST_NCAND];
-  const int base = chunk * kSelChunk;
-  if (base >= ncand) return;
-  const int end = min(base + kSelChunk, ncand);
-  int d, above;
-  const int need2 = st[ST_NEED2];
-  find_digit<2>(P.hist + ((int64_t)u * 3 + 2) * kHistBins, need2, sm, d, above);
-  const uint32_t tau = (uint32_t)st[ST_PREFIX2] | (uint32_t)d;
-  if (chunk == 0 && threadIdx.x == 0) {
-    st[ST_TAU] = (int32_t)tau;
-    st[ST_NEED3] = need2 - above;
-  }
-  const float* s = P.scores + (int64_t)u * P.N;
-  int32_t gt = 0, eq = 0;
-  for_each_key(s, base, end, (P.N & 3) == 0, [&](int, uint32_t key) {
-    gt += key > tau;
-    eq += key == tau;
-  });
-  int32_t tgt, teq;
-  block_exclusive_scan<int32_t>(gt, sm, tgt);
-  block_exclusive_scan<int32_t>(eq, sm, teq);
-  if (threadIdx.x == 0) {
-    P.cnt[((int64_t)u * P.nchunks + chunk) * 2] = tgt;
-    P.cnt[((int64_t)u * P.nchunks + chunk) * 2 + 1] = teq;
+  if constexpr (PASS == 2) {
+    int32_t above24 = 0;
+#pragma unroll
+    for (int i = 0; i < kKeysPerThread; ++i) above24 += (K.valid >> i & 1) && (K.key[i] >> 8) > (prefix >> 8);
+    int32_t tot;
+    block_exclusive_scan<int32_t>(above24, sm, tot);
+    // suffix sums: thread T holds digit 255 - T; scan from the top digit
+    const int32_t cnt = h[255 - threadIdx.x];
+    int32_t dummy;
+    const int32_t suf_excl = block_exclusive_scan<int32_t>(cnt, sm, dummy);
+    int32_t* cs = P.cnt + ((int64_t)u * P.nchunks + chunk) * 258;
+    cs[1 + (255 - threadIdx.x)] = suf_excl + cnt;  // keys with digit >= 255-T
+    if (threadIdx.x == 0) {
+      cs[0] = tot;
+      cs[257] = 0;  // suffix beyond the top digit
+    }
   }
 }
 
-// Ascending compaction: every key above tau, and the lowest-positioned keys
-// equal to tau, then (chunk 0) the forced window, the count and the padding.
+// Ascending compaction: every key above tau and the lowest-positioned keys
+// equal to tau (tau and their number from the last digit's histogram), then
+// (chunk 0) the forced window, the count and the padding.
 __global__ void __launch_bounds__(256) sel_emit(SelectParams P) {
   __shared__ int32_t sm[264];
   const int u = blockIdx.y, chunk = blockIdx.x;
@@ -251,16 +285,43 @@ __global__ void __launch_bounds__(256) sel_emit(SelectParams P) {
     for (int j = base + threadIdx.x; j < end; j += 256) out[j] = j;
     return;
   }
-  const uint32_t tau = (uint32_t)st[ST_TAU];
-  const int need = st[ST_NEED3];
-  // selected and equal-key counts of all earlier chunks
+  // this chunk's keys, 16 consecutive positions per thread per round of 4096
+  const float* s = P.scores + (int64_t)u * P.N;
+  const bool vec_ok = (P.N & 3) == 0;
+  uint32_t keys[kKeysPerThread];
+#pragma unroll
+  for (int rnd = 0; rnd < 4; ++rnd) {
+    const int j0 = base + rnd * 4096 + threadIdx.x * 16;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int j = j0 + 4 * q;
+      if (vec_ok && j + 3 < end) {
+        const float4 v = *(const float4*)(s + j);
+        keys[rnd * 16 + 4 * q] = score_key(v.x);
+        keys[rnd * 16 + 4 * q + 1] = score_key(v.y);
+        keys[rnd * 16 + 4 * q + 2] = score_key(v.z);
+        keys[rnd * 16 + 4 * q + 3] = score_key(v.w);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) keys[rnd * 16 + 4 * q + e] = (j + e < end) ? score_key(s[j + e]) : 0u;
+      }
+    }
+  }
+  // final digit, threshold tau and how many keys equal to it are taken
+  int d, above;
+  find_digit<2>(P.hist + ((int64_t)u * 3 + 2) * kHistBins, st[ST_NEED2], sm, d, above);
+  const uint32_t tau = (uint32_t)st[ST_PREFIX2] | (uint32_t)d;
+  const int need = st[ST_NEED2] - above;
+  // counts of all earlier chunks: above tau = above the 24-bit prefix + digits > d
   int32_t eq_before = 0, sel_before = 0;
   for (int c0 = 0; c0 < chunk; c0 += 256) {
     const int c = c0 + threadIdx.x;
     int32_t gt = 0, eq = 0;
     if (c < chunk) {
-      gt = P.cnt[((int64_t)u * P.nchunks + c) * 2];
-      eq = P.cnt[((int64_t)u * P.nchunks + c) * 2 + 1];
+      const int32_t* cs = P.cnt + ((int64_t)u * P.nchunks + c) * 258;
+      const int32_t suf_d = cs[1 + d], suf_d1 = cs[2 + d];
+      gt = cs[0] + suf_d1;
+      eq = suf_d - suf_d1;
     }
     int32_t eq_tot;
     const int32_t eqb = eq_before + block_exclusive_scan<int32_t>(eq, sm, eq_tot);
@@ -270,31 +331,25 @@ __global__ void __launch_bounds__(256) sel_emit(SelectParams P) {
     eq_before += eq_tot;
     sel_before += sel_tot;
   }
-  const float* s = P.scores + (int64_t)u * P.N;
   int32_t eq_rank = eq_before, slot = sel_before;
-  // 4 rounds of 4096 positions; a thread owns 16 consecutive ones per round
-  for (int rb = base; rb < end; rb += 4096) {
-    const int j0 = rb + threadIdx.x * 16;
-    uint32_t keys[16];
+#pragma unroll
+  for (int rnd = 0; rnd < 4; ++rnd) {
+    const int j0 = base + rnd * 4096 + threadIdx.x * 16;
     int32_t my_eq = 0;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int j = j0 + e;
-      keys[e] = (j < end) ? score_key(s[j]) : 0u;
-      my_eq += (j < end) && keys[e] == tau;
-    }
+    for (int e = 0; e < 16; ++e) my_eq += (j0 + e < end) && keys[rnd * 16 + e] == tau;
     int32_t teq;
     int32_t r_eq = eq_rank + block_exclusive_scan<int32_t>(my_eq, sm, teq);
     uint32_t selmask = 0;
     int32_t my_sel = 0;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const int j = j0 + e;
+      const uint32_t key = keys[rnd * 16 + e];
       bool take_it = false;
-      if (j < end) {
-        if (keys[e] > tau) {
+      if (j0 + e < end) {
+        if (key > tau) {
           take_it = true;
-        } else if (keys[e] == tau) {
+        } else if (key == tau) {
           take_it = r_eq < need;
           ++r_eq;
         }
@@ -407,7 +462,6 @@ hipError_t launch_select(const SelectParams& p, hipStream_t s) {
     HS2_L("select_hist", sel_hist<0>, grid_c);
     HS2_L("select_hist", sel_hist<1>, grid_c);
     HS2_L("select_hist", sel_hist<2>, grid_c);
-    HS2_L("select_count", sel_count, grid_c);
     HS2_L("select_emit", sel_emit, grid_c);
   } else {
     HS2_L("select_block_mass", sel_block_mass, dim3((p.nblocks_max + 255) / 256, p.units));

@@ -58,6 +58,9 @@ _select = _sig("hs2_select_topk_window", ctypes.c_int,
                [_vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _i32, _vp, _sz, _vp])
 _sparse = _sig("hs2_sparse_attn_gather", ctypes.c_int,
                [_KVP, _vp, _i32, _i32, _i32, _f32, _vp, _vp, _i32, _vp, _vp, _vp])
+_sparse_ws_size = _sig("hs2_sparse_attn_workspace", _sz, [_i32, _i32, _i32, _i32, _i32])
+_sparse_ws = _sig("hs2_sparse_attn_gather_ws", ctypes.c_int,
+                  [_KVP, _vp, _i32, _i32, _i32, _f32, _vp, _vp, _i32, _vp, _vp, _vp, _sz, _vp])
 _bridge = _sig("hs2_kv_bridge", ctypes.c_int, [_vp, _i32, _i32, _vp, _KVP, _i32, _i32, _vp])
 _dbg_e4m3 = _sig("hs2_debug_e4m3fn_to_f32", ctypes.c_int, [_vp, _vp, _i32, _vp])
 _dbg_stream = _sig("hs2_debug_stream_read", ctypes.c_int, [_vp, _sz, _vp, _i32, _vp])
@@ -70,7 +73,7 @@ _t_name = _sig("hs2_timing_kernel_name", ctypes.c_char_p, [_i32])
 EXPORTED = [
     "hs2_abi_version", "hs2_status_string", "hs2_last_error", "hs2_full_attn_scores_workspace",
     "hs2_full_attn_scores", "hs2_select_workspace", "hs2_select_workspace_for", "hs2_select_topk_window",
-    "hs2_sparse_attn_gather", "hs2_kv_bridge", "hs2_debug_e4m3fn_to_f32", "hs2_debug_stream_read",
+    "hs2_sparse_attn_gather", "hs2_sparse_attn_workspace", "hs2_sparse_attn_gather_ws", "hs2_kv_bridge", "hs2_debug_e4m3fn_to_f32", "hs2_debug_stream_read",
     "hs2_timing_enable",
     "hs2_timing_reset", "hs2_timing_collect", "hs2_timing_kernel_name",
 ]
@@ -192,6 +195,28 @@ def sparse_attn_gather(k, v, q, idx, count, softmax_scale: float | None = None, 
     st = _sparse(ctypes.byref(d), q.data_ptr(), _dtype_code(q), Tq, Hq, float(softmax_scale), idx.data_ptr(),
                  count.data_ptr(), idx.shape[-1], out.data_ptr(), None if lse is None else lse.data_ptr(), _stream())
     _check(st, "hs2_sparse_attn_gather")
+    return out, lse
+
+
+def sparse_attn_workspace(B, Tq, Hkv, D, max_sel) -> int:
+    return int(_sparse_ws_size(B, Tq, Hkv, D, max_sel))
+
+
+def sparse_attn_gather_ws(k, v, q, idx, count, workspace, softmax_scale: float | None = None, k_scale=None,
+                          v_scale=None, out=None, lse=None, want_lse: bool = True):
+    """Sparse layer, split over list slices; `workspace` must start zero-filled (calls keep it so)."""
+    d = kv_desc(k, v, k_scale, v_scale)
+    B, Tq, Hq, D = q.shape
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Tq, Hq), dtype=torch.float32, device=q.device)
+    st = _sparse_ws(ctypes.byref(d), q.data_ptr(), _dtype_code(q), Tq, Hq, float(softmax_scale), idx.data_ptr(),
+                    count.data_ptr(), idx.shape[-1], out.data_ptr(), None if lse is None else lse.data_ptr(),
+                    workspace.data_ptr(), workspace.numel(), _stream())
+    _check(st, "hs2_sparse_attn_gather_ws")
     return out, lse
 
 

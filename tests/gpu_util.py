@@ -59,16 +59,23 @@ class DeviceBlock:
         self.qs = [dev(x) for x in inp.q_sparse]
 
 
-def run_block(hs2, blk: DeviceBlock, spec, k=None, window=None, block_size=1, layers=None):
-    """full -> select -> sparse layers on the GPU; returns host arrays."""
+def run_block(hs2, blk: DeviceBlock, spec, k=None, window=None, block_size=1, layers=None, split_gather=False):
+    """full -> select -> sparse layers on the GPU (as bench.py runs them; the
+    split gather with a zero-filled workspace when split_gather=True);
+    returns host arrays."""
     k = spec.k if k is None else k
     window = spec.window if window is None else window
     out, lse, sc = hs2.full_attn_scores(blk.k, blk.v, blk.q, spec.q_pos0, k_scale=blk.ks, v_scale=blk.vs)
     max_sel = min(spec.N, k * block_size + window)
     idx, cnt = hs2.select_topk_window(sc, spec.q_pos0, k, window, block_size=block_size, max_sel=max_sel)
+    ws = torch.zeros(max(hs2.sparse_attn_workspace(spec.B, spec.Tq, spec.Hkv, spec.D, max_sel), 256),
+                     dtype=torch.uint8, device="cuda")
     sp = []
     for q in (blk.qs if layers is None else blk.qs[:layers]):
-        o, l = hs2.sparse_attn_gather(blk.k, blk.v, q, idx, cnt, k_scale=blk.ks, v_scale=blk.vs)
+        if split_gather:
+            o, l = hs2.sparse_attn_gather_ws(blk.k, blk.v, q, idx, cnt, ws, k_scale=blk.ks, v_scale=blk.vs)
+        else:
+            o, l = hs2.sparse_attn_gather(blk.k, blk.v, q, idx, cnt, k_scale=blk.ks, v_scale=blk.vs)
         sp.append((host(o), host(l)))
     torch.cuda.synchronize()
     return dict(out=host(out), lse=host(lse), scores=host(sc), idx=host(idx), count=host(cnt), sparse=sp)

@@ -154,18 +154,53 @@ def test_select_deterministic(hs2):
 
 # ------------------------------------------------------------ sparse layers
 
-@pytest.mark.parametrize("kv,D,G", [("f32", 64, 4), ("bf16", 128, 8), ("fp8", 128, 8), ("bf16", 64, 16)])
-def test_sparse_parity_on_gpu_selection(hs2, kv, D, G):
+@pytest.mark.parametrize("split", [True, False], ids=["split", "single"])
+@pytest.mark.parametrize("kv,D,G", [("f32", 64, 4), ("bf16", 128, 8), ("fp8", 128, 8), ("bf16", 64, 16), ("fp8", 64, 8)])
+def test_sparse_parity_on_gpu_selection(hs2, kv, D, G, split):
     spec = small_spec(kv, D=D, G=G, Hkv=2, B=2, N=3000, Tq=2, k=200, window=32)
-    gu.log(f"sparse parity {kv} D={D} G={G}")
+    gu.log(f"sparse parity {kv} D={D} G={G} split={split}")
     inp = synth.make_inputs(spec, seed=99)
     blk = gu.DeviceBlock(inp)
-    res = gu.run_block(hs2, blk, spec)
+    res = gu.run_block(hs2, blk, spec, split_gather=split)
     for layer, (o, l) in enumerate(res["sparse"]):
         o_or, l_or = oracle.sparse_attn(inp.q_sparse[layer], inp.k, inp.v, res["idx"], res["count"],
                                         k_scale=inp.k_scale, v_scale=inp.v_scale)
         gu.assert_close(o, o_or, gu.O_TOL[kv], f"sparse layer {layer} out")
         gu.assert_close(l, l_or, gu.LSE_TOL[kv], f"sparse layer {layer} lse")
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_split_gather_lists_repeated_calls(hs2, kv):
+    """Split gather over list lengths around the 128-slot slices, long lists
+    (more than 32 slices), an empty list, and many calls on one workspace:
+    every call must match the oracle (the arrival counters re-arm)."""
+    spec = small_spec(kv, B=1, N=9000, Tq=6, Hkv=2)
+    inp = synth.make_inputs(spec, seed=55)
+    blk = gu.DeviceBlock(inp)
+    rng = np.random.default_rng(1)
+    max_sel = 4500
+    idx = np.full((1, 6, 2, max_sel), -1, np.int32)
+    cnt = np.zeros((1, 6, 2), np.int32)
+    for u, n in zip(np.ndindex(1, 6, 2), [0, 1, 127, 128, 129, 1152, 1153, 2048, 4097, 4500, 300, 64]):
+        idx[u][:n] = np.sort(rng.choice(9000, n, replace=False))
+        cnt[u] = n
+    o_or, l_or = oracle.sparse_attn(inp.q_sparse[0], inp.k, inp.v, idx, cnt, k_scale=inp.k_scale,
+                                    v_scale=inp.v_scale)
+    ws = torch.zeros(hs2.sparse_attn_workspace(1, 6, 2, spec.D, max_sel), dtype=torch.uint8, device="cuda")
+    di, dc = gu.dev(idx), gu.dev(cnt)
+    first = None
+    for rep in range(5):
+        o, l = hs2.sparse_attn_gather_ws(blk.k, blk.v, blk.qs[0], di, dc, ws, k_scale=blk.ks, v_scale=blk.vs)
+        torch.cuda.synchronize()
+        o, l = gu.host(o), gu.host(l)
+        gu.assert_close(o, o_or, gu.O_TOL[kv], f"call {rep} out")
+        fin = ~np.isinf(l_or)
+        gu.assert_close(l[fin], l_or[fin], gu.LSE_TOL[kv], f"call {rep} lse")
+        assert np.all(np.isneginf(l[~fin]))
+        if first is None:
+            first = (o, l)
+        assert np.array_equal(o, first[0]) and np.array_equal(l, first[1]), "run-to-run difference"
+    assert np.all(gu.host(ws.view(torch.int32)[:12]) == 0), "arrival counters not re-armed"
 
 
 def test_sparse_random_lists_and_empty(hs2):
