@@ -30,8 +30,10 @@ if ROOT not in sys.path:
 
 METRIC = "µs/decode-step (full scan + top-k + 3 sparse layers) & HBM GB/s at 1M ctx"
 HBM_PEAK_GBPS = 8000.0
-SCAN_SRC = os.path.join(ROOT, "long_context_sparse_full_amd", "csrc", "attn.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "full_scan_decode1m_fp8_traffic.json")
+SCAN_SRCS = [os.path.join(ROOT, "long_context_sparse_full_amd", "csrc", f)
+             for f in ("attn.hip", "hs2_internal.hpp", "api.cpp")]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "full_scan_decode1m_fp8.md")
+TRAFFIC_WORKLOAD = "decode1m_fp8"
 
 
 def log(*a):
@@ -51,20 +53,22 @@ def algorithmic_bytes(spec) -> dict:
             "step": kv_bytes + 2 * scores + spec.n_sparse * gathered}
 
 
-def traffic_entry(launch_bytes: int):
-    """HBM bytes per scan launch from the committed rocprofv3 counter summary,
-    only if it was taken on the current kernel source."""
-    if not os.path.exists(TRAFFIC_FILE):
+def traffic_entry(workload: str):
+    """HBM bytes per scan launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated) from
+    the committed rocprofv3 summary; None unless it was taken on this workload
+    and on the current scan sources."""
+    if workload != TRAFFIC_WORKLOAD or not os.path.exists(TRAFFIC_FILE):
         return None
-    try:
-        with open(TRAFFIC_FILE) as f:
-            t = json.load(f)
-        src_hash = hashlib.sha256(open(SCAN_SRC, "rb").read()).hexdigest()
-        if t.get("kernel_src_sha256") != src_hash:
-            return None
-        return int(t["hbm_bytes_per_launch"])
-    except Exception:  # noqa: BLE001
+    fields = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if line.startswith("- ") and ":" in line:
+                key, val = line[2:].split(":", 1)
+                fields[key.strip()] = val.strip()
+    src_hash = hashlib.sha256(b"".join(open(p, "rb").read() for p in SCAN_SRCS)).hexdigest()
+    if fields.get("kernel_src_sha256") != src_hash or "hbm_bytes_per_launch" not in fields:
         return None
+    return int(fields["hbm_bytes_per_launch"])
 
 
 def main():
@@ -109,8 +113,7 @@ def main():
         return
     spec = synth.config(args.config)
     if spec.Tq != 1:
-        log("bench.py times decode workloads (Tq = 1)")
-        sys.exit(2)
+        return bench_chunk(spec, args)
     log(f"[bench] generating {spec.name}")
     t0 = time.time()
     inp = synth.make_inputs(spec)
@@ -177,7 +180,7 @@ def main():
     achieved = ab["scan_kv"] / (scan_us * 1e-6) / 1e9
     roofline = {"kernel": "full_scan", "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                "traffic": traffic_entry(ab["scan_kv"]), "algorithmic_bytes_per_launch": ab["scan_kv"],
+                "traffic": traffic_entry(spec.name), "algorithmic_bytes_per_launch": ab["scan_kv"],
                 "avg_launch_us": scan_us}
 
     cpu = None
@@ -226,6 +229,78 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+def bench_chunk(spec, args):
+    """Multi-query chunk: K/V bridge of the new tokens, full layer, token top-k
+    and 64-token block selection, 3 sparse layers; tokens/s = Tq / chunk time."""
+    import numpy as np
+    import torch
+
+    from long_context_sparse_full_amd import hs2, synth
+
+    log(f"[bench] generating {spec.name}")
+    inp = synth.make_inputs(spec)
+
+    def dev(a):
+        t = torch.from_numpy(np.ascontiguousarray(a))
+        return (t.view(torch.bfloat16) if a.dtype == np.uint16 else t).cuda()
+
+    k, v, q = dev(inp.k), dev(inp.v), dev(inp.q_full)
+    qs = [dev(x) for x in inp.q_sparse]
+    hidden, w = dev(inp.hidden), dev(inp.w_kv)
+    B, Tq, Hq, D, Hkv, N = spec.B, spec.Tq, spec.Hq, spec.D, spec.Hkv, spec.N
+    T = spec.bridge[0]
+    out = torch.empty_like(q)
+    lse = torch.empty((B, Tq, Hq), dtype=torch.float32, device="cuda")
+    scores = torch.empty((B, Tq, Hkv, N), dtype=torch.float32, device="cuda")
+    ws_full = torch.empty(hs2.full_attn_scores_workspace(k, v, Tq, Hq), dtype=torch.uint8, device="cuda")
+    idx = torch.empty((B, Tq, Hkv, spec.max_sel), dtype=torch.int32, device="cuda")
+    cnt = torch.empty((B, Tq, Hkv), dtype=torch.int32, device="cuda")
+    bsel = spec.block_k * spec.block_size + spec.window
+    bidx = torch.empty((B, Tq, Hkv, bsel), dtype=torch.int32, device="cuda")
+    bcnt = torch.empty((B, Tq, Hkv), dtype=torch.int32, device="cuda")
+    ws_sel = torch.empty(hs2.select_workspace(B, Tq, Hkv, N), dtype=torch.uint8, device="cuda")
+    sp_out = [torch.empty_like(q) for _ in qs]
+
+    def step():
+        hs2.kv_bridge(hidden, w, k, v, 0, N - T)
+        hs2.full_attn_scores(k, v, q, spec.q_pos0, out=out, lse=lse, scores=scores, workspace=ws_full)
+        hs2.select_topk_window(scores, spec.q_pos0, spec.k, spec.window, max_sel=spec.max_sel, idx=idx, count=cnt,
+                               workspace=ws_sel)
+        hs2.select_topk_window(scores, spec.q_pos0, spec.block_k, spec.window, block_size=spec.block_size,
+                               max_sel=bsel, idx=bidx, count=bcnt, workspace=ws_sel)
+        for i, ql in enumerate(qs):
+            hs2.sparse_attn_gather(k, v, ql, idx, cnt, out=sp_out[i], want_lse=False)
+
+    steps = max(1, min(args.steps, 5))
+    for _ in range(max(1, args.warmup)):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    hs2.timing_reset()
+    hs2.timing_enable(True)
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    kernels = {}
+    for name in hs2.timing_kernel_names():
+        tot, n = hs2.timing_collect(name)
+        if n:
+            kernels[name] = {"avg_us": round(tot * 1e3 / n, 3), "launches_per_step": n / steps}
+    hs2.timing_enable(False)
+    hs2.timing_reset()
+    print(json.dumps({"metric": "tokens/s per 512-query chunk (bridge + full + token & block select + 3 sparse)",
+                      "value": round(Tq / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": steps,
+                      "ms_per_step": round(ms, 4), "higher_is_better": True, "dtype": "bf16/f32-acc",
+                      "data": "synthetic", "config": {"workload": spec.name, "Tq": Tq, "context": N},
+                      "kernels": kernels}), flush=True)
 
 
 if __name__ == "__main__":

@@ -162,7 +162,7 @@ struct WaveState {
 template <bool FP8, int D, bool WRITE_LOGITS>
 __device__ __forceinline__ void compute_tile(const RawTile<FP8, D>& R, const u32x4_t (&qf)[D / 32], float cs, int j0,
                                              int jlim, bool need_mask, int g4, uint16_t* lg, float* lgm,
-                                             WaveState<D>& S) {
+                                             int lgm_stride, WaveState<D>& S) {
   constexpr int NC = D / 32, VE = D / 16;
   u32x4_t kf[2][NC];
   uint32_t vd[8][VE / 2];
@@ -231,7 +231,7 @@ __device__ __forceinline__ void compute_tile(const RawTile<FP8, D>& R, const u32
         const uint32_t c2 = logit_code(tmax, x[hh][2]), c3 = logit_code(tmax, x[hh][3]);
         *(u32x2_t*)(lg + 16 * hh) = u32x2_t{c0 | (c1 << 16), c2 | (c3 << 16)};
       }
-      if (g4 == 0) lgm[j0 >> 5] = tmax;
+      if (g4 == 0) lgm[(j0 >> 5) * lgm_stride] = tmax;
     }
   }
 
@@ -385,7 +385,7 @@ __global__ void __launch_bounds__(WAVES * 64, HS2_SCAN_MIN_WAVES) scan_full(Scan
   if constexpr (WRITE_LOGITS) {
     if (row_ok) {
       lg_row = P.lg16 + ((int64_t)unit * P.rows + r) * P.npad + 4 * g4;
-      lgm_row = P.lgmax + ((int64_t)unit * P.rows + r) * (P.npad >> 5);
+      lgm_row = P.lgmax + (int64_t)unit * (P.npad >> 5) * P.rows + r;  // [unit][tile][row]
     }
   }
 
@@ -424,7 +424,7 @@ __global__ void __launch_bounds__(WAVES * 64, HS2_SCAN_MIN_WAVES) scan_full(Scan
   };
   auto compute = [&](const RawTile<FP8, D>& R, int j0) {
     compute_tile<FP8, D, WRITE_LOGITS>(R, qf, cs, j0, jlim, j0 + 31 > j_nomask, g4,
-                                       WRITE_LOGITS && lg_row ? lg_row + j0 : nullptr, lgm_row, S);
+                                       WRITE_LOGITS && lg_row ? lg_row + j0 : nullptr, lgm_row, P.rows, S);
   };
 
   RawTile<FP8, D> A, B;
@@ -500,7 +500,7 @@ __global__ void __launch_bounds__(WAVES * 64) scan_gather(ScanParams P) {
       load_tile<FP8, D, false>(R, kp, vp);
     };
     auto compute = [&](const RawTile<FP8, D>& R, int j0) {
-      compute_tile<FP8, D, false>(R, qf, cs, j0, jl, j0 + 31 > jl, g4, nullptr, nullptr, S);
+      compute_tile<FP8, D, false>(R, qf, cs, j0, jl, j0 + 31 > jl, g4, nullptr, nullptr, 0, S);
     };
     const int jend = base + nb;
     int j0 = base + wave * 32;
@@ -604,11 +604,11 @@ __global__ void __launch_bounds__(WAVES * 64) scan_gather_split(ScanParams P) {
     while (j0 < hi) {
       const int j1 = j0 + STEP;
       if (j1 < hi) load(B, j1);
-      compute_tile<FP8, D, false>(A, qf, cs, j0, jl, j0 + 31 > jl, g4, nullptr, nullptr, S);
+      compute_tile<FP8, D, false>(A, qf, cs, j0, jl, j0 + 31 > jl, g4, nullptr, nullptr, 0, S);
       if (j1 >= hi) break;
       const int j2 = j1 + STEP;
       if (j2 < hi) load(A, j2);
-      compute_tile<FP8, D, false>(B, qf, cs, j1, jl, j1 + 31 > jl, g4, nullptr, nullptr, S);
+      compute_tile<FP8, D, false>(B, qf, cs, j1, jl, j1 + 31 > jl, g4, nullptr, nullptr, 0, S);
       j0 = j2;
     }
   }
@@ -721,13 +721,13 @@ __global__ void __launch_bounds__(256) scan_f32(ScanParams P) {
       }
       if (r < R) {
         uint16_t* lg = P.lg16 + ((int64_t)unit * P.rows + r) * P.npad + j0;
-        float* lgm = P.lgmax + ((int64_t)unit * P.rows + r) * (P.npad >> 5) + (j0 >> 5);
+        float* lgm = P.lgmax + ((int64_t)unit * (P.npad >> 5) + (j0 >> 5)) * P.rows + r;  // [unit][tile][row]
 #pragma unroll
         for (int s = 0; s < 4; ++s)
           if (c + 16 * s < nt) lg[c + 16 * s] = (uint16_t)logit_code(s < 2 ? hm0 : hm1, x[s]);
         if (c == 0) {
           lgm[0] = hm0;
-          if (nt > 32) lgm[1] = hm1;
+          if (nt > 32) lgm[P.rows] = hm1;
         }
       }
     }
@@ -885,7 +885,7 @@ __global__ void __launch_bounds__(256) score(ScoreParams P) {
     if (j4 <= p) {
       for (int i = 0; i < P.G; ++i) {
         const int64_t row = (int64_t)unit * P.rows + tl * P.G + i;
-        const float c = P.lgmax[row * (P.npad >> 5) + (j4 >> 5)] - P.lse2[row];
+        const float c = P.lgmax[((int64_t)unit * (P.npad >> 5) + (j4 >> 5)) * P.rows + tl * P.G + i] - P.lse2[row];
         const u32x2_t w = *(const u32x2_t*)(P.lg16 + row * P.npad + j4);
         const uint32_t code[4] = {w.x & 0xffffu, w.x >> 16, w.y & 0xffffu, w.y >> 16};
 #pragma unroll

@@ -34,7 +34,7 @@ struct ScanParams {
   // per-head logits for the score pass, 16-bit log-domain code relative to the
   // row's maximum over each aligned 32-position tile (see the score kernel)
   uint16_t* lg16;    // [units][rows][npad]  code = round((tile max - x) * 4096), 65535 = below range
-  float* lgmax;      // [units][rows][npad/32] tile maxima (log2 domain)
+  float* lgmax;      // [units][npad/32][rows] tile maxima (log2 domain)
   int64_t npad;
   // gather (sparse layer) mode: one unit per (b, t, g), tpack = 1
   const int32_t* idx;

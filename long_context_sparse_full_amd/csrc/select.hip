@@ -383,8 +383,17 @@ __global__ void __launch_bounds__(256) sel_block_mass(SelectParams P) {
   const float* s = P.scores + (int64_t)u * P.N;
   const int lo = beta * P.block_size;
   const int hi = min(lo + P.block_size, ncand);
+  // ascending-position fp64 sum; loads issued 16 at a time
   double m = 0.0;
-  for (int j = lo; j < hi; ++j) m += (double)s[j];
+  int j = lo;
+  for (; j + 16 <= hi; j += 16) {
+    float v[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) v[e] = s[j + e];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) m += (double)v[e];
+  }
+  for (; j < hi; ++j) m += (double)s[j];
   P.bmass[(int64_t)u * P.nblocks_max + beta] = m;
 }
 

@@ -295,3 +295,30 @@ def test_strided_cache_view(hs2):
     o_or, l_or, s_or = oracle_full(inp, spec)
     gu.assert_close(gu.host(out), o_or, gu.O_TOL["bf16"], "out")
     gu.assert_scores(gu.host(sc), s_or, G=spec.G)
+
+
+@pytest.mark.parametrize("T,dm,Hkv,D", [(77, 192, 3, 64), (130, 512, 2, 128), (1, 64, 1, 64)])
+def test_kv_bridge_parity(hs2, T, dm, Hkv, D):
+    """K/V bridge into rows [pos0, pos0 + T) of batch 1 of a padded cache view:
+    ragged token count (partial 64-token tile), several column tiles; every
+    element within one bf16 step of the fp64 projection, nothing else touched."""
+    rng = np.random.default_rng(0x4252 + T)
+    h = synth.to_bf16_bits(rng.standard_normal((T, dm)).astype(np.float32))
+    w = synth.to_bf16_bits((rng.standard_normal((dm, 2 * Hkv * D)) / math.sqrt(dm)).astype(np.float32))
+    N, pos0 = T + 40, 23
+    big_k = torch.full((2, Hkv + 1, N + 9, D + 8), 7.0, dtype=torch.bfloat16, device="cuda")
+    big_v = torch.full_like(big_k, -3.0)
+    k, v = big_k[:, :Hkv, :N, :D], big_v[:, :Hkv, :N, :D]
+    hs2.kv_bridge(gu.dev(h), gu.dev(w), k, v, 1, pos0)
+    torch.cuda.synchronize()
+    Kr, Vr = oracle.kv_bridge(h, w, Hkv, D)
+    for name, big, ref, fill in (("K", big_k, Kr, 7.0), ("V", big_v, Vr, -3.0)):
+        got_all = gu.host(big)
+        got = got_all[1, :Hkv, pos0:pos0 + T, :D]
+        want = np.transpose(ref, (1, 0, 2))
+        _, e = np.frexp(want)
+        err = np.abs(got - want) - np.ldexp(1.0, e - 8)
+        assert np.all(err <= 1e-5), f"bridge {name}: worst {float(err.max()):.3e} beyond one bf16 step"
+        mask = np.ones(got_all.shape, bool)
+        mask[1, :Hkv, pos0:pos0 + T, :D] = False
+        assert np.all(got_all[mask] == fill), f"bridge {name} wrote outside its rows"
