@@ -78,6 +78,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="decode1m_fp8")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--split-gather", type=int, default=1, choices=(0, 1),
+                    help="sparse layers with the split-list gather (1, default) or one workgroup per (b, t, g) (0)")
+    ap.add_argument("--full-mode", type=int, default=0, choices=(0, 1),
+                    help="full layer as scan + merge + score kernels (0, default) or as one cooperative kernel (1)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (counter calibration)")
     args = ap.parse_args()
@@ -111,6 +115,7 @@ def main():
                 f"({2 * n / c0.elapsed_time(c1) / 1e6:.1f} GB/s)")
         print(json.dumps({"copy_probe_bytes": n, "ms": c0.elapsed_time(c1)}), flush=True)
         return
+    hs2.full_attn_set_mode(args.full_mode)
     spec = synth.config(args.config)
     if spec.Tq != 1:
         return bench_chunk(spec, args)
@@ -137,6 +142,8 @@ def main():
     ws_sel = torch.empty(hs2.select_workspace(B, Tq, Hkv, N, 1), dtype=torch.uint8, device="cuda")
     sp_out = [torch.empty_like(q) for _ in qs]
     sp_lse = [torch.empty((B, Tq, Hq), dtype=torch.float32, device="cuda") for _ in qs]
+    ws_gather = torch.zeros(max(hs2.sparse_attn_workspace(B, Tq, Hkv, D, spec.max_sel), 256), dtype=torch.uint8,
+                            device="cuda")  # zero-filled once; every call leaves its counters at zero
 
     def step():
         hs2.full_attn_scores(k, v, q, spec.q_pos0, k_scale=ks, v_scale=vs, out=out, lse=lse, scores=scores,
@@ -144,7 +151,11 @@ def main():
         hs2.select_topk_window(scores, spec.q_pos0, spec.k, spec.window, max_sel=spec.max_sel, idx=idx, count=cnt,
                                workspace=ws_sel)
         for i, ql in enumerate(qs):
-            hs2.sparse_attn_gather(k, v, ql, idx, cnt, k_scale=ks, v_scale=vs, out=sp_out[i], lse=sp_lse[i])
+            if args.split_gather:
+                hs2.sparse_attn_gather_ws(k, v, ql, idx, cnt, ws_gather, k_scale=ks, v_scale=vs, out=sp_out[i],
+                                          lse=sp_lse[i])
+            else:
+                hs2.sparse_attn_gather(k, v, ql, idx, cnt, k_scale=ks, v_scale=vs, out=sp_out[i], lse=sp_lse[i])
 
     for _ in range(args.warmup):
         step()
@@ -218,7 +229,7 @@ def main():
         "vs_baseline": None,
         "dtype": {"fp8": "fp8e4m3-kv/bf16-q/f32-acc", "bf16": "bf16/f32-acc", "f32": "f32"}[spec.kv_dtype],
         "data": "synthetic (seeded; planted needle keys)",
-        "config": {"workload": spec.name, "B": B, "context": N, "Tq": Tq, "q_heads": Hq, "kv_heads": Hkv,
+        "config": {"workload": spec.name, "full_layer": ["kernels", "cooperative"][args.full_mode], "B": B, "context": N, "Tq": Tq, "q_heads": Hq, "kv_heads": Hkv,
                    "head_dim": D, "kv_dtype": spec.kv_dtype, "top_k": spec.k, "window": spec.window,
                    "sparse_layers": spec.n_sparse},
         "hbm_gbps": round(ab["step"] / (ms_step * 1e-3) / 1e9, 1),

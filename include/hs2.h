@@ -93,7 +93,13 @@ const char* hs2_last_error(void);
  *                     for j <= p, and 0 for p < j < N.
  * Requires 0 <= q_pos0 and q_pos0 + Tq <= N.  Workspace: at least
  * hs2_full_attn_scores_workspace(kv, Tq, Hq) bytes, 256-byte aligned, device
- * memory; its contents on entry are ignored. */
+ * memory; its contents on entry are ignored.  Two calls that share one
+ * workspace must not run concurrently (different streams).
+ * Execution: a scan, a merge and a score kernel; or, selected with
+ * hs2_full_attn_set_mode(1) for bf16 and FP8 caches when the device can
+ * co-schedule one workgroup per compute unit for every (b, query pack, kv
+ * head), a single cooperative kernel (scan, device-wide barrier, output merge
+ * and scores).  Both compute the same quantities to the same bounds. */
 size_t hs2_full_attn_scores_workspace(const hs2_kv_desc* kv, int32_t Tq, int32_t Hq);
 int hs2_full_attn_scores(const hs2_kv_desc* kv, const void* q, hs2_dtype q_dtype, int32_t Tq,
                          int32_t Hq, int32_t q_pos0, float softmax_scale, void* out, float* lse,
@@ -173,6 +179,14 @@ int hs2_debug_e4m3fn_to_f32(const uint8_t* codes, float* out, int32_t n, hipStre
  * HBM read bandwidth this GPU actually sustains, the ceiling the scan is
  * compared with. */
 int hs2_debug_stream_read(const void* buf, size_t bytes, uint32_t* out, int32_t blocks, hipStream_t stream);
+
+/* Process-wide choice of the full-layer execution (a tuning and testing
+ * knob): mode 0 (default) the three-kernel sequence, mode 1 the single
+ * cooperative kernel where possible, mode 2 the cooperative kernel with its
+ * on-chip code store limited to one tile per workgroup (later tiles' codes go
+ * through the workspace, as they do at 1M context).  Returns
+ * HS2_ERR_INVALID_ARG for other values. */
+int hs2_full_attn_set_mode(int mode);
 
 /* Per-kernel timing with HIP events on the launch stream (off by default).
  * While enabled, every kernel launch of the library is bracketed by an event

@@ -4,9 +4,11 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <ctime>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -68,7 +70,7 @@ int check_q(const hs2_kv_desc* kv, const void* q, int q_dtype, int Tq, int Hq, c
 struct FullPlan {
   int tpack, n_tpacks, rows, units, nsplit, split_len;
   int64_t npad;
-  size_t off_ml, off_o, off_lse2, off_lg16, off_lgmax, total;
+  size_t off_ml, off_o, off_lse2, off_lg16, off_lgmax, off_flags, total;
 };
 
 // Position splits: about HS2_SCAN_TARGET_WGS workgroups in total (4 per CU on
@@ -100,8 +102,28 @@ FullPlan plan_full(const hs2_kv_desc* kv, int Tq, int Hq) {
   off = a256(off + (size_t)p.units * p.rows * (size_t)p.npad * sizeof(uint16_t));
   p.off_lgmax = off;
   off = a256(off + (size_t)p.units * p.rows * (size_t)(p.npad / 32) * sizeof(float));
+  p.off_flags = off;  // fused path: one grid-barrier word per workgroup (<= units * nsplit)
+  off = a256(off + (size_t)p.units * p.nsplit * sizeof(uint64_t));
   p.total = off;
   return p;
+}
+
+// Full-layer path selection (process-wide): 0 = the scan + combine + score
+// kernels, 1 = the fused cooperative kernel when the device can co-schedule
+// it, 2 = fused with LDS code storage cut to one tile per workgroup (every
+// later tile takes the global-buffer route; exercises that route at small
+// sizes).
+std::atomic<int> g_full_mode{0};
+
+// Grid-barrier epochs: unique per fused launch in this process, never 0.
+uint64_t next_epoch() {
+  static std::atomic<uint64_t> ctr{((uint64_t)(uintptr_t)&ctr << 16) ^ ((uint64_t)time(nullptr) << 40) ^
+                                   0x9e3779b97f4a7c15ull};
+  uint64_t e;
+  do {
+    e = ctr.fetch_add(1, std::memory_order_relaxed) + 1;
+  } while (e == 0);
+  return e;
 }
 
 struct SelPlan {
@@ -191,6 +213,12 @@ extern "C" {
 
 int hs2_abi_version(void) { return HS2_ABI_VERSION; }
 
+int hs2_full_attn_set_mode(int mode) {
+  if (mode < 0 || mode > 2) return fail(HS2_ERR_INVALID_ARG, "hs2_full_attn_set_mode: mode must be 0, 1 or 2");
+  g_full_mode.store(mode, std::memory_order_relaxed);
+  return HS2_OK;
+}
+
 const char* hs2_status_string(int status) {
   switch (status) {
     case HS2_OK: return "ok";
@@ -254,7 +282,34 @@ int hs2_full_attn_scores(const hs2_kv_desc* kv, const void* q, hs2_dtype q_dtype
   p.lg16 = at<uint16_t>(workspace, pl.off_lg16);
   p.lgmax = at<float>(workspace, pl.off_lgmax);
   p.npad = pl.npad;
-  hipError_t e = hs2::launch_scan(p, kv->dtype, false, true, stream);
+  hipError_t e;
+
+  // fused path: one workgroup per CU slot, nsplit of them per unit
+  const int mode = g_full_mode.load(std::memory_order_relaxed);
+  const int nwg = mode != 0 ? hs2::fused_max_workgroups(kv->dtype, kv->D) : 0;
+  if (nwg >= pl.units) {
+    const int W = hs2::fused_waves(kv->dtype, kv->D);
+    const int64_t step = 32 * W;
+    const int64_t su = std::max<int64_t>(1, std::min<int64_t>({nwg / pl.units, pl.nsplit, cdiv(kv->N, step)}));
+    const int64_t scan_steps = cdiv((int64_t)q_pos0 + Tq, step);  // steps covering [0, last query position]
+    const int64_t need = cdiv(scan_steps, su) * W;                 // tiles of the busiest workgroup
+    const int64_t fit = (hs2::kFusedLdsBytes - hs2::fused_merge_bytes(pl.rows, kv->D) - 256) /
+                        hs2::fused_slot_bytes(pl.rows);
+    hs2::ScanParams f = p;
+    f.nsplit = (int)su;
+    f.lds_slots = (int)std::min(need, mode == 2 ? (int64_t)1 : fit);
+    f.scores = scores;
+    f.out = out;
+    f.lse = lse;
+    f.flags = at<uint64_t>(workspace, pl.off_flags);
+    f.epoch = next_epoch();
+    e = hs2::launch_scan_fused(f, kv->dtype, pl.units, stream);
+    if (e == hipSuccess) return HS2_OK;
+    if (e != hipErrorNotSupported && e != hipErrorCooperativeLaunchTooLarge) return hip_fail(e, "fused full layer launch");
+    (void)hipGetLastError();  // the device declined the cooperative grid: use the kernel sequence
+  }
+
+  e = hs2::launch_scan(p, kv->dtype, false, true, stream);
   if (e != hipSuccess) return hip_fail(e, "full_scan launch");
 
   hs2::CombineParams c{};
@@ -441,6 +496,11 @@ int hs2_sparse_attn_gather_ws(const hs2_kv_desc* kv, const void* q, hs2_dtype q_
   const GatherPlan gp = plan_gather(units, max_sel, kv->D);
   if (!workspace || workspace_bytes < gp.total)
     return fail(HS2_ERR_WORKSPACE, "hs2_sparse_attn_gather_ws: workspace needs " + std::to_string(gp.total) + " bytes");
+  // the merging workgroup keeps one weight per (slice, row) in its 4-wave
+  // merge buffer (4 * 16 * (D + 1) floats); longer lists use the one-workgroup
+  // kernel, which needs no workspace
+  if ((int64_t)gp.nsplit * 16 > 4 * 16 * (kv->D + 1))
+    return hs2_sparse_attn_gather(kv, q, q_dtype, Tq, Hq, softmax_scale, idx, count, max_sel, out, lse, stream);
   if ((uintptr_t)workspace & 255)
     return fail(HS2_ERR_INVALID_ARG, "hs2_sparse_attn_gather_ws: workspace must be 256-byte aligned");
   hs2::ScanParams p{};

@@ -36,6 +36,15 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 #ifndef HS2_SCAN_INTERLEAVE
 #define HS2_SCAN_INTERLEAVE 1  // split s takes workgroup tiles s, s+nsplit, ... (all splits sweep together)
 #endif
+#ifndef HS2_FUSED_PLAIN_LAUNCH
+#define HS2_FUSED_PLAIN_LAUNCH 0  // timing experiments only: plain (non-cooperative) launch
+#endif
+#ifndef HS2_FUSED_ACQUIRE
+#define HS2_FUSED_ACQUIRE 0  // grid barrier ends with a device-scope acquire (cache invalidation)
+#endif
+#ifndef HS2_FUSED_SWIZZLE
+#define HS2_FUSED_SWIZZLE 0  // fused full layer: workgroup -> (unit, split) unit-fastest
+#endif
 #ifndef HS2_SCAN_MIN_WAVES
 #define HS2_SCAN_MIN_WAVES 1  // occupancy floor handed to the register allocator
 #endif
@@ -159,10 +168,14 @@ struct WaveState {
 // One 32-position tile: decode, QK^T, mask (only when the tile crosses the
 // causal / range limit), logits, online softmax, PV.  Positions of this lane's
 // logits: j0 + 16*hh + 4*g4 + ii.
-template <bool FP8, int D, bool WRITE_LOGITS>
+// RET_CODES: instead of storing, hand this lane's codes (positions
+// j0 + 4*g4 + {0..3} in cw[0..1], j0 + 16 + 4*g4 + {0..3} in cw[2..3], two per
+// dword) and the row's tile maximum back to the caller.
+template <bool FP8, int D, bool WRITE_LOGITS, bool RET_CODES = false>
 __device__ __forceinline__ void compute_tile(const RawTile<FP8, D>& R, const u32x4_t (&qf)[D / 32], float cs, int j0,
                                              int jlim, bool need_mask, int g4, uint16_t* lg, float* lgm,
-                                             int lgm_stride, WaveState<D>& S) {
+                                             int lgm_stride, WaveState<D>& S, uint32_t* cw = nullptr,
+                                             float* tmax_out = nullptr) {
   constexpr int NC = D / 32, VE = D / 16;
   u32x4_t kf[2][NC];
   uint32_t vd[8][VE / 2];
@@ -234,6 +247,14 @@ __device__ __forceinline__ void compute_tile(const RawTile<FP8, D>& R, const u32
       if (g4 == 0) lgm[(j0 >> 5) * lgm_stride] = tmax;
     }
   }
+  if constexpr (RET_CODES) {
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      cw[2 * hh] = logit_code(tmax, x[hh][0]) | (logit_code(tmax, x[hh][1]) << 16);
+      cw[2 * hh + 1] = logit_code(tmax, x[hh][2]) | (logit_code(tmax, x[hh][3]) << 16);
+    }
+    *tmax_out = tmax;
+  }
 
   // online softmax in the log2 domain
   const float m_new = fmaxf(S.m, tmax);
@@ -272,9 +293,18 @@ __device__ __forceinline__ void compute_tile(const RawTile<FP8, D>& R, const u32
   }
 }
 
+// Device-coherent scalar accesses for the per-workgroup partials exchanged
+// across the grid barrier (they bypass the non-coherent per-XCD caches).
+__device__ __forceinline__ void st_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_coherent(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Merge the waves of a workgroup through LDS and emit, per row, either the
 // split partial (max, sum, output) or the final normalised output and LSE.
-template <bool FP8, int D, bool GATHER, int WAVES>
+template <bool FP8, int D, bool GATHER, int WAVES, bool COHERENT = false>
 __device__ __forceinline__ void merge_and_store(const ScanParams& P, WaveState<D>& S, int unit, int split, int b, int g,
                                                 int wave, int r, int g4, float (*sm_m)[16], float (*sm_l)[16],
                                                 float (*sm_o)[16][D + 1]) {
@@ -315,10 +345,18 @@ __device__ __forceinline__ void merge_and_store(const ScanParams& P, WaveState<D
       if (d == 0 && P.lse) P.lse[orow] = (L > 0.f) ? (M + log2f(L)) * kLn2 : kNegInf;
     } else {
       const int64_t pbase = ((int64_t)unit * P.nsplit + split) * 16 + rr;
-      P.part_o[pbase * D + d] = O;
-      if (d == 0) {
-        P.part_ml[pbase * 2] = M;
-        P.part_ml[pbase * 2 + 1] = L;
+      if constexpr (COHERENT) {  // read by another workgroup of the same launch
+        st_coherent(P.part_o + pbase * D + d, O);
+        if (d == 0) {
+          st_coherent(P.part_ml + pbase * 2, M);
+          st_coherent(P.part_ml + pbase * 2 + 1, L);
+        }
+      } else {
+        P.part_o[pbase * D + d] = O;
+        if (d == 0) {
+          P.part_ml[pbase * 2] = M;
+          P.part_ml[pbase * 2 + 1] = L;
+        }
       }
     }
   }
@@ -441,6 +479,417 @@ __global__ void __launch_bounds__(WAVES * 64, HS2_SCAN_MIN_WAVES) scan_full(Scan
     j0 = j2;
   }
   merge_and_store<FP8, D, false, WAVES>(P, S, unit, split, b, g, wave, r, g4, sm_m, sm_l, sm_o);
+}
+
+// ---------------------------------------------------------------------------
+// Fused decode full layer: one cooperative launch, every workgroup resident
+// (one per CU).  Phase 1 is the scan above with 8 waves per workgroup; the
+// 16-bit logit codes and tile maxima of a workgroup's first lds_slots tiles
+// stay in LDS, later tiles go to the global code buffer.  A grid barrier
+// follows; phase 2 derives each head's (max, sum) from all workgroup partials,
+// merges the outputs (each workgroup a strided share of the unit's outputs)
+// and writes the scores of its own tiles from the codes.  Compared with the
+// scan + combine + score sequence this removes most scratch writes during the
+// streaming read and two launches; the arithmetic of every step is the same.
+// ---------------------------------------------------------------------------
+constexpr uint32_t kSpinLimit = 1u << 24;  // polls per word (~1 s) before a waiter gives up
+
+// Grid barrier: each workgroup publishes this launch's epoch in its own word,
+// then its threads poll every word until it carries the epoch.  The bounded
+// poll guarantees every wave exits even if the grid were not co-resident
+// (results would then be wrong, never a hang).  Only thread 0 fences at device
+// scope: the workgroup barrier before it has completed every wave's stores to
+// this XCD's L2, which the release fence writes back; its acquire fence
+// invalidates the caches every wave of the workgroup reads through.
+__device__ __forceinline__ void grid_barrier(uint64_t* flags, int nwg, uint64_t epoch, int wg) {
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __hip_atomic_store(flags + wg, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  for (int w = threadIdx.x; w < nwg; w += blockDim.x) {
+    for (uint32_t it = 0; it < kSpinLimit; ++it) {
+      if (__hip_atomic_load(flags + w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == epoch) break;
+      __builtin_amdgcn_s_sleep(2);
+    }
+  }
+#if HS2_FUSED_ACQUIRE
+  __syncthreads();
+  if (threadIdx.x == 0) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+#endif
+  __syncthreads();
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// Scores of one fused workgroup's tiles (every position of its steps over
+// [0, N)).  A thread takes OPT octets (8 consecutive positions of one tile)
+// per pass and loads every head's codes and tile maximum for all of them
+// before using any (LDS, or the global code buffer for slots past lds_slots),
+// so a pass costs one memory round trip.  Same per-head expression and head
+// order as the score kernel.
+template <int GM, int OPT, int WAVES>
+__device__ __forceinline__ void fused_scores(const ScanParams& P, const uint16_t* lcode, const float* lmax,
+                                             const float* red, int unit, int wu, int b, int g, int tp) {
+  constexpr int STEP = WAVES * 32, NT = WAVES * 64;
+  const int rows = P.rows, ns = P.nsplit;
+  const int wsteps = (P.N + STEP - 1) / STEP;  // workgroup steps covering [0, N)
+  const int my_steps = wu < wsteps ? (wsteps - wu + ns - 1) / ns : 0;
+  const int noct = my_steps * WAVES * 4;
+  for (int tl2 = 0; tl2 < P.tpack; ++tl2) {
+    const int t2 = tp * P.tpack + tl2;
+    if (t2 >= P.Tq) break;
+    const int p = P.q_pos0 + t2;
+    float* srow = P.scores + (((int64_t)b * P.Tq + t2) * P.Hkv + g) * P.N;
+    for (int base = 0; base < noct; base += NT * OPT) {
+      u32x4_t w[OPT][GM];
+      float c[OPT][GM];
+      int jo[OPT], j0o[OPT];
+      bool live[OPT];
+#pragma unroll
+      for (int o = 0; o < OPT; ++o) {
+        const int oi = base + o * NT + threadIdx.x;
+        const int slot = oi >> 2, o8 = (oi & 3) * 8;
+        const int k = slot / WAVES, wv = slot - k * WAVES;
+        j0o[o] = (wu + k * ns) * STEP + wv * 32;
+        jo[o] = j0o[o] + o8;
+        live[o] = oi < noct && jo[o] < P.N;
+        const bool scanned = live[o] && jo[o] <= p;  // such a tile was scanned in phase 1 under this slot
+        if (scanned && slot < P.lds_slots) {
+          const uint16_t* cb = lcode + ((size_t)slot * rows + tl2 * P.G) * 32 + o8;
+          const float* mb = lmax + slot * rows + tl2 * P.G;
+#pragma unroll
+          for (int i = 0; i < GM; ++i) {
+            w[o][i] = (i < P.G) ? *(const u32x4_t*)(cb + i * 32) : u32x4_t{0u, 0u, 0u, 0u};
+            c[o][i] = (i < P.G) ? mb[i] : 0.f;
+          }
+        } else if (scanned) {
+          const uint16_t* cb = P.lg16 + ((int64_t)unit * rows + tl2 * P.G) * P.npad + jo[o];
+          const float* mb = P.lgmax + ((int64_t)unit * (P.npad >> 5) + (j0o[o] >> 5)) * rows + tl2 * P.G;
+#pragma unroll
+          for (int i = 0; i < GM; ++i) {
+            w[o][i] = (i < P.G) ? *(const u32x4_t*)(cb + (int64_t)i * P.npad) : u32x4_t{0u, 0u, 0u, 0u};
+            c[o][i] = (i < P.G) ? mb[i] : 0.f;
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < GM; ++i) {
+            w[o][i] = u32x4_t{0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu};  // all codes "below range"
+            c[o][i] = 0.f;
+          }
+        }
+      }
+#pragma unroll
+      for (int o = 0; o < OPT; ++o) {
+        float sv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < GM; ++i) {
+          if (i < P.G) {
+            const float ci = c[o][i] - red[(tl2 * P.G + i) * 4 + 2];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const uint32_t code = (w[o][i][e >> 1] >> (16 * (e & 1))) & 0xffffu;
+              sv[e] += (code == 65535u) ? 0.f : exp2f(ci - (float)code * kCodeInv);
+            }
+          }
+        }
+        if (live[o]) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (jo[o] + e > p) sv[e] = 0.f;
+          float* dst = srow + jo[o];
+          if ((P.N & 3) == 0) {  // jo is a multiple of 8, so dst is 16-byte aligned
+            if (jo[o] + 8 <= P.N) {
+              *(f32x4_t*)dst = f32x4_t{sv[0], sv[1], sv[2], sv[3]};
+              *(f32x4_t*)(dst + 4) = f32x4_t{sv[4], sv[5], sv[6], sv[7]};
+            } else {
+              *(f32x4_t*)dst = f32x4_t{sv[0], sv[1], sv[2], sv[3]};
+            }
+          } else {
+            for (int e = 0; e < 8 && jo[o] + e < P.N; ++e) dst[e] = sv[e];
+          }
+        }
+      }
+    }
+  }
+}
+
+template <bool FP8, int D, int WAVES>
+__global__ void __launch_bounds__(WAVES * 64, 1) scan_fused(ScanParams P) {
+  constexpr int VE = D / 16, NC = D / 32, EB = FP8 ? 1 : 2;
+  constexpr int STEP = WAVES * 32;
+  constexpr int MS = D + 4;  // merge-buffer row stride (floats): O[0..D), m, l
+  extern __shared__ __align__(16) unsigned char lds[];
+  const int rows = P.rows;
+  float* mbuf = (float*)lds;                                          // [4][rows][MS]
+  float* red = (float*)(lds + fused_merge_bytes(rows, D));            // [16][4]: M, L, lse2
+  uint16_t* lcode = (uint16_t*)((unsigned char*)red + 256);           // [lds_slots][rows][32]
+  float* lmax = (float*)(lcode + (size_t)P.lds_slots * rows * 32);    // [lds_slots][rows]
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane & 15, g4 = lane >> 4;
+  const int wg = blockIdx.x;
+  const int ns = P.nsplit;
+#if HS2_FUSED_SWIZZLE
+  // consecutive workgroups (which land on different XCDs) take different units
+  const int units_all = gridDim.x / ns;
+  const int unit = wg % units_all, wu = wg / units_all;
+#else
+  const int unit = wg / ns, wu = wg - unit * ns;
+#endif
+  const int g = unit % P.Hkv;
+  const int tp = (unit / P.Hkv) % P.n_tpacks;
+  const int b = unit / (P.Hkv * P.n_tpacks);
+  const int tl = r / P.G;
+  const int t = tp * P.tpack + tl;
+  const bool row_ok = (r < rows) && (t < P.Tq);
+  const int h = g * P.G + (r - tl * P.G);
+
+  const int p_max = P.q_pos0 + min(tp * P.tpack + P.tpack, P.Tq) - 1;
+  const int j_end = p_max + 1;
+  const int jstride = ns * STEP;
+  const int jlim = min(row_ok ? P.q_pos0 + t : -1, j_end - 1);
+  const int j_nomask = min(P.q_pos0 + tp * P.tpack, j_end - 1);
+
+  u32x4_t qf[NC];
+  load_q<FP8, D>(qf, P, b, t, h, row_ok, g4);
+  const int64_t kvoff = ((int64_t)b * P.sb + (int64_t)g * P.sh) * EB;
+  const char* kb = (const char*)P.k + kvoff;
+  const char* vb = (const char*)P.v + kvoff;
+  const int64_t snb = P.sn * EB;
+  float cs = P.scale_log2;
+  if constexpr (FP8) cs *= P.k_scale[b * P.Hkv + g];
+  uint16_t* lg_row = P.lg16 + ((int64_t)unit * rows + (row_ok ? r : 0)) * P.npad + 4 * g4;
+  float* lgm_row = P.lgmax + (int64_t)unit * (P.npad >> 5) * rows + (row_ok ? r : 0);
+
+  uint32_t koff[2], voff[8];
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) koff[hh] = (uint32_t)((16 * hh + r) * snb) + 16u * g4;
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk)
+    voff[kk] = (uint32_t)((16 * (kk >> 2) + 4 * g4 + (kk & 3)) * snb) + (uint32_t)(VE * r * EB);
+
+  WaveState<D> S;
+  S.m = kNegInf;
+  S.l = 0.f;
+#pragma unroll
+  for (int dt = 0; dt < VE; ++dt) S.o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  auto load = [&](RawTile<FP8, D>& R, int j0) {
+    const char* kp[2];
+    const char* vp[8];
+    if (j0 + 31 <= p_max) {
+      const char* tk = kb + (int64_t)j0 * snb;
+      const char* tv = vb + (int64_t)j0 * snb;
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) kp[hh] = tk + koff[hh];
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) vp[kk] = tv + voff[kk];
+    } else {  // tail tile: rows past the last position repeat it
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) kp[hh] = kb + (int64_t)min(j0 + 16 * hh + r, p_max) * snb + 16 * g4;
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk)
+        vp[kk] = vb + (int64_t)min(j0 + 16 * (kk >> 2) + 4 * g4 + (kk & 3), p_max) * snb + VE * r * EB;
+    }
+    load_tile<FP8, D, false>(R, kp, vp);
+  };
+  // slot = this workgroup's tile ordinal (step * WAVES + wave)
+  auto compute = [&](const RawTile<FP8, D>& R, int j0, int slot) {
+    uint32_t cw[4];
+    float tm;
+    compute_tile<FP8, D, false, true>(R, qf, cs, j0, jlim, j0 + 31 > j_nomask, g4, nullptr, nullptr, 0, S, cw, &tm);
+    if (row_ok) {
+      if (slot < P.lds_slots) {
+        uint16_t* c = lcode + ((size_t)slot * rows + r) * 32 + 4 * g4;
+        *(u32x2_t*)c = u32x2_t{cw[0], cw[1]};
+        *(u32x2_t*)(c + 16) = u32x2_t{cw[2], cw[3]};
+        if (g4 == 0) lmax[slot * rows + r] = tm;
+      } else {
+        *(u32x2_t*)(lg_row + j0) = u32x2_t{cw[0], cw[1]};
+        *(u32x2_t*)(lg_row + j0 + 16) = u32x2_t{cw[2], cw[3]};
+        if (g4 == 0) lgm_row[(int64_t)(j0 >> 5) * rows] = tm;
+      }
+    }
+  };
+
+  // ---- phase 1: stream the cache; wave w takes tiles w, w + WAVES, ... of the
+  // workgroup's steps (slot k = tile k % WAVES of step k / WAVES).  With two
+  // waves per SIMD (waves w and w ^ 4), the one behind in tiles raises its
+  // issue priority, so the pair finishes together; the assignment of tiles to
+  // waves (and hence every result bit) does not depend on timing.
+  volatile int* prog = (volatile int*)red;  // prog[4 * w + 3]: tiles done by wave w (free pad of red)
+  int done = 0;
+  auto pace = [&]() {
+    if constexpr (WAVES == 8) {
+      ++done;
+      if (lane == 0) prog[4 * wave + 3] = done;
+      const int other = __builtin_amdgcn_readfirstlane(prog[4 * (wave ^ 4) + 3]);
+      if (other > done) {
+        __builtin_amdgcn_s_setprio(3);
+      } else {
+        __builtin_amdgcn_s_setprio(0);
+      }
+    }
+  };
+  if (threadIdx.x < WAVES) prog[4 * threadIdx.x + 3] = 0;
+  __syncthreads();
+  {
+    RawTile<FP8, D> A, B;
+    int j0 = wu * STEP + wave * 32;
+    int slot = wave;
+    if (j0 < j_end) load(A, j0);
+    while (j0 < j_end) {  // ping-pong: load tile n+1 while computing tile n
+      const int j1 = j0 + jstride;
+      if (j1 < j_end) load(B, j1);
+      compute(A, j0, slot);
+      pace();
+      if (j1 >= j_end) break;
+      const int j2 = j1 + jstride;
+      if (j2 < j_end) load(A, j2);
+      compute(B, j1, slot + WAVES);
+      pace();
+      j0 = j2;
+      slot += 2 * WAVES;
+    }
+    if constexpr (WAVES == 8) __builtin_amdgcn_s_setprio(0);
+  }
+
+  // ---- merge the waves (tree through a 4-slot LDS buffer), publish the partial
+  {
+    float lt = S.l;
+    lt += __shfl_xor(lt, 16);
+    lt += __shfl_xor(lt, 32);
+    S.l = lt;  // every lane of a row holds the row total
+  }
+#pragma unroll
+  for (int half = WAVES / 2; half >= 1; half >>= 1) {
+    __syncthreads();
+    if (wave >= half && wave < 2 * half && r < rows) {
+      float* sp = mbuf + ((size_t)(wave - half) * rows + r) * MS;
+#pragma unroll
+      for (int dt = 0; dt < VE; ++dt)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) sp[VE * (4 * g4 + ii) + dt] = S.o[dt][ii];
+      if (g4 == 0) {
+        sp[D] = S.m;
+        sp[D + 1] = S.l;
+      }
+    }
+    __syncthreads();
+    if (wave < half && r < rows) {
+      const float* sp = mbuf + ((size_t)wave * rows + r) * MS;
+      const float m2 = sp[D], l2 = sp[D + 1];
+      const float M = fmaxf(S.m, m2);
+      const float Ms = (M == kNegInf) ? 0.f : M;
+      const float a = exp2_fast(S.m - Ms), a2 = exp2_fast(m2 - Ms);
+      S.l = S.l * a + l2 * a2;
+#pragma unroll
+      for (int dt = 0; dt < VE; ++dt)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) S.o[dt][ii] = S.o[dt][ii] * a + sp[VE * (4 * g4 + ii) + dt] * a2;
+      S.m = M;
+    }
+  }
+  if (wave == 0 && r < rows) {
+    const int64_t pb = ((int64_t)unit * ns + wu) * 16 + r;
+#pragma unroll
+    for (int dt = 0; dt < VE; ++dt)
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) st_coherent(P.part_o + pb * D + VE * (4 * g4 + ii) + dt, S.o[dt][ii]);
+    if (g4 == 0) {
+      st_coherent(P.part_ml + pb * 2, S.m);
+      st_coherent(P.part_ml + pb * 2 + 1, S.l);
+    }
+  }
+
+  grid_barrier(P.flags, gridDim.x, P.epoch, wg);
+
+  // ---- phase 2a: (max, sum) per row of this unit over all its workgroups, one
+  // pass: lanes merge their partials in order, then a fixed butterfly
+  for (int rr = wave; rr < rows; rr += WAVES) {
+    const float* ml = P.part_ml + ((int64_t)unit * ns * 16 + rr) * 2;
+    float m = kNegInf, l = 0.f;
+    for (int sp = lane; sp < ns; sp += 64) {
+      const f32x2_t v = f32x2_t{ld_coherent(ml + sp * 32), ld_coherent(ml + sp * 32 + 1)};
+      const float M = fmaxf(m, v.x);
+      const float Ms = (M == kNegInf) ? 0.f : M;
+      l = l * exp2_fast(m - Ms) + v.y * exp2_fast(v.x - Ms);
+      m = M;
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      const float m2 = __shfl_xor(m, o), l2 = __shfl_xor(l, o);
+      const float M = fmaxf(m, m2);
+      const float Ms = (M == kNegInf) ? 0.f : M;
+      l = l * exp2_fast(m - Ms) + l2 * exp2_fast(m2 - Ms);
+      m = M;
+    }
+    if (lane == 0) {
+      red[rr * 4 + 0] = (m == kNegInf) ? 0.f : m;
+      red[rr * 4 + 1] = l;
+      red[rr * 4 + 2] = (l > 0.f) ? m + log2f(l) : kNegInf;
+    }
+  }
+  __syncthreads();
+  if (wu == 0 && P.lse && threadIdx.x < rows) {
+    const int rr = threadIdx.x;
+    const int t2 = tp * P.tpack + rr / P.G;
+    if (t2 < P.Tq) P.lse[((int64_t)b * P.Tq + t2) * P.Hq + g * P.G + rr % P.G] = red[rr * 4 + 2] * kLn2;
+  }
+
+  // ---- phase 2b: outputs e = wu, wu + ns, ... of the unit's rows x D, one
+  // group of lw lanes per output summing the weighted partials
+  {
+    int lw = 1;
+    while (lw < ns && lw < 64) lw <<= 1;
+    const int opw = 64 / lw;
+    const int total = rows * D;
+    const int n_out = (total - wu + ns - 1) / ns;
+    const int sl = lane & (lw - 1);
+    for (int base = wave * opw; base < n_out; base += WAVES * opw) {
+      const int i = base + lane / lw;
+      const bool ok = i < n_out;
+      const int e = ok ? wu + i * ns : 0;
+      const int rr = e / D, d = e - rr * D;
+      float acc = 0.f;
+      if (ok) {
+        const float Ms = red[rr * 4];
+        for (int sp = sl; sp < ns; sp += lw) {
+          const int64_t pb = ((int64_t)unit * ns + sp) * 16 + rr;
+          acc += ld_coherent(P.part_o + pb * D + d) * exp2_fast(ld_coherent(P.part_ml + pb * 2) - Ms);
+        }
+      }
+      for (int o = lw / 2; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
+      if (ok && sl == 0) {
+        const int t2 = tp * P.tpack + rr / P.G;
+        if (t2 < P.Tq) {
+          const float L = red[rr * 4 + 1];
+          float o = (L > 0.f) ? acc / L : 0.f;
+          if constexpr (FP8) o *= P.v_scale[b * P.Hkv + g];
+          const int64_t orow = ((int64_t)b * P.Tq + t2) * P.Hq + g * P.G + rr % P.G;
+          ((__bf16*)P.out)[orow * D + d] = (__bf16)o;
+        }
+      }
+    }
+  }
+
+  // ---- phase 2c: scores of this workgroup's tiles, 0 past each query's position
+  if (P.G <= 8) {
+    fused_scores<8, 4, WAVES>(P, lcode, lmax, red, unit, wu, b, g, tp);
+  } else {
+    fused_scores<16, 2, WAVES>(P, lcode, lmax, red, unit, wu, b, g, tp);
+  }
 }
 
 constexpr int kGatherIdxCap = 2048;  // index-list entries staged in LDS at a time
@@ -612,27 +1061,61 @@ __global__ void __launch_bounds__(WAVES * 64) scan_gather_split(ScanParams P) {
       j0 = j2;
     }
   }
-  // partial of this slice (rows = G heads), same layout as the full-layer splits
-  merge_and_store<FP8, D, false, WAVES>(P, S, unit, split, b, g, wave, r, g4, sm_m, sm_l, sm_o);
+  // partial of this slice (rows = G heads), same layout as the full-layer
+  // splits, stored device-coherent for the merging workgroup
+  merge_and_store<FP8, D, false, WAVES, true>(P, S, unit, split, b, g, wave, r, g4, sm_m, sm_l, sm_o);
 
-  __threadfence();  // release the partial device-wide
+  // arrival: the workgroup barrier completes every wave's stores, one release
+  // fence orders them before the counter update
   __syncthreads();
-  if (threadIdx.x == 0) s_last = (atomicAdd(&P.gcounter[unit], 1) == P.nsplit - 1);
+  if (threadIdx.x == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    s_last = (atomicAdd(&P.gcounter[unit], 1) == P.nsplit - 1);
+  }
   __syncthreads();
   if (!s_last) return;
-  __threadfence();  // acquire the other slices' partials
+  // the last slice merges all partials (device-coherent loads): weights first,
+  // then every output element with its loads issued together
+  float* sw = &sm_o[0][0][0];  // [nsplit][16] weights 2^(m_s - M), reusing the merge buffer
+  for (int e = threadIdx.x; e < P.nsplit * 16; e += WAVES * 64) {
+    const int sp = e >> 4, rr = e & 15;
+    const int64_t pb = ((int64_t)unit * P.nsplit + sp) * 16 + rr;
+    sw[e] = rr < P.G ? ld_coherent(P.part_ml + pb * 2) : kNegInf;
+  }
+  __syncthreads();
+  if (threadIdx.x < P.G) {
+    const int rr = threadIdx.x;
+    float M = kNegInf;
+    for (int sp = 0; sp < P.nsplit; ++sp) M = fmaxf(M, sw[sp * 16 + rr]);
+    const float Ms = (M == kNegInf) ? 0.f : M;
+    float L = 0.f;
+    for (int sp = 0; sp < P.nsplit; ++sp) {
+      const int64_t pb = ((int64_t)unit * P.nsplit + sp) * 16 + rr;
+      const float w = exp2_fast(sw[sp * 16 + rr] - Ms);
+      L += ld_coherent(P.part_ml + pb * 2 + 1) * w;
+      sw[sp * 16 + rr] = w;
+    }
+    sm_m[0][rr] = M;
+    sm_l[0][rr] = L;
+  }
+  __syncthreads();
   for (int e = threadIdx.x; e < P.G * D; e += WAVES * 64) {
     const int rr = e / D, d = e - rr * D;
-    const int64_t pb = (int64_t)unit * P.nsplit * 16 + rr;
-    float M = kNegInf;
-    for (int sp = 0; sp < P.nsplit; ++sp) M = fmaxf(M, P.part_ml[(pb + sp * 16) * 2]);
-    const float Ms = (M == kNegInf) ? 0.f : M;
-    float L = 0.f, O = 0.f;
-    for (int sp = 0; sp < P.nsplit; ++sp) {
-      const float f = exp2_fast(P.part_ml[(pb + sp * 16) * 2] - Ms);
-      L += P.part_ml[(pb + sp * 16) * 2 + 1] * f;
-      O += P.part_o[(pb + sp * 16) * D + d] * f;
+    const float* po = P.part_o + ((int64_t)unit * P.nsplit * 16 + rr) * D + d;
+    const int64_t sst = (int64_t)16 * D;
+    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+    int sp = 0;
+    for (; sp + 3 < P.nsplit; sp += 4) {
+      const float v0 = ld_coherent(po + sp * sst), v1 = ld_coherent(po + (sp + 1) * sst);
+      const float v2 = ld_coherent(po + (sp + 2) * sst), v3 = ld_coherent(po + (sp + 3) * sst);
+      a0 += sw[sp * 16 + rr] * v0;
+      a1 += sw[(sp + 1) * 16 + rr] * v1;
+      a2 += sw[(sp + 2) * 16 + rr] * v2;
+      a3 += sw[(sp + 3) * 16 + rr] * v3;
     }
+    for (; sp < P.nsplit; ++sp) a0 += sw[sp * 16 + rr] * ld_coherent(po + sp * sst);
+    const float O = (a0 + a1) + (a2 + a3);
+    const float M = sm_m[0][rr], L = sm_l[0][rr];
     float o = (L > 0.f) ? O / L : 0.f;
     if constexpr (FP8) o *= P.v_scale[b * P.Hkv + g];
     const int64_t orow = ((int64_t)b * P.Tq + t) * P.Hq + g * P.G + rr;
@@ -939,6 +1422,35 @@ hipError_t go_full(const ScanParams& p, dim3 grid, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <bool FP8, int D>
+hipError_t go_fused(const ScanParams& p, int units, hipStream_t s) {
+  constexpr int W = fused_waves(FP8 ? HS2_FP8_E4M3FN : HS2_BF16, D);
+  const void* fn = (const void*)&scan_fused<FP8, D, W>;
+  const size_t lds = (size_t)fused_merge_bytes(p.rows, D) + 256 + (size_t)p.lds_slots * fused_slot_bytes(p.rows);
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kFusedLdsBytes);
+  if (e != hipSuccess) return e;
+  TimedLaunch tl("full_scan", s);
+  ScanParams arg = p;
+  void* args[] = {(void*)&arg};
+#if HS2_FUSED_PLAIN_LAUNCH
+  (void)args;
+  hipLaunchKernelGGL((scan_fused<FP8, D, W>), dim3(units * p.nsplit), dim3(W * 64), lds, s, arg);
+  return hipGetLastError();
+#else
+  return hipLaunchCooperativeKernel(fn, dim3(units * p.nsplit), dim3(W * 64), args, (unsigned)lds, s);
+#endif
+}
+
+template <bool FP8, int D>
+int fused_occupancy() {
+  int nb = 0;
+  constexpr int W = fused_waves(FP8 ? HS2_FP8_E4M3FN : HS2_BF16, D);
+  const void* fn = (const void*)&scan_fused<FP8, D, W>;
+  if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kFusedLdsBytes) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, W * 64, kFusedLdsBytes) != hipSuccess) return 0;
+  return nb;
+}
+
 template <bool FP8, int D, int WAVES>
 hipError_t go_gather_split(const ScanParams& p, dim3 grid, hipStream_t s) {
   TimedLaunch tl("sparse_gather", s);
@@ -1001,6 +1513,41 @@ hipError_t launch_gather_split(const ScanParams& p, int kv_dtype, hipStream_t s)
   if (kv_dtype == HS2_FP8_E4M3FN)
     return p.D == 128 ? go_gather_split<true, 128, 4>(p, grid, s) : go_gather_split<true, 64, 4>(p, grid, s);
   return p.D == 128 ? go_gather_split<false, 128, 4>(p, grid, s) : go_gather_split<false, 64, 4>(p, grid, s);
+}
+
+hipError_t launch_scan_fused(const ScanParams& p, int kv_dtype, int units, hipStream_t s) {
+  if (kv_dtype == HS2_F32) return hipErrorNotSupported;
+  if (kv_dtype == HS2_FP8_E4M3FN) return p.D == 128 ? go_fused<true, 128>(p, units, s) : go_fused<true, 64>(p, units, s);
+  return p.D == 128 ? go_fused<false, 128>(p, units, s) : go_fused<false, 64>(p, units, s);
+}
+
+// Co-resident fused workgroups on the current device (CUs x workgroups per
+// CU), cached per device; 0 when cooperative launch is unavailable.
+int fused_max_workgroups(int kv_dtype, int D) {
+  if (kv_dtype == HS2_F32) return 0;
+  constexpr int kMaxDev = 64;
+  static int cache[kMaxDev][4];
+  static bool ready[kMaxDev][4];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return 0;
+  const int which = (kv_dtype == HS2_FP8_E4M3FN ? 2 : 0) + (D == 128 ? 1 : 0);
+  if (ready[dev][which]) return cache[dev][which];
+  int cus = 0, coop = 0;
+  int n = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+      hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) == hipSuccess && coop) {
+    int occ = 0;
+    switch (which) {
+      case 0: occ = fused_occupancy<false, 64>(); break;
+      case 1: occ = fused_occupancy<false, 128>(); break;
+      case 2: occ = fused_occupancy<true, 64>(); break;
+      default: occ = fused_occupancy<true, 128>(); break;
+    }
+    n = cus * occ;
+  }
+  cache[dev][which] = n;
+  ready[dev][which] = true;
+  return n;
 }
 
 hipError_t launch_combine(const CombineParams& p, int units, hipStream_t s) {

@@ -43,7 +43,26 @@ struct ScanParams {
   void* out;         // [B, Tq, Hq, D] in q's element type
   float* lse;        // [B, Tq, Hq] natural log (nullable)
   int32_t* gcounter; // split gather: per-(b, t, g) arrival counters (zero between calls)
+  // fused full layer (one cooperative launch): nsplit workgroups per unit
+  float* scores;       // [B, Tq, Hkv, N]
+  int lds_slots;       // tiles per workgroup whose codes stay in LDS; later tiles use lg16/lgmax
+  uint64_t* flags;     // [units * nsplit] grid-barrier arrival words
+  uint64_t epoch;      // this launch's arrival value (unique per launch)
 };
+
+// Fused decode full layer: workgroup shape and LDS plan shared by the launcher
+// and the host planner.
+// 8 waves (2 per SIMD) per workgroup; 4 for the bf16 D=128 scan, whose two
+// in-flight 16 KiB tiles per wave need the whole register file of a SIMD.
+#ifndef HS2_FUSED_FP8_WAVES
+#define HS2_FUSED_FP8_WAVES 8
+#endif
+__host__ __device__ constexpr int fused_waves(int kv_dtype, int D) {
+  return (kv_dtype == HS2_BF16 && D == 128) ? 4 : (kv_dtype == HS2_FP8_E4M3FN ? HS2_FUSED_FP8_WAVES : 8);
+}
+constexpr int kFusedLdsBytes = 160 * 1024;
+__host__ __device__ inline int fused_merge_bytes(int rows, int D) { return 4 * rows * (D + 4) * 4; }
+__host__ __device__ inline int fused_slot_bytes(int rows) { return rows * (32 * 2 + 4); }
 
 struct CombineParams {
   const float* part_ml;
@@ -86,6 +105,11 @@ struct SelectParams {
 // launchers (return hipError_t of the launch)
 hipError_t launch_scan(const ScanParams& p, int kv_dtype, bool gather, bool write_logits, hipStream_t s);
 hipError_t launch_gather_split(const ScanParams& p, int kv_dtype, hipStream_t s);
+// Cooperative launch of the fused full layer (scan, grid barrier, combine,
+// scores).  Returns hipErrorNotSupported when the device cannot co-schedule
+// the grid; the caller then uses the multi-kernel path.
+hipError_t launch_scan_fused(const ScanParams& p, int kv_dtype, int units, hipStream_t s);
+int fused_max_workgroups(int kv_dtype, int D);  // co-resident workgroups, 0 if unavailable
 hipError_t launch_combine(const CombineParams& p, int units, hipStream_t s);
 hipError_t launch_score(const ScoreParams& p, int units, hipStream_t s);
 hipError_t launch_select(const SelectParams& p, hipStream_t s);

@@ -65,6 +65,7 @@ _bridge = _sig("hs2_kv_bridge", ctypes.c_int, [_vp, _i32, _i32, _vp, _KVP, _i32,
 _dbg_e4m3 = _sig("hs2_debug_e4m3fn_to_f32", ctypes.c_int, [_vp, _vp, _i32, _vp])
 _dbg_stream = _sig("hs2_debug_stream_read", ctypes.c_int, [_vp, _sz, _vp, _i32, _vp])
 _t_enable = _sig("hs2_timing_enable", ctypes.c_int, [ctypes.c_int])
+_set_mode = _sig("hs2_full_attn_set_mode", ctypes.c_int, [ctypes.c_int])
 _t_reset = _sig("hs2_timing_reset", ctypes.c_int, [])
 _t_collect = _sig("hs2_timing_collect", ctypes.c_int,
                   [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int32)])
@@ -74,7 +75,7 @@ EXPORTED = [
     "hs2_abi_version", "hs2_status_string", "hs2_last_error", "hs2_full_attn_scores_workspace",
     "hs2_full_attn_scores", "hs2_select_workspace", "hs2_select_workspace_for", "hs2_select_topk_window",
     "hs2_sparse_attn_gather", "hs2_sparse_attn_workspace", "hs2_sparse_attn_gather_ws", "hs2_kv_bridge", "hs2_debug_e4m3fn_to_f32", "hs2_debug_stream_read",
-    "hs2_timing_enable",
+    "hs2_full_attn_set_mode", "hs2_timing_enable",
     "hs2_timing_reset", "hs2_timing_collect", "hs2_timing_kernel_name",
 ]
 
@@ -241,6 +242,12 @@ def debug_stream_read(buf: torch.Tensor, blocks: int = 2048) -> torch.Tensor:
     _check(_dbg_stream(buf.data_ptr(), nbytes - nbytes % 16, out.data_ptr(), blocks, _stream()),
            "hs2_debug_stream_read")
     return out
+
+
+def full_attn_set_mode(mode: int):
+    """0: scan + merge + score kernels (default); 1: single cooperative full-layer kernel where the device
+    allows it; 2: cooperative kernel with its LDS code store limited to one tile per workgroup."""
+    _check(_set_mode(int(mode)), "hs2_full_attn_set_mode")
 
 
 def timing_enable(on: bool = True):

@@ -31,15 +31,27 @@ def test_decode_config_end_to_end(hs2, name):
     gu.log(f"[{name}] generating inputs")
     inp = synth.make_inputs(spec)
     blk = gu.DeviceBlock(inp)
-    gu.log(f"[{name}] GPU block")
-    res = gu.run_block(hs2, blk, spec)
+    runs = {}
+    for mode in (0, 1):  # three-kernel full layer, then the cooperative kernel
+        gu.log(f"[{name}] GPU block, full-layer mode {mode}")
+        hs2.full_attn_set_mode(mode)
+        try:
+            runs[mode] = gu.run_block(hs2, blk, spec)
+        finally:
+            hs2.full_attn_set_mode(0)
     del blk
     torch.cuda.empty_cache()
-    kv = spec.kv_dtype
 
     gu.log(f"[{name}] oracle full layer ({spec.B * spec.Tq * spec.Hkv} units)")
     o_or, l_or, s_or = oracle.full_attn_scores(inp.q_full, inp.k, inp.v, spec.q_pos0, k_scale=inp.k_scale,
                                                v_scale=inp.v_scale)
+    for mode, res in runs.items():
+        gu.log(f"[{name}] checking full-layer mode {mode}")
+        check_run(name, spec, inp, res, o_or, l_or, s_or)
+
+
+def check_run(name, spec, inp, res, o_or, l_or, s_or):
+    kv = spec.kv_dtype
     e_o = gu.assert_close(res["out"], o_or, gu.O_TOL[kv], "full out")
     e_l = gu.assert_close(res["lse"], l_or, gu.LSE_TOL[kv], "full lse")
     e_s = gu.assert_scores(res["scores"], s_or, G=spec.G)

@@ -59,11 +59,20 @@ CASES = [
 ]
 
 
+@pytest.fixture(params=[0, 1, 2], ids=["kernels", "fused", "fused-spill"])
+def full_mode(hs2, request):
+    """Full-layer execution: the three-kernel sequence, the cooperative kernel,
+    and the cooperative kernel with its codes routed through the workspace."""
+    hs2.full_attn_set_mode(request.param)
+    yield request.param
+    hs2.full_attn_set_mode(0)
+
+
 @pytest.mark.parametrize("case", CASES, ids=lambda c: "-".join(map(str, c)))
-def test_full_layer_parity(hs2, case):
+def test_full_layer_parity(hs2, case, full_mode):
     kv, D, G, Hkv, B, N, Tq = case
     spec = small_spec(kv, D=D, G=G, Hkv=Hkv, B=B, N=N, Tq=Tq, needles=min(8, max(0, N - 16)))
-    gu.log(f"full-layer parity {case}")
+    gu.log(f"full-layer parity {case} mode {full_mode}")
     inp = synth.make_inputs(spec, seed=1234)
     blk = gu.DeviceBlock(inp)
     out, lse, sc = hs2.full_attn_scores(blk.k, blk.v, blk.q, spec.q_pos0, k_scale=blk.ks, v_scale=blk.vs)
@@ -75,7 +84,7 @@ def test_full_layer_parity(hs2, case):
     gu.log(f"  max|dO|={e_o:.2e} max|dLSE|={e_l:.2e} max rel dS={e_s:.2e}")
 
 
-def test_full_layer_q_pos0_before_end(hs2):
+def test_full_layer_q_pos0_before_end(hs2, full_mode):
     spec = small_spec("bf16", N=900, Tq=2)
     inp = synth.make_inputs(spec, seed=7)
     blk = gu.DeviceBlock(inp)
@@ -268,7 +277,7 @@ def test_planted_gap_indices_bit_exact(hs2, kv):
             assert sel == set(inp.needle_pos[b, g].tolist())
 
 
-def test_full_path_bitwise_deterministic(hs2):
+def test_full_path_bitwise_deterministic(hs2, full_mode):
     spec = small_spec("fp8", B=1, N=20000, Hkv=4)
     inp = synth.make_inputs(spec, seed=8)
     blk = gu.DeviceBlock(inp)
@@ -280,7 +289,7 @@ def test_full_path_bitwise_deterministic(hs2):
         assert np.array_equal(oa, ob) and np.array_equal(la, lb)
 
 
-def test_strided_cache_view(hs2):
+def test_strided_cache_view(hs2, full_mode):
     """A cache that is a view into a longer buffer (padded rows, extra heads)."""
     spec = small_spec("bf16", B=1, N=700, Hkv=2)
     inp = synth.make_inputs(spec, seed=21)
@@ -322,3 +331,27 @@ def test_kv_bridge_parity(hs2, T, dm, Hkv, D):
         mask = np.ones(got_all.shape, bool)
         mask[1, :Hkv, pos0:pos0 + T, :D] = False
         assert np.all(got_all[mask] == fill), f"bridge {name} wrote outside its rows"
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_fused_and_kernel_paths_agree(hs2, kv):
+    """The cooperative kernel and the three-kernel sequence compute the same
+    layer: outputs within the parity bound of each other, scores within the
+    score bound, at a size with several splits and a ragged tail."""
+    spec = small_spec(kv, B=2, N=12345, Hkv=4)
+    inp = synth.make_inputs(spec, seed=77)
+    blk = gu.DeviceBlock(inp)
+    res = {}
+    for mode in (0, 1, 2):
+        hs2.full_attn_set_mode(mode)
+        out, lse, sc = hs2.full_attn_scores(blk.k, blk.v, blk.q, spec.q_pos0, k_scale=blk.ks, v_scale=blk.vs)
+        torch.cuda.synchronize()
+        res[mode] = (gu.host(out), gu.host(lse), gu.host(sc))
+    hs2.full_attn_set_mode(0)
+    o_or, l_or, s_or = oracle_full(inp, spec)
+    for mode, (o, l, sc) in res.items():
+        gu.assert_close(o, o_or, gu.O_TOL[kv], f"out mode {mode}")
+        gu.assert_close(l, l_or, gu.LSE_TOL[kv], f"lse mode {mode}")
+        gu.assert_scores(sc, s_or, f"scores mode {mode}", G=spec.G)
+    # the spill route stores the same codes as the on-chip route
+    assert np.array_equal(res[1][2], res[2][2]) and np.array_equal(res[1][0], res[2][0])
