@@ -30,6 +30,7 @@ if ROOT not in sys.path:
 
 METRIC = "µs/decode-step (full scan + top-k + 3 sparse layers) & HBM GB/s at 1M ctx"
 HBM_PEAK_GBPS = 8000.0
+MFMA_BF16_TFLOPS = 2500.0
 SCAN_SRCS = [os.path.join(ROOT, "long_context_sparse_full_amd", "csrc", f)
              for f in ("attn.hip", "hs2_internal.hpp", "api.cpp")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "full_scan_decode1m_fp8.md")
@@ -307,11 +308,27 @@ def bench_chunk(spec, args):
             kernels[name] = {"avg_us": round(tot * 1e3 / n, 3), "launches_per_step": n / steps}
     hs2.timing_enable(False)
     hs2.timing_reset()
+    # dense MFMA work of the chunk's full layer: query token t sees p_t + 1 positions;
+    # QK^T and PV are 2 * Hq * D flops per (t, position) each; the score pass redoes QK^T
+    visible = sum(spec.q_pos0 + t + 1 for t in range(Tq))
+    flops_full = 2 * 2 * visible * Hq * D
+    flops_score = 2 * visible * Hq * D
+    roofline = None
+    if "chunk_full" in kernels:
+        us = kernels["chunk_full"]["avg_us"]
+        tf = flops_full / (us * 1e-6) / 1e12
+        roofline = {"kernel": "chunk_full", "bound": "mfma", "achieved": round(tf, 1), "peak": MFMA_BF16_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_TFLOPS, 4), "traffic": None,
+                    "algorithmic_flops_per_launch": flops_full, "avg_launch_us": us}
+        if "chunk_score" in kernels:
+            us2 = kernels["chunk_score"]["avg_us"]
+            roofline["score_pass"] = {"achieved": round(flops_score / (us2 * 1e-6) / 1e12, 1),
+                                      "algorithmic_flops_per_launch": flops_score, "avg_launch_us": us2}
     print(json.dumps({"metric": "tokens/s per 512-query chunk (bridge + full + token & block select + 3 sparse)",
                       "value": round(Tq / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": steps,
                       "ms_per_step": round(ms, 4), "higher_is_better": True, "dtype": "bf16/f32-acc",
                       "data": "synthetic", "config": {"workload": spec.name, "Tq": Tq, "context": N},
-                      "kernels": kernels}), flush=True)
+                      "kernels": kernels, "roofline": roofline}), flush=True)
 
 
 if __name__ == "__main__":

@@ -68,6 +68,7 @@ int check_q(const hs2_kv_desc* kv, const void* q, int q_dtype, int Tq, int Hq, c
 }
 
 struct FullPlan {
+  bool chunk;  // multi-query chunk kernels (MFMA pass + merge + score recompute)
   int tpack, n_tpacks, rows, units, nsplit, split_len;
   int64_t npad;
   size_t off_ml, off_o, off_lse2, off_lg16, off_lgmax, off_flags, total;
@@ -86,9 +87,18 @@ FullPlan plan_full(const hs2_kv_desc* kv, int Tq, int Hq) {
   p.n_tpacks = (int)cdiv(Tq, p.tpack);
   p.rows = p.tpack * G;
   p.units = kv->B * p.n_tpacks * kv->Hkv;
-  const int64_t per_unit = std::max<int64_t>(1, HS2_SCAN_TARGET_WGS / p.units);
-  const int64_t quantum = f32 ? 64 : 256;
-  p.split_len = (int)rup(cdiv(kv->N, per_unit), quantum);
+  const bool g_pow2 = G == 4 || G == 8 || G == 16;  // the chunk score pass sums heads in 4-row lane groups
+  const int rg = hs2::chunk_rg(kv->dtype, kv->D);
+  p.chunk = !f32 && g_pow2 && p.n_tpacks >= rg;
+  if (p.chunk) {  // work items (b, block of rg packs, g) x position splits, about 1024 in all
+    const int64_t items = (int64_t)kv->B * cdiv(p.n_tpacks, rg) * kv->Hkv;
+    const int64_t per_item = std::max<int64_t>(1, HS2_SCAN_TARGET_WGS / items);
+    p.split_len = (int)rup(cdiv(kv->N, per_item), 32 * hs2::kChunkWaves);
+  } else {
+    const int64_t per_unit = std::max<int64_t>(1, HS2_SCAN_TARGET_WGS / p.units);
+    const int64_t quantum = f32 ? 64 : 256;
+    p.split_len = (int)rup(cdiv(kv->N, per_unit), quantum);
+  }
   p.nsplit = (int)cdiv(kv->N, p.split_len);
   p.npad = rup(kv->N, 64);
   size_t off = 0;
@@ -98,10 +108,11 @@ FullPlan plan_full(const hs2_kv_desc* kv, int Tq, int Hq) {
   off = a256(off + (size_t)p.units * p.nsplit * 16 * kv->D * sizeof(float));
   p.off_lse2 = off;
   off = a256(off + (size_t)p.units * p.rows * sizeof(float));
+  const size_t code_units = p.chunk ? 0 : (size_t)p.units;  // the chunk path stores no logit codes
   p.off_lg16 = off;
-  off = a256(off + (size_t)p.units * p.rows * (size_t)p.npad * sizeof(uint16_t));
+  off = a256(off + code_units * p.rows * (size_t)p.npad * sizeof(uint16_t));
   p.off_lgmax = off;
-  off = a256(off + (size_t)p.units * p.rows * (size_t)(p.npad / 32) * sizeof(float));
+  off = a256(off + code_units * p.rows * (size_t)(p.npad / 32) * sizeof(float));
   p.off_flags = off;  // fused path: one grid-barrier word per workgroup (<= units * nsplit)
   off = a256(off + (size_t)p.units * p.nsplit * sizeof(uint64_t));
   p.total = off;
@@ -167,7 +178,7 @@ int hip_fail(hipError_t e, const char* what) {
 const char* const kKernelNames[] = {"full_scan",   "combine",     "score",        "select_init",
                                     "select_hist", "select_emit",
                                     "select_block_mass", "select_block_pick", "sparse_gather", "kv_bridge", "stream_read",
-                                    nullptr};
+                                    "chunk_full",  "chunk_score", nullptr};
 
 std::mutex g_tmu;
 bool g_timing = false;
@@ -285,6 +296,32 @@ int hs2_full_attn_scores(const hs2_kv_desc* kv, const void* q, hs2_dtype q_dtype
   hipError_t e;
 
   // fused path: one workgroup per CU slot, nsplit of them per unit
+  if (pl.chunk) {  // many query tokens: MFMA pass -> merge -> score recompute
+    hs2::CombineParams c{};
+    c.part_ml = p.part_ml;
+    c.part_o = p.part_o;
+    c.nsplit = pl.nsplit;
+    c.rows = pl.rows;
+    c.tpack = pl.tpack;
+    c.n_tpacks = pl.n_tpacks;
+    c.G = p.G;
+    c.Hkv = kv->Hkv;
+    c.Hq = Hq;
+    c.Tq = Tq;
+    c.D = kv->D;
+    c.v_scale = kv->dtype == HS2_FP8_E4M3FN ? kv->v_scale : nullptr;
+    c.out_bf16 = q_dtype == HS2_BF16;
+    c.out = out;
+    c.lse = lse;
+    c.lse2 = at<float>(workspace, pl.off_lse2);
+    if ((e = hs2::launch_chunk_full(p, kv->dtype, stream)) != hipSuccess) return hip_fail(e, "chunk_full launch");
+    if ((e = hs2::launch_combine(c, pl.units, stream)) != hipSuccess) return hip_fail(e, "combine launch");
+    p.lse2_in = c.lse2;
+    p.scores = scores;
+    if ((e = hs2::launch_chunk_score(p, kv->dtype, stream)) != hipSuccess) return hip_fail(e, "chunk_score launch");
+    return HS2_OK;
+  }
+
   const int mode = g_full_mode.load(std::memory_order_relaxed);
   const int nwg = mode != 0 ? hs2::fused_max_workgroups(kv->dtype, kv->D) : 0;
   if (nwg >= pl.units) {

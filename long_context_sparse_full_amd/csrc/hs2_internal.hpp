@@ -48,7 +48,17 @@ struct ScanParams {
   int lds_slots;       // tiles per workgroup whose codes stay in LDS; later tiles use lg16/lgmax
   uint64_t* flags;     // [units * nsplit] grid-barrier arrival words
   uint64_t epoch;      // this launch's arrival value (unique per launch)
+  // multi-query chunk path: log2-domain LSE per (unit, row) from the merge,
+  // read by the score pass
+  const float* lse2_in;
 };
+
+// Multi-query chunk path: one wave holds chunk_rg() groups of 16 query rows
+// (tpack tokens x G heads each), kChunkWaves waves split a position range.
+// Three groups for a bf16 D=128 cache (its tile buffers are twice the size),
+// four otherwise, so queries, accumulators and two tiles stay in registers.
+__host__ __device__ constexpr int chunk_rg(int kv_dtype, int D) { return (kv_dtype == HS2_BF16 && D == 128) ? 3 : 4; }
+constexpr int kChunkWaves = 4;
 
 // Fused decode full layer: workgroup shape and LDS plan shared by the launcher
 // and the host planner.
@@ -110,6 +120,10 @@ hipError_t launch_gather_split(const ScanParams& p, int kv_dtype, hipStream_t s)
 // the grid; the caller then uses the multi-kernel path.
 hipError_t launch_scan_fused(const ScanParams& p, int kv_dtype, int units, hipStream_t s);
 int fused_max_workgroups(int kv_dtype, int D);  // co-resident workgroups, 0 if unavailable
+// Multi-query chunk full layer: MFMA pass writing split partials (then
+// launch_combine), and the score pass recomputing QK^T against the merged LSE.
+hipError_t launch_chunk_full(const ScanParams& p, int kv_dtype, hipStream_t s);
+hipError_t launch_chunk_score(const ScanParams& p, int kv_dtype, hipStream_t s);
 hipError_t launch_combine(const CombineParams& p, int units, hipStream_t s);
 hipError_t launch_score(const ScoreParams& p, int units, hipStream_t s);
 hipError_t launch_select(const SelectParams& p, hipStream_t s);

@@ -56,6 +56,12 @@ CASES = [
     ("fp8", 128, 8, 2, 2, 1000, 1),
     ("fp8", 128, 8, 4, 1, 5000, 1),
     ("fp8", 64, 4, 2, 1, 513, 4),
+    # many query tokens per kv head: the multi-query chunk kernels (ragged blocks and tails)
+    ("bf16", 128, 8, 2, 1, 3000, 37),
+    ("fp8", 128, 8, 2, 1, 2500, 20),
+    ("bf16", 64, 4, 2, 2, 1500, 50),
+    ("bf16", 128, 16, 1, 1, 700, 9),
+    ("fp8", 64, 8, 1, 1, 333, 24),
 ]
 
 
@@ -96,6 +102,24 @@ def test_full_layer_q_pos0_before_end(hs2, full_mode):
     gu.assert_close(gu.host(lse), l_or, gu.LSE_TOL["bf16"], "lse")
     gu.assert_scores(gu.host(sc), s_or, G=spec.G)
     assert np.all(gu.host(sc)[..., qp + 2:] == 0.0)
+
+
+def test_chunk_q_pos0_before_end(hs2):
+    """Multi-query chunk with the queries in the middle of a longer cache: every
+    score past each query's position is exactly 0."""
+    spec = small_spec("bf16", N=1700, Tq=24)
+    inp = synth.make_inputs(spec, seed=9)
+    blk = gu.DeviceBlock(inp)
+    qp = 901
+    out, lse, sc = hs2.full_attn_scores(blk.k, blk.v, blk.q, qp)
+    torch.cuda.synchronize()
+    o_or, l_or, s_or = oracle.full_attn_scores(inp.q_full, inp.k, inp.v, qp)
+    gu.assert_close(gu.host(out), o_or, gu.O_TOL["bf16"], "out")
+    gu.assert_close(gu.host(lse), l_or, gu.LSE_TOL["bf16"], "lse")
+    sc = gu.host(sc)
+    gu.assert_scores(sc, s_or, G=spec.G)
+    for t in range(spec.Tq):
+        assert np.all(sc[:, t, :, qp + t + 1:] == 0.0), t
 
 
 # ---------------------------------------------------------------- selection
