@@ -31,8 +31,7 @@ if ROOT not in sys.path:
 METRIC = "µs/decode-step (full scan + top-k + 3 sparse layers) & HBM GB/s at 1M ctx"
 HBM_PEAK_GBPS = 8000.0
 MFMA_BF16_TFLOPS = 2500.0
-SCAN_SRCS = [os.path.join(ROOT, "long_context_sparse_full_amd", "csrc", f)
-             for f in ("attn.hip", "hs2_internal.hpp", "api.cpp")]
+SCAN_SRCS = [os.path.join(ROOT, "long_context_sparse_full_amd", "csrc", f) for f in ("attn.hip", "hs2_internal.hpp")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "full_scan_decode1m_fp8.md")
 TRAFFIC_WORKLOAD = "decode1m_fp8"
 
@@ -195,6 +194,8 @@ def main():
                 "traffic": traffic_entry(spec.name), "algorithmic_bytes_per_launch": ab["scan_kv"],
                 "avg_launch_us": scan_us}
 
+    gather_tp = gather_throughput(hs2, synth, k, v, ks, vs, spec, args) if spec.name == TRAFFIC_WORKLOAD else None
+
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
@@ -238,9 +239,51 @@ def main():
         "wall_us_per_step": round(wall_ms * 1e3, 2),
         "kernels": kernels,
         "roofline": roofline,
+        "gather_throughput": gather_tp,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+def gather_throughput(hs2, synth, k, v, ks, vs, spec, args):
+    """The sparse-layer gather against the same 1M-position FP8 cache with B_q
+    independent query streams, each with its own list of 1152 random rows per
+    kv head (the decode step has B_q = 1).  Bytes = gathered K + V rows."""
+    import numpy as np
+    import torch
+    res = []
+    Hkv, D, N = spec.Hkv, spec.D, spec.N
+    rows = spec.max_sel
+    for bq in (1, 8, 64, 256):
+        q = (torch.randn(1, bq, spec.Hq, D, device="cuda") * spec.q_std).to(torch.bfloat16)
+        idx_np, c_np = synth.random_index_lists(0x6A7 + bq, bq * Hkv, N, rows)
+        idx = torch.from_numpy(idx_np.reshape(1, bq, Hkv, -1)).cuda()
+        cnt = torch.from_numpy(c_np.reshape(1, bq, Hkv)).cuda()
+        ws = torch.zeros(max(hs2.sparse_attn_workspace(1, bq, Hkv, D, rows), 256), dtype=torch.uint8, device="cuda")
+        out = torch.empty_like(q)
+        entry = {"B_q": bq, "rows_per_list": rows}
+        for name, call in (("single", lambda: hs2.sparse_attn_gather(k, v, q, idx, cnt, k_scale=ks, v_scale=vs,
+                                                                        out=out, want_lse=False)),
+                           ("split", lambda: hs2.sparse_attn_gather_ws(k, v, q, idx, cnt, ws, k_scale=ks,
+                                                                       v_scale=vs, out=out, want_lse=False))):
+            for _ in range(3):
+                call()
+            torch.cuda.synchronize()
+            hs2.timing_reset()
+            hs2.timing_enable(True)
+            for _ in range(args.steps):
+                call()
+            torch.cuda.synchronize()
+            tot, n = hs2.timing_collect("sparse_gather")
+            hs2.timing_enable(False)
+            hs2.timing_reset()
+            us = tot * 1e3 / n
+            gb = bq * Hkv * rows * 2 * D * esize(spec.kv_dtype)
+            entry[name] = {"avg_us": round(us, 3), "GBps": round(gb / (us * 1e-6) / 1e9, 1),
+                           "frac": round(gb / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4), "bytes": gb}
+        res.append(entry)
+    log(f"[bench] gather throughput: {json.dumps(res)}")
+    return res
 
 
 def bench_chunk(spec, args):

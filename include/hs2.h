@@ -150,7 +150,8 @@ int hs2_sparse_attn_gather(const hs2_kv_desc* kv, const void* q, hs2_dtype q_dty
  * bytes) holds per-(b, t, g) arrival counters that MUST be zero before the
  * first call on it (e.g. zero-filled at allocation); every call leaves them
  * zero again.  Calls that share a workspace must be ordered on one stream.
- * fp32 caches take the workspace-free path. */
+ * fp32 caches, and calls with 64 or more (b, t, g) lists (where one
+ * workgroup per list already fills the GPU), take the workspace-free path. */
 size_t hs2_sparse_attn_workspace(int32_t B, int32_t Tq, int32_t Hkv, int32_t D, int32_t max_sel);
 int hs2_sparse_attn_gather_ws(const hs2_kv_desc* kv, const void* q, hs2_dtype q_dtype, int32_t Tq,
                               int32_t Hq, float softmax_scale, const int32_t* idx,

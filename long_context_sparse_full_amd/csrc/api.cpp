@@ -490,6 +490,8 @@ struct GatherPlan {
   size_t off_ml, off_o, off_cnt, total;
 };
 // slices of 128 list slots (one 32-row tile per wave of a 4-wave workgroup)
+constexpr int kSplitGatherMaxUnits = 64;
+
 GatherPlan plan_gather(int units, int max_sel, int D) {
   GatherPlan g{};
   g.slice = 128;
@@ -533,10 +535,12 @@ int hs2_sparse_attn_gather_ws(const hs2_kv_desc* kv, const void* q, hs2_dtype q_
   const GatherPlan gp = plan_gather(units, max_sel, kv->D);
   if (!workspace || workspace_bytes < gp.total)
     return fail(HS2_ERR_WORKSPACE, "hs2_sparse_attn_gather_ws: workspace needs " + std::to_string(gp.total) + " bytes");
-  // the merging workgroup keeps one weight per (slice, row) in its 4-wave
-  // merge buffer (4 * 16 * (D + 1) floats); longer lists use the one-workgroup
-  // kernel, which needs no workspace
-  if ((int64_t)gp.nsplit * 16 > 4 * 16 * (kv->D + 1))
+  // The split form pays off only while one workgroup per (b, t, g) leaves the
+  // GPU mostly idle; from 64 units on, the one-workgroup kernel is used (it
+  // needs no workspace).  Also the merging workgroup keeps one weight per
+  // (slice, row) in its 4-wave merge buffer (4 * 16 * (D + 1) floats), so
+  // longer lists take the one-workgroup kernel too.
+  if (units >= kSplitGatherMaxUnits || (int64_t)gp.nsplit * 16 > 4 * 16 * (kv->D + 1))
     return hs2_sparse_attn_gather(kv, q, q_dtype, Tq, Hq, softmax_scale, idx, count, max_sel, out, lse, stream);
   if ((uintptr_t)workspace & 255)
     return fail(HS2_ERR_INVALID_ARG, "hs2_sparse_attn_gather_ws: workspace must be 256-byte aligned");
