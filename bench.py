@@ -81,7 +81,10 @@ def main():
     ap.add_argument("--split-gather", type=int, default=1, choices=(0, 1),
                     help="sparse layers with the split-list gather (1, default) or one workgroup per (b, t, g) (0)")
     ap.add_argument("--full-mode", type=int, default=0, choices=(0, 1),
-                    help="full layer as scan + merge + score kernels (0, default) or as one cooperative kernel (1)")
+                    help="full-layer execution (hs2_full_attn_set_mode): 0 automatic (default), 1 cooperative "
+                         "kernel wherever possible (with the selection inside)")
+    ap.add_argument("--topk-call", type=int, default=1, choices=(0, 1),
+                    help="full layer + selection through hs2_full_attn_topk (1, default) or two calls (0)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (counter calibration)")
     args = ap.parse_args()
@@ -145,11 +148,17 @@ def main():
     ws_gather = torch.zeros(max(hs2.sparse_attn_workspace(B, Tq, Hkv, D, spec.max_sel), 256), dtype=torch.uint8,
                             device="cuda")  # zero-filled once; every call leaves its counters at zero
 
+    ws_topk = torch.empty(hs2.full_attn_topk_workspace(k, v, Tq, Hq), dtype=torch.uint8, device="cuda")
+
     def step():
-        hs2.full_attn_scores(k, v, q, spec.q_pos0, k_scale=ks, v_scale=vs, out=out, lse=lse, scores=scores,
-                             workspace=ws_full)
-        hs2.select_topk_window(scores, spec.q_pos0, spec.k, spec.window, max_sel=spec.max_sel, idx=idx, count=cnt,
-                               workspace=ws_sel)
+        if args.topk_call:
+            hs2.full_attn_topk(k, v, q, spec.q_pos0, spec.k, spec.window, max_sel=spec.max_sel, k_scale=ks,
+                               v_scale=vs, out=out, lse=lse, scores=scores, idx=idx, count=cnt, workspace=ws_topk)
+        else:
+            hs2.full_attn_scores(k, v, q, spec.q_pos0, k_scale=ks, v_scale=vs, out=out, lse=lse, scores=scores,
+                                 workspace=ws_full)
+            hs2.select_topk_window(scores, spec.q_pos0, spec.k, spec.window, max_sel=spec.max_sel, idx=idx,
+                                   count=cnt, workspace=ws_sel)
         for i, ql in enumerate(qs):
             if args.split_gather:
                 hs2.sparse_attn_gather_ws(k, v, ql, idx, cnt, ws_gather, k_scale=ks, v_scale=vs, out=sp_out[i],
@@ -231,7 +240,8 @@ def main():
         "vs_baseline": None,
         "dtype": {"fp8": "fp8e4m3-kv/bf16-q/f32-acc", "bf16": "bf16/f32-acc", "f32": "f32"}[spec.kv_dtype],
         "data": "synthetic (seeded; planted needle keys)",
-        "config": {"workload": spec.name, "full_layer": ["kernels", "cooperative"][args.full_mode], "B": B, "context": N, "Tq": Tq, "q_heads": Hq, "kv_heads": Hkv,
+        "config": {"workload": spec.name, "full_layer": {0: "auto", 1: "cooperative", 3: "kernels"}[args.full_mode],
+                   "full_and_select": "one call" if args.topk_call else "two calls", "B": B, "context": N, "Tq": Tq, "q_heads": Hq, "kv_heads": Hkv,
                    "head_dim": D, "kv_dtype": spec.kv_dtype, "top_k": spec.k, "window": spec.window,
                    "sparse_layers": spec.n_sparse},
         "hbm_gbps": round(ab["step"] / (ms_step * 1e-3) / 1e9, 1),

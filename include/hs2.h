@@ -181,11 +181,29 @@ int hs2_debug_e4m3fn_to_f32(const uint8_t* codes, float* out, int32_t n, hipStre
  * compared with. */
 int hs2_debug_stream_read(const void* buf, size_t bytes, uint32_t* out, int32_t blocks, hipStream_t stream);
 
+/* Full layer and token selection in one call: the results of
+ * hs2_full_attn_scores followed by hs2_select_topk_window with block_size 1
+ * (same layouts, rules and requirements; both passages above).  With
+ * hs2_full_attn_set_mode(1), for bf16 and FP8 caches with one query token
+ * (Tq = 1) and at most 8 query heads per kv head, when the device co-schedules
+ * one workgroup per compute unit for every (b, kv head) and each workgroup's
+ * scores fit its registers, both run inside one cooperative kernel: the
+ * scores stay on chip for the selection (they are still written to
+ * `scores`).  Otherwise the two calls run in sequence.  Workspace: at least
+ * hs2_full_attn_topk_workspace() bytes, 256-byte aligned. */
+size_t hs2_full_attn_topk_workspace(const hs2_kv_desc* kv, int32_t Tq, int32_t Hq);
+int hs2_full_attn_topk(const hs2_kv_desc* kv, const void* q, hs2_dtype q_dtype, int32_t Tq, int32_t Hq,
+                       int32_t q_pos0, float softmax_scale, void* out, float* lse, float* scores, int32_t k,
+                       int32_t window, int32_t* idx, int32_t* count, int32_t max_sel, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream);
+
 /* Process-wide choice of the full-layer execution (a tuning and testing
- * knob): mode 0 (default) the three-kernel sequence, mode 1 the single
- * cooperative kernel where possible, mode 2 the cooperative kernel with its
- * on-chip code store limited to one tile per workgroup (later tiles' codes go
- * through the workspace, as they do at 1M context).  Returns
+ * knob): mode 0 (default) automatic -- the three-kernel full layer (and for
+ * hs2_full_attn_topk the select kernels after it); mode 1 the single
+ * cooperative kernel wherever possible (with the selection inside for
+ * hs2_full_attn_topk); mode 2 as 1 with the on-chip code store limited to one
+ * tile per workgroup (later tiles' codes go through the workspace, as they
+ * do at 1M context); mode 3 never the cooperative kernel.  Returns
  * HS2_ERR_INVALID_ARG for other values. */
 int hs2_full_attn_set_mode(int mode);
 

@@ -113,17 +113,21 @@ FullPlan plan_full(const hs2_kv_desc* kv, int Tq, int Hq) {
   off = a256(off + code_units * p.rows * (size_t)p.npad * sizeof(uint16_t));
   p.off_lgmax = off;
   off = a256(off + code_units * p.rows * (size_t)(p.npad / 32) * sizeof(float));
-  p.off_flags = off;  // fused path: one grid-barrier word per workgroup (<= units * nsplit)
-  off = a256(off + (size_t)p.units * p.nsplit * sizeof(uint64_t));
+  p.off_flags = off;  // fused path: per grid barrier one word per workgroup (<= units * nsplit)
+  off = a256(off + (size_t)hs2::kFusedBarriers * p.units * p.nsplit * sizeof(uint64_t));
   p.total = off;
   return p;
 }
 
-// Full-layer path selection (process-wide): 0 = the scan + combine + score
-// kernels, 1 = the fused cooperative kernel when the device can co-schedule
-// it, 2 = fused with LDS code storage cut to one tile per workgroup (every
-// later tile takes the global-buffer route; exercises that route at small
-// sizes).
+// Full-layer path selection (process-wide):
+//   0 = automatic: the scan + combine + score kernels, then (for
+//       hs2_full_attn_topk) the select kernels -- the fastest form measured at
+//       1M context, where the cooperative launch and the selection's grid
+//       barriers cost more than the scratch traffic they save;
+//   1 = the fused cooperative kernel wherever the device can co-schedule it;
+//   2 = as 1 with LDS code storage cut to one tile per workgroup (every later
+//       tile takes the global-buffer route; exercises it at small sizes);
+//   3 = never fused.
 std::atomic<int> g_full_mode{0};
 
 // Grid-barrier epochs: unique per fused launch in this process, never 0.
@@ -225,7 +229,7 @@ extern "C" {
 int hs2_abi_version(void) { return HS2_ABI_VERSION; }
 
 int hs2_full_attn_set_mode(int mode) {
-  if (mode < 0 || mode > 2) return fail(HS2_ERR_INVALID_ARG, "hs2_full_attn_set_mode: mode must be 0, 1 or 2");
+  if (mode < 0 || mode > 3) return fail(HS2_ERR_INVALID_ARG, "hs2_full_attn_set_mode: mode must be 0..3");
   g_full_mode.store(mode, std::memory_order_relaxed);
   return HS2_OK;
 }
@@ -248,9 +252,44 @@ size_t hs2_full_attn_scores_workspace(const hs2_kv_desc* kv, int32_t Tq, int32_t
   return plan_full(kv, Tq, Hq).total;
 }
 
+}  // extern "C"
+
+namespace {
+// Selection folded into the fused full layer (hs2_full_attn_topk).
+struct SelFuse {
+  int32_t k, window, max_sel;
+  int32_t* idx;
+  int32_t* count;
+  void* ws;  // fused-selection region: histograms, then step counts
+  bool done = false;
+};
+
+size_t sel_fuse_hist_bytes(int units) { return a256((size_t)units * 3 * hs2::kHistBins * sizeof(int32_t)); }
+int sel_fuse_nsteps(int N) { return (int)cdiv(N, 128); }  // the smallest workgroup step (4 waves)
+size_t sel_fuse_bytes(int units, int N) {
+  return sel_fuse_hist_bytes(units) + a256((size_t)units * sel_fuse_nsteps(N) * 2 * sizeof(int32_t));
+}
+
+int full_layer(const hs2_kv_desc* kv, const void* q, hs2_dtype q_dtype, int32_t Tq, int32_t Hq, int32_t q_pos0,
+               float softmax_scale, void* out, float* lse, float* scores, void* workspace, size_t workspace_bytes,
+               hipStream_t stream, SelFuse* sel);
+}  // namespace
+
+extern "C" {
+
 int hs2_full_attn_scores(const hs2_kv_desc* kv, const void* q, hs2_dtype q_dtype, int32_t Tq, int32_t Hq,
                          int32_t q_pos0, float softmax_scale, void* out, float* lse, float* scores, void* workspace,
                          size_t workspace_bytes, hipStream_t stream) {
+  return full_layer(kv, q, q_dtype, Tq, Hq, q_pos0, softmax_scale, out, lse, scores, workspace, workspace_bytes,
+                    stream, nullptr);
+}
+
+}  // extern "C"
+
+namespace {
+int full_layer(const hs2_kv_desc* kv, const void* q, hs2_dtype q_dtype, int32_t Tq, int32_t Hq, int32_t q_pos0,
+               float softmax_scale, void* out, float* lse, float* scores, void* workspace, size_t workspace_bytes,
+               hipStream_t stream, SelFuse* sel) {
   int st = check_kv(kv, "hs2_full_attn_scores");
   if (st) return st;
   if ((st = check_q(kv, q, q_dtype, Tq, Hq, "hs2_full_attn_scores"))) return st;
@@ -323,7 +362,8 @@ int hs2_full_attn_scores(const hs2_kv_desc* kv, const void* q, hs2_dtype q_dtype
   }
 
   const int mode = g_full_mode.load(std::memory_order_relaxed);
-  const int nwg = mode != 0 ? hs2::fused_max_workgroups(kv->dtype, kv->D) : 0;
+  const bool want_fused = mode == 1 || mode == 2;
+  const int nwg = want_fused ? hs2::fused_max_workgroups(kv->dtype, kv->D) : 0;
   if (nwg >= pl.units) {
     const int W = hs2::fused_waves(kv->dtype, kv->D);
     const int64_t step = 32 * W;
@@ -332,6 +372,10 @@ int hs2_full_attn_scores(const hs2_kv_desc* kv, const void* q, hs2_dtype q_dtype
     const int64_t need = cdiv(scan_steps, su) * W;                 // tiles of the busiest workgroup
     const int64_t fit = (hs2::kFusedLdsBytes - hs2::fused_merge_bytes(pl.rows, kv->D) - 256) /
                         hs2::fused_slot_bytes(pl.rows);
+    // the selection keeps every score of a workgroup in registers: 4 octets per
+    // thread, i.e. at most kFusedSelMaxSteps steps per workgroup over [0, N)
+    const int64_t my_steps = cdiv(cdiv(kv->N, step), su);
+    const bool fuse_sel = sel != nullptr && pl.tpack == 1 && p.G <= 8 && my_steps <= hs2::kFusedSelMaxSteps;
     hs2::ScanParams f = p;
     f.nsplit = (int)su;
     f.lds_slots = (int)std::min(need, mode == 2 ? (int64_t)1 : fit);
@@ -340,10 +384,26 @@ int hs2_full_attn_scores(const hs2_kv_desc* kv, const void* q, hs2_dtype q_dtype
     f.lse = lse;
     f.flags = at<uint64_t>(workspace, pl.off_flags);
     f.epoch = next_epoch();
-    e = hs2::launch_scan_fused(f, kv->dtype, pl.units, stream);
-    if (e == hipSuccess) return HS2_OK;
-    if (e != hipErrorNotSupported && e != hipErrorCooperativeLaunchTooLarge) return hip_fail(e, "fused full layer launch");
-    (void)hipGetLastError();  // the device declined the cooperative grid: use the kernel sequence
+    if (fuse_sel) {
+      f.sel_k = sel->k;
+      f.sel_window = sel->window;
+      f.sel_nsteps = (int)cdiv(kv->N, step);
+      f.sel_hist = static_cast<int32_t*>(sel->ws);
+      f.sel_stepcnt = at<int32_t>(sel->ws, sel_fuse_hist_bytes(pl.units));
+      f.idx = sel->idx;
+      f.count = sel->count;
+      f.max_sel = sel->max_sel;
+    }
+    if (sel == nullptr || fuse_sel) {
+      e = hs2::launch_scan_fused(f, kv->dtype, pl.units, stream);
+      if (e == hipSuccess) {
+        if (sel) sel->done = fuse_sel;
+        return HS2_OK;
+      }
+      if (e != hipErrorNotSupported && e != hipErrorCooperativeLaunchTooLarge)
+        return hip_fail(e, "fused full layer launch");
+      (void)hipGetLastError();  // the device declined the cooperative grid: use the kernel sequence
+    }
   }
 
   e = hs2::launch_scan(p, kv->dtype, false, true, stream);
@@ -384,6 +444,44 @@ int hs2_full_attn_scores(const hs2_kv_desc* kv, const void* q, hs2_dtype q_dtype
   s.scores = scores;
   if ((e = hs2::launch_score(s, pl.units, stream)) != hipSuccess) return hip_fail(e, "score launch");
   return HS2_OK;
+}
+}  // namespace
+
+extern "C" {
+
+size_t hs2_full_attn_topk_workspace(const hs2_kv_desc* kv, int32_t Tq, int32_t Hq) {
+  if (!kv || kv->B <= 0 || kv->Hkv <= 0 || kv->N <= 0 || kv->D <= 0 || Tq <= 0 || Hq <= 0 || Hq % kv->Hkv) return 0;
+  const FullPlan pl = plan_full(kv, Tq, Hq);
+  const size_t sel = plan_select(kv->B, Tq, kv->Hkv, kv->N, 1).total;
+  return pl.total + std::max(sel, sel_fuse_bytes(kv->B * Tq * kv->Hkv, kv->N));
+}
+
+int hs2_full_attn_topk(const hs2_kv_desc* kv, const void* q, hs2_dtype q_dtype, int32_t Tq, int32_t Hq,
+                       int32_t q_pos0, float softmax_scale, void* out, float* lse, float* scores, int32_t k,
+                       int32_t window, int32_t* idx, int32_t* count, int32_t max_sel, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream) {
+  int st = check_kv(kv, "hs2_full_attn_topk");
+  if (st) return st;
+  if (!idx || !count) return fail(HS2_ERR_INVALID_ARG, "hs2_full_attn_topk: NULL idx/count");
+  if (k < 0 || window < 0) return fail(HS2_ERR_INVALID_ARG, "hs2_full_attn_topk: need k >= 0 and window >= 0");
+  const int64_t need_sel = std::min<int64_t>((int64_t)k + window, kv->N);
+  if (max_sel < need_sel)
+    return fail(HS2_ERR_INVALID_ARG, "hs2_full_attn_topk: max_sel must be >= min(k + window, N) = " +
+                                         std::to_string(need_sel));
+  if (((uintptr_t)idx & 3) || ((uintptr_t)count & 3))
+    return fail(HS2_ERR_INVALID_ARG, "hs2_full_attn_topk: idx/count must be 4-byte aligned");
+  if (Tq <= 0 || Hq <= 0 || Hq % kv->Hkv) return check_q(kv, q, q_dtype, Tq, Hq, "hs2_full_attn_topk");
+  const size_t need_ws = hs2_full_attn_topk_workspace(kv, Tq, Hq);
+  if (!workspace || workspace_bytes < need_ws)
+    return fail(HS2_ERR_WORKSPACE, "hs2_full_attn_topk: workspace needs " + std::to_string(need_ws) + " bytes");
+  const size_t full_bytes = plan_full(kv, Tq, Hq).total;
+  void* rest = static_cast<char*>(workspace) + full_bytes;
+  SelFuse sel{k, window, max_sel, idx, count, rest};
+  st = full_layer(kv, q, q_dtype, Tq, Hq, q_pos0, softmax_scale, out, lse, scores, workspace, full_bytes, stream,
+                  &sel);
+  if (st || sel.done) return st;
+  return hs2_select_topk_window(scores, kv->B, Tq, kv->Hkv, kv->N, q_pos0, k, window, 1, idx, count, max_sel, rest,
+                                workspace_bytes - full_bytes, stream);
 }
 
 size_t hs2_select_workspace(int32_t B, int32_t Tq, int32_t Hkv, int32_t N) {

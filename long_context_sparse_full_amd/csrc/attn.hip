@@ -17,6 +17,10 @@
 // cache (aitop.news item 35442; javabetter.cn, KV Reuse paragraph).
 #include <math.h>
 
+#include <algorithm>
+
+#include <type_traits>
+
 #include "hs2_internal.hpp"
 
 namespace hs2 {
@@ -522,6 +526,12 @@ __device__ __forceinline__ void grid_barrier(uint64_t* flags, int nwg, uint64_t 
   __syncthreads();
 }
 
+__device__ __forceinline__ int wave_isum(int v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
@@ -539,9 +549,11 @@ __device__ __forceinline__ float wave_sum(float v) {
 // before using any (LDS, or the global code buffer for slots past lds_slots),
 // so a pass costs one memory round trip.  Same per-head expression and head
 // order as the score kernel.
-template <int GM, int OPT, int WAVES>
+template <int GM, int OPT, int WAVES, bool KEEP = false>
 __device__ __forceinline__ void fused_scores(const ScanParams& P, const uint16_t* lcode, const float* lmax,
-                                             const float* red, int unit, int wu, int b, int g, int tp) {
+                                             const float* red, int unit, int wu, int b, int g, int tp,
+                                             float (*keep)[8] = nullptr, int* keep_j = nullptr,
+                                             bool* keep_live = nullptr) {
   constexpr int STEP = WAVES * 32, NT = WAVES * 64;
   const int rows = P.rows, ns = P.nsplit;
   const int wsteps = (P.N + STEP - 1) / STEP;  // workgroup steps covering [0, N)
@@ -600,9 +612,15 @@ __device__ __forceinline__ void fused_scores(const ScanParams& P, const uint16_t
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
               const uint32_t code = (w[o][i][e >> 1] >> (16 * (e & 1))) & 0xffffu;
-              sv[e] += (code == 65535u) ? 0.f : exp2f(ci - (float)code * kCodeInv);
+              sv[e] += (code == 65535u) ? 0.f : exp2_fast(__builtin_fmaf((float)code, -kCodeInv, ci));
             }
           }
+        }
+        if constexpr (KEEP) {  // one pass covers every octet (the caller checked)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) keep[o][e] = (jo[o] + e > p) ? 0.f : sv[e];
+          keep_j[o] = jo[o];
+          keep_live[o] = live[o];
         }
         if (live[o]) {
 #pragma unroll
@@ -620,6 +638,283 @@ __device__ __forceinline__ void fused_scores(const ScanParams& P, const uint16_t
             for (int e = 0; e < 8 && jo[o] + e < P.N; ++e) dst[e] = sv[e];
           }
         }
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ uint32_t sel_key(float s) {
+  const uint32_t u = __float_as_uint(s);
+  return u == 0x80000000u ? 0u : u;  // -0 orders as +0
+}
+
+// Exclusive scan of one value per thread over a workgroup of NT threads (LDS
+// scratch sm >= NT / 64 ints); total returned in `total`.
+template <int NT>
+__device__ __forceinline__ int block_scan_excl(int v, int* sm, int& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  __syncthreads();
+  if (lane == 63) sm[wave] = x;
+  __syncthreads();
+  int base = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) {
+    const int c = sm[w];
+    base += (w < wave) ? c : 0;
+    tot += c;
+  }
+  total = tot;
+  return base + x - v;
+}
+
+// Token top-k + forced window of one unit inside the fused kernel, on the
+// scores this thread holds (OPT octets of 8 positions).  Same rule and result
+// as the select kernels: the k highest scores of C = [0, p - window] (ties to
+// the lower position, exact radix select over the fp32 bit patterns with
+// 12/8/12-bit digits), ascending, then the window, then -1 padding.  Every
+// workgroup runs the same three histogram passes and the step-count exchange
+// (grid barriers 1..4), whatever its unit's mode.
+template <int WAVES, int OPT>
+__device__ __forceinline__ void fused_select(const ScanParams& P, const float (&sv)[OPT][8], const int (&jo)[OPT],
+                                             const bool (&lv)[OPT], int wu, int b, int t, int g, int32_t* lds,
+                                             int wg) {
+  constexpr int STEP = WAVES * 32, NT = WAVES * 64, SEG = 4 * WAVES;  // SEG octets = one workgroup step
+  const int ns = P.nsplit;
+  const int tid = threadIdx.x;
+  const int p = P.q_pos0 + t;
+  const int cand_end = p - P.sel_window;  // candidates 0 <= j <= cand_end
+  const int ncand = max(0, cand_end + 1);
+  const int take = min(P.sel_k, ncand);
+  const bool radix = take > 0 && take < ncand;
+  const int su = (b * P.Tq + t) * P.Hkv + g;
+  // idx / count are outputs here (the gather reads them as inputs)
+  int32_t* out = const_cast<int32_t*>(P.idx) + (int64_t)su * P.max_sel;
+  int32_t* gh = P.sel_hist + (int64_t)su * 3 * kHistBins;
+  int32_t* lh = lds;                       // [kHistBins]
+  int32_t* scr = lds + kHistBins;          // [NT / 64] scan scratch
+  int32_t* pre = scr + 16;                 // [my steps][2] step prefixes
+
+  if (wu == 0) {  // window, padding and count
+    const int wlo = max(0, p - P.sel_window + 1);
+    const int nw = p - wlo + 1;
+    for (int i = tid; i < nw; i += NT) out[take + i] = wlo + i;
+    for (int i = take + nw + tid; i < P.max_sel; i += NT) out[i] = -1;
+    if (tid == 0) const_cast<int32_t*>(P.count)[su] = take + nw;
+  }
+  if (take > 0 && take == ncand) {  // every candidate selected: idx[j] = j
+#pragma unroll
+    for (int o = 0; o < OPT; ++o)
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (lv[o] && jo[o] + e <= cand_end) out[jo[o] + e] = jo[o] + e;
+  }
+  uint32_t key[OPT][8];
+  uint32_t cm[OPT];  // bit e: candidate of a radix unit
+#pragma unroll
+  for (int o = 0; o < OPT; ++o) {
+    cm[o] = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      key[o][e] = sel_key(sv[o][e]);
+      if (radix && lv[o] && jo[o] + e <= cand_end) cm[o] |= 1u << e;
+    }
+  }
+
+  uint32_t prefix = 0;
+  int need = take;
+  // digits of 12, 8 and 12 bits: the middle pass (keys of the boundary bin,
+  // which spread widely) flushes at most 256 bins; the last pass sees few keys
+  auto pass = [&](auto pass_c) {
+    constexpr int PASS = decltype(pass_c)::value;
+    constexpr int SHIFT = PASS == 0 ? 20 : (PASS == 1 ? 12 : 0);
+    constexpr int BINS = PASS == 1 ? 256 : 4096;
+    constexpr uint32_t MATCH = PASS == 0 ? 0u : (PASS == 1 ? 0xFFF00000u : 0xFFFFF000u);
+    for (int i = tid; i < BINS; i += NT) lh[i] = 0;
+    __syncthreads();
+    if (radix && PASS != 0) {  // few keys per bin: plain LDS atomics
+#pragma unroll
+      for (int o = 0; o < OPT; ++o)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (((cm[o] >> e) & 1) && (key[o][e] & MATCH) == prefix) atomicAdd(&lh[(key[o][e] >> SHIFT) & (BINS - 1)], 1);
+    }
+    if (radix && PASS == 0) {
+      // The keys of one row cluster in few bins: up to four (bin, count) pairs
+      // per thread in registers, then one LDS atomic per distinct bin of the
+      // wave (lanes holding the same bin are summed first).
+      constexpr int SL = 4;
+      uint32_t sb[SL];
+      int scnt[SL];
+#pragma unroll
+      for (int q = 0; q < SL; ++q) {
+        sb[q] = 0xffffffffu;
+        scnt[q] = 0;
+      }
+#pragma unroll
+      for (int o = 0; o < OPT; ++o)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          if (!((cm[o] >> e) & 1) || (key[o][e] & MATCH) != prefix) continue;
+          const uint32_t bin = (key[o][e] >> SHIFT) & (BINS - 1);
+          bool hit = false;
+#pragma unroll
+          for (int q = 0; q < SL; ++q) {
+            if (!hit && (sb[q] == bin || scnt[q] == 0)) {
+              sb[q] = bin;
+              ++scnt[q];
+              hit = true;
+            }
+          }
+          if (!hit) atomicAdd(&lh[bin], 1);
+        }
+#pragma unroll
+      for (int q = 0; q < SL; ++q) {
+        bool pend = scnt[q] > 0;
+        while (__any(pend)) {  // one pass per distinct bin of the wave
+          const uint64_t bal = __ballot(pend);
+          const int leader = __builtin_ctzll(bal);
+          const uint32_t b0 = __shfl(sb[q], leader);
+          const bool mine = pend && sb[q] == b0;
+          const int tot = wave_isum(mine ? scnt[q] : 0);
+          if (threadIdx.x % 64 == leader) atomicAdd(&lh[b0], tot);
+          pend = pend && !mine;
+        }
+      }
+    }
+    __syncthreads();
+    if (radix)
+      for (int i = tid; i < BINS; i += NT)
+        if (lh[i]) atomicAdd(&gh[PASS * kHistBins + i], lh[i]);
+    grid_barrier(P.flags + (1 + PASS) * (int64_t)gridDim.x, gridDim.x, P.epoch, wg);
+    // digit holding the need-th largest key: threads own BINS/NT bins from the top
+    constexpr int BPT = BINS >= NT ? BINS / NT : 1;
+    int c[BPT];
+    int mine = 0;
+    const int hi_d = BINS - tid * BPT - 1;
+#pragma unroll
+    for (int q = 0; q < BPT; ++q) {
+      const int d = hi_d - q;
+      c[q] = (radix && d >= 0) ? __hip_atomic_load(&gh[PASS * kHistBins + d], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
+      mine += c[q];
+    }
+    int tot;
+    const int above = block_scan_excl<NT>(mine, scr, tot);
+    __syncthreads();
+    if (radix && above < need && need <= above + mine) {
+      int a = above;
+#pragma unroll
+      for (int q = 0; q < BPT; ++q) {
+        if (a < need && need <= a + c[q]) {
+          lh[0] = hi_d - q;
+          lh[1] = a;
+        }
+        a += c[q];
+      }
+    }
+    __syncthreads();
+    if (radix) {
+      prefix |= (uint32_t)lh[0] << SHIFT;
+      need -= lh[1];
+    }
+    __syncthreads();
+  };
+  pass(std::integral_constant<int, 0>{});
+  pass(std::integral_constant<int, 1>{});
+  pass(std::integral_constant<int, 2>{});
+  const uint32_t tau = prefix;
+
+  // counts per octet and per workgroup step (SEG consecutive octets = threads)
+  int gt_x[OPT], eq_x[OPT], gt_o[OPT], eq_o[OPT];
+  const int lane = tid & 63;
+#pragma unroll
+  for (int o = 0; o < OPT; ++o) {
+    int gt = 0, eq = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const bool cnd = (cm[o] >> e) & 1;
+      gt += (cnd && key[o][e] > tau);
+      eq += (cnd && key[o][e] == tau);
+    }
+    gt_o[o] = gt;
+    eq_o[o] = eq;
+    int xg = gt, xe = eq;
+#pragma unroll
+    for (int d = 1; d < SEG; d <<= 1) {
+      const int yg = __shfl_up(xg, d, SEG), ye = __shfl_up(xe, d, SEG);
+      if ((lane & (SEG - 1)) >= d) {
+        xg += yg;
+        xe += ye;
+      }
+    }
+    gt_x[o] = xg - gt;  // exclusive within the step
+    eq_x[o] = xe - eq;
+    const int oi = o * NT + tid;
+    const int k = (oi >> 2) / WAVES;
+    const int st = wu + k * ns;
+    if ((lane & (SEG - 1)) == SEG - 1 && radix && st < P.sel_nsteps) {
+      int32_t* sc = P.sel_stepcnt + ((int64_t)su * P.sel_nsteps + st) * 2;
+      __hip_atomic_store(sc, xg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(sc + 1, xe, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  grid_barrier(P.flags + 4 * (int64_t)gridDim.x, gridDim.x, P.epoch, wg);
+  if (!radix) return;
+
+  // exclusive prefixes over the unit's steps (in position order) of the
+  // above / equal counts; this workgroup keeps those of its own steps
+  const int nst = min(P.sel_nsteps, (cand_end + STEP) / STEP);  // steps holding candidates
+  const int per = (nst + NT - 1) / NT;
+  int sg = 0, se = 0;
+  for (int q = 0; q < per; ++q) {
+    const int st = tid * per + q;
+    if (st < nst) {
+      const int32_t* sc = P.sel_stepcnt + ((int64_t)su * P.sel_nsteps + st) * 2;
+      sg += __hip_atomic_load(sc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      se += __hip_atomic_load(sc + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  int tg, te;
+  int bg = block_scan_excl<NT>(sg, scr, tg);
+  __syncthreads();
+  int be = block_scan_excl<NT>(se, scr, te);
+  for (int q = 0; q < per; ++q) {
+    const int st = tid * per + q;
+    if (st < nst) {
+      if (st % ns == wu) {
+        pre[(st / ns) * 2] = bg;
+        pre[(st / ns) * 2 + 1] = be;
+      }
+      const int32_t* sc = P.sel_stepcnt + ((int64_t)su * P.sel_nsteps + st) * 2;
+      bg += __hip_atomic_load(sc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      be += __hip_atomic_load(sc + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  __syncthreads();
+  // ordered writes: rank of a selected position = above-threshold keys before
+  // it + min(equal keys before it, need)
+#pragma unroll
+  for (int o = 0; o < OPT; ++o) {
+    if (!cm[o]) continue;
+    const int oi = o * NT + tid;
+    const int k = (oi >> 2) / WAVES;
+    int gb = pre[2 * k] + gt_x[o];
+    int eb = pre[2 * k + 1] + eq_x[o];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if (!((cm[o] >> e) & 1)) continue;
+      const uint32_t kk = key[o][e];
+      if (kk > tau) {
+        out[gb + min(eb, need)] = jo[o] + e;
+        ++gb;
+      } else if (kk == tau) {
+        if (eb < need) out[gb + eb] = jo[o] + e;
+        ++eb;
       }
     }
   }
@@ -815,6 +1110,12 @@ __global__ void __launch_bounds__(WAVES * 64, 1) scan_fused(ScanParams P) {
     }
   }
 
+  if (P.sel_hist != nullptr) {  // this workgroup's share of its unit's selection histograms
+    const int su = (b * P.Tq + tp) * P.Hkv + g;
+    int32_t* gh = P.sel_hist + (int64_t)su * 3 * kHistBins;
+    for (int i = wu * (WAVES * 64) + threadIdx.x; i < 3 * kHistBins; i += ns * WAVES * 64)
+      __hip_atomic_store(gh + i, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
   grid_barrier(P.flags, gridDim.x, P.epoch, wg);
 
   // ---- phase 2a: (max, sum) per row of this unit over all its workgroups, one
@@ -887,7 +1188,14 @@ __global__ void __launch_bounds__(WAVES * 64, 1) scan_fused(ScanParams P) {
   }
 
   // ---- phase 2c: scores of this workgroup's tiles, 0 past each query's position
-  if (P.G <= 8) {
+  if (P.sel_hist != nullptr) {  // scores kept in registers for the selection (tpack 1, G <= 8)
+    float keep[4][8];
+    int kj[4];
+    bool kl[4];
+    fused_scores<8, 4, WAVES, true>(P, lcode, lmax, red, unit, wu, b, g, tp, keep, kj, kl);
+    __syncthreads();  // LDS codes are dead from here on
+    fused_select<WAVES, 4>(P, keep, kj, kl, wu, b, tp, g, (int32_t*)lds, wg);
+  } else if (P.G <= 8) {
     fused_scores<8, 4, WAVES>(P, lcode, lmax, red, unit, wu, b, g, tp);
   } else {
     fused_scores<16, 2, WAVES>(P, lcode, lmax, red, unit, wu, b, g, tp);
@@ -1867,7 +2175,8 @@ template <bool FP8, int D>
 hipError_t go_fused(const ScanParams& p, int units, hipStream_t s) {
   constexpr int W = fused_waves(FP8 ? HS2_FP8_E4M3FN : HS2_BF16, D);
   const void* fn = (const void*)&scan_fused<FP8, D, W>;
-  const size_t lds = (size_t)fused_merge_bytes(p.rows, D) + 256 + (size_t)p.lds_slots * fused_slot_bytes(p.rows);
+  size_t lds = (size_t)fused_merge_bytes(p.rows, D) + 256 + (size_t)p.lds_slots * fused_slot_bytes(p.rows);
+  if (p.sel_hist) lds = std::max(lds, (size_t)kFusedSelectLds);
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kFusedLdsBytes);
   if (e != hipSuccess) return e;
   TimedLaunch tl("full_scan", s);

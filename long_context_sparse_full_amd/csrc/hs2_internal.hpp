@@ -51,6 +51,14 @@ struct ScanParams {
   // multi-query chunk path: log2-domain LSE per (unit, row) from the merge,
   // read by the score pass
   const float* lse2_in;
+  // fused full layer + token selection (tpack = 1): top-k of C = [0, p - window]
+  // with the window appended; output idx/count/max_sel above.  sel_hist:
+  // [units][3][kHistBins] radix histograms; sel_stepcnt: [units][nsteps][2]
+  // (above-threshold, equal-to-threshold) counts per workgroup step.  nullptr
+  // sel_hist = no selection.
+  int sel_k, sel_window, sel_nsteps;
+  int32_t* sel_hist;
+  int32_t* sel_stepcnt;
 };
 
 // Multi-query chunk path: one wave holds chunk_rg() groups of 16 query rows
@@ -59,6 +67,9 @@ struct ScanParams {
 // four otherwise, so queries, accumulators and two tiles stay in registers.
 __host__ __device__ constexpr int chunk_rg(int kv_dtype, int D) { return (kv_dtype == HS2_BF16 && D == 128) ? 3 : 4; }
 constexpr int kChunkWaves = 4;
+
+constexpr int kSelChunk = 16384;  // candidates per workgroup in the select passes
+constexpr int kHistBins = 4096;  // 12-bit digits
 
 // Fused decode full layer: workgroup shape and LDS plan shared by the launcher
 // and the host planner.
@@ -72,6 +83,11 @@ __host__ __device__ constexpr int fused_waves(int kv_dtype, int D) {
 }
 constexpr int kFusedLdsBytes = 160 * 1024;
 __host__ __device__ inline int fused_merge_bytes(int rows, int D) { return 4 * rows * (D + 4) * 4; }
+// fused selection: LDS histogram, scan scratch and up to kFusedSelMaxSteps step
+// prefixes per workgroup; grid barriers: 1 (layer) + 4 (selection)
+constexpr int kFusedSelMaxSteps = 64;
+constexpr int kFusedSelectLds = (kHistBins + 16 + 2 * kFusedSelMaxSteps) * 4;
+constexpr int kFusedBarriers = 5;
 __host__ __device__ inline int fused_slot_bytes(int rows) { return rows * (32 * 2 + 4); }
 
 struct CombineParams {
@@ -97,8 +113,6 @@ struct ScoreParams {
 // ---------------------------------------------------------------------------
 // selection
 // ---------------------------------------------------------------------------
-constexpr int kSelChunk = 16384;  // candidates per workgroup in the select passes
-constexpr int kHistBins = 4096;  // 12-bit digits
 
 struct SelectParams {
   const float* scores;  // [units][N]

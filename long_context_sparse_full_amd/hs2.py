@@ -52,6 +52,9 @@ _last_error = _sig("hs2_last_error", ctypes.c_char_p, [])
 _full_ws = _sig("hs2_full_attn_scores_workspace", _sz, [_KVP, _i32, _i32])
 _full = _sig("hs2_full_attn_scores", ctypes.c_int,
              [_KVP, _vp, _i32, _i32, _i32, _i32, _f32, _vp, _vp, _vp, _vp, _sz, _vp])
+_topk_ws = _sig("hs2_full_attn_topk_workspace", _sz, [_KVP, _i32, _i32])
+_topk = _sig("hs2_full_attn_topk", ctypes.c_int,
+             [_KVP, _vp, _i32, _i32, _i32, _i32, _f32, _vp, _vp, _vp, _i32, _i32, _vp, _vp, _i32, _vp, _sz, _vp])
 _sel_ws = _sig("hs2_select_workspace", _sz, [_i32, _i32, _i32, _i32])
 _sel_ws_for = _sig("hs2_select_workspace_for", _sz, [_i32, _i32, _i32, _i32, _i32])
 _select = _sig("hs2_select_topk_window", ctypes.c_int,
@@ -73,7 +76,7 @@ _t_name = _sig("hs2_timing_kernel_name", ctypes.c_char_p, [_i32])
 
 EXPORTED = [
     "hs2_abi_version", "hs2_status_string", "hs2_last_error", "hs2_full_attn_scores_workspace",
-    "hs2_full_attn_scores", "hs2_select_workspace", "hs2_select_workspace_for", "hs2_select_topk_window",
+    "hs2_full_attn_scores", "hs2_full_attn_topk_workspace", "hs2_full_attn_topk", "hs2_select_workspace", "hs2_select_workspace_for", "hs2_select_topk_window",
     "hs2_sparse_attn_gather", "hs2_sparse_attn_workspace", "hs2_sparse_attn_gather_ws", "hs2_kv_bridge", "hs2_debug_e4m3fn_to_f32", "hs2_debug_stream_read",
     "hs2_full_attn_set_mode", "hs2_timing_enable",
     "hs2_timing_reset", "hs2_timing_collect", "hs2_timing_kernel_name",
@@ -155,6 +158,43 @@ def full_attn_scores(k, v, q, q_pos0: int, softmax_scale: float | None = None, k
                workspace.data_ptr(), workspace.numel(), _stream())
     _check(st, "hs2_full_attn_scores")
     return out, lse, scores
+
+
+def full_attn_topk_workspace(k, v, Tq: int, Hq: int) -> int:
+    d = kv_desc(k, v)
+    return int(_topk_ws(ctypes.byref(d), Tq, Hq))
+
+
+def full_attn_topk(k, v, q, q_pos0: int, topk: int, window: int, max_sel: int | None = None,
+                   softmax_scale: float | None = None, k_scale=None, v_scale=None, out=None, lse=None, scores=None,
+                   idx=None, count=None, workspace=None, want_lse: bool = True):
+    """Full layer + token top-k with forced window in one call.
+    Returns (out, lse, scores, idx [B,Tq,Hkv,max_sel] int32, count [B,Tq,Hkv] int32)."""
+    d = kv_desc(k, v, k_scale, v_scale)
+    B, Tq, Hq, D = q.shape
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(D)
+    if max_sel is None:
+        max_sel = min(d.N, topk + window)
+    dev = q.device
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Tq, Hq), dtype=torch.float32, device=dev)
+    if scores is None:
+        scores = torch.empty((B, Tq, d.Hkv, d.N), dtype=torch.float32, device=dev)
+    if idx is None:
+        idx = torch.empty((B, Tq, d.Hkv, max_sel), dtype=torch.int32, device=dev)
+    if count is None:
+        count = torch.empty((B, Tq, d.Hkv), dtype=torch.int32, device=dev)
+    need = int(_topk_ws(ctypes.byref(d), Tq, Hq))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    st = _topk(ctypes.byref(d), q.data_ptr(), _dtype_code(q), Tq, Hq, int(q_pos0), float(softmax_scale),
+               out.data_ptr(), None if lse is None else lse.data_ptr(), scores.data_ptr(), int(topk), int(window),
+               idx.data_ptr(), count.data_ptr(), int(max_sel), workspace.data_ptr(), workspace.numel(), _stream())
+    _check(st, "hs2_full_attn_topk")
+    return out, lse, scores, idx, count
 
 
 def select_workspace(B, Tq, Hkv, N, block_size: int | None = None) -> int:

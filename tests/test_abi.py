@@ -168,6 +168,20 @@ def test_select_max_sel_rule_uses_context_cap(hs2):
     assert st == -3
 
 
+def test_full_attn_topk_validation(hs2):
+    d = desc(hs2)
+    ws = int(hs2._topk_ws(ctypes.byref(d), 1, 16))
+    full = int(hs2._full_ws(ctypes.byref(d), 1, 16))
+    assert ws > full
+    args = lambda idx=FAKE, k=8, window=4, max_sel=12, wsb=ws: (ctypes.byref(d), FAKE, 1, 1, 16, 255, 0.1, FAKE, None,
+                                                                 FAKE, k, window, idx, FAKE, max_sel, FAKE, wsb, None)
+    assert hs2._topk(*args(idx=None)) == -1            # NULL idx
+    assert hs2._topk(*args(k=-1)) == -1                # negative k
+    assert hs2._topk(*args(max_sel=11)) == -1          # max_sel < k + window
+    assert hs2._topk(*args(wsb=ws - 1)) == -3          # workspace too small
+    assert hs2._set_mode(4) == -1 and hs2._set_mode(-1) == -1
+
+
 def test_sparse_and_bridge_validation(hs2):
     d = desc(hs2)
     assert hs2._sparse(ctypes.byref(d), FAKE, 1, 1, 16, 0.1, None, FAKE, 8, FAKE, None, None) == -1

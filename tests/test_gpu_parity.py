@@ -379,3 +379,83 @@ def test_fused_and_kernel_paths_agree(hs2, kv):
         gu.assert_scores(sc, s_or, f"scores mode {mode}", G=spec.G)
     # the spill route stores the same codes as the on-chip route
     assert np.array_equal(res[1][2], res[2][2]) and np.array_equal(res[1][0], res[2][0])
+
+
+# ------------------------------------------------ full layer + selection in one call
+
+TOPK_CASES = [
+    # kv, D, G, Hkv, B, N, k, window, queries
+    ("bf16", 128, 8, 4, 2, 20000, 1024, 128, "rand"),
+    ("fp8", 128, 8, 4, 1, 70000, 1024, 128, "rand"),
+    ("bf16", 64, 4, 2, 2, 5000, 300, 32, "rand"),
+    ("fp8", 64, 8, 2, 1, 3001, 3000, 16, "rand"),    # k >= |C|: every candidate
+    ("bf16", 128, 8, 2, 1, 4000, 0, 64, "rand"),     # k = 0: the window only
+    ("bf16", 128, 8, 2, 1, 100, 10, 128, "rand"),    # p < window: no candidates
+    ("bf16", 128, 8, 2, 1, 9000, 500, 16, "zero"),   # all scores equal: ties to the lower positions
+    ("fp8", 128, 8, 1, 1, 5000, 7, 0, "rand"),       # no window
+]
+
+
+@pytest.mark.parametrize("mode", [1, 0], ids=["fused", "sequence"])
+@pytest.mark.parametrize("case", TOPK_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_full_attn_topk(hs2, case, mode):
+    """hs2_full_attn_topk: outputs and scores against the oracle; the selection
+    bit for bit equal to the oracle's selection on the returned scores.  Mode 1
+    must run the selection inside the cooperative kernel (no select kernels),
+    mode 0 the select kernels."""
+    kv, D, G, Hkv, B, N, k, window, qk = case
+    spec = small_spec(kv, D=D, G=G, Hkv=Hkv, B=B, N=N, Tq=1, k=k, window=window, needles=min(8, max(0, N - window - 1)))
+    inp = synth.make_inputs(spec, seed=4321)
+    if qk == "zero":
+        inp.q_full[...] = 0
+    blk = gu.DeviceBlock(inp)
+    gu.log(f"topk {case} mode {mode}")
+    hs2.full_attn_set_mode(mode)
+    try:
+        hs2.timing_reset()
+        hs2.timing_enable(True)
+        out, lse, sc, idx, cnt = hs2.full_attn_topk(blk.k, blk.v, blk.q, spec.q_pos0, k, window, max_sel=spec.max_sel,
+                                                    k_scale=blk.ks, v_scale=blk.vs)
+        torch.cuda.synchronize()
+        _, n_hist = hs2.timing_collect("select_hist")
+    finally:
+        hs2.timing_enable(False)
+        hs2.timing_reset()
+        hs2.full_attn_set_mode(0)
+    if mode == 1:
+        assert n_hist == 0, "selection did not run inside the cooperative kernel"
+    else:
+        assert n_hist == 3, "expected the select kernels"
+    o_or, l_or, s_or = oracle_full(inp, spec)
+    gu.assert_close(gu.host(out), o_or, gu.O_TOL[kv], "out")
+    gu.assert_close(gu.host(lse), l_or, gu.LSE_TOL[kv], "lse")
+    sc = gu.host(sc)
+    gu.assert_scores(sc, s_or, G=G)
+    idx, cnt = gu.host(idx), gu.host(cnt)
+    i_g, c_g = oracle.select_topk_window(sc.astype(np.float64), spec.q_pos0, k, window, max_sel=spec.max_sel)
+    assert np.array_equal(cnt, c_g), "counts differ from the oracle's selection on the same scores"
+    assert np.array_equal(idx, i_g), "indices differ from the oracle's selection on the same scores"
+    gu.check_structure(idx, cnt, spec.q_pos0, k, window, N)
+
+
+def test_full_attn_topk_repeated_calls(hs2):
+    """The cooperative kernel's grid barriers and histograms start clean on
+    every launch: three calls on one workspace give identical results."""
+    spec = small_spec("fp8", B=1, N=40000, Hkv=4)
+    inp = synth.make_inputs(spec, seed=5)
+    blk = gu.DeviceBlock(inp)
+    ws = torch.empty(hs2.full_attn_topk_workspace(blk.k, blk.v, 1, spec.Hq), dtype=torch.uint8, device="cuda")
+    res = []
+    hs2.full_attn_set_mode(1)
+    try:
+        for _ in range(3):
+            r = hs2.full_attn_topk(blk.k, blk.v, blk.q, spec.q_pos0, spec.k, spec.window, max_sel=spec.max_sel,
+                                   k_scale=blk.ks, v_scale=blk.vs, workspace=ws)
+            torch.cuda.synchronize()
+            res.append([gu.host(x) for x in r])
+    finally:
+        hs2.full_attn_set_mode(0)
+    for a, b in zip(res[0], res[1]):
+        assert np.array_equal(a, b)
+    for a, b in zip(res[0], res[2]):
+        assert np.array_equal(a, b)
