@@ -2122,7 +2122,7 @@ __global__ void __launch_bounds__(256) score(ScoreParams P) {
         const uint32_t code[4] = {w.x & 0xffffu, w.x >> 16, w.y & 0xffffu, w.y >> 16};
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          s[e] += (code[e] == 65535u) ? 0.f : exp2f(c - (float)code[e] * kCodeInv);
+          s[e] += (code[e] == 65535u) ? 0.f : exp2_fast(__builtin_fmaf((float)code[e], -kCodeInv, c));
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e)
