@@ -25,21 +25,27 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          "-Wno-unused-command-line-argument", "-I", INCLUDE, "-I", CSRC]
 
 
-def _compile(src: str, build_dir: str = BUILD_DIR, defines: tuple = ()) -> str:
+# Per-source flags.  attn.hip: MFMA results in VGPRs rather than AGPRs, so the
+# online-softmax rescale of the accumulators needs no AGPR round trips.
+SOURCE_FLAGS = {"attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
+def _compile(src: str, build_dir: str = BUILD_DIR, defines: tuple = (), extra: tuple = ()) -> str:
     obj = os.path.join(build_dir, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, *[f"-D{d}" for d in defines], "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *SOURCE_FLAGS.get(src, []), *extra, *[f"-D{d}" for d in defines], "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
     return obj
 
 
-def build(verbose: bool = False, out: str = LIB, defines: tuple = ()) -> str:
-    """Compile and link; `defines` are extra -D flags (compile-time tuning)."""
+def build(verbose: bool = False, out: str = LIB, defines: tuple = (), extra: tuple = ()) -> str:
+    """Compile and link; `defines` are extra -D flags and `extra` extra compiler
+    flags (compile-time tuning)."""
     build_dir = BUILD_DIR if out == LIB else os.path.join(os.path.dirname(out), "_build")
     os.makedirs(build_dir, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=min(4, os.cpu_count() or 1)) as ex:
-        objs = list(ex.map(lambda src: _compile(src, build_dir, tuple(defines)), SOURCES))
+        objs = list(ex.map(lambda src: _compile(src, build_dir, tuple(defines), tuple(extra)), SOURCES))
     tmp = out + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -79,6 +79,27 @@ __device__ __forceinline__ f32x4_t mfma_bf16(u32x4_t a, u32x4_t b, f32x4_t c) {
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Lane pairs (l, l ^ 16) and (l, l ^ 32) through the gfx950 permlane swaps:
+// VALU lane exchanges with no LDS round trip.  Each swap hands every lane the
+// two values of its pair (in some order); max and sum are symmetric in them.
+__device__ __forceinline__ float fmax2(float a, float b) { return a > b ? a : b; }
+__device__ __forceinline__ float max_x16(float x) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmax2(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float max_x32(float x) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmax2(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float sum_x16(float x) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float sum_x32(float x) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
 // 16-bit code of a log2-domain logit x below its tile maximum m:
 // round((m - x) * 2^12), saturated; 65535 stands for "at least 16 below m" and
 // decodes to a zero contribution.  Step 2^-12 bounds the relative error of
@@ -240,8 +261,8 @@ __device__ __forceinline__ void compute_tile(const RawTile<FP8, D>& R, const u32
   for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) tmax = fmaxf(tmax, x[hh][ii]);
-  tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-  tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+  tmax = max_x16(tmax);
+  tmax = max_x32(tmax);
   if constexpr (WRITE_LOGITS) {
     if (lg) {  // lg -> this row's code at position j0 + 4*g4; lgm -> this row's tile maxima
 #pragma unroll
@@ -316,8 +337,8 @@ __device__ __forceinline__ void merge_and_store(const ScanParams& P, WaveState<D
                                                 float (*sm_o)[16][D + 1]) {
   constexpr int VE = D / 16;
   float l_run = S.l;
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
+  l_run = sum_x16(l_run);
+  l_run = sum_x32(l_run);
   __syncthreads();
   if (g4 == 0) {
     sm_m[wave][r] = S.m;
@@ -1065,8 +1086,8 @@ __global__ void __launch_bounds__(WAVES * 64, 1) scan_fused(ScanParams P) {
   // ---- merge the waves (tree through a 4-slot LDS buffer), publish the partial
   {
     float lt = S.l;
-    lt += __shfl_xor(lt, 16);
-    lt += __shfl_xor(lt, 32);
+    lt = sum_x16(lt);
+    lt = sum_x32(lt);
     S.l = lt;  // every lane of a row holds the row total
   }
 #pragma unroll
@@ -1307,8 +1328,8 @@ __device__ __forceinline__ void chunk_tile(const RawTile<FP8, D>& R, const u32x4
     for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) tmax = fmaxf(tmax, s[rg][hh][ii]);
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    tmax = max_x16(tmax);
+    tmax = max_x32(tmax);
     tmax *= cs;  // cs > 0: the maximum of the scaled logits
     const bool move = tmax > S.m[rg] + kLazyMax;
     if (__any(move)) {
@@ -1466,6 +1487,267 @@ __global__ void __launch_bounds__(kChunkWaves * 64, 1) chunk_full(ScanParams P) 
   }
 }
 
+// ---------------------------------------------------------------------------
+// Chunk full layer, LDS-staged form.  A workgroup of 4 waves covers 4 x
+// kFlashRG row groups of one (b, kv head) over a position split; every
+// 32-position K/V tile is fetched once by the whole workgroup (16-byte pieces,
+// three tiles ahead in registers), stored to one of two LDS tile buffers with
+// the 16-byte chunks of a row XOR-swizzled by the row index (conflict-free
+// fragment reads), and each wave reads its MFMA fragments from LDS for its
+// own row groups.  Each wave writes the split partials of its row groups.
+// ---------------------------------------------------------------------------
+
+template <bool FP8, int D>
+struct FlashGeom {
+  static constexpr int EB = FP8 ? 1 : 2;
+  static constexpr int ROWB = D * EB;          // bytes per cached row
+  static constexpr int CH = ROWB / 16;         // 16-byte chunks per row
+  static constexpr int HALF = 32 * ROWB;       // K (or V) part of a tile
+  static constexpr int TILE = 2 * HALF;        // one LDS tile buffer
+  static constexpr int PER = 2 * 32 * CH / 256;  // chunks per thread per tile
+};
+
+template <bool FP8, int D>
+__device__ __forceinline__ const char* flash_at(const char* base, int row, int byte) {
+  using FG = FlashGeom<FP8, D>;
+  return base + row * FG::ROWB + ((((byte >> 4) ^ (row & (FG::CH - 1)))) << 4) + (byte & 15);
+}
+
+template <bool FP8, int D, int RG>
+__device__ __forceinline__ void flash_tile(const char* kl, const char* vl, const u32x4_t (&qf)[RG][D / 32], float cs,
+                                           int j0, const int (&jlim)[RG], bool need_mask, int r, int g4,
+                                           ChunkState<D, RG>& S) {
+  constexpr int NC = D / 32, VE = D / 16;
+  using RT = RawTile<FP8, D>;
+  // K fragments (A of S^T): row 16*hh + r, bytes 64*c + 16*g4 of the row
+  u32x4_t kf[2][NC];
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    const int row = 16 * hh + r;
+    if constexpr (!FP8) {
+#pragma unroll
+      for (int c = 0; c < NC; ++c) kf[hh][c] = *(const u32x4_t*)flash_at<FP8, D>(kl, row, 64 * c + 16 * g4);
+    } else {
+#pragma unroll
+      for (int ii = 0; ii < RT::KW; ++ii) {
+        const u32x4_t raw = *(const u32x4_t*)flash_at<FP8, D>(kl, row, 64 * ii + 16 * g4);
+        uint32_t a0, a1, a2, a3, b0, b1, b2, b3;
+        e4m3x4_to_bf16(raw.x, a0, a1);
+        e4m3x4_to_bf16(raw.y, a2, a3);
+        e4m3x4_to_bf16(raw.z, b0, b1);
+        e4m3x4_to_bf16(raw.w, b2, b3);
+        kf[hh][2 * ii] = u32x4_t{a0, a1, a2, a3};
+        kf[hh][2 * ii + 1] = u32x4_t{b0, b1, b2, b3};
+      }
+    }
+  }
+  f32x4_t s[RG][2];
+#pragma unroll
+  for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) s[rg][hh] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) s[rg][hh] = mfma_bf16(kf[hh][c], qf[rg][c], s[rg][hh]);
+  u32x4_t pf[RG];
+#pragma unroll
+  for (int rg = 0; rg < RG; ++rg) {
+    float tmax = kNegInf;
+    if (need_mask) {
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii)
+          if (j0 + 16 * hh + 4 * g4 + ii > jlim[rg]) s[rg][hh][ii] = kNegInf;
+    }
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) tmax = fmaxf(tmax, s[rg][hh][ii]);
+    tmax = max_x16(tmax);
+    tmax = max_x32(tmax);
+    tmax *= cs;
+    const bool move = tmax > S.m[rg] + kLazyMax;
+    if (__any(move)) {
+      const float m_new = move ? tmax : S.m[rg];
+      const float alpha = (S.m[rg] == kNegInf) ? 0.f : exp2_fast(S.m[rg] - m_new);
+      S.l[rg] *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < VE; ++dt) S.o[rg][dt] *= alpha;
+      S.m[rg] = m_new;
+    }
+    const float m_use = (S.m[rg] == kNegInf) ? 0.f : S.m[rg];
+    float pr[2][4];
+    float psum = 0.f;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        pr[hh][ii] = exp2_fast(__builtin_fmaf(s[rg][hh][ii], cs, -m_use));
+        psum += pr[hh][ii];
+      }
+    S.l[rg] += psum;
+    pf[rg] = u32x4_t{pack_bf16(pr[0][0], pr[0][1]), pack_bf16(pr[0][2], pr[0][3]), pack_bf16(pr[1][0], pr[1][1]),
+                     pack_bf16(pr[1][2], pr[1][3])};
+  }
+  // V slices: rows 16*(kk>>2) + 4*g4 + (kk&3), VE elements from element VE*r
+  uint32_t vd[8][VE / 2];
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) {
+    const int row = 16 * (kk >> 2) + 4 * g4 + (kk & 3);
+    const char* a = flash_at<FP8, D>(vl, row, VE * r * (FP8 ? 1 : 2));
+    if constexpr (!FP8) {
+      if constexpr (VE == 8) {
+        const u32x4_t w = *(const u32x4_t*)a;
+        vd[kk][0] = w.x; vd[kk][1] = w.y; vd[kk][2] = w.z; vd[kk][3] = w.w;
+      } else {
+        const u32x2_t w = *(const u32x2_t*)a;
+        vd[kk][0] = w.x; vd[kk][1] = w.y;
+      }
+    } else {
+      if constexpr (VE == 8) {
+        const u32x2_t w = *(const u32x2_t*)a;
+        e4m3x4_to_bf16(w.x, vd[kk][0], vd[kk][1]);
+        e4m3x4_to_bf16(w.y, vd[kk][2], vd[kk][3]);
+      } else {
+        e4m3x4_to_bf16(*(const uint32_t*)a, vd[kk][0], vd[kk][1]);
+      }
+    }
+  }
+#pragma unroll
+  for (int dt = 0; dt < VE; ++dt) {
+    const int w = dt >> 1;
+    u32x4_t va;
+#pragma unroll
+    for (int q2 = 0; q2 < 4; ++q2) {
+      const uint32_t e0 = vd[2 * q2][w], e1 = vd[2 * q2 + 1][w];
+      va[q2] = (dt & 1) ? __builtin_amdgcn_perm(e1, e0, 0x07060302u) : __builtin_amdgcn_perm(e1, e0, 0x05040100u);
+    }
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg) S.o[rg][dt] = mfma_bf16(va, pf[rg], S.o[rg][dt]);
+  }
+}
+
+template <bool FP8, int D>
+__global__ void __launch_bounds__(256, 1) chunk_flash(ScanParams P) {
+  constexpr int RG = kFlashRG, VE = D / 16, NC = D / 32;
+  using FG = FlashGeom<FP8, D>;
+  __shared__ __align__(16) char tiles[2][FG::TILE];
+  const int lane = threadIdx.x & 63, tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane & 15, g4 = lane >> 4;
+  const int nblk = (P.n_tpacks + 4 * RG - 1) / (4 * RG);
+  const ChunkItem it = chunk_item(P, nblk);
+  const int b = it.b, g = it.g;
+  const int blk_w = it.blk * 4 + wave;  // this wave's block of RG packs
+
+  u32x4_t qf[RG][NC];
+  int jlim[RG];
+#pragma unroll
+  for (int rg = 0; rg < RG; ++rg) {
+    const ChunkRows cr = chunk_row<RG>(P, blk_w, rg, r);
+    jlim[rg] = cr.jlim;
+    load_q<FP8, D>(qf[rg], P, b, cr.ok ? cr.t : 0, g * P.G + (r % P.G), cr.ok, g4);
+  }
+  const int t_first = it.blk * 4 * RG * P.tpack;  // first token of the workgroup
+  const int t_last = min(t_first + 4 * RG * P.tpack, P.Tq) - 1;
+  const int p_max = P.q_pos0 + t_last;
+  const int wt_first = blk_w * RG * P.tpack;  // first token of this wave
+  const int j_nomask = P.q_pos0 + min(wt_first, P.Tq - 1);
+  const int j_begin = it.split * P.split_len;
+  const int j_end = min(j_begin + P.split_len, p_max + 1);
+  const int ntile = j_end > j_begin ? (j_end - j_begin + 31) / 32 : 0;
+
+  const int64_t kvoff = ((int64_t)b * P.sb + (int64_t)g * P.sh) * FG::EB;
+  const char* kb = (const char*)P.k + kvoff;
+  const char* vb = (const char*)P.v + kvoff;
+  const int64_t snb = P.sn * FG::EB;
+  float cs = P.scale_log2;
+  if constexpr (FP8) cs *= P.k_scale[b * P.Hkv + g];
+
+  // this thread's 16-byte pieces of a tile: piece q = tid + 256 * i; K pieces
+  // first (32 rows x CH), then V; global row j0 + row (clamped to p_max)
+  auto gload = [&](u32x4_t (&dst)[FG::PER], int tile) {
+    if (tile >= ntile) return;
+    const int j0 = j_begin + 32 * tile;
+#pragma unroll
+    for (int i = 0; i < FG::PER; ++i) {
+      const int q = tid + 256 * i;
+      const int which = q / (32 * FG::CH), rem = q - which * 32 * FG::CH;
+      const int row = rem / FG::CH, gc = rem - row * FG::CH;
+      const int64_t j = min(j0 + row, p_max);
+      dst[i] = *(const u32x4_t*)((which ? vb : kb) + j * snb + 16 * gc);
+    }
+  };
+  auto lstore = [&](const u32x4_t (&src)[FG::PER], int buf) {
+#pragma unroll
+    for (int i = 0; i < FG::PER; ++i) {
+      const int q = tid + 256 * i;
+      const int which = q / (32 * FG::CH), rem = q - which * 32 * FG::CH;
+      const int row = rem / FG::CH, gc = rem - row * FG::CH;
+      *(u32x4_t*)(tiles[buf] + which * FG::HALF + row * FG::ROWB + ((gc ^ (row & (FG::CH - 1))) << 4)) = src[i];
+    }
+  };
+
+  ChunkState<D, RG> S;
+#pragma unroll
+  for (int rg = 0; rg < RG; ++rg) {
+    S.m[rg] = kNegInf;
+    S.l[rg] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < VE; ++dt) S.o[rg][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  auto compute = [&](int n) {
+    const int j0 = j_begin + 32 * n;
+    const char* kl = tiles[n & 1];
+    flash_tile<FP8, D, RG>(kl, kl + FG::HALF, qf, cs, j0, jlim, j0 + 31 > j_nomask, r, g4, S);
+  };
+  // pipeline: tile n computed from LDS buffer n % 2 while tiles n+1..n+3 are
+  // in flight in the register ring; one workgroup barrier per tile
+  u32x4_t R0[FG::PER], R1[FG::PER], R2[FG::PER];
+  gload(R0, 0);
+  gload(R1, 1);
+  gload(R2, 2);
+  if (ntile > 0) lstore(R0, 0);
+  __syncthreads();
+  gload(R0, 3);
+  auto step = [&](int n, u32x4_t (&R)[FG::PER]) {
+    if (n < ntile) compute(n);
+    if (n + 1 < ntile) lstore(R, (n + 1) & 1);
+    __syncthreads();
+    gload(R, n + 4);
+  };
+  for (int n = 0; n < ntile; n += 3) {
+    step(n, R1);
+    step(n + 1, R2);
+    step(n + 2, R0);
+  }
+
+  // partials of this wave's row groups (16 rows each)
+#pragma unroll
+  for (int rg = 0; rg < RG; ++rg) {
+    const int tp = blk_w * RG + rg;
+    if (tp >= P.n_tpacks) continue;  // uniform per wave
+    float l = S.l[rg];
+    l = sum_x16(l);
+    l = sum_x32(l);
+    if (r >= P.rows) continue;
+    const int unit = (b * P.n_tpacks + tp) * P.Hkv + g;
+    const int64_t pb = ((int64_t)unit * P.nsplit + it.split) * 16 + r;
+#pragma unroll
+    for (int dt = 0; dt < VE; ++dt)
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) P.part_o[pb * D + VE * (4 * g4 + ii) + dt] = S.o[rg][dt][ii];
+    if (g4 == 0) {
+      P.part_ml[pb * 2] = S.m[rg];
+      P.part_ml[pb * 2 + 1] = l;
+    }
+  }
+}
+
 // Score pass of the chunk: S[b,t,g,j] = sum over the G heads of token t of
 // 2^(x_hj - lse2_h) for j <= p_t, 0 beyond.  K only; tiles past the block's
 // last query position are zeros without loads.  Logits in the S = Q K^T
@@ -1474,8 +1756,8 @@ __global__ void __launch_bounds__(kChunkWaves * 64, 1) chunk_full(ScanParams P) 
 template <int G>
 __device__ __forceinline__ float head_sum_s(const float (&a)[4]) {
   float v = (a[0] + a[1]) + (a[2] + a[3]);
-  if constexpr (G >= 8) v += __shfl_xor(v, 16);
-  if constexpr (G >= 16) v += __shfl_xor(v, 32);
+  if constexpr (G >= 8) v = sum_x16(v);
+  if constexpr (G >= 16) v = sum_x32(v);
   return v;
 }
 
@@ -2301,10 +2583,21 @@ int fused_max_workgroups(int kv_dtype, int D) {
 }
 
 hipError_t launch_chunk_full(const ScanParams& p, int kv_dtype, hipStream_t s) {
+  TimedLaunch tl("chunk_full", s);
+#if HS2_CHUNK_FLASH
+  const int nblk = (p.n_tpacks + 4 * kFlashRG - 1) / (4 * kFlashRG);  // chunk_full_packs()
+  const dim3 grid(p.B * nblk * p.Hkv * p.nsplit);
+  if (kv_dtype == HS2_FP8_E4M3FN) {
+    if (p.D == 128) hipLaunchKernelGGL((chunk_flash<true, 128>), grid, dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((chunk_flash<true, 64>), grid, dim3(256), 0, s, p);
+  } else {
+    if (p.D == 128) hipLaunchKernelGGL((chunk_flash<false, 128>), grid, dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((chunk_flash<false, 64>), grid, dim3(256), 0, s, p);
+  }
+#else
   const int rg = chunk_rg(kv_dtype, p.D);
   const int nblk = (p.n_tpacks + rg - 1) / rg;
   const dim3 grid(p.B * nblk * p.Hkv * p.nsplit);
-  TimedLaunch tl("chunk_full", s);
   if (kv_dtype == HS2_FP8_E4M3FN) {
     if (p.D == 128) hipLaunchKernelGGL((chunk_full<true, 128>), grid, dim3(kChunkWaves * 64), 0, s, p);
     else hipLaunchKernelGGL((chunk_full<true, 64>), grid, dim3(kChunkWaves * 64), 0, s, p);
@@ -2312,6 +2605,7 @@ hipError_t launch_chunk_full(const ScanParams& p, int kv_dtype, hipStream_t s) {
     if (p.D == 128) hipLaunchKernelGGL((chunk_full<false, 128>), grid, dim3(kChunkWaves * 64), 0, s, p);
     else hipLaunchKernelGGL((chunk_full<false, 64>), grid, dim3(kChunkWaves * 64), 0, s, p);
   }
+#endif
   return hipGetLastError();
 }
 

@@ -65,8 +65,28 @@ struct ScanParams {
 // (tpack tokens x G heads each), kChunkWaves waves split a position range.
 // Three groups for a bf16 D=128 cache (its tile buffers are twice the size),
 // four otherwise, so queries, accumulators and two tiles stay in registers.
-__host__ __device__ constexpr int chunk_rg(int kv_dtype, int D) { return (kv_dtype == HS2_BF16 && D == 128) ? 3 : 4; }
+#ifndef HS2_CHUNK_RG
+#define HS2_CHUNK_RG 0  // 0: per dtype (3 for bf16 D = 128, 4 otherwise); >0: fixed (tuning)
+#endif
+__host__ __device__ constexpr int chunk_rg(int kv_dtype, int D) {
+  return HS2_CHUNK_RG > 0 ? HS2_CHUNK_RG : ((kv_dtype == HS2_BF16 && D == 128) ? 3 : 4);
+}
 constexpr int kChunkWaves = 4;
+// The chunk full pass runs either as the per-wave streaming kernel above
+// (default) or LDS-staged: a workgroup's 4 waves share each K/V tile through
+// LDS and each wave holds kFlashRG row groups, 4 * kFlashRG packs per
+// workgroup.
+#ifndef HS2_CHUNK_FLASH
+#define HS2_CHUNK_FLASH 0
+#endif
+// Chunk position splits: about this many full-pass work items in all.
+#ifndef HS2_CHUNK_TARGET_WGS
+#define HS2_CHUNK_TARGET_WGS 3072
+#endif
+constexpr int kFlashRG = 2;
+__host__ __device__ constexpr int chunk_full_packs(int kv_dtype, int D) {
+  return HS2_CHUNK_FLASH ? 4 * kFlashRG : chunk_rg(kv_dtype, D);
+}
 
 constexpr int kSelChunk = 16384;  // candidates per workgroup in the select passes
 constexpr int kHistBins = 4096;  // 12-bit digits
