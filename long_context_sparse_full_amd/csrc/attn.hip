@@ -28,6 +28,7 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
@@ -1504,13 +1505,69 @@ struct FlashGeom {
   static constexpr int CH = ROWB / 16;         // 16-byte chunks per row
   static constexpr int HALF = 32 * ROWB;       // K (or V) part of a tile
   static constexpr int TILE = 2 * HALF;        // one LDS tile buffer
-  static constexpr int PER = 2 * 32 * CH / 256;  // chunks per thread per tile
 };
 
 template <bool FP8, int D>
 __device__ __forceinline__ const char* flash_at(const char* base, int row, int byte) {
   using FG = FlashGeom<FP8, D>;
   return base + row * FG::ROWB + ((((byte >> 4) ^ (row & (FG::CH - 1)))) << 4) + (byte & 15);
+}
+
+// wait until at most N vector-memory operations of this wave are in flight
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Tile loads straight from global memory into LDS (16 bytes per lane) for a
+// 256-thread workgroup: load i of thread tid fills LDS slot s = 256 i + tid
+// of the tile (PARTS = 1: K rows; 2: K rows then V rows, 32 rows x CH chunks
+// each), a wave-contiguous 1 KiB per instruction.  Slot (row, c) holds chunk
+// c ^ (row & (CH - 1)) of the row, the swizzle flash_at() undoes; rows past
+// p_max are clamped to it.  Waves whose slots lie past the tile issue nothing.
+template <bool FP8, int D, int PARTS>
+struct TileLoader {
+  using FG = FlashGeom<FP8, D>;
+  static constexpr int SLOTS = PARTS * 32 * FG::CH;
+  static constexpr int PER = (SLOTS + 255) / 256;  // loads per thread per tile
+  static constexpr int BYTES = PARTS * FG::HALF;   // one LDS tile buffer
+  int prow[PER];
+  const char* pbase[PER];
+  __device__ __forceinline__ TileLoader(const char* kb, const char* vb, int tid) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int s = min(256 * i + tid, SLOTS - 1);
+      const int which = s / (32 * FG::CH), rem = s - which * 32 * FG::CH;
+      const int row = rem / FG::CH, pos = rem - row * FG::CH;
+      prow[i] = row;
+      pbase[i] = (which ? vb : kb) + 16 * (pos ^ (row & (FG::CH - 1)));
+    }
+  }
+  __device__ __forceinline__ void issue(char* dst, int j0, int p_max, int64_t snb, int wave) const {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      if (256 * i + 64 * wave >= SLOTS) continue;  // wave-uniform
+      const int64_t j = min(j0 + prow[i], p_max);
+      __builtin_amdgcn_global_load_lds((const void*)(pbase[i] + j * snb),
+                                       (__attribute__((address_space(3))) void*)(dst + 16 * (256 * i + 64 * wave)), 16,
+                                       0, 0);
+    }
+  }
+};
+
+// Ring pipeline step n over LDS tile buffers (tile n in buffer n % NBUF):
+// wait for this wave's loads of tile n (later tiles, up to NBUF - 2 of them,
+// may stay in flight), then a workgroup barrier: tile n is visible to every
+// wave and the buffer of tile n - 1 is free for tile n + NBUF - 1.
+template <int NBUF, int PER>
+__device__ __forceinline__ void ring_wait(int n, int ntile) {
+  static_assert(NBUF == 4, "wait counts below assume a 4-buffer ring");
+  const int ahead = min(NBUF - 2, ntile - 1 - n);  // tiles issued after tile n
+  if (ahead >= 2) wait_vm<2 * PER>();
+  else if (ahead == 1) wait_vm<PER>();
+  else wait_vm<0>();
+  __syncthreads();
 }
 
 template <bool FP8, int D, int RG>
@@ -1593,21 +1650,37 @@ __device__ __forceinline__ void flash_tile(const char* kl, const char* vl, const
     pf[rg] = u32x4_t{pack_bf16(pr[0][0], pr[0][1]), pack_bf16(pr[0][2], pr[0][3]), pack_bf16(pr[1][0], pr[1][1]),
                      pack_bf16(pr[1][2], pr[1][3])};
   }
-  // V slices: rows 16*(kk>>2) + 4*g4 + (kk&3), VE elements from element VE*r
-  uint32_t vd[8][VE / 2];
+  if constexpr (!FP8) {
+    // V^T operands straight from LDS with the transposing 64-bit read: in each
+    // 16-lane group, source lane s = 4k + a names 4 consecutive head dims
+    // (piece a) of one V row (position k of the group's four); lane i then
+    // receives head dim 16 dt + i of those four positions.  Two reads give the
+    // 8 positions 4 g4 + {0..3}, 16 + 4 g4 + {0..3} that match the P layout.
+    // Accumulator row m of block dt is head dim 16 dt + m.
+    const int k4 = (r >> 2), a4 = r & 3;
 #pragma unroll
-  for (int kk = 0; kk < 8; ++kk) {
-    const int row = 16 * (kk >> 2) + 4 * g4 + (kk & 3);
-    const char* a = flash_at<FP8, D>(vl, row, VE * r * (FP8 ? 1 : 2));
-    if constexpr (!FP8) {
-      if constexpr (VE == 8) {
-        const u32x4_t w = *(const u32x4_t*)a;
-        vd[kk][0] = w.x; vd[kk][1] = w.y; vd[kk][2] = w.z; vd[kk][3] = w.w;
-      } else {
-        const u32x2_t w = *(const u32x2_t*)a;
-        vd[kk][0] = w.x; vd[kk][1] = w.y;
+    for (int dt = 0; dt < VE; ++dt) {
+      u32x4_t va;
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const char* src = flash_at<FP8, D>(vl, 16 * c + 4 * g4 + k4, 32 * dt + 8 * a4);
+        const s16x4_t t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)src);
+        const u32x2_t w = __builtin_bit_cast(u32x2_t, t);
+        va[2 * c] = w.x;
+        va[2 * c + 1] = w.y;
       }
-    } else {
+#pragma unroll
+      for (int rg = 0; rg < RG; ++rg) S.o[rg][dt] = mfma_bf16(va, pf[rg], S.o[rg][dt]);
+    }
+  } else {
+    // FP8: each lane decodes VE-element slices of 8 V rows (positions
+    // 16 (kk >> 2) + 4 g4 + (kk & 3), head dims VE r ..), and byte permutes
+    // build the V^T operand of each block dt; accumulator row m of block dt is
+    // head dim VE m + dt.
+    uint32_t vd[8][VE / 2];
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      const char* a = flash_at<FP8, D>(vl, 16 * (kk >> 2) + 4 * g4 + (kk & 3), VE * r);
       if constexpr (VE == 8) {
         const u32x2_t w = *(const u32x2_t*)a;
         e4m3x4_to_bf16(w.x, vd[kk][0], vd[kk][1]);
@@ -1616,26 +1689,27 @@ __device__ __forceinline__ void flash_tile(const char* kl, const char* vl, const
         e4m3x4_to_bf16(*(const uint32_t*)a, vd[kk][0], vd[kk][1]);
       }
     }
-  }
 #pragma unroll
-  for (int dt = 0; dt < VE; ++dt) {
-    const int w = dt >> 1;
-    u32x4_t va;
+    for (int dt = 0; dt < VE; ++dt) {
+      const int w = dt >> 1;
+      u32x4_t va;
 #pragma unroll
-    for (int q2 = 0; q2 < 4; ++q2) {
-      const uint32_t e0 = vd[2 * q2][w], e1 = vd[2 * q2 + 1][w];
-      va[q2] = (dt & 1) ? __builtin_amdgcn_perm(e1, e0, 0x07060302u) : __builtin_amdgcn_perm(e1, e0, 0x05040100u);
+      for (int q2 = 0; q2 < 4; ++q2) {
+        const uint32_t e0 = vd[2 * q2][w], e1 = vd[2 * q2 + 1][w];
+        va[q2] = (dt & 1) ? __builtin_amdgcn_perm(e1, e0, 0x07060302u) : __builtin_amdgcn_perm(e1, e0, 0x05040100u);
+      }
+#pragma unroll
+      for (int rg = 0; rg < RG; ++rg) S.o[rg][dt] = mfma_bf16(va, pf[rg], S.o[rg][dt]);
     }
-#pragma unroll
-    for (int rg = 0; rg < RG; ++rg) S.o[rg][dt] = mfma_bf16(va, pf[rg], S.o[rg][dt]);
   }
 }
 
 template <bool FP8, int D>
-__global__ void __launch_bounds__(256, 1) chunk_flash(ScanParams P) {
+__global__ void __launch_bounds__(256, 2) chunk_flash(ScanParams P) {
   constexpr int RG = kFlashRG, VE = D / 16, NC = D / 32;
+  constexpr int NBUF = 4;  // LDS tile ring: tile n in buffer n % NBUF, NBUF - 1 tiles in flight
   using FG = FlashGeom<FP8, D>;
-  __shared__ __align__(16) char tiles[2][FG::TILE];
+  __shared__ __align__(16) char tiles[NBUF][TileLoader<FP8, D, 2>::BYTES];
   const int lane = threadIdx.x & 63, tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15, g4 = lane >> 4;
@@ -1668,28 +1742,9 @@ __global__ void __launch_bounds__(256, 1) chunk_flash(ScanParams P) {
   float cs = P.scale_log2;
   if constexpr (FP8) cs *= P.k_scale[b * P.Hkv + g];
 
-  // this thread's 16-byte pieces of a tile: piece q = tid + 256 * i; K pieces
-  // first (32 rows x CH), then V; global row j0 + row (clamped to p_max)
-  auto gload = [&](u32x4_t (&dst)[FG::PER], int tile) {
-    if (tile >= ntile) return;
-    const int j0 = j_begin + 32 * tile;
-#pragma unroll
-    for (int i = 0; i < FG::PER; ++i) {
-      const int q = tid + 256 * i;
-      const int which = q / (32 * FG::CH), rem = q - which * 32 * FG::CH;
-      const int row = rem / FG::CH, gc = rem - row * FG::CH;
-      const int64_t j = min(j0 + row, p_max);
-      dst[i] = *(const u32x4_t*)((which ? vb : kb) + j * snb + 16 * gc);
-    }
-  };
-  auto lstore = [&](const u32x4_t (&src)[FG::PER], int buf) {
-#pragma unroll
-    for (int i = 0; i < FG::PER; ++i) {
-      const int q = tid + 256 * i;
-      const int which = q / (32 * FG::CH), rem = q - which * 32 * FG::CH;
-      const int row = rem / FG::CH, gc = rem - row * FG::CH;
-      *(u32x4_t*)(tiles[buf] + which * FG::HALF + row * FG::ROWB + ((gc ^ (row & (FG::CH - 1))) << 4)) = src[i];
-    }
+  const TileLoader<FP8, D, 2> ld(kb, vb, tid);
+  auto issue = [&](int tile) {
+    if (tile < ntile) ld.issue(tiles[tile % NBUF], j_begin + 32 * tile, p_max, snb, wave);
   };
 
   ChunkState<D, RG> S;
@@ -1702,28 +1757,15 @@ __global__ void __launch_bounds__(256, 1) chunk_flash(ScanParams P) {
   }
   auto compute = [&](int n) {
     const int j0 = j_begin + 32 * n;
-    const char* kl = tiles[n & 1];
+    const char* kl = tiles[n % NBUF];
     flash_tile<FP8, D, RG>(kl, kl + FG::HALF, qf, cs, j0, jlim, j0 + 31 > j_nomask, r, g4, S);
   };
-  // pipeline: tile n computed from LDS buffer n % 2 while tiles n+1..n+3 are
-  // in flight in the register ring; one workgroup barrier per tile
-  u32x4_t R0[FG::PER], R1[FG::PER], R2[FG::PER];
-  gload(R0, 0);
-  gload(R1, 1);
-  gload(R2, 2);
-  if (ntile > 0) lstore(R0, 0);
-  __syncthreads();
-  gload(R0, 3);
-  auto step = [&](int n, u32x4_t (&R)[FG::PER]) {
-    if (n < ntile) compute(n);
-    if (n + 1 < ntile) lstore(R, (n + 1) & 1);
-    __syncthreads();
-    gload(R, n + 4);
-  };
-  for (int n = 0; n < ntile; n += 3) {
-    step(n, R1);
-    step(n + 1, R2);
-    step(n + 2, R0);
+#pragma unroll
+  for (int t = 0; t < NBUF - 1; ++t) issue(t);
+  for (int n = 0; n < ntile; ++n) {
+    ring_wait<NBUF, TileLoader<FP8, D, 2>::PER>(n, ntile);
+    issue(n + NBUF - 1);
+    compute(n);
   }
 
   // partials of this wave's row groups (16 rows each)
@@ -1740,7 +1782,10 @@ __global__ void __launch_bounds__(256, 1) chunk_flash(ScanParams P) {
 #pragma unroll
     for (int dt = 0; dt < VE; ++dt)
 #pragma unroll
-      for (int ii = 0; ii < 4; ++ii) P.part_o[pb * D + VE * (4 * g4 + ii) + dt] = S.o[rg][dt][ii];
+      for (int ii = 0; ii < 4; ++ii) {
+        const int d = FP8 ? VE * (4 * g4 + ii) + dt : 16 * dt + 4 * g4 + ii;  // see flash_tile
+        P.part_o[pb * D + d] = S.o[rg][dt][ii];
+      }
     if (g4 == 0) {
       P.part_ml[pb * 2] = S.m[rg];
       P.part_ml[pb * 2 + 1] = l;
@@ -1920,6 +1965,162 @@ __global__ void __launch_bounds__(kChunkWaves * 64, 1) chunk_score(ScanParams P)
   if (j0 < j_end) {
     for (int q = lane; q < RG * TP * 32; q += 64) st[q] = 0.f;
     for (; j0 < j_end; j0 += STEP) stage_flush(j0);
+  }
+}
+
+// Score pass, LDS-staged form: the workgroup's 4 waves hold kFlashRG row
+// groups each (4 * kFlashRG packs per workgroup) and share every K tile
+// through the LDS ring; each wave stages its tokens' 32-position score rows
+// in LDS and writes them with 16-byte stores.
+template <bool FP8, int D, int G>
+__global__ void __launch_bounds__(256, 2) chunk_score_flash(ScanParams P) {
+  static_assert(G == 4 || G == 8 || G == 16, "chunk score pass: G in {4, 8, 16}");
+  constexpr int RG = kFlashRG, NC = D / 32, NBUF = 4;
+  constexpr int TP = 16 / G;  // tokens per row group
+  using FG = FlashGeom<FP8, D>;
+  using TL = TileLoader<FP8, D, 1>;
+  using RT = RawTile<FP8, D>;
+  __shared__ __align__(16) char tiles[NBUF][TL::BYTES];
+  __shared__ __align__(16) float stage[4][RG * TP * 32];
+  const int lane = threadIdx.x & 63, tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane & 15, g4 = lane >> 4;
+  const int nblk = (P.n_tpacks + 4 * RG - 1) / (4 * RG);
+  const ChunkItem it = chunk_item(P, nblk);
+  const int b = it.b, g = it.g;
+  const int blk_w = it.blk * 4 + wave;  // this wave's block of RG packs
+
+  // query fragments (row r of each group), and this lane's four S rows
+  // 4*g4 + ii: their token, causal limit and log2-sum-exp
+  // Rows past Tq (or past the pack) have a zero query, so their logits are 0;
+  // a log2-sum-exp of +inf turns them into exact zeros with no extra test.
+  u32x4_t qf[RG][NC];
+  int rl_lim[RG][4];
+  float rl_l2[RG][4];
+#pragma unroll
+  for (int rg = 0; rg < RG; ++rg) {
+    const ChunkRows cr = chunk_row<RG>(P, blk_w, rg, r);
+    load_q<FP8, D>(qf[rg], P, b, cr.ok ? cr.t : 0, g * P.G + (r % P.G), cr.ok, g4);
+    const int tp = blk_w * RG + rg;
+    const int unit = (b * P.n_tpacks + min(tp, P.n_tpacks - 1)) * P.Hkv + g;
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      const ChunkRows crr = chunk_row<RG>(P, blk_w, rg, 4 * g4 + ii);
+      rl_lim[rg][ii] = crr.jlim;  // -1 for such rows
+      rl_l2[rg][ii] = crr.ok ? P.lse2_in[(int64_t)unit * P.rows + 4 * g4 + ii] : __builtin_inff();
+    }
+  }
+  const int t_first = it.blk * 4 * RG * P.tpack;  // first token of the workgroup
+  const int t_last = min(t_first + 4 * RG * P.tpack, P.Tq) - 1;
+  const int p_max = P.q_pos0 + t_last;
+  const int wt_first = blk_w * RG * P.tpack;  // first token of this wave
+  const int j_nomask = P.q_pos0 + min(wt_first, P.Tq - 1);
+  const int j_begin = it.split * P.split_len;
+  const int j_end = min(j_begin + P.split_len, P.N);  // every position gets a score (0 past p)
+  const int j_load = min(j_end, p_max + 1);           // tiles starting below it are computed
+  const int ntile = j_load > j_begin ? (j_load - j_begin + 31) / 32 : 0;
+
+  const int64_t kvoff = ((int64_t)b * P.sb + (int64_t)g * P.sh) * FG::EB;
+  const char* kb = (const char*)P.k + kvoff;
+  const int64_t snb = P.sn * FG::EB;
+  float cs = P.scale_log2;
+  if constexpr (FP8) cs *= P.k_scale[b * P.Hkv + g];
+  const TL ld(kb, kb, tid);
+  auto issue = [&](int tile) {
+    if (tile < ntile) ld.issue(tiles[tile % NBUF], j_begin + 32 * tile, p_max, snb, wave);
+  };
+
+  // writers: one lane group per token (G = 4: every group; 8: even groups; 16: group 0)
+  const bool writer = (g4 % (G / 4)) == 0;
+  const int wtok = (4 * g4) / G;
+  float* st = stage[wave];
+  auto stage_flush = [&](int j0) {
+    for (int q = lane; q < RG * TP * 8; q += 64) {  // q: 4-float piece
+      const int row = q >> 3, pos = (q & 7) * 4;
+      const int rg = row / TP, tl = row - rg * TP;
+      const int t = (blk_w * RG + rg) * TP + tl;
+      const f32x4_t v = *(const f32x4_t*)(st + row * 32 + pos);
+      if (t >= P.Tq) continue;
+      float* dst = P.scores + (((int64_t)b * P.Tq + t) * P.Hkv + g) * P.N + j0 + pos;
+      if ((P.N & 3) == 0 && j0 + pos + 3 < P.N) {
+        *(f32x4_t*)dst = v;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (j0 + pos + e < P.N) dst[e] = v[e];
+      }
+    }
+  };
+  auto compute = [&](int n) {
+    const int j0 = j_begin + 32 * n;
+    const char* kl = tiles[n % NBUF];
+    u32x4_t kf[2][NC];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int row = 16 * hh + r;
+      if constexpr (!FP8) {
+#pragma unroll
+        for (int c = 0; c < NC; ++c) kf[hh][c] = *(const u32x4_t*)flash_at<FP8, D>(kl, row, 64 * c + 16 * g4);
+      } else {
+#pragma unroll
+        for (int ii = 0; ii < RT::KW; ++ii) {
+          const u32x4_t raw = *(const u32x4_t*)flash_at<FP8, D>(kl, row, 64 * ii + 16 * g4);
+          uint32_t a0, a1, a2, a3, b0, b1, b2, b3;
+          e4m3x4_to_bf16(raw.x, a0, a1);
+          e4m3x4_to_bf16(raw.y, a2, a3);
+          e4m3x4_to_bf16(raw.z, b0, b1);
+          e4m3x4_to_bf16(raw.w, b2, b3);
+          kf[hh][2 * ii] = u32x4_t{a0, a1, a2, a3};
+          kf[hh][2 * ii + 1] = u32x4_t{b0, b1, b2, b3};
+        }
+      }
+    }
+    // tiles ending at or before j_nomask lie inside every live row's window
+    const bool need_mask = j0 + 31 > j_nomask;
+    f32x4_t sacc[RG][2];
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) sacc[rg][hh] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) sacc[rg][hh] = mfma_bf16(qf[rg][c], kf[hh][c], sacc[rg][hh]);
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg) {
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int j = j0 + 16 * hh + r;  // this lane's position
+        float acc[4];
+        if (need_mask) {
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii) {
+            const float x = __builtin_fmaf(sacc[rg][hh][ii], cs, -rl_l2[rg][ii]);
+            acc[ii] = exp2_fast(j <= rl_lim[rg][ii] ? x : kNegInf);
+          }
+        } else {
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii) acc[ii] = exp2_fast(__builtin_fmaf(sacc[rg][hh][ii], cs, -rl_l2[rg][ii]));
+        }
+        const float v = head_sum_s<G>(acc);
+        if (writer) st[(rg * TP + wtok) * 32 + 16 * hh + r] = v;
+      }
+    }
+    stage_flush(j0);
+  };
+#pragma unroll
+  for (int t = 0; t < NBUF - 1; ++t) issue(t);
+  for (int n = 0; n < ntile; ++n) {
+    ring_wait<NBUF, TL::PER>(n, ntile);
+    issue(n + NBUF - 1);
+    compute(n);
+  }
+  // remaining tiles lie past every query position of the workgroup: zeros
+  if (ntile * 32 + j_begin < j_end) {
+    for (int q = lane; q < RG * TP * 32; q += 64) st[q] = 0.f;
+    for (int j0 = j_begin + 32 * ntile; j0 < j_end; j0 += 32) stage_flush(j0);
   }
 }
 
@@ -2611,17 +2812,25 @@ hipError_t launch_chunk_full(const ScanParams& p, int kv_dtype, hipStream_t s) {
 
 template <bool FP8, int D>
 void go_chunk_score(const ScanParams& p, dim3 grid, hipStream_t s) {
+#if HS2_CHUNK_FLASH
+  switch (p.G) {
+    case 4: hipLaunchKernelGGL((chunk_score_flash<FP8, D, 4>), grid, dim3(256), 0, s, p); break;
+    case 8: hipLaunchKernelGGL((chunk_score_flash<FP8, D, 8>), grid, dim3(256), 0, s, p); break;
+    default: hipLaunchKernelGGL((chunk_score_flash<FP8, D, 16>), grid, dim3(256), 0, s, p); break;
+  }
+#else
   switch (p.G) {
     case 4: hipLaunchKernelGGL((chunk_score<FP8, D, 4>), grid, dim3(kChunkWaves * 64), 0, s, p); break;
     case 8: hipLaunchKernelGGL((chunk_score<FP8, D, 8>), grid, dim3(kChunkWaves * 64), 0, s, p); break;
     default: hipLaunchKernelGGL((chunk_score<FP8, D, 16>), grid, dim3(kChunkWaves * 64), 0, s, p); break;
   }
+#endif
 }
 
 hipError_t launch_chunk_score(const ScanParams& p, int kv_dtype, hipStream_t s) {
   if (p.G != 4 && p.G != 8 && p.G != 16) return hipErrorInvalidValue;
-  const int rg = chunk_rg(kv_dtype, p.D);
-  const int nblk = (p.n_tpacks + rg - 1) / rg;
+  const int packs = HS2_CHUNK_FLASH ? 4 * kFlashRG : chunk_rg(kv_dtype, p.D);
+  const int nblk = (p.n_tpacks + packs - 1) / packs;
   const dim3 grid(p.B * nblk * p.Hkv * p.nsplit);
   TimedLaunch tl("chunk_score", s);
   if (kv_dtype == HS2_FP8_E4M3FN) {

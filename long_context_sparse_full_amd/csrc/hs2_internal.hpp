@@ -77,11 +77,11 @@ constexpr int kChunkWaves = 4;
 // LDS and each wave holds kFlashRG row groups, 4 * kFlashRG packs per
 // workgroup.
 #ifndef HS2_CHUNK_FLASH
-#define HS2_CHUNK_FLASH 0
+#define HS2_CHUNK_FLASH 1
 #endif
 // Chunk position splits: about this many full-pass work items in all.
 #ifndef HS2_CHUNK_TARGET_WGS
-#define HS2_CHUNK_TARGET_WGS 3072
+#define HS2_CHUNK_TARGET_WGS 1024
 #endif
 constexpr int kFlashRG = 2;
 __host__ __device__ constexpr int chunk_full_packs(int kv_dtype, int D) {
