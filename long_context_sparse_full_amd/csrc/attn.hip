@@ -1507,10 +1507,21 @@ struct FlashGeom {
   static constexpr int TILE = 2 * HALF;        // one LDS tile buffer
 };
 
-template <bool FP8, int D>
+// LDS swizzle of a tile row: 16-byte chunk c of row `row` sits at chunk
+// c ^ flash_swz(row).  Chosen by measured bank conflicts (SQ_LDS_BANK_CONFLICT):
+// the 16-byte K fragment reads (16 consecutive rows, one chunk each) are
+// conflict-free with row & (CH - 1); the transposing 8-byte V reads (4
+// consecutive rows x 2 adjacent chunks per 16 lanes) are with
+// 2 (row & 7) + bit 3 of the row on 256-byte rows.
+template <int CH, bool VPART>
+__device__ __forceinline__ int flash_swz(int row) {
+  if constexpr (VPART && CH == 16) return 2 * (row & 7) + ((row >> 3) & 1);
+  return row & (CH - 1);
+}
+template <bool FP8, int D, bool VPART = false>
 __device__ __forceinline__ const char* flash_at(const char* base, int row, int byte) {
   using FG = FlashGeom<FP8, D>;
-  return base + row * FG::ROWB + ((((byte >> 4) ^ (row & (FG::CH - 1)))) << 4) + (byte & 15);
+  return base + row * FG::ROWB + (((byte >> 4) ^ flash_swz<FG::CH, VPART>(row)) << 4) + (byte & 15);
 }
 
 // wait until at most N vector-memory operations of this wave are in flight
@@ -1520,12 +1531,27 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// One 16-byte global -> LDS load per lane: lane l's 16 bytes at sbase + voff
+// land at LDS byte address lds + 16 l (M0 holds lds).  Written as inline asm
+// so the compiler does not treat it as an LDS store of unknown extent and
+// stall every later LDS read until the newest tile has landed: the ring below
+// orders these loads and the reads with explicit waits and barriers.
+__device__ __forceinline__ void lds_dma16(const char* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds)
+               : "memory", "m0");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
+}
+
 // Tile loads straight from global memory into LDS (16 bytes per lane) for a
 // 256-thread workgroup: load i of thread tid fills LDS slot s = 256 i + tid
 // of the tile (PARTS = 1: K rows; 2: K rows then V rows, 32 rows x CH chunks
 // each), a wave-contiguous 1 KiB per instruction.  Slot (row, c) holds chunk
-// c ^ (row & (CH - 1)) of the row, the swizzle flash_at() undoes; rows past
-// p_max are clamped to it.  Waves whose slots lie past the tile issue nothing.
+// c ^ flash_swz(row) of the row (per part), the swizzle flash_at() undoes;
+// rows past p_max are clamped to it.  Waves whose slots lie past the tile
+// issue nothing.  Row offsets are 32-bit (32 rows x the row stride < 2 GiB,
+// checked by the launcher).
 template <bool FP8, int D, int PARTS>
 struct TileLoader {
   using FG = FlashGeom<FP8, D>;
@@ -1533,25 +1559,32 @@ struct TileLoader {
   static constexpr int PER = (SLOTS + 255) / 256;  // loads per thread per tile
   static constexpr int BYTES = PARTS * FG::HALF;   // one LDS tile buffer
   int prow[PER];
-  const char* pbase[PER];
-  __device__ __forceinline__ TileLoader(const char* kb, const char* vb, int tid) {
+  uint32_t coff[PER];  // byte offset of the chunk within its row
+  const char* kb;
+  const char* vb;
+  int64_t snb;
+  int wave;
+  __device__ __forceinline__ TileLoader(const char* kb_, const char* vb_, int64_t snb_, int tid, int wave_)
+      : kb(kb_), vb(vb_), snb(snb_), wave(wave_) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int s = min(256 * i + tid, SLOTS - 1);
       const int which = s / (32 * FG::CH), rem = s - which * 32 * FG::CH;
       const int row = rem / FG::CH, pos = rem - row * FG::CH;
       prow[i] = row;
-      pbase[i] = (which ? vb : kb) + 16 * (pos ^ (row & (FG::CH - 1)));
+      coff[i] = 16u * (uint32_t)(pos ^ (which ? flash_swz<FG::CH, true>(row) : flash_swz<FG::CH, false>(row)));
     }
   }
-  __device__ __forceinline__ void issue(char* dst, int j0, int p_max, int64_t snb, int wave) const {
+  __device__ __forceinline__ void issue(const char* dst, int j0, int p_max) const {
+    const int lim = p_max - j0;  // rows past it repeat row p_max
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      if (256 * i + 64 * wave >= SLOTS) continue;  // wave-uniform
-      const int64_t j = min(j0 + prow[i], p_max);
-      __builtin_amdgcn_global_load_lds((const void*)(pbase[i] + j * snb),
-                                       (__attribute__((address_space(3))) void*)(dst + 16 * (256 * i + 64 * wave)), 16,
-                                       0, 0);
+      const int s0 = 256 * i + 64 * wave;  // wave-uniform
+      if (s0 >= SLOTS) continue;
+      const bool vpart = s0 >= 32 * FG::CH;
+      const char* base = (vpart ? vb : kb) + (int64_t)j0 * snb;
+      const uint32_t voff = (uint32_t)(min(prow[i], lim) * (int)snb) + coff[i];
+      lds_dma16(base, voff, lds_addr(dst + 16 * s0));
     }
   }
 };
@@ -1562,10 +1595,10 @@ struct TileLoader {
 // wave and the buffer of tile n - 1 is free for tile n + NBUF - 1.
 template <int NBUF, int PER>
 __device__ __forceinline__ void ring_wait(int n, int ntile) {
-  static_assert(NBUF == 4, "wait counts below assume a 4-buffer ring");
+  static_assert(NBUF == 3 || NBUF == 4, "ring of 3 or 4 buffers");
   const int ahead = min(NBUF - 2, ntile - 1 - n);  // tiles issued after tile n
-  if (ahead >= 2) wait_vm<2 * PER>();
-  else if (ahead == 1) wait_vm<PER>();
+  if (NBUF == 4 && ahead >= 2) wait_vm<2 * PER>();
+  else if (ahead >= 1) wait_vm<PER>();
   else wait_vm<0>();
   __syncthreads();
 }
@@ -1663,7 +1696,7 @@ __device__ __forceinline__ void flash_tile(const char* kl, const char* vl, const
       u32x4_t va;
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        const char* src = flash_at<FP8, D>(vl, 16 * c + 4 * g4 + k4, 32 * dt + 8 * a4);
+        const char* src = flash_at<FP8, D, true>(vl, 16 * c + 4 * g4 + k4, 32 * dt + 8 * a4);
         const s16x4_t t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)src);
         const u32x2_t w = __builtin_bit_cast(u32x2_t, t);
         va[2 * c] = w.x;
@@ -1680,7 +1713,7 @@ __device__ __forceinline__ void flash_tile(const char* kl, const char* vl, const
     uint32_t vd[8][VE / 2];
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
-      const char* a = flash_at<FP8, D>(vl, 16 * (kk >> 2) + 4 * g4 + (kk & 3), VE * r);
+      const char* a = flash_at<FP8, D, true>(vl, 16 * (kk >> 2) + 4 * g4 + (kk & 3), VE * r);
       if constexpr (VE == 8) {
         const u32x2_t w = *(const u32x2_t*)a;
         e4m3x4_to_bf16(w.x, vd[kk][0], vd[kk][1]);
@@ -1704,10 +1737,16 @@ __device__ __forceinline__ void flash_tile(const char* kl, const char* vl, const
   }
 }
 
+#ifndef HS2_FLASH_NBUF
+#define HS2_FLASH_NBUF 4
+#endif
+#ifndef HS2_FLASH_OCC
+#define HS2_FLASH_OCC 2
+#endif
 template <bool FP8, int D>
-__global__ void __launch_bounds__(256, 2) chunk_flash(ScanParams P) {
+__global__ void __launch_bounds__(256, HS2_FLASH_OCC) chunk_flash(ScanParams P) {
   constexpr int RG = kFlashRG, VE = D / 16, NC = D / 32;
-  constexpr int NBUF = 4;  // LDS tile ring: tile n in buffer n % NBUF, NBUF - 1 tiles in flight
+  constexpr int NBUF = HS2_FLASH_NBUF;  // LDS tile ring: tile n in buffer n % NBUF, NBUF - 1 tiles in flight
   using FG = FlashGeom<FP8, D>;
   __shared__ __align__(16) char tiles[NBUF][TileLoader<FP8, D, 2>::BYTES];
   const int lane = threadIdx.x & 63, tid = threadIdx.x;
@@ -1742,9 +1781,9 @@ __global__ void __launch_bounds__(256, 2) chunk_flash(ScanParams P) {
   float cs = P.scale_log2;
   if constexpr (FP8) cs *= P.k_scale[b * P.Hkv + g];
 
-  const TileLoader<FP8, D, 2> ld(kb, vb, tid);
+  const TileLoader<FP8, D, 2> ld(kb, vb, snb, tid, wave);
   auto issue = [&](int tile) {
-    if (tile < ntile) ld.issue(tiles[tile % NBUF], j_begin + 32 * tile, p_max, snb, wave);
+    if (tile < ntile) ld.issue(tiles[tile % NBUF], j_begin + 32 * tile, p_max);
   };
 
   ChunkState<D, RG> S;
@@ -1760,6 +1799,9 @@ __global__ void __launch_bounds__(256, 2) chunk_flash(ScanParams P) {
     const char* kl = tiles[n % NBUF];
     flash_tile<FP8, D, RG>(kl, kl + FG::HALF, qf, cs, j0, jlim, j0 + 31 > j_nomask, r, g4, S);
   };
+  // the query loads complete here, so the compiler's own wait bookkeeping has
+  // nothing pending across the loop (the tile loads are invisible to it)
+  wait_vm<0>();
 #pragma unroll
   for (int t = 0; t < NBUF - 1; ++t) issue(t);
   for (int n = 0; n < ntile; ++n) {
@@ -2025,9 +2067,9 @@ __global__ void __launch_bounds__(256, 2) chunk_score_flash(ScanParams P) {
   const int64_t snb = P.sn * FG::EB;
   float cs = P.scale_log2;
   if constexpr (FP8) cs *= P.k_scale[b * P.Hkv + g];
-  const TL ld(kb, kb, tid);
+  const TL ld(kb, kb, snb, tid, wave);
   auto issue = [&](int tile) {
-    if (tile < ntile) ld.issue(tiles[tile % NBUF], j_begin + 32 * tile, p_max, snb, wave);
+    if (tile < ntile) ld.issue(tiles[tile % NBUF], j_begin + 32 * tile, p_max);
   };
 
   // writers: one lane group per token (G = 4: every group; 8: even groups; 16: group 0)
@@ -2110,6 +2152,8 @@ __global__ void __launch_bounds__(256, 2) chunk_score_flash(ScanParams P) {
     }
     stage_flush(j0);
   };
+  // query and log-sum-exp loads complete before the tile loads start
+  wait_vm<0>();
 #pragma unroll
   for (int t = 0; t < NBUF - 1; ++t) issue(t);
   for (int n = 0; n < ntile; ++n) {
@@ -2783,9 +2827,16 @@ int fused_max_workgroups(int kv_dtype, int D) {
   return n;
 }
 
+// LDS-staged chunk kernels address a tile's rows with 32-bit offsets
+bool flash_rows_fit(const ScanParams& p, int kv_dtype) {
+  const int64_t snb = p.sn * (kv_dtype == HS2_FP8_E4M3FN ? 1 : 2);
+  return snb > 0 && snb < (int64_t(1) << 26);
+}
+
 hipError_t launch_chunk_full(const ScanParams& p, int kv_dtype, hipStream_t s) {
   TimedLaunch tl("chunk_full", s);
 #if HS2_CHUNK_FLASH
+  if (!flash_rows_fit(p, kv_dtype)) return hipErrorInvalidValue;
   const int nblk = (p.n_tpacks + 4 * kFlashRG - 1) / (4 * kFlashRG);  // chunk_full_packs()
   const dim3 grid(p.B * nblk * p.Hkv * p.nsplit);
   if (kv_dtype == HS2_FP8_E4M3FN) {
@@ -2829,6 +2880,7 @@ void go_chunk_score(const ScanParams& p, dim3 grid, hipStream_t s) {
 
 hipError_t launch_chunk_score(const ScanParams& p, int kv_dtype, hipStream_t s) {
   if (p.G != 4 && p.G != 8 && p.G != 16) return hipErrorInvalidValue;
+  if (HS2_CHUNK_FLASH && !flash_rows_fit(p, kv_dtype)) return hipErrorInvalidValue;
   const int packs = HS2_CHUNK_FLASH ? 4 * kFlashRG : chunk_rg(kv_dtype, p.D);
   const int nblk = (p.n_tpacks + packs - 1) / packs;
   const dim3 grid(p.B * nblk * p.Hkv * p.nsplit);
