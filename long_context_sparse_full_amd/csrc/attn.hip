@@ -1241,6 +1241,7 @@ template <int D, int RG>
 struct ChunkState {
   float m[RG], l[RG];
   f32x4_t o[RG][D / 16];
+  float mu[RG], thr[RG];  // LDS-staged form: exponent offset and move threshold
 };
 
 struct ChunkItem {
@@ -1603,11 +1604,12 @@ __device__ __forceinline__ void ring_wait(int n, int ntile) {
   __syncthreads();
 }
 
+// QK^T of one tile from LDS: s[rg][hh] = the S^T block of positions
+// 16 hh + (0..15) and row group rg.
 template <bool FP8, int D, int RG>
-__device__ __forceinline__ void flash_tile(const char* kl, const char* vl, const u32x4_t (&qf)[RG][D / 32], float cs,
-                                           int j0, const int (&jlim)[RG], bool need_mask, int r, int g4,
-                                           ChunkState<D, RG>& S) {
-  constexpr int NC = D / 32, VE = D / 16;
+__device__ __forceinline__ void flash_qk(const char* kl, const u32x4_t (&qf)[RG][D / 32], int r, int g4,
+                                         f32x4_t (&s)[RG][2]) {
+  constexpr int NC = D / 32;
   using RT = RawTile<FP8, D>;
   // K fragments (A of S^T): row 16*hh + r, bytes 64*c + 16*g4 of the row
   u32x4_t kf[2][NC];
@@ -1631,7 +1633,6 @@ __device__ __forceinline__ void flash_tile(const char* kl, const char* vl, const
       }
     }
   }
-  f32x4_t s[RG][2];
 #pragma unroll
   for (int rg = 0; rg < RG; ++rg)
 #pragma unroll
@@ -1642,10 +1643,21 @@ __device__ __forceinline__ void flash_tile(const char* kl, const char* vl, const
     for (int rg = 0; rg < RG; ++rg)
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) s[rg][hh] = mfma_bf16(kf[hh][c], qf[rg][c], s[rg][hh]);
+}
+
+// Softmax and PV of one tile whose logits s came from flash_qk.
+template <bool FP8, int D, int RG>
+__device__ __forceinline__ void flash_pv(const char* vl, f32x4_t (&s)[RG][2], float cs, int j0,
+                                         const int (&jlim)[RG], bool need_mask, int r, int g4, ChunkState<D, RG>& S) {
+  constexpr int VE = D / 16;
+  // Online softmax against each row's reference S.m (mu = S.m, or 0 before
+  // the row has one).  The exponents x = s cs - mu are formed first; only when
+  // some lane's x exceeds thr (kLazyMax, or -inf for a row with no reference
+  // yet) does the rare path take the row maximum across lanes and move the
+  // reference, rescaling that row's accumulators.
   u32x4_t pf[RG];
 #pragma unroll
   for (int rg = 0; rg < RG; ++rg) {
-    float tmax = kNegInf;
     if (need_mask) {
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh)
@@ -1653,30 +1665,36 @@ __device__ __forceinline__ void flash_tile(const char* kl, const char* vl, const
         for (int ii = 0; ii < 4; ++ii)
           if (j0 + 16 * hh + 4 * g4 + ii > jlim[rg]) s[rg][hh][ii] = kNegInf;
     }
+    float x[2][4];
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-      for (int ii = 0; ii < 4; ++ii) tmax = fmaxf(tmax, s[rg][hh][ii]);
-    tmax = max_x16(tmax);
-    tmax = max_x32(tmax);
-    tmax *= cs;
-    const bool move = tmax > S.m[rg] + kLazyMax;
-    if (__any(move)) {
-      const float m_new = move ? tmax : S.m[rg];
-      const float alpha = (S.m[rg] == kNegInf) ? 0.f : exp2_fast(S.m[rg] - m_new);
+      for (int ii = 0; ii < 4; ++ii) x[hh][ii] = __builtin_fmaf(s[rg][hh][ii], cs, -S.mu[rg]);
+    const float xm = fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])),
+                           fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])));
+    if (__any(xm > S.thr[rg])) {
+      const float rmax = max_x32(max_x16(xm));  // the row's largest exponent
+      const bool move = rmax > S.thr[rg];       // uniform over the row's lanes
+      const float m_new = move ? S.mu[rg] + rmax : S.m[rg];
+      const float alpha = !move ? 1.f : (S.m[rg] == kNegInf) ? 0.f : exp2_fast(S.m[rg] - m_new);
       S.l[rg] *= alpha;
 #pragma unroll
       for (int dt = 0; dt < VE; ++dt) S.o[rg][dt] *= alpha;
       S.m[rg] = m_new;
+      S.mu[rg] = move ? m_new : S.mu[rg];
+      S.thr[rg] = move ? kLazyMax : S.thr[rg];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) x[hh][ii] = __builtin_fmaf(s[rg][hh][ii], cs, -S.mu[rg]);
     }
-    const float m_use = (S.m[rg] == kNegInf) ? 0.f : S.m[rg];
     float pr[2][4];
     float psum = 0.f;
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
-        pr[hh][ii] = exp2_fast(__builtin_fmaf(s[rg][hh][ii], cs, -m_use));
+        pr[hh][ii] = exp2_fast(x[hh][ii]);
         psum += pr[hh][ii];
       }
     S.l[rg] += psum;
@@ -1791,13 +1809,17 @@ __global__ void __launch_bounds__(256, HS2_FLASH_OCC) chunk_flash(ScanParams P) 
   for (int rg = 0; rg < RG; ++rg) {
     S.m[rg] = kNegInf;
     S.l[rg] = 0.f;
+    S.mu[rg] = 0.f;
+    S.thr[rg] = kNegInf;
 #pragma unroll
     for (int dt = 0; dt < VE; ++dt) S.o[rg][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
   auto compute = [&](int n) {
     const int j0 = j_begin + 32 * n;
     const char* kl = tiles[n % NBUF];
-    flash_tile<FP8, D, RG>(kl, kl + FG::HALF, qf, cs, j0, jlim, j0 + 31 > j_nomask, r, g4, S);
+    f32x4_t sc[RG][2];
+    flash_qk<FP8, D, RG>(kl, qf, r, g4, sc);
+    flash_pv<FP8, D, RG>(kl + FG::HALF, sc, cs, j0, jlim, j0 + 31 > j_nomask, r, g4, S);
   };
   // the query loads complete here, so the compiler's own wait bookkeeping has
   // nothing pending across the loop (the tile loads are invisible to it)
