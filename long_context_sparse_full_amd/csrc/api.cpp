@@ -88,12 +88,11 @@ FullPlan plan_full(const hs2_kv_desc* kv, int Tq, int Hq) {
   p.rows = p.tpack * G;
   p.units = kv->B * p.n_tpacks * kv->Hkv;
   const bool g_pow2 = G == 4 || G == 8 || G == 16;  // the chunk score pass sums heads in 4-row lane groups
-  const int rg = hs2::chunk_rg(kv->dtype, kv->D);
-  p.chunk = !f32 && g_pow2 && p.n_tpacks >= rg;
+  p.chunk = !f32 && g_pow2 && p.n_tpacks >= hs2::kChunkMinPacks;
   if (p.chunk) {  // work items (b, block of packs, g) x position splits, HS2_CHUNK_TARGET_WGS in all
-    const int64_t items = (int64_t)kv->B * cdiv(p.n_tpacks, hs2::chunk_full_packs(kv->dtype, kv->D)) * kv->Hkv;
+    const int64_t items = (int64_t)kv->B * cdiv(p.n_tpacks, hs2::kChunkPacks) * kv->Hkv;
     const int64_t per_item = std::max<int64_t>(1, HS2_CHUNK_TARGET_WGS / items);
-    p.split_len = (int)rup(cdiv(kv->N, per_item), 32 * hs2::kChunkWaves);
+    p.split_len = (int)rup(cdiv(kv->N, per_item), 128);  // whole 32-position tiles
   } else {
     const int64_t per_unit = std::max<int64_t>(1, HS2_SCAN_TARGET_WGS / p.units);
     const int64_t quantum = f32 ? 64 : 256;

@@ -1225,23 +1225,24 @@ __global__ void __launch_bounds__(WAVES * 64, 1) scan_fused(ScanParams P) {
 }
 
 // ---------------------------------------------------------------------------
-// Multi-query chunk full layer (many query tokens per kv head).  A wave keeps
-// RG groups of 16 query rows (tpack tokens x G heads) and reuses every K/V
-// tile it loads for all of them: S^T = K Q^T and O^T += V^T P^T on MFMA as in
-// the decode scan, RG times per tile.  Work item = (b, token block of
-// RG * tpack tokens, kv head, position split); waves take interleaved
-// 32-position tiles of the split.  Pass 1 writes the split partials of each
-// 16-row group in the decode layout (unit = (b, 2-token pack, g)), merged by
-// the combine kernel; pass 2 recomputes the logits and writes the scores
-// against the merged log-sum-exp, so no per-head scratch is stored.
-// Linear work index: split fastest, then kv head, so the workgroups that read
-// the same K/V range (same head and split, all token blocks) share an XCD.
+// Multi-query chunk (many query tokens per kv head).  A workgroup of 4 waves
+// covers 4 x kFlashRG groups of 16 query rows (tpack tokens x G heads each) of
+// one (b, kv head) over a position split.  Every 32-position K/V tile is
+// fetched once by the whole workgroup straight from global memory into an LDS
+// ring (4 buffers, one barrier per tile); each wave reads its MFMA fragments
+// from LDS for its own row groups: S^T = K Q^T and O^T += V^T P^T as in the
+// decode scan.  Pass 1 writes the split partials of each 16-row group in the
+// decode layout (unit = (b, pack, g)), merged by the combine kernel; pass 2
+// recomputes the logits and writes the scores against the merged
+// log-sum-exp, so no per-head scratch is stored.  Linear work index: split
+// fastest, then kv head, so the workgroups that read the same K/V range
+// (same head and split, all token blocks) share an XCD.
 // ---------------------------------------------------------------------------
 template <int D, int RG>
 struct ChunkState {
   float m[RG], l[RG];
   f32x4_t o[RG][D / 16];
-  float mu[RG], thr[RG];  // LDS-staged form: exponent offset and move threshold
+  float mu[RG], thr[RG];  // exponent offset (m, or 0 before a reference) and move threshold
 };
 
 struct ChunkItem {
@@ -1257,118 +1258,6 @@ __device__ __forceinline__ ChunkItem chunk_item(const ScanParams& P, int nblk) {
   c.blk = L % nblk;
   c.b = L / nblk;
   return c;
-}
-
-// One 32-position tile for RG row groups.  K (decoded once for FP8) and the
-// V^T operand of each head-dim block (byte permutes of the V slices) feed
-// every group.
-template <bool FP8, int D, int RG>
-__device__ __forceinline__ void chunk_tile(const RawTile<FP8, D>& R, const u32x4_t (&qf)[RG][D / 32], float cs,
-                                           int j0, const int (&jlim)[RG], bool need_mask, int g4,
-                                           ChunkState<D, RG>& S) {
-  constexpr int NC = D / 32, VE = D / 16;
-  u32x4_t kf[2][NC];
-  uint32_t vd[8][VE / 2];
-  if constexpr (!FP8) {
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-      for (int c = 0; c < NC; ++c) kf[hh][c] = R.k[hh][c];
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk)
-#pragma unroll
-      for (int w = 0; w < VE / 2; ++w) vd[kk][w] = R.v[kk][w];
-  } else {
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-      for (int ii = 0; ii < NC / 2; ++ii) {
-        const u32x4_t raw = R.k[hh][ii];
-        uint32_t a0, a1, a2, a3, b0, b1, b2, b3;
-        e4m3x4_to_bf16(raw.x, a0, a1);
-        e4m3x4_to_bf16(raw.y, a2, a3);
-        e4m3x4_to_bf16(raw.z, b0, b1);
-        e4m3x4_to_bf16(raw.w, b2, b3);
-        kf[hh][2 * ii] = u32x4_t{a0, a1, a2, a3};
-        kf[hh][2 * ii + 1] = u32x4_t{b0, b1, b2, b3};
-      }
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      e4m3x4_to_bf16(R.v[kk][0], vd[kk][0], vd[kk][1]);
-      if constexpr (VE == 8) e4m3x4_to_bf16(R.v[kk][1], vd[kk][2], vd[kk][3]);
-    }
-  }
-  // QK^T for every row group, chains interleaved so the matrix pipe always has
-  // independent work
-  f32x4_t s[RG][2];
-#pragma unroll
-  for (int rg = 0; rg < RG; ++rg)
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) s[rg][hh] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int c = 0; c < NC; ++c)
-#pragma unroll
-    for (int rg = 0; rg < RG; ++rg)
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) s[rg][hh] = mfma_bf16(kf[hh][c], qf[rg][c], s[rg][hh]);
-  // online softmax per row group.  A row's reference maximum only moves when
-  // its tile maximum exceeds it by more than kLazyMax (log2 units); until then
-  // the probabilities are taken against the stale reference (at most
-  // 2^kLazyMax), so the accumulators are rarely rescaled.
-  u32x4_t pf[RG];
-#pragma unroll
-  for (int rg = 0; rg < RG; ++rg) {
-    float tmax = kNegInf;
-    if (need_mask) {
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii)
-          if (j0 + 16 * hh + 4 * g4 + ii > jlim[rg]) s[rg][hh][ii] = kNegInf;
-    }
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) tmax = fmaxf(tmax, s[rg][hh][ii]);
-    tmax = max_x16(tmax);
-    tmax = max_x32(tmax);
-    tmax *= cs;  // cs > 0: the maximum of the scaled logits
-    const bool move = tmax > S.m[rg] + kLazyMax;
-    if (__any(move)) {
-      const float m_new = move ? tmax : S.m[rg];
-      const float alpha = (S.m[rg] == kNegInf) ? 0.f : exp2_fast(S.m[rg] - m_new);
-      S.l[rg] *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < VE; ++dt) S.o[rg][dt] *= alpha;
-      S.m[rg] = m_new;
-    }
-    const float m_use = (S.m[rg] == kNegInf) ? 0.f : S.m[rg];
-    float pr[2][4];
-    float psum = 0.f;
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        pr[hh][ii] = exp2_fast(__builtin_fmaf(s[rg][hh][ii], cs, -m_use));
-        psum += pr[hh][ii];
-      }
-    S.l[rg] += psum;
-    pf[rg] = u32x4_t{pack_bf16(pr[0][0], pr[0][1]), pack_bf16(pr[0][2], pr[0][3]), pack_bf16(pr[1][0], pr[1][1]),
-                     pack_bf16(pr[1][2], pr[1][3])};
-  }
-  // PV: each V^T operand built once, used by every row group
-#pragma unroll
-  for (int dt = 0; dt < VE; ++dt) {
-    const int w = dt >> 1;
-    u32x4_t va;
-#pragma unroll
-    for (int q2 = 0; q2 < 4; ++q2) {
-      const uint32_t e0 = vd[2 * q2][w], e1 = vd[2 * q2 + 1][w];
-      va[q2] = (dt & 1) ? __builtin_amdgcn_perm(e1, e0, 0x07060302u) : __builtin_amdgcn_perm(e1, e0, 0x05040100u);
-    }
-#pragma unroll
-    for (int rg = 0; rg < RG; ++rg) S.o[rg][dt] = mfma_bf16(va, pf[rg], S.o[rg][dt]);
-  }
 }
 
 // Per-lane row data of a chunk work item: the query token of row r in group rg
@@ -1387,117 +1276,6 @@ __device__ __forceinline__ ChunkRows chunk_row(const ScanParams& P, int blk, int
   c.jlim = c.ok ? P.q_pos0 + c.t : -1;
   return c;
 }
-
-template <bool FP8, int D>
-__global__ void __launch_bounds__(kChunkWaves * 64, 1) chunk_full(ScanParams P) {
-  constexpr int RG = chunk_rg(FP8 ? HS2_FP8_E4M3FN : HS2_BF16, D), WAVES = kChunkWaves, VE = D / 16, NC = D / 32, EB = FP8 ? 1 : 2;
-  constexpr int STEP = WAVES * 32;
-  __shared__ float sm_m[WAVES][16];
-  __shared__ float sm_l[WAVES][16];
-  __shared__ float sm_o[WAVES][16][D + 1];
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int r = lane & 15, g4 = lane >> 4;
-  const int nblk = (P.n_tpacks + RG - 1) / RG;
-  const ChunkItem it = chunk_item(P, nblk);
-  const int b = it.b, g = it.g;
-
-  u32x4_t qf[RG][NC];
-  int jlim[RG];
-  int t_first = P.Tq, t_last = 0;
-#pragma unroll
-  for (int rg = 0; rg < RG; ++rg) {
-    const ChunkRows cr = chunk_row<RG>(P, it.blk, rg, r);
-    jlim[rg] = cr.jlim;
-    load_q<FP8, D>(qf[rg], P, b, cr.ok ? cr.t : 0, g * P.G + (r % P.G), cr.ok, g4);
-  }
-  t_first = it.blk * RG * P.tpack;
-  t_last = min(t_first + RG * P.tpack, P.Tq) - 1;
-  const int p_max = P.q_pos0 + t_last;
-  const int j_nomask = P.q_pos0 + t_first;  // tiles ending at or before it need no mask
-  const int j_begin = it.split * P.split_len;
-  const int j_end = min(j_begin + P.split_len, p_max + 1);
-
-  const int64_t kvoff = ((int64_t)b * P.sb + (int64_t)g * P.sh) * EB;
-  const char* kb = (const char*)P.k + kvoff;
-  const char* vb = (const char*)P.v + kvoff;
-  const int64_t snb = P.sn * EB;
-  float cs = P.scale_log2;
-  if constexpr (FP8) cs *= P.k_scale[b * P.Hkv + g];
-  uint32_t koff[2], voff[8];
-#pragma unroll
-  for (int hh = 0; hh < 2; ++hh) koff[hh] = (uint32_t)((16 * hh + r) * snb) + 16u * g4;
-#pragma unroll
-  for (int kk = 0; kk < 8; ++kk)
-    voff[kk] = (uint32_t)((16 * (kk >> 2) + 4 * g4 + (kk & 3)) * snb) + (uint32_t)(VE * r * EB);
-
-  ChunkState<D, RG> S;
-#pragma unroll
-  for (int rg = 0; rg < RG; ++rg) {
-    S.m[rg] = kNegInf;
-    S.l[rg] = 0.f;
-#pragma unroll
-    for (int dt = 0; dt < VE; ++dt) S.o[rg][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  }
-  auto load = [&](RawTile<FP8, D>& R, int j0) {
-    const char* kp[2];
-    const char* vp[8];
-    if (j0 + 31 <= p_max) {
-      const char* tk = kb + (int64_t)j0 * snb;
-      const char* tv = vb + (int64_t)j0 * snb;
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) kp[hh] = tk + koff[hh];
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk) vp[kk] = tv + voff[kk];
-    } else {
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) kp[hh] = kb + (int64_t)min(j0 + 16 * hh + r, p_max) * snb + 16 * g4;
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk)
-        vp[kk] = vb + (int64_t)min(j0 + 16 * (kk >> 2) + 4 * g4 + (kk & 3), p_max) * snb + VE * r * EB;
-    }
-    load_tile<FP8, D, false>(R, kp, vp);
-  };
-  {
-    RawTile<FP8, D> A, B;
-    int j0 = j_begin + wave * 32;
-    if (j0 < j_end) load(A, j0);
-    while (j0 < j_end) {  // ping-pong: load tile n+1 while computing tile n
-      const int j1 = j0 + STEP;
-      if (j1 < j_end) load(B, j1);
-      chunk_tile<FP8, D, RG>(A, qf, cs, j0, jlim, j0 + 31 > j_nomask, g4, S);
-      if (j1 >= j_end) break;
-      const int j2 = j1 + STEP;
-      if (j2 < j_end) load(A, j2);
-      chunk_tile<FP8, D, RG>(B, qf, cs, j1, jlim, j1 + 31 > j_nomask, g4, S);
-      j0 = j2;
-    }
-  }
-  // merge the waves per row group and store that group's split partial
-#pragma unroll
-  for (int rg = 0; rg < RG; ++rg) {
-    const int tp = it.blk * RG + rg;
-    WaveState<D> W;
-    W.m = S.m[rg];
-    W.l = S.l[rg];
-#pragma unroll
-    for (int dt = 0; dt < VE; ++dt) W.o[dt] = S.o[rg][dt];
-    const int unit = (b * P.n_tpacks + min(tp, P.n_tpacks - 1)) * P.Hkv + g;
-    if (tp < P.n_tpacks)  // uniform over the workgroup
-      merge_and_store<FP8, D, false, WAVES>(P, W, unit, it.split, b, g, wave, r, g4, sm_m, sm_l, sm_o);
-    __syncthreads();
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Chunk full layer, LDS-staged form.  A workgroup of 4 waves covers 4 x
-// kFlashRG row groups of one (b, kv head) over a position split; every
-// 32-position K/V tile is fetched once by the whole workgroup (16-byte pieces,
-// three tiles ahead in registers), stored to one of two LDS tile buffers with
-// the 16-byte chunks of a row XOR-swizzled by the row index (conflict-free
-// fragment reads), and each wave reads its MFMA fragments from LDS for its
-// own row groups.  Each wave writes the split partials of its row groups.
-// ---------------------------------------------------------------------------
 
 template <bool FP8, int D>
 struct FlashGeom {
@@ -1755,16 +1533,10 @@ __device__ __forceinline__ void flash_pv(const char* vl, f32x4_t (&s)[RG][2], fl
   }
 }
 
-#ifndef HS2_FLASH_NBUF
-#define HS2_FLASH_NBUF 4
-#endif
-#ifndef HS2_FLASH_OCC
-#define HS2_FLASH_OCC 2
-#endif
 template <bool FP8, int D>
-__global__ void __launch_bounds__(256, HS2_FLASH_OCC) chunk_flash(ScanParams P) {
+__global__ void __launch_bounds__(256, 2) chunk_flash(ScanParams P) {
   constexpr int RG = kFlashRG, VE = D / 16, NC = D / 32;
-  constexpr int NBUF = HS2_FLASH_NBUF;  // LDS tile ring: tile n in buffer n % NBUF, NBUF - 1 tiles in flight
+  constexpr int NBUF = 4;  // LDS tile ring: tile n in buffer n % NBUF, NBUF - 1 tiles in flight
   using FG = FlashGeom<FP8, D>;
   __shared__ __align__(16) char tiles[NBUF][TileLoader<FP8, D, 2>::BYTES];
   const int lane = threadIdx.x & 63, tid = threadIdx.x;
@@ -1858,178 +1630,17 @@ __global__ void __launch_bounds__(256, HS2_FLASH_OCC) chunk_flash(ScanParams P) 
 }
 
 // Score pass of the chunk: S[b,t,g,j] = sum over the G heads of token t of
-// 2^(x_hj - lse2_h) for j <= p_t, 0 beyond.  K only; tiles past the block's
-// last query position are zeros without loads.  Logits in the S = Q K^T
-// orientation (G >= 4): lane l holds rows 4*(l/16)+i of position l%16, all of
-// one token, so the head sum is three in-lane adds plus G/8 lane exchanges.
+// 2^(x_hj - lse2_h) for j <= p_t, 0 beyond.  K only; tiles past the
+// workgroup's last query position are zeros without loads.  Logits in the
+// S = Q K^T orientation (G >= 4): lane l holds rows 4*(l/16)+i of position
+// l%16, all of one token, so the head sum is three in-lane adds plus G/8 lane
+// exchanges.
 template <int G>
 __device__ __forceinline__ float head_sum_s(const float (&a)[4]) {
   float v = (a[0] + a[1]) + (a[2] + a[3]);
   if constexpr (G >= 8) v = sum_x16(v);
   if constexpr (G >= 16) v = sum_x32(v);
   return v;
-}
-
-template <bool FP8, int D, int G>
-__global__ void __launch_bounds__(kChunkWaves * 64, 1) chunk_score(ScanParams P) {
-  static_assert(G == 4 || G == 8 || G == 16, "chunk score pass: G in {4, 8, 16}");
-  constexpr int RG = chunk_rg(FP8 ? HS2_FP8_E4M3FN : HS2_BF16, D), WAVES = kChunkWaves, NC = D / 32, EB = FP8 ? 1 : 2;
-  constexpr int STEP = WAVES * 32;
-  constexpr int TP = 16 / G;  // tokens per row group
-  using RT = RawTile<FP8, D>;
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int r = lane & 15, g4 = lane >> 4;
-  const int nblk = (P.n_tpacks + RG - 1) / RG;
-  const ChunkItem it = chunk_item(P, nblk);
-  const int b = it.b, g = it.g;
-
-  // query fragments (row r of each group), and this lane's four S rows
-  // 4*g4 + ii: their token, causal limit and log2-sum-exp
-  u32x4_t qf[RG][NC];
-  bool rl_ok[RG][4];
-  int rl_lim[RG][4];
-  float rl_l2[RG][4];
-#pragma unroll
-  for (int rg = 0; rg < RG; ++rg) {
-    const ChunkRows cr = chunk_row<RG>(P, it.blk, rg, r);
-    load_q<FP8, D>(qf[rg], P, b, cr.ok ? cr.t : 0, g * P.G + (r % P.G), cr.ok, g4);
-    const int tp = it.blk * RG + rg;
-    const int unit = (b * P.n_tpacks + min(tp, P.n_tpacks - 1)) * P.Hkv + g;
-#pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
-      const ChunkRows crr = chunk_row<RG>(P, it.blk, rg, 4 * g4 + ii);
-      rl_ok[rg][ii] = crr.ok;
-      rl_lim[rg][ii] = crr.jlim;
-      rl_l2[rg][ii] = crr.ok ? P.lse2_in[(int64_t)unit * P.rows + 4 * g4 + ii] : 0.f;
-    }
-  }
-  const int t_first = it.blk * RG * P.tpack;
-  const int t_last = min(t_first + RG * P.tpack, P.Tq) - 1;
-  const int p_max = P.q_pos0 + t_last;
-  const int j_nomask = P.q_pos0 + t_first;
-  const int j_begin = it.split * P.split_len;
-  const int j_end = min(j_begin + P.split_len, P.N);  // every position gets a score (0 past p)
-
-  const int64_t kvoff = ((int64_t)b * P.sb + (int64_t)g * P.sh) * EB;
-  const char* kb = (const char*)P.k + kvoff;
-  const int64_t snb = P.sn * EB;
-  float cs = P.scale_log2;
-  if constexpr (FP8) cs *= P.k_scale[b * P.Hkv + g];
-  uint32_t koff[2];
-#pragma unroll
-  for (int hh = 0; hh < 2; ++hh) koff[hh] = (uint32_t)((16 * hh + r) * snb) + 16u * g4;
-
-  // writers: one lane group per token (G = 4: every group; 8: even groups; 16: group 0)
-  const bool writer = (g4 % (G / 4)) == 0;
-  const int wtok = (4 * g4) / G;
-  __shared__ __align__(16) float stage[WAVES][RG * TP * 32];
-  float* st = stage[wave];
-  auto stage_put_s = [&](int rg, int hh, float v) {
-    if (writer) st[(rg * TP + wtok) * 32 + 16 * hh + r] = v;
-  };
-  auto loadk = [&](u32x4_t (&kr)[2][RT::KW], int j0) {
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      const char* kp = (j0 + 31 <= p_max) ? kb + (int64_t)j0 * snb + koff[hh]
-                                          : kb + (int64_t)min(j0 + 16 * hh + r, p_max) * snb + 16 * g4;
-#pragma unroll
-      for (int c = 0; c < RT::KW; ++c) kr[hh][c] = *(const u32x4_t*)(kp + 64 * c);
-    }
-  };
-  auto stage_flush = [&](int j0) {
-#pragma unroll
-    for (int q = lane; q < RG * TP * 8; q += 64) {  // q: 4-float piece
-      const int row = q >> 3, pos = (q & 7) * 4;
-      const int rg = row / TP, tl = row - rg * TP;
-      const int t = (it.blk * RG + rg) * TP + tl;
-      const f32x4_t v = *(const f32x4_t*)(st + row * 32 + pos);
-      if (t >= P.Tq) continue;
-      float* dst = P.scores + (((int64_t)b * P.Tq + t) * P.Hkv + g) * P.N + j0 + pos;
-      if ((P.N & 3) == 0 && j0 + pos + 3 < P.N) {
-        *(f32x4_t*)dst = v;
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (j0 + pos + e < P.N) dst[e] = v[e];
-      }
-    }
-  };
-  auto compute = [&](const u32x4_t (&kr)[2][RT::KW], int j0) {
-    u32x4_t kf[2][NC];
-    if constexpr (!FP8) {
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-        for (int c = 0; c < NC; ++c) kf[hh][c] = kr[hh][c];
-    } else {
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-        for (int ii = 0; ii < NC / 2; ++ii) {
-          uint32_t a0, a1, a2, a3, b0, b1, b2, b3;
-          e4m3x4_to_bf16(kr[hh][ii].x, a0, a1);
-          e4m3x4_to_bf16(kr[hh][ii].y, a2, a3);
-          e4m3x4_to_bf16(kr[hh][ii].z, b0, b1);
-          e4m3x4_to_bf16(kr[hh][ii].w, b2, b3);
-          kf[hh][2 * ii] = u32x4_t{a0, a1, a2, a3};
-          kf[hh][2 * ii + 1] = u32x4_t{b0, b1, b2, b3};
-        }
-    }
-    const bool need_mask = j0 + 31 > j_nomask;
-    // S = Q K^T: lane l holds rows 4*(l/16)+i (i < 4) of position l%16 of each
-    // 16-position half, so a token's heads are summed mostly inside the lane
-    f32x4_t sacc[RG][2];
-#pragma unroll
-    for (int rg = 0; rg < RG; ++rg)
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) sacc[rg][hh] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int c = 0; c < NC; ++c)
-#pragma unroll
-      for (int rg = 0; rg < RG; ++rg)
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) sacc[rg][hh] = mfma_bf16(qf[rg][c], kf[hh][c], sacc[rg][hh]);
-#pragma unroll
-    for (int rg = 0; rg < RG; ++rg) {
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int j = j0 + 16 * hh + r;  // this lane's position
-        float acc[4];
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-          const bool live = rl_ok[rg][ii] && (!need_mask || j <= rl_lim[rg][ii]);
-          acc[ii] = live ? exp2_fast(__builtin_fmaf(sacc[rg][hh][ii], cs, -rl_l2[rg][ii])) : 0.f;
-        }
-        const float v = head_sum_s<G>(acc);
-        stage_put_s(rg, hh, v);
-      }
-    }
-    stage_flush(j0);
-  };
-  u32x4_t A[2][RT::KW], B[2][RT::KW];
-  int j0 = j_begin + wave * 32;
-  // tiles with loads: those starting at or before p_max
-  if (j0 < j_end && j0 <= p_max) loadk(A, j0);
-  while (j0 < j_end && j0 <= p_max) {
-    const int j1 = j0 + STEP;
-    const bool l1 = j1 < j_end && j1 <= p_max;
-    if (l1) loadk(B, j1);
-    compute(A, j0);
-    if (!l1) {
-      j0 = j1;
-      break;
-    }
-    const int j2 = j1 + STEP;
-    if (j2 < j_end && j2 <= p_max) loadk(A, j2);
-    compute(B, j1);
-    j0 = j2;
-  }
-  // remaining tiles lie past every query position of the block: zeros
-  if (j0 < j_end) {
-    for (int q = lane; q < RG * TP * 32; q += 64) st[q] = 0.f;
-    for (; j0 < j_end; j0 += STEP) stage_flush(j0);
-  }
 }
 
 // Score pass, LDS-staged form: the workgroup's 4 waves hold kFlashRG row
@@ -2857,9 +2468,8 @@ bool flash_rows_fit(const ScanParams& p, int kv_dtype) {
 
 hipError_t launch_chunk_full(const ScanParams& p, int kv_dtype, hipStream_t s) {
   TimedLaunch tl("chunk_full", s);
-#if HS2_CHUNK_FLASH
   if (!flash_rows_fit(p, kv_dtype)) return hipErrorInvalidValue;
-  const int nblk = (p.n_tpacks + 4 * kFlashRG - 1) / (4 * kFlashRG);  // chunk_full_packs()
+  const int nblk = (p.n_tpacks + kChunkPacks - 1) / kChunkPacks;
   const dim3 grid(p.B * nblk * p.Hkv * p.nsplit);
   if (kv_dtype == HS2_FP8_E4M3FN) {
     if (p.D == 128) hipLaunchKernelGGL((chunk_flash<true, 128>), grid, dim3(256), 0, s, p);
@@ -2868,43 +2478,22 @@ hipError_t launch_chunk_full(const ScanParams& p, int kv_dtype, hipStream_t s) {
     if (p.D == 128) hipLaunchKernelGGL((chunk_flash<false, 128>), grid, dim3(256), 0, s, p);
     else hipLaunchKernelGGL((chunk_flash<false, 64>), grid, dim3(256), 0, s, p);
   }
-#else
-  const int rg = chunk_rg(kv_dtype, p.D);
-  const int nblk = (p.n_tpacks + rg - 1) / rg;
-  const dim3 grid(p.B * nblk * p.Hkv * p.nsplit);
-  if (kv_dtype == HS2_FP8_E4M3FN) {
-    if (p.D == 128) hipLaunchKernelGGL((chunk_full<true, 128>), grid, dim3(kChunkWaves * 64), 0, s, p);
-    else hipLaunchKernelGGL((chunk_full<true, 64>), grid, dim3(kChunkWaves * 64), 0, s, p);
-  } else {
-    if (p.D == 128) hipLaunchKernelGGL((chunk_full<false, 128>), grid, dim3(kChunkWaves * 64), 0, s, p);
-    else hipLaunchKernelGGL((chunk_full<false, 64>), grid, dim3(kChunkWaves * 64), 0, s, p);
-  }
-#endif
   return hipGetLastError();
 }
 
 template <bool FP8, int D>
 void go_chunk_score(const ScanParams& p, dim3 grid, hipStream_t s) {
-#if HS2_CHUNK_FLASH
   switch (p.G) {
     case 4: hipLaunchKernelGGL((chunk_score_flash<FP8, D, 4>), grid, dim3(256), 0, s, p); break;
     case 8: hipLaunchKernelGGL((chunk_score_flash<FP8, D, 8>), grid, dim3(256), 0, s, p); break;
     default: hipLaunchKernelGGL((chunk_score_flash<FP8, D, 16>), grid, dim3(256), 0, s, p); break;
   }
-#else
-  switch (p.G) {
-    case 4: hipLaunchKernelGGL((chunk_score<FP8, D, 4>), grid, dim3(kChunkWaves * 64), 0, s, p); break;
-    case 8: hipLaunchKernelGGL((chunk_score<FP8, D, 8>), grid, dim3(kChunkWaves * 64), 0, s, p); break;
-    default: hipLaunchKernelGGL((chunk_score<FP8, D, 16>), grid, dim3(kChunkWaves * 64), 0, s, p); break;
-  }
-#endif
 }
 
 hipError_t launch_chunk_score(const ScanParams& p, int kv_dtype, hipStream_t s) {
   if (p.G != 4 && p.G != 8 && p.G != 16) return hipErrorInvalidValue;
-  if (HS2_CHUNK_FLASH && !flash_rows_fit(p, kv_dtype)) return hipErrorInvalidValue;
-  const int packs = HS2_CHUNK_FLASH ? 4 * kFlashRG : chunk_rg(kv_dtype, p.D);
-  const int nblk = (p.n_tpacks + packs - 1) / packs;
+  if (!flash_rows_fit(p, kv_dtype)) return hipErrorInvalidValue;
+  const int nblk = (p.n_tpacks + kChunkPacks - 1) / kChunkPacks;
   const dim3 grid(p.B * nblk * p.Hkv * p.nsplit);
   TimedLaunch tl("chunk_score", s);
   if (kv_dtype == HS2_FP8_E4M3FN) {

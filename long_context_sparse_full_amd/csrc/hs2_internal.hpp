@@ -61,32 +61,17 @@ struct ScanParams {
   int32_t* sel_stepcnt;
 };
 
-// Multi-query chunk path: one wave holds chunk_rg() groups of 16 query rows
-// (tpack tokens x G heads each), kChunkWaves waves split a position range.
-// Three groups for a bf16 D=128 cache (its tile buffers are twice the size),
-// four otherwise, so queries, accumulators and two tiles stay in registers.
-#ifndef HS2_CHUNK_RG
-#define HS2_CHUNK_RG 0  // 0: per dtype (3 for bf16 D = 128, 4 otherwise); >0: fixed (tuning)
-#endif
-__host__ __device__ constexpr int chunk_rg(int kv_dtype, int D) {
-  return HS2_CHUNK_RG > 0 ? HS2_CHUNK_RG : ((kv_dtype == HS2_BF16 && D == 128) ? 3 : 4);
-}
-constexpr int kChunkWaves = 4;
-// The chunk full pass runs either as the per-wave streaming kernel above
-// (default) or LDS-staged: a workgroup's 4 waves share each K/V tile through
-// LDS and each wave holds kFlashRG row groups, 4 * kFlashRG packs per
-// workgroup.
-#ifndef HS2_CHUNK_FLASH
-#define HS2_CHUNK_FLASH 1
-#endif
+// Multi-query chunk path: a workgroup of 4 waves, each holding kFlashRG
+// groups of 16 query rows (tpack tokens x G heads), so kChunkPacks packs per
+// workgroup share every K/V tile through LDS.  The planner takes it when there
+// are at least kChunkMinPacks packs per (b, kv head).
+constexpr int kFlashRG = 2;
+constexpr int kChunkPacks = 4 * kFlashRG;
+constexpr int kChunkMinPacks = 4;
 // Chunk position splits: about this many full-pass work items in all.
 #ifndef HS2_CHUNK_TARGET_WGS
 #define HS2_CHUNK_TARGET_WGS 1024
 #endif
-constexpr int kFlashRG = 2;
-__host__ __device__ constexpr int chunk_full_packs(int kv_dtype, int D) {
-  return HS2_CHUNK_FLASH ? 4 * kFlashRG : chunk_rg(kv_dtype, D);
-}
 
 constexpr int kSelChunk = 16384;  // candidates per workgroup in the select passes
 constexpr int kHistBins = 4096;  // 12-bit digits
