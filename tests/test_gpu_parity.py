@@ -150,6 +150,9 @@ SEL_CASES = [
     (1, 1, 1, 6000, 7, 5, 64, "blockties"),
     (1, 1, 1, 3000, 100, 16, 64, "random"),    # k blocks cover everything
     (1, 1, 1, 50000, 1024, 128, 1, "tiny"),    # exercises the low digits
+    (1, 1, 2, 20000, 300, 16, 1, "allequal"),  # every candidate in one bin of each digit
+    (1, 2, 1, 30000, 3000, 64, 1, "random"),   # k of several thousand
+    (2, 2, 2, 40000, 2048, 128, 1, "ties"),    # heavy ties across chunks
 ]
 
 
