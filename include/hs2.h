@@ -99,7 +99,14 @@ const char* hs2_last_error(void);
  * hs2_full_attn_set_mode(1) for bf16 and FP8 caches when the device can
  * co-schedule one workgroup per compute unit for every (b, query pack, kv
  * head), a single cooperative kernel (scan, device-wide barrier, output merge
- * and scores).  Both compute the same quantities to the same bounds. */
+ * and scores).  With many query tokens (bf16 or FP8 cache, 4, 8 or 16 query
+ * heads per kv head, at least 4 packs of 16/G tokens per (b, kv head), as in
+ * a 512-token chunk) the scan is a matrix-core pass over K/V tiles staged in
+ * LDS, and the score kernel recomputes the logits against the merged
+ * log-sum-exp instead of reading stored codes.  All compute the same
+ * quantities to the same bounds.  Rows of the cache must be 16-byte aligned;
+ * the chunk kernels also need 32 rows to span less than 2 GiB
+ * (HS2_ERR_HIP otherwise). */
 size_t hs2_full_attn_scores_workspace(const hs2_kv_desc* kv, int32_t Tq, int32_t Hq);
 int hs2_full_attn_scores(const hs2_kv_desc* kv, const void* q, hs2_dtype q_dtype, int32_t Tq,
                          int32_t Hq, int32_t q_pos0, float softmax_scale, void* out, float* lse,
