@@ -15,15 +15,23 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
 // MFMA form: a workgroup computes a 64 (tokens) x 64 (columns) tile; wave w
 // owns the 32 x 32 quarter (w >> 1, w & 1) as 2 x 2 tiles of 16 x 16.
 // Stage = 64 of the d_model contraction: hidden rows go straight from global
 // memory into the MFMA A layout (8 consecutive elements per lane); the w_kv
 // tile [64 x 64] goes through LDS, where each lane gathers the 8 contraction
-// elements of its column.  The next stage's global loads are issued before the
-// current stage is computed.
-constexpr int kBT = 64, kBC = 64, kKS = 64, kWPad = 8;
+// elements of its column.  The global loads of a stage are issued kRing
+// stages ahead (a register ring), so the contraction is not paced by one load
+// latency per stage.
+constexpr int kBT = 64, kBC = 64, kKS = 64, kWPad = 8, kRing = 4;
+
+struct BridgeStage {
+  u32x4_t w[2];
+  u32x4_t a[2][2];
+};
 
 __global__ void __launch_bounds__(256) bridge_mfma(const uint16_t* __restrict__ H, int T, int dm,
                                                    const uint16_t* __restrict__ W, int Hkv, int D, uint16_t* kout,
@@ -45,48 +53,78 @@ __global__ void __launch_bounds__(256) bridge_mfma(const uint16_t* __restrict__ 
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt) arow[rt] = min(t0 + wr * 32 + rt * 16 + r16, T - 1);
 
-  auto load_stage = [&](int k0, u32x4_t (&wreg)[2], u32x4_t (&areg)[2][2]) {
+  auto load_stage = [&](int k0, BridgeStage& S) {
+    // stages past the end reload the last one (unused): the loads stay
+    // unconditional, so the compiler's wait counts keep the ring in flight
+    k0 = min(k0, dm - kKS);
     const uint16_t* wp = W + (int64_t)(k0 + wrow) * C + c0 + wcol;
-    wreg[0] = *(const u32x4_t*)wp;
-    wreg[1] = *(const u32x4_t*)(wp + 8);
+    S.w[0] = *(const u32x4_t*)wp;
+    S.w[1] = *(const u32x4_t*)(wp + 8);
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) areg[rt][ks] = *(const u32x4_t*)(H + (int64_t)arow[rt] * dm + k0 + ks * 32 + 8 * g4);
+      for (int ks = 0; ks < 2; ++ks) S.a[rt][ks] = *(const u32x4_t*)(H + (int64_t)arow[rt] * dm + k0 + ks * 32 + 8 * g4);
   };
-  u32x4_t wcur[2], wnxt[2], acur[2][2], anxt[2][2];
-  load_stage(0, wcur, acur);
-  for (int k0 = 0; k0 < dm; k0 += kKS) {
+  auto compute_stage = [&](const BridgeStage& S) {
     __syncthreads();  // previous stage's LDS reads done
-    *(u32x4_t*)&Ws[wrow][wcol] = wcur[0];
-    *(u32x4_t*)&Ws[wrow][wcol + 8] = wcur[1];
+    *(u32x4_t*)&Ws[wrow][wcol] = S.w[0];
+    *(u32x4_t*)&Ws[wrow][wcol + 8] = S.w[1];
     __syncthreads();
-    if (k0 + kKS < dm) load_stage(k0 + kKS, wnxt, anxt);
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
-        const int col = wc * 32 + ct * 16 + r16;
-        uint32_t b[4];
+        // B operand (contraction index 8 g4 + 0..7 of column r16) by two
+        // transposing 64-bit LDS reads: in each 16-lane group, source lane
+        // 4 k4 + a4 names columns 4 a4 .. 4 a4 + 3 of contraction row
+        // 8 g4 + 4 h + k4, and lane i receives column i of those four rows
+        const int k4 = r16 >> 2, a4 = r16 & 3;
+        u32x4_t bf;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const uint32_t lo = Ws[ks * 32 + 8 * g4 + 2 * q][col], hi = Ws[ks * 32 + 8 * g4 + 2 * q + 1][col];
-          b[q] = lo | (hi << 16);
+        for (int hh = 0; hh < 2; ++hh) {
+          const uint16_t* src = &Ws[ks * 32 + 8 * g4 + 4 * hh + k4][wc * 32 + ct * 16 + 4 * a4];
+          const s16x4_t t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)src);
+          const u32x2_t w2 = __builtin_bit_cast(u32x2_t, t);
+          bf[2 * hh] = w2.x;
+          bf[2 * hh + 1] = w2.y;
         }
-        const u32x4_t bf = u32x4_t{b[0], b[1], b[2], b[3]};
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt)
-          acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, acur[rt][ks]),
+          acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, S.a[rt][ks]),
                                                                 __builtin_bit_cast(bf16x8_t, bf), acc[rt][ct], 0, 0, 0);
       }
     }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) wcur[i] = wnxt[i];
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) acur[rt][ks] = anxt[rt][ks];
+  };
+  BridgeStage R0, R1, R2, R3;
+  load_stage(0, R0);
+  load_stage(kKS, R1);
+  load_stage(2 * kKS, R2);
+  load_stage(3 * kKS, R3);
+  // Stage s is computed from ring slot s % kRing, which then loads stage
+  // s + kRing.  Whole groups of kRing stages run without branches (so each
+  // refill stays right after its stage; the scheduling barriers keep the
+  // compiler from batching the refills), the last d_model / 64 % kRing stages
+  // after them.
+  const int ns = dm / kKS, nfull = ns / kRing * kRing;
+  int k0 = 0;
+  for (; k0 < nfull * kKS; k0 += kRing * kKS) {
+    compute_stage(R0);
+    load_stage(k0 + kRing * kKS, R0);
+    __builtin_amdgcn_sched_barrier(0);
+    compute_stage(R1);
+    load_stage(k0 + (kRing + 1) * kKS, R1);
+    __builtin_amdgcn_sched_barrier(0);
+    compute_stage(R2);
+    load_stage(k0 + (kRing + 2) * kKS, R2);
+    __builtin_amdgcn_sched_barrier(0);
+    compute_stage(R3);
+    load_stage(k0 + (kRing + 3) * kKS, R3);
+    __builtin_amdgcn_sched_barrier(0);
   }
+  const int rem = ns - nfull;  // 0..3 stages, in slots R0.. in order
+  if (rem > 0) compute_stage(R0);
+  if (rem > 1) compute_stage(R1);
+  if (rem > 2) compute_stage(R2);
   // scatter: column c -> K or V cache, head c/D, element c%D; token t
   const int half = Hkv * D;
 #pragma unroll
