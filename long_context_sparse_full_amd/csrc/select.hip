@@ -161,34 +161,24 @@ __device__ __forceinline__ void load_keys(const float* s, int base, int end, boo
 
 // LDS histogram of one digit over the keys that match `prefix`.  PASS 0 keys
 // cluster in a few bins (the scores of one row share exponent and leading
-// mantissa bits), so each thread first counts its two most recent bins in
-// registers and only spills the others to the (contended) LDS atomics.
+// mantissa bits), so each thread counts the keys in the bin of its first key
+// in a register, with no branches, and sends only the others to the
+// (contended) LDS atomics.
 template <int PASS>
 __device__ __forceinline__ void hist_keys(const ChunkKeys& K, uint32_t prefix, int32_t* h) {
   using DG = Digit<PASS>;
   if constexpr (PASS == 0) {
-    uint32_t b1 = 0xffffffffu, b2 = 0xffffffffu;
-    int32_t c1 = 0, c2 = 0;
+    const uint32_t b1 = K.key[0] >> DG::SHIFT;  // a bin of this row (key 0 may be a padding 0)
+    int32_t c1 = 0;
 #pragma unroll
     for (int i = 0; i < kKeysPerThread; ++i) {
-      if (!(K.valid >> i & 1)) continue;
+      const bool v = K.valid >> i & 1;
       const uint32_t bin = K.key[i] >> DG::SHIFT;
-      if (bin == b1) {
-        ++c1;
-      } else if (bin == b2) {
-        ++c2;
-      } else if (c1 == 0) {
-        b1 = bin;
-        c1 = 1;
-      } else if (c2 == 0) {
-        b2 = bin;
-        c2 = 1;
-      } else {
-        atomicAdd(&h[bin], 1);
-      }
+      const bool hit = v && bin == b1;
+      c1 += hit;
+      if (v && !hit) atomicAdd(&h[bin], 1);
     }
     if (c1) atomicAdd(&h[b1], c1);
-    if (c2) atomicAdd(&h[b2], c2);
   } else {
 #pragma unroll
     for (int i = 0; i < kKeysPerThread; ++i)
