@@ -161,14 +161,17 @@ __device__ __forceinline__ void load_keys(const float* s, int base, int end, boo
 
 // LDS histogram of one digit over the keys that match `prefix`.  PASS 0 keys
 // cluster in a few bins (the scores of one row share exponent and leading
-// mantissa bits), so each thread counts the keys in the bin of its first key
-// in a register, with no branches, and sends only the others to the
-// (contended) LDS atomics.
-template <int PASS>
+// mantissa bits), so each thread counts some bins in registers and sends only
+// the other keys to the (contended) LDS atomics.  SHORT (grids that do not
+// fill the GPU several times over, whose passes are latency-bound): the bin of
+// the thread's first key, counted with no branches.  Otherwise (throughput-
+// bound grids): the first two bins the thread meets, fewer LDS atomics for a
+// longer dependent chain.
+template <int PASS, bool SHORT>
 __device__ __forceinline__ void hist_keys(const ChunkKeys& K, uint32_t prefix, int32_t* h) {
   using DG = Digit<PASS>;
-  if constexpr (PASS == 0) {
-    const uint32_t b1 = K.key[0] >> DG::SHIFT;  // a bin of this row (key 0 may be a padding 0)
+  if constexpr (PASS == 0 && SHORT) {
+    const uint32_t b1 = K.key[0] >> DG::SHIFT;  // (key 0 may be a padding 0: only register hits lost)
     int32_t c1 = 0;
 #pragma unroll
     for (int i = 0; i < kKeysPerThread; ++i) {
@@ -179,6 +182,29 @@ __device__ __forceinline__ void hist_keys(const ChunkKeys& K, uint32_t prefix, i
       if (v && !hit) atomicAdd(&h[bin], 1);
     }
     if (c1) atomicAdd(&h[b1], c1);
+  } else if constexpr (PASS == 0) {
+    uint32_t b1 = 0xffffffffu, b2 = 0xffffffffu;
+    int32_t c1 = 0, c2 = 0;
+#pragma unroll
+    for (int i = 0; i < kKeysPerThread; ++i) {
+      if (!(K.valid >> i & 1)) continue;
+      const uint32_t bin = K.key[i] >> DG::SHIFT;
+      if (bin == b1) {
+        ++c1;
+      } else if (bin == b2) {
+        ++c2;
+      } else if (c1 == 0) {
+        b1 = bin;
+        c1 = 1;
+      } else if (c2 == 0) {
+        b2 = bin;
+        c2 = 1;
+      } else {
+        atomicAdd(&h[bin], 1);
+      }
+    }
+    if (c1) atomicAdd(&h[b1], c1);
+    if (c2) atomicAdd(&h[b2], c2);
   } else {
 #pragma unroll
     for (int i = 0; i < kKeysPerThread; ++i)
@@ -192,7 +218,7 @@ __device__ __forceinline__ void hist_keys(const ChunkKeys& K, uint32_t prefix, i
 // PASS 2 also stores, per chunk, the count of keys above the 24-bit prefix and
 // the suffix sums of its 256-bin histogram, from which the emit pass gets every
 // chunk's counts above and equal to the final threshold.
-template <int PASS>
+template <int PASS, bool SHORT>
 __global__ void __launch_bounds__(256) sel_hist(SelectParams P) {
   using DG = Digit<PASS>;
   __shared__ int32_t h[DG::BINS];
@@ -223,7 +249,7 @@ __global__ void __launch_bounds__(256) sel_hist(SelectParams P) {
   }
   for (int i = threadIdx.x; i < DG::BINS; i += 256) h[i] = 0;
   __syncthreads();
-  hist_keys<PASS>(K, prefix, h);
+  hist_keys<PASS, SHORT>(K, prefix, h);
   __syncthreads();
   int32_t* gh = hist + PASS * kHistBins;
   for (int i = threadIdx.x; i < DG::BINS; i += 256)
@@ -458,9 +484,13 @@ hipError_t launch_select(const SelectParams& p, hipStream_t s) {
   } while (0)
   HS2_L("select_init", sel_init, dim3(p.units));
   if (p.block_size == 1) {
-    HS2_L("select_hist", sel_hist<0>, grid_c);
-    HS2_L("select_hist", sel_hist<1>, grid_c);
-    HS2_L("select_hist", sel_hist<2>, grid_c);
+    if (p.units * p.nchunks < 2048) {  // latency-bound passes
+      HS2_L("select_hist", (sel_hist<0, true>), grid_c);
+    } else {
+      HS2_L("select_hist", (sel_hist<0, false>), grid_c);
+    }
+    HS2_L("select_hist", (sel_hist<1, false>), grid_c);
+    HS2_L("select_hist", (sel_hist<2, false>), grid_c);
     HS2_L("select_emit", sel_emit, grid_c);
   } else {
     HS2_L("select_block_mass", sel_block_mass, dim3((p.nblocks_max + 255) / 256, p.units));
