@@ -1586,22 +1586,31 @@ __global__ void __launch_bounds__(256, 2) chunk_flash(ScanParams P) {
 #pragma unroll
     for (int dt = 0; dt < VE; ++dt) S.o[rg][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
-  auto compute = [&](int n) {
-    const int j0 = j_begin + 32 * n;
-    const char* kl = tiles[n % NBUF];
-    f32x4_t sc[RG][2];
-    flash_qk<FP8, D, RG>(kl, qf, r, g4, sc);
-    flash_pv<FP8, D, RG>(kl + FG::HALF, sc, cs, j0, jlim, j0 + 31 > j_nomask, r, g4, S);
-  };
   // the query loads complete here, so the compiler's own wait bookkeeping has
   // nothing pending across the loop (the tile loads are invisible to it)
   wait_vm<0>();
 #pragma unroll
   for (int t = 0; t < NBUF - 1; ++t) issue(t);
-  for (int n = 0; n < ntile; ++n) {
+  // step n (buffer n % NBUF known at compile time in the unrolled body, so
+  // every LDS address is a per-lane constant plus an immediate offset)
+  auto step = [&](auto buf, int n) {
+    constexpr int B = decltype(buf)::value;
     ring_wait<NBUF, TileLoader<FP8, D, 2>::PER>(n, ntile);
-    issue(n + NBUF - 1);
-    compute(n);
+    if (n + NBUF - 1 < ntile) ld.issue(tiles[(B + NBUF - 1) % NBUF], j_begin + 32 * (n + NBUF - 1), p_max);
+    const int j0 = j_begin + 32 * n;
+    f32x4_t sc[RG][2];
+    flash_qk<FP8, D, RG>(tiles[B], qf, r, g4, sc);
+    flash_pv<FP8, D, RG>(tiles[B] + FG::HALF, sc, cs, j0, jlim, j0 + 31 > j_nomask, r, g4, S);
+  };
+  static_assert(NBUF == 4, "the unrolled ring below has 4 buffers");
+  for (int n = 0; n < ntile; n += NBUF) {
+    step(std::integral_constant<int, 0>{}, n);
+    if (n + 1 >= ntile) break;
+    step(std::integral_constant<int, 1>{}, n + 1);
+    if (n + 2 >= ntile) break;
+    step(std::integral_constant<int, 2>{}, n + 2);
+    if (n + 3 >= ntile) break;
+    step(std::integral_constant<int, 3>{}, n + 3);
   }
 
   // partials of this wave's row groups (16 rows each)
@@ -1726,9 +1735,8 @@ __global__ void __launch_bounds__(256, 2) chunk_score_flash(ScanParams P) {
       }
     }
   };
-  auto compute = [&](int n) {
+  auto compute = [&](const char* kl, int n) {
     const int j0 = j_begin + 32 * n;
-    const char* kl = tiles[n % NBUF];
     u32x4_t kf[2][NC];
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
@@ -1789,10 +1797,22 @@ __global__ void __launch_bounds__(256, 2) chunk_score_flash(ScanParams P) {
   wait_vm<0>();
 #pragma unroll
   for (int t = 0; t < NBUF - 1; ++t) issue(t);
-  for (int n = 0; n < ntile; ++n) {
+  // unrolled over the ring so each step's buffer is a compile-time constant
+  auto step = [&](auto buf, int n) {
+    constexpr int B = decltype(buf)::value;
     ring_wait<NBUF, TL::PER>(n, ntile);
-    issue(n + NBUF - 1);
-    compute(n);
+    if (n + NBUF - 1 < ntile) ld.issue(tiles[(B + NBUF - 1) % NBUF], j_begin + 32 * (n + NBUF - 1), p_max);
+    compute(tiles[B], n);
+  };
+  static_assert(NBUF == 4, "the unrolled ring below has 4 buffers");
+  for (int n = 0; n < ntile; n += NBUF) {
+    step(std::integral_constant<int, 0>{}, n);
+    if (n + 1 >= ntile) break;
+    step(std::integral_constant<int, 1>{}, n + 1);
+    if (n + 2 >= ntile) break;
+    step(std::integral_constant<int, 2>{}, n + 2);
+    if (n + 3 >= ntile) break;
+    step(std::integral_constant<int, 3>{}, n + 3);
   }
   // remaining tiles lie past every query position of the workgroup: zeros
   if (ntile * 32 + j_begin < j_end) {
