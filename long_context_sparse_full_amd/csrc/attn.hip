@@ -1229,9 +1229,9 @@ __global__ void __launch_bounds__(WAVES * 64, 1) scan_fused(ScanParams P) {
 // covers 4 x kFlashRG groups of 16 query rows (tpack tokens x G heads each) of
 // one (b, kv head) over a position split.  Every 32-position K/V tile is
 // fetched once by the whole workgroup straight from global memory into an LDS
-// ring (4 buffers, one barrier per tile); each wave reads its MFMA fragments
-// from LDS for its own row groups: S^T = K Q^T and O^T += V^T P^T as in the
-// decode scan.  Pass 1 writes the split partials of each 16-row group in the
+// ring (3 buffers in the full pass, 4 in the score pass; one barrier per
+// tile); each wave reads its MFMA fragments from LDS for its own row groups:
+// S^T = K Q^T and O^T += V^T P^T as in the decode scan.  Pass 1 writes the split partials of each 16-row group in the
 // decode layout (unit = (b, pack, g)), merged by the combine kernel; pass 2
 // recomputes the logits and writes the scores against the merged
 // log-sum-exp, so no per-head scratch is stored.  Linear work index: split
@@ -1533,10 +1533,12 @@ __device__ __forceinline__ void flash_pv(const char* vl, f32x4_t (&s)[RG][2], fl
   }
 }
 
+// 3 waves per SIMD: 3 workgroups of 48 KiB LDS rings per CU (bf16 D = 128),
+// at most 168 VGPRs per wave
 template <bool FP8, int D>
-__global__ void __launch_bounds__(256, 2) chunk_flash(ScanParams P) {
+__global__ void __launch_bounds__(256, 3) chunk_flash(ScanParams P) {
   constexpr int RG = kFlashRG, VE = D / 16, NC = D / 32;
-  constexpr int NBUF = 4;  // LDS tile ring: tile n in buffer n % NBUF, NBUF - 1 tiles in flight
+  constexpr int NBUF = 3;  // LDS tile ring: tile n in buffer n % NBUF, NBUF - 1 tiles in flight
   using FG = FlashGeom<FP8, D>;
   __shared__ __align__(16) char tiles[NBUF][TileLoader<FP8, D, 2>::BYTES];
   const int lane = threadIdx.x & 63, tid = threadIdx.x;
@@ -1602,15 +1604,17 @@ __global__ void __launch_bounds__(256, 2) chunk_flash(ScanParams P) {
     flash_qk<FP8, D, RG>(tiles[B], qf, r, g4, sc);
     flash_pv<FP8, D, RG>(tiles[B] + FG::HALF, sc, cs, j0, jlim, j0 + 31 > j_nomask, r, g4, S);
   };
-  static_assert(NBUF == 4, "the unrolled ring below has 4 buffers");
+  static_assert(NBUF == 3 || NBUF == 4, "the unrolled ring below has 3 or 4 buffers");
   for (int n = 0; n < ntile; n += NBUF) {
     step(std::integral_constant<int, 0>{}, n);
     if (n + 1 >= ntile) break;
     step(std::integral_constant<int, 1>{}, n + 1);
     if (n + 2 >= ntile) break;
     step(std::integral_constant<int, 2>{}, n + 2);
-    if (n + 3 >= ntile) break;
-    step(std::integral_constant<int, 3>{}, n + 3);
+    if constexpr (NBUF == 4) {
+      if (n + 3 >= ntile) break;
+      step(std::integral_constant<int, NBUF - 1>{}, n + 3);
+    }
   }
 
   // partials of this wave's row groups (16 rows each)
@@ -1804,15 +1808,17 @@ __global__ void __launch_bounds__(256, 2) chunk_score_flash(ScanParams P) {
     if (n + NBUF - 1 < ntile) ld.issue(tiles[(B + NBUF - 1) % NBUF], j_begin + 32 * (n + NBUF - 1), p_max);
     compute(tiles[B], n);
   };
-  static_assert(NBUF == 4, "the unrolled ring below has 4 buffers");
+  static_assert(NBUF == 3 || NBUF == 4, "the unrolled ring below has 3 or 4 buffers");
   for (int n = 0; n < ntile; n += NBUF) {
     step(std::integral_constant<int, 0>{}, n);
     if (n + 1 >= ntile) break;
     step(std::integral_constant<int, 1>{}, n + 1);
     if (n + 2 >= ntile) break;
     step(std::integral_constant<int, 2>{}, n + 2);
-    if (n + 3 >= ntile) break;
-    step(std::integral_constant<int, 3>{}, n + 3);
+    if constexpr (NBUF == 4) {
+      if (n + 3 >= ntile) break;
+      step(std::integral_constant<int, NBUF - 1>{}, n + 3);
+    }
   }
   // remaining tiles lie past every query position of the workgroup: zeros
   if (ntile * 32 + j_begin < j_end) {
