@@ -34,15 +34,12 @@ typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
-// Compile-time tuning of the full-layer scan (fixed for gfx950; see the design notes).
+// Compile-time tuning of the full-layer scan (the defaults are the measured best on gfx950).
 #ifndef HS2_SCAN_NT
 #define HS2_SCAN_NT 0  // non-temporal K/V loads in the streaming scan (measured slower on gfx950)
 #endif
 #ifndef HS2_SCAN_INTERLEAVE
 #define HS2_SCAN_INTERLEAVE 1  // split s takes workgroup tiles s, s+nsplit, ... (all splits sweep together)
-#endif
-#ifndef HS2_FUSED_PLAIN_LAUNCH
-#define HS2_FUSED_PLAIN_LAUNCH 0  // timing experiments only: plain (non-cooperative) launch
 #endif
 #ifndef HS2_FUSED_ACQUIRE
 #define HS2_FUSED_ACQUIRE 0  // grid barrier ends with a device-scope acquire (cache invalidation)
@@ -2368,13 +2365,7 @@ hipError_t go_fused(const ScanParams& p, int units, hipStream_t s) {
   TimedLaunch tl("full_scan", s);
   ScanParams arg = p;
   void* args[] = {(void*)&arg};
-#if HS2_FUSED_PLAIN_LAUNCH
-  (void)args;
-  hipLaunchKernelGGL((scan_fused<FP8, D, W>), dim3(units * p.nsplit), dim3(W * 64), lds, s, arg);
-  return hipGetLastError();
-#else
   return hipLaunchCooperativeKernel(fn, dim3(units * p.nsplit), dim3(W * 64), args, (unsigned)lds, s);
-#endif
 }
 
 template <bool FP8, int D>

@@ -24,10 +24,9 @@
  *                    self-decoder hidden state with that layer's own projection
  *                    (javabetter.cn, KV Bridging paragraph).
  *
- * Readings where the pages are silent (score aggregation over GQA heads, tie
- * rule, whether the window competes, window includes the current token,
- * output rounding, ...) are listed in the repository's design notes; each
- * function below states the one it uses.
+ * Where the pages are silent (score aggregation over GQA heads, tie rule,
+ * whether the window competes, whether the window includes the current token,
+ * output rounding, ...), each function below states the reading it uses.
  *
  * All arithmetic is IEEE fp64, two-pass softmax, sequential sums; no blocking,
  * no fusion, no reordering beyond what the definitions state.
