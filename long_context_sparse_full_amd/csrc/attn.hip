@@ -387,6 +387,13 @@ __device__ __forceinline__ void merge_and_store(const ScanParams& P, WaveState<D
   }
 }
 
+// wait until at most N vector-memory operations of this wave are in flight
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 // Query fragments (MFMA B operand of QK^T): row r, head-dim slice dmap(c, g4).
 template <bool FP8, int D>
 __device__ __forceinline__ void load_q(u32x4_t (&qf)[D / 32], const ScanParams& P, int b, int t, int h, bool row_ok,
@@ -394,6 +401,10 @@ __device__ __forceinline__ void load_q(u32x4_t (&qf)[D / 32], const ScanParams& 
   const uint16_t* qb = (const uint16_t*)P.q + (((int64_t)b * P.Tq + (row_ok ? t : 0)) * P.Hq + (row_ok ? h : 0)) * D;
 #pragma unroll
   for (int c = 0; c < D / 32; ++c) qf[c] = row_ok ? *(const u32x4_t*)(qb + dmap<FP8, D>(c, g4)) : u32x4_t{0u, 0u, 0u, 0u};
+  // The fragments arrive before any tile load is issued: left in flight, the
+  // compiler's wait bookkeeping would count them as pending inside the tile
+  // loops and drain the prefetched tile (a full vmcnt(0)) on every iteration.
+  wait_vm<0>();
 }
 
 // Full layer: one workgroup per (position split, unit); waves take interleaved
@@ -466,42 +477,65 @@ __global__ void __launch_bounds__(WAVES * 64, HS2_SCAN_MIN_WAVES) scan_full(Scan
 #pragma unroll
   for (int dt = 0; dt < VE; ++dt) S.o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  auto load = [&](RawTile<FP8, D>& R, int j0) {
+  // full tile (j0 + 31 <= p_max): scalar tile base plus the fixed lane offsets
+  auto load_full = [&](RawTile<FP8, D>& R, int j0) {
     const char* kp[2];
     const char* vp[8];
+    const char* tk = kb + (int64_t)j0 * snb;
+    const char* tv = vb + (int64_t)j0 * snb;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) kp[hh] = tk + koff[hh];
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) vp[kk] = tv + voff[kk];
+    load_tile<FP8, D, HS2_SCAN_NT != 0>(R, kp, vp);
+  };
+  auto load = [&](RawTile<FP8, D>& R, int j0) {
     if (j0 + 31 <= p_max) {
-      const char* tk = kb + (int64_t)j0 * snb;
-      const char* tv = vb + (int64_t)j0 * snb;
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) kp[hh] = tk + koff[hh];
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk) vp[kk] = tv + voff[kk];
+      load_full(R, j0);
     } else {  // tail tile: rows past the last position repeat it
+      const char* kp[2];
+      const char* vp[8];
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) kp[hh] = kb + (int64_t)min(j0 + 16 * hh + r, p_max) * snb + 16 * g4;
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk)
         vp[kk] = vb + (int64_t)min(j0 + 16 * (kk >> 2) + 4 * g4 + (kk & 3), p_max) * snb + VE * r * EB;
+      load_tile<FP8, D, HS2_SCAN_NT != 0>(R, kp, vp);
     }
-    load_tile<FP8, D, HS2_SCAN_NT != 0>(R, kp, vp);
   };
   auto compute = [&](const RawTile<FP8, D>& R, int j0) {
     compute_tile<FP8, D, WRITE_LOGITS>(R, qf, cs, j0, jlim, j0 + 31 > j_nomask, g4,
                                        WRITE_LOGITS && lg_row ? lg_row + j0 : nullptr, lgm_row, P.rows, S);
   };
 
+  // This wave's tiles: j_first + i * jstride for i < n; only the last one can
+  // run past p_max.  The steady-state loop issues its two prefetches without
+  // conditions, so the wait before each compute covers exactly the older tile
+  // (a conditional load makes the compiler's in-order wait counts drain the
+  // prefetch as well); at most three tiles are left to the epilogue.
+  const int j_first = j_begin + wave * 32;
+  const int n = j_first < j_end ? (j_end - 1 - j_first) / jstride + 1 : 0;
+  const int n_full = j_first + 31 <= p_max ? min(n, (p_max - 31 - j_first) / jstride + 1) : 0;
   RawTile<FP8, D> A, B;
-  int j0 = j_begin + wave * 32;
-  if (j0 < j_end) load(A, j0);
-  while (j0 < j_end) {  // ping-pong: load tile n+1 while computing tile n
-    const int j1 = j0 + jstride;
-    if (j1 < j_end) load(B, j1);
+  int i = 0;
+  if (n > 0) load(A, j_first);
+  for (; i + 2 < n_full; i += 2) {
+    const int j0 = j_first + i * jstride;
+    load_full(B, j0 + jstride);
     compute(A, j0);
-    if (j1 >= j_end) break;
-    const int j2 = j1 + jstride;
-    if (j2 < j_end) load(A, j2);
-    compute(B, j1);
-    j0 = j2;
+    load_full(A, j0 + 2 * jstride);
+    compute(B, j0 + jstride);
+  }
+  // tail: A holds tile i; at most three tiles remain
+  if (i < n) {
+    const int j0 = j_first + i * jstride;
+    if (i + 1 < n) load(B, j0 + jstride);
+    compute(A, j0);
+    if (i + 1 < n) {
+      if (i + 2 < n) load(A, j0 + 2 * jstride);
+      compute(B, j0 + jstride);
+      if (i + 2 < n) compute(A, j0 + 2 * jstride);
+    }
   }
   merge_and_store<FP8, D, false, WAVES>(P, S, unit, split, b, g, wave, r, g4, sm_m, sm_l, sm_o);
 }
@@ -1298,13 +1332,6 @@ template <bool FP8, int D, bool VPART = false>
 __device__ __forceinline__ const char* flash_at(const char* base, int row, int byte) {
   using FG = FlashGeom<FP8, D>;
   return base + row * FG::ROWB + (((byte >> 4) ^ flash_swz<FG::CH, VPART>(row)) << 4) + (byte & 15);
-}
-
-// wait until at most N vector-memory operations of this wave are in flight
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt field");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
 // One 16-byte global -> LDS load per lane: lane l's 16 bytes at sbase + voff
