@@ -142,7 +142,7 @@ uint64_t next_epoch() {
 
 struct SelPlan {
   int units, nchunks, nblocks_max;
-  size_t off_state, off_hist, off_cnt, off_bmass, total;
+  size_t off_state, off_hist, off_cnt, off_cand, off_bmass, total;
 };
 
 SelPlan plan_select(int B, int Tq, int Hkv, int N, int block_size) {
@@ -158,6 +158,8 @@ SelPlan plan_select(int B, int Tq, int Hkv, int N, int block_size) {
     off = a256(off + (size_t)p.units * 3 * hs2::kHistBins * sizeof(int32_t));
     p.off_cnt = off;
     off = a256(off + (size_t)p.units * p.nchunks * 258 * sizeof(int32_t));
+    p.off_cand = off;
+    off = a256(off + (size_t)p.units * hs2::kCandWords * sizeof(int32_t));
   } else {
     p.off_bmass = off;
     off = a256(off + (size_t)p.units * p.nblocks_max * sizeof(double));
@@ -179,7 +181,7 @@ int hip_fail(hipError_t e, const char* what) {
 // event timing
 // ---------------------------------------------------------------------------
 const char* const kKernelNames[] = {"full_scan",   "combine",     "score",        "select_init",
-                                    "select_hist", "select_emit",
+                                    "select_hist", "select_collect", "select_finish", "select_emit",
                                     "select_block_mass", "select_block_pick", "sparse_gather", "kv_bridge", "stream_read",
                                     "chunk_full",  "chunk_score", nullptr};
 
@@ -531,6 +533,7 @@ int hs2_select_topk_window(const float* scores, int32_t B, int32_t Tq, int32_t H
   p.state = at<int32_t>(workspace, pl.off_state);
   p.hist = block_size == 1 ? at<int32_t>(workspace, pl.off_hist) : nullptr;
   p.cnt = block_size == 1 ? at<int32_t>(workspace, pl.off_cnt) : nullptr;
+  p.cand = block_size == 1 ? at<int32_t>(workspace, pl.off_cand) : nullptr;
   p.bmass = block_size > 1 ? at<double>(workspace, pl.off_bmass) : nullptr;
   p.nblocks_max = pl.nblocks_max;
   const hipError_t e = hs2::launch_select(p, stream);

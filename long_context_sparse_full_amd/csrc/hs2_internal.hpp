@@ -75,6 +75,14 @@ constexpr int kChunkMinPacks = 4;
 
 constexpr int kSelChunk = 16384;  // candidates per workgroup in the select passes
 constexpr int kHistBins = 4096;  // 12-bit digits
+// collected selection path: largest k, largest 24-bit threshold bin, and the
+// per-row list words (positions above the bin, then the bin's keys and positions)
+constexpr int kCompactTake = 2048;
+constexpr int kCompactBin = 1024;
+constexpr int kCandWords = kCompactTake + 2 * kCompactBin;
+// candidates per row of the collected path (its finishing step keeps a bitmap
+// of them in LDS: 128 KiB at this size)
+constexpr int kCompactMaxCand = 1 << 20;
 
 // Fused decode full layer: workgroup shape and LDS plan shared by the launcher
 // and the host planner.
@@ -127,6 +135,7 @@ struct SelectParams {
   int32_t* state;   // [units][16]
   int32_t* hist;    // [units][3][4096] digit histograms of the three passes
   int32_t* cnt;     // [units][nchunks][258]: keys above the 24-bit prefix, suffix sums of the last digit
+  int32_t* cand;    // [units][kCandWords]: the collected path's lists
   double* bmass;    // [units][nblocks_max] (block mode)
   int nblocks_max;
 };

@@ -14,19 +14,32 @@
 // The emit pass keeps every key above the threshold and the lowest-positioned
 // keys equal to it, compacted in ascending position order.
 //
+// Collected path: the keys that share the 24-bit prefix found by the first two
+// passes are few (a handful on attention scores: the third digit only splits
+// near-equal values).  Where that bin and k are small enough, one pass
+// collects the keys above the prefix (all selected) and the bin's keys, and
+// one workgroup per row finishes the selection on chip: the bin's keys in
+// (score desc, position asc) order, then every taken position sorted
+// ascending.  That replaces the third histogram pass and the emit pass, each a
+// full read of the scores; rows whose bin is too large take those two passes.
+//
 // Block mode (block_size > 1) is the previous generation's 64-token block
 // selection (zgeo.com.cn comparison table): block mass = fp64 sum of its
 // scores over C in ascending position, heaviest blocks first, ties to the
 // lower block.
+#include <atomic>
+
 #include "hs2_internal.hpp"
 
 namespace hs2 {
 namespace {
 
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
 // per-unit state; each pass reads the slots of the previous kernel and writes
 // its own, so no kernel reads a slot that a sibling workgroup is writing
 enum { ST_MODE = 0, ST_NCAND = 1, ST_TAKE = 2, ST_P = 3, ST_PREFIX1 = 4, ST_NEED1 = 5,
-       ST_PREFIX2 = 6, ST_NEED2 = 7, ST_WORDS = 16 };
+       ST_PREFIX2 = 6, ST_NEED2 = 7, ST_COMPACT = 8, ST_NABOVE = 9, ST_NBIN = 10, ST_WORDS = 16 };
 enum { MODE_RADIX = 0, MODE_ALL = 1, MODE_NONE = 2 };
 
 __device__ __forceinline__ uint32_t score_key(float s) {
@@ -76,6 +89,9 @@ __global__ void __launch_bounds__(256) sel_init(SelectParams P) {
     st[ST_NCAND] = ncand;
     st[ST_TAKE] = take;
     st[ST_P] = p;
+    st[ST_COMPACT] = 0;
+    st[ST_NABOVE] = 0;
+    st[ST_NBIN] = 0;
   }
   if (P.block_size == 1) {
     int32_t* h = P.hist + (int64_t)u * 3 * kHistBins;
@@ -96,9 +112,10 @@ struct Digit {
 // number of keys in higher digits.  Thread T owns the BINS/256 digits just
 // below BINS - T*BINS/256, so a forward scan over threads runs from the top.
 template <int PASS>
-__device__ void find_digit(const int32_t* gh, int need, int32_t* sm, int& digit, int& above_out) {
+__device__ void find_digit(const int32_t* gh, int need, int32_t* sm, int& digit, int& above_out,
+                           int* count_out = nullptr) {
   constexpr int BINS = Digit<PASS>::BINS, BPT = BINS / 256;
-  __shared__ int32_t s_digit, s_above;
+  __shared__ int32_t s_digit, s_above, s_count;
   const int T = threadIdx.x;
   const int hi_d = BINS - T * BPT - 1;
   int32_t c[BPT];
@@ -117,6 +134,7 @@ __device__ void find_digit(const int32_t* gh, int need, int32_t* sm, int& digit,
       if (a < need && need <= a + c[e]) {
         s_digit = hi_d - e;
         s_above = a;
+        s_count = c[e];
       }
       a += c[e];
     }
@@ -124,6 +142,7 @@ __device__ void find_digit(const int32_t* gh, int need, int32_t* sm, int& digit,
   __syncthreads();
   digit = s_digit;
   above_out = s_above;
+  if (count_out) *count_out = s_count;
   __syncthreads();
 }
 
@@ -226,6 +245,7 @@ __global__ void __launch_bounds__(256) sel_hist(SelectParams P) {
   const int u = blockIdx.y, chunk = blockIdx.x;
   int32_t* st = P.state + (int64_t)u * ST_WORDS;
   if (st[ST_MODE] != MODE_RADIX) return;
+  if (PASS == 2 && st[ST_COMPACT]) return;  // finished by the collected path
   const int ncand = st[ST_NCAND];
   const int base = chunk * kSelChunk;
   if (base >= ncand) return;
@@ -273,6 +293,202 @@ __global__ void __launch_bounds__(256) sel_hist(SelectParams P) {
   }
 }
 
+// Forced window after the `take` selected positions, then the count and the
+// -1 padding of the row's list.
+__device__ __forceinline__ void write_window(const SelectParams& P, int u, int take, int p, int32_t* out) {
+  const int wlo = max(0, p - P.window + 1);
+  const int nw = p - wlo + 1;
+  for (int i = threadIdx.x; i < nw; i += 256) out[take + i] = wlo + i;
+  for (int i = take + nw + threadIdx.x; i < P.max_sel; i += 256) out[i] = -1;
+  if (threadIdx.x == 0) P.count[u] = take + nw;
+}
+
+// Collected path, first step (after the second histogram pass): settle the
+// second digit, decide whether the row is collected (k <= kCompactTake and at
+// most kCompactBin keys share the 24-bit prefix -- both known exactly from the
+// histograms), and if so append this chunk's keys above the prefix (positions)
+// and in its bin (key, position) to the row's lists.  Offsets come from one
+// atomic per list and workgroup, so list order varies between runs; the
+// finishing kernel sorts, which makes the result deterministic.
+__global__ void __launch_bounds__(256) sel_collect(SelectParams P) {
+  __shared__ int32_t sm[264];
+  __shared__ int32_t s_base[2];
+  const int u = blockIdx.y, chunk = blockIdx.x;
+  int32_t* st = P.state + (int64_t)u * ST_WORDS;
+  if (st[ST_MODE] != MODE_RADIX) return;
+  const int ncand = st[ST_NCAND];
+  const int base = chunk * kSelChunk;
+  if (base >= ncand) return;
+  const int end = min(base + kSelChunk, ncand);
+  ChunkKeys K;
+  load_keys(P.scores + (int64_t)u * P.N, base, end, (P.N & 3) == 0, K);
+  const int32_t* hist = P.hist + (int64_t)u * 3 * kHistBins;
+  int need = st[ST_NEED1];
+  int d, above, nbin;
+  find_digit<1>(hist + kHistBins, need, sm, d, above, &nbin);
+  const uint32_t prefix = (uint32_t)st[ST_PREFIX1] | ((uint32_t)d << Digit<1>::SHIFT);
+  need -= above;
+  const bool compact = st[ST_TAKE] <= kCompactTake && nbin <= kCompactBin && ncand <= kCompactMaxCand;
+  if (chunk == 0 && threadIdx.x == 0) {
+    st[ST_PREFIX2] = (int32_t)prefix;
+    st[ST_NEED2] = need;
+    st[ST_COMPACT] = compact;
+  }
+  if (!compact) return;
+  const uint32_t p24 = prefix >> 8;
+  uint64_t hit_a = 0, hit_b = 0;  // keys above the prefix / in its bin
+#pragma unroll
+  for (int i = 0; i < kKeysPerThread; ++i) {
+    const uint32_t hk = K.key[i] >> 8;
+    hit_a |= (uint64_t)(hk > p24) << i;
+    hit_b |= (uint64_t)(hk == p24) << i;
+  }
+  hit_a &= K.valid;
+  hit_b &= K.valid;
+  const int32_t na = __popcll(hit_a), nb = __popcll(hit_b);
+  // both counts in one scan: at most kSelChunk each, so the halves never carry
+  int32_t tot;
+  const int32_t off = block_exclusive_scan<int32_t>((na << 16) | nb, sm, tot);
+  if (threadIdx.x == 0) {
+    s_base[0] = atomicAdd(&st[ST_NABOVE], tot >> 16);
+    s_base[1] = atomicAdd(&st[ST_NBIN], tot & 0xffff);
+  }
+  __syncthreads();
+  int32_t* cand = P.cand + (int64_t)u * kCandWords;
+  int oa = s_base[0] + (off >> 16), ob = s_base[1] + (off & 0xffff);
+  if (hit_a | hit_b) {
+#pragma unroll
+    for (int i = 0; i < kKeysPerThread; ++i) {
+      const int pos = base + 4 * (threadIdx.x + 256 * (i >> 2)) + (i & 3);
+      if (hit_a >> i & 1) {
+        if (oa < kCompactTake) cand[oa] = pos;
+        ++oa;
+      } else if (hit_b >> i & 1) {
+        if (ob < kCompactBin) {
+          cand[kCompactTake + ob] = (int32_t)K.key[i];
+          cand[kCompactTake + kCompactBin + ob] = pos;
+        }
+        ++ob;
+      }
+    }
+  }
+}
+
+// Ascending bitonic sort of n (a power of two) LDS elements by the workgroup.
+template <typename T>
+__device__ void lds_bitonic_sort(T* a, int n) {
+  for (int k = 2; k <= n; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = threadIdx.x; i < n; i += 256) {
+        const int l = i ^ j;
+        if (l > i) {
+          const T x = a[i], y = a[l];
+          if ((x > y) == ((i & k) == 0)) {
+            a[i] = y;
+            a[l] = x;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+__device__ __forceinline__ int pow2_at_least(int n) {
+  int m = 1;
+  while (m < n) m <<= 1;
+  return m;
+}
+
+// Collected path, second step: one workgroup per collected row.  The bin's
+// keys sorted by (score desc, position asc) give the need2 highest keys with
+// ties to the lower position.  Those and the keys above the prefix are the
+// row's `take` positions: marked in an LDS bitmap over the candidates, they
+// come out in ascending order from a prefix count of the bitmap, followed by
+// the window.  Each thread counts a run of 16-byte bitmap groups; group q sits
+// at q + q/32, so the runs of 16 consecutive threads start on distinct banks.
+__host__ __device__ __forceinline__ int bm_slot4(int q) { return q + (q >> 5); }
+// workgroups per selection pass from which the passes are throughput-bound
+constexpr int kCollectMinWorkgroups = 2048;
+// dynamic LDS of the finishing kernel for rows of up to min(N, kCompactMaxCand) candidates
+inline size_t finish_lds_bytes(int N) {
+  const int nq = (min(N, kCompactMaxCand) + 127) >> 7;
+  return ((size_t)bm_slot4(nq - 1) + 1) * 16;
+}
+
+__global__ void __launch_bounds__(256) sel_finish(SelectParams P) {
+  extern __shared__ __align__(16) u32x4_t bm4[];  // finish_lds_bytes(N)
+  __shared__ uint64_t s_bin[kCompactBin];
+  __shared__ int32_t sm[264];
+  const int u = blockIdx.x;
+  const int32_t* st = P.state + (int64_t)u * ST_WORDS;
+  if (st[ST_MODE] != MODE_RADIX || !st[ST_COMPACT]) return;
+  const int take = st[ST_TAKE], p = st[ST_P], ncand = st[ST_NCAND];
+  // the histograms make these exact (na + need = take, need <= nb); the clamps
+  // only keep LDS accesses inside their arrays
+  const int na = min(st[ST_NABOVE], kCompactTake);
+  const int nb = min(st[ST_NBIN], kCompactBin);
+  const int need = min(max(st[ST_NEED2], 0), nb);
+  const int32_t* cand = P.cand + (int64_t)u * kCandWords;
+  // every list load issued at once: positions above the prefix, then the bin
+  constexpr int kAbovePerThread = kCompactTake / 256;
+  int32_t apos[kAbovePerThread];
+#pragma unroll
+  for (int r = 0; r < kAbovePerThread; ++r) {
+    const int i = threadIdx.x + 256 * r;
+    apos[r] = i < na ? cand[i] : -1;
+  }
+  const int nbp = pow2_at_least(nb);
+  for (int i = threadIdx.x; i < nbp; i += 256)
+    s_bin[i] = i < nb ? ((uint64_t)(~(uint32_t)cand[kCompactTake + i]) << 32) |
+                            (uint32_t)cand[kCompactTake + kCompactBin + i]
+                      : ~0ull;
+  const int nq = (ncand + 127) >> 7;  // 128-position groups
+  const int nslots = bm_slot4(nq - 1) + 1;
+  for (int i = threadIdx.x; i < nslots; i += 256) bm4[i] = u32x4_t{0u, 0u, 0u, 0u};
+  __syncthreads();
+  lds_bitonic_sort(s_bin, nbp);
+  uint32_t* bm = (uint32_t*)bm4;
+  auto mark = [&](int pos) {
+    if (pos >= 0 && pos < ncand) atomicOr(&bm[4 * bm_slot4(pos >> 7) + ((pos >> 5) & 3)], 1u << (pos & 31));
+  };
+#pragma unroll
+  for (int r = 0; r < kAbovePerThread; ++r) mark(apos[r]);
+  for (int i = threadIdx.x; i < need; i += 256) mark((int)(uint32_t)s_bin[i]);
+  __syncthreads();
+  // at most 32 groups per thread (kCompactMaxCand / 128 / 256); the mask of
+  // the non-empty ones lets the output loop visit only those
+  const int per = (nq + 255) >> 8;
+  const int q0 = min((int)threadIdx.x * per, nq), q1 = min(q0 + per, nq);
+  int32_t cnt = 0;
+  uint32_t nz = 0;
+#pragma unroll 4
+  for (int q = q0; q < q1; ++q) {
+    const u32x4_t v = bm4[bm_slot4(q)];
+    const int c = __popc(v.x) + __popc(v.y) + __popc(v.z) + __popc(v.w);
+    cnt += c;
+    nz |= (uint32_t)(c != 0) << (q - q0);
+  }
+  int32_t tot;
+  int32_t o = block_exclusive_scan<int32_t>(cnt, sm, tot);
+  int32_t* out = P.idx + (int64_t)u * P.max_sel;
+  while (nz) {
+    const int q = q0 + __builtin_ctz(nz);
+    nz &= nz - 1;
+    const u32x4_t v = bm4[bm_slot4(q)];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      uint32_t bits = v[c];
+      while (bits) {
+        if (o < take) out[o] = (q << 7) + (c << 5) + __builtin_ctz(bits);
+        ++o;
+        bits &= bits - 1;
+      }
+    }
+  }
+  write_window(P, u, take, p, out);
+}
+
 // Ascending compaction: every key above tau and the lowest-positioned keys
 // equal to tau (tau and their number from the last digit's histogram), then
 // (chunk 0) the forced window, the count and the padding.
@@ -286,13 +502,8 @@ __global__ void __launch_bounds__(256) sel_emit(SelectParams P) {
   const int p = st[ST_P];
   int32_t* out = P.idx + (int64_t)u * P.max_sel;
 
-  if (chunk == 0) {
-    const int wlo = max(0, p - P.window + 1);
-    const int nw = p - wlo + 1;
-    for (int i = threadIdx.x; i < nw; i += 256) out[take + i] = wlo + i;
-    for (int i = take + nw + threadIdx.x; i < P.max_sel; i += 256) out[i] = -1;
-    if (threadIdx.x == 0) P.count[u] = take + nw;
-  }
+  if (mode == MODE_RADIX && st[ST_COMPACT]) return;  // written by the collected path
+  if (chunk == 0) write_window(P, u, take, p, out);
   if (mode == MODE_NONE) return;
   const int base = chunk * kSelChunk;
   if (base >= ncand) return;
@@ -484,12 +695,32 @@ hipError_t launch_select(const SelectParams& p, hipStream_t s) {
   } while (0)
   HS2_L("select_init", sel_init, dim3(p.units));
   if (p.block_size == 1) {
-    if (p.units * p.nchunks < 2048) {  // latency-bound passes
+    if (p.units * p.nchunks < kCollectMinWorkgroups) {  // latency-bound passes
       HS2_L("select_hist", (sel_hist<0, true>), grid_c);
     } else {
       HS2_L("select_hist", (sel_hist<0, false>), grid_c);
     }
     HS2_L("select_hist", (sel_hist<1, false>), grid_c);
+    // The collected path saves two full reads of the scores but adds two
+    // launches: taken where the passes are throughput-bound.
+    if (p.units * p.nchunks >= kCollectMinWorkgroups) {
+      HS2_L("select_collect", sel_collect, grid_c);
+      // the LDS attribute is set once per device, for the largest bitmap
+      static std::atomic<uint64_t> attr_done{0};
+      int dev = 0;
+      if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
+      const uint64_t bit = 1ull << (dev & 63);
+      if (!(attr_done.load() & bit)) {
+        if ((e = hipFuncSetAttribute((const void*)sel_finish, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     (int)finish_lds_bytes(kCompactMaxCand))) != hipSuccess)
+          return e;
+        attr_done.fetch_or(bit);
+      }
+      const size_t lds = finish_lds_bytes(p.N);
+      TimedLaunch tl_("select_finish", s);
+      hipLaunchKernelGGL(sel_finish, dim3(p.units), dim3(256), lds, s, p);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     HS2_L("select_hist", (sel_hist<2, false>), grid_c);
     HS2_L("select_emit", sel_emit, grid_c);
   } else {

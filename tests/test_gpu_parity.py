@@ -153,6 +153,18 @@ SEL_CASES = [
     (1, 1, 2, 20000, 300, 16, 1, "allequal"),  # every candidate in one bin of each digit
     (1, 2, 1, 30000, 3000, 64, 1, "random"),   # k of several thousand
     (2, 2, 2, 40000, 2048, 128, 1, "ties"),    # heavy ties across chunks
+    # a few thousand levels: small 24-bit bins with exact ties at the threshold
+    # (collected path; ties resolved by position on chip)
+    (1, 2, 2, 70000, 1024, 128, 1, "levels"),
+    (1, 1, 3, 40000, 2048, 64, 1, "levels"),   # largest k of the collected path
+    (1, 1, 2, 40000, 2049, 64, 1, "levels"),   # one more: the histogram path
+    (3, 1, 1, 20001, 700, 5, 1, "levels"),     # odd N (scalar key loads)
+    # 2048 rows or more: the collected path (passes throughput-bound)
+    (1, 512, 4, 16384, 1024, 128, 1, "levels"),
+    (1, 512, 4, 16384, 1024, 128, 1, "mixed"),  # rows alternate small and huge threshold bins
+    (2, 256, 4, 8000, 2048, 16, 1, "levels"),   # largest k of the collected path
+    (1, 256, 8, 20000, 2049, 64, 1, "levels"),  # k above it: every row on the histogram path
+    (1, 1024, 2, 12001, 300, 0, 1, "tiny"),     # odd N, no window, every row's bin too large
 ]
 
 
@@ -167,6 +179,11 @@ def test_select_bit_exact_on_identical_scores(hs2, case):
         sc = (rng.integers(0, 6, (B, Tq, Hkv, N)) / 64.0).astype(np.float32)
     elif kind == "allequal":
         sc = np.full((B, Tq, Hkv, N), 1.0 / N, np.float32)
+    elif kind == "levels":
+        sc = (rng.integers(0, 20000, (B, Tq, Hkv, N)) / 20000.0 * 1e-3).astype(np.float32)
+    elif kind == "mixed":  # even rows: a few thousand levels; odd rows: six values
+        sc = (rng.integers(0, 20000, (B, Tq, Hkv, N)) / 20000.0 * 1e-3).astype(np.float32)
+        sc[:, :, 1::2] = (rng.integers(0, 6, sc[:, :, 1::2].shape) / 64.0).astype(np.float32)
     elif kind == "blockties":
         sc = np.zeros((B, Tq, Hkv, N), np.float32)
         sc[..., ::64] = 0.5  # every block has the same mass
