@@ -75,6 +75,9 @@ constexpr int kChunkMinPacks = 4;
 
 constexpr int kSelChunk = 16384;  // candidates per workgroup in the select passes
 constexpr int kHistBins = 4096;  // 12-bit digits
+// Workgroups per selection pass from which the passes are throughput-bound
+// (larger grids take the collected path).
+constexpr int kSelMinWorkgroups = 2048;
 // collected selection path: largest k, largest 24-bit threshold bin, and the
 // per-row list words (positions above the bin, then the bin's keys and positions)
 constexpr int kCompactTake = 2048;

@@ -408,8 +408,7 @@ __device__ __forceinline__ int pow2_at_least(int n) {
 // the window.  Each thread counts a run of 16-byte bitmap groups; group q sits
 // at q + q/32, so the runs of 16 consecutive threads start on distinct banks.
 __host__ __device__ __forceinline__ int bm_slot4(int q) { return q + (q >> 5); }
-// workgroups per selection pass from which the passes are throughput-bound
-constexpr int kCollectMinWorkgroups = 2048;
+
 // dynamic LDS of the finishing kernel for rows of up to min(N, kCompactMaxCand) candidates
 inline size_t finish_lds_bytes(int N) {
   const int nq = (min(N, kCompactMaxCand) + 127) >> 7;
@@ -624,6 +623,218 @@ __global__ void __launch_bounds__(256) sel_block_mass(SelectParams P) {
   P.bmass[(int64_t)u * P.nblocks_max + beta] = m;
 }
 
+// Block masses with coalesced loads: a workgroup stages 4096 consecutive
+// scores (64 threads x 16 floats per wave row) in LDS, then one thread per
+// block adds its block's scores in ascending position, as the plain kernel
+// does.  Power-of-two block sizes up to 256; LDS slot i + i / BS keeps the
+// threads' sequential reads on distinct banks.
+constexpr int kMassTile = 4096;
+template <int BS>
+__global__ void __launch_bounds__(256) sel_block_mass_tiled(SelectParams P) {
+  __shared__ float sv[kMassTile + kMassTile / BS];
+  const int u = blockIdx.y;
+  const int32_t* st = P.state + (int64_t)u * ST_WORDS;
+  const int ncand = st[ST_NCAND];
+  const int lo = blockIdx.x * kMassTile;
+  if (lo >= ncand) return;
+  const float* s = P.scores + (int64_t)u * P.N;
+  const bool vec_ok = (P.N & 3) == 0;
+#pragma unroll
+  for (int r = 0; r < kMassTile / 1024; ++r) {
+    const int i = 4 * threadIdx.x + 1024 * r;  // tile offset of this float4
+    const int j = lo + i;
+    float4 v;
+    if (vec_ok && j + 3 < ncand) {
+      v = *(const float4*)(s + j);
+    } else {
+      v.x = j < ncand ? s[j] : 0.f;
+      v.y = j + 1 < ncand ? s[j + 1] : 0.f;
+      v.z = j + 2 < ncand ? s[j + 2] : 0.f;
+      v.w = j + 3 < ncand ? s[j + 3] : 0.f;
+    }
+    const int base = i + i / BS;  // 4 | BS, so the float4 stays inside one block
+    sv[base] = v.x;
+    sv[base + 1] = v.y;
+    sv[base + 2] = v.z;
+    sv[base + 3] = v.w;
+  }
+  __syncthreads();
+  constexpr int NB = kMassTile / BS;
+  for (int t = threadIdx.x; t < NB; t += 256) {
+    const int beta = blockIdx.x * NB + t;
+    if (beta * BS >= ncand) break;
+    const int n = min(BS, ncand - beta * BS);
+    const float* b = sv + t * (BS + 1);
+    double m = 0.0;
+    for (int e = 0; e < n; ++e) m += (double)b[e];
+    P.bmass[(int64_t)u * P.nblocks_max + beta] = m;
+  }
+}
+
+// (mass desc, block asc) order: true when (m, b) comes before (bm, bb)
+__device__ __forceinline__ bool mass_before(double m, int b, double bm, int bb) {
+  return m > bm || (m == bm && b < bb);
+}
+
+// Better of two (mass, block) candidates in (mass desc, block asc) order.
+__device__ __forceinline__ void pick_better(double& m, int& b, double m2, int b2) {
+  if (mass_before(m2, b2, m, b)) {
+    m = m2;
+    b = b2;
+  }
+}
+__device__ __forceinline__ double dbl_of(uint32_t lo, uint32_t hi) {
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+// DPP step: candidate of the lane given by dpp_ctrl (within its row of 16)
+template <int CTRL>
+__device__ __forceinline__ void argmax_dpp(double& m, int& b) {
+  const uint64_t u = (uint64_t)__double_as_longlong(m);
+  const uint32_t lo = __builtin_amdgcn_update_dpp(0u, (uint32_t)u, CTRL, 0xF, 0xF, false);
+  const uint32_t hi = __builtin_amdgcn_update_dpp(0u, (uint32_t)(u >> 32), CTRL, 0xF, 0xF, false);
+  const int b2 = __builtin_amdgcn_update_dpp(0, b, CTRL, 0xF, 0xF, false);
+  pick_better(m, b, dbl_of(lo, hi), b2);
+}
+// Wave-wide best (mass desc, block asc); every lane returns it.  Quad swaps,
+// the 8- and 16-lane mirrors, then the gfx950 permlane swaps of 16-lane rows
+// and 32-lane halves: each step merges two groups that already agree.
+__device__ __forceinline__ void wave_argmax(double& m, int& b) {
+  argmax_dpp<0xB1>(m, b);   // quad_perm [1,0,3,2]
+  argmax_dpp<0x4E>(m, b);   // quad_perm [2,3,0,1]
+  argmax_dpp<0x141>(m, b);  // row_half_mirror
+  argmax_dpp<0x140>(m, b);  // row_mirror
+  {
+    const uint64_t u = (uint64_t)__double_as_longlong(m);
+    const auto lo = __builtin_amdgcn_permlane16_swap((uint32_t)u, (uint32_t)u, false, false);
+    const auto hi = __builtin_amdgcn_permlane16_swap((uint32_t)(u >> 32), (uint32_t)(u >> 32), false, false);
+    const auto bb = __builtin_amdgcn_permlane16_swap((uint32_t)b, (uint32_t)b, false, false);
+    m = dbl_of(lo[0], hi[0]);
+    b = (int)bb[0];
+    pick_better(m, b, dbl_of(lo[1], hi[1]), (int)bb[1]);
+  }
+  {
+    const uint64_t u = (uint64_t)__double_as_longlong(m);
+    const auto lo = __builtin_amdgcn_permlane32_swap((uint32_t)u, (uint32_t)u, false, false);
+    const auto hi = __builtin_amdgcn_permlane32_swap((uint32_t)(u >> 32), (uint32_t)(u >> 32), false, false);
+    const auto bb = __builtin_amdgcn_permlane32_swap((uint32_t)b, (uint32_t)b, false, false);
+    m = dbl_of(lo[0], hi[0]);
+    b = (int)bb[0];
+    pick_better(m, b, dbl_of(lo[1], hi[1]), (int)bb[1]);
+  }
+}
+
+// Heaviest blocks, one wave per row, masses in LDS (rows of up to
+// kPickLdsBlocks blocks: at most 64 KiB).  Each lane keeps the best of its
+// strided blocks; a round takes the wave's best (no barriers) and only its
+// owner lane rescans.  Same order and ties as the plain kernel.  The ascending
+// emit then walks the blocks 64 at a time: a ballot gives each taken block its
+// rank, and the wave writes a taken block's positions with coalesced stores.
+constexpr int kPickLdsBlocks = 8192;
+__global__ void __launch_bounds__(64) sel_block_pick_wave(SelectParams P) {
+  extern __shared__ double s_mass[];  // [nblocks_max]
+  const int u = blockIdx.x;
+  const int lane = threadIdx.x;
+  const int32_t* st = P.state + (int64_t)u * ST_WORDS;
+  const int ncand = st[ST_NCAND];
+  const int take = st[ST_TAKE];
+  const int p = st[ST_P];
+  const int bs = P.block_size;
+  const int nb = ncand > 0 ? (ncand - 1) / bs + 1 : 0;
+  const double* bm = P.bmass + (int64_t)u * P.nblocks_max;
+  // each lane's four best blocks, best first; (-1, INT_MAX) marks an empty slot
+  constexpr int L = 4;
+  double cm[L];
+  int cb[L];
+  auto clear = [&]() {
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+      cm[i] = -1.0;
+      cb[i] = 0x7fffffff;
+    }
+  };
+  auto insert = [&](double x, int beta) {
+    if (!mass_before(x, beta, cm[L - 1], cb[L - 1])) return;
+    cm[L - 1] = x;
+    cb[L - 1] = beta;
+#pragma unroll
+    for (int i = L - 1; i > 0; --i)
+      if (mass_before(cm[i], cb[i], cm[i - 1], cb[i - 1])) {
+        const double tm = cm[i];
+        const int tb = cb[i];
+        cm[i] = cm[i - 1];
+        cb[i] = cb[i - 1];
+        cm[i - 1] = tm;
+        cb[i - 1] = tb;
+      }
+  };
+  clear();
+  constexpr int R = 16;  // loads in flight per lane
+  for (int b0 = 0; b0 < nb; b0 += 64 * R) {
+    double x[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int beta = b0 + lane + 64 * r;
+      x[r] = beta < nb ? bm[beta] : -1.0;
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int beta = b0 + lane + 64 * r;
+      if (beta < nb) {
+        s_mass[beta] = x[r];
+        insert(x[r], beta);
+      }
+    }
+  }
+  int left = L;  // entries of the list not taken yet
+  for (int round = 0; round < take; ++round) {
+    double m = cm[0];
+    int b = cb[0];
+    wave_argmax(m, b);
+    if (cb[0] == b) {  // the owner lane takes its head
+      s_mass[b] = -1.0;
+#pragma unroll
+      for (int i = 0; i < L - 1; ++i) {
+        cm[i] = cm[i + 1];
+        cb[i] = cb[i + 1];
+      }
+      cm[L - 1] = -1.0;
+      cb[L - 1] = 0x7fffffff;
+      if (--left == 0) {  // list used up: rebuild it from the untaken blocks
+        clear();
+#pragma unroll 4
+        for (int beta = lane; beta < nb; beta += 64) {
+          const double x = s_mass[beta];
+          if (x >= 0.0) insert(x, beta);
+        }
+        left = L;
+      }
+    }
+  }
+  int32_t* out = P.idx + (int64_t)u * P.max_sel;
+  int32_t written = 0;
+  for (int b0 = 0; b0 < nb; b0 += 64) {
+    const int beta = b0 + lane;
+    const uint64_t tk = __ballot(beta < nb && s_mass[beta] == -1.0);
+    uint64_t rest = tk;
+    int32_t off = written;
+    while (rest) {  // wave-uniform: one taken block at a time, in ascending order
+      const int lb2 = __builtin_ctzll(rest);
+      rest &= rest - 1;
+      const int blk = b0 + lb2;
+      const int n = min(blk * bs + bs, ncand) - blk * bs;
+      for (int e = lane; e < n; e += 64)
+        if (off + e < P.max_sel) out[off + e] = blk * bs + e;
+      off += n;
+    }
+    written = off;
+  }
+  const int wlo = max(0, p - P.window + 1);
+  const int nw = p - wlo + 1;
+  for (int i = lane; i < nw && written + i < P.max_sel; i += 64) out[written + i] = wlo + i;
+  for (int i = written + nw + lane; i < P.max_sel; i += 64) out[i] = -1;
+  if (lane == 0) P.count[u] = written + nw;
+}
+
 __global__ void __launch_bounds__(256) sel_block_pick(SelectParams P) {
   __shared__ double s_m[256];
   __shared__ int s_b[256];
@@ -695,7 +906,7 @@ hipError_t launch_select(const SelectParams& p, hipStream_t s) {
   } while (0)
   HS2_L("select_init", sel_init, dim3(p.units));
   if (p.block_size == 1) {
-    if (p.units * p.nchunks < kCollectMinWorkgroups) {  // latency-bound passes
+    if (p.units * p.nchunks < kSelMinWorkgroups) {  // latency-bound passes
       HS2_L("select_hist", (sel_hist<0, true>), grid_c);
     } else {
       HS2_L("select_hist", (sel_hist<0, false>), grid_c);
@@ -703,7 +914,7 @@ hipError_t launch_select(const SelectParams& p, hipStream_t s) {
     HS2_L("select_hist", (sel_hist<1, false>), grid_c);
     // The collected path saves two full reads of the scores but adds two
     // launches: taken where the passes are throughput-bound.
-    if (p.units * p.nchunks >= kCollectMinWorkgroups) {
+    if (p.units * p.nchunks >= kSelMinWorkgroups) {
       HS2_L("select_collect", sel_collect, grid_c);
       // the LDS attribute is set once per device, for the largest bitmap
       static std::atomic<uint64_t> attr_done{0};
@@ -724,8 +935,25 @@ hipError_t launch_select(const SelectParams& p, hipStream_t s) {
     HS2_L("select_hist", (sel_hist<2, false>), grid_c);
     HS2_L("select_emit", sel_emit, grid_c);
   } else {
-    HS2_L("select_block_mass", sel_block_mass, dim3((p.nblocks_max + 255) / 256, p.units));
-    HS2_L("select_block_pick", sel_block_pick, dim3(p.units));
+    const dim3 grid_t((p.N + kMassTile - 1) / kMassTile, p.units);
+    switch (p.block_size) {
+      case 4: HS2_L("select_block_mass", sel_block_mass_tiled<4>, grid_t); break;
+      case 8: HS2_L("select_block_mass", sel_block_mass_tiled<8>, grid_t); break;
+      case 16: HS2_L("select_block_mass", sel_block_mass_tiled<16>, grid_t); break;
+      case 32: HS2_L("select_block_mass", sel_block_mass_tiled<32>, grid_t); break;
+      case 64: HS2_L("select_block_mass", sel_block_mass_tiled<64>, grid_t); break;
+      case 128: HS2_L("select_block_mass", sel_block_mass_tiled<128>, grid_t); break;
+      case 256: HS2_L("select_block_mass", sel_block_mass_tiled<256>, grid_t); break;
+      default: HS2_L("select_block_mass", sel_block_mass, dim3((p.nblocks_max + 255) / 256, p.units));
+    }
+    if (p.nblocks_max <= kPickLdsBlocks) {
+      const size_t lds = (size_t)max(p.nblocks_max, 1) * sizeof(double);
+      TimedLaunch tl_("select_block_pick", s);
+      hipLaunchKernelGGL(sel_block_pick_wave, dim3(p.units), dim3(64), lds, s, p);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    } else {
+      HS2_L("select_block_pick", sel_block_pick, dim3(p.units));
+    }
   }
 #undef HS2_L
   return hipSuccess;

@@ -165,6 +165,15 @@ SEL_CASES = [
     (2, 256, 4, 8000, 2048, 16, 1, "levels"),   # largest k of the collected path
     (1, 256, 8, 20000, 2049, 64, 1, "levels"),  # k above it: every row on the histogram path
     (1, 1024, 2, 12001, 300, 0, 1, "tiny"),     # odd N, no window, every row's bin too large
+    (1, 32, 8, 300001, 700, 64, 1, "levels"),   # 19 chunks per row, two per workgroup
+    (1, 32, 8, 300001, 700, 64, 1, "mixed"),
+    # block baseline: staged block masses (power-of-two sizes), LDS pick
+    (1, 64, 4, 131072, 16, 128, 64, "random"),  # the chunk workload's row shape
+    (1, 3, 2, 10001, 40, 7, 4, "random"),       # 4-position blocks, odd N
+    (1, 2, 2, 9000, 25, 16, 16, "blockties"),
+    (1, 1, 2, 70000, 9, 3, 256, "random"),
+    (1, 1, 1, 9000, 5, 3, 100, "random"),       # other sizes: plain mass kernel
+    (1, 1, 1, 600000, 30, 64, 64, "random"),    # more blocks than the LDS pick holds
 ]
 
 
