@@ -179,51 +179,49 @@ __device__ __forceinline__ void load_keys(const float* s, int base, int end, boo
 }
 
 // LDS histogram of one digit over the keys that match `prefix`.  PASS 0 keys
-// cluster in a few bins (the scores of one row share exponent and leading
-// mantissa bits), so each thread counts some bins in registers and sends only
-// the other keys to the (contended) LDS atomics.  SHORT (grids that do not
-// fill the GPU several times over, whose passes are latency-bound): the bin of
-// the thread's first key, counted with no branches.  Otherwise (throughput-
-// bound grids): the first two bins the thread meets, fewer LDS atomics for a
-// longer dependent chain.
-template <int PASS, bool SHORT>
+// cluster in a few neighbouring bins (the scores of one row share their
+// exponent and leading mantissa bits), which would serialise the LDS atomics.
+// So each thread counts the keys of an 8-bin window, starting three bins below
+// the bin of the wave's first key, in 8-bit fields of one 64-bit word (at most
+// 64 keys per thread: no field overflows); only keys outside the window use
+// LDS atomics.  The window counts are summed over the wave (16-bit fields) and
+// added by one lane.
+template <int PASS>
 __device__ __forceinline__ void hist_keys(const ChunkKeys& K, uint32_t prefix, int32_t* h) {
   using DG = Digit<PASS>;
-  if constexpr (PASS == 0 && SHORT) {
-    const uint32_t b1 = K.key[0] >> DG::SHIFT;  // (key 0 may be a padding 0: only register hits lost)
-    int32_t c1 = 0;
+  if constexpr (PASS == 0) {
+    const uint32_t first = __builtin_amdgcn_readfirstlane(K.key[0] >> DG::SHIFT);
+    const uint32_t wbase = first >= 3 ? first - 3 : 0;
+    uint64_t acc = 0;
 #pragma unroll
     for (int i = 0; i < kKeysPerThread; ++i) {
       const bool v = K.valid >> i & 1;
       const uint32_t bin = K.key[i] >> DG::SHIFT;
-      const bool hit = v && bin == b1;
-      c1 += hit;
-      if (v && !hit) atomicAdd(&h[bin], 1);
+      const uint32_t off = bin - wbase;
+      const bool in = off < 8u;
+      acc += (v && in) ? 1ull << (8 * off) : 0ull;
+      if (v && !in) atomicAdd(&h[bin], 1);
     }
-    if (c1) atomicAdd(&h[b1], c1);
-  } else if constexpr (PASS == 0) {
-    uint32_t b1 = 0xffffffffu, b2 = 0xffffffffu;
-    int32_t c1 = 0, c2 = 0;
+    // fields 0-3 and 4-7 widened to 16 bits, then summed over the wave
+    uint64_t lo = 0, hi = 0;
 #pragma unroll
-    for (int i = 0; i < kKeysPerThread; ++i) {
-      if (!(K.valid >> i & 1)) continue;
-      const uint32_t bin = K.key[i] >> DG::SHIFT;
-      if (bin == b1) {
-        ++c1;
-      } else if (bin == b2) {
-        ++c2;
-      } else if (c1 == 0) {
-        b1 = bin;
-        c1 = 1;
-      } else if (c2 == 0) {
-        b2 = bin;
-        c2 = 1;
-      } else {
-        atomicAdd(&h[bin], 1);
+    for (int j = 0; j < 4; ++j) {
+      lo |= ((acc >> (8 * j)) & 0xFFull) << (16 * j);
+      hi |= ((acc >> (8 * j + 32)) & 0xFFull) << (16 * j);
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      lo += __shfl_xor(lo, o);
+      hi += __shfl_xor(hi, o);
+    }
+    if ((threadIdx.x & 63) == 0) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int32_t c0 = (int32_t)((lo >> (16 * j)) & 0xFFFFull), c1 = (int32_t)((hi >> (16 * j)) & 0xFFFFull);
+        if (c0 && wbase + j < (uint32_t)DG::BINS) atomicAdd(&h[wbase + j], c0);
+        if (c1 && wbase + 4 + j < (uint32_t)DG::BINS) atomicAdd(&h[wbase + 4 + j], c1);
       }
     }
-    if (c1) atomicAdd(&h[b1], c1);
-    if (c2) atomicAdd(&h[b2], c2);
   } else {
 #pragma unroll
     for (int i = 0; i < kKeysPerThread; ++i)
@@ -237,7 +235,7 @@ __device__ __forceinline__ void hist_keys(const ChunkKeys& K, uint32_t prefix, i
 // PASS 2 also stores, per chunk, the count of keys above the 24-bit prefix and
 // the suffix sums of its 256-bin histogram, from which the emit pass gets every
 // chunk's counts above and equal to the final threshold.
-template <int PASS, bool SHORT>
+template <int PASS>
 __global__ void __launch_bounds__(256) sel_hist(SelectParams P) {
   using DG = Digit<PASS>;
   __shared__ int32_t h[DG::BINS];
@@ -269,7 +267,7 @@ __global__ void __launch_bounds__(256) sel_hist(SelectParams P) {
   }
   for (int i = threadIdx.x; i < DG::BINS; i += 256) h[i] = 0;
   __syncthreads();
-  hist_keys<PASS, SHORT>(K, prefix, h);
+  hist_keys<PASS>(K, prefix, h);
   __syncthreads();
   int32_t* gh = hist + PASS * kHistBins;
   for (int i = threadIdx.x; i < DG::BINS; i += 256)
@@ -906,12 +904,8 @@ hipError_t launch_select(const SelectParams& p, hipStream_t s) {
   } while (0)
   HS2_L("select_init", sel_init, dim3(p.units));
   if (p.block_size == 1) {
-    if (p.units * p.nchunks < kSelMinWorkgroups) {  // latency-bound passes
-      HS2_L("select_hist", (sel_hist<0, true>), grid_c);
-    } else {
-      HS2_L("select_hist", (sel_hist<0, false>), grid_c);
-    }
-    HS2_L("select_hist", (sel_hist<1, false>), grid_c);
+    HS2_L("select_hist", sel_hist<0>, grid_c);
+    HS2_L("select_hist", sel_hist<1>, grid_c);
     // The collected path saves two full reads of the scores but adds two
     // launches: taken where the passes are throughput-bound.
     if (p.units * p.nchunks >= kSelMinWorkgroups) {
@@ -932,7 +926,7 @@ hipError_t launch_select(const SelectParams& p, hipStream_t s) {
       hipLaunchKernelGGL(sel_finish, dim3(p.units), dim3(256), lds, s, p);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    HS2_L("select_hist", (sel_hist<2, false>), grid_c);
+    HS2_L("select_hist", sel_hist<2>, grid_c);
     HS2_L("select_emit", sel_emit, grid_c);
   } else {
     const dim3 grid_t((p.N + kMassTile - 1) / kMassTile, p.units);
