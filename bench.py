@@ -53,6 +53,17 @@ def algorithmic_bytes(spec) -> dict:
             "step": kv_bytes + 2 * scores + spec.n_sparse * gathered}
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def traffic_entry(workload: str):
     """HBM bytes per scan launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated) from
     the committed rocprofv3 summary; None unless it was taken on this workload
@@ -150,7 +161,7 @@ def main():
 
     ws_topk = torch.empty(hs2.full_attn_topk_workspace(k, v, Tq, Hq), dtype=torch.uint8, device="cuda")
 
-    def step():
+    def step(layer1_events=None):
         if args.topk_call:
             hs2.full_attn_topk(k, v, q, spec.q_pos0, spec.k, spec.window, max_sel=spec.max_sel, k_scale=ks,
                                v_scale=vs, out=out, lse=lse, scores=scores, idx=idx, count=cnt, workspace=ws_topk)
@@ -160,11 +171,15 @@ def main():
             hs2.select_topk_window(scores, spec.q_pos0, spec.k, spec.window, max_sel=spec.max_sel, idx=idx,
                                    count=cnt, workspace=ws_sel)
         for i, ql in enumerate(qs):
+            if i == 0 and layer1_events:
+                layer1_events[0].record()
             if args.split_gather:
                 hs2.sparse_attn_gather_ws(k, v, ql, idx, cnt, ws_gather, k_scale=ks, v_scale=vs, out=sp_out[i],
                                           lse=sp_lse[i])
             else:
                 hs2.sparse_attn_gather(k, v, ql, idx, cnt, k_scale=ks, v_scale=vs, out=sp_out[i], lse=sp_lse[i])
+            if i == 0 and layer1_events:
+                layer1_events[1].record()
 
     for _ in range(args.warmup):
         step()
@@ -179,6 +194,60 @@ def main():
     wall_ms = (time.perf_counter() - w0) * 1e3 / args.steps
     ms_step = e0.elapsed_time(e1) / args.steps
     log(f"[bench] {ms_step * 1e3:.1f} us/step (events), {wall_ms * 1e3:.1f} us/step (wall)")
+
+    # per-step distribution (an event pair around each step), warm and cold;
+    # cold: a 512 MiB buffer read before each step, outside its events, evicts
+    # L2 and the 256 MB memory-side cache with clean lines (a written buffer
+    # would leave dirty lines whose write-back the next step would pay); the
+    # first sparse layer is also timed on its own there (its rows then come
+    # from HBM)
+    def pct(xs, q):
+        xs = sorted(xs)
+        return round(xs[min(len(xs) - 1, max(0, int(round(q * (len(xs) - 1)))))], 2)
+
+    def one_step(layer1=None):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        step(layer1)
+        b.record()
+        return a, b
+
+    flush = torch.ones(512 << 20, dtype=torch.uint8, device="cuda")
+    warm, cold, cold_l1 = [], [], []
+    for _ in range(args.steps):
+        warm.append(one_step())
+    for i in range(args.steps):
+        hs2.debug_stream_read(flush)
+        la, lb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        cold.append(one_step((la, lb)))
+        cold_l1.append((la, lb))
+    torch.cuda.synchronize()
+    # the same cold steps again with every launch bracketed by events (these
+    # events add a few us per launch, so the step distribution above has none)
+    hs2.timing_reset()
+    hs2.timing_enable(True)
+    for i in range(args.steps):
+        hs2.debug_stream_read(flush)
+        step()
+    torch.cuda.synchronize()
+    cold_kernels = {}
+    for name in hs2.timing_kernel_names():
+        tot, n = hs2.timing_collect(name)
+        if n and name != "stream_read":
+            cold_kernels[name] = round(tot * 1e3 / n, 2)
+    hs2.timing_enable(False)
+    hs2.timing_reset()
+    warm_us = [a.elapsed_time(b) * 1e3 for a, b in warm]
+    cold_us = [a.elapsed_time(b) * 1e3 for a, b in cold]
+    l1_us = [a.elapsed_time(b) * 1e3 for a, b in cold_l1]
+    del flush
+    gathered = algorithmic_bytes(spec)["gather_per_layer"]
+    step_dist = {"warm_us": {"p10": pct(warm_us, 0.1), "p50": pct(warm_us, 0.5), "p90": pct(warm_us, 0.9)},
+                 "cold_us": {"p10": pct(cold_us, 0.1), "p50": pct(cold_us, 0.5), "p90": pct(cold_us, 0.9)},
+                 "cold_kernels_avg_us": cold_kernels,
+                 "cold_sparse_layer1_us_p50": pct(l1_us, 0.5),
+                 "cold_sparse_layer1_gbps": round(gathered / (pct(l1_us, 0.5) * 1e-6) / 1e9, 1)}
+    log(f"[bench] step distribution: {json.dumps(step_dist)}")
 
     # per-kernel durations from HIP events bracketing each launch on its stream
     hs2.timing_reset()
@@ -220,11 +289,15 @@ def main():
             oracle.sparse_attn(ql, inp.k, inp.v, idx_or, cnt_or, k_scale=inp.k_scale, v_scale=inp.v_scale)
         c2 = time.perf_counter()
         units = B * Tq * Hkv
-        cpu = {"value": round((c2 - c0) * 1e6, 1), "unit": "us/decode-step", "cores": min(units, oracle.num_threads()),
+        used = min(units, oracle.num_threads())
+        cpu = {"value": round((c2 - c0) * 1e6, 1), "unit": "us/decode-step", "cores": used,
                "kind": "oracle",
                "sample": f"one whole decode step of {spec.name} (all {units} kv-head units; the oracle "
-                         f"parallelises over units), fp64; full layer {c1 - c0:.2f}s, select+3 sparse {c2 - c1:.2f}s",
-               "threads_available": threads}
+                         f"parallelises over units, one thread per unit), fp64; full layer {c1 - c0:.2f}s, "
+                         f"select+3 sparse {c2 - c1:.2f}s",
+               "threads_available": threads, "cpu_model": cpu_model(),
+               # one thread per unit: a single thread would run the units one after another
+               "single_thread_estimate_us": round((c1 - c0) * 1e6 * units / -(-units // used) + (c2 - c1) * 1e6, 1)}
         log(f"[bench] oracle: {c2 - c0:.2f}s per step")
 
     line = {
@@ -247,6 +320,7 @@ def main():
         "hbm_gbps": round(ab["step"] / (ms_step * 1e-3) / 1e9, 1),
         "algorithmic_bytes_per_step": ab["step"],
         "wall_us_per_step": round(wall_ms * 1e3, 2),
+        "step_distribution": step_dist,
         "kernels": kernels,
         "roofline": roofline,
         "gather_throughput": gather_tp,
