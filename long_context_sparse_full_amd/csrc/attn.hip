@@ -2309,6 +2309,59 @@ __global__ void __launch_bounds__(256) combine(CombineParams P) {
   }
 }
 
+// The same merge for few splits (the chunk path: a handful per unit): one
+// workgroup per unit.  Rows' (M, L) and split weights go to LDS first, then
+// each thread forms whole outputs (row, head dim) from the splits' partials,
+// which a wave reads as contiguous runs of the head dimension.
+constexpr int kFewSplits = 32;
+__global__ void __launch_bounds__(256) combine_few(CombineParams P) {
+  __shared__ float sw[16][kFewSplits];
+  __shared__ float sM[16], sL[16];
+  const int unit = blockIdx.x, tid = threadIdx.x;
+  const int g = unit % P.Hkv;
+  const int tp = (unit / P.Hkv) % P.n_tpacks;
+  const int b = unit / (P.Hkv * P.n_tpacks);
+  if (tid < P.rows) {
+    const float* ml = P.part_ml + ((int64_t)unit * P.nsplit * 16 + tid) * 2;
+    float m = kNegInf;
+    for (int sp = 0; sp < P.nsplit; ++sp) m = fmaxf(m, ml[sp * 32]);
+    const float Ms = (m == kNegInf) ? 0.f : m;
+    float l = 0.f;
+    for (int sp = 0; sp < P.nsplit; ++sp) {
+      const float w = exp2f(ml[sp * 32] - Ms);
+      sw[tid][sp] = w;
+      l += ml[sp * 32 + 1] * w;
+    }
+    sM[tid] = m;
+    sL[tid] = l;
+  }
+  __syncthreads();
+  const int64_t sstride = (int64_t)16 * P.D;
+  const float vsc = P.v_scale ? P.v_scale[b * P.Hkv + g] : 1.f;
+  for (int e = tid; e < P.rows * P.D; e += 256) {
+    const int r = e / P.D, d = e - r * P.D;
+    const int tl = r / P.G, i = r - tl * P.G;
+    const int t = tp * P.tpack + tl;
+    if (t >= P.Tq) continue;
+    const float* po = P.part_o + ((int64_t)unit * P.nsplit * 16 + r) * P.D + d;
+    float O = 0.f;
+    for (int sp = 0; sp < P.nsplit; ++sp) O += sw[r][sp] * po[sp * sstride];
+    const float L = sL[r];
+    float o = (L > 0.f) ? O / L : 0.f;
+    o *= vsc;
+    const int64_t orow = ((int64_t)b * P.Tq + t) * P.Hq + g * P.G + i;
+    if (P.out_bf16)
+      ((__bf16*)P.out)[orow * P.D + d] = (__bf16)o;
+    else
+      ((float*)P.out)[orow * P.D + d] = o;
+    if (d == 0) {
+      const float l2 = (L > 0.f) ? sM[r] + log2f(L) : kNegInf;
+      if (P.lse) P.lse[orow] = l2 * kLn2;
+      P.lse2[(int64_t)unit * P.rows + r] = l2;
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // scores[b,t,g,j] = sum_{heads of g} 2^(x_hj - lse2_h) for j <= p, 0 beyond
 // ---------------------------------------------------------------------------
@@ -2552,7 +2605,10 @@ hipError_t launch_chunk_score(const ScanParams& p, int kv_dtype, hipStream_t s) 
 
 hipError_t launch_combine(const CombineParams& p, int units, hipStream_t s) {
   TimedLaunch tl("combine", s);
-  hipLaunchKernelGGL(combine, dim3(units, p.rows, p.D / 32), dim3(256), 0, s, p);
+  if (p.nsplit <= kFewSplits)
+    hipLaunchKernelGGL(combine_few, dim3(units), dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL(combine, dim3(units, p.rows, p.D / 32), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
