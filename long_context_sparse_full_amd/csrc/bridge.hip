@@ -9,6 +9,7 @@
 // bf16 MFMA (16x16x32) tiles.
 #include "hs2_internal.hpp"
 
+
 namespace hs2 {
 namespace {
 
@@ -18,42 +19,50 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
-// MFMA form: a workgroup computes a 64 (tokens) x 64 (columns) tile; wave w
-// owns the 32 x 32 quarter (w >> 1, w & 1) as 2 x 2 tiles of 16 x 16.
+// MFMA form: a workgroup computes a BT (tokens) x 64 (columns) tile; wave w
+// owns the (BT/2) x 32 quarter (w >> 1, w & 1) as RT x 2 tiles of 16 x 16
+// (RT = BT / 32).  BT = 32 halves the work per workgroup so that a 512-token
+// block still gives every CU a workgroup (measured: 24 us against 39 us for
+// BT = 64 at 512 x 4096 x 1024; 16-token tiles re-read the weights too often).
 // Stage = 64 of the d_model contraction: hidden rows go straight from global
 // memory into the MFMA A layout (8 consecutive elements per lane); the w_kv
 // tile [64 x 64] goes through LDS, where each lane gathers the 8 contraction
 // elements of its column.  The global loads of a stage are issued kRing
 // stages ahead (a register ring), so the contraction is not paced by one load
 // latency per stage.
-constexpr int kBT = 64, kBC = 64, kKS = 64, kWPad = 8, kRing = 4;
+constexpr int kBC = 64, kKS = 64, kWPad = 8, kRing = 4;
 
+template <int RT>
 struct BridgeStage {
   u32x4_t w[2];
-  u32x4_t a[2][2];
+  u32x4_t a[RT][2];
 };
 
+template <int BT>
 __global__ void __launch_bounds__(256) bridge_mfma(const uint16_t* __restrict__ H, int T, int dm,
                                                    const uint16_t* __restrict__ W, int Hkv, int D, uint16_t* kout,
                                                    uint16_t* vout, int64_t sn, int64_t sh) {
+  static_assert(BT == 32 || BT == 64, "token tile");
+  constexpr int RT = BT / 32, CT = 2;
+  using Stage = BridgeStage<RT>;
   __shared__ uint16_t Ws[kKS][kBC + kWPad];
   const int C = 2 * Hkv * D;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, g4 = lane >> 4;
   const int wr = wave >> 1, wc = wave & 1;
-  const int t0 = blockIdx.y * kBT, c0 = blockIdx.x * kBC;
+  const int t0 = blockIdx.y * BT, c0 = blockIdx.x * kBC;
   // this thread's part of a w_kv stage: row tid/4 of the stage, 16 columns
   const int wrow = tid >> 2, wcol = (tid & 3) * 16;
-  f32x4_t acc[2][2];
+  f32x4_t acc[RT][CT];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < RT; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  int arow[2];
+    for (int b = 0; b < CT; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  int arow[RT];
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt) arow[rt] = min(t0 + wr * 32 + rt * 16 + r16, T - 1);
+  for (int rt = 0; rt < RT; ++rt) arow[rt] = min(t0 + wr * 16 * RT + rt * 16 + r16, T - 1);
 
-  auto load_stage = [&](int k0, BridgeStage& S) {
+  auto load_stage = [&](int k0, Stage& S) {
     // stages past the end reload the last one (unused): the loads stay
     // unconditional, so the compiler's wait counts keep the ring in flight
     k0 = min(k0, dm - kKS);
@@ -61,11 +70,11 @@ __global__ void __launch_bounds__(256) bridge_mfma(const uint16_t* __restrict__ 
     S.w[0] = *(const u32x4_t*)wp;
     S.w[1] = *(const u32x4_t*)(wp + 8);
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
+    for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) S.a[rt][ks] = *(const u32x4_t*)(H + (int64_t)arow[rt] * dm + k0 + ks * 32 + 8 * g4);
   };
-  auto compute_stage = [&](const BridgeStage& S) {
+  auto compute_stage = [&](const Stage& S) {
     __syncthreads();  // previous stage's LDS reads done
     *(u32x4_t*)&Ws[wrow][wcol] = S.w[0];
     *(u32x4_t*)&Ws[wrow][wcol + 8] = S.w[1];
@@ -73,7 +82,7 @@ __global__ void __launch_bounds__(256) bridge_mfma(const uint16_t* __restrict__ 
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
+      for (int ct = 0; ct < CT; ++ct) {
         // B operand (contraction index 8 g4 + 0..7 of column r16) by two
         // transposing 64-bit LDS reads: in each 16-lane group, source lane
         // 4 k4 + a4 names columns 4 a4 .. 4 a4 + 3 of contraction row
@@ -82,20 +91,20 @@ __global__ void __launch_bounds__(256) bridge_mfma(const uint16_t* __restrict__ 
         u32x4_t bf;
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-          const uint16_t* src = &Ws[ks * 32 + 8 * g4 + 4 * hh + k4][wc * 32 + ct * 16 + 4 * a4];
+          const uint16_t* src = &Ws[ks * 32 + 8 * g4 + 4 * hh + k4][wc * 16 * CT + ct * 16 + 4 * a4];
           const s16x4_t t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)src);
           const u32x2_t w2 = __builtin_bit_cast(u32x2_t, t);
           bf[2 * hh] = w2.x;
           bf[2 * hh + 1] = w2.y;
         }
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
+        for (int rt = 0; rt < RT; ++rt)
           acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, S.a[rt][ks]),
                                                                 __builtin_bit_cast(bf16x8_t, bf), acc[rt][ct], 0, 0, 0);
       }
     }
   };
-  BridgeStage R0, R1, R2, R3;
+  Stage R0, R1, R2, R3;
   load_stage(0, R0);
   load_stage(kKS, R1);
   load_stage(2 * kKS, R2);
@@ -128,13 +137,13 @@ __global__ void __launch_bounds__(256) bridge_mfma(const uint16_t* __restrict__ 
   // scatter: column c -> K or V cache, head c/D, element c%D; token t
   const int half = Hkv * D;
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
+  for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct)
+    for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int t = t0 + wr * 32 + rt * 16 + 4 * g4 + i;
-        const int c = c0 + wc * 32 + ct * 16 + r16;
+        const int t = t0 + wr * 16 * RT + rt * 16 + 4 * g4 + i;
+        const int c = c0 + wc * 16 * CT + ct * 16 + r16;
         if (t >= T) continue;
         const int cc = c < half ? c : c - half;
         const int hh = cc / D, d = cc - hh * D;
@@ -152,8 +161,14 @@ hipError_t launch_bridge(const uint16_t* hidden, int T, int dm, const uint16_t* 
   // the entry point admits D in {64, 128} and d_model % 64 == 0, so C and d_model
   // divide into whole tiles; tokens are clamped/guarded inside the kernel
   if (C % kBC != 0 || dm % kKS != 0) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(bridge_mfma, dim3(C / kBC, (T + kBT - 1) / kBT), dim3(256), 0, s, hidden, T, dm, w, Hkv, D,
-                     k_out, v_out, sn, sh);
+  // 64-token tiles where they still give every CU a workgroup, else 32
+  const int ctiles = C / kBC;
+  if (ctiles * ((T + 63) / 64) >= 256)
+    hipLaunchKernelGGL(bridge_mfma<64>, dim3(ctiles, (T + 63) / 64), dim3(256), 0, s, hidden, T, dm, w, Hkv, D, k_out,
+                       v_out, sn, sh);
+  else
+    hipLaunchKernelGGL(bridge_mfma<32>, dim3(ctiles, (T + 31) / 32), dim3(256), 0, s, hidden, T, dm, w, Hkv, D, k_out,
+                       v_out, sn, sh);
   return hipGetLastError();
 }
 

@@ -359,10 +359,11 @@ def test_strided_cache_view(hs2, full_mode):
     gu.assert_scores(gu.host(sc), s_or, G=spec.G)
 
 
-@pytest.mark.parametrize("T,dm,Hkv,D", [(77, 192, 3, 64), (130, 512, 2, 128), (1, 64, 1, 64)])
+@pytest.mark.parametrize("T,dm,Hkv,D", [(77, 192, 3, 64), (130, 512, 2, 128), (1, 64, 1, 64), (1090, 256, 4, 128)])
 def test_kv_bridge_parity(hs2, T, dm, Hkv, D):
     """K/V bridge into rows [pos0, pos0 + T) of batch 1 of a padded cache view:
-    ragged token count (partial 64-token tile), several column tiles; every
+    ragged token count (partial token tile; 32-token tiles, and 64-token tiles
+    once those fill the GPU: the last case), several column tiles; every
     element within one bf16 step of the fp64 projection, nothing else touched."""
     rng = np.random.default_rng(0x4252 + T)
     h = synth.to_bf16_bits(rng.standard_normal((T, dm)).astype(np.float32))
