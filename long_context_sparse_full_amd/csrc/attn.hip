@@ -2309,11 +2309,12 @@ __global__ void __launch_bounds__(256) combine(CombineParams P) {
   }
 }
 
-// The same merge for few splits (the chunk path: a handful per unit): one
-// workgroup per unit.  Rows' (M, L) and split weights go to LDS first, then
+// The same merge for many units with few splits each (the chunk path: a
+// handful of splits per unit): one workgroup per unit.  Rows' (M, L) and split weights go to LDS first, then
 // each thread forms whole outputs (row, head dim) from the splits' partials,
 // which a wave reads as contiguous runs of the head dimension.
 constexpr int kFewSplits = 32;
+constexpr int kFewSplitsMinUnits = 512;  // fewer units: the per-(row, slice) grid fills the GPU better
 __global__ void __launch_bounds__(256) combine_few(CombineParams P) {
   __shared__ float sw[16][kFewSplits];
   __shared__ float sM[16], sL[16];
@@ -2605,7 +2606,7 @@ hipError_t launch_chunk_score(const ScanParams& p, int kv_dtype, hipStream_t s) 
 
 hipError_t launch_combine(const CombineParams& p, int units, hipStream_t s) {
   TimedLaunch tl("combine", s);
-  if (p.nsplit <= kFewSplits)
+  if (p.nsplit <= kFewSplits && units >= kFewSplitsMinUnits)
     hipLaunchKernelGGL(combine_few, dim3(units), dim3(256), 0, s, p);
   else
     hipLaunchKernelGGL(combine, dim3(units, p.rows, p.D / 32), dim3(256), 0, s, p);
