@@ -249,6 +249,34 @@ def main():
                  "cold_sparse_layer1_gbps": round(gathered / (pct(l1_us, 0.5) * 1e-6) / 1e9, 1)}
     log(f"[bench] step distribution: {json.dumps(step_dist)}")
 
+    # the same step captured once in a HIP graph and replayed (the default
+    # kernel sequence has no memsets, allocations or host syncs; the
+    # cooperative kernel's per-launch epoch would be frozen by a capture)
+    graph = None
+    if args.full_mode == 0:
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()  # warm the side stream
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            step()
+        for _ in range(args.warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        ga, gb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ga.record()
+        for _ in range(args.steps):
+            g.replay()
+        gb.record()
+        torch.cuda.synchronize()
+        graph = {"us_per_step": round(ga.elapsed_time(gb) * 1e3 / args.steps, 2), "steps": args.steps}
+        log(f"[bench] hip graph replay: {graph['us_per_step']} us/step")
+        del g
+
     # per-kernel durations from HIP events bracketing each launch on its stream
     hs2.timing_reset()
     hs2.timing_enable(True)
@@ -321,6 +349,7 @@ def main():
         "algorithmic_bytes_per_step": ab["step"],
         "wall_us_per_step": round(wall_ms * 1e3, 2),
         "step_distribution": step_dist,
+        "hip_graph": graph,
         "kernels": kernels,
         "roofline": roofline,
         "gather_throughput": gather_tp,

@@ -468,6 +468,64 @@ def test_full_attn_topk(hs2, case, mode):
     gu.check_structure(idx, cnt, spec.q_pos0, k, window, N)
 
 
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_decode_step_in_hip_graph(hs2, kv):
+    """The default decode step (full layer and top-k in one call, then two
+    split-gather sparse layers) captured once in a HIP graph: three replays,
+    with the outputs overwritten and an eager step between them, each equal
+    the eager step bit for bit (the step records no memset, allocation or host
+    sync, and the split gather's counters return to zero)."""
+    gu.log(f"hip graph {kv}")
+    spec = small_spec(kv, B=2, N=30000, Hkv=2, k=256, window=32)
+    inp = synth.make_inputs(spec, seed=17)
+    blk = gu.DeviceBlock(inp)
+    B, Tq, Hq, D, Hkv, N = spec.B, spec.Tq, spec.Hq, spec.D, spec.Hkv, spec.N
+    out = torch.empty_like(blk.q)
+    lse = torch.empty((B, Tq, Hq), dtype=torch.float32, device="cuda")
+    sc = torch.empty((B, Tq, Hkv, N), dtype=torch.float32, device="cuda")
+    idx = torch.empty((B, Tq, Hkv, spec.max_sel), dtype=torch.int32, device="cuda")
+    cnt = torch.empty((B, Tq, Hkv), dtype=torch.int32, device="cuda")
+    ws = torch.empty(hs2.full_attn_topk_workspace(blk.k, blk.v, Tq, Hq), dtype=torch.uint8, device="cuda")
+    wsg = torch.zeros(max(hs2.sparse_attn_workspace(B, Tq, Hkv, D, spec.max_sel), 256), dtype=torch.uint8,
+                      device="cuda")
+    sp = [(torch.empty_like(blk.q), torch.empty((B, Tq, Hq), dtype=torch.float32, device="cuda")) for _ in blk.qs]
+    outs = [out, lse, sc, idx, cnt] + [t for pair in sp for t in pair]
+
+    def step():
+        hs2.full_attn_topk(blk.k, blk.v, blk.q, spec.q_pos0, spec.k, spec.window, max_sel=spec.max_sel,
+                           k_scale=blk.ks, v_scale=blk.vs, out=out, lse=lse, scores=sc, idx=idx, count=cnt,
+                           workspace=ws)
+        for ql, (o, l) in zip(blk.qs, sp):
+            hs2.sparse_attn_gather_ws(blk.k, blk.v, ql, idx, cnt, wsg, k_scale=blk.ks, v_scale=blk.vs, out=o, lse=l)
+
+    step()
+    torch.cuda.synchronize()
+    ref = [gu.host(t).copy() for t in outs]
+
+    def check(what):
+        torch.cuda.synchronize()
+        for t, r in zip(outs, ref):
+            got = gu.host(t)
+            assert np.array_equal(got, r, equal_nan=True), f"{what}: differs from the eager step"
+
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(3):
+        for t in outs:
+            t.fill_(-1)
+        g.replay()
+        check(f"replay {rep}")
+        step()
+        check(f"eager step after replay {rep}")
+
+
 def test_full_attn_topk_repeated_calls(hs2):
     """The cooperative kernel's grid barriers and histograms start clean on
     every launch: three calls on one workspace give identical results."""
