@@ -480,11 +480,36 @@ def bench_chunk(spec, args):
             us2 = kernels["chunk_score"]["avg_us"]
             roofline["score_pass"] = {"achieved": round(flops_score / (us2 * 1e-6) / 1e12, 1),
                                       "algorithmic_flops_per_launch": flops_score, "avg_launch_us": us2}
+    cpu = None
+    if not args.no_cpu_baseline:
+        # bounded sample: the chunk's last S query tokens (each sees the whole
+        # cache) through the same steps, and the bridge rows of S tokens
+        import oracle
+        S = 32
+        threads = len(os.sched_getaffinity(0))
+        os.environ.setdefault("OMP_NUM_THREADS", str(threads))
+        log(f"[bench] oracle on the last {S} query tokens ({threads} threads available)")
+        c0 = time.perf_counter()
+        oracle.kv_bridge(inp.hidden[-S:], inp.w_kv, Hkv, D)
+        qp = spec.q_pos0 + Tq - S
+        _, _, s_or = oracle.full_attn_scores(inp.q_full[:, -S:], inp.k, inp.v, qp)
+        idx_or, cnt_or = oracle.select_topk_window(s_or, qp, spec.k, spec.window, max_sel=spec.max_sel)
+        oracle.select_topk_window(s_or, qp, spec.block_k, spec.window, block_size=spec.block_size, max_sel=bsel)
+        for ql in inp.q_sparse:
+            oracle.sparse_attn(ql[:, -S:], inp.k, inp.v, idx_or, cnt_or)
+        c1 = time.perf_counter()
+        units = B * S * Hkv
+        cpu = {"value": round(S / (c1 - c0), 2), "unit": "tokens/s", "cores": min(units, oracle.num_threads()),
+               "kind": "oracle",
+               "sample": f"the last {S} of the {Tq} query tokens of {spec.name} (each sees the whole cache): "
+                         f"bridge rows, full layer, token and block selection, 3 sparse layers, fp64; "
+                         f"{c1 - c0:.2f}s", "threads_available": threads, "cpu_model": cpu_model()}
+        log(f"[bench] oracle: {c1 - c0:.2f}s for {S} tokens")
     print(json.dumps({"metric": "tokens/s per 512-query chunk (bridge + full + token & block select + 3 sparse)",
                       "value": round(Tq / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": steps,
                       "ms_per_step": round(ms, 4), "higher_is_better": True, "dtype": "bf16/f32-acc",
                       "data": "synthetic", "config": {"workload": spec.name, "Tq": Tq, "context": N},
-                      "kernels": kernels, "roofline": roofline}), flush=True)
+                      "kernels": kernels, "roofline": roofline, "cpu_baseline": cpu}), flush=True)
 
 
 if __name__ == "__main__":
