@@ -464,6 +464,22 @@ def bench_chunk(spec, args):
             kernels[name] = {"avg_us": round(tot * 1e3 / n, 3), "launches_per_step": n / steps}
     hs2.timing_enable(False)
     hs2.timing_reset()
+    # the same bridge into an E4M3FN cache of the same shape (per-head scales)
+    k8 = torch.zeros(k.shape, dtype=torch.uint8, device="cuda")
+    v8 = torch.zeros_like(k8)
+    sc8 = torch.full((B, Hkv), 1.0 / 112.0, dtype=torch.float32, device="cuda")
+    for _ in range(2):
+        hs2.kv_bridge(hidden, w, k8, v8, 0, N - T, k_scale=sc8, v_scale=sc8)
+    torch.cuda.synchronize()
+    hs2.timing_enable(True)
+    for _ in range(steps):
+        hs2.kv_bridge(hidden, w, k8, v8, 0, N - T, k_scale=sc8, v_scale=sc8)
+    torch.cuda.synchronize()
+    tot, n = hs2.timing_collect("kv_bridge")
+    hs2.timing_enable(False)
+    hs2.timing_reset()
+    bridge_fp8_us = round(tot * 1e3 / max(n, 1), 3)
+    del k8, v8
     # dense MFMA work of the chunk's full layer: query token t sees p_t + 1 positions;
     # QK^T and PV are 2 * Hq * D flops per (t, position) each; the score pass redoes QK^T
     visible = sum(spec.q_pos0 + t + 1 for t in range(Tq))
@@ -509,7 +525,8 @@ def bench_chunk(spec, args):
                       "value": round(Tq / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": steps,
                       "ms_per_step": round(ms, 4), "higher_is_better": True, "dtype": "bf16/f32-acc",
                       "data": "synthetic", "config": {"workload": spec.name, "Tq": Tq, "context": N},
-                      "kernels": kernels, "roofline": roofline, "cpu_baseline": cpu}), flush=True)
+                      "kernels": kernels, "kv_bridge_into_fp8_cache_us": bridge_fp8_us, "roofline": roofline,
+                      "cpu_baseline": cpu}), flush=True)
 
 
 if __name__ == "__main__":

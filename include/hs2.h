@@ -169,9 +169,14 @@ int hs2_sparse_attn_gather_ws(const hs2_kv_desc* kv, const void* q, hs2_dtype q_
  * computes its K and V from a self-decoder layer's hidden state, with its own
  * parameters).  y = hidden [T, d_model] (bf16) x w_kv [d_model, 2*Hkv*D]
  * (bf16), fp32 accumulation; columns [0, Hkv*D) are K heads 0..Hkv-1 and
- * [Hkv*D, 2*Hkv*D) are V heads, head-major.  The rounded (bf16, RNE) rows are
- * written into kv_out (a BF16 cache) at batch batch_index, positions
- * [pos0, pos0 + T).  Requires d_model % 64 == 0. */
+ * [Hkv*D, 2*Hkv*D) are V heads, head-major.  The rows are written into
+ * kv_out at batch batch_index, positions [pos0, pos0 + T): a BF16 cache
+ * receives y rounded to bf16 (RNE); an FP8_E4M3FN cache (the pages' FP8 KV
+ * cache -- zgeo.com.cn comparison table) receives the E4M3FN code of
+ * y / scale, scale = kv_out's k_scale or v_scale entry of (batch_index, head)
+ * (read, not changed: the caller keeps each head's scale, which must be
+ * positive), rounded to nearest even with magnitudes above 448 saturating to
+ * 448.  Requires d_model % 64 == 0. */
 int hs2_kv_bridge(const void* hidden, int32_t T, int32_t d_model, const void* w_kv,
                   const hs2_kv_desc* kv_out, int32_t batch_index, int32_t pos0, hipStream_t stream);
 

@@ -689,7 +689,8 @@ int hs2_kv_bridge(const void* hidden, int32_t T, int32_t d_model, const void* w_
                   int32_t batch_index, int32_t pos0, hipStream_t stream) {
   int st = check_kv(kv_out, "hs2_kv_bridge");
   if (st) return st;
-  if (kv_out->dtype != HS2_BF16) return fail(HS2_ERR_UNSUPPORTED, "hs2_kv_bridge: output cache must be BF16");
+  if (kv_out->dtype != HS2_BF16 && kv_out->dtype != HS2_FP8_E4M3FN)
+    return fail(HS2_ERR_UNSUPPORTED, "hs2_kv_bridge: output cache must be BF16 or FP8_E4M3FN");
   if (!hidden || !w_kv) return fail(HS2_ERR_INVALID_ARG, "hs2_kv_bridge: NULL hidden or w_kv");
   if (T <= 0 || d_model <= 0) return fail(HS2_ERR_INVALID_ARG, "hs2_kv_bridge: T and d_model must be positive");
   if (d_model % 64) return fail(HS2_ERR_UNSUPPORTED, "hs2_kv_bridge: d_model must be a multiple of 64");
@@ -699,11 +700,17 @@ int hs2_kv_bridge(const void* hidden, int32_t T, int32_t d_model, const void* w_
     return fail(HS2_ERR_INVALID_ARG, "hs2_kv_bridge: need 0 <= pos0 and pos0 + T <= N");
   if (!al16(hidden) || !al16(w_kv)) return fail(HS2_ERR_INVALID_ARG, "hs2_kv_bridge: hidden/w_kv must be 16-byte aligned");
   const int64_t off = (int64_t)batch_index * kv_out->stride_b + (int64_t)pos0 * kv_out->stride_n;
-  uint16_t* kb = const_cast<uint16_t*>(static_cast<const uint16_t*>(kv_out->k)) + off;
-  uint16_t* vb = const_cast<uint16_t*>(static_cast<const uint16_t*>(kv_out->v)) + off;
+  const bool fp8 = kv_out->dtype == HS2_FP8_E4M3FN;
+  const size_t esz = fp8 ? 1 : 2;
+  hs2::BridgeOut o{};
+  o.k = static_cast<char*>(const_cast<void*>(kv_out->k)) + off * esz;
+  o.v = static_cast<char*>(const_cast<void*>(kv_out->v)) + off * esz;
+  o.sn = kv_out->stride_n;
+  o.sh = kv_out->stride_h;
+  o.k_scale = fp8 ? kv_out->k_scale + (int64_t)batch_index * kv_out->Hkv : nullptr;
+  o.v_scale = fp8 ? kv_out->v_scale + (int64_t)batch_index * kv_out->Hkv : nullptr;
   const hipError_t e = hs2::launch_bridge(static_cast<const uint16_t*>(hidden), T, d_model,
-                                          static_cast<const uint16_t*>(w_kv), kv_out->Hkv, kv_out->D, kb, vb,
-                                          kv_out->stride_n, kv_out->stride_h, stream);
+                                          static_cast<const uint16_t*>(w_kv), kv_out->Hkv, kv_out->D, o, stream);
   if (e != hipSuccess) return hip_fail(e, "kv_bridge launch");
   return HS2_OK;
 }

@@ -4,9 +4,11 @@
 // siami.tw "xiaomi-mimo-v3-hysparse-2", section one).
 //
 // y[t, c] = sum_r hidden[t, r] * w[r, c], bf16 inputs, fp32 accumulation,
-// rounded to bf16 (RNE) and scattered into the cache: columns [0, Hkv*D) are
-// K heads, [Hkv*D, 2*Hkv*D) are V heads.  A dense contraction, so it runs on
-// bf16 MFMA (16x16x32) tiles.
+// scattered into the cache: columns [0, Hkv*D) are K heads, [Hkv*D, 2*Hkv*D)
+// are V heads.  A bf16 cache receives y rounded to bf16 (RNE); an FP8 cache
+// the OCP E4M3FN code of y / scale of its head, rounded to nearest even and
+// saturated at +-448.  A dense contraction, so it runs on bf16 MFMA
+// (16x16x32) tiles.
 #include "hs2_internal.hpp"
 
 
@@ -32,16 +34,32 @@ typedef short s16x4_t __attribute__((ext_vector_type(4)));
 // latency per stage.
 constexpr int kBC = 64, kKS = 64, kWPad = 8, kRing = 4;
 
+// E4M3FN code of x, round to nearest even, magnitudes above 448 saturating
+// to 448 (x finite): subnormal codes are multiples of 2^-9 below 2^-6, normal
+// codes (exponent e + 7, 3 mantissa bits) above; a mantissa that rounds up to
+// 8 carries into the exponent field.
+__device__ __forceinline__ uint8_t e4m3fn_rne_sat(float x) {
+  const uint32_t sign = x < 0.f ? 0x80u : 0u;
+  const float a = fminf(fabsf(x), 448.f);
+  uint32_t code;
+  if (a < 0.015625f) {
+    code = (uint32_t)rintf(a * 512.f);
+  } else {
+    const int e = ilogbf(a);
+    code = (uint32_t)((e + 7) * 8) + (uint32_t)rintf((ldexpf(a, -e) - 1.f) * 8.f);
+  }
+  return (uint8_t)(sign | code);
+}
+
 template <int RT>
 struct BridgeStage {
   u32x4_t w[2];
   u32x4_t a[RT][2];
 };
 
-template <int BT>
+template <int BT, bool FP8OUT>
 __global__ void __launch_bounds__(256) bridge_mfma(const uint16_t* __restrict__ H, int T, int dm,
-                                                   const uint16_t* __restrict__ W, int Hkv, int D, uint16_t* kout,
-                                                   uint16_t* vout, int64_t sn, int64_t sh) {
+                                                   const uint16_t* __restrict__ W, int Hkv, int D, BridgeOut O) {
   static_assert(BT == 32 || BT == 64, "token tile");
   constexpr int RT = BT / 32, CT = 2;
   using Stage = BridgeStage<RT>;
@@ -147,15 +165,20 @@ __global__ void __launch_bounds__(256) bridge_mfma(const uint16_t* __restrict__ 
         if (t >= T) continue;
         const int cc = c < half ? c : c - half;
         const int hh = cc / D, d = cc - hh * D;
-        uint16_t* dst = (c < half ? kout : vout) + (int64_t)hh * sh + (int64_t)t * sn + d;
-        *dst = __builtin_bit_cast(uint16_t, (__bf16)acc[rt][ct][i]);
+        const int64_t e = (int64_t)hh * O.sh + (int64_t)t * O.sn + d;
+        if constexpr (FP8OUT) {
+          const float sc = (c < half ? O.k_scale : O.v_scale)[hh];
+          ((uint8_t*)(c < half ? O.k : O.v))[e] = e4m3fn_rne_sat(acc[rt][ct][i] / sc);
+        } else {
+          ((uint16_t*)(c < half ? O.k : O.v))[e] = __builtin_bit_cast(uint16_t, (__bf16)acc[rt][ct][i]);
+        }
       }
 }
 
 }  // namespace
 
 hipError_t launch_bridge(const uint16_t* hidden, int T, int dm, const uint16_t* w, int Hkv, int D,
-                         uint16_t* k_out, uint16_t* v_out, int64_t sn, int64_t sh, hipStream_t s) {
+                         const BridgeOut& out, hipStream_t s) {
   TimedLaunch tl("kv_bridge", s);
   const int C = 2 * Hkv * D;
   // the entry point admits D in {64, 128} and d_model % 64 == 0, so C and d_model
@@ -163,12 +186,20 @@ hipError_t launch_bridge(const uint16_t* hidden, int T, int dm, const uint16_t* 
   if (C % kBC != 0 || dm % kKS != 0) return hipErrorInvalidValue;
   // 64-token tiles where they still give every CU a workgroup, else 32
   const int ctiles = C / kBC;
+  const bool fp8 = out.k_scale != nullptr;
+#define HS2_BRIDGE(BT)                                                                                         \
+  do {                                                                                                       \
+    const dim3 grid(ctiles, (T + BT - 1) / BT);                                                              \
+    if (fp8)                                                                                                 \
+      hipLaunchKernelGGL((bridge_mfma<BT, true>), grid, dim3(256), 0, s, hidden, T, dm, w, Hkv, D, out);     \
+    else                                                                                                     \
+      hipLaunchKernelGGL((bridge_mfma<BT, false>), grid, dim3(256), 0, s, hidden, T, dm, w, Hkv, D, out);    \
+  } while (0)
   if (ctiles * ((T + 63) / 64) >= 256)
-    hipLaunchKernelGGL(bridge_mfma<64>, dim3(ctiles, (T + 63) / 64), dim3(256), 0, s, hidden, T, dm, w, Hkv, D, k_out,
-                       v_out, sn, sh);
+    HS2_BRIDGE(64);
   else
-    hipLaunchKernelGGL(bridge_mfma<32>, dim3(ctiles, (T + 31) / 32), dim3(256), 0, s, hidden, T, dm, w, Hkv, D, k_out,
-                       v_out, sn, sh);
+    HS2_BRIDGE(32);
+#undef HS2_BRIDGE
   return hipGetLastError();
 }
 

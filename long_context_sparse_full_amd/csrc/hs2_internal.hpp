@@ -158,8 +158,18 @@ hipError_t launch_chunk_score(const ScanParams& p, int kv_dtype, hipStream_t s);
 hipError_t launch_combine(const CombineParams& p, int units, hipStream_t s);
 hipError_t launch_score(const ScoreParams& p, int units, hipStream_t s);
 hipError_t launch_select(const SelectParams& p, hipStream_t s);
+// K/V bridge output: the cache rows of one batch entry from the first new
+// position on (element (h, t, d) at h*sh + t*sn + d); FP8 caches pass that
+// batch entry's per-head scales (Hkv each), bf16 caches nullptr.
+struct BridgeOut {
+  void* k;
+  void* v;
+  int64_t sn, sh;
+  const float* k_scale;
+  const float* v_scale;
+};
 hipError_t launch_bridge(const uint16_t* hidden, int T, int dm, const uint16_t* w, int Hkv, int D,
-                         uint16_t* k_out, uint16_t* v_out, int64_t sn, int64_t sh, hipStream_t s);
+                         const BridgeOut& out, hipStream_t s);
 hipError_t launch_debug_e4m3fn(const uint8_t* codes, float* out, int n, hipStream_t s);
 hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* out, int blocks, hipStream_t s);
 

@@ -261,9 +261,10 @@ def sparse_attn_gather_ws(k, v, q, idx, count, workspace, softmax_scale: float |
     return out, lse
 
 
-def kv_bridge(hidden, w_kv, k_cache, v_cache, batch_index: int, pos0: int):
-    """Project bf16 hidden states [T, d_model] with w_kv [d_model, 2*Hkv*D] into the bf16 cache rows."""
-    d = kv_desc(k_cache, v_cache)
+def kv_bridge(hidden, w_kv, k_cache, v_cache, batch_index: int, pos0: int, k_scale=None, v_scale=None):
+    """Project bf16 hidden states [T, d_model] with w_kv [d_model, 2*Hkv*D] into the cache rows
+    (bf16 cache, or E4M3FN cache with its per-(b, head) scales)."""
+    d = kv_desc(k_cache, v_cache, k_scale, v_scale)
     T, dm = hidden.shape
     st = _bridge(hidden.data_ptr(), T, dm, w_kv.data_ptr(), ctypes.byref(d), int(batch_index), int(pos0), _stream())
     _check(st, "hs2_kv_bridge")

@@ -138,6 +138,24 @@ def e4m3fn_table(mutant: int = 0) -> np.ndarray:
     return np.array([e4m3fn_decode(c, mutant) for c in range(256)], dtype=np.float64)
 
 
+def e4m3fn_encode(x) -> np.ndarray:
+    """OCP E4M3FN code of each real x: the nearest finite value of the format
+    (magnitudes above the largest, 448, saturate to it), ties to the code with
+    an even mantissa, the sign from x < 0.  A nearest-value search over the
+    format's positive codes 0x00..0x7E decoded by e4m3fn_decode (the definition
+    of the values; 0x7F is NaN); storing an FP8 KV cache (zgeo.com.cn
+    comparison table) needs this encoder."""
+    vals = e4m3fn_table()[:0x7F]  # increasing with the code
+    x = np.asarray(x, dtype=np.float64)
+    a = np.minimum(np.abs(x), vals[-1])
+    hi = np.clip(np.searchsorted(vals, a, side="left"), 0, len(vals) - 1)  # first value >= a
+    lo = np.maximum(hi - 1, 0)
+    d_hi, d_lo = vals[hi] - a, a - vals[lo]
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo).astype(np.uint8)
+    return np.where(x < 0, code | np.uint8(0x80), code).astype(np.uint8)
+
+
 def bf16_decode(bits: np.ndarray) -> np.ndarray:
     lib = load()
     flat = np.asarray(bits, dtype=np.uint16).ravel()

@@ -49,6 +49,27 @@ def pin_e4m3fn_table(mutant=0):
     assert np.array_equal(np.signbit(ours[~nan_o]), np.signbit(theirs[~nan_t])), "signed zero differs"
 
 
+def pin_e4m3fn_encode(mutant=0):
+    """Encoder: every finite code round-trips; random values and every midpoint
+    between neighbouring codes (ties) against torch's round-to-nearest-even
+    cast to float8_e4m3fn; magnitudes above 448 saturate by the definition."""
+    import torch
+    table = oracle.e4m3fn_table()
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF, 0x80)], dtype=np.uint8)
+    assert np.array_equal(oracle.e4m3fn_encode(table[codes]), codes), "finite codes do not round-trip"
+    pos = np.sort(table[:0x7F])
+    mids = (pos[:-1] + pos[1:]) / 2
+    rng = np.random.default_rng(8)
+    x = np.concatenate([mids, -mids, rng.uniform(-448, 448, 20000), rng.standard_normal(20000) * 0.01])
+    x = x.astype(np.float32)  # every value here is exact in fp32
+    theirs = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    ours = oracle.e4m3fn_encode(x.astype(np.float64))
+    zero = x == 0  # torch keeps the sign of -0; the encoder defines x < 0 only
+    assert np.array_equal(ours[~zero], theirs[~zero]), "rounding differs from round-to-nearest-even"
+    big = np.array([448.0, 448.5, 464.0, 1e6, np.inf, -449.0, -1e30])
+    assert np.array_equal(oracle.e4m3fn_encode(big), np.array([0x7E] * 5 + [0xFE] * 2, np.uint8)), "saturation"
+
+
 def pin_bf16_decode(mutant=0):
     """Every 64th bf16 pattern against torch's bf16 -> float32 cast."""
     bits = np.arange(0, 65536, 64, dtype=np.uint32).astype(np.uint16)
@@ -328,7 +349,7 @@ def pin_bridge_vs_matmul(mutant=0):
 
 
 ALL_PINS = [
-    pin_e4m3fn_table, pin_bf16_decode, pin_full_vs_sdpa, pin_scores_vs_sdpa_probs,
+    pin_e4m3fn_table, pin_e4m3fn_encode, pin_bf16_decode, pin_full_vs_sdpa, pin_scores_vs_sdpa_probs,
     pin_score_mass_is_group_size, pin_zero_query, pin_single_position, pin_key_shift_invariance,
     pin_position_permutation, pin_select_bruteforce, pin_select_structure, pin_select_pages_budget,
     pin_window_competes_alternative, pin_sparse_equals_full_when_k_covers,

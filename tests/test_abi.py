@@ -188,8 +188,10 @@ def test_sparse_and_bridge_validation(hs2):
     assert hs2._sparse(ctypes.byref(d), FAKE, 1, 1, 16, 0.1, FAKE, FAKE, 0, FAKE, None, None) == -1
     assert hs2._sparse(ctypes.byref(d), FAKE, 0, 1, 16, 0.1, FAKE, FAKE, 8, FAKE, None, None) == -2
     assert hs2._sparse(ctypes.byref(d), FAKE, 1, 1, 16, float("nan"), FAKE, FAKE, 8, FAKE, None, None) == -1
-    d8 = desc(hs2, dtype=2, scales=True)
-    assert hs2._bridge(FAKE, 4, 4096, FAKE, ctypes.byref(d8), 0, 0, None) == -2  # cache must be bf16
+    d32 = desc(hs2, dtype=0)
+    assert hs2._bridge(FAKE, 4, 4096, FAKE, ctypes.byref(d32), 0, 0, None) == -2  # cache bf16 or FP8
+    d8n = desc(hs2, dtype=2, scales=False)
+    assert hs2._bridge(FAKE, 4, 4096, FAKE, ctypes.byref(d8n), 0, 0, None) == -2  # FP8 cache needs scales
     assert hs2._bridge(FAKE, 4, 4000, FAKE, ctypes.byref(d), 0, 0, None) == -2   # d_model % 64
     assert hs2._bridge(FAKE, 4, 4096, FAKE, ctypes.byref(d), 1, 0, None) == -1   # batch index
     assert hs2._bridge(FAKE, 4, 4096, FAKE, ctypes.byref(d), 0, 253, None) == -1  # pos0 + T > N

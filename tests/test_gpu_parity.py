@@ -387,6 +387,54 @@ def test_kv_bridge_parity(hs2, T, dm, Hkv, D):
         assert np.all(got_all[mask] == fill), f"bridge {name} wrote outside its rows"
 
 
+@pytest.mark.parametrize("T,dm,Hkv,D", [(77, 192, 3, 64), (130, 512, 2, 128), (1090, 256, 4, 128)])
+def test_kv_bridge_fp8_cache(hs2, T, dm, Hkv, D):
+    """K/V bridge into an E4M3FN cache view: codes of y / scale against the
+    oracle's encoder on the fp64 projection; a code may differ only by one
+    step and only where y / scale lies at the midpoint of the two codes up to
+    fp32 accumulation; one head per cache has a scale small enough that large
+    values saturate to +-448; nothing outside the rows is touched."""
+    rng = np.random.default_rng(0x4253 + T)
+    h = synth.to_bf16_bits(rng.standard_normal((T, dm)).astype(np.float32))
+    w = synth.to_bf16_bits((rng.standard_normal((dm, 2 * Hkv * D)) / math.sqrt(dm)).astype(np.float32))
+    N, pos0, B = T + 40, 23, 2
+    ks = np.full((B, Hkv), 1.0 / 112.0, np.float32)  # |y| up to ~4 maps to ~448
+    vs = np.full((B, Hkv), 1.0 / 96.0, np.float32)
+    ks[1, 0] = 1.0 / 2048.0  # saturating head
+    big_k = torch.full((B, Hkv + 1, N + 9, D + 16), 0x3C, dtype=torch.uint8, device="cuda")
+    big_v = torch.full_like(big_k, 0xC3)
+    k, v = big_k[:, :Hkv, :N, :D], big_v[:, :Hkv, :N, :D]
+    hs2.kv_bridge(gu.dev(h), gu.dev(w), k, v, 1, pos0, k_scale=gu.dev(ks), v_scale=gu.dev(vs))
+    torch.cuda.synchronize()
+    Kr, Vr = oracle.kv_bridge(h, w, Hkv, D)
+    # fp32 accumulation error bound per output: d_model * 2^-23 * sum_r |h w|
+    habs = np.abs(oracle.bf16_decode(h))
+    wabs = np.abs(oracle.bf16_decode(w))
+    err = dm * 2.0 ** -23 * (habs @ wabs)  # [T, 2*Hkv*D]
+    table = oracle.e4m3fn_table()
+    saturated = 0
+    for part, (name, big, ref, sc, fill) in enumerate((("K", big_k, Kr, ks, 0x3C), ("V", big_v, Vr, vs, 0xC3))):
+        got_all = big.cpu().numpy()
+        got = got_all[1, :Hkv, pos0:pos0 + T, :D]
+        s1 = sc[1].astype(np.float64)[:, None, None]
+        y = np.transpose(ref, (1, 0, 2)) / s1
+        bound = np.transpose(err[:, part * Hkv * D:(part + 1) * Hkv * D].reshape(T, Hkv, D), (1, 0, 2)) / s1
+        want = oracle.e4m3fn_encode(y)
+        diff = got != want
+        if diff.any():
+            vg, vw = table[got[diff]], table[want[diff]]
+            mid = (vg + vw) / 2
+            codes_apart = np.abs(got[diff].astype(int) - want[diff].astype(int))
+            assert np.all(codes_apart == 1), f"bridge {name}: codes more than one step apart"
+            assert np.all(np.abs(y[diff] - mid) <= bound[diff] + 1e-7 * np.abs(mid)), \
+                f"bridge {name}: a code differs farther from the rounding midpoint than fp32 accumulation explains"
+        saturated += int(np.sum((got & 0x7F) == 0x7E))
+        mask = np.ones(got_all.shape, bool)
+        mask[1, :Hkv, pos0:pos0 + T, :D] = False
+        assert np.all(got_all[mask] == fill), f"bridge {name} wrote outside its rows"
+    assert saturated > 0, "the saturating head produced no +-448 codes"
+
+
 @pytest.mark.parametrize("kv", ["bf16", "fp8"])
 def test_fused_and_kernel_paths_agree(hs2, kv):
     """The cooperative kernel and the three-kernel sequence compute the same
