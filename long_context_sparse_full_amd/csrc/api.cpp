@@ -269,6 +269,9 @@ struct SelFuse {
   int32_t* count;
   void* ws;  // fused-selection region: histograms, then step counts
   bool done = false;
+  // kernel sequence: the merge set the selection up and the score pass built
+  // its first histogram (layout of plan_select over ws)
+  bool hist0_done = false;
 };
 
 size_t sel_fuse_hist_bytes(int units) { return a256((size_t)units * 3 * hs2::kHistBins * sizeof(int32_t)); }
@@ -280,6 +283,11 @@ size_t sel_fuse_bytes(int units, int N) {
 int full_layer(const hs2_kv_desc* kv, const void* q, hs2_dtype q_dtype, int32_t Tq, int32_t Hq, int32_t q_pos0,
                float softmax_scale, void* out, float* lse, float* scores, void* workspace, size_t workspace_bytes,
                hipStream_t stream, SelFuse* sel);
+// hs2_select_topk_window; pre_hist0: the row state and first histogram are
+// already built (full layer's merge and score pass)
+int select_impl(const float* scores, int32_t B, int32_t Tq, int32_t Hkv, int32_t N, int32_t q_pos0, int32_t k,
+                int32_t window, int32_t block_size, int32_t* idx, int32_t* count, int32_t max_sel, void* workspace,
+                size_t workspace_bytes, hipStream_t stream, bool pre_hist0);
 }  // namespace
 
 extern "C" {
@@ -433,6 +441,18 @@ int full_layer(const hs2_kv_desc* kv, const void* q, hs2_dtype q_dtype, int32_t 
   c.out = out;
   c.lse = lse;
   c.lse2 = at<float>(workspace, pl.off_lse2);
+  // one query token per unit: the merge sets the selection's rows up and the
+  // score pass counts their first digit, which saves the selection two passes
+  const bool pre_sel = sel != nullptr && pl.tpack == 1;
+  int32_t* sel_hist = nullptr;
+  if (pre_sel) {
+    const SelPlan sp = plan_select(kv->B, Tq, kv->Hkv, kv->N, 1);
+    c.sel_state = at<int32_t>(sel->ws, sp.off_state);
+    c.sel_hist = sel_hist = at<int32_t>(sel->ws, sp.off_hist);
+    c.sel_k = sel->k;
+    c.sel_window = sel->window;
+    c.q_pos0 = q_pos0;
+  }
   if ((e = hs2::launch_combine(c, pl.units, stream)) != hipSuccess) return hip_fail(e, "combine launch");
 
   hs2::ScoreParams s{};
@@ -449,7 +469,11 @@ int full_layer(const hs2_kv_desc* kv, const void* q, hs2_dtype q_dtype, int32_t 
   s.N = kv->N;
   s.q_pos0 = q_pos0;
   s.scores = scores;
+  s.sel_hist = sel_hist;
+  s.sel_k = pre_sel ? sel->k : 0;
+  s.sel_window = pre_sel ? sel->window : 0;
   if ((e = hs2::launch_score(s, pl.units, stream)) != hipSuccess) return hip_fail(e, "score launch");
+  if (pre_sel) sel->hist0_done = true;
   return HS2_OK;
 }
 }  // namespace
@@ -487,8 +511,8 @@ int hs2_full_attn_topk(const hs2_kv_desc* kv, const void* q, hs2_dtype q_dtype, 
   st = full_layer(kv, q, q_dtype, Tq, Hq, q_pos0, softmax_scale, out, lse, scores, workspace, full_bytes, stream,
                   &sel);
   if (st || sel.done) return st;
-  return hs2_select_topk_window(scores, kv->B, Tq, kv->Hkv, kv->N, q_pos0, k, window, 1, idx, count, max_sel, rest,
-                                workspace_bytes - full_bytes, stream);
+  return select_impl(scores, kv->B, Tq, kv->Hkv, kv->N, q_pos0, k, window, 1, idx, count, max_sel, rest,
+                     workspace_bytes - full_bytes, stream, sel.hist0_done);
 }
 
 size_t hs2_select_workspace(int32_t B, int32_t Tq, int32_t Hkv, int32_t N) {
@@ -504,6 +528,16 @@ size_t hs2_select_workspace_for(int32_t B, int32_t Tq, int32_t Hkv, int32_t N, i
 int hs2_select_topk_window(const float* scores, int32_t B, int32_t Tq, int32_t Hkv, int32_t N, int32_t q_pos0,
                            int32_t k, int32_t window, int32_t block_size, int32_t* idx, int32_t* count,
                            int32_t max_sel, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return select_impl(scores, B, Tq, Hkv, N, q_pos0, k, window, block_size, idx, count, max_sel, workspace,
+                     workspace_bytes, stream, false);
+}
+
+}  // extern "C"
+
+namespace {
+int select_impl(const float* scores, int32_t B, int32_t Tq, int32_t Hkv, int32_t N, int32_t q_pos0, int32_t k,
+                int32_t window, int32_t block_size, int32_t* idx, int32_t* count, int32_t max_sel, void* workspace,
+                size_t workspace_bytes, hipStream_t stream, bool pre_hist0) {
   if (!scores || !idx || !count) return fail(HS2_ERR_INVALID_ARG, "hs2_select_topk_window: NULL scores/idx/count");
   if (B <= 0 || Tq <= 0 || Hkv <= 0 || N <= 0)
     return fail(HS2_ERR_INVALID_ARG, "hs2_select_topk_window: B, Tq, Hkv, N must be positive");
@@ -542,10 +576,14 @@ int hs2_select_topk_window(const float* scores, int32_t B, int32_t Tq, int32_t H
   p.cand = block_size == 1 ? at<int32_t>(workspace, pl.off_cand) : nullptr;
   p.bmass = block_size > 1 ? at<double>(workspace, pl.off_bmass) : nullptr;
   p.nblocks_max = pl.nblocks_max;
+  p.pre_hist0 = pre_hist0 ? 1 : 0;
   const hipError_t e = hs2::launch_select(p, stream);
   if (e != hipSuccess) return hip_fail(e, "select launch");
   return HS2_OK;
 }
+}  // namespace
+
+extern "C" {
 
 int hs2_sparse_attn_gather(const hs2_kv_desc* kv, const void* q, hs2_dtype q_dtype, int32_t Tq, int32_t Hq,
                            float softmax_scale, const int32_t* idx, const int32_t* count, int32_t max_sel, void* out,
@@ -643,10 +681,10 @@ int hs2_sparse_attn_gather_ws(const hs2_kv_desc* kv, const void* q, hs2_dtype q_
     return fail(HS2_ERR_WORKSPACE, "hs2_sparse_attn_gather_ws: workspace needs " + std::to_string(gp.total) + " bytes");
   // The split form pays off only while one workgroup per (b, t, g) leaves the
   // GPU mostly idle; from 64 units on, the one-workgroup kernel is used (it
-  // needs no workspace).  Also the merging workgroup keeps one weight per
-  // (slice, row) in its 4-wave merge buffer (4 * 16 * (D + 1) floats), so
-  // longer lists take the one-workgroup kernel too.
-  if (units >= kSplitGatherMaxUnits || (int64_t)gp.nsplit * 16 > 4 * 16 * (kv->D + 1))
+  // needs no workspace).  Also the merging workgroup keeps a maximum (then
+  // weight) and a sum per (slice, row) in its 4-wave merge buffer
+  // (4 * 16 * (D + 1) floats), so longer lists take the one-workgroup kernel too.
+  if (units >= kSplitGatherMaxUnits || (int64_t)2 * gp.nsplit * 16 > 4 * 16 * (kv->D + 1))
     return hs2_sparse_attn_gather(kv, q, q_dtype, Tq, Hq, softmax_scale, idx, count, max_sel, out, lse, stream);
   if ((uintptr_t)workspace & 255)
     return fail(HS2_ERR_INVALID_ARG, "hs2_sparse_attn_gather_ws: workspace must be 256-byte aligned");

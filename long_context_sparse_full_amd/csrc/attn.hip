@@ -22,6 +22,7 @@
 #include <type_traits>
 
 #include "hs2_internal.hpp"
+#include "select_common.hpp"
 
 namespace hs2 {
 namespace {
@@ -46,6 +47,9 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 #endif
 #ifndef HS2_FUSED_SWIZZLE
 #define HS2_FUSED_SWIZZLE 0  // fused full layer: workgroup -> (unit, split) unit-fastest
+#endif
+#ifndef HS2_SCORE_HIST_R
+#define HS2_SCORE_HIST_R 4  // 4-position groups per thread of the score pass with the selection's first histogram
 #endif
 #ifndef HS2_SCAN_MIN_WAVES
 #define HS2_SCAN_MIN_WAVES 1  // occupancy floor handed to the register allocator
@@ -1972,8 +1976,13 @@ __global__ void __launch_bounds__(WAVES * 64) scan_gather_split(ScanParams P) {
   const bool row_ok = r < P.G;
   const int h = g * P.G + r;
   const int32_t* list = P.idx + (int64_t)unit * P.max_sel;
-  const int n = min(max(P.count[unit], 0), P.max_sel);
   const int lo = split * P.split_len;  // gslice
+  // The slice's first WAVES*64 list slots are read together with the count and
+  // the query (one memory round trip instead of two); slots past the count lie
+  // inside the list buffer and are never used.
+  const int nspec = min(P.split_len, P.max_sel - lo);
+  const int e0 = (int)threadIdx.x < nspec ? list[lo + threadIdx.x] : 0;
+  const int n = min(max(P.count[unit], 0), P.max_sel);
   const int hi = min(lo + P.split_len, n);
 
   u32x4_t qf[NC];
@@ -1992,7 +2001,8 @@ __global__ void __launch_bounds__(WAVES * 64) scan_gather_split(ScanParams P) {
   for (int dt = 0; dt < VE; ++dt) S.o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   const int nb = max(0, hi - lo);  // <= gslice <= kGatherIdxCap
-  for (int i = threadIdx.x; i < nb; i += WAVES * 64) s_idx[i] = min(max(list[lo + i], 0), P.N - 1);
+  if ((int)threadIdx.x < nb) s_idx[threadIdx.x] = min(max(e0, 0), P.N - 1);
+  for (int i = threadIdx.x + WAVES * 64; i < nb; i += WAVES * 64) s_idx[i] = min(max(list[lo + i], 0), P.N - 1);
   __syncthreads();
   if (nb > 0) {
     const int jl = lo + nb - 1;
@@ -2033,13 +2043,19 @@ __global__ void __launch_bounds__(WAVES * 64) scan_gather_split(ScanParams P) {
   }
   __syncthreads();
   if (!s_last) return;
-  // the last slice merges all partials (device-coherent loads): weights first,
-  // then every output element with its loads issued together
-  float* sw = &sm_o[0][0][0];  // [nsplit][16] weights 2^(m_s - M), reusing the merge buffer
+  // the last slice merges all partials (device-coherent loads): every slice's
+  // (max, sum) in one round of loads, the weights from LDS, then every output
+  // element with its loads issued together
+  float* sw = &sm_o[0][0][0];  // [nsplit][16] maxima, then weights 2^(m_s - M), in the merge buffer
+  float* sl = sw + P.nsplit * 16;  // [nsplit][16] sums (the host keeps 2 * nsplit * 16 within the buffer)
   for (int e = threadIdx.x; e < P.nsplit * 16; e += WAVES * 64) {
     const int sp = e >> 4, rr = e & 15;
     const int64_t pb = ((int64_t)unit * P.nsplit + sp) * 16 + rr;
-    sw[e] = rr < P.G ? ld_coherent(P.part_ml + pb * 2) : kNegInf;
+    const bool ok = rr < P.G;
+    const float mv = ok ? ld_coherent(P.part_ml + pb * 2) : kNegInf;
+    const float lv = ok ? ld_coherent(P.part_ml + pb * 2 + 1) : 0.f;
+    sw[e] = mv;
+    sl[e] = lv;
   }
   __syncthreads();
   if (threadIdx.x < P.G) {
@@ -2049,9 +2065,8 @@ __global__ void __launch_bounds__(WAVES * 64) scan_gather_split(ScanParams P) {
     const float Ms = (M == kNegInf) ? 0.f : M;
     float L = 0.f;
     for (int sp = 0; sp < P.nsplit; ++sp) {
-      const int64_t pb = ((int64_t)unit * P.nsplit + sp) * 16 + rr;
       const float w = exp2_fast(sw[sp * 16 + rr] - Ms);
-      L += ld_coherent(P.part_ml + pb * 2 + 1) * w;
+      L += sl[sp * 16 + rr] * w;
       sw[sp * 16 + rr] = w;
     }
     sm_m[0][rr] = M;
@@ -2262,6 +2277,9 @@ __global__ void __launch_bounds__(256) combine(CombineParams P) {
   const int b = unit / (P.Hkv * P.n_tpacks);
   const int tl = r / P.G, i = r - tl * P.G;
   const int t = tp * P.tpack + tl;
+  if (P.sel_state && r == 0 && blockIdx.z == 0)  // one query token per unit: unit = selection row
+    sel_init_row(P.sel_state + (int64_t)unit * ST_WORDS, P.sel_hist + (int64_t)unit * 3 * kHistBins,
+                 P.q_pos0 + tp, P.sel_k, P.sel_window, 1, tid, 256);
   if (t >= P.Tq) return;
   const int h = g * P.G + i;
   const float* ml = P.part_ml + ((int64_t)unit * P.nsplit * 16 + r) * 2;
@@ -2322,6 +2340,9 @@ __global__ void __launch_bounds__(256) combine_few(CombineParams P) {
   const int g = unit % P.Hkv;
   const int tp = (unit / P.Hkv) % P.n_tpacks;
   const int b = unit / (P.Hkv * P.n_tpacks);
+  if (P.sel_state)
+    sel_init_row(P.sel_state + (int64_t)unit * ST_WORDS, P.sel_hist + (int64_t)unit * 3 * kHistBins,
+                 P.q_pos0 + tp, P.sel_k, P.sel_window, 1, tid, 256);
   if (tid < P.rows) {
     const float* ml = P.part_ml + ((int64_t)unit * P.nsplit * 16 + tid) * 2;
     float m = kNegInf;
@@ -2399,6 +2420,83 @@ __global__ void __launch_bounds__(256) score(ScoreParams P) {
       for (int e = 0; e < 4 && j4 + e < P.N; ++e) dst[e] = s[e];
     }
   }
+}
+
+// The score pass of a decode step whose selection follows (one query token
+// per unit): the scores as above, R groups of 4 positions per thread (1024 R
+// positions per workgroup), and the first radix digit of every candidate's
+// score counted into the selection's pass-0 histogram (an LDS histogram per
+// workgroup, flushed with one global atomic per non-empty digit).  Counts are
+// integers, so the histogram equals the one the selection's own first pass
+// would build from the stored scores.
+template <int R>
+__global__ void __launch_bounds__(256) score_hist(ScoreParams P) {
+  __shared__ int32_t h[kHistBins];
+  const int unit = blockIdx.y;
+  const int g = unit % P.Hkv;
+  const int t = (unit / P.Hkv) % P.n_tpacks;  // tpack = 1
+  const int b = unit / (P.Hkv * P.n_tpacks);
+  const int p = P.q_pos0 + t;
+  const int base = blockIdx.x * 1024 * R;
+  const int ncand = sel_ncand(p, P.sel_window);
+  const int take = sel_take(ncand, P.sel_k, 1);
+  float* dst = P.scores + (((int64_t)b * P.Tq + t) * P.Hkv + g) * P.N;
+  // head-outer, group-inner: each head's loads for all R groups are issued
+  // together (a thread waits G times, not G * R; measured faster than also
+  // prefetching the next head's loads)
+  float s[R][4];
+#pragma unroll
+  for (int q = 0; q < R; ++q) s[q][0] = s[q][1] = s[q][2] = s[q][3] = 0.f;
+  for (int i = 0; i < P.G; ++i) {
+    const int64_t row = (int64_t)unit * P.rows + i;
+    const float l2 = P.lse2[row];
+    u32x2_t w[R];
+    float mx[R];
+#pragma unroll
+    for (int q = 0; q < R; ++q) {
+      const int j4 = min(base + 4 * (threadIdx.x + 256 * q), p);  // clamped: groups past p are zeroed below
+      w[q] = *(const u32x2_t*)(P.lg16 + row * P.npad + (j4 & ~3));
+      mx[q] = P.lgmax[((int64_t)unit * (P.npad >> 5) + (j4 >> 5)) * P.rows + i];
+    }
+#pragma unroll
+    for (int q = 0; q < R; ++q) {
+      const float c = mx[q] - l2;
+      const uint32_t code[4] = {w[q].x & 0xffffu, w[q].x >> 16, w[q].y & 0xffffu, w[q].y >> 16};
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        s[q][e] += (code[e] == 65535u) ? 0.f : exp2_fast(__builtin_fmaf((float)code[e], -kCodeInv, c));
+    }
+  }
+  uint32_t key[4 * R];
+  uint64_t valid = 0;
+#pragma unroll
+  for (int q = 0; q < R; ++q) {
+    const int j4 = base + 4 * (threadIdx.x + 256 * q);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (j4 + e > p) s[q][e] = 0.f;
+    if (j4 < P.N) {
+      if ((P.N & 3) == 0) {
+        *(f32x4_t*)(dst + j4) = f32x4_t{s[q][0], s[q][1], s[q][2], s[q][3]};
+      } else {
+        for (int e = 0; e < 4 && j4 + e < P.N; ++e) dst[j4 + e] = s[q][e];
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      key[4 * q + e] = score_key(s[q][e]);
+      valid |= (uint64_t)(j4 + e < ncand) << (4 * q + e);
+    }
+  }
+  // workgroup-uniform: rows that need no radix pass, chunks past the candidates
+  if (!(take > 0 && take < ncand) || base >= ncand) return;
+  for (int i = threadIdx.x; i < kHistBins; i += 256) h[i] = 0;
+  __syncthreads();
+  hist_digit0<4 * R>(key, valid, h);
+  __syncthreads();
+  int32_t* gh = P.sel_hist + (int64_t)unit * 3 * kHistBins;
+  for (int i = threadIdx.x; i < kHistBins; i += 256)
+    if (h[i]) atomicAdd(&gh[i], h[i]);
 }
 
 // Streaming-read probe: every byte of buf read once with 16-byte non-temporal
@@ -2615,8 +2713,15 @@ hipError_t launch_combine(const CombineParams& p, int units, hipStream_t s) {
 
 hipError_t launch_score(const ScoreParams& p, int units, hipStream_t s) {
   TimedLaunch tl("score", s);
-  const int blocks = (p.N + 1023) / 1024;
-  hipLaunchKernelGGL(score, dim3(blocks, units), dim3(256), 0, s, p);
+  if (p.sel_hist) {
+    if (p.tpack != 1) return hipErrorInvalidValue;
+    constexpr int R = HS2_SCORE_HIST_R;
+    const int blocks = (p.N + 1024 * R - 1) / (1024 * R);
+    hipLaunchKernelGGL(score_hist<R>, dim3(blocks, units), dim3(256), 0, s, p);
+  } else {
+    const int blocks = (p.N + 1023) / 1024;
+    hipLaunchKernelGGL(score, dim3(blocks, units), dim3(256), 0, s, p);
+  }
   return hipGetLastError();
 }
 

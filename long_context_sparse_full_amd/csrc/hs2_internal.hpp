@@ -115,6 +115,13 @@ struct CombineParams {
   void* out;
   float* lse;    // natural log, nullable
   float* lse2;   // [units][rows] log2-domain, for the score pass
+  // token selection prepared by the merge (one query token per unit): the
+  // state words and digit histograms of row `unit` at sel_state + unit * 16
+  // and sel_hist + unit * 3 * kHistBins are initialised as the selection's
+  // own set-up would; sel_state nullptr = no selection
+  int32_t* sel_state;
+  int32_t* sel_hist;
+  int sel_k, sel_window, q_pos0;
 };
 
 struct ScoreParams {
@@ -124,6 +131,12 @@ struct ScoreParams {
   int64_t npad;
   int rows, tpack, n_tpacks, G, Hkv, Tq, N, q_pos0;
   float* scores;  // [B, Tq, Hkv, N]
+  // one query token per unit: also count the first radix digit of every
+  // candidate's score (positions [0, p - sel_window]) into the selection's
+  // pass-0 histogram sel_hist + unit * 3 * kHistBins, cleared beforehand by the
+  // merge; rows whose selection needs no radix pass are skipped.  nullptr = none
+  int32_t* sel_hist;
+  int sel_k, sel_window;
 };
 
 // ---------------------------------------------------------------------------
@@ -141,6 +154,8 @@ struct SelectParams {
   int32_t* cand;    // [units][kCandWords]: the collected path's lists
   double* bmass;    // [units][nblocks_max] (block mode)
   int nblocks_max;
+  int pre_hist0;    // token mode: state and pass-0 histogram already built (merge + score pass)
+  int collected;    // set by the launcher: the collected path runs (rows may finish there)
 };
 
 // launchers (return hipError_t of the launch)

@@ -30,22 +30,12 @@
 #include <atomic>
 
 #include "hs2_internal.hpp"
+#include "select_common.hpp"
 
 namespace hs2 {
 namespace {
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-
-// per-unit state; each pass reads the slots of the previous kernel and writes
-// its own, so no kernel reads a slot that a sibling workgroup is writing
-enum { ST_MODE = 0, ST_NCAND = 1, ST_TAKE = 2, ST_P = 3, ST_PREFIX1 = 4, ST_NEED1 = 5,
-       ST_PREFIX2 = 6, ST_NEED2 = 7, ST_COMPACT = 8, ST_NABOVE = 9, ST_NBIN = 10, ST_WORDS = 16 };
-enum { MODE_RADIX = 0, MODE_ALL = 1, MODE_NONE = 2 };
-
-__device__ __forceinline__ uint32_t score_key(float s) {
-  const uint32_t u = __float_as_uint(s);
-  return u == 0x80000000u ? 0u : u;  // -0 orders as +0
-}
 
 template <typename T>
 __device__ __forceinline__ T block_exclusive_scan(T v, T* sm, T& total) {
@@ -74,29 +64,8 @@ __device__ __forceinline__ T block_exclusive_scan(T v, T* sm, T& total) {
 __global__ void __launch_bounds__(256) sel_init(SelectParams P) {
   const int u = blockIdx.x;
   const int t = (u / P.Hkv) % P.Tq;
-  const int p = P.q_pos0 + t;
-  const int ncand = max(0, p - P.window + 1);
-  int take;
-  if (P.block_size == 1) {
-    take = min(P.k, ncand);
-  } else {
-    const int nb = ncand > 0 ? (ncand - 1) / P.block_size + 1 : 0;
-    take = min(P.k, nb);
-  }
-  if (threadIdx.x == 0) {
-    int32_t* st = P.state + (int64_t)u * ST_WORDS;
-    st[ST_MODE] = (take == 0) ? MODE_NONE : ((P.block_size == 1 && take == ncand) ? MODE_ALL : MODE_RADIX);
-    st[ST_NCAND] = ncand;
-    st[ST_TAKE] = take;
-    st[ST_P] = p;
-    st[ST_COMPACT] = 0;
-    st[ST_NABOVE] = 0;
-    st[ST_NBIN] = 0;
-  }
-  if (P.block_size == 1) {
-    int32_t* h = P.hist + (int64_t)u * 3 * kHistBins;
-    for (int i = threadIdx.x; i < 3 * kHistBins; i += 256) h[i] = 0;
-  }
+  sel_init_row(P.state + (int64_t)u * ST_WORDS, P.block_size == 1 ? P.hist + (int64_t)u * 3 * kHistBins : nullptr,
+               P.q_pos0 + t, P.k, P.window, P.block_size, threadIdx.x, 256);
 }
 
 // digits: pass 0 = bits 31..20, pass 1 = bits 19..8, pass 2 = bits 7..0
@@ -155,7 +124,40 @@ struct ChunkKeys {
   uint64_t valid;  // bit 4*i + e
 };
 
-__device__ __forceinline__ void load_keys(const float* s, int base, int end, bool vec_ok, ChunkKeys& K) {
+__device__ __forceinline__ void load_keys_first(const float* s, int base, int end, bool vec_ok, ChunkKeys& K) {
+  // Every load is issued before any key is formed (a conversion right after
+  // its own load makes each load wait for the previous one): measured faster
+  // for the collecting pass, whose work after the loads is longer.
+  float4 v[kKeysPerThread / 4];
+  if (vec_ok && end - base == kSelChunk) {  // whole chunk (workgroup-uniform): unguarded 16-byte loads
+#pragma unroll
+    for (int i = 0; i < kKeysPerThread / 4; ++i) v[i] = *(const float4*)(s + base + 4 * (threadIdx.x + 256 * i));
+    K.valid = ~0ull;
+  } else {
+    K.valid = 0;
+#pragma unroll
+    for (int i = 0; i < kKeysPerThread / 4; ++i) {
+      const int j = base + 4 * (threadIdx.x + 256 * i);
+      v[i].x = j < end ? s[j] : 0.f;
+      v[i].y = j + 1 < end ? s[j + 1] : 0.f;
+      v[i].z = j + 2 < end ? s[j + 2] : 0.f;
+      v[i].w = j + 3 < end ? s[j + 3] : 0.f;
+      const uint64_t nv = (uint64_t)min(max(end - j, 0), 4);
+      K.valid |= ((1ull << nv) - 1) << (4 * i);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kKeysPerThread / 4; ++i) {
+    K.key[4 * i] = score_key(v[i].x);
+    K.key[4 * i + 1] = score_key(v[i].y);
+    K.key[4 * i + 2] = score_key(v[i].z);
+    K.key[4 * i + 3] = score_key(v[i].w);
+  }
+}
+
+// Keys converted as their loads return: measured faster for the histogram
+// passes (at 2048 rows x 128K scores by 10%; within 2% at 4 rows).
+__device__ __forceinline__ void load_keys_inline(const float* s, int base, int end, bool vec_ok, ChunkKeys& K) {
   K.valid = 0;
 #pragma unroll
   for (int i = 0; i < kKeysPerThread / 4; ++i) {
@@ -178,50 +180,13 @@ __device__ __forceinline__ void load_keys(const float* s, int base, int end, boo
   }
 }
 
-// LDS histogram of one digit over the keys that match `prefix`.  PASS 0 keys
-// cluster in a few neighbouring bins (the scores of one row share their
-// exponent and leading mantissa bits), which would serialise the LDS atomics.
-// So each thread counts the keys of an 8-bin window, starting three bins below
-// the bin of the wave's first key, in 8-bit fields of one 64-bit word (at most
-// 64 keys per thread: no field overflows); only keys outside the window use
-// LDS atomics.  The window counts are summed over the wave (16-bit fields) and
-// added by one lane.
+// LDS histogram of one digit over the keys that match `prefix` (pass 0: all
+// keys, by the windowed register counts of hist_digit0).
 template <int PASS>
 __device__ __forceinline__ void hist_keys(const ChunkKeys& K, uint32_t prefix, int32_t* h) {
   using DG = Digit<PASS>;
   if constexpr (PASS == 0) {
-    const uint32_t first = __builtin_amdgcn_readfirstlane(K.key[0] >> DG::SHIFT);
-    const uint32_t wbase = first >= 3 ? first - 3 : 0;
-    uint64_t acc = 0;
-#pragma unroll
-    for (int i = 0; i < kKeysPerThread; ++i) {
-      const bool v = K.valid >> i & 1;
-      const uint32_t bin = K.key[i] >> DG::SHIFT;
-      const uint32_t off = bin - wbase;
-      const bool in = off < 8u;
-      acc += (v && in) ? 1ull << (8 * off) : 0ull;
-      if (v && !in) atomicAdd(&h[bin], 1);
-    }
-    // fields 0-3 and 4-7 widened to 16 bits, then summed over the wave
-    uint64_t lo = 0, hi = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      lo |= ((acc >> (8 * j)) & 0xFFull) << (16 * j);
-      hi |= ((acc >> (8 * j + 32)) & 0xFFull) << (16 * j);
-    }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      lo += __shfl_xor(lo, o);
-      hi += __shfl_xor(hi, o);
-    }
-    if ((threadIdx.x & 63) == 0) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int32_t c0 = (int32_t)((lo >> (16 * j)) & 0xFFFFull), c1 = (int32_t)((hi >> (16 * j)) & 0xFFFFull);
-        if (c0 && wbase + j < (uint32_t)DG::BINS) atomicAdd(&h[wbase + j], c0);
-        if (c1 && wbase + 4 + j < (uint32_t)DG::BINS) atomicAdd(&h[wbase + 4 + j], c1);
-      }
-    }
+    hist_digit0<kKeysPerThread>(K.key, K.valid, h);
   } else {
 #pragma unroll
     for (int i = 0; i < kKeysPerThread; ++i)
@@ -242,20 +207,23 @@ __global__ void __launch_bounds__(256) sel_hist(SelectParams P) {
   __shared__ int32_t sm[264];
   const int u = blockIdx.y, chunk = blockIdx.x;
   int32_t* st = P.state + (int64_t)u * ST_WORDS;
-  if (st[ST_MODE] != MODE_RADIX) return;
-  if (PASS == 2 && st[ST_COMPACT]) return;  // finished by the collected path
-  const int ncand = st[ST_NCAND];
+  // the row's mode and candidate count follow from its position (the same
+  // values the set-up stored), so the score loads need not wait for a state read
+  const int ncand = sel_ncand(P.q_pos0 + (u / P.Hkv) % P.Tq, P.window);
+  const int take = sel_take(ncand, P.k, 1);
+  if (sel_mode(take, ncand, 1) != MODE_RADIX) return;
+  if (PASS == 2 && P.collected && st[ST_COMPACT]) return;  // finished by the collected path
   const int base = chunk * kSelChunk;
   if (base >= ncand) return;
   const int end = min(base + kSelChunk, ncand);
   ChunkKeys K;
-  load_keys(P.scores + (int64_t)u * P.N, base, end, (P.N & 3) == 0, K);
+  load_keys_inline(P.scores + (int64_t)u * P.N, base, end, (P.N & 3) == 0, K);
   int32_t* hist = P.hist + (int64_t)u * 3 * kHistBins;
   uint32_t prefix = 0;
   if constexpr (PASS > 0) {
     // the previous pass's digit; inputs are what the kernel before wrote
     const uint32_t prev = PASS == 1 ? 0u : (uint32_t)st[ST_PREFIX1];
-    int need = PASS == 1 ? st[ST_TAKE] : st[ST_NEED1];
+    int need = PASS == 1 ? take : st[ST_NEED1];
     int d, above;
     find_digit<PASS - 1>(hist + (PASS - 1) * kHistBins, need, sm, d, above);
     prefix = prev | ((uint32_t)d << Digit<PASS - 1>::SHIFT);
@@ -319,7 +287,7 @@ __global__ void __launch_bounds__(256) sel_collect(SelectParams P) {
   if (base >= ncand) return;
   const int end = min(base + kSelChunk, ncand);
   ChunkKeys K;
-  load_keys(P.scores + (int64_t)u * P.N, base, end, (P.N & 3) == 0, K);
+  load_keys_first(P.scores + (int64_t)u * P.N, base, end, (P.N & 3) == 0, K);
   const int32_t* hist = P.hist + (int64_t)u * 3 * kHistBins;
   int need = st[ST_NEED1];
   int d, above, nbin;
@@ -493,13 +461,13 @@ __global__ void __launch_bounds__(256) sel_emit(SelectParams P) {
   __shared__ int32_t sm[264];
   const int u = blockIdx.y, chunk = blockIdx.x;
   const int32_t* st = P.state + (int64_t)u * ST_WORDS;
-  const int mode = st[ST_MODE];
-  const int ncand = st[ST_NCAND];
-  const int take = st[ST_TAKE];
-  const int p = st[ST_P];
+  const int p = P.q_pos0 + (u / P.Hkv) % P.Tq;  // as stored by the set-up
+  const int ncand = sel_ncand(p, P.window);
+  const int take = sel_take(ncand, P.k, 1);
+  const int mode = sel_mode(take, ncand, 1);
   int32_t* out = P.idx + (int64_t)u * P.max_sel;
 
-  if (mode == MODE_RADIX && st[ST_COMPACT]) return;  // written by the collected path
+  if (mode == MODE_RADIX && P.collected && st[ST_COMPACT]) return;  // written by the collected path
   if (chunk == 0) write_window(P, u, take, p, out);
   if (mode == MODE_NONE) return;
   const int base = chunk * kSelChunk;
@@ -600,8 +568,7 @@ __global__ void __launch_bounds__(256) sel_emit(SelectParams P) {
 __global__ void __launch_bounds__(256) sel_block_mass(SelectParams P) {
   const int u = blockIdx.y;
   const int beta = blockIdx.x * 256 + threadIdx.x;
-  const int32_t* st = P.state + (int64_t)u * ST_WORDS;
-  const int ncand = st[ST_NCAND];
+  const int ncand = sel_ncand(P.q_pos0 + (u / P.Hkv) % P.Tq, P.window);  // as stored by the set-up
   const int nb = ncand > 0 ? (ncand - 1) / P.block_size + 1 : 0;
   if (beta >= nb) return;
   const float* s = P.scores + (int64_t)u * P.N;
@@ -631,8 +598,7 @@ template <int BS>
 __global__ void __launch_bounds__(256) sel_block_mass_tiled(SelectParams P) {
   __shared__ float sv[kMassTile + kMassTile / BS];
   const int u = blockIdx.y;
-  const int32_t* st = P.state + (int64_t)u * ST_WORDS;
-  const int ncand = st[ST_NCAND];
+  const int ncand = sel_ncand(P.q_pos0 + (u / P.Hkv) % P.Tq, P.window);  // as stored by the set-up
   const int lo = blockIdx.x * kMassTile;
   if (lo >= ncand) return;
   const float* s = P.scores + (int64_t)u * P.N;
@@ -893,7 +859,9 @@ __global__ void __launch_bounds__(256) sel_block_pick(SelectParams P) {
 
 }  // namespace
 
-hipError_t launch_select(const SelectParams& p, hipStream_t s) {
+hipError_t launch_select(const SelectParams& p_in, hipStream_t s) {
+  SelectParams p = p_in;
+  p.collected = p.block_size == 1 && p.units * p.nchunks >= kSelMinWorkgroups;
   const dim3 grid_c(p.nchunks, p.units);
   hipError_t e;
 #define HS2_L(name, kern, grid)                                   \
@@ -902,13 +870,13 @@ hipError_t launch_select(const SelectParams& p, hipStream_t s) {
     hipLaunchKernelGGL(kern, grid, dim3(256), 0, s, p);           \
     if ((e = hipGetLastError()) != hipSuccess) return e;          \
   } while (0)
-  HS2_L("select_init", sel_init, dim3(p.units));
+  if (!(p.pre_hist0 && p.block_size == 1)) HS2_L("select_init", sel_init, dim3(p.units));
   if (p.block_size == 1) {
-    HS2_L("select_hist", sel_hist<0>, grid_c);
+    if (!p.pre_hist0) HS2_L("select_hist", sel_hist<0>, grid_c);
     HS2_L("select_hist", sel_hist<1>, grid_c);
     // The collected path saves two full reads of the scores but adds two
     // launches: taken where the passes are throughput-bound.
-    if (p.units * p.nchunks >= kSelMinWorkgroups) {
+    if (p.collected) {
       HS2_L("select_collect", sel_collect, grid_c);
       // the LDS attribute is set once per device, for the largest bitmap
       static std::atomic<uint64_t> attr_done{0};
