@@ -1914,38 +1914,43 @@ __global__ void __launch_bounds__(WAVES * 64) scan_gather(ScanParams P) {
     auto compute = [&](const RawTile<FP8, D>& R, int j0) {
       compute_tile<FP8, D, false>(R, qf, cs, j0, jl, j0 + 31 > jl, g4, nullptr, nullptr, 0, S);
     };
+    // This wave's tiles j_first + i * STEP, i < nt.  Loads are issued without
+    // conditions (tiles past the list reload its last row, unused), so the
+    // compiler's in-order wait counts leave the prefetched tiles in flight; a
+    // conditional load would make every wait drain the ring.
     const int jend = base + nb;
-    int j0 = base + wave * 32;
-    if constexpr (!FP8 && D == 128) {  // 64-register tiles: two-tile ping-pong
-      RawTile<FP8, D> A, B;
-      if (j0 < jend) load(A, j0);
-      while (j0 < jend) {
-        if (j0 + STEP < jend) load(B, j0 + STEP);
-        compute(A, j0);
-        j0 += STEP;
-        if (j0 >= jend) break;
-        if (j0 + STEP < jend) load(A, j0 + STEP);
-        compute(B, j0);
-        j0 += STEP;
+    const int j_first = base + wave * 32;
+    const int nt = j_first < jend ? (jend - 1 - j_first) / STEP + 1 : 0;
+    if (nt > 0) {
+      if constexpr (!FP8 && D == 128) {  // 64-register tiles: two-tile ping-pong
+        RawTile<FP8, D> A, B;
+        load(A, j_first);
+        int i = 0;
+        for (; i + 2 <= nt; i += 2) {
+          const int j0 = j_first + i * STEP;
+          load(B, j0 + STEP);
+          compute(A, j0);
+          load(A, j0 + 2 * STEP);
+          compute(B, j0 + STEP);
+        }
+        if (i < nt) compute(A, j_first + i * STEP);
+      } else {  // three-tile register ring: two tiles in flight while one is computed
+        RawTile<FP8, D> A, B, C;
+        load(A, j_first);
+        load(B, j_first + STEP);
+        int i = 0;
+        for (; i + 3 <= nt; i += 3) {
+          const int j0 = j_first + i * STEP;
+          load(C, j0 + 2 * STEP);
+          compute(A, j0);
+          load(A, j0 + 3 * STEP);
+          compute(B, j0 + STEP);
+          load(B, j0 + 4 * STEP);
+          compute(C, j0 + 2 * STEP);
+        }
+        if (i < nt) compute(A, j_first + i * STEP);
+        if (i + 1 < nt) compute(B, j_first + (i + 1) * STEP);
       }
-    } else {
-    // three-tile register ring: two tiles of loads in flight while one is computed
-    RawTile<FP8, D> A, B, C;
-    if (j0 < jend) load(A, j0);
-    if (j0 + STEP < jend) load(B, j0 + STEP);
-    while (j0 < jend) {
-      if (j0 + 2 * STEP < jend) load(C, j0 + 2 * STEP);
-      compute(A, j0);
-      j0 += STEP;
-      if (j0 >= jend) break;
-      if (j0 + 2 * STEP < jend) load(A, j0 + 2 * STEP);
-      compute(B, j0);
-      j0 += STEP;
-      if (j0 >= jend) break;
-      if (j0 + 2 * STEP < jend) load(B, j0 + 2 * STEP);
-      compute(C, j0);
-      j0 += STEP;
-    }
     }
   }
   merge_and_store<FP8, D, true, WAVES>(P, S, unit, 0, b, g, wave, r, g4, sm_m, sm_l, sm_o);
@@ -2016,18 +2021,25 @@ __global__ void __launch_bounds__(WAVES * 64) scan_gather_split(ScanParams P) {
         vp[kk] = vb + (int64_t)s_idx[min(j0 - lo + 16 * (kk >> 2) + 4 * g4 + (kk & 3), nb - 1)] * snb;
       load_tile<FP8, D, false>(R, kp, vp);
     };
-    RawTile<FP8, D> A, B;
-    int j0 = lo + wave * 32;
-    if (j0 < hi) load(A, j0);
-    while (j0 < hi) {
-      const int j1 = j0 + STEP;
-      if (j1 < hi) load(B, j1);
-      compute_tile<FP8, D, false>(A, qf, cs, j0, jl, j0 + 31 > jl, g4, nullptr, nullptr, 0, S);
-      if (j1 >= hi) break;
-      const int j2 = j1 + STEP;
-      if (j2 < hi) load(A, j2);
-      compute_tile<FP8, D, false>(B, qf, cs, j1, jl, j1 + 31 > jl, g4, nullptr, nullptr, 0, S);
-      j0 = j2;
+    // this wave's tiles j_first + i * STEP, i < nt; unconditional loads as in
+    // the one-workgroup form (tiles past the slice reload its last row, unused)
+    const int j_first = lo + wave * 32;
+    const int nt = j_first < hi ? (hi - 1 - j_first) / STEP + 1 : 0;
+    if (nt > 0) {
+      RawTile<FP8, D> A, B;
+      load(A, j_first);
+      int i = 0;
+      for (; i + 2 <= nt; i += 2) {
+        const int j0 = j_first + i * STEP;
+        load(B, j0 + STEP);
+        compute_tile<FP8, D, false>(A, qf, cs, j0, jl, j0 + 31 > jl, g4, nullptr, nullptr, 0, S);
+        load(A, j0 + 2 * STEP);
+        compute_tile<FP8, D, false>(B, qf, cs, j0 + STEP, jl, j0 + STEP + 31 > jl, g4, nullptr, nullptr, 0, S);
+      }
+      if (i < nt) {
+        const int j0 = j_first + i * STEP;
+        compute_tile<FP8, D, false>(A, qf, cs, j0, jl, j0 + 31 > jl, g4, nullptr, nullptr, 0, S);
+      }
     }
   }
   // partial of this slice (rows = G heads), same layout as the full-layer
@@ -2043,12 +2055,36 @@ __global__ void __launch_bounds__(WAVES * 64) scan_gather_split(ScanParams P) {
   }
   __syncthreads();
   if (!s_last) return;
-  // the last slice merges all partials (device-coherent loads): every slice's
-  // (max, sum) in one round of loads, the weights from LDS, then every output
-  // element with its loads issued together
+  // The last slice merges all partials (device-coherent loads).  Output
+  // elements e0 + q * NT (q < EPT) of this thread take their slices in batches
+  // of SB whose loads are all issued before any is used (slices past nsplit
+  // reload the last one with no weight); the first batch goes out before the
+  // slices' (max, sum) loads, so both arrive in one memory round trip.
+  constexpr int NT = WAVES * 64, EPT = 4, SB = 16;
+  const int GD = P.G * D;
+  const int64_t sst = (int64_t)16 * D;
+  const float* po[EPT];
+  int rq[EPT];
+  float vv[EPT][SB];
+  auto setup = [&](int e0) {
+#pragma unroll
+    for (int q = 0; q < EPT; ++q) {
+      const int e = min(e0 + q * NT, GD - 1);
+      rq[q] = e / D;
+      po[q] = P.part_o + ((int64_t)unit * P.nsplit * 16 + rq[q]) * D + (e - rq[q] * D);
+    }
+  };
+  auto load_batch = [&](int sp0) {
+#pragma unroll
+    for (int q = 0; q < EPT; ++q)
+#pragma unroll
+      for (int k = 0; k < SB; ++k) vv[q][k] = ld_coherent(po[q] + min(sp0 + k, P.nsplit - 1) * sst);
+  };
+  setup(threadIdx.x);
+  load_batch(0);
   float* sw = &sm_o[0][0][0];  // [nsplit][16] maxima, then weights 2^(m_s - M), in the merge buffer
   float* sl = sw + P.nsplit * 16;  // [nsplit][16] sums (the host keeps 2 * nsplit * 16 within the buffer)
-  for (int e = threadIdx.x; e < P.nsplit * 16; e += WAVES * 64) {
+  for (int e = threadIdx.x; e < P.nsplit * 16; e += NT) {
     const int sp = e >> 4, rr = e & 15;
     const int64_t pb = ((int64_t)unit * P.nsplit + sp) * 16 + rr;
     const bool ok = rr < P.G;
@@ -2073,28 +2109,34 @@ __global__ void __launch_bounds__(WAVES * 64) scan_gather_split(ScanParams P) {
     sm_l[0][rr] = L;
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < P.G * D; e += WAVES * 64) {
-    const int rr = e / D, d = e - rr * D;
-    const float* po = P.part_o + ((int64_t)unit * P.nsplit * 16 + rr) * D + d;
-    const int64_t sst = (int64_t)16 * D;
-    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-    int sp = 0;
-    for (; sp + 3 < P.nsplit; sp += 4) {
-      const float v0 = ld_coherent(po + sp * sst), v1 = ld_coherent(po + (sp + 1) * sst);
-      const float v2 = ld_coherent(po + (sp + 2) * sst), v3 = ld_coherent(po + (sp + 3) * sst);
-      a0 += sw[sp * 16 + rr] * v0;
-      a1 += sw[(sp + 1) * 16 + rr] * v1;
-      a2 += sw[(sp + 2) * 16 + rr] * v2;
-      a3 += sw[(sp + 3) * 16 + rr] * v3;
+  for (int e0 = threadIdx.x; e0 < GD; e0 += EPT * NT) {
+    if (e0 != (int)threadIdx.x) {
+      setup(e0);
+      load_batch(0);
     }
-    for (; sp < P.nsplit; ++sp) a0 += sw[sp * 16 + rr] * ld_coherent(po + sp * sst);
-    const float O = (a0 + a1) + (a2 + a3);
-    const float M = sm_m[0][rr], L = sm_l[0][rr];
-    float o = (L > 0.f) ? O / L : 0.f;
-    if constexpr (FP8) o *= P.v_scale[b * P.Hkv + g];
-    const int64_t orow = ((int64_t)b * P.Tq + t) * P.Hq + g * P.G + rr;
-    ((__bf16*)P.out)[orow * D + d] = (__bf16)o;
-    if (d == 0 && P.lse) P.lse[orow] = (L > 0.f) ? (M + log2f(L)) * kLn2 : kNegInf;
+    float acc[EPT] = {};
+    for (int sp0 = 0;;) {
+#pragma unroll
+      for (int q = 0; q < EPT; ++q)
+#pragma unroll
+        for (int k = 0; k < SB; ++k)
+          if (sp0 + k < P.nsplit) acc[q] += sw[(sp0 + k) * 16 + rq[q]] * vv[q][k];
+      sp0 += SB;
+      if (sp0 >= P.nsplit) break;
+      load_batch(sp0);
+    }
+#pragma unroll
+    for (int q = 0; q < EPT; ++q) {
+      const int e = e0 + q * NT;
+      if (e >= GD) break;
+      const int rr = rq[q], d = e - rr * D;
+      const float M = sm_m[0][rr], L = sm_l[0][rr];
+      float o = (L > 0.f) ? acc[q] / L : 0.f;
+      if constexpr (FP8) o *= P.v_scale[b * P.Hkv + g];
+      const int64_t orow = ((int64_t)b * P.Tq + t) * P.Hq + g * P.G + rr;
+      ((__bf16*)P.out)[orow * D + d] = (__bf16)o;
+      if (d == 0 && P.lse) P.lse[orow] = (L > 0.f) ? (M + log2f(L)) * kLn2 : kNegInf;
+    }
   }
   if (threadIdx.x == 0) P.gcounter[unit] = 0;  // re-armed for the next call
 }
@@ -2266,9 +2308,10 @@ __device__ __forceinline__ float block_reduce_256(float v, float* red, bool is_m
 
 // grid (unit, row, head-dim chunk of 32): every workgroup recomputes the split
 // weights 2^(m_s - M) into LDS, then 8 groups of 32 threads sum interleaved
-// splits with 4 independent accumulators each (many loads in flight).
+// splits, each thread's loads issued 32 at a time.
 __global__ void __launch_bounds__(256) combine(CombineParams P) {
   __shared__ float sw[kMaxSplits];
+  __shared__ float sl[kMaxSplits];
   __shared__ float red[8];
   __shared__ float part[256];
   const int unit = blockIdx.x, r = blockIdx.y, tid = threadIdx.x;
@@ -2283,31 +2326,48 @@ __global__ void __launch_bounds__(256) combine(CombineParams P) {
   if (t >= P.Tq) return;
   const int h = g * P.G + i;
   const float* ml = P.part_ml + ((int64_t)unit * P.nsplit * 16 + r) * 2;
-  float m = kNegInf;
-  for (int s = tid; s < P.nsplit; s += 256) m = fmaxf(m, ml[s * 32]);
-  const float M = block_reduce_256(m, red, true);
-  const float Ms = (M == kNegInf) ? 0.f : M;
-  float l = 0.f;
-  for (int s = tid; s < P.nsplit; s += 256) {
-    const float w = exp2f(ml[s * 32] - Ms);
-    sw[s] = w;
-    l += ml[s * 32 + 1] * w;
-  }
-  const float L = block_reduce_256(l, red, false);  // its barriers also publish sw
   const int dl = tid & 31, pp = tid >> 5;
   const int d = blockIdx.z * 32 + dl;
   const float* po = P.part_o + ((int64_t)unit * P.nsplit * 16 + r) * P.D + d;
   const int64_t sstride = (int64_t)16 * P.D;
-  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-  int s = pp;
-  for (; s + 24 < P.nsplit; s += 32) {
-    a0 += sw[s] * po[s * sstride];
-    a1 += sw[s + 8] * po[(s + 8) * sstride];
-    a2 += sw[s + 16] * po[(s + 16) * sstride];
-    a3 += sw[s + 24] * po[(s + 24) * sstride];
+  // This thread sums splits pp, pp + 8, ... in batches of CB whose loads are
+  // all issued before any is used (splits past nsplit reload the last one
+  // with no weight).  The first batch is issued before the (max, sum) loads,
+  // so both arrive in one memory round trip.
+  constexpr int CB = 32;
+  float vv[CB];
+  auto load_batch = [&](int s0) {
+#pragma unroll
+    for (int k = 0; k < CB; ++k) vv[k] = po[(int64_t)min(s0 + 8 * k, P.nsplit - 1) * sstride];
+  };
+  load_batch(pp);
+  // each split's (max, sum) read once; the sums wait in LDS
+  float m = kNegInf;
+  for (int s = tid; s < P.nsplit; s += 256) {
+    const float ms = ml[s * 32], ls = ml[s * 32 + 1];
+    sw[s] = ms;
+    sl[s] = ls;
+    m = fmaxf(m, ms);
   }
-  for (; s < P.nsplit; s += 8) a0 += sw[s] * po[s * sstride];
-  part[tid] = (a0 + a1) + (a2 + a3);
+  const float M = block_reduce_256(m, red, true);  // its barriers also publish sw, sl
+  const float Ms = (M == kNegInf) ? 0.f : M;
+  float l = 0.f;
+  for (int s = tid; s < P.nsplit; s += 256) {
+    const float w = exp2f(sw[s] - Ms);
+    sw[s] = w;
+    l += sl[s] * w;
+  }
+  const float L = block_reduce_256(l, red, false);  // its barriers also publish the weights
+  float acc = 0.f;
+  for (int s0 = pp;;) {
+#pragma unroll
+    for (int k = 0; k < CB; ++k)
+      if (s0 + 8 * k < P.nsplit) acc += sw[s0 + 8 * k] * vv[k];
+    s0 += 8 * CB;
+    if (s0 >= P.nsplit) break;
+    load_batch(s0);
+  }
+  part[tid] = acc;
   __syncthreads();
   if (pp != 0) return;
   float O = 0.f;
