@@ -37,28 +37,56 @@ namespace {
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
+// Inclusive prefix sum over the 64 lanes of a wave by DPP moves: shifts of
+// 1, 2, 4 and 8 lanes within each row of 16 (lanes shifted in from outside the
+// row add 0), then the last lane of row 0 / row 2 added to rows 1 / 3 and the
+// last lane of row 1 added to rows 2 and 3.
+__device__ __forceinline__ int32_t wave_inclusive_scan(int32_t x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15 into rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31 into rows 2, 3
+  return x;
+}
+
+// Exclusive prefix sums over the 256 threads of a workgroup of N values per
+// thread at once (one pair of barriers); total[k] = sum of v[k] over the
+// workgroup.  sm has >= 256 + 4 * N slots.
+template <int N>
+__device__ __forceinline__ void block_exclusive_scan_n(int32_t (&v)[N], int32_t* sm, int32_t (&total)[N]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int32_t x[N];
+#pragma unroll
+  for (int k = 0; k < N; ++k) x[k] = wave_inclusive_scan(v[k]);
+  if (lane == 63) {
+#pragma unroll
+    for (int k = 0; k < N; ++k) sm[256 + 4 * k + wave] = x[k];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < N; ++k) {
+    int32_t wbase = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int32_t s = sm[256 + 4 * k + w];
+      if (w < wave) wbase += s;
+      tot += s;
+    }
+    total[k] = tot;
+    v[k] = wbase + x[k] - v[k];
+  }
+  __syncthreads();
+}
+
 template <typename T>
 __device__ __forceinline__ T block_exclusive_scan(T v, T* sm, T& total) {
-  // 256 threads; sm has >= 256 + 8 slots
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  T x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const T y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
-  if (lane == 63) sm[256 + wave] = x;
-  __syncthreads();
-  T wbase = 0, tot = 0;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    const T s = sm[256 + w];
-    if (w < wave) wbase += s;
-    tot += s;
-  }
-  __syncthreads();
-  total = tot;
-  return wbase + x - v;
+  static_assert(sizeof(T) == 4, "32-bit scan");
+  int32_t a[1] = {(int32_t)v}, t[1];
+  block_exclusive_scan_n<1>(a, (int32_t*)sm, t);
+  total = (T)t[0];
+  return (T)a[0];
 }
 
 __global__ void __launch_bounds__(256) sel_init(SelectParams P) {
@@ -523,17 +551,31 @@ __global__ void __launch_bounds__(256) sel_emit(SelectParams P) {
     eq_before += eq_tot;
     sel_before += sel_tot;
   }
-  int32_t eq_rank = eq_before, slot = sel_before;
+  // The four rounds' counts go through two packed scans (16 bits per round;
+  // a round holds at most 4096 keys): first the keys equal to tau, whose rank
+  // decides which of them are taken, then the taken keys, whose prefix is the
+  // output slot.  Positions are ordered by (round, thread, element).
+  int32_t eqc[4];
 #pragma unroll
   for (int rnd = 0; rnd < 4; ++rnd) {
     const int j0 = base + rnd * 4096 + threadIdx.x * 16;
-    int32_t my_eq = 0;
+    int32_t c = 0;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) my_eq += (j0 + e < end) && keys[rnd * 16 + e] == tau;
-    int32_t teq;
-    int32_t r_eq = eq_rank + block_exclusive_scan<int32_t>(my_eq, sm, teq);
-    uint32_t selmask = 0;
-    int32_t my_sel = 0;
+    for (int e = 0; e < 16; ++e) c += (j0 + e < end) && keys[rnd * 16 + e] == tau;
+    eqc[rnd] = c;
+  }
+  int32_t pe[2] = {eqc[0] | (eqc[1] << 16), eqc[2] | (eqc[3] << 16)}, te[2];
+  block_exclusive_scan_n<2>(pe, sm, te);
+  uint32_t selmask[4];
+  int32_t selc[4];
+  int32_t rbase = eq_before;
+#pragma unroll
+  for (int rnd = 0; rnd < 4; ++rnd) {
+    const int j0 = base + rnd * 4096 + threadIdx.x * 16;
+    const int f = (rnd & 1) * 16, w = rnd >> 1;
+    int32_t r_eq = rbase + ((pe[w] >> f) & 0xffff);
+    rbase += (te[w] >> f) & 0xffff;
+    uint32_t m = 0;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const uint32_t key = keys[rnd * 16 + e];
@@ -546,19 +588,26 @@ __global__ void __launch_bounds__(256) sel_emit(SelectParams P) {
           ++r_eq;
         }
       }
-      selmask |= (uint32_t)take_it << e;
-      my_sel += take_it;
+      m |= (uint32_t)take_it << e;
     }
-    int32_t tsel;
-    int32_t sl = slot + block_exclusive_scan<int32_t>(my_sel, sm, tsel);
+    selmask[rnd] = m;
+    selc[rnd] = __builtin_popcount(m);
+  }
+  int32_t ps[2] = {selc[0] | (selc[1] << 16), selc[2] | (selc[3] << 16)}, ts[2];
+  block_exclusive_scan_n<2>(ps, sm, ts);
+  int32_t sbase = sel_before;
+#pragma unroll
+  for (int rnd = 0; rnd < 4; ++rnd) {
+    const int j0 = base + rnd * 4096 + threadIdx.x * 16;
+    const int f = (rnd & 1) * 16, w = rnd >> 1;
+    int32_t sl = sbase + ((ps[w] >> f) & 0xffff);
+    sbase += (ts[w] >> f) & 0xffff;
 #pragma unroll
     for (int e = 0; e < 16; ++e)
-      if (selmask >> e & 1u) {
-        if (sl < take) out[sl] = j0 + e;  // never past this unit's budget
+      if (selmask[rnd] >> e & 1u) {
+        if ((uint32_t)sl < (uint32_t)take) out[sl] = j0 + e;  // never past this unit's budget
         ++sl;
       }
-    eq_rank += teq;
-    slot += tsel;
   }
 }
 
