@@ -151,6 +151,7 @@ def main():
     lse = torch.empty((B, Tq, Hq), dtype=torch.float32, device="cuda")
     scores = torch.empty((B, Tq, Hkv, N), dtype=torch.float32, device="cuda")
     ws_full = torch.empty(hs2.full_attn_scores_workspace(k, v, Tq, Hq), dtype=torch.uint8, device="cuda")
+    ws_topk = torch.empty(hs2.full_attn_topk_workspace(k, v, Tq, Hq), dtype=torch.uint8, device="cuda")
     idx = torch.empty((B, Tq, Hkv, spec.max_sel), dtype=torch.int32, device="cuda")
     cnt = torch.empty((B, Tq, Hkv), dtype=torch.int32, device="cuda")
     ws_sel = torch.empty(hs2.select_workspace(B, Tq, Hkv, N, 1), dtype=torch.uint8, device="cuda")
@@ -423,6 +424,7 @@ def bench_chunk(spec, args):
     lse = torch.empty((B, Tq, Hq), dtype=torch.float32, device="cuda")
     scores = torch.empty((B, Tq, Hkv, N), dtype=torch.float32, device="cuda")
     ws_full = torch.empty(hs2.full_attn_scores_workspace(k, v, Tq, Hq), dtype=torch.uint8, device="cuda")
+    ws_topk = torch.empty(hs2.full_attn_topk_workspace(k, v, Tq, Hq), dtype=torch.uint8, device="cuda")
     idx = torch.empty((B, Tq, Hkv, spec.max_sel), dtype=torch.int32, device="cuda")
     cnt = torch.empty((B, Tq, Hkv), dtype=torch.int32, device="cuda")
     bsel = spec.block_k * spec.block_size + spec.window
@@ -433,9 +435,13 @@ def bench_chunk(spec, args):
 
     def step():
         hs2.kv_bridge(hidden, w, k, v, 0, N - T)
-        hs2.full_attn_scores(k, v, q, spec.q_pos0, out=out, lse=lse, scores=scores, workspace=ws_full)
-        hs2.select_topk_window(scores, spec.q_pos0, spec.k, spec.window, max_sel=spec.max_sel, idx=idx, count=cnt,
-                               workspace=ws_sel)
+        if args.topk_call:  # full layer and token top-k in one call
+            hs2.full_attn_topk(k, v, q, spec.q_pos0, spec.k, spec.window, max_sel=spec.max_sel, out=out, lse=lse,
+                               scores=scores, idx=idx, count=cnt, workspace=ws_topk)
+        else:
+            hs2.full_attn_scores(k, v, q, spec.q_pos0, out=out, lse=lse, scores=scores, workspace=ws_full)
+            hs2.select_topk_window(scores, spec.q_pos0, spec.k, spec.window, max_sel=spec.max_sel, idx=idx,
+                                   count=cnt, workspace=ws_sel)
         hs2.select_topk_window(scores, spec.q_pos0, spec.block_k, spec.window, block_size=spec.block_size,
                                max_sel=bsel, idx=bidx, count=bcnt, workspace=ws_sel)
         for i, ql in enumerate(qs):
@@ -524,7 +530,8 @@ def bench_chunk(spec, args):
     print(json.dumps({"metric": "tokens/s per 512-query chunk (bridge + full + token & block select + 3 sparse)",
                       "value": round(Tq / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": steps,
                       "ms_per_step": round(ms, 4), "higher_is_better": True, "dtype": "bf16/f32-acc",
-                      "data": "synthetic", "config": {"workload": spec.name, "Tq": Tq, "context": N},
+                      "data": "synthetic", "config": {"workload": spec.name, "Tq": Tq, "context": N,
+                                                           "full_and_select": "one call" if args.topk_call else "two calls"},
                       "kernels": kernels, "kv_bridge_into_fp8_cache_us": bridge_fp8_us, "roofline": roofline,
                       "cpu_baseline": cpu}), flush=True)
 

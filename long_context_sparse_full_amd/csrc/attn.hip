@@ -2306,6 +2306,18 @@ __device__ __forceinline__ float block_reduce_256(float v, float* red, bool is_m
   return t;
 }
 
+// The selection rows (b, t, g) of the unit's tokens set up as the selection's
+// own initialisation would (one workgroup, 256 threads).
+__device__ __forceinline__ void sel_init_unit_rows(const CombineParams& P, int b, int tp, int g, int tid) {
+  for (int tl = 0; tl < P.tpack; ++tl) {
+    const int t = tp * P.tpack + tl;
+    if (t >= P.Tq) break;
+    const int64_t u = ((int64_t)b * P.Tq + t) * P.Hkv + g;
+    sel_init_row(P.sel_state + u * ST_WORDS, P.sel_hist + u * 3 * kHistBins, P.q_pos0 + t, P.sel_k, P.sel_window, 1,
+                 tid, 256);
+  }
+}
+
 // grid (unit, row, head-dim chunk of 32): every workgroup recomputes the split
 // weights 2^(m_s - M) into LDS, then 8 groups of 32 threads sum interleaved
 // splits, each thread's loads issued 32 at a time.
@@ -2320,9 +2332,7 @@ __global__ void __launch_bounds__(256) combine(CombineParams P) {
   const int b = unit / (P.Hkv * P.n_tpacks);
   const int tl = r / P.G, i = r - tl * P.G;
   const int t = tp * P.tpack + tl;
-  if (P.sel_state && r == 0 && blockIdx.z == 0)  // one query token per unit: unit = selection row
-    sel_init_row(P.sel_state + (int64_t)unit * ST_WORDS, P.sel_hist + (int64_t)unit * 3 * kHistBins,
-                 P.q_pos0 + tp, P.sel_k, P.sel_window, 1, tid, 256);
+  if (P.sel_state && r == 0 && blockIdx.z == 0) sel_init_unit_rows(P, b, tp, g, tid);
   if (t >= P.Tq) return;
   const int h = g * P.G + i;
   const float* ml = P.part_ml + ((int64_t)unit * P.nsplit * 16 + r) * 2;
@@ -2400,9 +2410,7 @@ __global__ void __launch_bounds__(256) combine_few(CombineParams P) {
   const int g = unit % P.Hkv;
   const int tp = (unit / P.Hkv) % P.n_tpacks;
   const int b = unit / (P.Hkv * P.n_tpacks);
-  if (P.sel_state)
-    sel_init_row(P.sel_state + (int64_t)unit * ST_WORDS, P.sel_hist + (int64_t)unit * 3 * kHistBins,
-                 P.q_pos0 + tp, P.sel_k, P.sel_window, 1, tid, 256);
+  if (P.sel_state) sel_init_unit_rows(P, b, tp, g, tid);
   if (tid < P.rows) {
     const float* ml = P.part_ml + ((int64_t)unit * P.nsplit * 16 + tid) * 2;
     float m = kNegInf;

@@ -473,6 +473,9 @@ TOPK_CASES = [
     ("fp8", 128, 8, 1, 1, 5000, 7, 0, "rand"),       # no window
     ("bf16", 64, 16, 2, 1, 9001, 256, 32, "rand", 2),  # two query tokens, one per unit (16 heads fill a tile)
     ("fp8", 128, 8, 2, 1, 70001, 1024, 128, "rand"),   # several score workgroups per row, ragged end
+    ("bf16", 128, 8, 2, 1, 9001, 256, 32, "rand", 64),   # 64 query tokens: the multi-query chunk path
+    ("fp8", 64, 4, 2, 2, 5003, 100, 16, "rand", 40),     # chunk path, 4 heads per group, ragged
+    ("bf16", 128, 16, 1, 1, 3000, 2999, 1, "rand", 32),  # chunk path, 16 heads per group, k covers most rows
 ]
 
 
@@ -500,15 +503,18 @@ def test_full_attn_topk(hs2, case, mode):
                                                     k_scale=blk.ks, v_scale=blk.vs)
         torch.cuda.synchronize()
         _, n_hist = hs2.timing_collect("select_hist")
+        _, n_chunk = hs2.timing_collect("chunk_full")
     finally:
         hs2.timing_enable(False)
         hs2.timing_reset()
         hs2.full_attn_set_mode(0)
     if mode == 1 and Tq == 1:
         assert n_hist == 0, "selection did not run inside the cooperative kernel"
-    elif mode == 0:
+    elif mode == 0 and n_chunk == 0:
         # the merge sets the rows up and the score pass counts the first digit
         assert n_hist == 2, "expected the last two histogram passes of the select kernels"
+    elif mode == 0:
+        assert n_hist == 3, "the multi-query path runs all three histogram passes"
     o_or, l_or, s_or = oracle_full(inp, spec)
     gu.assert_close(gu.host(out), o_or, gu.O_TOL[kv], "out")
     gu.assert_close(gu.host(lse), l_or, gu.LSE_TOL[kv], "lse")
