@@ -31,7 +31,7 @@ if ROOT not in sys.path:
 METRIC = "µs/decode-step (full scan + top-k + 3 sparse layers) & HBM GB/s at 1M ctx"
 HBM_PEAK_GBPS = 8000.0
 MFMA_BF16_TFLOPS = 2500.0
-SCAN_SRCS = [os.path.join(ROOT, "long_context_sparse_full_amd", "csrc", f) for f in ("attn.hip", "hs2_internal.hpp")]
+SCAN_SRCS = [os.path.join(ROOT, "long_context_sparse_full_amd", "csrc", f) for f in ("attn.hip", "hs2_internal.hpp", "select_common.hpp")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "full_scan_decode1m_fp8.md")
 TRAFFIC_WORKLOAD = "decode1m_fp8"
 
