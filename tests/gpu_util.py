@@ -59,15 +59,22 @@ class DeviceBlock:
         self.qs = [dev(x) for x in inp.q_sparse]
 
 
-def run_block(hs2, blk: DeviceBlock, spec, k=None, window=None, block_size=1, layers=None, split_gather=False):
-    """full -> select -> sparse layers on the GPU (as bench.py runs them; the
-    split gather with a zero-filled workspace when split_gather=True);
-    returns host arrays."""
+def run_block(hs2, blk: DeviceBlock, spec, k=None, window=None, block_size=1, layers=None, split_gather=False,
+              topk_call=False):
+    """full -> select -> sparse layers on the GPU; topk_call=True runs the full
+    layer and the token selection as one hs2_full_attn_topk call, and
+    split_gather=True the split gather with a zero-filled workspace (together:
+    the launch configuration bench.py times); returns host arrays."""
     k = spec.k if k is None else k
     window = spec.window if window is None else window
-    out, lse, sc = hs2.full_attn_scores(blk.k, blk.v, blk.q, spec.q_pos0, k_scale=blk.ks, v_scale=blk.vs)
     max_sel = min(spec.N, k * block_size + window)
-    idx, cnt = hs2.select_topk_window(sc, spec.q_pos0, k, window, block_size=block_size, max_sel=max_sel)
+    if topk_call:
+        assert block_size == 1
+        out, lse, sc, idx, cnt = hs2.full_attn_topk(blk.k, blk.v, blk.q, spec.q_pos0, k, window, max_sel=max_sel,
+                                                    k_scale=blk.ks, v_scale=blk.vs)
+    else:
+        out, lse, sc = hs2.full_attn_scores(blk.k, blk.v, blk.q, spec.q_pos0, k_scale=blk.ks, v_scale=blk.vs)
+        idx, cnt = hs2.select_topk_window(sc, spec.q_pos0, k, window, block_size=block_size, max_sel=max_sel)
     ws = torch.zeros(max(hs2.sparse_attn_workspace(spec.B, spec.Tq, spec.Hkv, spec.D, max_sel), 256),
                      dtype=torch.uint8, device="cuda")
     sp = []

@@ -4,6 +4,7 @@ top-1024 + window and the 16 x 64-token block baseline, 3 sparse layers.
 
 The fp64 oracle cannot redo the whole chunk in seconds (about 1e12 multiply-
 adds), so: the bridge rows are compared in full; full-layer outputs and scores
+(full layer and token top-k run as one call, as bench.py runs them)
 on sampled (t, g) units; both selections bit for bit against the oracle's
 selection on the GPU's own scores for every unit; sparse layers against the
 oracle on every unit's GPU index list."""
@@ -73,8 +74,9 @@ def test_chunk512_end_to_end(hs2):
 
     # ---- full layer, selection (token and block), sparse layers
     gu.log("[chunk512] GPU full layer + selections + sparse layers")
-    out, lse, sc = hs2.full_attn_scores(blk.k, blk.v, blk.q, spec.q_pos0)
-    idx, cnt = hs2.select_topk_window(sc, spec.q_pos0, spec.k, spec.window, max_sel=spec.max_sel)
+    # full layer and token top-k in one call, as bench.py runs the chunk
+    out, lse, sc, idx, cnt = hs2.full_attn_topk(blk.k, blk.v, blk.q, spec.q_pos0, spec.k, spec.window,
+                                                max_sel=spec.max_sel)
     bidx, bcnt = hs2.select_topk_window(sc, spec.q_pos0, spec.block_k, spec.window, block_size=spec.block_size,
                                         max_sel=spec.block_k * spec.block_size + spec.window)
     sp = [hs2.sparse_attn_gather(blk.k, blk.v, q, idx, cnt) for q in blk.qs]

@@ -32,11 +32,14 @@ def test_decode_config_end_to_end(hs2, name):
     inp = synth.make_inputs(spec)
     blk = gu.DeviceBlock(inp)
     runs = {}
-    for mode in (0, 1):  # three-kernel full layer, then the cooperative kernel
-        gu.log(f"[{name}] GPU block, full-layer mode {mode}")
+    # the launch configuration bench.py times (kernel-sequence full layer and
+    # top-k in one call, split gather), the separate calls with the
+    # one-workgroup gather, and the one call with the cooperative kernel
+    for label, mode, one_call in (("bench", 0, True), ("separate calls", 0, False), ("cooperative", 1, True)):
+        gu.log(f"[{name}] GPU block: {label}")
         hs2.full_attn_set_mode(mode)
         try:
-            runs[mode] = gu.run_block(hs2, blk, spec)
+            runs[label] = gu.run_block(hs2, blk, spec, split_gather=one_call, topk_call=one_call)
         finally:
             hs2.full_attn_set_mode(0)
     del blk
@@ -45,8 +48,8 @@ def test_decode_config_end_to_end(hs2, name):
     gu.log(f"[{name}] oracle full layer ({spec.B * spec.Tq * spec.Hkv} units)")
     o_or, l_or, s_or = oracle.full_attn_scores(inp.q_full, inp.k, inp.v, spec.q_pos0, k_scale=inp.k_scale,
                                                v_scale=inp.v_scale)
-    for mode, res in runs.items():
-        gu.log(f"[{name}] checking full-layer mode {mode}")
+    for label, res in runs.items():
+        gu.log(f"[{name}] checking: {label}")
         check_run(name, spec, inp, res, o_or, l_or, s_or)
 
 
