@@ -48,9 +48,6 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 #ifndef HS2_FUSED_SWIZZLE
 #define HS2_FUSED_SWIZZLE 0  // fused full layer: workgroup -> (unit, split) unit-fastest
 #endif
-#ifndef HS2_SCORE_HIST_R
-#define HS2_SCORE_HIST_R 4  // 4-position groups per thread of the score pass with the selection's first histogram
-#endif
 #ifndef HS2_SCAN_MIN_WAVES
 #define HS2_SCAN_MIN_WAVES 1  // occupancy floor handed to the register allocator
 #endif
@@ -2497,7 +2494,7 @@ __global__ void __launch_bounds__(256) score(ScoreParams P) {
 // workgroup, flushed with one global atomic per non-empty digit).  Counts are
 // integers, so the histogram equals the one the selection's own first pass
 // would build from the stored scores.
-template <int R>
+template <int R, int GC>
 __global__ void __launch_bounds__(256) score_hist(ScoreParams P) {
   __shared__ int32_t h[kHistBins];
   const int unit = blockIdx.y;
@@ -2509,23 +2506,13 @@ __global__ void __launch_bounds__(256) score_hist(ScoreParams P) {
   const int ncand = sel_ncand(p, P.sel_window);
   const int take = sel_take(ncand, P.sel_k, 1);
   float* dst = P.scores + (((int64_t)b * P.Tq + t) * P.Hkv + g) * P.N;
-  // head-outer, group-inner: each head's loads for all R groups are issued
-  // together (a thread waits G times, not G * R; measured faster than also
-  // prefetching the next head's loads)
   float s[R][4];
 #pragma unroll
   for (int q = 0; q < R; ++q) s[q][0] = s[q][1] = s[q][2] = s[q][3] = 0.f;
-  for (int i = 0; i < P.G; ++i) {
-    const int64_t row = (int64_t)unit * P.rows + i;
-    const float l2 = P.lse2[row];
-    u32x2_t w[R];
-    float mx[R];
+  int jc[R];  // group starts clamped to p: groups past p are zeroed below
 #pragma unroll
-    for (int q = 0; q < R; ++q) {
-      const int j4 = min(base + 4 * (threadIdx.x + 256 * q), p);  // clamped: groups past p are zeroed below
-      w[q] = *(const u32x2_t*)(P.lg16 + row * P.npad + (j4 & ~3));
-      mx[q] = P.lgmax[((int64_t)unit * (P.npad >> 5) + (j4 >> 5)) * P.rows + i];
-    }
+  for (int q = 0; q < R; ++q) jc[q] = min(base + 4 * (threadIdx.x + 256 * q), p);
+  auto add_head = [&](const u32x2_t (&w)[R], const float (&mx)[R], float l2) {
 #pragma unroll
     for (int q = 0; q < R; ++q) {
       const float c = mx[q] - l2;
@@ -2533,6 +2520,36 @@ __global__ void __launch_bounds__(256) score_hist(ScoreParams P) {
 #pragma unroll
       for (int e = 0; e < 4; ++e)
         s[q][e] += (code[e] == 65535u) ? 0.f : exp2_fast(__builtin_fmaf((float)code[e], -kCodeInv, c));
+    }
+  };
+  if constexpr (GC > 0) {
+    // every head's loads issued before any is used: one memory round trip
+    u32x2_t w[GC][R];
+    float mx[GC][R], l2[GC];
+#pragma unroll
+    for (int i = 0; i < GC; ++i) {
+      const int64_t row = (int64_t)unit * P.rows + i;
+      l2[i] = P.lse2[row];
+#pragma unroll
+      for (int q = 0; q < R; ++q) {
+        w[i][q] = *(const u32x2_t*)(P.lg16 + row * P.npad + (jc[q] & ~3));
+        mx[i][q] = P.lgmax[((int64_t)unit * (P.npad >> 5) + (jc[q] >> 5)) * P.rows + i];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < GC; ++i) add_head(w[i], mx[i], l2[i]);
+  } else {
+    // head-outer, group-inner: each head's loads for all R groups together
+    for (int i = 0; i < P.G; ++i) {
+      const int64_t row = (int64_t)unit * P.rows + i;
+      u32x2_t w[R];
+      float mx[R];
+#pragma unroll
+      for (int q = 0; q < R; ++q) {
+        w[q] = *(const u32x2_t*)(P.lg16 + row * P.npad + (jc[q] & ~3));
+        mx[q] = P.lgmax[((int64_t)unit * (P.npad >> 5) + (jc[q] >> 5)) * P.rows + i];
+      }
+      add_head(w, mx, P.lse2[row]);
     }
   }
   uint32_t key[4 * R];
@@ -2783,9 +2800,18 @@ hipError_t launch_score(const ScoreParams& p, int units, hipStream_t s) {
   TimedLaunch tl("score", s);
   if (p.sel_hist) {
     if (p.tpack != 1) return hipErrorInvalidValue;
-    constexpr int R = HS2_SCORE_HIST_R;
-    const int blocks = (p.N + 1024 * R - 1) / (1024 * R);
-    hipLaunchKernelGGL(score_hist<R>, dim3(blocks, units), dim3(256), 0, s, p);
+    // Large grids (the pass is near its memory bound): 4 position groups per
+    // thread and one head's loads at a time.  Small grids (latency-bound,
+    // fewer workgroups than CUs): 2 groups per thread and, for 8 heads per
+    // group, every head's loads at once (measured at 1M: 24.0 against 25.6 us;
+    // at 32K: 11.2 against 14.5 us).
+    const int blocks4 = (p.N + 4095) / 4096;
+    if ((int64_t)blocks4 * units >= 512 || p.G != 8) {
+      hipLaunchKernelGGL((score_hist<4, 0>), dim3(blocks4, units), dim3(256), 0, s, p);
+    } else {
+      const int blocks2 = (p.N + 2047) / 2048;
+      hipLaunchKernelGGL((score_hist<2, 8>), dim3(blocks2, units), dim3(256), 0, s, p);
+    }
   } else {
     const int blocks = (p.N + 1023) / 1024;
     hipLaunchKernelGGL(score, dim3(blocks, units), dim3(256), 0, s, p);
