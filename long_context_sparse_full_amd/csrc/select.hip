@@ -155,7 +155,7 @@ struct ChunkKeys {
 __device__ __forceinline__ void load_keys_first(const float* s, int base, int end, bool vec_ok, ChunkKeys& K) {
   // Every load is issued before any key is formed (a conversion right after
   // its own load makes each load wait for the previous one): measured faster
-  // for the collecting pass, whose work after the loads is longer.
+  // for the collecting pass, and for the histogram passes on small grids.
   float4 v[kKeysPerThread / 4];
   if (vec_ok && end - base == kSelChunk) {  // whole chunk (workgroup-uniform): unguarded 16-byte loads
 #pragma unroll
@@ -184,7 +184,7 @@ __device__ __forceinline__ void load_keys_first(const float* s, int base, int en
 }
 
 // Keys converted as their loads return: measured faster for the histogram
-// passes (at 2048 rows x 128K scores by 10%; within 2% at 4 rows).
+// passes on large grids (by 10% at 2048 rows x 128K scores).
 __device__ __forceinline__ void load_keys_inline(const float* s, int base, int end, bool vec_ok, ChunkKeys& K) {
   K.valid = 0;
 #pragma unroll
@@ -228,7 +228,9 @@ __device__ __forceinline__ void hist_keys(const ChunkKeys& K, uint32_t prefix, i
 // PASS 2 also stores, per chunk, the count of keys above the 24-bit prefix and
 // the suffix sums of its 256-bin histogram, from which the emit pass gets every
 // chunk's counts above and equal to the final threshold.
-template <int PASS>
+// FIRST: all score loads issued before any key is formed (measured faster on
+// grids of up to about two workgroups per CU, slower on large ones).
+template <int PASS, bool FIRST>
 __global__ void __launch_bounds__(256) sel_hist(SelectParams P) {
   using DG = Digit<PASS>;
   __shared__ int32_t h[DG::BINS];
@@ -245,7 +247,10 @@ __global__ void __launch_bounds__(256) sel_hist(SelectParams P) {
   if (base >= ncand) return;
   const int end = min(base + kSelChunk, ncand);
   ChunkKeys K;
-  load_keys_inline(P.scores + (int64_t)u * P.N, base, end, (P.N & 3) == 0, K);
+  if constexpr (FIRST)
+    load_keys_first(P.scores + (int64_t)u * P.N, base, end, (P.N & 3) == 0, K);
+  else
+    load_keys_inline(P.scores + (int64_t)u * P.N, base, end, (P.N & 3) == 0, K);
   int32_t* hist = P.hist + (int64_t)u * 3 * kHistBins;
   uint32_t prefix = 0;
   if constexpr (PASS > 0) {
@@ -921,8 +926,13 @@ hipError_t launch_select(const SelectParams& p_in, hipStream_t s) {
   } while (0)
   if (!(p.pre_hist0 && p.block_size == 1)) HS2_L("select_init", sel_init, dim3(p.units));
   if (p.block_size == 1) {
-    if (!p.pre_hist0) HS2_L("select_hist", sel_hist<0>, grid_c);
-    HS2_L("select_hist", sel_hist<1>, grid_c);
+    const bool small = p.units * p.nchunks <= 512;  // up to about two workgroups per CU: latency-bound passes
+    if (!p.pre_hist0) {
+      if (small) HS2_L("select_hist", (sel_hist<0, true>), grid_c);
+      else HS2_L("select_hist", (sel_hist<0, false>), grid_c);
+    }
+    if (small) HS2_L("select_hist", (sel_hist<1, true>), grid_c);
+    else HS2_L("select_hist", (sel_hist<1, false>), grid_c);
     // The collected path saves two full reads of the scores but adds two
     // launches: taken where the passes are throughput-bound.
     if (p.collected) {
@@ -943,7 +953,8 @@ hipError_t launch_select(const SelectParams& p_in, hipStream_t s) {
       hipLaunchKernelGGL(sel_finish, dim3(p.units), dim3(256), lds, s, p);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    HS2_L("select_hist", sel_hist<2>, grid_c);
+    if (small) HS2_L("select_hist", (sel_hist<2, true>), grid_c);
+    else HS2_L("select_hist", (sel_hist<2, false>), grid_c);
     HS2_L("select_emit", sel_emit, grid_c);
   } else {
     const dim3 grid_t((p.N + kMassTile - 1) / kMassTile, p.units);
