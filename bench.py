@@ -91,9 +91,6 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--split-gather", type=int, default=1, choices=(0, 1),
                     help="sparse layers with the split-list gather (1, default) or one workgroup per (b, t, g) (0)")
-    ap.add_argument("--full-mode", type=int, default=0, choices=(0, 1),
-                    help="full-layer execution (hs2_full_attn_set_mode): 0 automatic (default), 1 cooperative "
-                         "kernel wherever possible (with the selection inside)")
     ap.add_argument("--topk-call", type=int, default=1, choices=(0, 1),
                     help="full layer + selection through hs2_full_attn_topk (1, default) or two calls (0)")
     ap.add_argument("--copy-probe", action="store_true",
@@ -129,7 +126,6 @@ def main():
                 f"({2 * n / c0.elapsed_time(c1) / 1e6:.1f} GB/s)")
         print(json.dumps({"copy_probe_bytes": n, "ms": c0.elapsed_time(c1)}), flush=True)
         return
-    hs2.full_attn_set_mode(args.full_mode)
     spec = synth.config(args.config)
     if spec.Tq != 1:
         return bench_chunk(spec, args)
@@ -159,8 +155,6 @@ def main():
     sp_lse = [torch.empty((B, Tq, Hq), dtype=torch.float32, device="cuda") for _ in qs]
     ws_gather = torch.zeros(max(hs2.sparse_attn_workspace(B, Tq, Hkv, D, spec.max_sel), 256), dtype=torch.uint8,
                             device="cuda")  # zero-filled once; every call leaves its counters at zero
-
-    ws_topk = torch.empty(hs2.full_attn_topk_workspace(k, v, Tq, Hq), dtype=torch.uint8, device="cuda")
 
     def step(layer1_events=None):
         if args.topk_call:
@@ -250,33 +244,30 @@ def main():
                  "cold_sparse_layer1_gbps": round(gathered / (pct(l1_us, 0.5) * 1e-6) / 1e9, 1)}
     log(f"[bench] step distribution: {json.dumps(step_dist)}")
 
-    # the same step captured once in a HIP graph and replayed (the default
-    # kernel sequence has no memsets, allocations or host syncs; the
-    # cooperative kernel's per-launch epoch would be frozen by a capture)
-    graph = None
-    if args.full_mode == 0:
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            step()  # warm the side stream
-        torch.cuda.current_stream().wait_stream(side)
-        torch.cuda.synchronize()
-        with torch.cuda.graph(g):
-            step()
-        for _ in range(args.warmup):
-            g.replay()
-        torch.cuda.synchronize()
-        ga, gb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        ga.record()
-        for _ in range(args.steps):
-            g.replay()
-        gb.record()
-        torch.cuda.synchronize()
-        graph = {"us_per_step": round(ga.elapsed_time(gb) * 1e3 / args.steps, 2), "steps": args.steps}
-        log(f"[bench] hip graph replay: {graph['us_per_step']} us/step")
-        del g
+    # the same step captured once in a HIP graph and replayed (the step has no
+    # memsets, allocations or host syncs)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()  # warm the side stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(args.warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    ga, gb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ga.record()
+    for _ in range(args.steps):
+        g.replay()
+    gb.record()
+    torch.cuda.synchronize()
+    graph = {"us_per_step": round(ga.elapsed_time(gb) * 1e3 / args.steps, 2), "steps": args.steps}
+    log(f"[bench] hip graph replay: {graph['us_per_step']} us/step")
+    del g
 
     # per-kernel durations from HIP events bracketing each launch on its stream
     hs2.timing_reset()
@@ -342,7 +333,7 @@ def main():
         "vs_baseline": None,
         "dtype": {"fp8": "fp8e4m3-kv/bf16-q/f32-acc", "bf16": "bf16/f32-acc", "f32": "f32"}[spec.kv_dtype],
         "data": "synthetic (seeded; planted needle keys)",
-        "config": {"workload": spec.name, "full_layer": {0: "auto", 1: "cooperative", 3: "kernels"}[args.full_mode],
+        "config": {"workload": spec.name,
                    "full_and_select": "one call" if args.topk_call else "two calls", "B": B, "context": N, "Tq": Tq, "q_heads": Hq, "kv_heads": Hkv,
                    "head_dim": D, "kv_dtype": spec.kv_dtype, "top_k": spec.k, "window": spec.window,
                    "sparse_layers": spec.n_sparse},

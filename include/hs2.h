@@ -21,6 +21,9 @@
  *     library never allocates, frees or retains a pointer beyond the call.
  *   - Calls are asynchronous on `stream`; results are valid once the stream
  *     reaches the call.  Calls never synchronise, print or abort.
+ *   - The library keeps no state of its own beyond the per-kernel timing
+ *     records (hs2_timing_*); every call is thread-safe.  Calls that share a
+ *     workspace must be ordered on one stream.
  *   - Every call validates its arguments before any launch and returns an
  *     hs2 status; on failure hs2_last_error() holds a thread-local message.
  *   - Layouts are dense row-major unless strides are given:
@@ -48,7 +51,7 @@ extern "C" {
 struct ihipStream_t;
 typedef struct ihipStream_t* hipStream_t;
 
-#define HS2_ABI_VERSION 1
+#define HS2_ABI_VERSION 2
 
 typedef enum { HS2_F32 = 0, HS2_BF16 = 1, HS2_FP8_E4M3FN = 2 } hs2_dtype;
 
@@ -66,7 +69,7 @@ enum {
  * cache accounting -- zgeo.com.cn comparison table), k_scale and v_scale hold
  * one fp32 scale per (b, kv head), index b*Hkv + h, and the cache value is
  * decode(code) * scale; they are ignored (may be NULL) otherwise.  The
- * attention calls only read k and v; hs2_kv_bridge writes them. */
+ * attention calls only read through this descriptor. */
 typedef struct {
   const void* k;
   const void* v;
@@ -76,6 +79,18 @@ typedef struct {
   const float* v_scale;
   int32_t B, Hkv, N, D;
 } hs2_kv_desc;
+
+/* The same cache seen by a call that writes it (hs2_kv_bridge): same fields,
+ * layout and rules as hs2_kv_desc, with writable pointers. */
+typedef struct {
+  void* k;
+  void* v;
+  int32_t dtype; /* hs2_dtype */
+  int64_t stride_b, stride_h, stride_n;
+  float* k_scale;
+  float* v_scale;
+  int32_t B, Hkv, N, D;
+} hs2_kv_out_desc;
 
 int hs2_abi_version(void);
 const char* hs2_status_string(int status);
@@ -95,17 +110,14 @@ const char* hs2_last_error(void);
  * hs2_full_attn_scores_workspace(kv, Tq, Hq) bytes, 256-byte aligned, device
  * memory; its contents on entry are ignored.  Two calls that share one
  * workspace must not run concurrently (different streams).
- * Execution: a scan, a merge and a score kernel; or, selected with
- * hs2_full_attn_set_mode(1) for bf16 and FP8 caches when the device can
- * co-schedule one workgroup per compute unit for every (b, query pack, kv
- * head), a single cooperative kernel (scan, device-wide barrier, output merge
- * and scores).  With many query tokens (bf16 or FP8 cache, 4, 8 or 16 query
- * heads per kv head, at least 4 packs of 16/G tokens per (b, kv head), as in
- * a 512-token chunk) the scan is a matrix-core pass over K/V tiles staged in
- * LDS, and the score kernel recomputes the logits against the merged
- * log-sum-exp instead of reading stored codes.  All compute the same
- * quantities to the same bounds.  Rows of the cache must be 16-byte aligned;
- * the chunk kernels also need 32 rows to span less than 2 GiB
+ * Execution: a scan, a merge and a score kernel.  With many query tokens
+ * (bf16 or FP8 cache, 4, 8 or 16 query heads per kv head, at least 4 packs of
+ * 16/G tokens per (b, kv head), as in a 512-token chunk) the scan is a
+ * matrix-core pass over K/V tiles staged in LDS, and the score kernel
+ * recomputes the logits against the merged log-sum-exp instead of reading
+ * stored codes.  Both compute the same quantities to the same bounds.  Rows
+ * of the cache must be 16-byte aligned; the chunk kernels also need 32 rows
+ * to span less than 2 GiB
  * (HS2_ERR_HIP otherwise). */
 size_t hs2_full_attn_scores_workspace(const hs2_kv_desc* kv, int32_t Tq, int32_t Hq);
 int hs2_full_attn_scores(const hs2_kv_desc* kv, const void* q, hs2_dtype q_dtype, int32_t Tq,
@@ -178,7 +190,7 @@ int hs2_sparse_attn_gather_ws(const hs2_kv_desc* kv, const void* q, hs2_dtype q_
  * positive), rounded to nearest even with magnitudes above 448 saturating to
  * 448.  Requires d_model % 64 == 0. */
 int hs2_kv_bridge(const void* hidden, int32_t T, int32_t d_model, const void* w_kv,
-                  const hs2_kv_desc* kv_out, int32_t batch_index, int32_t pos0, hipStream_t stream);
+                  const hs2_kv_out_desc* kv_out, int32_t batch_index, int32_t pos0, hipStream_t stream);
 
 /* Diagnostic: decode n OCP E4M3FN codes (device array) to fp32 through the
  * same in-register conversion the attention kernels use.  Lets a test compare
@@ -195,35 +207,25 @@ int hs2_debug_stream_read(const void* buf, size_t bytes, uint32_t* out, int32_t 
 
 /* Full layer and token selection in one call: the results of
  * hs2_full_attn_scores followed by hs2_select_topk_window with block_size 1
- * (same layouts, rules and requirements; both passages above).  With
- * hs2_full_attn_set_mode(1), for bf16 and FP8 caches with one query token
- * (Tq = 1) and at most 8 query heads per kv head, when the device co-schedules
- * one workgroup per compute unit for every (b, kv head) and each workgroup's
- * scores fit its registers, both run inside one cooperative kernel: the
- * scores stay on chip for the selection (they are still written to
- * `scores`).  Otherwise the two calls run in sequence.  Workspace: at least
- * hs2_full_attn_topk_workspace() bytes, 256-byte aligned. */
+ * (same layouts, rules and requirements; both passages above).  With one
+ * query token per (b, kv head) unit, the full layer's merge kernel sets the
+ * selection's rows up and its score kernel counts the selection's first radix
+ * digit while writing the scores, which saves the selection two passes over
+ * them.  Workspace: at least hs2_full_attn_topk_workspace() bytes, 256-byte
+ * aligned. */
 size_t hs2_full_attn_topk_workspace(const hs2_kv_desc* kv, int32_t Tq, int32_t Hq);
 int hs2_full_attn_topk(const hs2_kv_desc* kv, const void* q, hs2_dtype q_dtype, int32_t Tq, int32_t Hq,
                        int32_t q_pos0, float softmax_scale, void* out, float* lse, float* scores, int32_t k,
                        int32_t window, int32_t* idx, int32_t* count, int32_t max_sel, void* workspace,
                        size_t workspace_bytes, hipStream_t stream);
 
-/* Process-wide choice of the full-layer execution (a tuning and testing
- * knob): mode 0 (default) automatic -- the three-kernel full layer (and for
- * hs2_full_attn_topk the select kernels after it); mode 1 the single
- * cooperative kernel wherever possible (with the selection inside for
- * hs2_full_attn_topk); mode 2 as 1 with the on-chip code store limited to one
- * tile per workgroup (later tiles' codes go through the workspace, as they
- * do at 1M context); mode 3 never the cooperative kernel.  Returns
- * HS2_ERR_INVALID_ARG for other values. */
-int hs2_full_attn_set_mode(int mode);
-
-/* Per-kernel timing with HIP events on the launch stream (off by default).
- * While enabled, every kernel launch of the library is bracketed by an event
- * pair on its stream.  hs2_timing_collect synchronises those events and
- * returns, for launches of the named kernel since the last reset, the summed
- * milliseconds and the launch count.  Names: see hs2_timing_kernel_name. */
+/* Per-kernel timing with HIP events on the launch stream (off by default; a
+ * measurement aid, process-wide).  While enabled, every kernel launch of the
+ * library is bracketed by an event pair on its stream.  hs2_timing_collect
+ * synchronises those events and returns, for launches of the named kernel
+ * since the last reset, the summed milliseconds and the launch count;
+ * hs2_timing_reset waits for and destroys the recorded events.  Names: see
+ * hs2_timing_kernel_name. */
 int hs2_timing_enable(int on);
 int hs2_timing_reset(void);
 int hs2_timing_collect(const char* kernel_name, double* total_ms, int32_t* launches);

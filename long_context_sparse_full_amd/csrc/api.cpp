@@ -8,7 +8,6 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
-#include <ctime>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -67,11 +66,29 @@ int check_q(const hs2_kv_desc* kv, const void* q, int q_dtype, int Tq, int Hq, c
   return HS2_OK;
 }
 
+// The read-only view of a writable cache descriptor (for validation).
+hs2_kv_desc as_read_desc(const hs2_kv_out_desc& o) {
+  hs2_kv_desc d{};
+  d.k = o.k;
+  d.v = o.v;
+  d.dtype = o.dtype;
+  d.stride_b = o.stride_b;
+  d.stride_h = o.stride_h;
+  d.stride_n = o.stride_n;
+  d.k_scale = o.k_scale;
+  d.v_scale = o.v_scale;
+  d.B = o.B;
+  d.Hkv = o.Hkv;
+  d.N = o.N;
+  d.D = o.D;
+  return d;
+}
+
 struct FullPlan {
   bool chunk;  // multi-query chunk kernels (MFMA pass + merge + score recompute)
   int tpack, n_tpacks, rows, units, nsplit, split_len;
   int64_t npad;
-  size_t off_ml, off_o, off_lse2, off_lg16, off_lgmax, off_flags, total;
+  size_t off_ml, off_o, off_lse2, off_lg16, off_lgmax, total;
 };
 
 // Position splits: about HS2_SCAN_TARGET_WGS workgroups in total (4 per CU on
@@ -118,32 +135,8 @@ FullPlan plan_full(const hs2_kv_desc* kv, int Tq, int Hq) {
   off = a256(off + code_units * p.rows * (size_t)p.npad * sizeof(uint16_t));
   p.off_lgmax = off;
   off = a256(off + code_units * p.rows * (size_t)(p.npad / 32) * sizeof(float));
-  p.off_flags = off;  // fused path: per grid barrier one word per workgroup (<= units * nsplit)
-  off = a256(off + (size_t)hs2::kFusedBarriers * p.units * p.nsplit * sizeof(uint64_t));
   p.total = off;
   return p;
-}
-
-// Full-layer path selection (process-wide):
-//   0 = automatic: the scan + combine + score kernels, then (for
-//       hs2_full_attn_topk) the select kernels -- the fastest form measured at
-//       1M context, where the cooperative launch and the selection's grid
-//       barriers cost more than the scratch traffic they save;
-//   1 = the fused cooperative kernel wherever the device can co-schedule it;
-//   2 = as 1 with LDS code storage cut to one tile per workgroup (every later
-//       tile takes the global-buffer route; exercises it at small sizes);
-//   3 = never fused.
-std::atomic<int> g_full_mode{0};
-
-// Grid-barrier epochs: unique per fused launch in this process, never 0.
-uint64_t next_epoch() {
-  static std::atomic<uint64_t> ctr{((uint64_t)(uintptr_t)&ctr << 16) ^ ((uint64_t)time(nullptr) << 40) ^
-                                   0x9e3779b97f4a7c15ull};
-  uint64_t e;
-  do {
-    e = ctr.fetch_add(1, std::memory_order_relaxed) + 1;
-  } while (e == 0);
-  return e;
 }
 
 struct SelPlan {
@@ -191,42 +184,36 @@ const char* const kKernelNames[] = {"full_scan",   "combine",     "score",      
                                     "select_block_mass", "select_block_pick", "sparse_gather", "kv_bridge", "stream_read",
                                     "chunk_full",  "chunk_score", nullptr};
 
+// Timing state (only while hs2_timing_enable(1) is in force): the event pairs
+// of the launches since the last reset.  Events are created per launch and
+// destroyed by hs2_timing_reset, so none outlives the caller's reset.
 std::mutex g_tmu;
-bool g_timing = false;
+std::atomic<bool> g_timing{false};
 struct TimingRec {
   const char* name;
   hipEvent_t a, b;
 };
 std::vector<TimingRec> g_recs;
-std::vector<hipEvent_t> g_pool;
-
-hipEvent_t take_event() {
-  if (!g_pool.empty()) {
-    hipEvent_t e = g_pool.back();
-    g_pool.pop_back();
-    return e;
-  }
-  hipEvent_t e = nullptr;
-  if (hipEventCreate(&e) != hipSuccess) return nullptr;
-  return e;
-}
 
 }  // namespace
 
 namespace hs2 {
 TimedLaunch::TimedLaunch(const char* name, hipStream_t s) : name_(name), s_(s), ev0_(nullptr), ev1_(nullptr) {
-  if (!g_timing) return;
-  std::lock_guard<std::mutex> lk(g_tmu);
-  hipEvent_t a = take_event(), b = take_event();
-  if (!a || !b) return;
+  if (!g_timing.load(std::memory_order_acquire)) return;
+  hipEvent_t a = nullptr, b = nullptr;
+  if (hipEventCreate(&a) != hipSuccess) return;
+  if (hipEventCreate(&b) != hipSuccess) {
+    (void)hipEventDestroy(a);
+    return;
+  }
   ev0_ = a;
   ev1_ = b;
-  hipEventRecord(a, s);
+  (void)hipEventRecord(a, s);
 }
 TimedLaunch::~TimedLaunch() {
   if (!ev0_) return;
+  (void)hipEventRecord((hipEvent_t)ev1_, s_);
   std::lock_guard<std::mutex> lk(g_tmu);
-  hipEventRecord((hipEvent_t)ev1_, s_);
   g_recs.push_back(TimingRec{name_, (hipEvent_t)ev0_, (hipEvent_t)ev1_});
 }
 }  // namespace hs2
@@ -234,12 +221,6 @@ TimedLaunch::~TimedLaunch() {
 extern "C" {
 
 int hs2_abi_version(void) { return HS2_ABI_VERSION; }
-
-int hs2_full_attn_set_mode(int mode) {
-  if (mode < 0 || mode > 3) return fail(HS2_ERR_INVALID_ARG, "hs2_full_attn_set_mode: mode must be 0..3");
-  g_full_mode.store(mode, std::memory_order_relaxed);
-  return HS2_OK;
-}
 
 const char* hs2_status_string(int status) {
   switch (status) {
@@ -262,27 +243,18 @@ size_t hs2_full_attn_scores_workspace(const hs2_kv_desc* kv, int32_t Tq, int32_t
 }  // extern "C"
 
 namespace {
-// Selection folded into the fused full layer (hs2_full_attn_topk).
-struct SelFuse {
-  int32_t k, window, max_sel;
-  int32_t* idx;
-  int32_t* count;
-  void* ws;  // fused-selection region: histograms, then step counts
-  bool done = false;
-  // kernel sequence: the merge set the selection up and the score pass built
-  // its first histogram (layout of plan_select over ws)
+// Token selection prepared by the full layer (hs2_full_attn_topk): with one
+// query token per unit, the merge sets the selection rows up and the score
+// pass builds the first radix histogram (layout of plan_select over ws).
+struct SelPrep {
+  int32_t k, window;
+  void* ws;
   bool hist0_done = false;
 };
 
-size_t sel_fuse_hist_bytes(int units) { return a256((size_t)units * 3 * hs2::kHistBins * sizeof(int32_t)); }
-int sel_fuse_nsteps(int N) { return (int)cdiv(N, 128); }  // the smallest workgroup step (4 waves)
-size_t sel_fuse_bytes(int units, int N) {
-  return sel_fuse_hist_bytes(units) + a256((size_t)units * sel_fuse_nsteps(N) * 2 * sizeof(int32_t));
-}
-
 int full_layer(const hs2_kv_desc* kv, const void* q, hs2_dtype q_dtype, int32_t Tq, int32_t Hq, int32_t q_pos0,
                float softmax_scale, void* out, float* lse, float* scores, void* workspace, size_t workspace_bytes,
-               hipStream_t stream, SelFuse* sel);
+               hipStream_t stream, SelPrep* sel);
 // hs2_select_topk_window; pre_hist0: the row state and first histogram are
 // already built (full layer's merge and score pass)
 int select_impl(const float* scores, int32_t B, int32_t Tq, int32_t Hkv, int32_t N, int32_t q_pos0, int32_t k,
@@ -304,7 +276,7 @@ int hs2_full_attn_scores(const hs2_kv_desc* kv, const void* q, hs2_dtype q_dtype
 namespace {
 int full_layer(const hs2_kv_desc* kv, const void* q, hs2_dtype q_dtype, int32_t Tq, int32_t Hq, int32_t q_pos0,
                float softmax_scale, void* out, float* lse, float* scores, void* workspace, size_t workspace_bytes,
-               hipStream_t stream, SelFuse* sel) {
+               hipStream_t stream, SelPrep* sel) {
   int st = check_kv(kv, "hs2_full_attn_scores");
   if (st) return st;
   if ((st = check_q(kv, q, q_dtype, Tq, Hq, "hs2_full_attn_scores"))) return st;
@@ -349,7 +321,6 @@ int full_layer(const hs2_kv_desc* kv, const void* q, hs2_dtype q_dtype, int32_t 
   p.npad = pl.npad;
   hipError_t e;
 
-  // fused path: one workgroup per CU slot, nsplit of them per unit
   if (pl.chunk) {  // many query tokens: MFMA pass -> merge -> score recompute
     hs2::CombineParams c{};
     c.part_ml = p.part_ml;
@@ -374,51 +345,6 @@ int full_layer(const hs2_kv_desc* kv, const void* q, hs2_dtype q_dtype, int32_t 
     p.scores = scores;
     if ((e = hs2::launch_chunk_score(p, kv->dtype, stream)) != hipSuccess) return hip_fail(e, "chunk_score launch");
     return HS2_OK;
-  }
-
-  const int mode = g_full_mode.load(std::memory_order_relaxed);
-  const bool want_fused = mode == 1 || mode == 2;
-  const int nwg = want_fused ? hs2::fused_max_workgroups(kv->dtype, kv->D) : 0;
-  if (nwg >= pl.units) {
-    const int W = hs2::fused_waves(kv->dtype, kv->D);
-    const int64_t step = 32 * W;
-    const int64_t su = std::max<int64_t>(1, std::min<int64_t>({nwg / pl.units, pl.nsplit, cdiv(kv->N, step)}));
-    const int64_t scan_steps = cdiv((int64_t)q_pos0 + Tq, step);  // steps covering [0, last query position]
-    const int64_t need = cdiv(scan_steps, su) * W;                 // tiles of the busiest workgroup
-    const int64_t fit = (hs2::kFusedLdsBytes - hs2::fused_merge_bytes(pl.rows, kv->D) - 256) /
-                        hs2::fused_slot_bytes(pl.rows);
-    // the selection keeps every score of a workgroup in registers: 4 octets per
-    // thread, i.e. at most kFusedSelMaxSteps steps per workgroup over [0, N)
-    const int64_t my_steps = cdiv(cdiv(kv->N, step), su);
-    const bool fuse_sel = sel != nullptr && pl.tpack == 1 && p.G <= 8 && my_steps <= hs2::kFusedSelMaxSteps;
-    hs2::ScanParams f = p;
-    f.nsplit = (int)su;
-    f.lds_slots = (int)std::min(need, mode == 2 ? (int64_t)1 : fit);
-    f.scores = scores;
-    f.out = out;
-    f.lse = lse;
-    f.flags = at<uint64_t>(workspace, pl.off_flags);
-    f.epoch = next_epoch();
-    if (fuse_sel) {
-      f.sel_k = sel->k;
-      f.sel_window = sel->window;
-      f.sel_nsteps = (int)cdiv(kv->N, step);
-      f.sel_hist = static_cast<int32_t*>(sel->ws);
-      f.sel_stepcnt = at<int32_t>(sel->ws, sel_fuse_hist_bytes(pl.units));
-      f.idx = sel->idx;
-      f.count = sel->count;
-      f.max_sel = sel->max_sel;
-    }
-    if (sel == nullptr || fuse_sel) {
-      e = hs2::launch_scan_fused(f, kv->dtype, pl.units, stream);
-      if (e == hipSuccess) {
-        if (sel) sel->done = fuse_sel;
-        return HS2_OK;
-      }
-      if (e != hipErrorNotSupported && e != hipErrorCooperativeLaunchTooLarge)
-        return hip_fail(e, "fused full layer launch");
-      (void)hipGetLastError();  // the device declined the cooperative grid: use the kernel sequence
-    }
   }
 
   e = hs2::launch_scan(p, kv->dtype, false, true, stream);
@@ -472,6 +398,16 @@ int full_layer(const hs2_kv_desc* kv, const void* q, hs2_dtype q_dtype, int32_t 
   s.sel_hist = sel_hist;
   s.sel_k = pre_sel ? sel->k : 0;
   s.sel_window = pre_sel ? sel->window : 0;
+  s.q = q;
+  s.Hq = Hq;
+  s.D = kv->D;
+  s.kv_dtype = kv->dtype;
+  s.k = kv->k;
+  s.sb = kv->stride_b;
+  s.sh = kv->stride_h;
+  s.sn = kv->stride_n;
+  s.k_scale = kv->k_scale;
+  s.scale_log2 = p.scale_log2;
   if ((e = hs2::launch_score(s, pl.units, stream)) != hipSuccess) return hip_fail(e, "score launch");
   if (pre_sel) sel->hist0_done = true;
   return HS2_OK;
@@ -484,7 +420,7 @@ size_t hs2_full_attn_topk_workspace(const hs2_kv_desc* kv, int32_t Tq, int32_t H
   if (!kv || kv->B <= 0 || kv->Hkv <= 0 || kv->N <= 0 || kv->D <= 0 || Tq <= 0 || Hq <= 0 || Hq % kv->Hkv) return 0;
   const FullPlan pl = plan_full(kv, Tq, Hq);
   const size_t sel = plan_select(kv->B, Tq, kv->Hkv, kv->N, 1).total;
-  return pl.total + std::max(sel, sel_fuse_bytes(kv->B * Tq * kv->Hkv, kv->N));
+  return pl.total + sel;
 }
 
 int hs2_full_attn_topk(const hs2_kv_desc* kv, const void* q, hs2_dtype q_dtype, int32_t Tq, int32_t Hq,
@@ -507,10 +443,10 @@ int hs2_full_attn_topk(const hs2_kv_desc* kv, const void* q, hs2_dtype q_dtype, 
     return fail(HS2_ERR_WORKSPACE, "hs2_full_attn_topk: workspace needs " + std::to_string(need_ws) + " bytes");
   const size_t full_bytes = plan_full(kv, Tq, Hq).total;
   void* rest = static_cast<char*>(workspace) + full_bytes;
-  SelFuse sel{k, window, max_sel, idx, count, rest};
+  SelPrep sel{k, window, rest};
   st = full_layer(kv, q, q_dtype, Tq, Hq, q_pos0, softmax_scale, out, lse, scores, workspace, full_bytes, stream,
                   &sel);
-  if (st || sel.done) return st;
+  if (st) return st;
   return select_impl(scores, kv->B, Tq, kv->Hkv, kv->N, q_pos0, k, window, 1, idx, count, max_sel, rest,
                      workspace_bytes - full_bytes, stream, sel.hist0_done);
 }
@@ -723,9 +659,11 @@ int hs2_sparse_attn_gather_ws(const hs2_kv_desc* kv, const void* q, hs2_dtype q_
   return HS2_OK;
 }
 
-int hs2_kv_bridge(const void* hidden, int32_t T, int32_t d_model, const void* w_kv, const hs2_kv_desc* kv_out,
+int hs2_kv_bridge(const void* hidden, int32_t T, int32_t d_model, const void* w_kv, const hs2_kv_out_desc* kv_out,
                   int32_t batch_index, int32_t pos0, hipStream_t stream) {
-  int st = check_kv(kv_out, "hs2_kv_bridge");
+  if (!kv_out) return fail(HS2_ERR_INVALID_ARG, "hs2_kv_bridge: kv_out descriptor is NULL");
+  const hs2_kv_desc view = as_read_desc(*kv_out);
+  int st = check_kv(&view, "hs2_kv_bridge");
   if (st) return st;
   if (kv_out->dtype != HS2_BF16 && kv_out->dtype != HS2_FP8_E4M3FN)
     return fail(HS2_ERR_UNSUPPORTED, "hs2_kv_bridge: output cache must be BF16 or FP8_E4M3FN");
@@ -741,8 +679,8 @@ int hs2_kv_bridge(const void* hidden, int32_t T, int32_t d_model, const void* w_
   const bool fp8 = kv_out->dtype == HS2_FP8_E4M3FN;
   const size_t esz = fp8 ? 1 : 2;
   hs2::BridgeOut o{};
-  o.k = static_cast<char*>(const_cast<void*>(kv_out->k)) + off * esz;
-  o.v = static_cast<char*>(const_cast<void*>(kv_out->v)) + off * esz;
+  o.k = static_cast<char*>(kv_out->k) + off * esz;
+  o.v = static_cast<char*>(kv_out->v) + off * esz;
   o.sn = kv_out->stride_n;
   o.sh = kv_out->stride_h;
   o.k_scale = fp8 ? kv_out->k_scale + (int64_t)batch_index * kv_out->Hkv : nullptr;
@@ -769,17 +707,16 @@ int hs2_debug_stream_read(const void* buf, size_t bytes, uint32_t* out, int32_t 
 }
 
 int hs2_timing_enable(int on) {
-  std::lock_guard<std::mutex> lk(g_tmu);
-  g_timing = on != 0;
+  g_timing.store(on != 0, std::memory_order_release);
   return HS2_OK;
 }
 
 int hs2_timing_reset(void) {
   std::lock_guard<std::mutex> lk(g_tmu);
   for (auto& r : g_recs) {
-    hipEventSynchronize(r.b);
-    g_pool.push_back(r.a);
-    g_pool.push_back(r.b);
+    (void)hipEventSynchronize(r.b);
+    (void)hipEventDestroy(r.a);
+    (void)hipEventDestroy(r.b);
   }
   g_recs.clear();
   return HS2_OK;

@@ -35,23 +35,6 @@ typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
-// Compile-time tuning of the full-layer scan (the defaults are the measured best on gfx950).
-#ifndef HS2_SCAN_NT
-#define HS2_SCAN_NT 0  // non-temporal K/V loads in the streaming scan (measured slower on gfx950)
-#endif
-#ifndef HS2_SCAN_INTERLEAVE
-#define HS2_SCAN_INTERLEAVE 1  // split s takes workgroup tiles s, s+nsplit, ... (all splits sweep together)
-#endif
-#ifndef HS2_FUSED_ACQUIRE
-#define HS2_FUSED_ACQUIRE 0  // grid barrier ends with a device-scope acquire (cache invalidation)
-#endif
-#ifndef HS2_FUSED_SWIZZLE
-#define HS2_FUSED_SWIZZLE 0  // fused full layer: workgroup -> (unit, split) unit-fastest
-#endif
-#ifndef HS2_SCAN_MIN_WAVES
-#define HS2_SCAN_MIN_WAVES 1  // occupancy floor handed to the register allocator
-#endif
-
 constexpr float kNegInf = -__builtin_inff();
 // lazy reference maximum of the online softmax in the multi-query chunk kernel
 constexpr float kLazyMax = 8.f;
@@ -100,11 +83,15 @@ __device__ __forceinline__ float sum_x32(float x) {
 }
 
 // 16-bit code of a log2-domain logit x below its tile maximum m:
-// round((m - x) * 2^12), saturated; 65535 stands for "at least 16 below m" and
-// decodes to a zero contribution.  Step 2^-12 bounds the relative error of
-// 2^x by 2^-13 * ln 2 < 8.5e-5.
+// round((m - x) * 2^12), saturated; 65535 stands for "at least 16 below m".
+// Step 2^-12 bounds the relative error of 2^x by 2^-13 * ln 2 < 8.5e-5.  The
+// score pass takes the term of a saturated code as zero only when it is
+// provably negligible (the probability of the tile maximum below
+// 2^kExactFloor, so the term is below 2^(kExactFloor - 16)); otherwise it
+// recomputes that logit in fp32 from the query and the cache row.
 constexpr float kCodeScale = 4096.f;
 constexpr float kCodeInv = 1.f / 4096.f;
+constexpr float kExactFloor = -24.f;
 __device__ __forceinline__ uint32_t logit_code(float m, float x) {
   const float d = (m - x) * kCodeScale;  // >= 0; +inf when x = -inf
   return d < 65534.5f ? (uint32_t)__builtin_rintf(d) : 65535u;
@@ -194,14 +181,10 @@ struct WaveState {
 // One 32-position tile: decode, QK^T, mask (only when the tile crosses the
 // causal / range limit), logits, online softmax, PV.  Positions of this lane's
 // logits: j0 + 16*hh + 4*g4 + ii.
-// RET_CODES: instead of storing, hand this lane's codes (positions
-// j0 + 4*g4 + {0..3} in cw[0..1], j0 + 16 + 4*g4 + {0..3} in cw[2..3], two per
-// dword) and the row's tile maximum back to the caller.
-template <bool FP8, int D, bool WRITE_LOGITS, bool RET_CODES = false>
+template <bool FP8, int D, bool WRITE_LOGITS>
 __device__ __forceinline__ void compute_tile(const RawTile<FP8, D>& R, const u32x4_t (&qf)[D / 32], float cs, int j0,
                                              int jlim, bool need_mask, int g4, uint16_t* lg, float* lgm,
-                                             int lgm_stride, WaveState<D>& S, uint32_t* cw = nullptr,
-                                             float* tmax_out = nullptr) {
+                                             int lgm_stride, WaveState<D>& S) {
   constexpr int NC = D / 32, VE = D / 16;
   u32x4_t kf[2][NC];
   uint32_t vd[8][VE / 2];
@@ -273,15 +256,6 @@ __device__ __forceinline__ void compute_tile(const RawTile<FP8, D>& R, const u32
       if (g4 == 0) lgm[(j0 >> 5) * lgm_stride] = tmax;
     }
   }
-  if constexpr (RET_CODES) {
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      cw[2 * hh] = logit_code(tmax, x[hh][0]) | (logit_code(tmax, x[hh][1]) << 16);
-      cw[2 * hh + 1] = logit_code(tmax, x[hh][2]) | (logit_code(tmax, x[hh][3]) << 16);
-    }
-    *tmax_out = tmax;
-  }
-
   // online softmax in the log2 domain
   const float m_new = fmaxf(S.m, tmax);
   const float alpha = (m_new == S.m) ? 1.f : exp2_fast(S.m - m_new);
@@ -319,8 +293,9 @@ __device__ __forceinline__ void compute_tile(const RawTile<FP8, D>& R, const u32
   }
 }
 
-// Device-coherent scalar accesses for the per-workgroup partials exchanged
-// across the grid barrier (they bypass the non-coherent per-XCD caches).
+// Device-coherent scalar accesses for the per-workgroup partials that another
+// workgroup of the same launch merges (they bypass the non-coherent per-XCD
+// caches).
 __device__ __forceinline__ void st_coherent(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -413,7 +388,7 @@ __device__ __forceinline__ void load_q(u32x4_t (&qf)[D / 32], const ScanParams& 
 // Tile bases are wave-uniform (scalar registers); each lane adds a fixed
 // 32-bit offset, so interior tiles need no per-lane address arithmetic.
 template <bool FP8, int D, bool WRITE_LOGITS, int WAVES>
-__global__ void __launch_bounds__(WAVES * 64, HS2_SCAN_MIN_WAVES) scan_full(ScanParams P) {
+__global__ void __launch_bounds__(WAVES * 64) scan_full(ScanParams P) {
   constexpr int VE = D / 16, NC = D / 32, EB = FP8 ? 1 : 2;
   constexpr int STEP = WAVES * 32;
   __shared__ float sm_m[WAVES][16];
@@ -433,16 +408,11 @@ __global__ void __launch_bounds__(WAVES * 64, HS2_SCAN_MIN_WAVES) scan_full(Scan
   const int h = g * P.G + (r - tl * P.G);
 
   const int p_max = P.q_pos0 + min(tp * P.tpack + P.tpack, P.Tq) - 1;
-#if HS2_SCAN_INTERLEAVE
   // workgroup tile w = STEP positions; this split owns tiles split, split+nsplit, ...
+  // (all splits sweep the cache together)
   const int j_begin = split * STEP;
   const int j_end = p_max + 1;
   const int jstride = P.nsplit * STEP;
-#else
-  const int j_begin = split * P.split_len;
-  const int j_end = min(j_begin + P.split_len, p_max + 1);
-  const int jstride = STEP;
-#endif
   const int jlim = min(row_ok ? P.q_pos0 + t : -1, j_end - 1);
   // tiles ending at or before j_nomask need no masking for any valid row
   const int j_nomask = min(P.q_pos0 + tp * P.tpack, j_end - 1);
@@ -488,7 +458,7 @@ __global__ void __launch_bounds__(WAVES * 64, HS2_SCAN_MIN_WAVES) scan_full(Scan
     for (int hh = 0; hh < 2; ++hh) kp[hh] = tk + koff[hh];
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) vp[kk] = tv + voff[kk];
-    load_tile<FP8, D, HS2_SCAN_NT != 0>(R, kp, vp);
+    load_tile<FP8, D, false>(R, kp, vp);
   };
   auto load = [&](RawTile<FP8, D>& R, int j0) {
     if (j0 + 31 <= p_max) {
@@ -501,7 +471,7 @@ __global__ void __launch_bounds__(WAVES * 64, HS2_SCAN_MIN_WAVES) scan_full(Scan
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk)
         vp[kk] = vb + (int64_t)min(j0 + 16 * (kk >> 2) + 4 * g4 + (kk & 3), p_max) * snb + VE * r * EB;
-      load_tile<FP8, D, HS2_SCAN_NT != 0>(R, kp, vp);
+      load_tile<FP8, D, false>(R, kp, vp);
     }
   };
   auto compute = [&](const RawTile<FP8, D>& R, int j0) {
@@ -539,721 +509,6 @@ __global__ void __launch_bounds__(WAVES * 64, HS2_SCAN_MIN_WAVES) scan_full(Scan
     }
   }
   merge_and_store<FP8, D, false, WAVES>(P, S, unit, split, b, g, wave, r, g4, sm_m, sm_l, sm_o);
-}
-
-// ---------------------------------------------------------------------------
-// Fused decode full layer: one cooperative launch, every workgroup resident
-// (one per CU).  Phase 1 is the scan above with 8 waves per workgroup; the
-// 16-bit logit codes and tile maxima of a workgroup's first lds_slots tiles
-// stay in LDS, later tiles go to the global code buffer.  A grid barrier
-// follows; phase 2 derives each head's (max, sum) from all workgroup partials,
-// merges the outputs (each workgroup a strided share of the unit's outputs)
-// and writes the scores of its own tiles from the codes.  Compared with the
-// scan + combine + score sequence this removes most scratch writes during the
-// streaming read and two launches; the arithmetic of every step is the same.
-// ---------------------------------------------------------------------------
-constexpr uint32_t kSpinLimit = 1u << 24;  // polls per word (~1 s) before a waiter gives up
-
-// Grid barrier: each workgroup publishes this launch's epoch in its own word,
-// then its threads poll every word until it carries the epoch.  The bounded
-// poll guarantees every wave exits even if the grid were not co-resident
-// (results would then be wrong, never a hang).  Only thread 0 fences at device
-// scope: the workgroup barrier before it has completed every wave's stores to
-// this XCD's L2, which the release fence writes back; its acquire fence
-// invalidates the caches every wave of the workgroup reads through.
-__device__ __forceinline__ void grid_barrier(uint64_t* flags, int nwg, uint64_t epoch, int wg) {
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    __hip_atomic_store(flags + wg, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  for (int w = threadIdx.x; w < nwg; w += blockDim.x) {
-    for (uint32_t it = 0; it < kSpinLimit; ++it) {
-      if (__hip_atomic_load(flags + w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == epoch) break;
-      __builtin_amdgcn_s_sleep(2);
-    }
-  }
-#if HS2_FUSED_ACQUIRE
-  __syncthreads();
-  if (threadIdx.x == 0) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-#endif
-  __syncthreads();
-}
-
-__device__ __forceinline__ int wave_isum(int v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
-
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
-}
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
-
-// Scores of one fused workgroup's tiles (every position of its steps over
-// [0, N)).  A thread takes OPT octets (8 consecutive positions of one tile)
-// per pass and loads every head's codes and tile maximum for all of them
-// before using any (LDS, or the global code buffer for slots past lds_slots),
-// so a pass costs one memory round trip.  Same per-head expression and head
-// order as the score kernel.
-template <int GM, int OPT, int WAVES, bool KEEP = false>
-__device__ __forceinline__ void fused_scores(const ScanParams& P, const uint16_t* lcode, const float* lmax,
-                                             const float* red, int unit, int wu, int b, int g, int tp,
-                                             float (*keep)[8] = nullptr, int* keep_j = nullptr,
-                                             bool* keep_live = nullptr) {
-  constexpr int STEP = WAVES * 32, NT = WAVES * 64;
-  const int rows = P.rows, ns = P.nsplit;
-  const int wsteps = (P.N + STEP - 1) / STEP;  // workgroup steps covering [0, N)
-  const int my_steps = wu < wsteps ? (wsteps - wu + ns - 1) / ns : 0;
-  const int noct = my_steps * WAVES * 4;
-  for (int tl2 = 0; tl2 < P.tpack; ++tl2) {
-    const int t2 = tp * P.tpack + tl2;
-    if (t2 >= P.Tq) break;
-    const int p = P.q_pos0 + t2;
-    float* srow = P.scores + (((int64_t)b * P.Tq + t2) * P.Hkv + g) * P.N;
-    for (int base = 0; base < noct; base += NT * OPT) {
-      u32x4_t w[OPT][GM];
-      float c[OPT][GM];
-      int jo[OPT], j0o[OPT];
-      bool live[OPT];
-#pragma unroll
-      for (int o = 0; o < OPT; ++o) {
-        const int oi = base + o * NT + threadIdx.x;
-        const int slot = oi >> 2, o8 = (oi & 3) * 8;
-        const int k = slot / WAVES, wv = slot - k * WAVES;
-        j0o[o] = (wu + k * ns) * STEP + wv * 32;
-        jo[o] = j0o[o] + o8;
-        live[o] = oi < noct && jo[o] < P.N;
-        const bool scanned = live[o] && jo[o] <= p;  // such a tile was scanned in phase 1 under this slot
-        if (scanned && slot < P.lds_slots) {
-          const uint16_t* cb = lcode + ((size_t)slot * rows + tl2 * P.G) * 32 + o8;
-          const float* mb = lmax + slot * rows + tl2 * P.G;
-#pragma unroll
-          for (int i = 0; i < GM; ++i) {
-            w[o][i] = (i < P.G) ? *(const u32x4_t*)(cb + i * 32) : u32x4_t{0u, 0u, 0u, 0u};
-            c[o][i] = (i < P.G) ? mb[i] : 0.f;
-          }
-        } else if (scanned) {
-          const uint16_t* cb = P.lg16 + ((int64_t)unit * rows + tl2 * P.G) * P.npad + jo[o];
-          const float* mb = P.lgmax + ((int64_t)unit * (P.npad >> 5) + (j0o[o] >> 5)) * rows + tl2 * P.G;
-#pragma unroll
-          for (int i = 0; i < GM; ++i) {
-            w[o][i] = (i < P.G) ? *(const u32x4_t*)(cb + (int64_t)i * P.npad) : u32x4_t{0u, 0u, 0u, 0u};
-            c[o][i] = (i < P.G) ? mb[i] : 0.f;
-          }
-        } else {
-#pragma unroll
-          for (int i = 0; i < GM; ++i) {
-            w[o][i] = u32x4_t{0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu};  // all codes "below range"
-            c[o][i] = 0.f;
-          }
-        }
-      }
-#pragma unroll
-      for (int o = 0; o < OPT; ++o) {
-        float sv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int i = 0; i < GM; ++i) {
-          if (i < P.G) {
-            const float ci = c[o][i] - red[(tl2 * P.G + i) * 4 + 2];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const uint32_t code = (w[o][i][e >> 1] >> (16 * (e & 1))) & 0xffffu;
-              sv[e] += (code == 65535u) ? 0.f : exp2_fast(__builtin_fmaf((float)code, -kCodeInv, ci));
-            }
-          }
-        }
-        if constexpr (KEEP) {  // one pass covers every octet (the caller checked)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) keep[o][e] = (jo[o] + e > p) ? 0.f : sv[e];
-          keep_j[o] = jo[o];
-          keep_live[o] = live[o];
-        }
-        if (live[o]) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (jo[o] + e > p) sv[e] = 0.f;
-          float* dst = srow + jo[o];
-          if ((P.N & 3) == 0) {  // jo is a multiple of 8, so dst is 16-byte aligned
-            if (jo[o] + 8 <= P.N) {
-              *(f32x4_t*)dst = f32x4_t{sv[0], sv[1], sv[2], sv[3]};
-              *(f32x4_t*)(dst + 4) = f32x4_t{sv[4], sv[5], sv[6], sv[7]};
-            } else {
-              *(f32x4_t*)dst = f32x4_t{sv[0], sv[1], sv[2], sv[3]};
-            }
-          } else {
-            for (int e = 0; e < 8 && jo[o] + e < P.N; ++e) dst[e] = sv[e];
-          }
-        }
-      }
-    }
-  }
-}
-
-__device__ __forceinline__ uint32_t sel_key(float s) {
-  const uint32_t u = __float_as_uint(s);
-  return u == 0x80000000u ? 0u : u;  // -0 orders as +0
-}
-
-// Exclusive scan of one value per thread over a workgroup of NT threads (LDS
-// scratch sm >= NT / 64 ints); total returned in `total`.
-template <int NT>
-__device__ __forceinline__ int block_scan_excl(int v, int* sm, int& total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
-  __syncthreads();
-  if (lane == 63) sm[wave] = x;
-  __syncthreads();
-  int base = 0, tot = 0;
-#pragma unroll
-  for (int w = 0; w < NT / 64; ++w) {
-    const int c = sm[w];
-    base += (w < wave) ? c : 0;
-    tot += c;
-  }
-  total = tot;
-  return base + x - v;
-}
-
-// Token top-k + forced window of one unit inside the fused kernel, on the
-// scores this thread holds (OPT octets of 8 positions).  Same rule and result
-// as the select kernels: the k highest scores of C = [0, p - window] (ties to
-// the lower position, exact radix select over the fp32 bit patterns with
-// 12/8/12-bit digits), ascending, then the window, then -1 padding.  Every
-// workgroup runs the same three histogram passes and the step-count exchange
-// (grid barriers 1..4), whatever its unit's mode.
-template <int WAVES, int OPT>
-__device__ __forceinline__ void fused_select(const ScanParams& P, const float (&sv)[OPT][8], const int (&jo)[OPT],
-                                             const bool (&lv)[OPT], int wu, int b, int t, int g, int32_t* lds,
-                                             int wg) {
-  constexpr int STEP = WAVES * 32, NT = WAVES * 64, SEG = 4 * WAVES;  // SEG octets = one workgroup step
-  const int ns = P.nsplit;
-  const int tid = threadIdx.x;
-  const int p = P.q_pos0 + t;
-  const int cand_end = p - P.sel_window;  // candidates 0 <= j <= cand_end
-  const int ncand = max(0, cand_end + 1);
-  const int take = min(P.sel_k, ncand);
-  const bool radix = take > 0 && take < ncand;
-  const int su = (b * P.Tq + t) * P.Hkv + g;
-  // idx / count are outputs here (the gather reads them as inputs)
-  int32_t* out = const_cast<int32_t*>(P.idx) + (int64_t)su * P.max_sel;
-  int32_t* gh = P.sel_hist + (int64_t)su * 3 * kHistBins;
-  int32_t* lh = lds;                       // [kHistBins]
-  int32_t* scr = lds + kHistBins;          // [NT / 64] scan scratch
-  int32_t* pre = scr + 16;                 // [my steps][2] step prefixes
-
-  if (wu == 0) {  // window, padding and count
-    const int wlo = max(0, p - P.sel_window + 1);
-    const int nw = p - wlo + 1;
-    for (int i = tid; i < nw; i += NT) out[take + i] = wlo + i;
-    for (int i = take + nw + tid; i < P.max_sel; i += NT) out[i] = -1;
-    if (tid == 0) const_cast<int32_t*>(P.count)[su] = take + nw;
-  }
-  if (take > 0 && take == ncand) {  // every candidate selected: idx[j] = j
-#pragma unroll
-    for (int o = 0; o < OPT; ++o)
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (lv[o] && jo[o] + e <= cand_end) out[jo[o] + e] = jo[o] + e;
-  }
-  uint32_t key[OPT][8];
-  uint32_t cm[OPT];  // bit e: candidate of a radix unit
-#pragma unroll
-  for (int o = 0; o < OPT; ++o) {
-    cm[o] = 0;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      key[o][e] = sel_key(sv[o][e]);
-      if (radix && lv[o] && jo[o] + e <= cand_end) cm[o] |= 1u << e;
-    }
-  }
-
-  uint32_t prefix = 0;
-  int need = take;
-  // digits of 12, 8 and 12 bits: the middle pass (keys of the boundary bin,
-  // which spread widely) flushes at most 256 bins; the last pass sees few keys
-  auto pass = [&](auto pass_c) {
-    constexpr int PASS = decltype(pass_c)::value;
-    constexpr int SHIFT = PASS == 0 ? 20 : (PASS == 1 ? 12 : 0);
-    constexpr int BINS = PASS == 1 ? 256 : 4096;
-    constexpr uint32_t MATCH = PASS == 0 ? 0u : (PASS == 1 ? 0xFFF00000u : 0xFFFFF000u);
-    for (int i = tid; i < BINS; i += NT) lh[i] = 0;
-    __syncthreads();
-    if (radix && PASS != 0) {  // few keys per bin: plain LDS atomics
-#pragma unroll
-      for (int o = 0; o < OPT; ++o)
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (((cm[o] >> e) & 1) && (key[o][e] & MATCH) == prefix) atomicAdd(&lh[(key[o][e] >> SHIFT) & (BINS - 1)], 1);
-    }
-    if (radix && PASS == 0) {
-      // The keys of one row cluster in few bins: up to four (bin, count) pairs
-      // per thread in registers, then one LDS atomic per distinct bin of the
-      // wave (lanes holding the same bin are summed first).
-      constexpr int SL = 4;
-      uint32_t sb[SL];
-      int scnt[SL];
-#pragma unroll
-      for (int q = 0; q < SL; ++q) {
-        sb[q] = 0xffffffffu;
-        scnt[q] = 0;
-      }
-#pragma unroll
-      for (int o = 0; o < OPT; ++o)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          if (!((cm[o] >> e) & 1) || (key[o][e] & MATCH) != prefix) continue;
-          const uint32_t bin = (key[o][e] >> SHIFT) & (BINS - 1);
-          bool hit = false;
-#pragma unroll
-          for (int q = 0; q < SL; ++q) {
-            if (!hit && (sb[q] == bin || scnt[q] == 0)) {
-              sb[q] = bin;
-              ++scnt[q];
-              hit = true;
-            }
-          }
-          if (!hit) atomicAdd(&lh[bin], 1);
-        }
-#pragma unroll
-      for (int q = 0; q < SL; ++q) {
-        bool pend = scnt[q] > 0;
-        while (__any(pend)) {  // one pass per distinct bin of the wave
-          const uint64_t bal = __ballot(pend);
-          const int leader = __builtin_ctzll(bal);
-          const uint32_t b0 = __shfl(sb[q], leader);
-          const bool mine = pend && sb[q] == b0;
-          const int tot = wave_isum(mine ? scnt[q] : 0);
-          if (threadIdx.x % 64 == leader) atomicAdd(&lh[b0], tot);
-          pend = pend && !mine;
-        }
-      }
-    }
-    __syncthreads();
-    if (radix)
-      for (int i = tid; i < BINS; i += NT)
-        if (lh[i]) atomicAdd(&gh[PASS * kHistBins + i], lh[i]);
-    grid_barrier(P.flags + (1 + PASS) * (int64_t)gridDim.x, gridDim.x, P.epoch, wg);
-    // digit holding the need-th largest key: threads own BINS/NT bins from the top
-    constexpr int BPT = BINS >= NT ? BINS / NT : 1;
-    int c[BPT];
-    int mine = 0;
-    const int hi_d = BINS - tid * BPT - 1;
-#pragma unroll
-    for (int q = 0; q < BPT; ++q) {
-      const int d = hi_d - q;
-      c[q] = (radix && d >= 0) ? __hip_atomic_load(&gh[PASS * kHistBins + d], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
-      mine += c[q];
-    }
-    int tot;
-    const int above = block_scan_excl<NT>(mine, scr, tot);
-    __syncthreads();
-    if (radix && above < need && need <= above + mine) {
-      int a = above;
-#pragma unroll
-      for (int q = 0; q < BPT; ++q) {
-        if (a < need && need <= a + c[q]) {
-          lh[0] = hi_d - q;
-          lh[1] = a;
-        }
-        a += c[q];
-      }
-    }
-    __syncthreads();
-    if (radix) {
-      prefix |= (uint32_t)lh[0] << SHIFT;
-      need -= lh[1];
-    }
-    __syncthreads();
-  };
-  pass(std::integral_constant<int, 0>{});
-  pass(std::integral_constant<int, 1>{});
-  pass(std::integral_constant<int, 2>{});
-  const uint32_t tau = prefix;
-
-  // counts per octet and per workgroup step (SEG consecutive octets = threads)
-  int gt_x[OPT], eq_x[OPT], gt_o[OPT], eq_o[OPT];
-  const int lane = tid & 63;
-#pragma unroll
-  for (int o = 0; o < OPT; ++o) {
-    int gt = 0, eq = 0;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const bool cnd = (cm[o] >> e) & 1;
-      gt += (cnd && key[o][e] > tau);
-      eq += (cnd && key[o][e] == tau);
-    }
-    gt_o[o] = gt;
-    eq_o[o] = eq;
-    int xg = gt, xe = eq;
-#pragma unroll
-    for (int d = 1; d < SEG; d <<= 1) {
-      const int yg = __shfl_up(xg, d, SEG), ye = __shfl_up(xe, d, SEG);
-      if ((lane & (SEG - 1)) >= d) {
-        xg += yg;
-        xe += ye;
-      }
-    }
-    gt_x[o] = xg - gt;  // exclusive within the step
-    eq_x[o] = xe - eq;
-    const int oi = o * NT + tid;
-    const int k = (oi >> 2) / WAVES;
-    const int st = wu + k * ns;
-    if ((lane & (SEG - 1)) == SEG - 1 && radix && st < P.sel_nsteps) {
-      int32_t* sc = P.sel_stepcnt + ((int64_t)su * P.sel_nsteps + st) * 2;
-      __hip_atomic_store(sc, xg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(sc + 1, xe, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-  }
-  grid_barrier(P.flags + 4 * (int64_t)gridDim.x, gridDim.x, P.epoch, wg);
-  if (!radix) return;
-
-  // exclusive prefixes over the unit's steps (in position order) of the
-  // above / equal counts; this workgroup keeps those of its own steps
-  const int nst = min(P.sel_nsteps, (cand_end + STEP) / STEP);  // steps holding candidates
-  const int per = (nst + NT - 1) / NT;
-  int sg = 0, se = 0;
-  for (int q = 0; q < per; ++q) {
-    const int st = tid * per + q;
-    if (st < nst) {
-      const int32_t* sc = P.sel_stepcnt + ((int64_t)su * P.sel_nsteps + st) * 2;
-      sg += __hip_atomic_load(sc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      se += __hip_atomic_load(sc + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-  }
-  int tg, te;
-  int bg = block_scan_excl<NT>(sg, scr, tg);
-  __syncthreads();
-  int be = block_scan_excl<NT>(se, scr, te);
-  for (int q = 0; q < per; ++q) {
-    const int st = tid * per + q;
-    if (st < nst) {
-      if (st % ns == wu) {
-        pre[(st / ns) * 2] = bg;
-        pre[(st / ns) * 2 + 1] = be;
-      }
-      const int32_t* sc = P.sel_stepcnt + ((int64_t)su * P.sel_nsteps + st) * 2;
-      bg += __hip_atomic_load(sc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      be += __hip_atomic_load(sc + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-  }
-  __syncthreads();
-  // ordered writes: rank of a selected position = above-threshold keys before
-  // it + min(equal keys before it, need)
-#pragma unroll
-  for (int o = 0; o < OPT; ++o) {
-    if (!cm[o]) continue;
-    const int oi = o * NT + tid;
-    const int k = (oi >> 2) / WAVES;
-    int gb = pre[2 * k] + gt_x[o];
-    int eb = pre[2 * k + 1] + eq_x[o];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      if (!((cm[o] >> e) & 1)) continue;
-      const uint32_t kk = key[o][e];
-      if (kk > tau) {
-        out[gb + min(eb, need)] = jo[o] + e;
-        ++gb;
-      } else if (kk == tau) {
-        if (eb < need) out[gb + eb] = jo[o] + e;
-        ++eb;
-      }
-    }
-  }
-}
-
-template <bool FP8, int D, int WAVES>
-__global__ void __launch_bounds__(WAVES * 64, 1) scan_fused(ScanParams P) {
-  constexpr int VE = D / 16, NC = D / 32, EB = FP8 ? 1 : 2;
-  constexpr int STEP = WAVES * 32;
-  constexpr int MS = D + 4;  // merge-buffer row stride (floats): O[0..D), m, l
-  extern __shared__ __align__(16) unsigned char lds[];
-  const int rows = P.rows;
-  float* mbuf = (float*)lds;                                          // [4][rows][MS]
-  float* red = (float*)(lds + fused_merge_bytes(rows, D));            // [16][4]: M, L, lse2
-  uint16_t* lcode = (uint16_t*)((unsigned char*)red + 256);           // [lds_slots][rows][32]
-  float* lmax = (float*)(lcode + (size_t)P.lds_slots * rows * 32);    // [lds_slots][rows]
-
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int r = lane & 15, g4 = lane >> 4;
-  const int wg = blockIdx.x;
-  const int ns = P.nsplit;
-#if HS2_FUSED_SWIZZLE
-  // consecutive workgroups (which land on different XCDs) take different units
-  const int units_all = gridDim.x / ns;
-  const int unit = wg % units_all, wu = wg / units_all;
-#else
-  const int unit = wg / ns, wu = wg - unit * ns;
-#endif
-  const int g = unit % P.Hkv;
-  const int tp = (unit / P.Hkv) % P.n_tpacks;
-  const int b = unit / (P.Hkv * P.n_tpacks);
-  const int tl = r / P.G;
-  const int t = tp * P.tpack + tl;
-  const bool row_ok = (r < rows) && (t < P.Tq);
-  const int h = g * P.G + (r - tl * P.G);
-
-  const int p_max = P.q_pos0 + min(tp * P.tpack + P.tpack, P.Tq) - 1;
-  const int j_end = p_max + 1;
-  const int jstride = ns * STEP;
-  const int jlim = min(row_ok ? P.q_pos0 + t : -1, j_end - 1);
-  const int j_nomask = min(P.q_pos0 + tp * P.tpack, j_end - 1);
-
-  u32x4_t qf[NC];
-  load_q<FP8, D>(qf, P, b, t, h, row_ok, g4);
-  const int64_t kvoff = ((int64_t)b * P.sb + (int64_t)g * P.sh) * EB;
-  const char* kb = (const char*)P.k + kvoff;
-  const char* vb = (const char*)P.v + kvoff;
-  const int64_t snb = P.sn * EB;
-  float cs = P.scale_log2;
-  if constexpr (FP8) cs *= P.k_scale[b * P.Hkv + g];
-  uint16_t* lg_row = P.lg16 + ((int64_t)unit * rows + (row_ok ? r : 0)) * P.npad + 4 * g4;
-  float* lgm_row = P.lgmax + (int64_t)unit * (P.npad >> 5) * rows + (row_ok ? r : 0);
-
-  uint32_t koff[2], voff[8];
-#pragma unroll
-  for (int hh = 0; hh < 2; ++hh) koff[hh] = (uint32_t)((16 * hh + r) * snb) + 16u * g4;
-#pragma unroll
-  for (int kk = 0; kk < 8; ++kk)
-    voff[kk] = (uint32_t)((16 * (kk >> 2) + 4 * g4 + (kk & 3)) * snb) + (uint32_t)(VE * r * EB);
-
-  WaveState<D> S;
-  S.m = kNegInf;
-  S.l = 0.f;
-#pragma unroll
-  for (int dt = 0; dt < VE; ++dt) S.o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  auto load = [&](RawTile<FP8, D>& R, int j0) {
-    const char* kp[2];
-    const char* vp[8];
-    if (j0 + 31 <= p_max) {
-      const char* tk = kb + (int64_t)j0 * snb;
-      const char* tv = vb + (int64_t)j0 * snb;
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) kp[hh] = tk + koff[hh];
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk) vp[kk] = tv + voff[kk];
-    } else {  // tail tile: rows past the last position repeat it
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) kp[hh] = kb + (int64_t)min(j0 + 16 * hh + r, p_max) * snb + 16 * g4;
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk)
-        vp[kk] = vb + (int64_t)min(j0 + 16 * (kk >> 2) + 4 * g4 + (kk & 3), p_max) * snb + VE * r * EB;
-    }
-    load_tile<FP8, D, false>(R, kp, vp);
-  };
-  // slot = this workgroup's tile ordinal (step * WAVES + wave)
-  auto compute = [&](const RawTile<FP8, D>& R, int j0, int slot) {
-    uint32_t cw[4];
-    float tm;
-    compute_tile<FP8, D, false, true>(R, qf, cs, j0, jlim, j0 + 31 > j_nomask, g4, nullptr, nullptr, 0, S, cw, &tm);
-    if (row_ok) {
-      if (slot < P.lds_slots) {
-        uint16_t* c = lcode + ((size_t)slot * rows + r) * 32 + 4 * g4;
-        *(u32x2_t*)c = u32x2_t{cw[0], cw[1]};
-        *(u32x2_t*)(c + 16) = u32x2_t{cw[2], cw[3]};
-        if (g4 == 0) lmax[slot * rows + r] = tm;
-      } else {
-        *(u32x2_t*)(lg_row + j0) = u32x2_t{cw[0], cw[1]};
-        *(u32x2_t*)(lg_row + j0 + 16) = u32x2_t{cw[2], cw[3]};
-        if (g4 == 0) lgm_row[(int64_t)(j0 >> 5) * rows] = tm;
-      }
-    }
-  };
-
-  // ---- phase 1: stream the cache; wave w takes tiles w, w + WAVES, ... of the
-  // workgroup's steps (slot k = tile k % WAVES of step k / WAVES).  With two
-  // waves per SIMD (waves w and w ^ 4), the one behind in tiles raises its
-  // issue priority, so the pair finishes together; the assignment of tiles to
-  // waves (and hence every result bit) does not depend on timing.
-  volatile int* prog = (volatile int*)red;  // prog[4 * w + 3]: tiles done by wave w (free pad of red)
-  int done = 0;
-  auto pace = [&]() {
-    if constexpr (WAVES == 8) {
-      ++done;
-      if (lane == 0) prog[4 * wave + 3] = done;
-      const int other = __builtin_amdgcn_readfirstlane(prog[4 * (wave ^ 4) + 3]);
-      if (other > done) {
-        __builtin_amdgcn_s_setprio(3);
-      } else {
-        __builtin_amdgcn_s_setprio(0);
-      }
-    }
-  };
-  if (threadIdx.x < WAVES) prog[4 * threadIdx.x + 3] = 0;
-  __syncthreads();
-  {
-    RawTile<FP8, D> A, B;
-    int j0 = wu * STEP + wave * 32;
-    int slot = wave;
-    if (j0 < j_end) load(A, j0);
-    while (j0 < j_end) {  // ping-pong: load tile n+1 while computing tile n
-      const int j1 = j0 + jstride;
-      if (j1 < j_end) load(B, j1);
-      compute(A, j0, slot);
-      pace();
-      if (j1 >= j_end) break;
-      const int j2 = j1 + jstride;
-      if (j2 < j_end) load(A, j2);
-      compute(B, j1, slot + WAVES);
-      pace();
-      j0 = j2;
-      slot += 2 * WAVES;
-    }
-    if constexpr (WAVES == 8) __builtin_amdgcn_s_setprio(0);
-  }
-
-  // ---- merge the waves (tree through a 4-slot LDS buffer), publish the partial
-  {
-    float lt = S.l;
-    lt = sum_x16(lt);
-    lt = sum_x32(lt);
-    S.l = lt;  // every lane of a row holds the row total
-  }
-#pragma unroll
-  for (int half = WAVES / 2; half >= 1; half >>= 1) {
-    __syncthreads();
-    if (wave >= half && wave < 2 * half && r < rows) {
-      float* sp = mbuf + ((size_t)(wave - half) * rows + r) * MS;
-#pragma unroll
-      for (int dt = 0; dt < VE; ++dt)
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii) sp[VE * (4 * g4 + ii) + dt] = S.o[dt][ii];
-      if (g4 == 0) {
-        sp[D] = S.m;
-        sp[D + 1] = S.l;
-      }
-    }
-    __syncthreads();
-    if (wave < half && r < rows) {
-      const float* sp = mbuf + ((size_t)wave * rows + r) * MS;
-      const float m2 = sp[D], l2 = sp[D + 1];
-      const float M = fmaxf(S.m, m2);
-      const float Ms = (M == kNegInf) ? 0.f : M;
-      const float a = exp2_fast(S.m - Ms), a2 = exp2_fast(m2 - Ms);
-      S.l = S.l * a + l2 * a2;
-#pragma unroll
-      for (int dt = 0; dt < VE; ++dt)
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii) S.o[dt][ii] = S.o[dt][ii] * a + sp[VE * (4 * g4 + ii) + dt] * a2;
-      S.m = M;
-    }
-  }
-  if (wave == 0 && r < rows) {
-    const int64_t pb = ((int64_t)unit * ns + wu) * 16 + r;
-#pragma unroll
-    for (int dt = 0; dt < VE; ++dt)
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) st_coherent(P.part_o + pb * D + VE * (4 * g4 + ii) + dt, S.o[dt][ii]);
-    if (g4 == 0) {
-      st_coherent(P.part_ml + pb * 2, S.m);
-      st_coherent(P.part_ml + pb * 2 + 1, S.l);
-    }
-  }
-
-  if (P.sel_hist != nullptr) {  // this workgroup's share of its unit's selection histograms
-    const int su = (b * P.Tq + tp) * P.Hkv + g;
-    int32_t* gh = P.sel_hist + (int64_t)su * 3 * kHistBins;
-    for (int i = wu * (WAVES * 64) + threadIdx.x; i < 3 * kHistBins; i += ns * WAVES * 64)
-      __hip_atomic_store(gh + i, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  grid_barrier(P.flags, gridDim.x, P.epoch, wg);
-
-  // ---- phase 2a: (max, sum) per row of this unit over all its workgroups, one
-  // pass: lanes merge their partials in order, then a fixed butterfly
-  for (int rr = wave; rr < rows; rr += WAVES) {
-    const float* ml = P.part_ml + ((int64_t)unit * ns * 16 + rr) * 2;
-    float m = kNegInf, l = 0.f;
-    for (int sp = lane; sp < ns; sp += 64) {
-      const f32x2_t v = f32x2_t{ld_coherent(ml + sp * 32), ld_coherent(ml + sp * 32 + 1)};
-      const float M = fmaxf(m, v.x);
-      const float Ms = (M == kNegInf) ? 0.f : M;
-      l = l * exp2_fast(m - Ms) + v.y * exp2_fast(v.x - Ms);
-      m = M;
-    }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      const float m2 = __shfl_xor(m, o), l2 = __shfl_xor(l, o);
-      const float M = fmaxf(m, m2);
-      const float Ms = (M == kNegInf) ? 0.f : M;
-      l = l * exp2_fast(m - Ms) + l2 * exp2_fast(m2 - Ms);
-      m = M;
-    }
-    if (lane == 0) {
-      red[rr * 4 + 0] = (m == kNegInf) ? 0.f : m;
-      red[rr * 4 + 1] = l;
-      red[rr * 4 + 2] = (l > 0.f) ? m + log2f(l) : kNegInf;
-    }
-  }
-  __syncthreads();
-  if (wu == 0 && P.lse && threadIdx.x < rows) {
-    const int rr = threadIdx.x;
-    const int t2 = tp * P.tpack + rr / P.G;
-    if (t2 < P.Tq) P.lse[((int64_t)b * P.Tq + t2) * P.Hq + g * P.G + rr % P.G] = red[rr * 4 + 2] * kLn2;
-  }
-
-  // ---- phase 2b: outputs e = wu, wu + ns, ... of the unit's rows x D, one
-  // group of lw lanes per output summing the weighted partials
-  {
-    int lw = 1;
-    while (lw < ns && lw < 64) lw <<= 1;
-    const int opw = 64 / lw;
-    const int total = rows * D;
-    const int n_out = (total - wu + ns - 1) / ns;
-    const int sl = lane & (lw - 1);
-    for (int base = wave * opw; base < n_out; base += WAVES * opw) {
-      const int i = base + lane / lw;
-      const bool ok = i < n_out;
-      const int e = ok ? wu + i * ns : 0;
-      const int rr = e / D, d = e - rr * D;
-      float acc = 0.f;
-      if (ok) {
-        const float Ms = red[rr * 4];
-        for (int sp = sl; sp < ns; sp += lw) {
-          const int64_t pb = ((int64_t)unit * ns + sp) * 16 + rr;
-          acc += ld_coherent(P.part_o + pb * D + d) * exp2_fast(ld_coherent(P.part_ml + pb * 2) - Ms);
-        }
-      }
-      for (int o = lw / 2; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
-      if (ok && sl == 0) {
-        const int t2 = tp * P.tpack + rr / P.G;
-        if (t2 < P.Tq) {
-          const float L = red[rr * 4 + 1];
-          float o = (L > 0.f) ? acc / L : 0.f;
-          if constexpr (FP8) o *= P.v_scale[b * P.Hkv + g];
-          const int64_t orow = ((int64_t)b * P.Tq + t2) * P.Hq + g * P.G + rr % P.G;
-          ((__bf16*)P.out)[orow * D + d] = (__bf16)o;
-        }
-      }
-    }
-  }
-
-  // ---- phase 2c: scores of this workgroup's tiles, 0 past each query's position
-  if (P.sel_hist != nullptr) {  // scores kept in registers for the selection (tpack 1, G <= 8)
-    float keep[4][8];
-    int kj[4];
-    bool kl[4];
-    fused_scores<8, 4, WAVES, true>(P, lcode, lmax, red, unit, wu, b, g, tp, keep, kj, kl);
-    __syncthreads();  // LDS codes are dead from here on
-    fused_select<WAVES, 4>(P, keep, kj, kl, wu, b, tp, g, (int32_t*)lds, wg);
-  } else if (P.G <= 8) {
-    fused_scores<8, 4, WAVES>(P, lcode, lmax, red, unit, wu, b, g, tp);
-  } else {
-    fused_scores<16, 2, WAVES>(P, lcode, lmax, red, unit, wu, b, g, tp);
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -2452,6 +1707,74 @@ __global__ void __launch_bounds__(256) combine_few(CombineParams P) {
 // ---------------------------------------------------------------------------
 // scores[b,t,g,j] = sum_{heads of g} 2^(x_hj - lse2_h) for j <= p, 0 beyond
 // ---------------------------------------------------------------------------
+
+// log2-domain logit of query row (b, t, head h) against cache row j of kv head
+// g, recomputed in fp32 from the stored elements: the scan's expression, summed
+// in another order.
+__device__ __forceinline__ float recompute_logit(const ScoreParams& P, int b, int t, int h, int g, int j) {
+  const int64_t krow = (int64_t)b * P.sb + (int64_t)g * P.sh + (int64_t)j * P.sn;
+  const int64_t qrow = (((int64_t)b * P.Tq + t) * P.Hq + h) * P.D;
+  float acc = 0.f;
+  if (P.kv_dtype == HS2_F32) {
+    const f32x4_t* k = (const f32x4_t*)((const float*)P.k + krow);
+    const f32x4_t* q = (const f32x4_t*)((const float*)P.q + qrow);
+    for (int c = 0; c < P.D / 4; ++c) {
+      const f32x4_t kk = k[c], qq = q[c];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc = __builtin_fmaf(qq[e], kk[e], acc);
+    }
+    return acc * P.scale_log2;
+  }
+  const u32x4_t* q = (const u32x4_t*)((const uint16_t*)P.q + qrow);  // 8 bf16 elements per load
+  float cs = P.scale_log2;
+  for (int c = 0; c < P.D / 8; ++c) {
+    u32x4_t kk;
+    if (P.kv_dtype == HS2_BF16) {
+      kk = ((const u32x4_t*)((const uint16_t*)P.k + krow))[c];
+    } else {  // 8 E4M3FN codes -> 8 bf16 values (exact)
+      const u32x2_t raw = ((const u32x2_t*)((const uint8_t*)P.k + krow))[c];
+      uint32_t a0, a1, a2, a3;
+      e4m3x4_to_bf16(raw.x, a0, a1);
+      e4m3x4_to_bf16(raw.y, a2, a3);
+      kk = u32x4_t{a0, a1, a2, a3};
+    }
+    const u32x4_t qq = q[c];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      acc = __builtin_fmaf(bf16_bits_to_f32(qq[w] & 0xffffu), bf16_bits_to_f32(kk[w] & 0xffffu), acc);
+      acc = __builtin_fmaf(bf16_bits_to_f32(qq[w] >> 16), bf16_bits_to_f32(kk[w] >> 16), acc);
+    }
+  }
+  if (P.kv_dtype == HS2_FP8_E4M3FN) cs *= P.k_scale[b * P.Hkv + g];
+  return acc * cs;
+}
+
+// The terms of position j (j <= p) whose codes saturated, for row group tl
+// (token t) of a unit: exact where the probability of the code's tile maximum
+// exceeds 2^kExactFloor, zero otherwise -- the terms the code-based sum took
+// as zero.
+__device__ __forceinline__ float saturated_terms(const ScoreParams& P, int unit, int b, int t, int tl, int g, int j) {
+  float add = 0.f;
+  for (int i = 0; i < P.G; ++i) {
+    const int rr = tl * P.G + i;
+    const int64_t row = (int64_t)unit * P.rows + rr;
+    if (P.lg16[row * P.npad + j] != 65535u) continue;
+    const float l2 = P.lse2[row];
+    const float c = P.lgmax[((int64_t)unit * (P.npad >> 5) + (j >> 5)) * P.rows + rr] - l2;
+    if (!(c > kExactFloor)) continue;
+    add += exp2_fast(recompute_logit(P, b, t, g * P.G + i, g, j) - l2);
+  }
+  return add;
+}
+
+// One head's term from its code (c = tile maximum - lse2); `exact` is set when
+// the code saturated and the term is not provably negligible.
+__device__ __forceinline__ float code_term(uint32_t code, float c, bool& exact) {
+  const bool sat = code == 65535u;
+  exact |= sat && c > kExactFloor;
+  return sat ? 0.f : exp2_fast(__builtin_fmaf((float)code, -kCodeInv, c));
+}
+
 __global__ void __launch_bounds__(256) score(ScoreParams P) {
   const int unit = blockIdx.y;
   const int j4 = (blockIdx.x * 256 + threadIdx.x) * 4;
@@ -2465,14 +1788,18 @@ __global__ void __launch_bounds__(256) score(ScoreParams P) {
     const int p = P.q_pos0 + t;
     float s[4] = {0.f, 0.f, 0.f, 0.f};
     if (j4 <= p) {
+      bool exact = false;
       for (int i = 0; i < P.G; ++i) {
         const int64_t row = (int64_t)unit * P.rows + tl * P.G + i;
         const float c = P.lgmax[((int64_t)unit * (P.npad >> 5) + (j4 >> 5)) * P.rows + tl * P.G + i] - P.lse2[row];
         const u32x2_t w = *(const u32x2_t*)(P.lg16 + row * P.npad + j4);
         const uint32_t code[4] = {w.x & 0xffffu, w.x >> 16, w.y & 0xffffu, w.y >> 16};
 #pragma unroll
+        for (int e = 0; e < 4; ++e) s[e] += code_term(code[e], c, exact);
+      }
+      if (exact) {  // rare: a tile holding a dominant logit and terms 16+ log2 units below it
         for (int e = 0; e < 4; ++e)
-          s[e] += (code[e] == 65535u) ? 0.f : exp2_fast(__builtin_fmaf((float)code[e], -kCodeInv, c));
+          if (j4 + e <= p) s[e] += saturated_terms(P, unit, b, t, tl, g, j4 + e);
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e)
@@ -2512,14 +1839,14 @@ __global__ void __launch_bounds__(256) score_hist(ScoreParams P) {
   int jc[R];  // group starts clamped to p: groups past p are zeroed below
 #pragma unroll
   for (int q = 0; q < R; ++q) jc[q] = min(base + 4 * (threadIdx.x + 256 * q), p);
+  bool exact = false;
   auto add_head = [&](const u32x2_t (&w)[R], const float (&mx)[R], float l2) {
 #pragma unroll
     for (int q = 0; q < R; ++q) {
       const float c = mx[q] - l2;
       const uint32_t code[4] = {w[q].x & 0xffffu, w[q].x >> 16, w[q].y & 0xffffu, w[q].y >> 16};
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        s[q][e] += (code[e] == 65535u) ? 0.f : exp2_fast(__builtin_fmaf((float)code[e], -kCodeInv, c));
+      for (int e = 0; e < 4; ++e) s[q][e] += code_term(code[e], c, exact);
     }
   };
   if constexpr (GC > 0) {
@@ -2550,6 +1877,13 @@ __global__ void __launch_bounds__(256) score_hist(ScoreParams P) {
         mx[q] = P.lgmax[((int64_t)unit * (P.npad >> 5) + (jc[q] >> 5)) * P.rows + i];
       }
       add_head(w, mx, P.lse2[row]);
+    }
+  }
+  if (exact) {  // rare: a tile holding a dominant logit and terms 16+ log2 units below it
+    for (int q = 0; q < R; ++q) {
+      const int j4 = base + 4 * (threadIdx.x + 256 * q);
+      for (int e = 0; e < 4; ++e)
+        if (j4 + e <= p) s[q][e] += saturated_terms(P, unit, b, t, 0, g, j4 + e);
     }
   }
   uint32_t key[4 * R];
@@ -2618,30 +1952,6 @@ hipError_t go_full(const ScanParams& p, dim3 grid, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <bool FP8, int D>
-hipError_t go_fused(const ScanParams& p, int units, hipStream_t s) {
-  constexpr int W = fused_waves(FP8 ? HS2_FP8_E4M3FN : HS2_BF16, D);
-  const void* fn = (const void*)&scan_fused<FP8, D, W>;
-  size_t lds = (size_t)fused_merge_bytes(p.rows, D) + 256 + (size_t)p.lds_slots * fused_slot_bytes(p.rows);
-  if (p.sel_hist) lds = std::max(lds, (size_t)kFusedSelectLds);
-  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kFusedLdsBytes);
-  if (e != hipSuccess) return e;
-  TimedLaunch tl("full_scan", s);
-  ScanParams arg = p;
-  void* args[] = {(void*)&arg};
-  return hipLaunchCooperativeKernel(fn, dim3(units * p.nsplit), dim3(W * 64), args, (unsigned)lds, s);
-}
-
-template <bool FP8, int D>
-int fused_occupancy() {
-  int nb = 0;
-  constexpr int W = fused_waves(FP8 ? HS2_FP8_E4M3FN : HS2_BF16, D);
-  const void* fn = (const void*)&scan_fused<FP8, D, W>;
-  if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kFusedLdsBytes) != hipSuccess) return 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, W * 64, kFusedLdsBytes) != hipSuccess) return 0;
-  return nb;
-}
-
 template <bool FP8, int D, int WAVES>
 hipError_t go_gather_split(const ScanParams& p, dim3 grid, hipStream_t s) {
   TimedLaunch tl("sparse_gather", s);
@@ -2665,10 +1975,7 @@ hipError_t go_f32(const ScanParams& p, dim3 grid, hipStream_t s, const char* nam
 
 }  // namespace
 
-#ifndef HS2_SCAN_WAVES
-#define HS2_SCAN_WAVES 4
-#endif
-constexpr int kScanWaves = HS2_SCAN_WAVES;
+constexpr int kScanWaves = 4;
 constexpr int kGatherWaves = 8;
 
 hipError_t launch_scan(const ScanParams& p, int kv_dtype, bool gather, bool write_logits, hipStream_t s) {
@@ -2704,41 +2011,6 @@ hipError_t launch_gather_split(const ScanParams& p, int kv_dtype, hipStream_t s)
   if (kv_dtype == HS2_FP8_E4M3FN)
     return p.D == 128 ? go_gather_split<true, 128, 4>(p, grid, s) : go_gather_split<true, 64, 4>(p, grid, s);
   return p.D == 128 ? go_gather_split<false, 128, 4>(p, grid, s) : go_gather_split<false, 64, 4>(p, grid, s);
-}
-
-hipError_t launch_scan_fused(const ScanParams& p, int kv_dtype, int units, hipStream_t s) {
-  if (kv_dtype == HS2_F32) return hipErrorNotSupported;
-  if (kv_dtype == HS2_FP8_E4M3FN) return p.D == 128 ? go_fused<true, 128>(p, units, s) : go_fused<true, 64>(p, units, s);
-  return p.D == 128 ? go_fused<false, 128>(p, units, s) : go_fused<false, 64>(p, units, s);
-}
-
-// Co-resident fused workgroups on the current device (CUs x workgroups per
-// CU), cached per device; 0 when cooperative launch is unavailable.
-int fused_max_workgroups(int kv_dtype, int D) {
-  if (kv_dtype == HS2_F32) return 0;
-  constexpr int kMaxDev = 64;
-  static int cache[kMaxDev][4];
-  static bool ready[kMaxDev][4];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return 0;
-  const int which = (kv_dtype == HS2_FP8_E4M3FN ? 2 : 0) + (D == 128 ? 1 : 0);
-  if (ready[dev][which]) return cache[dev][which];
-  int cus = 0, coop = 0;
-  int n = 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
-      hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) == hipSuccess && coop) {
-    int occ = 0;
-    switch (which) {
-      case 0: occ = fused_occupancy<false, 64>(); break;
-      case 1: occ = fused_occupancy<false, 128>(); break;
-      case 2: occ = fused_occupancy<true, 64>(); break;
-      default: occ = fused_occupancy<true, 128>(); break;
-    }
-    n = cus * occ;
-  }
-  cache[dev][which] = n;
-  ready[dev][which] = true;
-  return n;
 }
 
 // LDS-staged chunk kernels address a tile's rows with 32-bit offsets

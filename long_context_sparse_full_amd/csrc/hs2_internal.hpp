@@ -43,22 +43,11 @@ struct ScanParams {
   void* out;         // [B, Tq, Hq, D] in q's element type
   float* lse;        // [B, Tq, Hq] natural log (nullable)
   int32_t* gcounter; // split gather: per-(b, t, g) arrival counters (zero between calls)
-  // fused full layer (one cooperative launch): nsplit workgroups per unit
-  float* scores;       // [B, Tq, Hkv, N]
-  int lds_slots;       // tiles per workgroup whose codes stay in LDS; later tiles use lg16/lgmax
-  uint64_t* flags;     // [units * nsplit] grid-barrier arrival words
-  uint64_t epoch;      // this launch's arrival value (unique per launch)
+  // multi-query chunk score pass: scores [B, Tq, Hkv, N]
+  float* scores;
   // multi-query chunk path: log2-domain LSE per (unit, row) from the merge,
   // read by the score pass
   const float* lse2_in;
-  // fused full layer + token selection (tpack = 1): top-k of C = [0, p - window]
-  // with the window appended; output idx/count/max_sel above.  sel_hist:
-  // [units][3][kHistBins] radix histograms; sel_stepcnt: [units][nsteps][2]
-  // (above-threshold, equal-to-threshold) counts per workgroup step.  nullptr
-  // sel_hist = no selection.
-  int sel_k, sel_window, sel_nsteps;
-  int32_t* sel_hist;
-  int32_t* sel_stepcnt;
 };
 
 // Multi-query chunk path: a workgroup of 4 waves, each holding kFlashRG
@@ -86,25 +75,6 @@ constexpr int kCandWords = kCompactTake + 2 * kCompactBin;
 // candidates per row of the collected path (its finishing step keeps a bitmap
 // of them in LDS: 128 KiB at this size)
 constexpr int kCompactMaxCand = 1 << 20;
-
-// Fused decode full layer: workgroup shape and LDS plan shared by the launcher
-// and the host planner.
-// 8 waves (2 per SIMD) per workgroup; 4 for the bf16 D=128 scan, whose two
-// in-flight 16 KiB tiles per wave need the whole register file of a SIMD.
-#ifndef HS2_FUSED_FP8_WAVES
-#define HS2_FUSED_FP8_WAVES 8
-#endif
-__host__ __device__ constexpr int fused_waves(int kv_dtype, int D) {
-  return (kv_dtype == HS2_BF16 && D == 128) ? 4 : (kv_dtype == HS2_FP8_E4M3FN ? HS2_FUSED_FP8_WAVES : 8);
-}
-constexpr int kFusedLdsBytes = 160 * 1024;
-__host__ __device__ inline int fused_merge_bytes(int rows, int D) { return 4 * rows * (D + 4) * 4; }
-// fused selection: LDS histogram, scan scratch and up to kFusedSelMaxSteps step
-// prefixes per workgroup; grid barriers: 1 (layer) + 4 (selection)
-constexpr int kFusedSelMaxSteps = 64;
-constexpr int kFusedSelectLds = (kHistBins + 16 + 2 * kFusedSelMaxSteps) * 4;
-constexpr int kFusedBarriers = 5;
-__host__ __device__ inline int fused_slot_bytes(int rows) { return rows * (32 * 2 + 4); }
 
 struct CombineParams {
   const float* part_ml;
@@ -137,6 +107,14 @@ struct ScoreParams {
   // merge; rows whose selection needs no radix pass are skipped.  nullptr = none
   int32_t* sel_hist;
   int sel_k, sel_window;
+  // The query and cache, for the exact terms of saturated codes (the score
+  // pass recomputes such a logit from q and the cache row).
+  const void* q;
+  int Hq, D, kv_dtype;
+  const void* k;
+  int64_t sb, sh, sn;     // cache strides, elements
+  const float* k_scale;   // FP8 only
+  float scale_log2;       // softmax_scale * log2(e)
 };
 
 // ---------------------------------------------------------------------------
@@ -161,11 +139,6 @@ struct SelectParams {
 // launchers (return hipError_t of the launch)
 hipError_t launch_scan(const ScanParams& p, int kv_dtype, bool gather, bool write_logits, hipStream_t s);
 hipError_t launch_gather_split(const ScanParams& p, int kv_dtype, hipStream_t s);
-// Cooperative launch of the fused full layer (scan, grid barrier, combine,
-// scores).  Returns hipErrorNotSupported when the device cannot co-schedule
-// the grid; the caller then uses the multi-kernel path.
-hipError_t launch_scan_fused(const ScanParams& p, int kv_dtype, int units, hipStream_t s);
-int fused_max_workgroups(int kv_dtype, int D);  // co-resident workgroups, 0 if unavailable
 // Multi-query chunk full layer: MFMA pass writing split partials (then
 // launch_combine), and the score pass recomputing QK^T against the merged LSE.
 hipError_t launch_chunk_full(const ScanParams& p, int kv_dtype, hipStream_t s);

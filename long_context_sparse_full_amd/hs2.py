@@ -27,12 +27,17 @@ OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
 
 
 class KVDesc(ctypes.Structure):
+    """hs2_kv_desc (read-only cache view); hs2_kv_out_desc has the same layout."""
     _fields_ = [
         ("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("dtype", ctypes.c_int32),
         ("stride_b", ctypes.c_int64), ("stride_h", ctypes.c_int64), ("stride_n", ctypes.c_int64),
         ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
         ("B", ctypes.c_int32), ("Hkv", ctypes.c_int32), ("N", ctypes.c_int32), ("D", ctypes.c_int32),
     ]
+
+
+class KVOutDesc(KVDesc):
+    """hs2_kv_out_desc: the writable view the bridge takes (same fields)."""
 
 
 _vp, _i32, _f32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
@@ -64,11 +69,10 @@ _sparse = _sig("hs2_sparse_attn_gather", ctypes.c_int,
 _sparse_ws_size = _sig("hs2_sparse_attn_workspace", _sz, [_i32, _i32, _i32, _i32, _i32])
 _sparse_ws = _sig("hs2_sparse_attn_gather_ws", ctypes.c_int,
                   [_KVP, _vp, _i32, _i32, _i32, _f32, _vp, _vp, _i32, _vp, _vp, _vp, _sz, _vp])
-_bridge = _sig("hs2_kv_bridge", ctypes.c_int, [_vp, _i32, _i32, _vp, _KVP, _i32, _i32, _vp])
+_bridge = _sig("hs2_kv_bridge", ctypes.c_int, [_vp, _i32, _i32, _vp, ctypes.POINTER(KVOutDesc), _i32, _i32, _vp])
 _dbg_e4m3 = _sig("hs2_debug_e4m3fn_to_f32", ctypes.c_int, [_vp, _vp, _i32, _vp])
 _dbg_stream = _sig("hs2_debug_stream_read", ctypes.c_int, [_vp, _sz, _vp, _i32, _vp])
 _t_enable = _sig("hs2_timing_enable", ctypes.c_int, [ctypes.c_int])
-_set_mode = _sig("hs2_full_attn_set_mode", ctypes.c_int, [ctypes.c_int])
 _t_reset = _sig("hs2_timing_reset", ctypes.c_int, [])
 _t_collect = _sig("hs2_timing_collect", ctypes.c_int,
                   [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int32)])
@@ -78,7 +82,7 @@ EXPORTED = [
     "hs2_abi_version", "hs2_status_string", "hs2_last_error", "hs2_full_attn_scores_workspace",
     "hs2_full_attn_scores", "hs2_full_attn_topk_workspace", "hs2_full_attn_topk", "hs2_select_workspace", "hs2_select_workspace_for", "hs2_select_topk_window",
     "hs2_sparse_attn_gather", "hs2_sparse_attn_workspace", "hs2_sparse_attn_gather_ws", "hs2_kv_bridge", "hs2_debug_e4m3fn_to_f32", "hs2_debug_stream_read",
-    "hs2_full_attn_set_mode", "hs2_timing_enable",
+    "hs2_timing_enable",
     "hs2_timing_reset", "hs2_timing_collect", "hs2_timing_kernel_name",
 ]
 
@@ -113,7 +117,14 @@ def _dtype_code(t: torch.Tensor) -> int:
     raise TypeError(f"unsupported element type {t.dtype}")
 
 
-def kv_desc(k: torch.Tensor, v: torch.Tensor, k_scale=None, v_scale=None) -> KVDesc:
+def _dense(*tensors):
+    """The C ABI takes dense row-major q/out/lse/scores/idx/count buffers."""
+    for t in tensors:
+        if t is not None and not t.is_contiguous():
+            raise ValueError("q, out, lse, scores, idx, count and workspace tensors must be contiguous")
+
+
+def kv_desc(k: torch.Tensor, v: torch.Tensor, k_scale=None, v_scale=None, cls=KVDesc) -> KVDesc:
     """Descriptor of a [B, Hkv, N, D] cache (uint8/float8_e4m3fn caches need scales)."""
     if k.shape != v.shape or k.dim() != 4 or k.stride() != v.stride() or k.dtype != v.dtype:
         raise ValueError("k and v must be [B, Hkv, N, D] tensors of one dtype and layout")
@@ -126,9 +137,10 @@ def kv_desc(k: torch.Tensor, v: torch.Tensor, k_scale=None, v_scale=None) -> KVD
         if k_scale is None or v_scale is None:
             ks = vs = None
         else:
+            _dense(k_scale, v_scale)
             ks = k_scale.data_ptr()
             vs = v_scale.data_ptr()
-    return KVDesc(k.data_ptr(), v.data_ptr(), code, k.stride(0), k.stride(1), k.stride(2), ks, vs, B, H, N, D)
+    return cls(k.data_ptr(), v.data_ptr(), code, k.stride(0), k.stride(1), k.stride(2), ks, vs, B, H, N, D)
 
 
 def full_attn_scores_workspace(k, v, Tq: int, Hq: int) -> int:
@@ -153,6 +165,7 @@ def full_attn_scores(k, v, q, q_pos0: int, softmax_scale: float | None = None, k
     need = int(_full_ws(ctypes.byref(d), Tq, Hq))
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    _dense(q, out, lse, scores, workspace)
     st = _full(ctypes.byref(d), q.data_ptr(), _dtype_code(q), Tq, Hq, int(q_pos0), float(softmax_scale),
                out.data_ptr(), None if lse is None else lse.data_ptr(), scores.data_ptr(),
                workspace.data_ptr(), workspace.numel(), _stream())
@@ -190,6 +203,7 @@ def full_attn_topk(k, v, q, q_pos0: int, topk: int, window: int, max_sel: int | 
     need = int(_topk_ws(ctypes.byref(d), Tq, Hq))
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    _dense(q, out, lse, scores, idx, count, workspace)
     st = _topk(ctypes.byref(d), q.data_ptr(), _dtype_code(q), Tq, Hq, int(q_pos0), float(softmax_scale),
                out.data_ptr(), None if lse is None else lse.data_ptr(), scores.data_ptr(), int(topk), int(window),
                idx.data_ptr(), count.data_ptr(), int(max_sel), workspace.data_ptr(), workspace.numel(), _stream())
@@ -216,6 +230,7 @@ def select_topk_window(scores, q_pos0: int, k: int, window: int, block_size: int
         count = torch.empty((B, Tq, Hkv), dtype=torch.int32, device=dev)
     if workspace is None:
         workspace = torch.empty(max(select_workspace(B, Tq, Hkv, N, block_size), 256), dtype=torch.uint8, device=dev)
+    _dense(scores, idx, count, workspace)
     st = _select(scores.data_ptr(), B, Tq, Hkv, N, int(q_pos0), int(k), int(window), int(block_size),
                  idx.data_ptr(), count.data_ptr(), int(max_sel), workspace.data_ptr(), workspace.numel(), _stream())
     _check(st, "hs2_select_topk_window")
@@ -233,6 +248,7 @@ def sparse_attn_gather(k, v, q, idx, count, softmax_scale: float | None = None, 
         out = torch.empty_like(q)
     if lse is None and want_lse:
         lse = torch.empty((B, Tq, Hq), dtype=torch.float32, device=q.device)
+    _dense(q, idx, count, out, lse)
     st = _sparse(ctypes.byref(d), q.data_ptr(), _dtype_code(q), Tq, Hq, float(softmax_scale), idx.data_ptr(),
                  count.data_ptr(), idx.shape[-1], out.data_ptr(), None if lse is None else lse.data_ptr(), _stream())
     _check(st, "hs2_sparse_attn_gather")
@@ -254,6 +270,7 @@ def sparse_attn_gather_ws(k, v, q, idx, count, workspace, softmax_scale: float |
         out = torch.empty_like(q)
     if lse is None and want_lse:
         lse = torch.empty((B, Tq, Hq), dtype=torch.float32, device=q.device)
+    _dense(q, idx, count, out, lse, workspace)
     st = _sparse_ws(ctypes.byref(d), q.data_ptr(), _dtype_code(q), Tq, Hq, float(softmax_scale), idx.data_ptr(),
                     count.data_ptr(), idx.shape[-1], out.data_ptr(), None if lse is None else lse.data_ptr(),
                     workspace.data_ptr(), workspace.numel(), _stream())
@@ -264,8 +281,9 @@ def sparse_attn_gather_ws(k, v, q, idx, count, workspace, softmax_scale: float |
 def kv_bridge(hidden, w_kv, k_cache, v_cache, batch_index: int, pos0: int, k_scale=None, v_scale=None):
     """Project bf16 hidden states [T, d_model] with w_kv [d_model, 2*Hkv*D] into the cache rows
     (bf16 cache, or E4M3FN cache with its per-(b, head) scales)."""
-    d = kv_desc(k_cache, v_cache, k_scale, v_scale)
+    d = kv_desc(k_cache, v_cache, k_scale, v_scale, cls=KVOutDesc)
     T, dm = hidden.shape
+    _dense(hidden, w_kv)
     st = _bridge(hidden.data_ptr(), T, dm, w_kv.data_ptr(), ctypes.byref(d), int(batch_index), int(pos0), _stream())
     _check(st, "hs2_kv_bridge")
 
@@ -283,12 +301,6 @@ def debug_stream_read(buf: torch.Tensor, blocks: int = 2048) -> torch.Tensor:
     _check(_dbg_stream(buf.data_ptr(), nbytes - nbytes % 16, out.data_ptr(), blocks, _stream()),
            "hs2_debug_stream_read")
     return out
-
-
-def full_attn_set_mode(mode: int):
-    """0: scan + merge + score kernels (default); 1: single cooperative full-layer kernel where the device
-    allows it; 2: cooperative kernel with its LDS code store limited to one tile per workgroup."""
-    _check(_set_mode(int(mode)), "hs2_full_attn_set_mode")
 
 
 def timing_enable(on: bool = True):

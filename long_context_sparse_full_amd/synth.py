@@ -67,6 +67,7 @@ class Spec:
     block_k: int = 0       # blocks selected by the 64-token block baseline (0 = none)
     block_size: int = 64
     needle_lo_limit: int = 0   # needles drawn from [0, N - max(window, this))
+    needle_norm: float = 3.0   # needle key = needle_norm * sqrt(D) * (unit query direction)
 
     @property
     def G(self) -> int:
@@ -183,7 +184,7 @@ def make_inputs(spec: Spec, seed: int | None = None, *, with_sparse: bool = True
     k32 = _normal(rs[1], (B, Hkv, N, D))
     v32 = _normal(rs[2], (B, Hkv, N, D))
 
-    # needles: a key of norm 3*sqrt(D) along the unit direction of one query of
+    # needles: a key of norm needle_norm*sqrt(D) along the unit direction of one query of
     # that kv group (head and token drawn per needle); planted in every kv head.
     rn = rs[3]
     hi = max(0, N - max(spec.window, spec.needle_lo_limit))
@@ -200,7 +201,7 @@ def make_inputs(spec: Spec, seed: int | None = None, *, with_sparse: bool = True
                 t = int(rn.integers(0, Tq))
                 u = q32[b, t, h].astype(np.float64)
                 u = u / max(np.linalg.norm(u), 1e-30)
-                k32[b, g, j] = (3.0 * math.sqrt(D) * u).astype(np.float32)
+                k32[b, g, j] = (spec.needle_norm * math.sqrt(D) * u).astype(np.float32)
 
     if spec.q_dtype == "f32":
         enc_q = lambda x: np.ascontiguousarray(x, np.float32)  # noqa: E731
@@ -242,3 +243,61 @@ def random_index_lists(rng_seed: int, units: int, n_rows: int, per_list: int) ->
     for u in range(units):
         idx[u] = np.sort(rng.choice(n_rows, size=per_list, replace=False)).astype(np.int32)
     return idx, np.full(units, per_list, np.int32)
+
+
+def make_dominant_inputs(spec: Spec, gaps, seed: int, dominant: float = 48.0) -> Inputs:
+    """A workload whose attention is dominated by one key per (b, kv head),
+    with weaker keys beside it in the same aligned 32-position tile.
+
+    Every query head of a group points along one random unit direction u of
+    that group (plus a 5% perturbation), scaled so that a key's projection on
+    u, in units of |u|, is its logit in log2 units at softmax scale 1/sqrt(D)
+    (q = u * sqrt(D) / log2(e)).  Keys and values are N(0, 1), so ordinary
+    logits are about N(0, 1) in those units.  One key per (b, g), at a random
+    position j*, is `dominant * u`; for each entry of `gaps` another key of
+    the same tile is (dominant - gap) * u.  So the dominant key holds nearly
+    all of every head's probability and the others sit `gap` log2 units below
+    it (before the storage rounding of q and K).  Needle positions are returned
+    in needle_pos[b, g] (the dominant one first).  Tq query tokens, one
+    sparse layer of ordinary queries."""
+    B, N, Tq, Hq, Hkv, D, G = spec.B, spec.N, spec.Tq, spec.Hq, spec.Hkv, spec.D, spec.G
+    gaps = list(gaps)
+    if len(gaps) > 31 or N < 32:
+        raise ValueError("at most 31 gaps, N >= 32")
+    rs = _streams(seed)
+    k32 = _normal(rs[1], (B, Hkv, N, D))
+    v32 = _normal(rs[2], (B, Hkv, N, D))
+    rn = rs[3]
+    q32 = np.empty((B, Tq, Hq, D), np.float32)
+    qscale = math.sqrt(D) / math.log2(math.e)
+    hi_tile = max(1, (N - spec.window) // 32)
+    pos = np.empty((B, Hkv, 1 + len(gaps)), np.int64)
+    for b in range(B):
+        for g in range(Hkv):
+            u = rn.standard_normal(D)
+            u /= np.linalg.norm(u)
+            for t in range(Tq):
+                for i in range(G):
+                    n = rn.standard_normal(D) / math.sqrt(D)
+                    q32[b, t, g * G + i] = (qscale * (u + 0.05 * n)).astype(np.float32)
+            tile = int(rn.integers(0, hi_tile))
+            offs = rn.permutation(32)[: 1 + len(gaps)]
+            js = [32 * tile + int(o) for o in offs]
+            k32[b, g, js[0]] = (dominant * u).astype(np.float32)
+            for j, gap in zip(js[1:], gaps):
+                k32[b, g, j] = ((dominant - gap) * u).astype(np.float32)
+            pos[b, g] = js
+    enc_q = (lambda x: np.ascontiguousarray(x, np.float32)) if spec.q_dtype == "f32" else to_bf16_bits
+    k_scale = v_scale = None
+    if spec.kv_dtype == "f32":
+        k_st, v_st = k32, v32
+    elif spec.kv_dtype == "bf16":
+        k_st, v_st = to_bf16_bits(k32), to_bf16_bits(v32)
+    else:
+        k_scale = (np.abs(k32).max(axis=(2, 3)) / E4M3FN_MAX).astype(np.float32)
+        v_scale = (np.abs(v32).max(axis=(2, 3)) / E4M3FN_MAX).astype(np.float32)
+        k_st, v_st = to_e4m3fn(k32, k_scale), to_e4m3fn(v32, v_scale)
+    inp = Inputs(spec=spec, seed=seed, q_full=enc_q(q32), k=k_st, v=v_st, k_scale=k_scale, v_scale=v_scale,
+                 needle_pos=pos)
+    inp.q_sparse.append(enc_q(_normal(rs[4], (B, Tq, Hq, D), spec.q_std)))
+    return inp

@@ -229,16 +229,3 @@ def kv_bridge(hidden_bits, w_bits, Hkv, D, mutant: int = 0):
     rc = lib.hs2ref_kv_bridge(h.ctypes.data, T, dm, w.ctypes.data, Hkv, D, y.ctypes.data)
     _check(rc, "kv_bridge")
     return y[:, : Hkv * D].reshape(T, Hkv, D), y[:, Hkv * D:].reshape(T, Hkv, D)
-
-
-def decode_kv(k, k_scale=None):
-    """Dequantised fp64 copy of a cache, element by element, as the oracle reads it."""
-    code = _dtype_code(k)
-    if code == F32:
-        return k.astype(np.float64)
-    if code == BF16:
-        return (k.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
-    table = e4m3fn_table().astype(np.float32)
-    B, H = k.shape[:2]
-    sc = np.asarray(k_scale, np.float32).reshape(B, H, 1, 1)
-    return (table[k] * sc).astype(np.float32).astype(np.float64)

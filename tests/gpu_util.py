@@ -15,14 +15,23 @@ import torch
 O_TOL = {"f32": 1e-5, "bf16": 1e-2, "fp8": 1e-2}
 # LSE (natural log), max-abs: fp32 logits on every path.
 LSE_TOL = {"f32": 1e-5, "bf16": 1e-4, "fp8": 1e-4}
-# Scores: the full layer keeps each head's log2-domain logit as a 16-bit code
-# below that head's maximum over the aligned 32-position tile, step 2^-12, so a
-# probability term carries a relative error <= 2^-13 ln 2 (8.5e-5) plus fp32
-# rounding; codes saturate 16 log2-units below the tile maximum, dropping terms
-# smaller than 2^-16 of the tile's largest probability of that head, which is
-# itself <= the tile's largest score.  Hence
-#   |dS_j| <= S_ABS + S_REL * S_j + 2^-16 * G * max_{j' in tile(j)} S_j'.
-S_REL, S_ABS, S_TILE = 1e-4, 1e-9, 2.0 ** -16
+# Relative output gate, per (b, t, h) row: max_d |dO| <= O_REL * max_d |O_oracle|
+# + O_FLOOR.  The absolute bounds above check little at long context, where
+# the outputs are of order 1e-3; this one scales with them.  bf16/FP8: the
+# probabilities enter the PV products rounded to bf16 (2^-9 relative each)
+# and the output is rounded to bf16 once more, so 2^-7 leaves a factor 2 over
+# their sum.  fp32: every step in fp32.
+O_REL = {"f32": 1e-4, "bf16": 2.0 ** -7, "fp8": 2.0 ** -7}
+O_FLOOR = {"f32": 1e-7, "bf16": 1e-6, "fp8": 1e-6}
+# Scores: |dS_j| <= S_ABS + S_REL * S_j.  The full layer keeps each head's
+# log2-domain logit as a 16-bit code below that head's maximum over the
+# aligned 32-position tile, step 2^-12, so a probability term carries a
+# relative error <= 2^-13 ln 2 (8.5e-5) plus fp32 rounding; a code that
+# saturates (16+ log2 units below the tile maximum) is recomputed exactly from
+# the cache unless the tile maximum's probability is below 2^-24, where the
+# term is below 2^-40 and G of them stay below S_ABS.  S_ABS is stricter than
+# the 1e-7 absolute term of the stated score gate.
+S_REL, S_ABS = 1e-4, 1e-9
 # Selection: bit-exact indices where the oracle's score gap at the k-th
 # boundary exceeds GAP; elsewhere the selected score mass must agree to MASS.
 GAP, MASS = 1e-4, 1e-4
@@ -103,19 +112,12 @@ def assert_close(got, want, tol, what):
     return err
 
 
-def tile_max(s: np.ndarray, tile: int = 32) -> np.ndarray:
-    """Per position, the maximum of s over its aligned tile of positions."""
-    N = s.shape[-1]
-    pad = (-N) % tile
-    sp = np.concatenate([s, np.zeros(s.shape[:-1] + (pad,), s.dtype)], -1) if pad else s
-    m = sp.reshape(sp.shape[:-1] + (-1, tile)).max(-1)
-    return np.repeat(m, tile, -1)[..., :N]
-
-
-def assert_scores(got, want, what="scores", G=8):
+def assert_scores(got, want, what="scores", G=None):
+    """Scores within |dS| <= S_ABS + S_REL * S of the oracle's, element by
+    element (G is accepted for call compatibility; the bound does not use it)."""
     got = np.asarray(got, np.float64)
     want = np.asarray(want, np.float64)
-    bound = S_ABS + S_REL * np.abs(want) + S_TILE * G * tile_max(want)
+    bound = S_ABS + S_REL * np.abs(want)
     bad = np.abs(got - want) > bound
     if bad.any():
         i = np.unravel_index(np.argmax(np.abs(got - want) - bound), got.shape)
@@ -123,6 +125,22 @@ def assert_scores(got, want, what="scores", G=8):
                              f"worst at {i}: got {got[i]:.9e} want {want[i]:.9e}")
     rel = np.max(np.abs(got - want) / (S_ABS + np.abs(want)))
     return float(rel)
+
+
+def assert_rows_rel(got, want, kv, what="out"):
+    """Per (b, t, h) row: max_d |dO| <= O_REL * max_d |O_oracle| + O_FLOOR.
+    Returns the worst ratio of a row's error to its scale max_d |O_oracle|."""
+    got = np.asarray(got, np.float64)
+    want = np.asarray(want, np.float64)
+    err = np.abs(got - want).max(-1)
+    scale = np.abs(want).max(-1)
+    bound = O_REL[kv] * scale + O_FLOOR[kv]
+    bad = err > bound
+    if bad.any():
+        i = np.unravel_index(np.argmax(err - bound), err.shape)
+        raise AssertionError(f"{what}: {int(bad.sum())} rows outside max|dO| <= {O_REL[kv]:.3g}*max|O| + "
+                             f"{O_FLOOR[kv]:g}; worst row {i}: err {err[i]:.3e}, max|O| {scale[i]:.3e}")
+    return float(np.max(err / np.maximum(scale, 1e-30)))
 
 
 def check_structure(idx, count, q_pos0, k, window, N, block_size=1):

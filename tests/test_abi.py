@@ -52,7 +52,7 @@ def test_every_declared_symbol_is_exported(hs2):
 
 
 def test_version_and_status_strings(hs2):
-    assert hs2.abi_version() == 1
+    assert hs2.abi_version() == 2
     for st in (0, -1, -2, -3, -4):
         assert hs2._status_string(st).decode()
 
@@ -67,10 +67,11 @@ def test_timing_names(hs2):
 FAKE = 1 << 20  # 16-byte aligned, never touched: every case fails validation first
 
 
-def desc(hs2, dtype=1, B=1, H=2, N=256, D=128, sn=None, k=FAKE, scales=False):
+def desc(hs2, dtype=1, B=1, H=2, N=256, D=128, sn=None, k=FAKE, scales=False, cls=None):
     sn = D if sn is None else sn
-    d = hs2.KVDesc(k, FAKE, dtype, H * N * sn, N * sn, sn, FAKE if scales else None, FAKE if scales else None,
-                   B, H, N, D)
+    cls = cls or hs2.KVDesc
+    d = cls(k, FAKE, dtype, H * N * sn, N * sn, sn, FAKE if scales else None, FAKE if scales else None,
+            B, H, N, D)
     return d
 
 
@@ -179,7 +180,6 @@ def test_full_attn_topk_validation(hs2):
     assert hs2._topk(*args(k=-1)) == -1                # negative k
     assert hs2._topk(*args(max_sel=11)) == -1          # max_sel < k + window
     assert hs2._topk(*args(wsb=ws - 1)) == -3          # workspace too small
-    assert hs2._set_mode(4) == -1 and hs2._set_mode(-1) == -1
 
 
 def test_sparse_and_bridge_validation(hs2):
@@ -188,11 +188,14 @@ def test_sparse_and_bridge_validation(hs2):
     assert hs2._sparse(ctypes.byref(d), FAKE, 1, 1, 16, 0.1, FAKE, FAKE, 0, FAKE, None, None) == -1
     assert hs2._sparse(ctypes.byref(d), FAKE, 0, 1, 16, 0.1, FAKE, FAKE, 8, FAKE, None, None) == -2
     assert hs2._sparse(ctypes.byref(d), FAKE, 1, 1, 16, float("nan"), FAKE, FAKE, 8, FAKE, None, None) == -1
-    d32 = desc(hs2, dtype=0)
+    out = hs2.KVOutDesc
+    d32 = desc(hs2, dtype=0, cls=out)
     assert hs2._bridge(FAKE, 4, 4096, FAKE, ctypes.byref(d32), 0, 0, None) == -2  # cache bf16 or FP8
-    d8n = desc(hs2, dtype=2, scales=False)
+    d8n = desc(hs2, dtype=2, scales=False, cls=out)
     assert hs2._bridge(FAKE, 4, 4096, FAKE, ctypes.byref(d8n), 0, 0, None) == -2  # FP8 cache needs scales
-    assert hs2._bridge(FAKE, 4, 4000, FAKE, ctypes.byref(d), 0, 0, None) == -2   # d_model % 64
-    assert hs2._bridge(FAKE, 4, 4096, FAKE, ctypes.byref(d), 1, 0, None) == -1   # batch index
-    assert hs2._bridge(FAKE, 4, 4096, FAKE, ctypes.byref(d), 0, 253, None) == -1  # pos0 + T > N
+    do = desc(hs2, cls=out)
+    assert hs2._bridge(FAKE, 4, 4000, FAKE, ctypes.byref(do), 0, 0, None) == -2   # d_model % 64
+    assert hs2._bridge(FAKE, 4, 4096, FAKE, ctypes.byref(do), 1, 0, None) == -1   # batch index
+    assert hs2._bridge(FAKE, 4, 4096, FAKE, ctypes.byref(do), 0, 253, None) == -1  # pos0 + T > N
+    assert hs2._bridge(FAKE, 4, 4096, FAKE, None, 0, 0, None) == -1                # NULL descriptor
     assert hs2._dbg_e4m3(None, FAKE, 4, None) == -1

@@ -65,32 +65,24 @@ CASES = [
 ]
 
 
-@pytest.fixture(params=[0, 1, 2], ids=["kernels", "fused", "fused-spill"])
-def full_mode(hs2, request):
-    """Full-layer execution: the three-kernel sequence, the cooperative kernel,
-    and the cooperative kernel with its codes routed through the workspace."""
-    hs2.full_attn_set_mode(request.param)
-    yield request.param
-    hs2.full_attn_set_mode(0)
-
-
 @pytest.mark.parametrize("case", CASES, ids=lambda c: "-".join(map(str, c)))
-def test_full_layer_parity(hs2, case, full_mode):
+def test_full_layer_parity(hs2, case):
     kv, D, G, Hkv, B, N, Tq = case
     spec = small_spec(kv, D=D, G=G, Hkv=Hkv, B=B, N=N, Tq=Tq, needles=min(8, max(0, N - 16)))
-    gu.log(f"full-layer parity {case} mode {full_mode}")
+    gu.log(f"full-layer parity {case}")
     inp = synth.make_inputs(spec, seed=1234)
     blk = gu.DeviceBlock(inp)
     out, lse, sc = hs2.full_attn_scores(blk.k, blk.v, blk.q, spec.q_pos0, k_scale=blk.ks, v_scale=blk.vs)
     torch.cuda.synchronize()
     o_or, l_or, s_or = oracle_full(inp, spec)
     e_o = gu.assert_close(gu.host(out), o_or, gu.O_TOL[kv], "out")
+    r_o = gu.assert_rows_rel(gu.host(out), o_or, kv)
     e_l = gu.assert_close(gu.host(lse), l_or, gu.LSE_TOL[kv], "lse")
     e_s = gu.assert_scores(gu.host(sc), s_or, G=G)
-    gu.log(f"  max|dO|={e_o:.2e} max|dLSE|={e_l:.2e} max rel dS={e_s:.2e}")
+    gu.log(f"  max|dO|={e_o:.2e} (row rel {r_o:.2e}) max|dLSE|={e_l:.2e} max rel dS={e_s:.2e}")
 
 
-def test_full_layer_q_pos0_before_end(hs2, full_mode):
+def test_full_layer_q_pos0_before_end(hs2):
     spec = small_spec("bf16", N=900, Tq=2)
     inp = synth.make_inputs(spec, seed=7)
     blk = gu.DeviceBlock(inp)
@@ -330,7 +322,7 @@ def test_planted_gap_indices_bit_exact(hs2, kv):
             assert sel == set(inp.needle_pos[b, g].tolist())
 
 
-def test_full_path_bitwise_deterministic(hs2, full_mode):
+def test_full_path_bitwise_deterministic(hs2):
     spec = small_spec("fp8", B=1, N=20000, Hkv=4)
     inp = synth.make_inputs(spec, seed=8)
     blk = gu.DeviceBlock(inp)
@@ -342,7 +334,7 @@ def test_full_path_bitwise_deterministic(hs2, full_mode):
         assert np.array_equal(oa, ob) and np.array_equal(la, lb)
 
 
-def test_strided_cache_view(hs2, full_mode):
+def test_strided_cache_view(hs2):
     """A cache that is a view into a longer buffer (padded rows, extra heads)."""
     spec = small_spec("bf16", B=1, N=700, Hkv=2)
     inp = synth.make_inputs(spec, seed=21)
@@ -435,30 +427,6 @@ def test_kv_bridge_fp8_cache(hs2, T, dm, Hkv, D):
     assert saturated > 0, "the saturating head produced no +-448 codes"
 
 
-@pytest.mark.parametrize("kv", ["bf16", "fp8"])
-def test_fused_and_kernel_paths_agree(hs2, kv):
-    """The cooperative kernel and the three-kernel sequence compute the same
-    layer: outputs within the parity bound of each other, scores within the
-    score bound, at a size with several splits and a ragged tail."""
-    spec = small_spec(kv, B=2, N=12345, Hkv=4)
-    inp = synth.make_inputs(spec, seed=77)
-    blk = gu.DeviceBlock(inp)
-    res = {}
-    for mode in (0, 1, 2):
-        hs2.full_attn_set_mode(mode)
-        out, lse, sc = hs2.full_attn_scores(blk.k, blk.v, blk.q, spec.q_pos0, k_scale=blk.ks, v_scale=blk.vs)
-        torch.cuda.synchronize()
-        res[mode] = (gu.host(out), gu.host(lse), gu.host(sc))
-    hs2.full_attn_set_mode(0)
-    o_or, l_or, s_or = oracle_full(inp, spec)
-    for mode, (o, l, sc) in res.items():
-        gu.assert_close(o, o_or, gu.O_TOL[kv], f"out mode {mode}")
-        gu.assert_close(l, l_or, gu.LSE_TOL[kv], f"lse mode {mode}")
-        gu.assert_scores(sc, s_or, f"scores mode {mode}", G=spec.G)
-    # the spill route stores the same codes as the on-chip route
-    assert np.array_equal(res[1][2], res[2][2]) and np.array_equal(res[1][0], res[2][0])
-
-
 # ------------------------------------------------ full layer + selection in one call
 
 TOPK_CASES = [
@@ -481,13 +449,13 @@ TOPK_CASES = [
 ]
 
 
-@pytest.mark.parametrize("mode", [1, 0], ids=["fused", "sequence"])
 @pytest.mark.parametrize("case", TOPK_CASES, ids=lambda c: "-".join(map(str, c)))
-def test_full_attn_topk(hs2, case, mode):
+def test_full_attn_topk(hs2, case):
     """hs2_full_attn_topk: outputs and scores against the oracle; the selection
-    bit for bit equal to the oracle's selection on the returned scores.  Mode 1
-    must run the selection inside the cooperative kernel (no select kernels)
-    for one bf16/FP8 query token, mode 0 the select kernels."""
+    bit for bit equal to the oracle's selection on the returned scores.  With
+    one bf16/FP8 query token per unit the merge sets the selection up and the
+    score pass counts the first digit, so only the last two histogram passes
+    of the select kernels run."""
     kv, D, G, Hkv, B, N, k, window, qk = case[:9]
     Tq = case[9] if len(case) > 9 else 1
     spec = small_spec(kv, D=D, G=G, Hkv=Hkv, B=B, N=N, Tq=Tq, k=k, window=window,
@@ -496,8 +464,7 @@ def test_full_attn_topk(hs2, case, mode):
     if qk == "zero":
         inp.q_full[...] = 0
     blk = gu.DeviceBlock(inp)
-    gu.log(f"topk {case} mode {mode}")
-    hs2.full_attn_set_mode(mode)
+    gu.log(f"topk {case}")
     try:
         hs2.timing_reset()
         hs2.timing_enable(True)
@@ -509,13 +476,10 @@ def test_full_attn_topk(hs2, case, mode):
     finally:
         hs2.timing_enable(False)
         hs2.timing_reset()
-        hs2.full_attn_set_mode(0)
-    if mode == 1 and Tq == 1 and kv != "f32":  # (no cooperative kernel for an fp32 cache)
-        assert n_hist == 0, "selection did not run inside the cooperative kernel"
-    elif mode == 0 and n_chunk == 0 and kv != "f32" and Tq == 1:
-        # the scan sets the rows up and the score pass counts the first digit
+    if n_chunk == 0 and Tq == 1:
+        # the merge sets the rows up and the score pass counts the first digit
         assert n_hist == 2, "expected the last two histogram passes of the select kernels"
-    elif mode == 0:
+    else:
         assert n_hist in (2, 3), "expected the select kernels"
     o_or, l_or, s_or = oracle_full(inp, spec)
     gu.assert_close(gu.host(out), o_or, gu.O_TOL[kv], "out")
@@ -588,23 +552,80 @@ def test_decode_step_in_hip_graph(hs2, kv):
 
 
 def test_full_attn_topk_repeated_calls(hs2):
-    """The cooperative kernel's grid barriers and histograms start clean on
-    every launch: three calls on one workspace give identical results."""
+    """The selection state and histograms start clean on every call: three
+    calls on one workspace give identical results."""
     spec = small_spec("fp8", B=1, N=40000, Hkv=4)
     inp = synth.make_inputs(spec, seed=5)
     blk = gu.DeviceBlock(inp)
     ws = torch.empty(hs2.full_attn_topk_workspace(blk.k, blk.v, 1, spec.Hq), dtype=torch.uint8, device="cuda")
     res = []
-    hs2.full_attn_set_mode(1)
-    try:
-        for _ in range(3):
-            r = hs2.full_attn_topk(blk.k, blk.v, blk.q, spec.q_pos0, spec.k, spec.window, max_sel=spec.max_sel,
-                                   k_scale=blk.ks, v_scale=blk.vs, workspace=ws)
-            torch.cuda.synchronize()
-            res.append([gu.host(x) for x in r])
-    finally:
-        hs2.full_attn_set_mode(0)
+    for _ in range(3):
+        r = hs2.full_attn_topk(blk.k, blk.v, blk.q, spec.q_pos0, spec.k, spec.window, max_sel=spec.max_sel,
+                               k_scale=blk.ks, v_scale=blk.vs, workspace=ws)
+        torch.cuda.synchronize()
+        res.append([gu.host(x) for x in r])
     for a, b in zip(res[0], res[1]):
         assert np.array_equal(a, b)
     for a, b in zip(res[0], res[2]):
         assert np.array_equal(a, b)
+
+
+# ------------------------------------------- dominant keys (saturated codes)
+
+DOMINANT_CASES = [
+    # kv, D, G, Hkv, B, N, Tq
+    ("bf16", 128, 8, 2, 2, 4096, 1),
+    ("bf16", 128, 16, 1, 1, 3000, 1),
+    ("bf16", 64, 4, 2, 1, 3000, 3),    # several query tokens per unit: the plain score kernel
+    ("fp8", 128, 8, 2, 1, 5000, 1),
+    ("fp8", 128, 16, 2, 1, 2048, 1),
+    ("fp8", 64, 8, 1, 2, 1111, 2),
+    ("f32", 64, 4, 2, 1, 4096, 8),     # the tiny workload's shape
+    ("f32", 64, 8, 2, 1, 2000, 1),
+    ("f32", 128, 16, 1, 1, 1500, 1),
+]
+# log2 units below the dominant key, all in its 32-position tile: codes
+# saturate from 16 on, so every term from the second entry needs the exact path
+DOMINANT_GAPS = (14.0, 16.0, 16.5, 17.0, 18.0, 19.0, 20.0, 22.0, 26.0)
+
+
+@pytest.mark.parametrize("case", DOMINANT_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_dominant_key_scores_exact(hs2, case):
+    """One key per (b, kv head) holds nearly all of every head's probability,
+    with weaker keys 14 to 26 log2 units below it in the same tile: the scores
+    of those keys (and every other) within |dS| <= 1e-9 + 1e-4 S of the
+    oracle's, through both the full-layer call and the full layer + top-k call;
+    the selection bit for bit equal to the oracle's on the GPU's scores and
+    under the gap/mass rule against the oracle's scores."""
+    kv, D, G, Hkv, B, N, Tq = case
+    k = len(DOMINANT_GAPS) + 1
+    spec = small_spec(kv, D=D, G=G, Hkv=Hkv, B=B, N=N, Tq=Tq, k=k, window=16)
+    inp = synth.make_dominant_inputs(spec, DOMINANT_GAPS, seed=2024 + N)
+    blk = gu.DeviceBlock(inp)
+    gu.log(f"dominant keys {case}")
+    o_or, l_or, s_or = oracle_full(inp, spec)
+    out, lse, sc = hs2.full_attn_scores(blk.k, blk.v, blk.q, spec.q_pos0, k_scale=blk.ks, v_scale=blk.vs)
+    out2, lse2, sc2, idx, cnt = hs2.full_attn_topk(blk.k, blk.v, blk.q, spec.q_pos0, k, spec.window,
+                                                   max_sel=spec.max_sel, k_scale=blk.ks, v_scale=blk.vs)
+    torch.cuda.synchronize()
+    for label, o, l, s in (("full", out, lse, sc), ("full+topk", out2, lse2, sc2)):
+        o, l, s = gu.host(o), gu.host(l), gu.host(s)
+        gu.assert_close(o, o_or, gu.O_TOL[kv], f"{label} out")
+        gu.assert_rows_rel(o, o_or, kv, f"{label} out (per row)")
+        gu.assert_close(l, l_or, gu.LSE_TOL[kv], f"{label} lse")
+        e_s = gu.assert_scores(s, s_or, f"{label} scores")
+        # the weak keys themselves, element by element
+        for b in range(B):
+            for t in range(Tq):
+                for g in range(Hkv):
+                    js = inp.needle_pos[b, g]
+                    got, want = s[b, t, g, js].astype(np.float64), s_or[b, t, g, js]
+                    assert np.all(want[1:] > 0) and np.all(np.abs(got - want) <= 1e-9 + 1e-4 * want), \
+                        f"{label}: weak keys at {js} got {got} want {want}"
+        gu.log(f"  {label}: max rel dS={e_s:.2e}")
+    idx, cnt, sc2 = gu.host(idx), gu.host(cnt), gu.host(sc2)
+    i_g, c_g = oracle.select_topk_window(sc2.astype(np.float64), spec.q_pos0, k, spec.window, max_sel=spec.max_sel)
+    assert np.array_equal(cnt, c_g) and np.array_equal(idx, i_g), "selection differs from the oracle's on the GPU scores"
+    i_or, c_or = oracle.select_topk_window(s_or, spec.q_pos0, k, spec.window, max_sel=spec.max_sel)
+    gu.check_selection_vs_oracle(idx, cnt, i_or, c_or, s_or, spec.q_pos0, k, spec.window)
+    gu.check_structure(idx, cnt, spec.q_pos0, k, spec.window, N)
