@@ -78,7 +78,7 @@ def check_run(name, spec, inp, res, o_or, l_or, s_or):
     kv = spec.kv_dtype
     e_o = gu.assert_close(res["out"], o_or, gu.O_TOL[kv], "full out")
     r_o = gu.assert_rows_rel(res["out"], o_or, kv, "full out (per row)")
-    e_l = gu.assert_close(res["lse"], l_or, gu.LSE_TOL[kv], "full lse")
+    e_l = gu.assert_lse(res["lse"], l_or, kv, "full lse")
     e_s = gu.assert_scores(res["scores"], s_or)
     gu.log(f"[{name}] full: max|dO|={e_o:.2e} (worst row {r_o:.2e} of its max|O|) max|dLSE|={e_l:.2e} "
            f"max rel dS={e_s:.2e}")
@@ -98,6 +98,6 @@ def check_run(name, spec, inp, res, o_or, l_or, s_or):
                                     k_scale=inp.k_scale, v_scale=inp.v_scale)
         e1 = gu.assert_close(o, o2, gu.O_TOL[kv], f"sparse {layer} out")
         r1 = gu.assert_rows_rel(o, o2, kv, f"sparse {layer} out (per row)")
-        e2 = gu.assert_close(l, l2, gu.LSE_TOL[kv], f"sparse {layer} lse")
+        e2 = gu.assert_lse(l, l2, kv, f"sparse {layer} lse")
         gu.log(f"[{name}] sparse layer {layer}: max|dO|={e1:.2e} (worst row {r1:.2e}) max|dLSE|={e2:.2e}")
     return exact, by_mass

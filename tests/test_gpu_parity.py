@@ -77,7 +77,7 @@ def test_full_layer_parity(hs2, case):
     o_or, l_or, s_or = oracle_full(inp, spec)
     e_o = gu.assert_close(gu.host(out), o_or, gu.O_TOL[kv], "out")
     r_o = gu.assert_rows_rel(gu.host(out), o_or, kv)
-    e_l = gu.assert_close(gu.host(lse), l_or, gu.LSE_TOL[kv], "lse")
+    e_l = gu.assert_lse(gu.host(lse), l_or, kv, "lse")
     e_s = gu.assert_scores(gu.host(sc), s_or, G=G)
     gu.log(f"  max|dO|={e_o:.2e} (row rel {r_o:.2e}) max|dLSE|={e_l:.2e} max rel dS={e_s:.2e}")
 
@@ -91,7 +91,7 @@ def test_full_layer_q_pos0_before_end(hs2):
     torch.cuda.synchronize()
     o_or, l_or, s_or = oracle.full_attn_scores(inp.q_full, inp.k, inp.v, qp)
     gu.assert_close(gu.host(out), o_or, gu.O_TOL["bf16"], "out")
-    gu.assert_close(gu.host(lse), l_or, gu.LSE_TOL["bf16"], "lse")
+    gu.assert_lse(gu.host(lse), l_or, "bf16", "lse")
     gu.assert_scores(gu.host(sc), s_or, G=spec.G)
     assert np.all(gu.host(sc)[..., qp + 2:] == 0.0)
 
@@ -107,7 +107,7 @@ def test_chunk_q_pos0_before_end(hs2):
     torch.cuda.synchronize()
     o_or, l_or, s_or = oracle.full_attn_scores(inp.q_full, inp.k, inp.v, qp)
     gu.assert_close(gu.host(out), o_or, gu.O_TOL["bf16"], "out")
-    gu.assert_close(gu.host(lse), l_or, gu.LSE_TOL["bf16"], "lse")
+    gu.assert_lse(gu.host(lse), l_or, "bf16", "lse")
     sc = gu.host(sc)
     gu.assert_scores(sc, s_or, G=spec.G)
     for t in range(spec.Tq):
@@ -220,7 +220,7 @@ def test_sparse_parity_on_gpu_selection(hs2, kv, D, G, split):
         o_or, l_or = oracle.sparse_attn(inp.q_sparse[layer], inp.k, inp.v, res["idx"], res["count"],
                                         k_scale=inp.k_scale, v_scale=inp.v_scale)
         gu.assert_close(o, o_or, gu.O_TOL[kv], f"sparse layer {layer} out")
-        gu.assert_close(l, l_or, gu.LSE_TOL[kv], f"sparse layer {layer} lse")
+        gu.assert_lse(l, l_or, kv, f"sparse layer {layer} lse")
 
 
 @pytest.mark.parametrize("kv", ["bf16", "fp8"])
@@ -249,7 +249,7 @@ def test_split_gather_lists_repeated_calls(hs2, kv):
         o, l = gu.host(o), gu.host(l)
         gu.assert_close(o, o_or, gu.O_TOL[kv], f"call {rep} out")
         fin = ~np.isinf(l_or)
-        gu.assert_close(l[fin], l_or[fin], gu.LSE_TOL[kv], f"call {rep} lse")
+        gu.assert_lse(l[fin], l_or[fin], kv, f"call {rep} lse")
         assert np.all(np.isneginf(l[~fin]))
         if first is None:
             first = (o, l)
@@ -276,7 +276,7 @@ def test_sparse_random_lists_and_empty(hs2):
     assert np.all(o[0, 0, :8] == 0.0) and np.all(np.isneginf(l[0, 0, :8]))
     gu.assert_close(o, o_or, gu.O_TOL["bf16"], "out")
     fin = ~np.isinf(l_or)
-    gu.assert_close(l[fin], l_or[fin], gu.LSE_TOL["bf16"], "lse")
+    gu.assert_lse(l[fin], l_or[fin], "bf16", "lse")
     assert empty.sum() == 1
 
 
@@ -483,7 +483,7 @@ def test_full_attn_topk(hs2, case):
         assert n_hist in (2, 3), "expected the select kernels"
     o_or, l_or, s_or = oracle_full(inp, spec)
     gu.assert_close(gu.host(out), o_or, gu.O_TOL[kv], "out")
-    gu.assert_close(gu.host(lse), l_or, gu.LSE_TOL[kv], "lse")
+    gu.assert_lse(gu.host(lse), l_or, kv, "lse")
     sc = gu.host(sc)
     gu.assert_scores(sc, s_or, G=G)
     idx, cnt = gu.host(idx), gu.host(cnt)
@@ -612,7 +612,7 @@ def test_dominant_key_scores_exact(hs2, case):
         o, l, s = gu.host(o), gu.host(l), gu.host(s)
         gu.assert_close(o, o_or, gu.O_TOL[kv], f"{label} out")
         gu.assert_rows_rel(o, o_or, kv, f"{label} out (per row)")
-        gu.assert_close(l, l_or, gu.LSE_TOL[kv], f"{label} lse")
+        gu.assert_lse(l, l_or, kv, f"{label} lse")
         e_s = gu.assert_scores(s, s_or, f"{label} scores")
         # the weak keys themselves, element by element
         for b in range(B):
