@@ -177,6 +177,26 @@ int hs2_sparse_attn_gather_ws(const hs2_kv_desc* kv, const void* q, hs2_dtype q_
                               const int32_t* count, int32_t max_sel, void* out, float* lse,
                               void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* The same split sparse layer for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): same arguments, rules and results as hs2_sparse_attn_gather_ws
+ * without the workspace.  The split's partials and arrival counters live in a
+ * static device array of the library, hs2_sparse_attn_static_limit() bytes
+ * (4 MiB) on every GPU the library runs on, held until the process ends; a
+ * call whose split would need more returns HS2_ERR_WORKSPACE (the split
+ * needs about units * ceil(max_sel / 128) * 16 * (D + 2) * 4 bytes, units =
+ * B * Tq * Hkv; a call that takes the one-workgroup path -- fp32 caches, 64
+ * or more lists, lists too long for the split's merge -- needs none).  The first call on a
+ * device also clears the counters on `stream`.  The call itself allocates
+ * nothing.  Every call on one GPU shares that GPU's array: calls that overlap
+ * on one GPU (any streams, any threads) race and must be ordered by the
+ * caller. */
+size_t hs2_sparse_attn_static_limit(void);
+int hs2_sparse_attn_gather_static(const hs2_kv_desc* kv, const void* q, hs2_dtype q_dtype, int32_t Tq,
+                                  int32_t Hq, float softmax_scale, const int32_t* idx,
+                                  const int32_t* count, int32_t max_sel, void* out, float* lse,
+                                  hipStream_t stream);
+
 /* KV bridge (javabetter.cn, KV Bridging paragraph: a cross-decoder full layer
  * computes its K and V from a self-decoder layer's hidden state, with its own
  * parameters).  y = hidden [T, d_model] (bf16) x w_kv [d_model, 2*Hkv*D]

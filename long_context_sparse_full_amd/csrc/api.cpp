@@ -597,33 +597,40 @@ size_t hs2_sparse_attn_workspace(int32_t B, int32_t Tq, int32_t Hkv, int32_t D, 
   return plan_gather(B * Tq * Hkv, max_sel, D).total;
 }
 
-int hs2_sparse_attn_gather_ws(const hs2_kv_desc* kv, const void* q, hs2_dtype q_dtype, int32_t Tq, int32_t Hq,
-                              float softmax_scale, const int32_t* idx, const int32_t* count, int32_t max_sel,
-                              void* out, float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  int st = check_kv(kv, "hs2_sparse_attn_gather_ws");
+}  // extern "C"
+
+namespace {
+// Checks shared by the split gather's entry points.
+int check_gather_args(const char* name, const hs2_kv_desc* kv, const void* q, hs2_dtype q_dtype, int32_t Tq,
+                      int32_t Hq, float softmax_scale, const int32_t* idx, const int32_t* count, int32_t max_sel,
+                      void* out, float* lse) {
+  const std::string w(name);
+  int st = check_kv(kv, name);
   if (st) return st;
-  if ((st = check_q(kv, q, q_dtype, Tq, Hq, "hs2_sparse_attn_gather_ws"))) return st;
-  if (!idx || !count || !out) return fail(HS2_ERR_INVALID_ARG, "hs2_sparse_attn_gather_ws: NULL idx/count/out");
-  if (max_sel <= 0) return fail(HS2_ERR_INVALID_ARG, "hs2_sparse_attn_gather_ws: max_sel must be positive");
+  if ((st = check_q(kv, q, q_dtype, Tq, Hq, name))) return st;
+  if (!idx || !count || !out) return fail(HS2_ERR_INVALID_ARG, w + ": NULL idx/count/out");
+  if (max_sel <= 0) return fail(HS2_ERR_INVALID_ARG, w + ": max_sel must be positive");
   if (!al16(out) || ((uintptr_t)idx & 3) || ((uintptr_t)count & 3) || (lse && ((uintptr_t)lse & 3)))
-    return fail(HS2_ERR_INVALID_ARG, "hs2_sparse_attn_gather_ws: out must be 16-byte aligned, idx/count/lse 4-byte");
-  if (!std::isfinite(softmax_scale))
-    return fail(HS2_ERR_INVALID_ARG, "hs2_sparse_attn_gather_ws: softmax_scale not finite");
-  if (kv->dtype == HS2_F32)  // the fp32 path has no split form; it needs no workspace
-    return hs2_sparse_attn_gather(kv, q, q_dtype, Tq, Hq, softmax_scale, idx, count, max_sel, out, lse, stream);
-  const int units = kv->B * Tq * kv->Hkv;
-  const GatherPlan gp = plan_gather(units, max_sel, kv->D);
-  if (!workspace || workspace_bytes < gp.total)
-    return fail(HS2_ERR_WORKSPACE, "hs2_sparse_attn_gather_ws: workspace needs " + std::to_string(gp.total) + " bytes");
-  // The split form pays off only while one workgroup per (b, t, g) leaves the
-  // GPU mostly idle; from 64 units on, the one-workgroup kernel is used (it
-  // needs no workspace).  Also the merging workgroup keeps a maximum (then
-  // weight) and a sum per (slice, row) in its 4-wave merge buffer
-  // (4 * 16 * (D + 1) floats), so longer lists take the one-workgroup kernel too.
-  if (units >= kSplitGatherMaxUnits || (int64_t)2 * gp.nsplit * 16 > 4 * 16 * (kv->D + 1))
-    return hs2_sparse_attn_gather(kv, q, q_dtype, Tq, Hq, softmax_scale, idx, count, max_sel, out, lse, stream);
-  if ((uintptr_t)workspace & 255)
-    return fail(HS2_ERR_INVALID_ARG, "hs2_sparse_attn_gather_ws: workspace must be 256-byte aligned");
+    return fail(HS2_ERR_INVALID_ARG, w + ": out must be 16-byte aligned, idx/count/lse 4-byte");
+  if (!std::isfinite(softmax_scale)) return fail(HS2_ERR_INVALID_ARG, w + ": softmax_scale not finite");
+  return HS2_OK;
+}
+
+// The split form pays off only while one workgroup per (b, t, g) leaves the
+// GPU mostly idle; from kSplitGatherMaxUnits units on, the one-workgroup
+// kernel is used (it needs no workspace).  The merging workgroup also keeps
+// a maximum (then weight) and a sum per (slice, row) in its 4-wave merge
+// buffer (4 * 16 * (D + 1) floats), so longer lists take the one-workgroup
+// kernel too, as does an fp32 cache (no split form).
+bool use_split_gather(const hs2_kv_desc* kv, int units, const GatherPlan& gp) {
+  return kv->dtype != HS2_F32 && units < kSplitGatherMaxUnits && (int64_t)2 * gp.nsplit * 16 <= 4 * 16 * (kv->D + 1);
+}
+
+// Launch of the split gather on a workspace already checked for size and
+// alignment (arrival counters zero on entry; zero again on exit).
+int launch_split_gather(const char* name, const hs2_kv_desc* kv, const void* q, int32_t Tq, int32_t Hq,
+                        float softmax_scale, const int32_t* idx, const int32_t* count, int32_t max_sel, void* out,
+                        float* lse, const GatherPlan& gp, void* workspace, hipStream_t stream) {
   hs2::ScanParams p{};
   p.k = kv->k;
   p.v = kv->v;
@@ -655,8 +662,95 @@ int hs2_sparse_attn_gather_ws(const hs2_kv_desc* kv, const void* q, hs2_dtype q_
   p.out = out;
   p.lse = lse;
   const hipError_t e = hs2::launch_gather_split(p, kv->dtype, stream);
-  if (e != hipSuccess) return hip_fail(e, "sparse_gather launch");
+  if (e != hipSuccess) return hip_fail(e, (std::string(name) + ": sparse_gather launch").c_str());
   return HS2_OK;
+}
+
+// ---- the no-allocation variant's scratch --------------------------------
+// The split gather's partials and arrival counters for
+// hs2_sparse_attn_gather_static live in this file-scope device array (one
+// copy per GPU, held until the process ends).  Host code never passes the
+// array's name to a kernel: the device address of each GPU's copy comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+constexpr size_t kStaticScratchBytes = size_t(4) << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// Clears the arrival-counter region (the first 4 KiB) of a device's copy.
+__global__ void clear_scratch_words(uint32_t* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+// Device address of the current device's scratch; the first call on a device
+// resolves it and clears the counter region on `stream`.
+int static_scratch(hipStream_t stream, void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hs2_sparse_attn_gather_static: hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(HS2_ERR_UNSUPPORTED, "hs2_sparse_attn_gather_static: device index above 63");
+  std::call_once(g_scratch_once[dev], [&] {
+    void* p = nullptr;
+    hipError_t r = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (r == hipSuccess && p == nullptr) r = hipErrorInvalidSymbol;
+    if (r == hipSuccess) {
+      hipLaunchKernelGGL(clear_scratch_words, dim3(4), dim3(256), 0, stream, static_cast<uint32_t*>(p), 1024);
+      r = hipGetLastError();
+    }
+    g_scratch_err[dev] = r;
+    g_scratch_ptr[dev] = r == hipSuccess ? p : nullptr;
+  });
+  if (g_scratch_err[dev] != hipSuccess)
+    return hip_fail(g_scratch_err[dev], "hs2_sparse_attn_gather_static: scratch set-up");
+  *ptr = g_scratch_ptr[dev];
+  return HS2_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int hs2_sparse_attn_gather_ws(const hs2_kv_desc* kv, const void* q, hs2_dtype q_dtype, int32_t Tq, int32_t Hq,
+                              float softmax_scale, const int32_t* idx, const int32_t* count, int32_t max_sel,
+                              void* out, float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const char* name = "hs2_sparse_attn_gather_ws";
+  int st = check_gather_args(name, kv, q, q_dtype, Tq, Hq, softmax_scale, idx, count, max_sel, out, lse);
+  if (st) return st;
+  if (kv->dtype == HS2_F32)  // the fp32 path has no split form; it needs no workspace
+    return hs2_sparse_attn_gather(kv, q, q_dtype, Tq, Hq, softmax_scale, idx, count, max_sel, out, lse, stream);
+  const int units = kv->B * Tq * kv->Hkv;
+  const GatherPlan gp = plan_gather(units, max_sel, kv->D);
+  if (!workspace || workspace_bytes < gp.total)
+    return fail(HS2_ERR_WORKSPACE, std::string(name) + ": workspace needs " + std::to_string(gp.total) + " bytes");
+  if (!use_split_gather(kv, units, gp))
+    return hs2_sparse_attn_gather(kv, q, q_dtype, Tq, Hq, softmax_scale, idx, count, max_sel, out, lse, stream);
+  if ((uintptr_t)workspace & 255) return fail(HS2_ERR_INVALID_ARG, std::string(name) + ": workspace must be 256-byte aligned");
+  return launch_split_gather(name, kv, q, Tq, Hq, softmax_scale, idx, count, max_sel, out, lse, gp, workspace, stream);
+}
+
+size_t hs2_sparse_attn_static_limit(void) { return kStaticScratchBytes; }
+
+int hs2_sparse_attn_gather_static(const hs2_kv_desc* kv, const void* q, hs2_dtype q_dtype, int32_t Tq, int32_t Hq,
+                                  float softmax_scale, const int32_t* idx, const int32_t* count, int32_t max_sel,
+                                  void* out, float* lse, hipStream_t stream) {
+  const char* name = "hs2_sparse_attn_gather_static";
+  int st = check_gather_args(name, kv, q, q_dtype, Tq, Hq, softmax_scale, idx, count, max_sel, out, lse);
+  if (st) return st;
+  const int units = kv->B * Tq * kv->Hkv;
+  const GatherPlan gp = plan_gather(units, max_sel, kv->D);
+  if (!use_split_gather(kv, units, gp))  // the one-workgroup kernel: no scratch
+    return hs2_sparse_attn_gather(kv, q, q_dtype, Tq, Hq, softmax_scale, idx, count, max_sel, out, lse, stream);
+  if (gp.total > kStaticScratchBytes)
+    return fail(HS2_ERR_WORKSPACE, std::string(name) + ": needs " + std::to_string(gp.total) +
+                                       " bytes of scratch; the library's static scratch holds " +
+                                       std::to_string(kStaticScratchBytes));
+  void* ws = nullptr;
+  if ((st = static_scratch(stream, &ws))) return st;
+  return launch_split_gather(name, kv, q, Tq, Hq, softmax_scale, idx, count, max_sel, out, lse, gp, ws, stream);
 }
 
 int hs2_kv_bridge(const void* hidden, int32_t T, int32_t d_model, const void* w_kv, const hs2_kv_out_desc* kv_out,

@@ -199,3 +199,17 @@ def test_sparse_and_bridge_validation(hs2):
     assert hs2._bridge(FAKE, 4, 4096, FAKE, ctypes.byref(do), 0, 253, None) == -1  # pos0 + T > N
     assert hs2._bridge(FAKE, 4, 4096, FAKE, None, 0, 0, None) == -1                # NULL descriptor
     assert hs2._dbg_e4m3(None, FAKE, 4, None) == -1
+
+
+def test_static_gather_limits(hs2):
+    """The no-allocation sparse layer rejects a split larger than its static
+    scratch before touching the device, and validates like the other calls."""
+    assert hs2.sparse_attn_static_limit() == 4 << 20
+    # 63 lists of 4096 entries at D = 128: 63 * 32 slices * 16 rows * 130 floats > 4 MiB
+    d = desc(hs2, H=63, N=8192)
+    st = hs2._sparse_static(ctypes.byref(d), FAKE, 1, 1, 63 * 8, 0.1, FAKE, FAKE, 4096, FAKE, None, None)
+    assert st == -3 and "static scratch" in hs2._last_error().decode()
+    d = desc(hs2)
+    assert hs2._sparse_static(ctypes.byref(d), FAKE, 1, 1, 16, 0.1, None, FAKE, 8, FAKE, None, None) == -1
+    assert hs2._sparse_static(ctypes.byref(d), FAKE, 1, 1, 16, 0.1, FAKE, FAKE, 0, FAKE, None, None) == -1
+    assert hs2._sparse_static(None, FAKE, 1, 1, 16, 0.1, FAKE, FAKE, 8, FAKE, None, None) == -1
