@@ -55,6 +55,9 @@ typedef struct ihipStream_t* hipStream_t;
 
 typedef enum { HS2_F32 = 0, HS2_BF16 = 1, HS2_FP8_E4M3FN = 2 } hs2_dtype;
 
+/* Selection flags (hs2_select_topk_window, hs2_full_attn_topk). */
+enum { HS2_SEL_WINDOW_COMPETES = 1 };
+
 enum {
   HS2_OK = 0,
   HS2_ERR_INVALID_ARG = -1, /* bad shape, pointer, alignment or range          */
@@ -137,6 +140,12 @@ int hs2_full_attn_scores(const hs2_kv_desc* kv, const void* q, hs2_dtype q_dtype
  *     ascending position), the min(k, #blocks) heaviest blocks (ties to the
  *     lower block), T = their positions; k counts blocks.
  *   idx[b,t,g,:count] = ascending(T union Wn); idx[b,t,g,count:] = -1.
+ * flags: 0, or HS2_SEL_WINDOW_COMPETES (token mode only; HS2_ERR_UNSUPPORTED
+ * with block_size > 1): the other reading of the two budgets, where the
+ * window does not reserve its own: C = [0, p], T = its min(k, p+1) best, and
+ * the list is the ascending union of T and Wn (count between
+ * min(k, p+1) and min(k, p+1) + |Wn|; the pages name 1024 global tokens and
+ * 128 forced recent ones without saying whether the two sets may overlap).
  * Scores must be finite and >= 0 (the full layer's scores are).
  * max_sel >= min(k*block_size + window, N) is required.  Workspace: at least
  * hs2_select_workspace(B, Tq, Hkv, N) bytes (covers both modes). */
@@ -144,7 +153,7 @@ size_t hs2_select_workspace(int32_t B, int32_t Tq, int32_t Hkv, int32_t N);
 /* Tighter figure for one block_size (what the call actually checks). */
 size_t hs2_select_workspace_for(int32_t B, int32_t Tq, int32_t Hkv, int32_t N, int32_t block_size);
 int hs2_select_topk_window(const float* scores, int32_t B, int32_t Tq, int32_t Hkv, int32_t N,
-                           int32_t q_pos0, int32_t k, int32_t window, int32_t block_size,
+                           int32_t q_pos0, int32_t k, int32_t window, int32_t block_size, int32_t flags,
                            int32_t* idx, int32_t* count, int32_t max_sel, void* workspace,
                            size_t workspace_bytes, hipStream_t stream);
 
@@ -227,7 +236,7 @@ int hs2_debug_stream_read(const void* buf, size_t bytes, uint32_t* out, int32_t 
 
 /* Full layer and token selection in one call: the results of
  * hs2_full_attn_scores followed by hs2_select_topk_window with block_size 1
- * (same layouts, rules and requirements; both passages above).  With one
+ * (same layouts, rules, flags and requirements; both passages above).  With one
  * query token per (b, kv head) unit, the full layer's merge kernel sets the
  * selection's rows up and its score kernel counts the selection's first radix
  * digit while writing the scores, which saves the selection two passes over
@@ -236,8 +245,8 @@ int hs2_debug_stream_read(const void* buf, size_t bytes, uint32_t* out, int32_t 
 size_t hs2_full_attn_topk_workspace(const hs2_kv_desc* kv, int32_t Tq, int32_t Hq);
 int hs2_full_attn_topk(const hs2_kv_desc* kv, const void* q, hs2_dtype q_dtype, int32_t Tq, int32_t Hq,
                        int32_t q_pos0, float softmax_scale, void* out, float* lse, float* scores, int32_t k,
-                       int32_t window, int32_t* idx, int32_t* count, int32_t max_sel, void* workspace,
-                       size_t workspace_bytes, hipStream_t stream);
+                       int32_t window, int32_t flags, int32_t* idx, int32_t* count, int32_t max_sel,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Per-kernel timing with HIP events on the launch stream (off by default; a
  * measurement aid, process-wide).  While enabled, every kernel launch of the

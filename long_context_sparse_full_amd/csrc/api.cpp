@@ -181,7 +181,7 @@ int hip_fail(hipError_t e, const char* what) {
 // ---------------------------------------------------------------------------
 const char* const kKernelNames[] = {"full_scan",   "combine",     "score",        "select_init",
                                     "select_hist", "select_collect", "select_finish", "select_emit",
-                                    "select_block_mass", "select_block_pick", "sparse_gather", "kv_bridge", "stream_read",
+                                    "select_window", "select_block_mass", "select_block_pick", "sparse_gather", "kv_bridge", "stream_read",
                                     "chunk_full",  "chunk_score", nullptr};
 
 // Timing state (only while hs2_timing_enable(1) is in force): the event pairs
@@ -248,6 +248,7 @@ namespace {
 // pass builds the first radix histogram (layout of plan_select over ws).
 struct SelPrep {
   int32_t k, window;
+  int32_t cand_window;  // window, or 0 when the window competes
   void* ws;
   bool hist0_done = false;
 };
@@ -258,8 +259,8 @@ int full_layer(const hs2_kv_desc* kv, const void* q, hs2_dtype q_dtype, int32_t 
 // hs2_select_topk_window; pre_hist0: the row state and first histogram are
 // already built (full layer's merge and score pass)
 int select_impl(const float* scores, int32_t B, int32_t Tq, int32_t Hkv, int32_t N, int32_t q_pos0, int32_t k,
-                int32_t window, int32_t block_size, int32_t* idx, int32_t* count, int32_t max_sel, void* workspace,
-                size_t workspace_bytes, hipStream_t stream, bool pre_hist0);
+                int32_t window, int32_t block_size, int32_t flags, int32_t* idx, int32_t* count, int32_t max_sel,
+                void* workspace, size_t workspace_bytes, hipStream_t stream, bool pre_hist0);
 }  // namespace
 
 extern "C" {
@@ -376,7 +377,7 @@ int full_layer(const hs2_kv_desc* kv, const void* q, hs2_dtype q_dtype, int32_t 
     c.sel_state = at<int32_t>(sel->ws, sp.off_state);
     c.sel_hist = sel_hist = at<int32_t>(sel->ws, sp.off_hist);
     c.sel_k = sel->k;
-    c.sel_window = sel->window;
+    c.sel_window = sel->cand_window;
     c.q_pos0 = q_pos0;
   }
   if ((e = hs2::launch_combine(c, pl.units, stream)) != hipSuccess) return hip_fail(e, "combine launch");
@@ -397,7 +398,7 @@ int full_layer(const hs2_kv_desc* kv, const void* q, hs2_dtype q_dtype, int32_t 
   s.scores = scores;
   s.sel_hist = sel_hist;
   s.sel_k = pre_sel ? sel->k : 0;
-  s.sel_window = pre_sel ? sel->window : 0;
+  s.sel_window = pre_sel ? sel->cand_window : 0;
   s.q = q;
   s.Hq = Hq;
   s.D = kv->D;
@@ -425,12 +426,13 @@ size_t hs2_full_attn_topk_workspace(const hs2_kv_desc* kv, int32_t Tq, int32_t H
 
 int hs2_full_attn_topk(const hs2_kv_desc* kv, const void* q, hs2_dtype q_dtype, int32_t Tq, int32_t Hq,
                        int32_t q_pos0, float softmax_scale, void* out, float* lse, float* scores, int32_t k,
-                       int32_t window, int32_t* idx, int32_t* count, int32_t max_sel, void* workspace,
+                       int32_t window, int32_t flags, int32_t* idx, int32_t* count, int32_t max_sel, void* workspace,
                        size_t workspace_bytes, hipStream_t stream) {
   int st = check_kv(kv, "hs2_full_attn_topk");
   if (st) return st;
   if (!idx || !count) return fail(HS2_ERR_INVALID_ARG, "hs2_full_attn_topk: NULL idx/count");
   if (k < 0 || window < 0) return fail(HS2_ERR_INVALID_ARG, "hs2_full_attn_topk: need k >= 0 and window >= 0");
+  if (flags & ~HS2_SEL_WINDOW_COMPETES) return fail(HS2_ERR_INVALID_ARG, "hs2_full_attn_topk: unknown flags");
   const int64_t need_sel = std::min<int64_t>((int64_t)k + window, kv->N);
   if (max_sel < need_sel)
     return fail(HS2_ERR_INVALID_ARG, "hs2_full_attn_topk: max_sel must be >= min(k + window, N) = " +
@@ -443,11 +445,12 @@ int hs2_full_attn_topk(const hs2_kv_desc* kv, const void* q, hs2_dtype q_dtype, 
     return fail(HS2_ERR_WORKSPACE, "hs2_full_attn_topk: workspace needs " + std::to_string(need_ws) + " bytes");
   const size_t full_bytes = plan_full(kv, Tq, Hq).total;
   void* rest = static_cast<char*>(workspace) + full_bytes;
-  SelPrep sel{k, window, rest};
+  const int32_t cand_window = (flags & HS2_SEL_WINDOW_COMPETES) ? 0 : window;
+  SelPrep sel{k, window, cand_window, rest};
   st = full_layer(kv, q, q_dtype, Tq, Hq, q_pos0, softmax_scale, out, lse, scores, workspace, full_bytes, stream,
                   &sel);
   if (st) return st;
-  return select_impl(scores, kv->B, Tq, kv->Hkv, kv->N, q_pos0, k, window, 1, idx, count, max_sel, rest,
+  return select_impl(scores, kv->B, Tq, kv->Hkv, kv->N, q_pos0, k, window, 1, flags, idx, count, max_sel, rest,
                      workspace_bytes - full_bytes, stream, sel.hist0_done);
 }
 
@@ -462,9 +465,10 @@ size_t hs2_select_workspace_for(int32_t B, int32_t Tq, int32_t Hkv, int32_t N, i
 }
 
 int hs2_select_topk_window(const float* scores, int32_t B, int32_t Tq, int32_t Hkv, int32_t N, int32_t q_pos0,
-                           int32_t k, int32_t window, int32_t block_size, int32_t* idx, int32_t* count,
-                           int32_t max_sel, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  return select_impl(scores, B, Tq, Hkv, N, q_pos0, k, window, block_size, idx, count, max_sel, workspace,
+                           int32_t k, int32_t window, int32_t block_size, int32_t flags, int32_t* idx,
+                           int32_t* count, int32_t max_sel, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
+  return select_impl(scores, B, Tq, Hkv, N, q_pos0, k, window, block_size, flags, idx, count, max_sel, workspace,
                      workspace_bytes, stream, false);
 }
 
@@ -472,8 +476,8 @@ int hs2_select_topk_window(const float* scores, int32_t B, int32_t Tq, int32_t H
 
 namespace {
 int select_impl(const float* scores, int32_t B, int32_t Tq, int32_t Hkv, int32_t N, int32_t q_pos0, int32_t k,
-                int32_t window, int32_t block_size, int32_t* idx, int32_t* count, int32_t max_sel, void* workspace,
-                size_t workspace_bytes, hipStream_t stream, bool pre_hist0) {
+                int32_t window, int32_t block_size, int32_t flags, int32_t* idx, int32_t* count, int32_t max_sel,
+                void* workspace, size_t workspace_bytes, hipStream_t stream, bool pre_hist0) {
   if (!scores || !idx || !count) return fail(HS2_ERR_INVALID_ARG, "hs2_select_topk_window: NULL scores/idx/count");
   if (B <= 0 || Tq <= 0 || Hkv <= 0 || N <= 0)
     return fail(HS2_ERR_INVALID_ARG, "hs2_select_topk_window: B, Tq, Hkv, N must be positive");
@@ -481,6 +485,10 @@ int select_impl(const float* scores, int32_t B, int32_t Tq, int32_t Hkv, int32_t
     return fail(HS2_ERR_INVALID_ARG, "hs2_select_topk_window: need 0 <= q_pos0 and q_pos0 + Tq <= N");
   if (k < 0 || window < 0 || block_size < 1)
     return fail(HS2_ERR_INVALID_ARG, "hs2_select_topk_window: need k >= 0, window >= 0, block_size >= 1");
+  if (flags & ~HS2_SEL_WINDOW_COMPETES) return fail(HS2_ERR_INVALID_ARG, "hs2_select_topk_window: unknown flags");
+  const bool competes = (flags & HS2_SEL_WINDOW_COMPETES) != 0;
+  if (competes && block_size != 1)
+    return fail(HS2_ERR_UNSUPPORTED, "hs2_select_topk_window: the competing window is token mode only");
   const int64_t need_sel = std::min<int64_t>((int64_t)k * block_size + window, N);
   if (max_sel < need_sel)
     return fail(HS2_ERR_INVALID_ARG, "hs2_select_topk_window: max_sel must be >= min(k*block_size + window, N) = " +
@@ -501,6 +509,8 @@ int select_impl(const float* scores, int32_t B, int32_t Tq, int32_t Hkv, int32_t
   p.q_pos0 = q_pos0;
   p.k = k;
   p.window = window;
+  p.cand_window = competes ? 0 : window;
+  p.competes = competes ? 1 : 0;
   p.block_size = block_size;
   p.max_sel = max_sel;
   p.nchunks = pl.nchunks;

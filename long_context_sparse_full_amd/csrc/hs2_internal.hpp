@@ -88,7 +88,8 @@ struct CombineParams {
   // token selection prepared by the merge (one query token per unit): the
   // state words and digit histograms of row `unit` at sel_state + unit * 16
   // and sel_hist + unit * 3 * kHistBins are initialised as the selection's
-  // own set-up would; sel_state nullptr = no selection
+  // own set-up would (candidates [0, p - sel_window]: the selection's
+  // candidate window); sel_state nullptr = no selection
   int32_t* sel_state;
   int32_t* sel_hist;
   int sel_k, sel_window, q_pos0;
@@ -102,7 +103,8 @@ struct ScoreParams {
   int rows, tpack, n_tpacks, G, Hkv, Tq, N, q_pos0;
   float* scores;  // [B, Tq, Hkv, N]
   // one query token per unit: also count the first radix digit of every
-  // candidate's score (positions [0, p - sel_window]) into the selection's
+  // candidate's score (positions [0, p - sel_window], sel_window being the
+  // selection's candidate window) into the selection's
   // pass-0 histogram sel_hist + unit * 3 * kHistBins, cleared beforehand by the
   // merge; rows whose selection needs no radix pass are skipped.  nullptr = none
   int32_t* sel_hist;
@@ -124,6 +126,10 @@ struct ScoreParams {
 struct SelectParams {
   const float* scores;  // [units][N]
   int units, Tq, Hkv, N, q_pos0, k, window, block_size, max_sel, nchunks;
+  // candidates of a query at p: [0, p - cand_window]; cand_window = window,
+  // or 0 when the window competes (then a last kernel places the window after
+  // the selected positions below it)
+  int cand_window, competes;
   int32_t* idx;
   int32_t* count;
   int32_t* state;   // [units][16]

@@ -93,7 +93,7 @@ __global__ void __launch_bounds__(256) sel_init(SelectParams P) {
   const int u = blockIdx.x;
   const int t = (u / P.Hkv) % P.Tq;
   sel_init_row(P.state + (int64_t)u * ST_WORDS, P.block_size == 1 ? P.hist + (int64_t)u * 3 * kHistBins : nullptr,
-               P.q_pos0 + t, P.k, P.window, P.block_size, threadIdx.x, 256);
+               P.q_pos0 + t, P.k, P.cand_window, P.block_size, threadIdx.x, 256);
 }
 
 // digits: pass 0 = bits 31..20, pass 1 = bits 19..8, pass 2 = bits 7..0
@@ -239,7 +239,7 @@ __global__ void __launch_bounds__(256) sel_hist(SelectParams P) {
   int32_t* st = P.state + (int64_t)u * ST_WORDS;
   // the row's mode and candidate count follow from its position (the same
   // values the set-up stored), so the score loads need not wait for a state read
-  const int ncand = sel_ncand(P.q_pos0 + (u / P.Hkv) % P.Tq, P.window);
+  const int ncand = sel_ncand(P.q_pos0 + (u / P.Hkv) % P.Tq, P.cand_window);
   const int take = sel_take(ncand, P.k, 1);
   if (sel_mode(take, ncand, 1) != MODE_RADIX) return;
   if (PASS == 2 && P.collected && st[ST_COMPACT]) return;  // finished by the collected path
@@ -293,8 +293,10 @@ __global__ void __launch_bounds__(256) sel_hist(SelectParams P) {
 }
 
 // Forced window after the `take` selected positions, then the count and the
-// -1 padding of the row's list.
+// -1 padding of the row's list.  When the window competes, sel_window_merge
+// writes these instead (some selected positions may lie in the window).
 __device__ __forceinline__ void write_window(const SelectParams& P, int u, int take, int p, int32_t* out) {
+  if (P.competes) return;
   const int wlo = max(0, p - P.window + 1);
   const int nw = p - wlo + 1;
   for (int i = threadIdx.x; i < nw; i += 256) out[take + i] = wlo + i;
@@ -495,7 +497,7 @@ __global__ void __launch_bounds__(256) sel_emit(SelectParams P) {
   const int u = blockIdx.y, chunk = blockIdx.x;
   const int32_t* st = P.state + (int64_t)u * ST_WORDS;
   const int p = P.q_pos0 + (u / P.Hkv) % P.Tq;  // as stored by the set-up
-  const int ncand = sel_ncand(p, P.window);
+  const int ncand = sel_ncand(p, P.cand_window);
   const int take = sel_take(ncand, P.k, 1);
   const int mode = sel_mode(take, ncand, 1);
   int32_t* out = P.idx + (int64_t)u * P.max_sel;
@@ -614,6 +616,32 @@ __global__ void __launch_bounds__(256) sel_emit(SelectParams P) {
         ++sl;
       }
   }
+}
+
+// The window competes (candidates [0, p]): the emit wrote the `take`
+// selected positions in ascending order, some of them possibly inside the
+// window [p - window + 1, p], which are then its last entries.  One workgroup
+// per row counts them, and the window follows the selected positions below it
+// (so the list is the ascending union, each position once), then the count
+// and the -1 padding.
+__global__ void __launch_bounds__(256) sel_window_merge(SelectParams P) {
+  __shared__ int32_t sm[264];
+  const int u = blockIdx.x;
+  const int p = P.q_pos0 + (u / P.Hkv) % P.Tq;
+  const int take = sel_take(sel_ncand(p, P.cand_window), P.k, 1);
+  const int wlo = max(0, p - P.window + 1);
+  const int nw = p - wlo + 1;
+  int32_t* out = P.idx + (int64_t)u * P.max_sel;
+  // the last min(take, nw) selected entries hold every selected window position
+  const int first = take - min(take, nw);
+  int32_t c = 0;
+  for (int i = first + threadIdx.x; i < take; i += 256) c += out[i] >= wlo;
+  int32_t in_window;
+  block_exclusive_scan<int32_t>(c, sm, in_window);  // its barriers also order the reads before the writes
+  const int below = take - in_window;
+  for (int i = threadIdx.x; i < nw; i += 256) out[below + i] = wlo + i;
+  for (int i = below + nw + threadIdx.x; i < P.max_sel; i += 256) out[i] = -1;
+  if (threadIdx.x == 0) P.count[u] = below + nw;
 }
 
 // ---------------------------------------------------------------------------
@@ -956,6 +984,7 @@ hipError_t launch_select(const SelectParams& p_in, hipStream_t s) {
     if (small) HS2_L("select_hist", (sel_hist<2, true>), grid_c);
     else HS2_L("select_hist", (sel_hist<2, false>), grid_c);
     HS2_L("select_emit", sel_emit, grid_c);
+    if (p.competes) HS2_L("select_window", sel_window_merge, dim3(p.units));
   } else {
     const dim3 grid_t((p.N + kMassTile - 1) / kMassTile, p.units);
     switch (p.block_size) {

@@ -23,6 +23,7 @@ if not os.path.exists(LIB_PATH):
 _lib = ctypes.CDLL(LIB_PATH)
 
 F32, BF16, FP8_E4M3FN = 0, 1, 2
+SEL_WINDOW_COMPETES = 1
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
 
 
@@ -59,11 +60,11 @@ _full = _sig("hs2_full_attn_scores", ctypes.c_int,
              [_KVP, _vp, _i32, _i32, _i32, _i32, _f32, _vp, _vp, _vp, _vp, _sz, _vp])
 _topk_ws = _sig("hs2_full_attn_topk_workspace", _sz, [_KVP, _i32, _i32])
 _topk = _sig("hs2_full_attn_topk", ctypes.c_int,
-             [_KVP, _vp, _i32, _i32, _i32, _i32, _f32, _vp, _vp, _vp, _i32, _i32, _vp, _vp, _i32, _vp, _sz, _vp])
+             [_KVP, _vp, _i32, _i32, _i32, _i32, _f32, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _i32, _vp, _sz, _vp])
 _sel_ws = _sig("hs2_select_workspace", _sz, [_i32, _i32, _i32, _i32])
 _sel_ws_for = _sig("hs2_select_workspace_for", _sz, [_i32, _i32, _i32, _i32, _i32])
 _select = _sig("hs2_select_topk_window", ctypes.c_int,
-               [_vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _i32, _vp, _sz, _vp])
+               [_vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _i32, _vp, _sz, _vp])
 _sparse = _sig("hs2_sparse_attn_gather", ctypes.c_int,
                [_KVP, _vp, _i32, _i32, _i32, _f32, _vp, _vp, _i32, _vp, _vp, _vp])
 _sparse_ws_size = _sig("hs2_sparse_attn_workspace", _sz, [_i32, _i32, _i32, _i32, _i32])
@@ -184,8 +185,9 @@ def full_attn_topk_workspace(k, v, Tq: int, Hq: int) -> int:
 
 def full_attn_topk(k, v, q, q_pos0: int, topk: int, window: int, max_sel: int | None = None,
                    softmax_scale: float | None = None, k_scale=None, v_scale=None, out=None, lse=None, scores=None,
-                   idx=None, count=None, workspace=None, want_lse: bool = True):
-    """Full layer + token top-k with forced window in one call.
+                   idx=None, count=None, workspace=None, want_lse: bool = True, window_competes: bool = False):
+    """Full layer + token top-k with forced window in one call (window_competes:
+    the window takes no budget of its own; see hs2.h).
     Returns (out, lse, scores, idx [B,Tq,Hkv,max_sel] int32, count [B,Tq,Hkv] int32)."""
     d = kv_desc(k, v, k_scale, v_scale)
     B, Tq, Hq, D = q.shape
@@ -210,7 +212,7 @@ def full_attn_topk(k, v, q, q_pos0: int, topk: int, window: int, max_sel: int | 
     _dense(q, out, lse, scores, idx, count, workspace)
     st = _topk(ctypes.byref(d), q.data_ptr(), _dtype_code(q), Tq, Hq, int(q_pos0), float(softmax_scale),
                out.data_ptr(), None if lse is None else lse.data_ptr(), scores.data_ptr(), int(topk), int(window),
-               idx.data_ptr(), count.data_ptr(), int(max_sel), workspace.data_ptr(), workspace.numel(), _stream())
+               SEL_WINDOW_COMPETES if window_competes else 0, idx.data_ptr(), count.data_ptr(), int(max_sel), workspace.data_ptr(), workspace.numel(), _stream())
     _check(st, "hs2_full_attn_topk")
     return out, lse, scores, idx, count
 
@@ -222,7 +224,7 @@ def select_workspace(B, Tq, Hkv, N, block_size: int | None = None) -> int:
 
 
 def select_topk_window(scores, q_pos0: int, k: int, window: int, block_size: int = 1, max_sel: int | None = None,
-                       idx=None, count=None, workspace=None):
+                       idx=None, count=None, workspace=None, window_competes: bool = False):
     """Top-k (token or block) + forced window: returns (idx int32, count int32)."""
     B, Tq, Hkv, N = scores.shape
     if max_sel is None:
@@ -236,7 +238,7 @@ def select_topk_window(scores, q_pos0: int, k: int, window: int, block_size: int
         workspace = torch.empty(max(select_workspace(B, Tq, Hkv, N, block_size), 256), dtype=torch.uint8, device=dev)
     _dense(scores, idx, count, workspace)
     st = _select(scores.data_ptr(), B, Tq, Hkv, N, int(q_pos0), int(k), int(window), int(block_size),
-                 idx.data_ptr(), count.data_ptr(), int(max_sel), workspace.data_ptr(), workspace.numel(), _stream())
+                 SEL_WINDOW_COMPETES if window_competes else 0, idx.data_ptr(), count.data_ptr(), int(max_sel), workspace.data_ptr(), workspace.numel(), _stream())
     _check(st, "hs2_select_topk_window")
     return idx, count
 

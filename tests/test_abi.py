@@ -139,11 +139,11 @@ def test_workspace_figures(hs2):
 
 @pytest.mark.parametrize("case,want", [
     ("small_ws", -3), ("max_sel_small", -1), ("neg_k", -1), ("neg_window", -1), ("block0", -1),
-    ("qpos_past_end", -1), ("null_idx", -1),
+    ("qpos_past_end", -1), ("null_idx", -1), ("bad_flags", -1), ("competes_blocks", -2),
 ])
 def test_select_validation(hs2, case, want):
-    a = dict(scores=FAKE, B=1, Tq=1, Hkv=4, N=4096, q_pos0=4095, k=1024, window=128, bs=1, idx=FAKE, cnt=FAKE,
-             max_sel=1152, ws=FAKE, wsb=1 << 40)
+    a = dict(scores=FAKE, B=1, Tq=1, Hkv=4, N=4096, q_pos0=4095, k=1024, window=128, bs=1, flags=0, idx=FAKE,
+             cnt=FAKE, max_sel=1152, ws=FAKE, wsb=1 << 40)
     if case == "small_ws":
         a["wsb"] = 100
     elif case == "max_sel_small":
@@ -158,14 +158,18 @@ def test_select_validation(hs2, case, want):
         a["q_pos0"] = 4096
     elif case == "null_idx":
         a["idx"] = None
+    elif case == "bad_flags":
+        a["flags"] = 2
+    elif case == "competes_blocks":
+        a["flags"], a["bs"], a["k"] = 1, 64, 16
     st = hs2._select(a["scores"], a["B"], a["Tq"], a["Hkv"], a["N"], a["q_pos0"], a["k"], a["window"], a["bs"],
-                     a["idx"], a["cnt"], a["max_sel"], a["ws"], a["wsb"], None)
+                     a["flags"], a["idx"], a["cnt"], a["max_sel"], a["ws"], a["wsb"], None)
     assert st == want
 
 
 def test_select_max_sel_rule_uses_context_cap(hs2):
     # N smaller than k + window: max_sel = N suffices (fails later only on the workspace)
-    st = hs2._select(FAKE, 1, 1, 1, 600, 599, 1024, 128, 1, FAKE, FAKE, 600, FAKE, 10, None)
+    st = hs2._select(FAKE, 1, 1, 1, 600, 599, 1024, 128, 1, 0, FAKE, FAKE, 600, FAKE, 10, None)
     assert st == -3
 
 
@@ -174,12 +178,14 @@ def test_full_attn_topk_validation(hs2):
     ws = int(hs2._topk_ws(ctypes.byref(d), 1, 16))
     full = int(hs2._full_ws(ctypes.byref(d), 1, 16))
     assert ws > full
-    args = lambda idx=FAKE, k=8, window=4, max_sel=12, wsb=ws: (ctypes.byref(d), FAKE, 1, 1, 16, 255, 0.1, FAKE, None,
-                                                                 FAKE, k, window, idx, FAKE, max_sel, FAKE, wsb, None)
+    args = lambda idx=FAKE, k=8, window=4, max_sel=12, wsb=ws, flags=0: (ctypes.byref(d), FAKE, 1, 1, 16, 255, 0.1,
+                                                                          FAKE, None, FAKE, k, window, flags, idx, FAKE,
+                                                                          max_sel, FAKE, wsb, None)
     assert hs2._topk(*args(idx=None)) == -1            # NULL idx
     assert hs2._topk(*args(k=-1)) == -1                # negative k
     assert hs2._topk(*args(max_sel=11)) == -1          # max_sel < k + window
     assert hs2._topk(*args(wsb=ws - 1)) == -3          # workspace too small
+    assert hs2._topk(*args(flags=4)) == -1             # unknown flag
 
 
 def test_sparse_and_bridge_validation(hs2):

@@ -629,3 +629,87 @@ def test_dominant_key_scores_exact(hs2, case):
     i_or, c_or = oracle.select_topk_window(s_or, spec.q_pos0, k, spec.window, max_sel=spec.max_sel)
     gu.check_selection_vs_oracle(idx, cnt, i_or, c_or, s_or, spec.q_pos0, k, spec.window)
     gu.check_structure(idx, cnt, spec.q_pos0, k, spec.window, N)
+
+
+# ------------------------------------------------ competing window (reading o3)
+
+COMPETE_CASES = [
+    # B, Tq, Hkv, N, k, window, kind
+    (1, 1, 4, 70000, 1024, 128, "random"),
+    (2, 3, 2, 9000, 300, 32, "recent"),       # recent positions score high: the top-k overlaps the window
+    (1, 2, 2, 5000, 100, 8, "ties"),
+    (1, 1, 1, 3000, 0, 16, "random"),         # k = 0: the window alone
+    (1, 1, 1, 3000, 5000, 16, "random"),      # k >= p + 1: every position
+    (1, 4, 1, 100, 10, 128, "random"),        # p < window
+    (1, 1, 2, 5000, 40, 0, "random"),         # no window
+    (1, 2, 2, 40000, 2049, 64, "recent"),     # k above the collected path's limit
+    (1, 512, 4, 16384, 1024, 128, "levels"),  # 2048 rows: the collected path
+    (1, 512, 4, 16384, 1024, 128, "recent"),
+]
+
+
+def compete_scores(rng, shape, kind):
+    B, Tq, Hkv, N = shape
+    if kind == "random":
+        return rng.random(shape).astype(np.float32) * 1e-3
+    if kind == "ties":
+        return (rng.integers(0, 6, shape) / 64.0).astype(np.float32)
+    if kind == "levels":
+        return (rng.integers(0, 20000, shape) / 20000.0 * 1e-3).astype(np.float32)
+    # "recent": a ramp over positions plus noise, so the highest scores sit at the end
+    ramp = np.linspace(0.0, 1e-3, N, dtype=np.float32)
+    return (ramp + rng.random(shape).astype(np.float32) * 2e-4).astype(np.float32)
+
+
+@pytest.mark.parametrize("case", COMPETE_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_select_window_competes_bit_exact(hs2, case):
+    """The other reading of the budgets (the window takes no budget of its
+    own): bit for bit equal to the oracle's window_competes selection on the
+    same scores, the window always in, no position twice."""
+    B, Tq, Hkv, N, k, W, kind = case
+    gu.log(f"select window competes {case}")
+    rng = np.random.default_rng(N + 7 * k + W)
+    sc = compete_scores(rng, (B, Tq, Hkv, N), kind)
+    qp = N - Tq
+    max_sel = min(N, k + W)
+    s = torch.from_numpy(sc).cuda()
+    idx, cnt = hs2.select_topk_window(s, qp, k, W, max_sel=max_sel, window_competes=True)
+    torch.cuda.synchronize()
+    idx, cnt = gu.host(idx), gu.host(cnt)
+    i_or, c_or = oracle.select_topk_window(sc.astype(np.float64), qp, k, W, max_sel=max_sel, window_competes=True)
+    assert np.array_equal(cnt, c_or), "counts differ"
+    assert np.array_equal(idx, i_or), "index lists differ"
+    overlap = 0
+    for u in np.ndindex(B, Tq, Hkv):
+        p = qp + u[1]
+        sel = idx[u][: cnt[u]]
+        assert np.all(np.diff(sel) > 0) and (sel.size == 0 or (sel[0] >= 0 and sel[-1] <= p))
+        wlo = max(0, p - W + 1)
+        assert set(range(wlo, p + 1)) <= set(sel.tolist()), f"window missing at {u}"
+        take = min(k, p + 1)
+        overlap += take + (p - wlo + 1) - int(cnt[u])
+        assert np.all(idx[u][cnt[u]:] == -1)
+    gu.log(f"  top-k positions inside the window (over all rows): {overlap}")
+    if kind == "recent" and k > 0:
+        assert overlap > 0, "the case meant to overlap the window did not"
+
+
+@pytest.mark.parametrize("kv,N", [("bf16", 20000), ("fp8", 70001)])
+def test_full_attn_topk_window_competes(hs2, kv, N):
+    """The one-call full layer + top-k with the competing window (the decode
+    path, where the merge and score kernels prepare the selection): equal to
+    the oracle's window_competes selection on the returned scores."""
+    spec = small_spec(kv, B=1, N=N, Hkv=4, k=1024, window=128, needles=8)
+    inp = synth.make_inputs(spec, seed=606)
+    blk = gu.DeviceBlock(inp)
+    out, lse, sc, idx, cnt = hs2.full_attn_topk(blk.k, blk.v, blk.q, spec.q_pos0, spec.k, spec.window,
+                                                max_sel=spec.max_sel, k_scale=blk.ks, v_scale=blk.vs,
+                                                window_competes=True)
+    torch.cuda.synchronize()
+    sc, idx, cnt = gu.host(sc), gu.host(idx), gu.host(cnt)
+    i_or, c_or = oracle.select_topk_window(sc.astype(np.float64), spec.q_pos0, spec.k, spec.window,
+                                           max_sel=spec.max_sel, window_competes=True)
+    assert np.array_equal(cnt, c_or) and np.array_equal(idx, i_or)
+    o_or, l_or, s_or = oracle_full(inp, spec)
+    gu.assert_scores(sc, s_or)
+    gu.assert_rows_rel(gu.host(out), o_or, kv)
