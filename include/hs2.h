@@ -206,6 +206,25 @@ int hs2_sparse_attn_gather_static(const hs2_kv_desc* kv, const void* q, hs2_dtyp
                                   const int32_t* count, int32_t max_sel, void* out, float* lse,
                                   hipStream_t stream);
 
+/* Sliding-window attention of the self-decoder's hybrid layers
+ * (javabetter.cn: MiMo-V2.6-Flash's 39 sliding-window layers, each token
+ * attending to its nearest 128 tokens; the self-decoder mixes such layers
+ * with full attention -- javabetter.cn, Self-Decoder paragraph; siami.tw
+ * section one).  For every (b, t, h), p = q_pos0 + t, rows
+ * j in [max(0, p - window + 1), p] (the current token included):
+ *   out[b,t,h] = sum_j softmax_j(softmax_scale * <q[b,t,h], k[b,g,j]>) v[b,g,j]
+ *   lse[b,t,h] = log sum_j exp(...)       (may be NULL)
+ * This is the sparse layer with k = 0 and the window alone; it reads the
+ * window's rows directly (no index list).  Prefill-sized calls (bf16 or FP8
+ * cache, 4, 8 or 16 query heads per kv head, at least 4 packs of 16/G tokens
+ * per (b, kv head)) run a banded matrix-core pass over the LDS-staged K/V
+ * tiles of each 16-token block's window; others one workgroup per
+ * (b, t, g).  Requires 0 <= q_pos0, q_pos0 + Tq <= N, window >= 1.  No
+ * workspace. */
+int hs2_swa_attn(const hs2_kv_desc* kv, const void* q, hs2_dtype q_dtype, int32_t Tq, int32_t Hq,
+                 int32_t q_pos0, int32_t window, float softmax_scale, void* out, float* lse,
+                 hipStream_t stream);
+
 /* KV bridge (javabetter.cn, KV Bridging paragraph: a cross-decoder full layer
  * computes its K and V from a self-decoder layer's hidden state, with its own
  * parameters).  y = hidden [T, d_model] (bf16) x w_kv [d_model, 2*Hkv*D]

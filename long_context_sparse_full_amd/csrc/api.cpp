@@ -182,7 +182,7 @@ int hip_fail(hipError_t e, const char* what) {
 const char* const kKernelNames[] = {"full_scan",   "combine",     "score",        "select_init",
                                     "select_hist", "select_collect", "select_finish", "select_emit",
                                     "select_window", "select_block_mass", "select_block_pick", "sparse_gather", "kv_bridge", "stream_read",
-                                    "chunk_full",  "chunk_score", nullptr};
+                                    "chunk_full",  "chunk_score", "swa_chunk", nullptr};
 
 // Timing state (only while hs2_timing_enable(1) is in force): the event pairs
 // of the launches since the last reset.  Events are created per launch and
@@ -761,6 +761,59 @@ int hs2_sparse_attn_gather_static(const hs2_kv_desc* kv, const void* q, hs2_dtyp
   void* ws = nullptr;
   if ((st = static_scratch(stream, &ws))) return st;
   return launch_split_gather(name, kv, q, Tq, Hq, softmax_scale, idx, count, max_sel, out, lse, gp, ws, stream);
+}
+
+int hs2_swa_attn(const hs2_kv_desc* kv, const void* q, hs2_dtype q_dtype, int32_t Tq, int32_t Hq, int32_t q_pos0,
+                 int32_t window, float softmax_scale, void* out, float* lse, hipStream_t stream) {
+  const char* name = "hs2_swa_attn";
+  int st = check_kv(kv, name);
+  if (st) return st;
+  if ((st = check_q(kv, q, q_dtype, Tq, Hq, name))) return st;
+  if (q_pos0 < 0 || (int64_t)q_pos0 + Tq > kv->N)
+    return fail(HS2_ERR_INVALID_ARG, "hs2_swa_attn: need 0 <= q_pos0 and q_pos0 + Tq <= N");
+  if (window < 1) return fail(HS2_ERR_INVALID_ARG, "hs2_swa_attn: window must be at least 1");
+  if (!out) return fail(HS2_ERR_INVALID_ARG, "hs2_swa_attn: out must not be NULL");
+  if (!al16(out) || (lse && ((uintptr_t)lse & 3)))
+    return fail(HS2_ERR_INVALID_ARG, "hs2_swa_attn: out must be 16-byte aligned, lse 4-byte");
+  if (!std::isfinite(softmax_scale)) return fail(HS2_ERR_INVALID_ARG, "hs2_swa_attn: softmax_scale not finite");
+  hs2::ScanParams p{};
+  p.k = kv->k;
+  p.v = kv->v;
+  p.sb = kv->stride_b;
+  p.sh = kv->stride_h;
+  p.sn = kv->stride_n;
+  p.k_scale = kv->k_scale;
+  p.v_scale = kv->v_scale;
+  p.B = kv->B;
+  p.Hkv = kv->Hkv;
+  p.N = kv->N;
+  p.D = kv->D;
+  p.G = Hq / kv->Hkv;
+  p.q = q;
+  p.Tq = Tq;
+  p.Hq = Hq;
+  p.q_pos0 = q_pos0;
+  p.scale_log2 = softmax_scale * 1.44269504088896340736f;
+  p.band = window;
+  p.out = out;
+  p.lse = lse;
+  p.nsplit = 1;
+  const FullPlan pl = plan_full(kv, Tq, Hq);
+  hipError_t e;
+  if (pl.chunk) {  // many query tokens: the banded matrix-core pass, one split, final outputs
+    p.tpack = pl.tpack;
+    p.n_tpacks = pl.n_tpacks;
+    p.rows = pl.rows;
+    p.split_len = kv->N;
+    e = hs2::launch_chunk_full(p, kv->dtype, stream);
+  } else {  // few query tokens: one workgroup per (b, t, g) over its contiguous window
+    p.tpack = 1;
+    p.n_tpacks = Tq;
+    p.rows = p.G;
+    e = hs2::launch_scan(p, kv->dtype, true, false, stream);
+  }
+  if (e != hipSuccess) return hip_fail(e, "hs2_swa_attn launch");
+  return HS2_OK;
 }
 
 int hs2_kv_bridge(const void* hidden, int32_t T, int32_t d_model, const void* w_kv, const hs2_kv_out_desc* kv_out,

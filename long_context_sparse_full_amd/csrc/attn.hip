@@ -704,9 +704,10 @@ __device__ __forceinline__ void flash_qk(const char* kl, const u32x4_t (&qf)[RG]
 }
 
 // Softmax and PV of one tile whose logits s came from flash_qk.
-template <bool FP8, int D, int RG>
+template <bool FP8, int D, int RG, bool BAND>
 __device__ __forceinline__ void flash_pv(const char* vl, f32x4_t (&s)[RG][2], float cs, int j0,
-                                         const int (&jlim)[RG], bool need_mask, int r, int g4, ChunkState<D, RG>& S) {
+                                         const int (&jlim)[RG], const int (&jlo)[RG], bool need_mask, int r, int g4,
+                                         ChunkState<D, RG>& S) {
   constexpr int VE = D / 16;
   // Online softmax against each row's reference S.m (mu = S.m, or 0 before
   // the row has one).  The exponents x = s cs - mu are formed first; only when
@@ -720,8 +721,10 @@ __device__ __forceinline__ void flash_pv(const char* vl, f32x4_t (&s)[RG][2], fl
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii)
-          if (j0 + 16 * hh + 4 * g4 + ii > jlim[rg]) s[rg][hh][ii] = kNegInf;
+        for (int ii = 0; ii < 4; ++ii) {
+          const int j = j0 + 16 * hh + 4 * g4 + ii;
+          if (j > jlim[rg] || (BAND && j < jlo[rg])) s[rg][hh][ii] = kNegInf;
+        }
     }
     float x[2][4];
 #pragma unroll
@@ -814,9 +817,11 @@ __device__ __forceinline__ void flash_pv(const char* vl, f32x4_t (&s)[RG][2], fl
 }
 
 // 3 waves per SIMD: 3 workgroups of 48 KiB LDS rings per CU (bf16 D = 128),
-// at most 168 VGPRs per wave
-template <bool FP8, int D>
-__global__ void __launch_bounds__(256, 3) chunk_flash(ScanParams P) {
+// at most 168 VGPRs per wave.  BAND: sliding-window attention (P.band rows
+// ending at each query), one split, final outputs written here; a handful of
+// tiles per workgroup, so 2 waves per SIMD (the row limits need registers).
+template <bool FP8, int D, bool BAND>
+__global__ void __launch_bounds__(256, BAND ? 2 : 3) chunk_flash(ScanParams P) {
   constexpr int RG = kFlashRG, VE = D / 16, NC = D / 32;
   constexpr int NBUF = 3;  // LDS tile ring: tile n in buffer n % NBUF, NBUF - 1 tiles in flight
   using FG = FlashGeom<FP8, D>;
@@ -830,20 +835,26 @@ __global__ void __launch_bounds__(256, 3) chunk_flash(ScanParams P) {
   const int blk_w = it.blk * 4 + wave;  // this wave's block of RG packs
 
   u32x4_t qf[RG][NC];
-  int jlim[RG];
+  int jlim[RG], jlo[RG];
 #pragma unroll
   for (int rg = 0; rg < RG; ++rg) {
     const ChunkRows cr = chunk_row<RG>(P, blk_w, rg, r);
     jlim[rg] = cr.jlim;
+    jlo[rg] = BAND ? cr.jlim - P.band + 1 : 0;  // sliding window: the row's first position
     load_q<FP8, D>(qf[rg], P, b, cr.ok ? cr.t : 0, g * P.G + (r % P.G), cr.ok, g4);
   }
   const int t_first = it.blk * 4 * RG * P.tpack;  // first token of the workgroup
   const int t_last = min(t_first + 4 * RG * P.tpack, P.Tq) - 1;
   const int p_max = P.q_pos0 + t_last;
   const int wt_first = blk_w * RG * P.tpack;  // first token of this wave
+  const int wt_last = min(wt_first + RG * P.tpack, P.Tq) - 1;
   const int j_nomask = P.q_pos0 + min(wt_first, P.Tq - 1);
-  const int j_begin = it.split * P.split_len;
-  const int j_end = min(j_begin + P.split_len, p_max + 1);
+  // sliding window (one split): from the window start of the workgroup's first
+  // token, in whole tiles; tiles before the window start of this wave's last
+  // token need the lower mask
+  const int j_begin = BAND ? max(0, P.q_pos0 + t_first - P.band + 1) & ~31 : it.split * P.split_len;
+  const int j_end = BAND ? p_max + 1 : min(j_begin + P.split_len, p_max + 1);
+  const int jlo_nomask = BAND ? P.q_pos0 + max(wt_last, 0) - P.band + 1 : 0;
   const int ntile = j_end > j_begin ? (j_end - j_begin + 31) / 32 : 0;
 
   const int64_t kvoff = ((int64_t)b * P.sb + (int64_t)g * P.sh) * FG::EB;
@@ -882,7 +893,8 @@ __global__ void __launch_bounds__(256, 3) chunk_flash(ScanParams P) {
     const int j0 = j_begin + 32 * n;
     f32x4_t sc[RG][2];
     flash_qk<FP8, D, RG>(tiles[B], qf, r, g4, sc);
-    flash_pv<FP8, D, RG>(tiles[B] + FG::HALF, sc, cs, j0, jlim, j0 + 31 > j_nomask, r, g4, S);
+    flash_pv<FP8, D, RG, BAND>(tiles[B] + FG::HALF, sc, cs, j0, jlim, jlo,
+                               j0 + 31 > j_nomask || (BAND && j0 < jlo_nomask), r, g4, S);
   };
   static_assert(NBUF == 3 || NBUF == 4, "the unrolled ring below has 3 or 4 buffers");
   for (int n = 0; n < ntile; n += NBUF) {
@@ -906,6 +918,22 @@ __global__ void __launch_bounds__(256, 3) chunk_flash(ScanParams P) {
     l = sum_x16(l);
     l = sum_x32(l);
     if (r >= P.rows) continue;
+    if constexpr (BAND) {  // one split: this is the row's whole softmax
+      const int t = tp * P.tpack + r / P.G;
+      if (t >= P.Tq) continue;
+      const int64_t orow = ((int64_t)b * P.Tq + t) * P.Hq + g * P.G + r % P.G;
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+      const float vsc = FP8 ? P.v_scale[b * P.Hkv + g] : 1.f;
+#pragma unroll
+      for (int dt = 0; dt < VE; ++dt)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          const int d = FP8 ? VE * (4 * g4 + ii) + dt : 16 * dt + 4 * g4 + ii;
+          ((__bf16*)P.out)[orow * D + d] = (__bf16)(S.o[rg][dt][ii] * inv * vsc);
+        }
+      if (g4 == 0 && P.lse) P.lse[orow] = l > 0.f ? (S.m[rg] + log2f(l)) * kLn2 : kNegInf;
+      continue;
+    }
     const int unit = (b * P.n_tpacks + tp) * P.Hkv + g;
     const int64_t pb = ((int64_t)unit * P.nsplit + it.split) * 16 + r;
 #pragma unroll
@@ -1129,8 +1157,12 @@ __global__ void __launch_bounds__(WAVES * 64) scan_gather(ScanParams P) {
   const int b = unit / (P.Hkv * P.Tq);
   const bool row_ok = r < P.G;
   const int h = g * P.G + r;
+  // the unit's rows: its index list, or with a sliding window the contiguous
+  // range [p - band + 1, p] (clipped at 0)
   const int32_t* list = P.idx + (int64_t)unit * P.max_sel;
-  const int n = min(max(P.count[unit], 0), P.max_sel);
+  const int p_t = P.q_pos0 + t;
+  const int n = P.band > 0 ? min(p_t + 1, P.band) : min(max(P.count[unit], 0), P.max_sel);
+  const int lo = p_t - n + 1;
 
   u32x4_t qf[NC];
   load_q<FP8, D>(qf, P, b, t, h, row_ok, g4);
@@ -1150,7 +1182,8 @@ __global__ void __launch_bounds__(WAVES * 64) scan_gather(ScanParams P) {
   for (int base = 0; base < n; base += kGatherIdxCap) {
     const int nb = min(kGatherIdxCap, n - base);
     __syncthreads();
-    for (int i = threadIdx.x; i < nb; i += WAVES * 64) s_idx[i] = min(max(list[base + i], 0), P.N - 1);
+    for (int i = threadIdx.x; i < nb; i += WAVES * 64)
+      s_idx[i] = P.band > 0 ? lo + base + i : min(max(list[base + i], 0), P.N - 1);
     __syncthreads();
     const int jl = base + nb - 1;
     auto load = [&](RawTile<FP8, D>& R, int j0) {
@@ -1417,10 +1450,12 @@ __global__ void __launch_bounds__(256) scan_f32(ScanParams P) {
 
   int j_begin, j_end;
   const int32_t* list = nullptr;
+  int band_lo = 0;  // sliding window: rows band_lo + i
   if constexpr (GATHER) {
     list = P.idx + (int64_t)unit * P.max_sel;
     j_begin = 0;
-    j_end = min(max(P.count[unit], 0), P.max_sel);
+    j_end = P.band > 0 ? min(p + 1, P.band) : min(max(P.count[unit], 0), P.max_sel);
+    band_lo = p - j_end + 1;
   } else {
     j_begin = split * P.split_len;
     j_end = min(j_begin + P.split_len, p + 1);
@@ -1441,7 +1476,10 @@ __global__ void __launch_bounds__(256) scan_f32(ScanParams P) {
 
   for (int j0 = j_begin; j0 < j_end; j0 += TJ) {
     const int nt = min(TJ, j_end - j0);
-    if (tid < TJ) s_rows[tid] = GATHER ? min(max(list[min(j0 + tid, j_end - 1)], 0), P.N - 1) : min(j0 + tid, j_end - 1);
+    if (tid < TJ)
+      s_rows[tid] = !GATHER       ? min(j0 + tid, j_end - 1)
+                    : P.band > 0 ? band_lo + min(j0 + tid, j_end - 1)
+                                 : min(max(list[min(j0 + tid, j_end - 1)], 0), P.N - 1);
     __syncthreads();
     for (int e = tid; e < TJ * D; e += 256) {
       const int jj = e / D, d = e - jj * D;
@@ -2020,17 +2058,23 @@ bool flash_rows_fit(const ScanParams& p, int kv_dtype) {
 }
 
 hipError_t launch_chunk_full(const ScanParams& p, int kv_dtype, hipStream_t s) {
-  TimedLaunch tl("chunk_full", s);
+  TimedLaunch tl(p.band > 0 ? "swa_chunk" : "chunk_full", s);
   if (!flash_rows_fit(p, kv_dtype)) return hipErrorInvalidValue;
   const int nblk = (p.n_tpacks + kChunkPacks - 1) / kChunkPacks;
   const dim3 grid(p.B * nblk * p.Hkv * p.nsplit);
+#define HS2_CF(F8, DD)                                                                         \
+  do {                                                                                         \
+    if (p.band > 0) hipLaunchKernelGGL((chunk_flash<F8, DD, true>), grid, dim3(256), 0, s, p); \
+    else hipLaunchKernelGGL((chunk_flash<F8, DD, false>), grid, dim3(256), 0, s, p);           \
+  } while (0)
   if (kv_dtype == HS2_FP8_E4M3FN) {
-    if (p.D == 128) hipLaunchKernelGGL((chunk_flash<true, 128>), grid, dim3(256), 0, s, p);
-    else hipLaunchKernelGGL((chunk_flash<true, 64>), grid, dim3(256), 0, s, p);
+    if (p.D == 128) HS2_CF(true, 128);
+    else HS2_CF(true, 64);
   } else {
-    if (p.D == 128) hipLaunchKernelGGL((chunk_flash<false, 128>), grid, dim3(256), 0, s, p);
-    else hipLaunchKernelGGL((chunk_flash<false, 64>), grid, dim3(256), 0, s, p);
+    if (p.D == 128) HS2_CF(false, 128);
+    else HS2_CF(false, 64);
   }
+#undef HS2_CF
   return hipGetLastError();
 }
 

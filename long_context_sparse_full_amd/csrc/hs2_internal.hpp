@@ -45,6 +45,10 @@ struct ScanParams {
   int32_t* gcounter; // split gather: per-(b, t, g) arrival counters (zero between calls)
   // multi-query chunk score pass: scores [B, Tq, Hkv, N]
   float* scores;
+  // sliding-window attention: query t attends to [p - band + 1, p] (0 = no
+  // lower limit).  Gathers then read that contiguous range instead of a list
+  // (idx unused), and the chunk pass, with one split, writes out / lse itself.
+  int band;
   // multi-query chunk path: log2-domain LSE per (unit, row) from the merge,
   // read by the score pass
   const float* lse2_in;

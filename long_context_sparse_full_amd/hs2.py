@@ -73,6 +73,7 @@ _sparse_ws = _sig("hs2_sparse_attn_gather_ws", ctypes.c_int,
 _sparse_static_limit = _sig("hs2_sparse_attn_static_limit", _sz, [])
 _sparse_static = _sig("hs2_sparse_attn_gather_static", ctypes.c_int,
                       [_KVP, _vp, _i32, _i32, _i32, _f32, _vp, _vp, _i32, _vp, _vp, _vp])
+_swa = _sig("hs2_swa_attn", ctypes.c_int, [_KVP, _vp, _i32, _i32, _i32, _i32, _i32, _f32, _vp, _vp, _vp])
 _bridge = _sig("hs2_kv_bridge", ctypes.c_int, [_vp, _i32, _i32, _vp, ctypes.POINTER(KVOutDesc), _i32, _i32, _vp])
 _dbg_e4m3 = _sig("hs2_debug_e4m3fn_to_f32", ctypes.c_int, [_vp, _vp, _i32, _vp])
 _dbg_stream = _sig("hs2_debug_stream_read", ctypes.c_int, [_vp, _sz, _vp, _i32, _vp])
@@ -86,7 +87,7 @@ EXPORTED = [
     "hs2_abi_version", "hs2_status_string", "hs2_last_error", "hs2_full_attn_scores_workspace",
     "hs2_full_attn_scores", "hs2_full_attn_topk_workspace", "hs2_full_attn_topk", "hs2_select_workspace", "hs2_select_workspace_for", "hs2_select_topk_window",
     "hs2_sparse_attn_gather", "hs2_sparse_attn_workspace", "hs2_sparse_attn_gather_ws",
-    "hs2_sparse_attn_static_limit", "hs2_sparse_attn_gather_static", "hs2_kv_bridge", "hs2_debug_e4m3fn_to_f32", "hs2_debug_stream_read",
+    "hs2_sparse_attn_static_limit", "hs2_sparse_attn_gather_static", "hs2_swa_attn", "hs2_kv_bridge", "hs2_debug_e4m3fn_to_f32", "hs2_debug_stream_read",
     "hs2_timing_enable",
     "hs2_timing_reset", "hs2_timing_collect", "hs2_timing_kernel_name",
 ]
@@ -305,6 +306,24 @@ def sparse_attn_gather_static(k, v, q, idx, count, softmax_scale: float | None =
                         count.data_ptr(), idx.shape[-1], out.data_ptr(), None if lse is None else lse.data_ptr(),
                         _stream())
     _check(st, "hs2_sparse_attn_gather_static")
+    return out, lse
+
+
+def swa_attn(k, v, q, q_pos0: int, window: int, softmax_scale: float | None = None, k_scale=None, v_scale=None,
+             out=None, lse=None, want_lse: bool = True):
+    """Sliding-window attention: query t attends to [q_pos0 + t - window + 1, q_pos0 + t]."""
+    d = kv_desc(k, v, k_scale, v_scale)
+    B, Tq, Hq, D = q.shape
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Tq, Hq), dtype=torch.float32, device=q.device)
+    _dense(q, out, lse)
+    st = _swa(ctypes.byref(d), q.data_ptr(), _dtype_code(q), Tq, Hq, int(q_pos0), int(window), float(softmax_scale),
+              out.data_ptr(), None if lse is None else lse.data_ptr(), _stream())
+    _check(st, "hs2_swa_attn")
     return out, lse
 
 

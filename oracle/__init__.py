@@ -229,3 +229,25 @@ def kv_bridge(hidden_bits, w_bits, Hkv, D, mutant: int = 0):
     rc = lib.hs2ref_kv_bridge(h.ctypes.data, T, dm, w.ctypes.data, Hkv, D, y.ctypes.data)
     _check(rc, "kv_bridge")
     return y[:, : Hkv * D].reshape(T, Hkv, D), y[:, Hkv * D:].reshape(T, Hkv, D)
+
+
+def swa_attn(q, k, v, q_pos0, window, scale=None, k_scale=None, v_scale=None, mutant: int = 0):
+    """fp64 sliding-window attention: query token t at position p = q_pos0 + t
+    attends to positions [max(0, p - window + 1), p] (javabetter.cn,
+    MiMo-V2.6-Flash paragraph: a sliding-window layer looks at each token's
+    nearest 128; the current token included, as in reading o4).  The sparse
+    layer of hs2ref.c over each query's window as its index list.
+    Returns (out, lse)."""
+    B, Tq, Hq, D = np.shape(q)
+    Hkv = k.shape[1]
+    window = int(window)
+    if window < 1:
+        raise ValueError("window must be at least 1")
+    idx = np.full((B, Tq, Hkv, window), -1, np.int32)
+    cnt = np.zeros((B, Tq, Hkv), np.int32)
+    for t in range(Tq):
+        p = int(q_pos0) + t
+        lo = max(0, p - window + 1)
+        idx[:, t, :, : p - lo + 1] = np.arange(lo, p + 1, dtype=np.int32)
+        cnt[:, t, :] = p - lo + 1
+    return sparse_attn(q, k, v, idx, cnt, scale=scale, k_scale=k_scale, v_scale=v_scale, mutant=mutant)

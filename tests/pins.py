@@ -308,6 +308,30 @@ def pin_sparse_k0_is_sliding_window(mutant=0):
         _close(out, ref, 1e-12, f"k=0 W={W} sparse")
 
 
+def pin_swa_vs_sdpa_band(mutant=0):
+    """Sliding-window attention (oracle.swa_attn) equals float64 SDPA with a
+    band mask of the last W positions, the current one included: windows
+    longer than the context so far, queries before the cache end, fp32 and
+    FP8 caches; lse equals torch.logsumexp over the band."""
+    import torch
+    for kv, qd, W, qp in (("f32", "f32", 1, None), ("f32", "f32", 4, None), ("fp8", "bf16", 9, 10),
+                          ("bf16", "bf16", 60, None), ("bf16", "bf16", 7, 2)):
+        spec, inp, q_pos0 = _small_inputs(kv, qd, Tq=3, N=41, q_pos0=qp)
+        out, lse = oracle.swa_attn(inp.q_full, inp.k, inp.v, q_pos0, W, k_scale=inp.k_scale, v_scale=inp.v_scale,
+                                   mutant=mutant)
+        q = refs.torch_decode(inp.q_full)
+        k = refs.torch_decode(inp.k, inp.k_scale)
+        v = refs.torch_decode(inp.v, inp.v_scale)
+        mask = refs.band_mask(spec.B, spec.Tq, spec.Hkv, spec.N, q_pos0, W)
+        scale = 1.0 / math.sqrt(spec.D)
+        _close(out, refs.sdpa(q, k, v, mask, scale), 1e-12, f"swa W={W} out")
+        logits = scale * torch.from_numpy(q).permute(0, 2, 1, 3) @ \
+            torch.from_numpy(k).repeat_interleave(spec.G, 1).transpose(-1, -2)
+        m = torch.from_numpy(mask).permute(0, 2, 1, 3).repeat_interleave(spec.G, 1)
+        ref_lse = torch.logsumexp(logits.masked_fill(~m, -math.inf), -1).permute(0, 2, 1).numpy()
+        _close(lse, ref_lse, 1e-12, f"swa W={W} lse")
+
+
 def pin_sparse_equals_masked_attention(mutant=0):
     """Any index list: sparse attention equals full attention with a mask that
     admits exactly the listed rows (float64 SDPA); lse equals torch.logsumexp."""
@@ -353,5 +377,6 @@ ALL_PINS = [
     pin_score_mass_is_group_size, pin_zero_query, pin_single_position, pin_key_shift_invariance,
     pin_position_permutation, pin_select_bruteforce, pin_select_structure, pin_select_pages_budget,
     pin_window_competes_alternative, pin_sparse_equals_full_when_k_covers,
-    pin_sparse_k0_is_sliding_window, pin_sparse_equals_masked_attention, pin_bridge_vs_matmul,
+    pin_sparse_k0_is_sliding_window, pin_swa_vs_sdpa_band, pin_sparse_equals_masked_attention,
+    pin_bridge_vs_matmul,
 ]

@@ -713,3 +713,53 @@ def test_full_attn_topk_window_competes(hs2, kv, N):
     o_or, l_or, s_or = oracle_full(inp, spec)
     gu.assert_scores(sc, s_or)
     gu.assert_rows_rel(gu.host(out), o_or, kv)
+
+
+# -------------------------------------------- sliding-window attention (SWA)
+
+SWA_CASES = [
+    # kv, D, G, Hkv, B, N, Tq, q_pos0 (None: N - Tq), window
+    ("bf16", 128, 8, 4, 1, 4096, 4096, None, 128),   # prefill of the whole context: banded matrix-core pass
+    ("fp8", 128, 8, 2, 1, 2000, 2000, None, 128),
+    ("bf16", 64, 4, 2, 2, 1500, 777, 200, 128),      # ragged token blocks, queries inside a longer cache
+    ("bf16", 128, 16, 1, 1, 900, 100, None, 37),     # odd window, 16 heads per kv head
+    ("fp8", 64, 8, 2, 1, 3000, 64, None, 500),       # window of many tiles
+    ("bf16", 128, 8, 4, 8, 32768, 1, None, 128),     # decode: one token per sequence (gather path)
+    ("fp8", 128, 8, 4, 1, 65536, 2, None, 128),
+    ("f32", 64, 4, 2, 1, 4096, 8, None, 32),         # fp32 cache (vector-ALU gather path)
+    ("bf16", 128, 8, 2, 1, 300, 3, None, 1),         # window of one: out = v_p
+    ("bf16", 128, 8, 2, 1, 100, 100, None, 300),     # window longer than the context
+]
+
+
+@pytest.mark.parametrize("case", SWA_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_swa_attn_parity(hs2, case):
+    """hs2_swa_attn against the oracle's sliding-window attention on the same
+    inputs: outputs element by element and per row relative, LSE."""
+    kv, D, G, Hkv, B, N, Tq, qp, W = case
+    spec = small_spec(kv, D=D, G=G, Hkv=Hkv, B=B, N=N, Tq=Tq, needles=min(8, N - 16))
+    qp = spec.q_pos0 if qp is None else qp
+    gu.log(f"swa {case}")
+    inp = synth.make_inputs(spec, seed=77 + N)
+    blk = gu.DeviceBlock(inp)
+    hs2.timing_reset()
+    hs2.timing_enable(True)
+    try:
+        out, lse = hs2.swa_attn(blk.k, blk.v, blk.q, qp, W, k_scale=blk.ks, v_scale=blk.vs)
+        torch.cuda.synchronize()
+        _, n_chunk = hs2.timing_collect("swa_chunk")
+    finally:
+        hs2.timing_enable(False)
+        hs2.timing_reset()
+    o_or, l_or = oracle.swa_attn(inp.q_full, inp.k, inp.v, qp, W, k_scale=inp.k_scale, v_scale=inp.v_scale)
+    e_o = gu.assert_close(gu.host(out), o_or, gu.O_TOL[kv], "out")
+    r_o = gu.assert_rows_rel(gu.host(out), o_or, kv)
+    e_l = gu.assert_lse(gu.host(lse), l_or, kv)
+    gu.log(f"  {'banded chunk pass' if n_chunk else 'gather'}: max|dO|={e_o:.2e} (row rel {r_o:.2e}) "
+           f"max|dLSE|={e_l:.2e}")
+    if kv != "f32" and Tq * G >= 64:  # at least 4 packs of 16 / G tokens per (b, kv head)
+        assert n_chunk == 1, "expected the banded matrix-core pass"
+    if W == 1:  # attention over the current token alone returns its value row
+        vv = gu.host(blk.v)[:, :, qp:qp + Tq]  # [B, Hkv, Tq, D]
+        want = np.repeat(np.transpose(vv, (0, 2, 1, 3)), G, axis=2)
+        gu.assert_close(gu.host(out), want, 0.0, "window of one")
