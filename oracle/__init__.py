@@ -251,3 +251,49 @@ def swa_attn(q, k, v, q_pos0, window, scale=None, k_scale=None, v_scale=None, mu
         idx[:, t, :, : p - lo + 1] = np.arange(lo, p + 1, dtype=np.int32)
         cnt[:, t, :] = p - lo + 1
     return sparse_attn(q, k, v, idx, cnt, scale=scale, k_scale=k_scale, v_scale=v_scale, mutant=mutant)
+
+
+def kv_bridge_fp8_write(hidden_bits, w_bits, k_codes, v_codes, k_scale, v_scale, batch_index, pos0, grow,
+                        mutant: int = 0):
+    """One layer's K/V bridge written into an FP8 (E4M3FN) cache with one fp32
+    scale per (batch, kv head) for K and one for V (javabetter.cn, KV Bridging
+    paragraph: the layer's own projection of the hidden state; zgeo.com.cn
+    comparison table: the FP8 KV cache).  Returns new (k_codes, v_codes,
+    k_scale, v_scale) arrays; the inputs are not modified.
+
+    The pages give no quantisation rule; reading o25, per head and per part
+    (K or V), with y the fp64 projection of the T new rows:
+      * grow = False: the scale stays; new codes = encode(y / scale).
+      * grow = True (scale maintenance): s' = max(s, fp32(max|y| / 448)); if
+        s' > s, every existing row [0, pos0) of the head is re-encoded,
+        code' = encode(fp32(decode(code) * s) / s') (its cache value read as
+        the attention reads it, then stored at the new scale); the new rows
+        are encoded at s'.  A head whose scale is 0 and whose new rows are all
+        0 keeps scale 0 and gets zero codes.
+    encode() rounds to nearest even and saturates at +-448."""
+    K, V = kv_bridge(hidden_bits, w_bits, k_codes.shape[1], k_codes.shape[3],
+                     mutant=mutant if mutant < 20 else 0)  # [T, Hkv, D] fp64
+    T = K.shape[0]
+    table = e4m3fn_table(mutant if mutant < 20 else 0)
+    out = []
+    for codes, scale, Y in ((k_codes, k_scale, K), (v_codes, v_scale, V)):
+        codes = np.array(codes, copy=True)
+        scale = np.array(scale, dtype=np.float32, copy=True)
+        Hkv = codes.shape[1]
+        for h in range(Hkv):
+            s_old = np.float32(scale[batch_index, h])
+            y = Y[:, h, :]
+            s_new = s_old
+            if grow:
+                s_new = max(s_old, np.float32(np.abs(y).max() / (1.0 if mutant == 23 else 448.0)))
+                if s_new > s_old and pos0 > 0 and mutant != 22:
+                    vals = (table[codes[batch_index, h, :pos0]].astype(np.float32) * s_old).astype(np.float64)
+                    q = vals * np.float64(s_new) / np.float64(s_old) ** 2 if mutant == 21 else vals / np.float64(s_new)
+                    codes[batch_index, h, :pos0] = e4m3fn_encode(q)
+            scale[batch_index, h] = s_new
+            if s_new > 0:
+                codes[batch_index, h, pos0:pos0 + T] = e4m3fn_encode(y / np.float64(s_new))
+            else:
+                codes[batch_index, h, pos0:pos0 + T] = 0
+        out += [codes, scale]
+    return out[0], out[2], out[1], out[3]

@@ -372,11 +372,133 @@ def pin_bridge_vs_matmul(mutant=0):
     _close(V, y[:, Hkv * D:].reshape(T, Hkv, D), 1e-12, "bridge V")
 
 
+# ------------------------------------------------ FP8 cache write (bridge)
+
+def _bf16_values(y):
+    """float32 values rounded to bf16 (torch's conversion), as float32."""
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(y, np.float32)).to(torch.bfloat16).float().numpy()
+
+
+def _identity_bridge(y_rows, dm):
+    """hidden = the first T rows of the identity, w_kv = the wanted outputs on
+    top of zeros: the projection of row t is exactly y_rows[t] (bf16 values)."""
+    T, C = y_rows.shape
+    assert np.array_equal(_bf16_values(y_rows), y_rows), "wanted outputs must be bf16 values"
+    h = np.zeros((T, dm), np.float32)
+    h[np.arange(T), np.arange(T)] = 1.0
+    w = np.zeros((dm, C), np.float32)
+    w[:T] = y_rows
+    return synth.to_bf16_bits(h), synth.to_bf16_bits(w)
+
+
+def _fp8_cache(rng, B, Hkv, N, D, lo_exp=0):
+    """Random finite E4M3FN codes (normal range, exponent field >= lo_exp)."""
+    e = rng.integers(max(1, lo_exp), 16, (B, Hkv, N, D))
+    m = rng.integers(0, 8, (B, Hkv, N, D))
+    m = np.where(e == 15, np.minimum(m, 6), m)  # 0x7F is NaN
+    sgn = rng.integers(0, 2, (B, Hkv, N, D)) << 7
+    return (sgn | (e << 3) | m).astype(np.uint8)
+
+
+def _torch_e4m3fn(x32):
+    """torch's float32 -> float8_e4m3fn cast (values clamped to +-448 first)."""
+    import torch
+    x = np.clip(np.asarray(x32, np.float32), -448.0, 448.0)
+    return torch.from_numpy(np.ascontiguousarray(x)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def pin_fp8_write_keep_vs_torch(mutant=0):
+    """Keep the scales: new rows are torch's cast of y / s, where y (multiples
+    of 1/8) and a power-of-two s make y / s exact in float32, values past 448
+    saturating; other rows and the scales untouched."""
+    rng = np.random.default_rng(31)
+    B, Hkv, N, D, T, pos0, b = 2, 2, 20, 8, 5, 9, 1
+    y = _bf16_values(rng.integers(-1200, 1200, (T, 2 * Hkv * D)) / 8.0)  # up to 150: some saturate
+    h, w = _identity_bridge(y, 16)
+    kc, vc = _fp8_cache(rng, B, Hkv, N, D), _fp8_cache(rng, B, Hkv, N, D)
+    ks = np.full((B, Hkv), 0.25, np.float32)
+    vs = np.full((B, Hkv), 0.5, np.float32)
+    k2, v2, ks2, vs2 = oracle.kv_bridge_fp8_write(h, w, kc, vc, ks, vs, b, pos0, grow=False, mutant=mutant)
+    for got, old, sc, part in ((k2, kc, ks, 0), (v2, vc, vs, 1)):
+        yy = y[:, part * Hkv * D:(part + 1) * Hkv * D].reshape(T, Hkv, D).transpose(1, 0, 2)
+        want = _torch_e4m3fn(yy / sc[b][:, None, None])
+        assert np.array_equal(got[b, :, pos0:pos0 + T], want), "new rows differ from torch's cast"
+        mask = np.ones(got.shape, bool)
+        mask[b, :, pos0:pos0 + T] = False
+        assert np.array_equal(got[mask], old[mask]), "rows outside the new ones changed"
+    assert np.array_equal(ks2, ks) and np.array_equal(vs2, vs)
+
+
+def pin_fp8_write_grow_doubling(mutant=0):
+    """Scale maintenance, closed form: new K rows of head 0 reach exactly
+    448 * 2 s (s = 2^-3), so that scale doubles and each older code of the head
+    (exponent field >= 2) becomes the code one exponent lower, the value
+    unchanged; heads whose new rows stay within 448 s keep scale and codes;
+    new rows are torch's cast of y / s' (exact)."""
+    rng = np.random.default_rng(32)
+    B, Hkv, N, D, T, pos0, b = 1, 2, 24, 8, 4, 13, 0
+    s = np.float32(2.0 ** -3)
+    y = _bf16_values(rng.integers(-300, 300, (T, 2 * Hkv * D)) / 8.0)  # |y| <= 37.5 < 448 s = 56
+    y[2, 3] = 112.0  # K head 0: amax / 448 = 2^-2
+    h, w = _identity_bridge(y, 16)
+    kc, vc = _fp8_cache(rng, B, Hkv, N, D, lo_exp=2), _fp8_cache(rng, B, Hkv, N, D, lo_exp=2)
+    ks = np.full((B, Hkv), s, np.float32)
+    vs = np.full((B, Hkv), s, np.float32)
+    k2, v2, ks2, vs2 = oracle.kv_bridge_fp8_write(h, w, kc, vc, ks, vs, b, pos0, grow=True, mutant=mutant)
+    assert ks2[b, 0] == np.float32(2.0 ** -2) and ks2[b, 1] == s and np.all(vs2 == s), "scales"
+    assert np.array_equal(k2[b, 0, :pos0], kc[b, 0, :pos0] - 8), "head 0: old codes not one exponent lower"
+    assert np.array_equal(k2[b, 1, :pos0], kc[b, 1, :pos0]), "head 1: old codes changed"
+    assert np.array_equal(v2[b, :, :pos0], vc[b, :, :pos0]), "V: old codes changed"
+    for got, sc, part in ((k2, ks2, 0), (v2, vs2, 1)):
+        yy = y[:, part * Hkv * D:(part + 1) * Hkv * D].reshape(T, Hkv, D).transpose(1, 0, 2)
+        assert np.array_equal(got[b, :, pos0:pos0 + T], _torch_e4m3fn(yy / sc[b][:, None, None])), "new rows"
+        assert np.array_equal(got[b, :, pos0 + T:], (kc if part == 0 else vc)[b, :, pos0 + T:]), "rows past"
+
+
+def pin_fp8_write_grow_nearest(mutant=0):
+    """Scale maintenance on random projections: each re-encoded old value is
+    within half an FP8 step (at the new scale) of its previous value, the
+    largest new element of a grown head maps to +-448, and no new element is
+    farther than half a step from its fp64 value."""
+    rng = np.random.default_rng(33)
+    B, Hkv, N, D, T, pos0, b, dm = 1, 3, 40, 16, 6, 30, 0, 64
+    h = synth.to_bf16_bits(rng.standard_normal((T, dm)).astype(np.float32))
+    w = synth.to_bf16_bits((rng.standard_normal((dm, 2 * Hkv * D)) * 0.4).astype(np.float32))
+    K, V = oracle.kv_bridge(h, w, Hkv, D)
+    table = oracle.e4m3fn_table()
+    kc, vc = _fp8_cache(rng, B, Hkv, N, D, lo_exp=1), _fp8_cache(rng, B, Hkv, N, D, lo_exp=1)
+    ks = np.array([[1e-3, 1.0, 2e-2]], np.float32)  # heads 0 and 2 must grow, head 1 not
+    vs = np.array([[1e-3, 1e-3, 1.0]], np.float32)
+    k2, v2, ks2, vs2 = oracle.kv_bridge_fp8_write(h, w, kc, vc, ks, vs, b, pos0, grow=True, mutant=mutant)
+
+    def step(x):  # FP8 spacing at |x| (units of the scale): 2^(e-3) for normals, 2^-9 below 2^-6
+        e = np.floor(np.log2(np.maximum(np.abs(x), 2.0 ** -6)))
+        return np.ldexp(1.0, (e - 3).astype(int))
+
+    for old, new, s0, s1, Y in ((kc, k2, ks, ks2, K), (vc, v2, vs, vs2, V)):
+        for hh in range(Hkv):
+            a, c = np.float64(s0[b, hh]), np.float64(s1[b, hh])
+            assert c >= a, "a scale shrank"
+            yv = Y[:, hh, :]
+            if np.abs(yv).max() > 448 * a:
+                assert c > a, "a scale that had to grow did not"
+                vals = (table[old[b, hh, :pos0]].astype(np.float32) * np.float32(a)).astype(np.float64)
+                newv = table[new[b, hh, :pos0]] * c
+                assert np.all(np.abs(newv - vals) <= 0.5 * step(vals / c) * c * (1 + 1e-9)), "re-encoding error"
+                i = np.unravel_index(np.argmax(np.abs(yv)), yv.shape)
+                assert (new[b, hh, pos0 + i[0], i[1]] & 0x7F) == 0x7E, "largest new value not at 448"
+            else:
+                assert c == a and np.array_equal(new[b, hh, :pos0], old[b, hh, :pos0])
+            got = table[new[b, hh, pos0:pos0 + T]] * c
+            assert np.all(np.abs(got - yv) <= 0.5 * step(yv / c) * c * (1 + 1e-9)), "new rows not nearest"
+
+
 ALL_PINS = [
     pin_e4m3fn_table, pin_e4m3fn_encode, pin_bf16_decode, pin_full_vs_sdpa, pin_scores_vs_sdpa_probs,
     pin_score_mass_is_group_size, pin_zero_query, pin_single_position, pin_key_shift_invariance,
     pin_position_permutation, pin_select_bruteforce, pin_select_structure, pin_select_pages_budget,
     pin_window_competes_alternative, pin_sparse_equals_full_when_k_covers,
     pin_sparse_k0_is_sliding_window, pin_swa_vs_sdpa_band, pin_sparse_equals_masked_attention,
-    pin_bridge_vs_matmul,
+    pin_bridge_vs_matmul, pin_fp8_write_keep_vs_torch, pin_fp8_write_grow_doubling, pin_fp8_write_grow_nearest,
 ]

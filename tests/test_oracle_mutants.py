@@ -34,3 +34,24 @@ def test_mutant_is_caught(mutant):
             except (AssertionError, RuntimeError, ValueError, IndexError) as e:
                 failures.append(f"{pin.__name__}: {str(e)[:80]}")
     assert failures, f"no pin caught mutant {mutant} ({MUTANTS[mutant]})"
+
+
+# Planted mistakes in the oracle's Python layer (the FP8 cache write).
+PY_MUTANTS = {
+    21: "old rows re-encoded with the scale ratio inverted",
+    22: "scale grown without re-encoding the old rows",
+    23: "new scale without the division by 448",
+}
+
+
+@pytest.mark.parametrize("mutant", sorted(PY_MUTANTS), ids=lambda m: f"m{m}")
+def test_python_mutant_is_caught(mutant):
+    failures = []
+    with np.errstate(all="ignore"):
+        for pin in (pins.pin_fp8_write_keep_vs_torch, pins.pin_fp8_write_grow_doubling,
+                    pins.pin_fp8_write_grow_nearest):
+            try:
+                pin(mutant)
+            except (AssertionError, RuntimeError, ValueError, IndexError) as e:
+                failures.append(f"{pin.__name__}: {str(e)[:80]}")
+    assert failures, f"no pin caught mutant {mutant} ({PY_MUTANTS[mutant]})"
