@@ -240,6 +240,31 @@ int hs2_swa_attn(const hs2_kv_desc* kv, const void* q, hs2_dtype q_dtype, int32_
 int hs2_kv_bridge(const void* hidden, int32_t T, int32_t d_model, const void* w_kv,
                   const hs2_kv_out_desc* kv_out, int32_t batch_index, int32_t pos0, hipStream_t stream);
 
+/* The bridge of L cross-decoder full layers from one hidden state (javabetter.cn,
+ * KV Bridging paragraph: every cross-decoder full layer derives its own K/V
+ * from the same self-decoder hidden state with its own parameters), in one
+ * launch: layer l projects `hidden` with w_kv + l * d_model * 2*Hkv*D
+ * ([L, d_model, 2*Hkv*D] bf16, contiguous) into caches[l] (a HOST array of L
+ * descriptors, 1 <= L <= 16, sharing dtype, Hkv and D), batch batch_index,
+ * rows [pos0, pos0 + T).  T = 1 is the per-token append of decoding.
+ * bf16 caches: as hs2_kv_bridge.  FP8_E4M3FN caches, by scale_mode:
+ *   HS2_SCALE_KEEP: as hs2_kv_bridge (the scales are read and must be > 0);
+ *   HS2_SCALE_GROW: per-head scale maintenance (the pages give no rule; this
+ *     is this library's reading): for each (layer, K/V, head), s' = max(s,
+ *     max|y| / 448) over the new rows y (fp32); the scale is set to s'; if s'
+ *     > s, the head's rows [0, pos0) are re-encoded in place as
+ *     encode(fp32(decode(code) * s) / s') -- a pass over those rows, paid only
+ *     when a scale grows; the new rows get encode(y / s') (zero codes while s'
+ *     is 0).  Needs a workspace of hs2_kv_bridge_layers_workspace(L, T, Hkv, D)
+ *     bytes (256-byte aligned).  A head's scale may start at 0 (empty cache).
+ * encode() rounds to nearest even and saturates at +-448.  Requires d_model %
+ * 64 == 0. */
+enum { HS2_SCALE_KEEP = 0, HS2_SCALE_GROW = 1 };
+size_t hs2_kv_bridge_layers_workspace(int32_t L, int32_t T, int32_t Hkv, int32_t D);
+int hs2_kv_bridge_layers(const void* hidden, int32_t T, int32_t d_model, const void* w_kv, int32_t L,
+                         const hs2_kv_out_desc* caches, int32_t batch_index, int32_t pos0,
+                         int32_t scale_mode, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Diagnostic: decode n OCP E4M3FN codes (device array) to fp32 through the
  * same in-register conversion the attention kernels use.  Lets a test compare
  * the hardware conversion with the format's definition code by code. */

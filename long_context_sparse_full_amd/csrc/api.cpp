@@ -816,36 +816,98 @@ int hs2_swa_attn(const hs2_kv_desc* kv, const void* q, hs2_dtype q_dtype, int32_
   return HS2_OK;
 }
 
+}  // extern "C"
+
+namespace {
+struct BridgePlan {
+  size_t off_y, off_amax, off_scale, total;
+};
+BridgePlan plan_bridge(int L, int T, int Hkv, int D) {
+  BridgePlan b{};
+  size_t off = 0;
+  b.off_y = off;
+  off = a256(off + (size_t)L * T * 2 * Hkv * D * sizeof(float));
+  b.off_amax = off;
+  off = a256(off + (size_t)L * 2 * Hkv * sizeof(uint32_t));
+  b.off_scale = off;
+  off = a256(off + (size_t)L * 2 * Hkv * sizeof(float));
+  b.total = off;
+  return b;
+}
+
+int bridge_impl(const char* name, const void* hidden, int32_t T, int32_t d_model, const void* w_kv, int32_t L,
+                const hs2_kv_out_desc* caches, int32_t batch_index, int32_t pos0, int32_t scale_mode, void* workspace,
+                size_t workspace_bytes, hipStream_t stream) {
+  const std::string w(name);
+  if (!caches) return fail(HS2_ERR_INVALID_ARG, w + ": cache descriptor is NULL");
+  if (L < 1 || L > hs2::kMaxBridgeLayers)
+    return fail(HS2_ERR_INVALID_ARG, w + ": layers must be 1.." + std::to_string(hs2::kMaxBridgeLayers));
+  if (scale_mode != HS2_SCALE_KEEP && scale_mode != HS2_SCALE_GROW)
+    return fail(HS2_ERR_INVALID_ARG, w + ": unknown scale mode");
+  if (!hidden || !w_kv) return fail(HS2_ERR_INVALID_ARG, w + ": NULL hidden or w_kv");
+  if (T <= 0 || d_model <= 0) return fail(HS2_ERR_INVALID_ARG, w + ": T and d_model must be positive");
+  if (d_model % 64) return fail(HS2_ERR_UNSUPPORTED, w + ": d_model must be a multiple of 64");
+  if (!al16(hidden) || !al16(w_kv)) return fail(HS2_ERR_INVALID_ARG, w + ": hidden/w_kv must be 16-byte aligned");
+  const hs2_kv_out_desc& c0 = caches[0];
+  hs2::BridgeLayers P{};
+  P.L = L;
+  P.pos0 = pos0;
+  for (int l = 0; l < L; ++l) {
+    const hs2_kv_out_desc& c = caches[l];
+    const hs2_kv_desc view = as_read_desc(c);
+    int st = check_kv(&view, name);
+    if (st) return st;
+    if (c.dtype != HS2_BF16 && c.dtype != HS2_FP8_E4M3FN)
+      return fail(HS2_ERR_UNSUPPORTED, w + ": output cache must be BF16 or FP8_E4M3FN");
+    if (c.dtype != c0.dtype || c.Hkv != c0.Hkv || c.D != c0.D)
+      return fail(HS2_ERR_INVALID_ARG, w + ": the layers' caches must share dtype, Hkv and D");
+    if (batch_index < 0 || batch_index >= c.B) return fail(HS2_ERR_INVALID_ARG, w + ": batch_index out of range");
+    if (pos0 < 0 || (int64_t)pos0 + T > c.N)
+      return fail(HS2_ERR_INVALID_ARG, w + ": need 0 <= pos0 and pos0 + T <= N");
+    const bool fp8 = c.dtype == HS2_FP8_E4M3FN;
+    const size_t esz = fp8 ? 1 : 2;
+    hs2::BridgeOut& o = P.out[l];
+    o.k = static_cast<char*>(c.k) + (int64_t)batch_index * c.stride_b * esz;
+    o.v = static_cast<char*>(c.v) + (int64_t)batch_index * c.stride_b * esz;
+    o.sn = c.stride_n;
+    o.sh = c.stride_h;
+    o.k_scale = fp8 ? c.k_scale + (int64_t)batch_index * c.Hkv : nullptr;
+    o.v_scale = fp8 ? c.v_scale + (int64_t)batch_index * c.Hkv : nullptr;
+  }
+  if (scale_mode == HS2_SCALE_GROW && c0.dtype == HS2_FP8_E4M3FN) {
+    const BridgePlan bp = plan_bridge(L, T, c0.Hkv, c0.D);
+    if (!workspace || workspace_bytes < bp.total)
+      return fail(HS2_ERR_WORKSPACE, w + ": workspace needs " + std::to_string(bp.total) + " bytes");
+    if ((uintptr_t)workspace & 255) return fail(HS2_ERR_INVALID_ARG, w + ": workspace must be 256-byte aligned");
+    P.y = at<float>(workspace, bp.off_y);
+    P.amax = at<uint32_t>(workspace, bp.off_amax);
+    P.old_scale = at<float>(workspace, bp.off_scale);
+  }
+  const hipError_t e = hs2::launch_bridge(static_cast<const uint16_t*>(hidden), T, d_model,
+                                          static_cast<const uint16_t*>(w_kv), c0.Hkv, c0.D, P, stream);
+  if (e != hipSuccess) return hip_fail(e, (w + " launch").c_str());
+  return HS2_OK;
+}
+}  // namespace
+
+extern "C" {
+
 int hs2_kv_bridge(const void* hidden, int32_t T, int32_t d_model, const void* w_kv, const hs2_kv_out_desc* kv_out,
                   int32_t batch_index, int32_t pos0, hipStream_t stream) {
-  if (!kv_out) return fail(HS2_ERR_INVALID_ARG, "hs2_kv_bridge: kv_out descriptor is NULL");
-  const hs2_kv_desc view = as_read_desc(*kv_out);
-  int st = check_kv(&view, "hs2_kv_bridge");
-  if (st) return st;
-  if (kv_out->dtype != HS2_BF16 && kv_out->dtype != HS2_FP8_E4M3FN)
-    return fail(HS2_ERR_UNSUPPORTED, "hs2_kv_bridge: output cache must be BF16 or FP8_E4M3FN");
-  if (!hidden || !w_kv) return fail(HS2_ERR_INVALID_ARG, "hs2_kv_bridge: NULL hidden or w_kv");
-  if (T <= 0 || d_model <= 0) return fail(HS2_ERR_INVALID_ARG, "hs2_kv_bridge: T and d_model must be positive");
-  if (d_model % 64) return fail(HS2_ERR_UNSUPPORTED, "hs2_kv_bridge: d_model must be a multiple of 64");
-  if (batch_index < 0 || batch_index >= kv_out->B)
-    return fail(HS2_ERR_INVALID_ARG, "hs2_kv_bridge: batch_index out of range");
-  if (pos0 < 0 || (int64_t)pos0 + T > kv_out->N)
-    return fail(HS2_ERR_INVALID_ARG, "hs2_kv_bridge: need 0 <= pos0 and pos0 + T <= N");
-  if (!al16(hidden) || !al16(w_kv)) return fail(HS2_ERR_INVALID_ARG, "hs2_kv_bridge: hidden/w_kv must be 16-byte aligned");
-  const int64_t off = (int64_t)batch_index * kv_out->stride_b + (int64_t)pos0 * kv_out->stride_n;
-  const bool fp8 = kv_out->dtype == HS2_FP8_E4M3FN;
-  const size_t esz = fp8 ? 1 : 2;
-  hs2::BridgeOut o{};
-  o.k = static_cast<char*>(kv_out->k) + off * esz;
-  o.v = static_cast<char*>(kv_out->v) + off * esz;
-  o.sn = kv_out->stride_n;
-  o.sh = kv_out->stride_h;
-  o.k_scale = fp8 ? kv_out->k_scale + (int64_t)batch_index * kv_out->Hkv : nullptr;
-  o.v_scale = fp8 ? kv_out->v_scale + (int64_t)batch_index * kv_out->Hkv : nullptr;
-  const hipError_t e = hs2::launch_bridge(static_cast<const uint16_t*>(hidden), T, d_model,
-                                          static_cast<const uint16_t*>(w_kv), kv_out->Hkv, kv_out->D, o, stream);
-  if (e != hipSuccess) return hip_fail(e, "kv_bridge launch");
-  return HS2_OK;
+  return bridge_impl("hs2_kv_bridge", hidden, T, d_model, w_kv, 1, kv_out, batch_index, pos0, HS2_SCALE_KEEP, nullptr,
+                     0, stream);
+}
+
+size_t hs2_kv_bridge_layers_workspace(int32_t L, int32_t T, int32_t Hkv, int32_t D) {
+  if (L <= 0 || T <= 0 || Hkv <= 0 || D <= 0) return 0;
+  return plan_bridge(L, T, Hkv, D).total;
+}
+
+int hs2_kv_bridge_layers(const void* hidden, int32_t T, int32_t d_model, const void* w_kv, int32_t L,
+                         const hs2_kv_out_desc* caches, int32_t batch_index, int32_t pos0, int32_t scale_mode,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return bridge_impl("hs2_kv_bridge_layers", hidden, T, d_model, w_kv, L, caches, batch_index, pos0, scale_mode,
+                     workspace, workspace_bytes, stream);
 }
 
 int hs2_debug_e4m3fn_to_f32(const uint8_t* codes, float* out, int32_t n, hipStream_t stream) {

@@ -8,8 +8,14 @@
 // are V heads.  A bf16 cache receives y rounded to bf16 (RNE); an FP8 cache
 // the OCP E4M3FN code of y / scale of its head, rounded to nearest even and
 // saturated at +-448.  A dense contraction, so it runs on bf16 MFMA
-// (16x16x32) tiles.
+// (16x16x32) tiles; the L layers of one call (each its own weights and cache,
+// one hidden state) are the grid's third dimension.  With FP8 scale
+// maintenance the contraction keeps y in fp32 and records each head's
+// max |y|, and a second kernel grows the scales, re-encodes the older rows of
+// a head whose scale grew and encodes the new rows.
 #include "hs2_internal.hpp"
+
+#include <algorithm>
 
 
 namespace hs2 {
@@ -51,15 +57,29 @@ __device__ __forceinline__ uint8_t e4m3fn_rne_sat(float x) {
   return (uint8_t)(sign | code);
 }
 
+// E4M3FN code -> fp32 value (exact): the code read as a bf16 number by the
+// hardware conversion (every E4M3FN value is a bf16 value).
+__device__ __forceinline__ void e4m3x4_to_f32(uint32_t w, float (&f)[4]) {
+  const uint32_t lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+  const uint32_t hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
+  f[0] = __uint_as_float(lo << 16);
+  f[1] = __uint_as_float(lo & 0xffff0000u);
+  f[2] = __uint_as_float(hi << 16);
+  f[3] = __uint_as_float(hi & 0xffff0000u);
+}
+
+// output modes of the contraction
+enum { kOutBf16 = 0, kOutFp8 = 1, kOutF32Amax = 2 };
+
 template <int RT>
 struct BridgeStage {
   u32x4_t w[2];
   u32x4_t a[RT][2];
 };
 
-template <int BT, bool FP8OUT>
+template <int BT, int MODE>
 __global__ void __launch_bounds__(256) bridge_mfma(const uint16_t* __restrict__ H, int T, int dm,
-                                                   const uint16_t* __restrict__ W, int Hkv, int D, BridgeOut O) {
+                                                   const uint16_t* __restrict__ Wall, int Hkv, int D, BridgeLayers P) {
   static_assert(BT == 32 || BT == 64, "token tile");
   constexpr int RT = BT / 32, CT = 2;
   using Stage = BridgeStage<RT>;
@@ -69,6 +89,9 @@ __global__ void __launch_bounds__(256) bridge_mfma(const uint16_t* __restrict__ 
   const int r16 = lane & 15, g4 = lane >> 4;
   const int wr = wave >> 1, wc = wave & 1;
   const int t0 = blockIdx.y * BT, c0 = blockIdx.x * kBC;
+  const int layer = blockIdx.z;
+  const uint16_t* __restrict__ W = Wall + (int64_t)layer * dm * C;
+  const BridgeOut& O = P.out[layer];
   // this thread's part of a w_kv stage: row tid/4 of the stage, 16 columns
   const int wrow = tid >> 2, wcol = (tid & 3) * 16;
   f32x4_t acc[RT][CT];
@@ -154,6 +177,7 @@ __global__ void __launch_bounds__(256) bridge_mfma(const uint16_t* __restrict__ 
   if (rem > 2) compute_stage(R2);
   // scatter: column c -> K or V cache, head c/D, element c%D; token t
   const int half = Hkv * D;
+  float amax = 0.f;  // kOutF32Amax: this thread's max |y| (the tile lies in one head)
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
@@ -163,44 +187,150 @@ __global__ void __launch_bounds__(256) bridge_mfma(const uint16_t* __restrict__ 
         const int t = t0 + wr * 16 * RT + rt * 16 + 4 * g4 + i;
         const int c = c0 + wc * 16 * CT + ct * 16 + r16;
         if (t >= T) continue;
+        const float yv = acc[rt][ct][i];
+        if constexpr (MODE == kOutF32Amax) {
+          P.y[((int64_t)layer * T + t) * C + c] = yv;
+          amax = fmaxf(amax, fabsf(yv));
+          continue;
+        }
         const int cc = c < half ? c : c - half;
         const int hh = cc / D, d = cc - hh * D;
-        const int64_t e = (int64_t)hh * O.sh + (int64_t)t * O.sn + d;
-        if constexpr (FP8OUT) {
+        const int64_t e = (int64_t)hh * O.sh + (int64_t)(P.pos0 + t) * O.sn + d;
+        if constexpr (MODE == kOutFp8) {
           const float sc = (c < half ? O.k_scale : O.v_scale)[hh];
-          ((uint8_t*)(c < half ? O.k : O.v))[e] = e4m3fn_rne_sat(acc[rt][ct][i] / sc);
+          ((uint8_t*)(c < half ? O.k : O.v))[e] = e4m3fn_rne_sat(yv / sc);
         } else {
-          ((uint16_t*)(c < half ? O.k : O.v))[e] = __builtin_bit_cast(uint16_t, (__bf16)acc[rt][ct][i]);
+          ((uint16_t*)(c < half ? O.k : O.v))[e] = __builtin_bit_cast(uint16_t, (__bf16)yv);
         }
       }
+  if constexpr (MODE == kOutF32Amax) {
+    // one (layer, K/V, head) per 64-column tile (D is 64 or 128): a workgroup
+    // maximum, then one atomic (non-negative floats order as their bits)
+    __shared__ float red[4];
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+    if (lane == 0) red[wave] = amax;
+    __syncthreads();
+    if (tid == 0) {
+      const float m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+      const int part = c0 < half ? 0 : 1, hh = (c0 - part * half) / D;
+      atomicMax(&P.amax[(layer * 2 + part) * Hkv + hh], __float_as_uint(m));
+    }
+  }
+}
+
+// Scale maintenance, set-up: each head's max |y| cleared and its scale on
+// entry kept (the finishing kernel overwrites the cache's scales).
+__global__ void __launch_bounds__(256) bridge_grow_prep(BridgeLayers P, int Hkv) {
+  const int n = P.L * 2 * Hkv;
+  for (int i = threadIdx.x; i < n; i += 256) {
+    const int l = i / (2 * Hkv), part = (i / Hkv) & 1, h = i % Hkv;
+    P.amax[i] = 0u;
+    P.old_scale[i] = (part ? P.out[l].v_scale : P.out[l].k_scale)[h];
+  }
+}
+
+// Scale maintenance, finish: per (layer, K/V, head) s' = max(s, max|y| / 448);
+// workgroup 0 stores s'.  When s' > s the head's rows [0, pos0) are
+// re-encoded in place, code' = encode(fp32(decode(code) * s) / s'); the new
+// rows [pos0, pos0 + T) get encode(y / s') (zero codes when s' = 0).  The
+// threads of the grid share each head's rows 16 bytes at a time.
+__global__ void __launch_bounds__(256) bridge_grow_finish(BridgeLayers P, int T, int Hkv, int D) {
+  const int nh = P.L * 2 * Hkv, C = 2 * Hkv * D, u16 = D / 16;
+  const int64_t gtid = (int64_t)blockIdx.x * 256 + threadIdx.x, gstride = (int64_t)gridDim.x * 256;
+  for (int i = 0; i < nh; ++i) {
+    const int l = i / (2 * Hkv), part = (i / Hkv) & 1, h = i % Hkv;
+    const BridgeOut& O = P.out[l];
+    const float s_old = P.old_scale[i];
+    const float s_new = fmaxf(s_old, __uint_as_float(P.amax[i]) / 448.f);
+    if (blockIdx.x == 0 && threadIdx.x == 0) (part ? O.v_scale : O.k_scale)[h] = s_new;
+    uint8_t* base = (uint8_t*)(part ? O.v : O.k) + (int64_t)h * O.sh;
+    if (s_new > s_old) {  // uniform: re-encode the older rows at the new scale
+      const int64_t units = (int64_t)P.pos0 * u16;
+      for (int64_t u = gtid; u < units; u += gstride) {
+        const int64_t row = u / u16;
+        u32x4_t* p = (u32x4_t*)(base + row * O.sn + (u - row * u16) * 16);
+        const u32x4_t w = *p;
+        u32x4_t o;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float f[4];
+          e4m3x4_to_f32(w[q], f);
+          uint32_t word = 0;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) word |= (uint32_t)e4m3fn_rne_sat((f[e] * s_old) / s_new) << (8 * e);
+          o[q] = word;
+        }
+        *p = o;
+      }
+    }
+    const int64_t units = (int64_t)T * u16;
+    const float* y = P.y + (int64_t)l * T * C + part * Hkv * D + h * D;
+    for (int64_t u = gtid; u < units; u += gstride) {
+      const int64_t t = u / u16;
+      const int col = (int)(u - t * u16) * 16;
+      const float* yp = y + t * C + col;
+      u32x4_t o;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          word |= (uint32_t)(s_new > 0.f ? e4m3fn_rne_sat(yp[4 * q + e] / s_new) : 0u) << (8 * e);
+        o[q] = word;
+      }
+      *(u32x4_t*)(base + (P.pos0 + t) * O.sn + col) = o;
+    }
+  }
 }
 
 }  // namespace
 
 hipError_t launch_bridge(const uint16_t* hidden, int T, int dm, const uint16_t* w, int Hkv, int D,
-                         const BridgeOut& out, hipStream_t s) {
-  TimedLaunch tl("kv_bridge", s);
+                         const BridgeLayers& out, hipStream_t s) {
   const int C = 2 * Hkv * D;
   // the entry point admits D in {64, 128} and d_model % 64 == 0, so C and d_model
   // divide into whole tiles; tokens are clamped/guarded inside the kernel
-  if (C % kBC != 0 || dm % kKS != 0) return hipErrorInvalidValue;
-  // 64-token tiles where they still give every CU a workgroup, else 32
+  if (C % kBC != 0 || dm % kKS != 0 || out.L < 1 || out.L > kMaxBridgeLayers) return hipErrorInvalidValue;
   const int ctiles = C / kBC;
-  const bool fp8 = out.k_scale != nullptr;
-#define HS2_BRIDGE(BT)                                                                                         \
-  do {                                                                                                       \
-    const dim3 grid(ctiles, (T + BT - 1) / BT);                                                              \
-    if (fp8)                                                                                                 \
-      hipLaunchKernelGGL((bridge_mfma<BT, true>), grid, dim3(256), 0, s, hidden, T, dm, w, Hkv, D, out);     \
-    else                                                                                                     \
-      hipLaunchKernelGGL((bridge_mfma<BT, false>), grid, dim3(256), 0, s, hidden, T, dm, w, Hkv, D, out);    \
+  const bool fp8 = out.out[0].k_scale != nullptr;
+  const bool grow = fp8 && out.y != nullptr;
+  hipError_t e;
+  if (grow) {
+    TimedLaunch tl("kv_bridge", s);
+    hipLaunchKernelGGL(bridge_grow_prep, dim3(1), dim3(256), 0, s, out, Hkv);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  {
+    TimedLaunch tl("kv_bridge", s);
+    const int mode = grow ? kOutF32Amax : (fp8 ? kOutFp8 : kOutBf16);
+    // 64-token tiles where they still give every CU a workgroup, else 32
+#define HS2_BRIDGE(BT)                                                                                            \
+  do {                                                                                                          \
+    const dim3 grid(ctiles, (T + BT - 1) / BT, out.L);                                                          \
+    if (mode == kOutF32Amax)                                                                                    \
+      hipLaunchKernelGGL((bridge_mfma<BT, kOutF32Amax>), grid, dim3(256), 0, s, hidden, T, dm, w, Hkv, D, out); \
+    else if (mode == kOutFp8)                                                                                   \
+      hipLaunchKernelGGL((bridge_mfma<BT, kOutFp8>), grid, dim3(256), 0, s, hidden, T, dm, w, Hkv, D, out);     \
+    else                                                                                                        \
+      hipLaunchKernelGGL((bridge_mfma<BT, kOutBf16>), grid, dim3(256), 0, s, hidden, T, dm, w, Hkv, D, out);    \
   } while (0)
-  if (ctiles * ((T + 63) / 64) >= 256)
-    HS2_BRIDGE(64);
-  else
-    HS2_BRIDGE(32);
+    if (ctiles * ((T + 63) / 64) * out.L >= 256)
+      HS2_BRIDGE(64);
+    else
+      HS2_BRIDGE(32);
 #undef HS2_BRIDGE
-  return hipGetLastError();
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if (grow) {
+    TimedLaunch tl("kv_bridge", s);
+    // enough threads for the largest head region, 16 bytes each, at most 2048 workgroups
+    const int64_t units = (int64_t)(out.pos0 + T) * (D / 16);
+    const int blocks = (int)std::min<int64_t>(2048, std::max<int64_t>(1, (units + 255) / 256));
+    hipLaunchKernelGGL(bridge_grow_finish, dim3(blocks), dim3(256), 0, s, out, T, Hkv, D);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace hs2

@@ -156,18 +156,29 @@ hipError_t launch_chunk_score(const ScanParams& p, int kv_dtype, hipStream_t s);
 hipError_t launch_combine(const CombineParams& p, int units, hipStream_t s);
 hipError_t launch_score(const ScoreParams& p, int units, hipStream_t s);
 hipError_t launch_select(const SelectParams& p, hipStream_t s);
-// K/V bridge output: the cache rows of one batch entry from the first new
-// position on (element (h, t, d) at h*sh + t*sn + d); FP8 caches pass that
-// batch entry's per-head scales (Hkv each), bf16 caches nullptr.
+// K/V bridge outputs: per layer, the cache of one batch entry (row n of head
+// h at k/v + h*sh + n*sn), new rows from pos0 on; FP8 caches pass that batch
+// entry's per-head scales (Hkv each), bf16 caches nullptr.
 struct BridgeOut {
   void* k;
   void* v;
   int64_t sn, sh;
-  const float* k_scale;
-  const float* v_scale;
+  float* k_scale;
+  float* v_scale;
+};
+constexpr int kMaxBridgeLayers = 16;
+struct BridgeLayers {
+  int L, pos0;
+  BridgeOut out[kMaxBridgeLayers];
+  // FP8 scale maintenance (nullptr y: the projection is encoded at once with
+  // the scales as they are): the fp32 projections [L][T][2 Hkv D], and per
+  // (layer, K/V, head) the bit pattern of max |y| and the scale on entry
+  float* y;
+  uint32_t* amax;
+  float* old_scale;
 };
 hipError_t launch_bridge(const uint16_t* hidden, int T, int dm, const uint16_t* w, int Hkv, int D,
-                         const BridgeOut& out, hipStream_t s);
+                         const BridgeLayers& out, hipStream_t s);
 hipError_t launch_debug_e4m3fn(const uint8_t* codes, float* out, int n, hipStream_t s);
 hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* out, int blocks, hipStream_t s);
 

@@ -24,6 +24,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 
 F32, BF16, FP8_E4M3FN = 0, 1, 2
 SEL_WINDOW_COMPETES = 1
+SCALE_KEEP, SCALE_GROW = 0, 1
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
 
 
@@ -73,6 +74,9 @@ _sparse_ws = _sig("hs2_sparse_attn_gather_ws", ctypes.c_int,
 _sparse_static_limit = _sig("hs2_sparse_attn_static_limit", _sz, [])
 _sparse_static = _sig("hs2_sparse_attn_gather_static", ctypes.c_int,
                       [_KVP, _vp, _i32, _i32, _i32, _f32, _vp, _vp, _i32, _vp, _vp, _vp])
+_bridge_layers_ws = _sig("hs2_kv_bridge_layers_workspace", _sz, [_i32, _i32, _i32, _i32])
+_bridge_layers = _sig("hs2_kv_bridge_layers", ctypes.c_int,
+                      [_vp, _i32, _i32, _vp, _i32, ctypes.POINTER(KVOutDesc), _i32, _i32, _i32, _vp, _sz, _vp])
 _swa = _sig("hs2_swa_attn", ctypes.c_int, [_KVP, _vp, _i32, _i32, _i32, _i32, _i32, _f32, _vp, _vp, _vp])
 _bridge = _sig("hs2_kv_bridge", ctypes.c_int, [_vp, _i32, _i32, _vp, ctypes.POINTER(KVOutDesc), _i32, _i32, _vp])
 _dbg_e4m3 = _sig("hs2_debug_e4m3fn_to_f32", ctypes.c_int, [_vp, _vp, _i32, _vp])
@@ -87,7 +91,8 @@ EXPORTED = [
     "hs2_abi_version", "hs2_status_string", "hs2_last_error", "hs2_full_attn_scores_workspace",
     "hs2_full_attn_scores", "hs2_full_attn_topk_workspace", "hs2_full_attn_topk", "hs2_select_workspace", "hs2_select_workspace_for", "hs2_select_topk_window",
     "hs2_sparse_attn_gather", "hs2_sparse_attn_workspace", "hs2_sparse_attn_gather_ws",
-    "hs2_sparse_attn_static_limit", "hs2_sparse_attn_gather_static", "hs2_swa_attn", "hs2_kv_bridge", "hs2_debug_e4m3fn_to_f32", "hs2_debug_stream_read",
+    "hs2_sparse_attn_static_limit", "hs2_sparse_attn_gather_static", "hs2_swa_attn", "hs2_kv_bridge",
+    "hs2_kv_bridge_layers_workspace", "hs2_kv_bridge_layers", "hs2_debug_e4m3fn_to_f32", "hs2_debug_stream_read",
     "hs2_timing_enable",
     "hs2_timing_reset", "hs2_timing_collect", "hs2_timing_kernel_name",
 ]
@@ -335,6 +340,23 @@ def kv_bridge(hidden, w_kv, k_cache, v_cache, batch_index: int, pos0: int, k_sca
     _dense(hidden, w_kv)
     st = _bridge(hidden.data_ptr(), T, dm, w_kv.data_ptr(), ctypes.byref(d), int(batch_index), int(pos0), _stream())
     _check(st, "hs2_kv_bridge")
+
+
+def kv_bridge_layers(hidden, w_kv, caches, batch_index: int, pos0: int, grow: bool = False, workspace=None):
+    """Bridge of L layers from one hidden state [T, d_model]: w_kv [L, d_model, 2*Hkv*D] (bf16, contiguous),
+    caches a list of L tuples (k, v) or (k, v, k_scale, v_scale); grow=True maintains FP8 scales."""
+    L = len(caches)
+    descs = (KVOutDesc * L)(*[kv_desc(*c, cls=KVOutDesc) if len(c) == 4 else kv_desc(c[0], c[1], cls=KVOutDesc)
+                              for c in caches])
+    T, dm = hidden.shape
+    _dense(hidden, w_kv)
+    d0 = descs[0]
+    if workspace is None:
+        need = int(_bridge_layers_ws(L, T, d0.Hkv, d0.D))
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=hidden.device)
+    st = _bridge_layers(hidden.data_ptr(), T, dm, w_kv.data_ptr(), L, descs, int(batch_index), int(pos0),
+                        SCALE_GROW if grow else SCALE_KEEP, workspace.data_ptr(), workspace.numel(), _stream())
+    _check(st, "hs2_kv_bridge_layers")
 
 
 def debug_e4m3fn_to_f32(codes: torch.Tensor) -> torch.Tensor:

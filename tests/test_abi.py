@@ -219,3 +219,20 @@ def test_static_gather_limits(hs2):
     assert hs2._sparse_static(ctypes.byref(d), FAKE, 1, 1, 16, 0.1, None, FAKE, 8, FAKE, None, None) == -1
     assert hs2._sparse_static(ctypes.byref(d), FAKE, 1, 1, 16, 0.1, FAKE, FAKE, 0, FAKE, None, None) == -1
     assert hs2._sparse_static(None, FAKE, 1, 1, 16, 0.1, FAKE, FAKE, 8, FAKE, None, None) == -1
+
+
+def test_bridge_layers_validation(hs2):
+    out = hs2.KVOutDesc
+    d = desc(hs2, cls=out)
+    arr = (out * 2)(d, d)
+    f = hs2._bridge_layers
+    assert f(FAKE, 4, 4096, FAKE, 0, arr, 0, 0, 0, None, 0, None) == -1     # no layers
+    assert f(FAKE, 4, 4096, FAKE, 17, arr, 0, 0, 0, None, 0, None) == -1    # too many layers
+    assert f(FAKE, 4, 4096, FAKE, 2, arr, 0, 0, 5, None, 0, None) == -1     # unknown scale mode
+    assert f(FAKE, 4, 4096, FAKE, 2, None, 0, 0, 0, None, 0, None) == -1    # NULL descriptors
+    d2 = desc(hs2, cls=out, D=64)
+    assert f(FAKE, 4, 4096, FAKE, 2, (out * 2)(d, d2), 0, 0, 0, None, 0, None) == -1  # caches disagree
+    d8 = desc(hs2, dtype=2, scales=True, cls=out)
+    ws = hs2._bridge_layers_ws(2, 4, d8.Hkv, d8.D)
+    assert ws > 2 * 4 * 2 * d8.Hkv * d8.D * 4
+    assert f(FAKE, 4, 4096, FAKE, 2, (out * 2)(d8, d8), 0, 0, 1, FAKE, ws - 1, None) == -3  # grow: workspace
