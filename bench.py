@@ -293,6 +293,7 @@ def main():
                 "avg_launch_us": scan_us}
 
     gather_tp = gather_throughput(hs2, synth, k, v, ks, vs, spec, args) if spec.name == TRAFFIC_WORKLOAD else None
+    extras = bench_extras(hs2, synth, k, v, ks, vs, q, spec, args) if spec.name == TRAFFIC_WORKLOAD else None
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -309,15 +310,13 @@ def main():
             oracle.sparse_attn(ql, inp.k, inp.v, idx_or, cnt_or, k_scale=inp.k_scale, v_scale=inp.v_scale)
         c2 = time.perf_counter()
         units = B * Tq * Hkv
-        used = min(units, oracle.num_threads())
+        used = oracle.num_threads()
         cpu = {"value": round((c2 - c0) * 1e6, 1), "unit": "us/decode-step", "cores": used,
                "kind": "oracle",
-               "sample": f"one whole decode step of {spec.name} (all {units} kv-head units; the oracle "
-                         f"parallelises over units, one thread per unit), fp64; full layer {c1 - c0:.2f}s, "
-                         f"select+3 sparse {c2 - c1:.2f}s",
-               "threads_available": threads, "cpu_model": cpu_model(),
-               # one thread per unit: a single thread would run the units one after another
-               "single_thread_estimate_us": round((c1 - c0) * 1e6 * units / -(-units // used) + (c2 - c1) * 1e6, 1)}
+               "sample": f"one whole decode step of {spec.name} ({units} kv-head units; with fewer units than "
+                         f"threads the oracle's threads share each unit's positions and head dimensions), fp64; "
+                         f"full layer {c1 - c0:.2f}s, select+3 sparse {c2 - c1:.2f}s",
+               "threads_available": threads, "cpu_model": cpu_model()}
         log(f"[bench] oracle: {c2 - c0:.2f}s per step")
 
     line = {
@@ -345,9 +344,111 @@ def main():
         "kernels": kernels,
         "roofline": roofline,
         "gather_throughput": gather_tp,
+        "extras": extras,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+def timed_us(call, reps, warm=2):
+    """Average microseconds of `call` over reps, HIP events on the current stream."""
+    import torch
+    for _ in range(warm):
+        call()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        call()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e3 / reps
+
+
+def bench_extras(hs2, synth, k, v, ks, vs, q, spec, args):
+    """The other paths of the library at the decode workload's shapes:
+    the competing-window selection, 64-token block lists against token lists
+    in the gather (throughput regime), sliding-window attention (decode at 1M
+    FP8 and a 32K-token bf16 prefill on the banded matrix-core pass), and the
+    K/V bridge of 4 layers (512-token block, and decoding's one-token append
+    into 1M-row FP8 caches with the scales kept or maintained)."""
+    import numpy as np
+    import torch
+    reps = max(5, args.steps)
+    Hq, Hkv, D, N = spec.Hq, spec.Hkv, spec.D, spec.N
+    ex = {}
+    # full layer + top-k, both readings of the window (one call each)
+    ws = torch.empty(hs2.full_attn_topk_workspace(k, v, 1, Hq), dtype=torch.uint8, device="cuda")
+    o = [torch.empty(x, device="cuda", dtype=dt) for x, dt in (((1, 1, Hq, D), torch.bfloat16), ((1, 1, Hq), torch.float32),
+                                                                ((1, 1, Hkv, N), torch.float32),
+                                                                ((1, 1, Hkv, spec.max_sel), torch.int32),
+                                                                ((1, 1, Hkv), torch.int32))]
+    for label, comp in (("full_topk_us", False), ("full_topk_window_competes_us", True)):
+        ex[label] = round(timed_us(lambda: hs2.full_attn_topk(
+            k, v, q, spec.q_pos0, spec.k, spec.window, max_sel=spec.max_sel, k_scale=ks, v_scale=vs, out=o[0],
+            lse=o[1], scores=o[2], idx=o[3], count=o[4], workspace=ws, window_competes=comp), reps), 2)
+    del ws, o
+    # gathers over token lists and over 64-token block lists (16 blocks + the 128-row window), 256 lists
+    bq, rows = 256, spec.max_sel
+    rng = np.random.default_rng(0xB10C)
+    qg = (torch.randn(1, bq, Hq, D, device="cuda") * spec.q_std).to(torch.bfloat16)
+    og = torch.empty_like(qg)
+    tok_np, c_np = synth.random_index_lists(0x6A7 + bq, bq * Hkv, N, rows)
+    blk_np = np.empty_like(tok_np)
+    nb = spec.k // 64
+    for u in range(bq * Hkv):
+        blocks = np.sort(rng.choice((N - spec.window) // 64, nb, replace=False))
+        blk_np[u, : nb * 64] = (blocks[:, None] * 64 + np.arange(64)[None, :]).ravel()
+        blk_np[u, nb * 64:] = np.arange(N - spec.window, N)
+    gb = bq * Hkv * rows * 2 * D * esize(spec.kv_dtype)
+    cnt = torch.from_numpy(c_np.reshape(1, bq, Hkv)).cuda()
+    for label, lists in (("token_lists", tok_np), ("block_lists", blk_np)):
+        idx = torch.from_numpy(lists.reshape(1, bq, Hkv, -1)).cuda()
+        us = timed_us(lambda: hs2.sparse_attn_gather(k, v, qg, idx, cnt, k_scale=ks, v_scale=vs, out=og,
+                                                     want_lse=False), reps)
+        ex[f"gather_256_{label}"] = {"avg_us": round(us, 2), "GBps": round(gb / (us * 1e-6) / 1e9, 1),
+                                     "frac": round(gb / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
+    del qg, og
+    # sliding-window attention: decode at this cache, and a 32K-token bf16 prefill
+    W = 128
+    so = torch.empty_like(q)
+    ex["swa128_decode_us"] = round(timed_us(lambda: hs2.swa_attn(k, v, q, spec.q_pos0, W, k_scale=ks, v_scale=vs,
+                                                                 out=so, want_lse=False), reps), 2)
+    Tp = 32768
+    kp = torch.randn(1, Hkv, Tp, D, device="cuda").to(torch.bfloat16)
+    vp = torch.randn(1, Hkv, Tp, D, device="cuda").to(torch.bfloat16)
+    qp = (torch.randn(1, Tp, Hq, D, device="cuda") * spec.q_std).to(torch.bfloat16)
+    op = torch.empty_like(qp)
+    us = timed_us(lambda: hs2.swa_attn(kp, vp, qp, 0, W, out=op, want_lse=False), reps)
+    flops = 4 * Hq * D * sum(min(W, t + 1) for t in range(Tp))
+    ex["swa128_prefill_32k"] = {"avg_us": round(us, 2), "tokens_per_s": round(Tp / (us * 1e-6), 1),
+                                "TFLOPs": round(flops / (us * 1e-6) / 1e12, 1),
+                                "mfma_frac": round(flops / (us * 1e-6) / 1e12 / MFMA_BF16_TFLOPS, 4),
+                                "algorithmic_flops": flops}
+    del kp, vp, qp, op
+    # K/V bridge of 4 layers from one hidden state
+    L, dm = 4, 4096
+    C = 2 * Hkv * D
+    wl = (torch.randn(L, dm, C, device="cuda") / 64.0).to(torch.bfloat16)
+    h512 = torch.randn(512, dm, device="cuda").to(torch.bfloat16)
+    cb = [(torch.zeros(1, Hkv, 4096, D, device="cuda", dtype=torch.bfloat16),
+           torch.zeros(1, Hkv, 4096, D, device="cuda", dtype=torch.bfloat16)) for _ in range(L)]
+    us = timed_us(lambda: hs2.kv_bridge_layers(h512, wl, cb, 0, 1024), reps)
+    ex["bridge_4_layers_512_tokens"] = {"avg_us": round(us, 2),
+                                        "TFLOPs": round(2 * L * 512 * dm * C / (us * 1e-6) / 1e12, 1)}
+    h1 = torch.randn(1, dm, device="cuda").to(torch.bfloat16)
+    c8 = [(torch.zeros(1, Hkv, N, D, device="cuda", dtype=torch.uint8),
+           torch.zeros(1, Hkv, N, D, device="cuda", dtype=torch.uint8),
+           torch.full((1, Hkv), 1.0, device="cuda"), torch.full((1, Hkv), 1.0, device="cuda")) for _ in range(L)]
+    wsb = torch.empty(max(hs2._bridge_layers_ws(L, 1, Hkv, D), 256), dtype=torch.uint8, device="cuda")
+    for label, grow in (("keep", False), ("grow_no_growth", True)):
+        us = timed_us(lambda: hs2.kv_bridge_layers(h1, wl, c8, 0, N - 1, grow=grow, workspace=wsb), reps)
+        ex[f"append_1_token_4_layers_fp8_{label}_us"] = round(us, 2)
+        ex[f"append_1_token_4_layers_fp8_{label}_weight_GBps"] = round(L * dm * C * 2 / (us * 1e-6) / 1e9, 1)
+    del c8, cb, wl
+    torch.cuda.empty_cache()
+    log(f"[bench] extras: {json.dumps(ex)}")
+    return ex
 
 
 def gather_throughput(hs2, synth, k, v, ks, vs, spec, args):

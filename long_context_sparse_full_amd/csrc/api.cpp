@@ -875,6 +875,8 @@ int bridge_impl(const char* name, const void* hidden, int32_t T, int32_t d_model
     o.v_scale = fp8 ? c.v_scale + (int64_t)batch_index * c.Hkv : nullptr;
   }
   if (scale_mode == HS2_SCALE_GROW && c0.dtype == HS2_FP8_E4M3FN) {
+    if (L * 2 * c0.Hkv > 1024)
+      return fail(HS2_ERR_UNSUPPORTED, w + ": scale maintenance handles at most 1024 (layer, K/V, head) scales");
     const BridgePlan bp = plan_bridge(L, T, c0.Hkv, c0.D);
     if (!workspace || workspace_bytes < bp.total)
       return fail(HS2_ERR_WORKSPACE, w + ": workspace needs " + std::to_string(bp.total) + " bytes");

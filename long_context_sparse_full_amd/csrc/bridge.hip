@@ -233,17 +233,36 @@ __global__ void __launch_bounds__(256) bridge_grow_prep(BridgeLayers P, int Hkv)
 // Scale maintenance, finish: per (layer, K/V, head) s' = max(s, max|y| / 448);
 // workgroup 0 stores s'.  When s' > s the head's rows [0, pos0) are
 // re-encoded in place, code' = encode(fp32(decode(code) * s) / s'); the new
-// rows [pos0, pos0 + T) get encode(y / s') (zero codes when s' = 0).  The
-// threads of the grid share each head's rows 16 bytes at a time.
+// rows [pos0, pos0 + T) get encode(y / s') (zero codes when s' = 0).  Every
+// workgroup first stages all heads' (s, s') in LDS (one memory round trip);
+// the grid's threads then share each head's rows 16 bytes at a time, and a
+// workgroup with no new rows to encode leaves at once unless a scale grew.
+constexpr int kGrowHeads = 1024;  // heads staged in LDS (the launcher checks L * 2 * Hkv)
 __global__ void __launch_bounds__(256) bridge_grow_finish(BridgeLayers P, int T, int Hkv, int D) {
+  __shared__ float s_old_l[kGrowHeads], s_new_l[kGrowHeads];
+  __shared__ int any_grew;
   const int nh = P.L * 2 * Hkv, C = 2 * Hkv * D, u16 = D / 16;
+  if (threadIdx.x == 0) any_grew = 0;
+  __syncthreads();
+  for (int i = threadIdx.x; i < nh; i += 256) {
+    const float so = P.old_scale[i];
+    const float sn = fmaxf(so, __uint_as_float(P.amax[i]) / 448.f);
+    s_old_l[i] = so;
+    s_new_l[i] = sn;
+    if (sn > so) any_grew = 1;
+    if (blockIdx.x == 0) {
+      const int l = i / (2 * Hkv), part = (i / Hkv) & 1, h = i % Hkv;
+      (part ? P.out[l].v_scale : P.out[l].k_scale)[h] = sn;
+    }
+  }
+  __syncthreads();
   const int64_t gtid = (int64_t)blockIdx.x * 256 + threadIdx.x, gstride = (int64_t)gridDim.x * 256;
+  const int64_t new_units = (int64_t)T * u16;
+  if (!any_grew && (int64_t)blockIdx.x * 256 >= new_units) return;  // uniform
   for (int i = 0; i < nh; ++i) {
     const int l = i / (2 * Hkv), part = (i / Hkv) & 1, h = i % Hkv;
     const BridgeOut& O = P.out[l];
-    const float s_old = P.old_scale[i];
-    const float s_new = fmaxf(s_old, __uint_as_float(P.amax[i]) / 448.f);
-    if (blockIdx.x == 0 && threadIdx.x == 0) (part ? O.v_scale : O.k_scale)[h] = s_new;
+    const float s_old = s_old_l[i], s_new = s_new_l[i];
     uint8_t* base = (uint8_t*)(part ? O.v : O.k) + (int64_t)h * O.sh;
     if (s_new > s_old) {  // uniform: re-encode the older rows at the new scale
       const int64_t units = (int64_t)P.pos0 * u16;
@@ -264,9 +283,8 @@ __global__ void __launch_bounds__(256) bridge_grow_finish(BridgeLayers P, int T,
         *p = o;
       }
     }
-    const int64_t units = (int64_t)T * u16;
     const float* y = P.y + (int64_t)l * T * C + part * Hkv * D + h * D;
-    for (int64_t u = gtid; u < units; u += gstride) {
+    for (int64_t u = gtid; u < new_units; u += gstride) {
       const int64_t t = u / u16;
       const int col = (int)(u - t * u16) * 16;
       const float* yp = y + t * C + col;
@@ -292,6 +310,7 @@ hipError_t launch_bridge(const uint16_t* hidden, int T, int dm, const uint16_t* 
   // the entry point admits D in {64, 128} and d_model % 64 == 0, so C and d_model
   // divide into whole tiles; tokens are clamped/guarded inside the kernel
   if (C % kBC != 0 || dm % kKS != 0 || out.L < 1 || out.L > kMaxBridgeLayers) return hipErrorInvalidValue;
+  if (out.y != nullptr && out.L * 2 * Hkv > kGrowHeads) return hipErrorInvalidValue;
   const int ctiles = C / kBC;
   const bool fp8 = out.out[0].k_scale != nullptr;
   const bool grow = fp8 && out.y != nullptr;

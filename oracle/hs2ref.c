@@ -112,7 +112,7 @@ static int check_kv(const hs2ref_kv* kv) {
  * related the current token is to each earlier one, pick the tokens). */
 static int full_unit(const hs2ref_kv* kv, const void* q, int32_t q_dtype, int32_t Tq, int32_t Hq,
                      int32_t q_pos0, double scale, int b, int t, int g,
-                     double* out, double* lse, double* scores) {
+                     double* out, double* lse, double* scores, int par) {
   const int D = kv->D, N = kv->N, G = Hq / kv->Hkv;
 #if HS2REF_MUTANT == 3
   const int64_t p = (int64_t)q_pos0 + t - 1; /* drops the current token */
@@ -137,6 +137,9 @@ static int full_unit(const hs2ref_kv* kv, const void* q, int32_t q_dtype, int32_
     for (int d = 0; d < D; ++d) qv[d] = q_elem(q, q_dtype, qoff + d);
     double* s = prob + (size_t)i * (size_t)npos;
     /* logits */
+#ifdef _OPENMP
+#pragma omp parallel for schedule(static) if (par)
+#endif
     for (int64_t j = 0; j < npos; ++j) {
       double acc = 0.0;
       for (int d = 0; d < D; ++d) acc += qv[d] * kv_elem(kv, 0, b, g, j, d);
@@ -149,28 +152,39 @@ static int full_unit(const hs2ref_kv* kv, const void* q, int32_t q_dtype, int32_
     /* two-pass softmax */
     double m = -INFINITY;
     for (int64_t j = 0; j < npos; ++j) m = s[j] > m ? s[j] : m;
+#ifdef _OPENMP
+#pragma omp parallel for schedule(static) if (par)
+#endif
+    for (int64_t j = 0; j < npos; ++j) s[j] = exp(s[j] - m);
     double L = 0.0;
-    for (int64_t j = 0; j < npos; ++j) {
-      s[j] = exp(s[j] - m);
-      L += s[j];
-    }
+    for (int64_t j = 0; j < npos; ++j) L += s[j];
 #if HS2REF_MUTANT != 4
+#ifdef _OPENMP
+#pragma omp parallel for schedule(static) if (par)
+#endif
     for (int64_t j = 0; j < npos; ++j) s[j] = s[j] / L;
 #endif
     /* output */
     if (out) {
-      for (int d = 0; d < D; ++d) row[d] = 0.0;
-      for (int64_t j = 0; j < npos; ++j) {
+      /* each element: its terms added in ascending position */
+#ifdef _OPENMP
+#pragma omp parallel for schedule(static) if (par)
+#endif
+      for (int d = 0; d < D; ++d) {
+        double acc = 0.0;
+        for (int64_t j = 0; j < npos; ++j) {
 #if HS2REF_MUTANT == 4
-        const double pj = s[j] / L;
+          const double pj = s[j] / L;
 #else
-        const double pj = s[j];
+          const double pj = s[j];
 #endif
 #if HS2REF_MUTANT == 15
-        for (int d = 0; d < D; ++d) row[d] += pj * kv_elem(kv, 0, b, g, j, d); /* K for V */
+          acc += pj * kv_elem(kv, 0, b, g, j, d); /* K for V */
 #else
-        for (int d = 0; d < D; ++d) row[d] += pj * kv_elem(kv, 1, b, g, j, d);
+          acc += pj * kv_elem(kv, 1, b, g, j, d);
 #endif
+        }
+        row[d] = acc;
       }
       const int64_t ooff = (((int64_t)b * Tq + t) * Hq + (g * G + i)) * D;
       for (int d = 0; d < D; ++d) out[ooff + d] = row[d];
@@ -185,6 +199,9 @@ static int full_unit(const hs2ref_kv* kv, const void* q, int32_t q_dtype, int32_
   }
   if (scores) {
     double* srow = scores + (((int64_t)b * Tq + t) * kv->Hkv + g) * (int64_t)N;
+#ifdef _OPENMP
+#pragma omp parallel for schedule(static) if (par)
+#endif
     for (int64_t j = 0; j < N; ++j) {
       double acc = 0.0;
       if (j < npos)
@@ -205,14 +222,20 @@ int hs2ref_full_attn_scores(const hs2ref_kv* kv, const void* q, int32_t q_dtype,
   ensure_tables();
   const int64_t units = (int64_t)kv->B * Tq * kv->Hkv;
   int rc = HS2REF_OK;
+  /* Threads go to the units; when there are fewer units than threads, to the
+     positions (logits, exponentials, scores) and head dimensions (outputs) of
+     one unit at a time.  Every value is formed by the same operations in the
+     same order either way (the one sequential sum, L, stays sequential), so
+     the results do not depend on the split. */
+  const int inner = units < hs2ref_num_threads();
 #ifdef _OPENMP
-#pragma omp parallel for schedule(dynamic, 1)
+#pragma omp parallel for schedule(dynamic, 1) if (!inner)
 #endif
   for (int64_t u = 0; u < units; ++u) {
     const int g = (int)(u % kv->Hkv);
     const int t = (int)((u / kv->Hkv) % Tq);
     const int b = (int)(u / ((int64_t)kv->Hkv * Tq));
-    int r = full_unit(kv, q, q_dtype, Tq, Hq, q_pos0, scale, b, t, g, out, lse, scores);
+    int r = full_unit(kv, q, q_dtype, Tq, Hq, q_pos0, scale, b, t, g, out, lse, scores, inner);
     if (r != HS2REF_OK) {
 #ifdef _OPENMP
 #pragma omp critical(hs2ref_rc)
