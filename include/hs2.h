@@ -32,6 +32,12 @@
  *       idx    : [B, Tq, Hkv, max_sel] int32, count : [B, Tq, Hkv] int32
  *     Query head h belongs to KV group g = h / (Hq / Hkv).  Query token t sits
  *     at cache position p = q_pos0 + t and attends to positions [0, p].
+ *   - Variable-length batches: the calls that take q_pos0 also take
+ *     q_pos0_b, a DEVICE array of B int32 (or NULL).  When given, query token
+ *     t of batch entry b sits at q_pos0_b[b] + t instead (each entry's own
+ *     context length, up to N); values outside [0, N - Tq] are clamped into
+ *     it on the device (the host cannot read them without a sync), so every
+ *     access stays inside the cache.  q_pos0 itself must still be valid.
  *   - Base pointers must be 16-byte aligned; the K/V row stride (stride_n
  *     times the element size) and the other K/V strides must be multiples of
  *     16 bytes.
@@ -124,8 +130,9 @@ const char* hs2_last_error(void);
  * (HS2_ERR_HIP otherwise). */
 size_t hs2_full_attn_scores_workspace(const hs2_kv_desc* kv, int32_t Tq, int32_t Hq);
 int hs2_full_attn_scores(const hs2_kv_desc* kv, const void* q, hs2_dtype q_dtype, int32_t Tq,
-                         int32_t Hq, int32_t q_pos0, float softmax_scale, void* out, float* lse,
-                         float* scores, void* workspace, size_t workspace_bytes, hipStream_t stream);
+                         int32_t Hq, int32_t q_pos0, const int32_t* q_pos0_b, float softmax_scale,
+                         void* out, float* lse, float* scores, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream);
 
 /* Token-level top-k with a forced recent window (zgeo.com.cn "core
  * principle": 1024 global tokens picked and the most recent 128 always kept;
@@ -153,9 +160,9 @@ size_t hs2_select_workspace(int32_t B, int32_t Tq, int32_t Hkv, int32_t N);
 /* Tighter figure for one block_size (what the call actually checks). */
 size_t hs2_select_workspace_for(int32_t B, int32_t Tq, int32_t Hkv, int32_t N, int32_t block_size);
 int hs2_select_topk_window(const float* scores, int32_t B, int32_t Tq, int32_t Hkv, int32_t N,
-                           int32_t q_pos0, int32_t k, int32_t window, int32_t block_size, int32_t flags,
-                           int32_t* idx, int32_t* count, int32_t max_sel, void* workspace,
-                           size_t workspace_bytes, hipStream_t stream);
+                           int32_t q_pos0, const int32_t* q_pos0_b, int32_t k, int32_t window,
+                           int32_t block_size, int32_t flags, int32_t* idx, int32_t* count,
+                           int32_t max_sel, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Sparse-attention layer with KV reuse (aitop.news item 35442: sparse layers
  * reuse the previous full-attention layer's KV cache and selection indices;
@@ -222,8 +229,8 @@ int hs2_sparse_attn_gather_static(const hs2_kv_desc* kv, const void* q, hs2_dtyp
  * (b, t, g).  Requires 0 <= q_pos0, q_pos0 + Tq <= N, window >= 1.  No
  * workspace. */
 int hs2_swa_attn(const hs2_kv_desc* kv, const void* q, hs2_dtype q_dtype, int32_t Tq, int32_t Hq,
-                 int32_t q_pos0, int32_t window, float softmax_scale, void* out, float* lse,
-                 hipStream_t stream);
+                 int32_t q_pos0, const int32_t* q_pos0_b, int32_t window, float softmax_scale,
+                 void* out, float* lse, hipStream_t stream);
 
 /* KV bridge (javabetter.cn, KV Bridging paragraph: a cross-decoder full layer
  * computes its K and V from a self-decoder layer's hidden state, with its own
@@ -288,9 +295,10 @@ int hs2_debug_stream_read(const void* buf, size_t bytes, uint32_t* out, int32_t 
  * aligned. */
 size_t hs2_full_attn_topk_workspace(const hs2_kv_desc* kv, int32_t Tq, int32_t Hq);
 int hs2_full_attn_topk(const hs2_kv_desc* kv, const void* q, hs2_dtype q_dtype, int32_t Tq, int32_t Hq,
-                       int32_t q_pos0, float softmax_scale, void* out, float* lse, float* scores, int32_t k,
-                       int32_t window, int32_t flags, int32_t* idx, int32_t* count, int32_t max_sel,
-                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+                       int32_t q_pos0, const int32_t* q_pos0_b, float softmax_scale, void* out, float* lse,
+                       float* scores, int32_t k, int32_t window, int32_t flags, int32_t* idx,
+                       int32_t* count, int32_t max_sel, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream);
 
 /* Per-kernel timing with HIP events on the launch stream (off by default; a
  * measurement aid, process-wide).  While enabled, every kernel launch of the

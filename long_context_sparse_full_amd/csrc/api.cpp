@@ -254,30 +254,31 @@ struct SelPrep {
 };
 
 int full_layer(const hs2_kv_desc* kv, const void* q, hs2_dtype q_dtype, int32_t Tq, int32_t Hq, int32_t q_pos0,
-               float softmax_scale, void* out, float* lse, float* scores, void* workspace, size_t workspace_bytes,
-               hipStream_t stream, SelPrep* sel);
+               const int32_t* q_pos0_b, float softmax_scale, void* out, float* lse, float* scores, void* workspace,
+               size_t workspace_bytes, hipStream_t stream, SelPrep* sel);
 // hs2_select_topk_window; pre_hist0: the row state and first histogram are
 // already built (full layer's merge and score pass)
-int select_impl(const float* scores, int32_t B, int32_t Tq, int32_t Hkv, int32_t N, int32_t q_pos0, int32_t k,
-                int32_t window, int32_t block_size, int32_t flags, int32_t* idx, int32_t* count, int32_t max_sel,
-                void* workspace, size_t workspace_bytes, hipStream_t stream, bool pre_hist0);
+int select_impl(const float* scores, int32_t B, int32_t Tq, int32_t Hkv, int32_t N, int32_t q_pos0,
+                const int32_t* q_pos0_b, int32_t k, int32_t window, int32_t block_size, int32_t flags, int32_t* idx,
+                int32_t* count, int32_t max_sel, void* workspace, size_t workspace_bytes, hipStream_t stream,
+                bool pre_hist0);
 }  // namespace
 
 extern "C" {
 
 int hs2_full_attn_scores(const hs2_kv_desc* kv, const void* q, hs2_dtype q_dtype, int32_t Tq, int32_t Hq,
-                         int32_t q_pos0, float softmax_scale, void* out, float* lse, float* scores, void* workspace,
-                         size_t workspace_bytes, hipStream_t stream) {
-  return full_layer(kv, q, q_dtype, Tq, Hq, q_pos0, softmax_scale, out, lse, scores, workspace, workspace_bytes,
-                    stream, nullptr);
+                         int32_t q_pos0, const int32_t* q_pos0_b, float softmax_scale, void* out, float* lse,
+                         float* scores, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return full_layer(kv, q, q_dtype, Tq, Hq, q_pos0, q_pos0_b, softmax_scale, out, lse, scores, workspace,
+                    workspace_bytes, stream, nullptr);
 }
 
 }  // extern "C"
 
 namespace {
 int full_layer(const hs2_kv_desc* kv, const void* q, hs2_dtype q_dtype, int32_t Tq, int32_t Hq, int32_t q_pos0,
-               float softmax_scale, void* out, float* lse, float* scores, void* workspace, size_t workspace_bytes,
-               hipStream_t stream, SelPrep* sel) {
+               const int32_t* q_pos0_b, float softmax_scale, void* out, float* lse, float* scores, void* workspace,
+               size_t workspace_bytes, hipStream_t stream, SelPrep* sel) {
   int st = check_kv(kv, "hs2_full_attn_scores");
   if (st) return st;
   if ((st = check_q(kv, q, q_dtype, Tq, Hq, "hs2_full_attn_scores"))) return st;
@@ -291,6 +292,7 @@ int full_layer(const hs2_kv_desc* kv, const void* q, hs2_dtype q_dtype, int32_t 
   if (!workspace || workspace_bytes < pl.total)
     return fail(HS2_ERR_WORKSPACE, "hs2_full_attn_scores: workspace needs " + std::to_string(pl.total) + " bytes");
   if ((uintptr_t)workspace & 255) return fail(HS2_ERR_INVALID_ARG, "hs2_full_attn_scores: workspace must be 256-byte aligned");
+  if ((uintptr_t)q_pos0_b & 3) return fail(HS2_ERR_INVALID_ARG, "hs2_full_attn_scores: q_pos0_b must be 4-byte aligned");
 
   hs2::ScanParams p{};
   p.k = kv->k;
@@ -309,6 +311,7 @@ int full_layer(const hs2_kv_desc* kv, const void* q, hs2_dtype q_dtype, int32_t 
   p.Tq = Tq;
   p.Hq = Hq;
   p.q_pos0 = q_pos0;
+  p.qpos_b = q_pos0_b;
   p.scale_log2 = softmax_scale * 1.44269504088896340736f;
   p.tpack = pl.tpack;
   p.n_tpacks = pl.n_tpacks;
@@ -379,6 +382,8 @@ int full_layer(const hs2_kv_desc* kv, const void* q, hs2_dtype q_dtype, int32_t 
     c.sel_k = sel->k;
     c.sel_window = sel->cand_window;
     c.q_pos0 = q_pos0;
+    c.N = kv->N;
+    c.qpos_b = q_pos0_b;
   }
   if ((e = hs2::launch_combine(c, pl.units, stream)) != hipSuccess) return hip_fail(e, "combine launch");
 
@@ -395,6 +400,7 @@ int full_layer(const hs2_kv_desc* kv, const void* q, hs2_dtype q_dtype, int32_t 
   s.Tq = Tq;
   s.N = kv->N;
   s.q_pos0 = q_pos0;
+  s.qpos_b = q_pos0_b;
   s.scores = scores;
   s.sel_hist = sel_hist;
   s.sel_k = pre_sel ? sel->k : 0;
@@ -425,7 +431,8 @@ size_t hs2_full_attn_topk_workspace(const hs2_kv_desc* kv, int32_t Tq, int32_t H
 }
 
 int hs2_full_attn_topk(const hs2_kv_desc* kv, const void* q, hs2_dtype q_dtype, int32_t Tq, int32_t Hq,
-                       int32_t q_pos0, float softmax_scale, void* out, float* lse, float* scores, int32_t k,
+                       int32_t q_pos0, const int32_t* q_pos0_b, float softmax_scale, void* out, float* lse,
+                       float* scores, int32_t k,
                        int32_t window, int32_t flags, int32_t* idx, int32_t* count, int32_t max_sel, void* workspace,
                        size_t workspace_bytes, hipStream_t stream) {
   int st = check_kv(kv, "hs2_full_attn_topk");
@@ -447,11 +454,11 @@ int hs2_full_attn_topk(const hs2_kv_desc* kv, const void* q, hs2_dtype q_dtype, 
   void* rest = static_cast<char*>(workspace) + full_bytes;
   const int32_t cand_window = (flags & HS2_SEL_WINDOW_COMPETES) ? 0 : window;
   SelPrep sel{k, window, cand_window, rest};
-  st = full_layer(kv, q, q_dtype, Tq, Hq, q_pos0, softmax_scale, out, lse, scores, workspace, full_bytes, stream,
-                  &sel);
+  st = full_layer(kv, q, q_dtype, Tq, Hq, q_pos0, q_pos0_b, softmax_scale, out, lse, scores, workspace, full_bytes,
+                  stream, &sel);
   if (st) return st;
-  return select_impl(scores, kv->B, Tq, kv->Hkv, kv->N, q_pos0, k, window, 1, flags, idx, count, max_sel, rest,
-                     workspace_bytes - full_bytes, stream, sel.hist0_done);
+  return select_impl(scores, kv->B, Tq, kv->Hkv, kv->N, q_pos0, q_pos0_b, k, window, 1, flags, idx, count, max_sel,
+                     rest, workspace_bytes - full_bytes, stream, sel.hist0_done);
 }
 
 size_t hs2_select_workspace(int32_t B, int32_t Tq, int32_t Hkv, int32_t N) {
@@ -465,19 +472,20 @@ size_t hs2_select_workspace_for(int32_t B, int32_t Tq, int32_t Hkv, int32_t N, i
 }
 
 int hs2_select_topk_window(const float* scores, int32_t B, int32_t Tq, int32_t Hkv, int32_t N, int32_t q_pos0,
-                           int32_t k, int32_t window, int32_t block_size, int32_t flags, int32_t* idx,
-                           int32_t* count, int32_t max_sel, void* workspace, size_t workspace_bytes,
+                           const int32_t* q_pos0_b, int32_t k, int32_t window, int32_t block_size, int32_t flags,
+                           int32_t* idx, int32_t* count, int32_t max_sel, void* workspace, size_t workspace_bytes,
                            hipStream_t stream) {
-  return select_impl(scores, B, Tq, Hkv, N, q_pos0, k, window, block_size, flags, idx, count, max_sel, workspace,
-                     workspace_bytes, stream, false);
+  return select_impl(scores, B, Tq, Hkv, N, q_pos0, q_pos0_b, k, window, block_size, flags, idx, count, max_sel,
+                     workspace, workspace_bytes, stream, false);
 }
 
 }  // extern "C"
 
 namespace {
-int select_impl(const float* scores, int32_t B, int32_t Tq, int32_t Hkv, int32_t N, int32_t q_pos0, int32_t k,
-                int32_t window, int32_t block_size, int32_t flags, int32_t* idx, int32_t* count, int32_t max_sel,
-                void* workspace, size_t workspace_bytes, hipStream_t stream, bool pre_hist0) {
+int select_impl(const float* scores, int32_t B, int32_t Tq, int32_t Hkv, int32_t N, int32_t q_pos0,
+                const int32_t* q_pos0_b, int32_t k, int32_t window, int32_t block_size, int32_t flags, int32_t* idx,
+                int32_t* count, int32_t max_sel, void* workspace, size_t workspace_bytes, hipStream_t stream,
+                bool pre_hist0) {
   if (!scores || !idx || !count) return fail(HS2_ERR_INVALID_ARG, "hs2_select_topk_window: NULL scores/idx/count");
   if (B <= 0 || Tq <= 0 || Hkv <= 0 || N <= 0)
     return fail(HS2_ERR_INVALID_ARG, "hs2_select_topk_window: B, Tq, Hkv, N must be positive");
@@ -493,7 +501,7 @@ int select_impl(const float* scores, int32_t B, int32_t Tq, int32_t Hkv, int32_t
   if (max_sel < need_sel)
     return fail(HS2_ERR_INVALID_ARG, "hs2_select_topk_window: max_sel must be >= min(k*block_size + window, N) = " +
                                          std::to_string(need_sel));
-  if (!al16(scores) || ((uintptr_t)idx & 3) || ((uintptr_t)count & 3))
+  if (!al16(scores) || ((uintptr_t)idx & 3) || ((uintptr_t)count & 3) || ((uintptr_t)q_pos0_b & 3))
     return fail(HS2_ERR_INVALID_ARG, "hs2_select_topk_window: scores must be 16-byte aligned, idx/count 4-byte");
   const SelPlan pl = plan_select(B, Tq, Hkv, N, block_size);
   if (!workspace || workspace_bytes < pl.total)
@@ -507,6 +515,7 @@ int select_impl(const float* scores, int32_t B, int32_t Tq, int32_t Hkv, int32_t
   p.Hkv = Hkv;
   p.N = N;
   p.q_pos0 = q_pos0;
+  p.qpos_b = q_pos0_b;
   p.k = k;
   p.window = window;
   p.cand_window = competes ? 0 : window;
@@ -764,7 +773,8 @@ int hs2_sparse_attn_gather_static(const hs2_kv_desc* kv, const void* q, hs2_dtyp
 }
 
 int hs2_swa_attn(const hs2_kv_desc* kv, const void* q, hs2_dtype q_dtype, int32_t Tq, int32_t Hq, int32_t q_pos0,
-                 int32_t window, float softmax_scale, void* out, float* lse, hipStream_t stream) {
+                 const int32_t* q_pos0_b, int32_t window, float softmax_scale, void* out, float* lse,
+                 hipStream_t stream) {
   const char* name = "hs2_swa_attn";
   int st = check_kv(kv, name);
   if (st) return st;
@@ -773,6 +783,7 @@ int hs2_swa_attn(const hs2_kv_desc* kv, const void* q, hs2_dtype q_dtype, int32_
     return fail(HS2_ERR_INVALID_ARG, "hs2_swa_attn: need 0 <= q_pos0 and q_pos0 + Tq <= N");
   if (window < 1) return fail(HS2_ERR_INVALID_ARG, "hs2_swa_attn: window must be at least 1");
   if (!out) return fail(HS2_ERR_INVALID_ARG, "hs2_swa_attn: out must not be NULL");
+  if ((uintptr_t)q_pos0_b & 3) return fail(HS2_ERR_INVALID_ARG, "hs2_swa_attn: q_pos0_b must be 4-byte aligned");
   if (!al16(out) || (lse && ((uintptr_t)lse & 3)))
     return fail(HS2_ERR_INVALID_ARG, "hs2_swa_attn: out must be 16-byte aligned, lse 4-byte");
   if (!std::isfinite(softmax_scale)) return fail(HS2_ERR_INVALID_ARG, "hs2_swa_attn: softmax_scale not finite");
@@ -793,6 +804,7 @@ int hs2_swa_attn(const hs2_kv_desc* kv, const void* q, hs2_dtype q_dtype, int32_
   p.Tq = Tq;
   p.Hq = Hq;
   p.q_pos0 = q_pos0;
+  p.qpos_b = q_pos0_b;
   p.scale_log2 = softmax_scale * 1.44269504088896340736f;
   p.band = window;
   p.out = out;

@@ -407,15 +407,16 @@ __global__ void __launch_bounds__(WAVES * 64) scan_full(ScanParams P) {
   const bool row_ok = (r < P.rows) && (t < P.Tq);
   const int h = g * P.G + (r - tl * P.G);
 
-  const int p_max = P.q_pos0 + min(tp * P.tpack + P.tpack, P.Tq) - 1;
+  const int q0 = qpos_of(P.qpos_b, P.q_pos0, b, P.N, P.Tq);
+  const int p_max = q0 + min(tp * P.tpack + P.tpack, P.Tq) - 1;
   // workgroup tile w = STEP positions; this split owns tiles split, split+nsplit, ...
   // (all splits sweep the cache together)
   const int j_begin = split * STEP;
   const int j_end = p_max + 1;
   const int jstride = P.nsplit * STEP;
-  const int jlim = min(row_ok ? P.q_pos0 + t : -1, j_end - 1);
+  const int jlim = min(row_ok ? q0 + t : -1, j_end - 1);
   // tiles ending at or before j_nomask need no masking for any valid row
-  const int j_nomask = min(P.q_pos0 + tp * P.tpack, j_end - 1);
+  const int j_nomask = min(q0 + tp * P.tpack, j_end - 1);
 
   u32x4_t qf[NC];
   load_q<FP8, D>(qf, P, b, t, h, row_ok, g4);
@@ -554,13 +555,13 @@ struct ChunkRows {
   bool ok;
 };
 template <int RG>
-__device__ __forceinline__ ChunkRows chunk_row(const ScanParams& P, int blk, int rg, int r) {
+__device__ __forceinline__ ChunkRows chunk_row(const ScanParams& P, int q0, int blk, int rg, int r) {
   ChunkRows c;
   const int tl = r / P.G;
   const int tp = blk * RG + rg;
   c.t = tp * P.tpack + tl;
   c.ok = (r < P.rows) && (c.t < P.Tq);
-  c.jlim = c.ok ? P.q_pos0 + c.t : -1;
+  c.jlim = c.ok ? q0 + c.t : -1;
   return c;
 }
 
@@ -833,28 +834,29 @@ __global__ void __launch_bounds__(256, BAND ? 2 : 3) chunk_flash(ScanParams P) {
   const ChunkItem it = chunk_item(P, nblk);
   const int b = it.b, g = it.g;
   const int blk_w = it.blk * 4 + wave;  // this wave's block of RG packs
+  const int q0 = qpos_of(P.qpos_b, P.q_pos0, b, P.N, P.Tq);
 
   u32x4_t qf[RG][NC];
   int jlim[RG], jlo[RG];
 #pragma unroll
   for (int rg = 0; rg < RG; ++rg) {
-    const ChunkRows cr = chunk_row<RG>(P, blk_w, rg, r);
+    const ChunkRows cr = chunk_row<RG>(P, q0, blk_w, rg, r);
     jlim[rg] = cr.jlim;
     jlo[rg] = BAND ? cr.jlim - P.band + 1 : 0;  // sliding window: the row's first position
     load_q<FP8, D>(qf[rg], P, b, cr.ok ? cr.t : 0, g * P.G + (r % P.G), cr.ok, g4);
   }
   const int t_first = it.blk * 4 * RG * P.tpack;  // first token of the workgroup
   const int t_last = min(t_first + 4 * RG * P.tpack, P.Tq) - 1;
-  const int p_max = P.q_pos0 + t_last;
+  const int p_max = q0 + t_last;
   const int wt_first = blk_w * RG * P.tpack;  // first token of this wave
   const int wt_last = min(wt_first + RG * P.tpack, P.Tq) - 1;
-  const int j_nomask = P.q_pos0 + min(wt_first, P.Tq - 1);
+  const int j_nomask = q0 + min(wt_first, P.Tq - 1);
   // sliding window (one split): from the window start of the workgroup's first
   // token, in whole tiles; tiles before the window start of this wave's last
   // token need the lower mask
-  const int j_begin = BAND ? max(0, P.q_pos0 + t_first - P.band + 1) & ~31 : it.split * P.split_len;
+  const int j_begin = BAND ? max(0, q0 + t_first - P.band + 1) & ~31 : it.split * P.split_len;
   const int j_end = BAND ? p_max + 1 : min(j_begin + P.split_len, p_max + 1);
-  const int jlo_nomask = BAND ? P.q_pos0 + max(wt_last, 0) - P.band + 1 : 0;
+  const int jlo_nomask = BAND ? q0 + max(wt_last, 0) - P.band + 1 : 0;
   const int ntile = j_end > j_begin ? (j_end - j_begin + 31) / 32 : 0;
 
   const int64_t kvoff = ((int64_t)b * P.sb + (int64_t)g * P.sh) * FG::EB;
@@ -985,6 +987,7 @@ __global__ void __launch_bounds__(256, 2) chunk_score_flash(ScanParams P) {
   const ChunkItem it = chunk_item(P, nblk);
   const int b = it.b, g = it.g;
   const int blk_w = it.blk * 4 + wave;  // this wave's block of RG packs
+  const int q0 = qpos_of(P.qpos_b, P.q_pos0, b, P.N, P.Tq);
 
   // query fragments (row r of each group), and this lane's four S rows
   // 4*g4 + ii: their token, causal limit and log2-sum-exp
@@ -995,22 +998,22 @@ __global__ void __launch_bounds__(256, 2) chunk_score_flash(ScanParams P) {
   float rl_l2[RG][4];
 #pragma unroll
   for (int rg = 0; rg < RG; ++rg) {
-    const ChunkRows cr = chunk_row<RG>(P, blk_w, rg, r);
+    const ChunkRows cr = chunk_row<RG>(P, q0, blk_w, rg, r);
     load_q<FP8, D>(qf[rg], P, b, cr.ok ? cr.t : 0, g * P.G + (r % P.G), cr.ok, g4);
     const int tp = blk_w * RG + rg;
     const int unit = (b * P.n_tpacks + min(tp, P.n_tpacks - 1)) * P.Hkv + g;
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
-      const ChunkRows crr = chunk_row<RG>(P, blk_w, rg, 4 * g4 + ii);
+      const ChunkRows crr = chunk_row<RG>(P, q0, blk_w, rg, 4 * g4 + ii);
       rl_lim[rg][ii] = crr.jlim;  // -1 for such rows
       rl_l2[rg][ii] = crr.ok ? P.lse2_in[(int64_t)unit * P.rows + 4 * g4 + ii] : __builtin_inff();
     }
   }
   const int t_first = it.blk * 4 * RG * P.tpack;  // first token of the workgroup
   const int t_last = min(t_first + 4 * RG * P.tpack, P.Tq) - 1;
-  const int p_max = P.q_pos0 + t_last;
+  const int p_max = q0 + t_last;
   const int wt_first = blk_w * RG * P.tpack;  // first token of this wave
-  const int j_nomask = P.q_pos0 + min(wt_first, P.Tq - 1);
+  const int j_nomask = q0 + min(wt_first, P.Tq - 1);
   const int j_begin = it.split * P.split_len;
   const int j_end = min(j_begin + P.split_len, P.N);  // every position gets a score (0 past p)
   const int j_load = min(j_end, p_max + 1);           // tiles starting below it are computed
@@ -1160,7 +1163,7 @@ __global__ void __launch_bounds__(WAVES * 64) scan_gather(ScanParams P) {
   // the unit's rows: its index list, or with a sliding window the contiguous
   // range [p - band + 1, p] (clipped at 0)
   const int32_t* list = P.idx + (int64_t)unit * P.max_sel;
-  const int p_t = P.q_pos0 + t;
+  const int p_t = qpos_of(P.qpos_b, P.q_pos0, b, P.N, P.Tq) + t;
   const int n = P.band > 0 ? min(p_t + 1, P.band) : min(max(P.count[unit], 0), P.max_sel);
   const int lo = p_t - n + 1;
 
@@ -1446,7 +1449,7 @@ __global__ void __launch_bounds__(256) scan_f32(ScanParams P) {
   const int t = (unit / P.Hkv) % P.Tq;  // tpack == 1
   const int b = unit / (P.Hkv * P.Tq);
   const int R = P.G;
-  const int p = P.q_pos0 + t;
+  const int p = qpos_of(P.qpos_b, P.q_pos0, b, P.N, P.Tq) + t;
 
   int j_begin, j_end;
   const int32_t* list = nullptr;
@@ -1603,8 +1606,8 @@ __device__ __forceinline__ void sel_init_unit_rows(const CombineParams& P, int b
     const int t = tp * P.tpack + tl;
     if (t >= P.Tq) break;
     const int64_t u = ((int64_t)b * P.Tq + t) * P.Hkv + g;
-    sel_init_row(P.sel_state + u * ST_WORDS, P.sel_hist + u * 3 * kHistBins, P.q_pos0 + t, P.sel_k, P.sel_window, 1,
-                 tid, 256);
+    sel_init_row(P.sel_state + u * ST_WORDS, P.sel_hist + u * 3 * kHistBins,
+                 qpos_of(P.qpos_b, P.q_pos0, b, P.N, P.Tq) + t, P.sel_k, P.sel_window, 1, tid, 256);
   }
 }
 
@@ -1823,7 +1826,7 @@ __global__ void __launch_bounds__(256) score(ScoreParams P) {
   for (int tl = 0; tl < P.tpack; ++tl) {
     const int t = tp * P.tpack + tl;
     if (t >= P.Tq) break;
-    const int p = P.q_pos0 + t;
+    const int p = qpos_of(P.qpos_b, P.q_pos0, b, P.N, P.Tq) + t;
     float s[4] = {0.f, 0.f, 0.f, 0.f};
     if (j4 <= p) {
       bool exact = false;
@@ -1866,7 +1869,7 @@ __global__ void __launch_bounds__(256) score_hist(ScoreParams P) {
   const int g = unit % P.Hkv;
   const int t = (unit / P.Hkv) % P.n_tpacks;  // tpack = 1
   const int b = unit / (P.Hkv * P.n_tpacks);
-  const int p = P.q_pos0 + t;
+  const int p = qpos_of(P.qpos_b, P.q_pos0, b, P.N, P.Tq) + t;
   const int base = blockIdx.x * 1024 * R;
   const int ncand = sel_ncand(p, P.sel_window);
   const int take = sel_take(ncand, P.sel_k, 1);

@@ -8,6 +8,15 @@
 
 namespace hs2 {
 
+// Position of query token 0 of batch entry b: the per-batch array when the
+// caller gave one (clamped into [0, N - Tq] so that every access stays inside
+// the cache), else the call's q_pos0.
+__host__ __device__ inline int qpos_of(const int32_t* qpos_b, int q_pos0, int b, int N, int Tq) {
+  if (!qpos_b) return q_pos0;
+  const int v = qpos_b[b];
+  return v < 0 ? 0 : (v > N - Tq ? N - Tq : v);
+}
+
 // ---------------------------------------------------------------------------
 // full / sparse attention "scan" launches
 // ---------------------------------------------------------------------------
@@ -23,6 +32,7 @@ struct ScanParams {
   int B, Hkv, N, D, G;
   const void* q;
   int Tq, Hq, q_pos0;
+  const int32_t* qpos_b;  // per-batch q_pos0 [B] (device), or nullptr
   float scale_log2;  // softmax_scale * log2(e)
   int tpack;         // tokens per unit
   int n_tpacks;      // ceil(Tq / tpack)
@@ -96,7 +106,8 @@ struct CombineParams {
   // candidate window); sel_state nullptr = no selection
   int32_t* sel_state;
   int32_t* sel_hist;
-  int sel_k, sel_window, q_pos0;
+  int sel_k, sel_window, q_pos0, N;
+  const int32_t* qpos_b;  // per-batch q_pos0 [B] (device), or nullptr
 };
 
 struct ScoreParams {
@@ -105,6 +116,7 @@ struct ScoreParams {
   const float* lse2;
   int64_t npad;
   int rows, tpack, n_tpacks, G, Hkv, Tq, N, q_pos0;
+  const int32_t* qpos_b;  // per-batch q_pos0 [B] (device), or nullptr
   float* scores;  // [B, Tq, Hkv, N]
   // one query token per unit: also count the first radix digit of every
   // candidate's score (positions [0, p - sel_window], sel_window being the
@@ -130,6 +142,7 @@ struct ScoreParams {
 struct SelectParams {
   const float* scores;  // [units][N]
   int units, Tq, Hkv, N, q_pos0, k, window, block_size, max_sel, nchunks;
+  const int32_t* qpos_b;  // per-batch q_pos0 [B] (device), or nullptr
   // candidates of a query at p: [0, p - cand_window]; cand_window = window,
   // or 0 when the window competes (then a last kernel places the window after
   // the selected positions below it)

@@ -89,11 +89,17 @@ __device__ __forceinline__ T block_exclusive_scan(T v, T* sm, T& total) {
   return (T)a[0];
 }
 
+// Query position of selection row u = (b, t, g).
+__device__ __forceinline__ int row_pos(const SelectParams& P, int u) {
+  return qpos_of(P.qpos_b, P.q_pos0, u / (P.Hkv * P.Tq), P.N, P.Tq) + (u / P.Hkv) % P.Tq;
+}
+
 __global__ void __launch_bounds__(256) sel_init(SelectParams P) {
   const int u = blockIdx.x;
   const int t = (u / P.Hkv) % P.Tq;
   sel_init_row(P.state + (int64_t)u * ST_WORDS, P.block_size == 1 ? P.hist + (int64_t)u * 3 * kHistBins : nullptr,
-               P.q_pos0 + t, P.k, P.cand_window, P.block_size, threadIdx.x, 256);
+               qpos_of(P.qpos_b, P.q_pos0, u / (P.Hkv * P.Tq), P.N, P.Tq) + t, P.k, P.cand_window, P.block_size,
+               threadIdx.x, 256);
 }
 
 // digits: pass 0 = bits 31..20, pass 1 = bits 19..8, pass 2 = bits 7..0
@@ -239,7 +245,7 @@ __global__ void __launch_bounds__(256) sel_hist(SelectParams P) {
   int32_t* st = P.state + (int64_t)u * ST_WORDS;
   // the row's mode and candidate count follow from its position (the same
   // values the set-up stored), so the score loads need not wait for a state read
-  const int ncand = sel_ncand(P.q_pos0 + (u / P.Hkv) % P.Tq, P.cand_window);
+  const int ncand = sel_ncand(row_pos(P, u), P.cand_window);
   const int take = sel_take(ncand, P.k, 1);
   if (sel_mode(take, ncand, 1) != MODE_RADIX) return;
   if (PASS == 2 && P.collected && st[ST_COMPACT]) return;  // finished by the collected path
@@ -496,7 +502,7 @@ __global__ void __launch_bounds__(256) sel_emit(SelectParams P) {
   __shared__ int32_t sm[264];
   const int u = blockIdx.y, chunk = blockIdx.x;
   const int32_t* st = P.state + (int64_t)u * ST_WORDS;
-  const int p = P.q_pos0 + (u / P.Hkv) % P.Tq;  // as stored by the set-up
+  const int p = row_pos(P, u);  // as stored by the set-up
   const int ncand = sel_ncand(p, P.cand_window);
   const int take = sel_take(ncand, P.k, 1);
   const int mode = sel_mode(take, ncand, 1);
@@ -627,7 +633,7 @@ __global__ void __launch_bounds__(256) sel_emit(SelectParams P) {
 __global__ void __launch_bounds__(256) sel_window_merge(SelectParams P) {
   __shared__ int32_t sm[264];
   const int u = blockIdx.x;
-  const int p = P.q_pos0 + (u / P.Hkv) % P.Tq;
+  const int p = row_pos(P, u);
   const int take = sel_take(sel_ncand(p, P.cand_window), P.k, 1);
   const int wlo = max(0, p - P.window + 1);
   const int nw = p - wlo + 1;
@@ -650,7 +656,7 @@ __global__ void __launch_bounds__(256) sel_window_merge(SelectParams P) {
 __global__ void __launch_bounds__(256) sel_block_mass(SelectParams P) {
   const int u = blockIdx.y;
   const int beta = blockIdx.x * 256 + threadIdx.x;
-  const int ncand = sel_ncand(P.q_pos0 + (u / P.Hkv) % P.Tq, P.window);  // as stored by the set-up
+  const int ncand = sel_ncand(row_pos(P, u), P.window);  // as stored by the set-up
   const int nb = ncand > 0 ? (ncand - 1) / P.block_size + 1 : 0;
   if (beta >= nb) return;
   const float* s = P.scores + (int64_t)u * P.N;
@@ -680,7 +686,7 @@ template <int BS>
 __global__ void __launch_bounds__(256) sel_block_mass_tiled(SelectParams P) {
   __shared__ float sv[kMassTile + kMassTile / BS];
   const int u = blockIdx.y;
-  const int ncand = sel_ncand(P.q_pos0 + (u / P.Hkv) % P.Tq, P.window);  // as stored by the set-up
+  const int ncand = sel_ncand(row_pos(P, u), P.window);  // as stored by the set-up
   const int lo = blockIdx.x * kMassTile;
   if (lo >= ncand) return;
   const float* s = P.scores + (int64_t)u * P.N;

@@ -58,14 +58,15 @@ _status_string = _sig("hs2_status_string", ctypes.c_char_p, [ctypes.c_int])
 _last_error = _sig("hs2_last_error", ctypes.c_char_p, [])
 _full_ws = _sig("hs2_full_attn_scores_workspace", _sz, [_KVP, _i32, _i32])
 _full = _sig("hs2_full_attn_scores", ctypes.c_int,
-             [_KVP, _vp, _i32, _i32, _i32, _i32, _f32, _vp, _vp, _vp, _vp, _sz, _vp])
+             [_KVP, _vp, _i32, _i32, _i32, _i32, _vp, _f32, _vp, _vp, _vp, _vp, _sz, _vp])
 _topk_ws = _sig("hs2_full_attn_topk_workspace", _sz, [_KVP, _i32, _i32])
 _topk = _sig("hs2_full_attn_topk", ctypes.c_int,
-             [_KVP, _vp, _i32, _i32, _i32, _i32, _f32, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _i32, _vp, _sz, _vp])
+             [_KVP, _vp, _i32, _i32, _i32, _i32, _vp, _f32, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _i32, _vp, _sz,
+              _vp])
 _sel_ws = _sig("hs2_select_workspace", _sz, [_i32, _i32, _i32, _i32])
 _sel_ws_for = _sig("hs2_select_workspace_for", _sz, [_i32, _i32, _i32, _i32, _i32])
 _select = _sig("hs2_select_topk_window", ctypes.c_int,
-               [_vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _i32, _vp, _sz, _vp])
+               [_vp, _i32, _i32, _i32, _i32, _i32, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _i32, _vp, _sz, _vp])
 _sparse = _sig("hs2_sparse_attn_gather", ctypes.c_int,
                [_KVP, _vp, _i32, _i32, _i32, _f32, _vp, _vp, _i32, _vp, _vp, _vp])
 _sparse_ws_size = _sig("hs2_sparse_attn_workspace", _sz, [_i32, _i32, _i32, _i32, _i32])
@@ -77,7 +78,7 @@ _sparse_static = _sig("hs2_sparse_attn_gather_static", ctypes.c_int,
 _bridge_layers_ws = _sig("hs2_kv_bridge_layers_workspace", _sz, [_i32, _i32, _i32, _i32])
 _bridge_layers = _sig("hs2_kv_bridge_layers", ctypes.c_int,
                       [_vp, _i32, _i32, _vp, _i32, ctypes.POINTER(KVOutDesc), _i32, _i32, _i32, _vp, _sz, _vp])
-_swa = _sig("hs2_swa_attn", ctypes.c_int, [_KVP, _vp, _i32, _i32, _i32, _i32, _i32, _f32, _vp, _vp, _vp])
+_swa = _sig("hs2_swa_attn", ctypes.c_int, [_KVP, _vp, _i32, _i32, _i32, _i32, _vp, _i32, _f32, _vp, _vp, _vp])
 _bridge = _sig("hs2_kv_bridge", ctypes.c_int, [_vp, _i32, _i32, _vp, ctypes.POINTER(KVOutDesc), _i32, _i32, _vp])
 _dbg_e4m3 = _sig("hs2_debug_e4m3fn_to_f32", ctypes.c_int, [_vp, _vp, _i32, _vp])
 _dbg_stream = _sig("hs2_debug_stream_read", ctypes.c_int, [_vp, _sz, _vp, _i32, _vp])
@@ -159,8 +160,17 @@ def full_attn_scores_workspace(k, v, Tq: int, Hq: int) -> int:
     return int(_full_ws(ctypes.byref(d), Tq, Hq))
 
 
+def _qpos(q_pos0_b):
+    if q_pos0_b is None:
+        return None
+    _dense(q_pos0_b)
+    if q_pos0_b.dtype != torch.int32:
+        raise TypeError("q_pos0_b must be an int32 device tensor [B]")
+    return q_pos0_b.data_ptr()
+
+
 def full_attn_scores(k, v, q, q_pos0: int, softmax_scale: float | None = None, k_scale=None, v_scale=None,
-                     out=None, lse=None, scores=None, workspace=None, want_lse: bool = True):
+                     out=None, lse=None, scores=None, workspace=None, want_lse: bool = True, q_pos0_b=None):
     """Full-attention layer: returns (out [B,Tq,Hq,D], lse [B,Tq,Hq] or None, scores [B,Tq,Hkv,N])."""
     d = kv_desc(k, v, k_scale, v_scale)
     B, Tq, Hq, D = q.shape
@@ -177,7 +187,7 @@ def full_attn_scores(k, v, q, q_pos0: int, softmax_scale: float | None = None, k
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
     _dense(q, out, lse, scores, workspace)
-    st = _full(ctypes.byref(d), q.data_ptr(), _dtype_code(q), Tq, Hq, int(q_pos0), float(softmax_scale),
+    st = _full(ctypes.byref(d), q.data_ptr(), _dtype_code(q), Tq, Hq, int(q_pos0), _qpos(q_pos0_b), float(softmax_scale),
                out.data_ptr(), None if lse is None else lse.data_ptr(), scores.data_ptr(),
                workspace.data_ptr(), workspace.numel(), _stream())
     _check(st, "hs2_full_attn_scores")
@@ -191,7 +201,8 @@ def full_attn_topk_workspace(k, v, Tq: int, Hq: int) -> int:
 
 def full_attn_topk(k, v, q, q_pos0: int, topk: int, window: int, max_sel: int | None = None,
                    softmax_scale: float | None = None, k_scale=None, v_scale=None, out=None, lse=None, scores=None,
-                   idx=None, count=None, workspace=None, want_lse: bool = True, window_competes: bool = False):
+                   idx=None, count=None, workspace=None, want_lse: bool = True, window_competes: bool = False,
+                   q_pos0_b=None):
     """Full layer + token top-k with forced window in one call (window_competes:
     the window takes no budget of its own; see hs2.h).
     Returns (out, lse, scores, idx [B,Tq,Hkv,max_sel] int32, count [B,Tq,Hkv] int32)."""
@@ -216,7 +227,7 @@ def full_attn_topk(k, v, q, q_pos0: int, topk: int, window: int, max_sel: int | 
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
     _dense(q, out, lse, scores, idx, count, workspace)
-    st = _topk(ctypes.byref(d), q.data_ptr(), _dtype_code(q), Tq, Hq, int(q_pos0), float(softmax_scale),
+    st = _topk(ctypes.byref(d), q.data_ptr(), _dtype_code(q), Tq, Hq, int(q_pos0), _qpos(q_pos0_b), float(softmax_scale),
                out.data_ptr(), None if lse is None else lse.data_ptr(), scores.data_ptr(), int(topk), int(window),
                SEL_WINDOW_COMPETES if window_competes else 0, idx.data_ptr(), count.data_ptr(), int(max_sel), workspace.data_ptr(), workspace.numel(), _stream())
     _check(st, "hs2_full_attn_topk")
@@ -230,7 +241,7 @@ def select_workspace(B, Tq, Hkv, N, block_size: int | None = None) -> int:
 
 
 def select_topk_window(scores, q_pos0: int, k: int, window: int, block_size: int = 1, max_sel: int | None = None,
-                       idx=None, count=None, workspace=None, window_competes: bool = False):
+                       idx=None, count=None, workspace=None, window_competes: bool = False, q_pos0_b=None):
     """Top-k (token or block) + forced window: returns (idx int32, count int32)."""
     B, Tq, Hkv, N = scores.shape
     if max_sel is None:
@@ -243,7 +254,7 @@ def select_topk_window(scores, q_pos0: int, k: int, window: int, block_size: int
     if workspace is None:
         workspace = torch.empty(max(select_workspace(B, Tq, Hkv, N, block_size), 256), dtype=torch.uint8, device=dev)
     _dense(scores, idx, count, workspace)
-    st = _select(scores.data_ptr(), B, Tq, Hkv, N, int(q_pos0), int(k), int(window), int(block_size),
+    st = _select(scores.data_ptr(), B, Tq, Hkv, N, int(q_pos0), _qpos(q_pos0_b), int(k), int(window), int(block_size),
                  SEL_WINDOW_COMPETES if window_competes else 0, idx.data_ptr(), count.data_ptr(), int(max_sel), workspace.data_ptr(), workspace.numel(), _stream())
     _check(st, "hs2_select_topk_window")
     return idx, count
@@ -315,7 +326,7 @@ def sparse_attn_gather_static(k, v, q, idx, count, softmax_scale: float | None =
 
 
 def swa_attn(k, v, q, q_pos0: int, window: int, softmax_scale: float | None = None, k_scale=None, v_scale=None,
-             out=None, lse=None, want_lse: bool = True):
+             out=None, lse=None, want_lse: bool = True, q_pos0_b=None):
     """Sliding-window attention: query t attends to [q_pos0 + t - window + 1, q_pos0 + t]."""
     d = kv_desc(k, v, k_scale, v_scale)
     B, Tq, Hq, D = q.shape
@@ -326,7 +337,8 @@ def swa_attn(k, v, q, q_pos0: int, window: int, softmax_scale: float | None = No
     if lse is None and want_lse:
         lse = torch.empty((B, Tq, Hq), dtype=torch.float32, device=q.device)
     _dense(q, out, lse)
-    st = _swa(ctypes.byref(d), q.data_ptr(), _dtype_code(q), Tq, Hq, int(q_pos0), int(window), float(softmax_scale),
+    st = _swa(ctypes.byref(d), q.data_ptr(), _dtype_code(q), Tq, Hq, int(q_pos0), _qpos(q_pos0_b), int(window),
+              float(softmax_scale),
               out.data_ptr(), None if lse is None else lse.data_ptr(), _stream())
     _check(st, "hs2_swa_attn")
     return out, lse

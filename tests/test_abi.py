@@ -77,7 +77,7 @@ def desc(hs2, dtype=1, B=1, H=2, N=256, D=128, sn=None, k=FAKE, scales=False, cl
 
 def full(hs2, d, q=FAKE, qdt=1, Tq=1, Hq=16, q_pos0=None, out=FAKE, scores=FAKE, ws=FAKE, wsb=1 << 40):
     q_pos0 = d.N - Tq if q_pos0 is None else q_pos0
-    return hs2._full(ctypes.byref(d), q, qdt, Tq, Hq, q_pos0, 0.1, out, None, scores, ws, wsb, None)
+    return hs2._full(ctypes.byref(d), q, qdt, Tq, Hq, q_pos0, None, 0.1, out, None, scores, ws, wsb, None)
 
 
 @pytest.mark.parametrize("case,want", [
@@ -85,7 +85,7 @@ def full(hs2, d, q=FAKE, qdt=1, Tq=1, Hq=16, q_pos0=None, out=FAKE, scores=FAKE,
     ("null_kv", -1), ("null_q", -1), ("null_out", -1), ("hq_not_multiple", -1),
     ("qpos_past_end", -1), ("neg_qpos", -1), ("misaligned_q", -1), ("misaligned_stride", -1),
     ("head_dim_96", -2), ("group_32", -2), ("fp8_without_scales", -2), ("q_f32_kv_bf16", -2),
-    ("bad_dtype", -2), ("ws_misaligned", -1),
+    ("bad_dtype", -2), ("ws_misaligned", -1), ("qpos_b_misaligned", -1),
 ])
 def test_full_attn_validation(hs2, case, want):
     d = desc(hs2)
@@ -93,7 +93,7 @@ def test_full_attn_validation(hs2, case, want):
     if case == "ok_shape_but_small_ws":
         kw["wsb"] = 16
     elif case == "null_kv":
-        assert hs2._full(None, FAKE, 1, 1, 16, 0, 0.1, FAKE, None, FAKE, FAKE, 1 << 40, None) == want
+        assert hs2._full(None, FAKE, 1, 1, 16, 0, None, 0.1, FAKE, None, FAKE, FAKE, 1 << 40, None) == want
         return
     elif case == "null_q":
         kw["q"] = None
@@ -122,6 +122,10 @@ def test_full_attn_validation(hs2, case, want):
         d = desc(hs2, dtype=7)
     elif case == "ws_misaligned":
         kw["ws"] = FAKE + 16
+    elif case == "qpos_b_misaligned":
+        assert hs2._full(ctypes.byref(d), FAKE, 1, 1, 16, d.N - 1, FAKE + 2, 0.1, FAKE, None, FAKE, FAKE, 1 << 40,
+                         None) == want
+        return
     assert full(hs2, d, **kw) == want
     assert hs2._last_error().decode()
 
@@ -162,14 +166,14 @@ def test_select_validation(hs2, case, want):
         a["flags"] = 2
     elif case == "competes_blocks":
         a["flags"], a["bs"], a["k"] = 1, 64, 16
-    st = hs2._select(a["scores"], a["B"], a["Tq"], a["Hkv"], a["N"], a["q_pos0"], a["k"], a["window"], a["bs"],
+    st = hs2._select(a["scores"], a["B"], a["Tq"], a["Hkv"], a["N"], a["q_pos0"], None, a["k"], a["window"], a["bs"],
                      a["flags"], a["idx"], a["cnt"], a["max_sel"], a["ws"], a["wsb"], None)
     assert st == want
 
 
 def test_select_max_sel_rule_uses_context_cap(hs2):
     # N smaller than k + window: max_sel = N suffices (fails later only on the workspace)
-    st = hs2._select(FAKE, 1, 1, 1, 600, 599, 1024, 128, 1, 0, FAKE, FAKE, 600, FAKE, 10, None)
+    st = hs2._select(FAKE, 1, 1, 1, 600, 599, None, 1024, 128, 1, 0, FAKE, FAKE, 600, FAKE, 10, None)
     assert st == -3
 
 
@@ -178,9 +182,9 @@ def test_full_attn_topk_validation(hs2):
     ws = int(hs2._topk_ws(ctypes.byref(d), 1, 16))
     full = int(hs2._full_ws(ctypes.byref(d), 1, 16))
     assert ws > full
-    args = lambda idx=FAKE, k=8, window=4, max_sel=12, wsb=ws, flags=0: (ctypes.byref(d), FAKE, 1, 1, 16, 255, 0.1,
-                                                                          FAKE, None, FAKE, k, window, flags, idx, FAKE,
-                                                                          max_sel, FAKE, wsb, None)
+    args = lambda idx=FAKE, k=8, window=4, max_sel=12, wsb=ws, flags=0: (ctypes.byref(d), FAKE, 1, 1, 16, 255, None,
+                                                                          0.1, FAKE, None, FAKE, k, window, flags, idx,
+                                                                          FAKE, max_sel, FAKE, wsb, None)
     assert hs2._topk(*args(idx=None)) == -1            # NULL idx
     assert hs2._topk(*args(k=-1)) == -1                # negative k
     assert hs2._topk(*args(max_sel=11)) == -1          # max_sel < k + window
