@@ -234,9 +234,11 @@ __global__ void __launch_bounds__(256) bridge_grow_prep(BridgeLayers P, int Hkv)
 // workgroup 0 stores s'.  When s' > s the head's rows [0, pos0) are
 // re-encoded in place, code' = encode(fp32(decode(code) * s) / s'); the new
 // rows [pos0, pos0 + T) get encode(y / s') (zero codes when s' = 0).  Every
-// workgroup first stages all heads' (s, s') in LDS (one memory round trip);
-// the grid's threads then share each head's rows 16 bytes at a time, and a
-// workgroup with no new rows to encode leaves at once unless a scale grew.
+// workgroup first stages all heads' (s, s') in LDS (one memory round trip).
+// The grid's threads share each grown head's older rows 16 bytes at a time,
+// and share the new rows of all heads at once (one 16-byte unit of one head
+// per thread, so a one-token append encodes every head in one round trip); a
+// workgroup with no new units leaves at once unless a scale grew.
 constexpr int kGrowHeads = 1024;  // heads staged in LDS (the launcher checks L * 2 * Hkv)
 __global__ void __launch_bounds__(256) bridge_grow_finish(BridgeLayers P, int T, int Hkv, int D) {
   __shared__ float s_old_l[kGrowHeads], s_new_l[kGrowHeads];
@@ -257,14 +259,15 @@ __global__ void __launch_bounds__(256) bridge_grow_finish(BridgeLayers P, int T,
   }
   __syncthreads();
   const int64_t gtid = (int64_t)blockIdx.x * 256 + threadIdx.x, gstride = (int64_t)gridDim.x * 256;
-  const int64_t new_units = (int64_t)T * u16;
+  const int64_t head_units = (int64_t)T * u16, new_units = head_units * nh;
   if (!any_grew && (int64_t)blockIdx.x * 256 >= new_units) return;  // uniform
-  for (int i = 0; i < nh; ++i) {
-    const int l = i / (2 * Hkv), part = (i / Hkv) & 1, h = i % Hkv;
-    const BridgeOut& O = P.out[l];
-    const float s_old = s_old_l[i], s_new = s_new_l[i];
-    uint8_t* base = (uint8_t*)(part ? O.v : O.k) + (int64_t)h * O.sh;
-    if (s_new > s_old) {  // uniform: re-encode the older rows at the new scale
+  if (any_grew) {
+    for (int i = 0; i < nh; ++i) {
+      const float s_old = s_old_l[i], s_new = s_new_l[i];
+      if (!(s_new > s_old)) continue;  // uniform: re-encode the older rows at the new scale
+      const int l = i / (2 * Hkv), part = (i / Hkv) & 1, h = i % Hkv;
+      const BridgeOut& O = P.out[l];
+      uint8_t* base = (uint8_t*)(part ? O.v : O.k) + (int64_t)h * O.sh;
       const int64_t units = (int64_t)P.pos0 * u16;
       for (int64_t u = gtid; u < units; u += gstride) {
         const int64_t row = u / u16;
@@ -283,22 +286,26 @@ __global__ void __launch_bounds__(256) bridge_grow_finish(BridgeLayers P, int T,
         *p = o;
       }
     }
-    const float* y = P.y + (int64_t)l * T * C + part * Hkv * D + h * D;
-    for (int64_t u = gtid; u < new_units; u += gstride) {
-      const int64_t t = u / u16;
-      const int col = (int)(u - t * u16) * 16;
-      const float* yp = y + t * C + col;
-      u32x4_t o;
+  }
+  for (int64_t u = gtid; u < new_units; u += gstride) {
+    const int i = (int)(u / head_units);
+    const int64_t r = u - i * head_units, t = r / u16;
+    const int col = (int)(r - t * u16) * 16;
+    const int l = i / (2 * Hkv), part = (i / Hkv) & 1, h = i % Hkv;
+    const BridgeOut& O = P.out[l];
+    const float s_new = s_new_l[i];
+    const float* yp = P.y + ((int64_t)l * T + t) * C + part * Hkv * D + h * D + col;
+    u32x4_t o;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        uint32_t word = 0;
+    for (int q = 0; q < 4; ++q) {
+      uint32_t word = 0;
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          word |= (uint32_t)(s_new > 0.f ? e4m3fn_rne_sat(yp[4 * q + e] / s_new) : 0u) << (8 * e);
-        o[q] = word;
-      }
-      *(u32x4_t*)(base + (P.pos0 + t) * O.sn + col) = o;
+      for (int e = 0; e < 4; ++e)
+        word |= (uint32_t)(s_new > 0.f ? e4m3fn_rne_sat(yp[4 * q + e] / s_new) : 0u) << (8 * e);
+      o[q] = word;
     }
+    uint8_t* base = (uint8_t*)(part ? O.v : O.k) + (int64_t)h * O.sh;
+    *(u32x4_t*)(base + (P.pos0 + t) * O.sn + col) = o;
   }
 }
 
@@ -343,8 +350,9 @@ hipError_t launch_bridge(const uint16_t* hidden, int T, int dm, const uint16_t* 
   }
   if (grow) {
     TimedLaunch tl("kv_bridge", s);
-    // enough threads for the largest head region, 16 bytes each, at most 2048 workgroups
-    const int64_t units = (int64_t)(out.pos0 + T) * (D / 16);
+    // enough threads for the largest head region or all heads' new rows, 16
+    // bytes each, at most 2048 workgroups
+    const int64_t units = std::max<int64_t>((int64_t)out.pos0, (int64_t)T * out.L * 2 * Hkv) * (D / 16);
     const int blocks = (int)std::min<int64_t>(2048, std::max<int64_t>(1, (units + 255) / 256));
     hipLaunchKernelGGL(bridge_grow_finish, dim3(blocks), dim3(256), 0, s, out, T, Hkv, D);
     if ((e = hipGetLastError()) != hipSuccess) return e;
