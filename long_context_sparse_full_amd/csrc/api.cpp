@@ -152,13 +152,18 @@ SelPlan plan_select(int B, int Tq, int Hkv, int N, int block_size) {
   size_t off = 0;
   p.off_state = off;
   off = a256(off + (size_t)p.units * 16 * sizeof(int32_t));
-  if (block_size == 1) {
+  if (block_size == 1 && !hs2::sel_bracketed(p.units, p.nchunks)) {  // digit histograms and per-chunk counts
     p.off_hist = off;
     off = a256(off + (size_t)p.units * 3 * hs2::kHistBins * sizeof(int32_t));
     p.off_cnt = off;
     off = a256(off + (size_t)p.units * p.nchunks * 258 * sizeof(int32_t));
     p.off_cand = off;
-    off = a256(off + (size_t)p.units * hs2::kCandWords * sizeof(int32_t));
+  } else if (block_size == 1) {  // bracketed: each chunk's list lengths and lists
+    p.off_hist = off;
+    p.off_cnt = off;
+    off = a256(off + (size_t)p.units * p.nchunks * 2 * sizeof(int32_t));
+    p.off_cand = off;
+    off = a256(off + (size_t)p.units * p.nchunks * hs2::kCandWords * sizeof(int32_t));
   } else {
     p.off_bmass = off;
     off = a256(off + (size_t)p.units * p.nblocks_max * sizeof(double));
@@ -179,10 +184,11 @@ int hip_fail(hipError_t e, const char* what) {
 // ---------------------------------------------------------------------------
 // event timing
 // ---------------------------------------------------------------------------
-const char* const kKernelNames[] = {"full_scan",   "combine",     "score",        "select_init",
-                                    "select_hist", "select_collect", "select_finish", "select_emit",
-                                    "select_window", "select_block_mass", "select_block_pick", "sparse_gather", "kv_bridge", "stream_read",
-                                    "chunk_full",  "chunk_score", "swa_chunk", nullptr};
+const char* const kKernelNames[] = {"full_scan",      "combine",        "score",         "select_init",
+                                    "select_hist",    "select_bracket", "select_collect", "select_finish",
+                                    "select_exact",   "select_emit",    "select_window",  "select_block_mass",
+                                    "select_block_pick", "sparse_gather", "kv_bridge",    "stream_read",
+                                    "chunk_full",     "chunk_score",    "swa_chunk",      nullptr};
 
 // Timing state (only while hs2_timing_enable(1) is in force): the event pairs
 // of the launches since the last reset.  Events are created per launch and
@@ -373,7 +379,9 @@ int full_layer(const hs2_kv_desc* kv, const void* q, hs2_dtype q_dtype, int32_t 
   c.lse2 = at<float>(workspace, pl.off_lse2);
   // one query token per unit: the merge sets the selection's rows up and the
   // score pass counts their first digit, which saves the selection two passes
-  const bool pre_sel = sel != nullptr && pl.tpack == 1;
+  // (grids of many rows take the bracketed selection, which needs neither)
+  const bool pre_sel = sel != nullptr && pl.tpack == 1 &&
+                       !hs2::sel_bracketed(pl.units, (int)cdiv(kv->N, hs2::kSelChunk));
   int32_t* sel_hist = nullptr;
   if (pre_sel) {
     const SelPlan sp = plan_select(kv->B, Tq, kv->Hkv, kv->N, 1);

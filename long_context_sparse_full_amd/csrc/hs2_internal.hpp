@@ -78,17 +78,25 @@ constexpr int kChunkMinPacks = 4;
 
 constexpr int kSelChunk = 16384;  // candidates per workgroup in the select passes
 constexpr int kHistBins = 4096;  // 12-bit digits
-// Workgroups per selection pass from which the passes are throughput-bound
-// (larger grids take the collected path).
+// Workgroups per selection pass (units x chunks) from which a grid takes the
+// bracketed path: one pass over the scores instead of four.
 constexpr int kSelMinWorkgroups = 2048;
-// collected selection path: largest k, largest 24-bit threshold bin, and the
-// per-row list words (positions above the bin, then the bin's keys and positions)
+// bracketed path: largest k it settles, largest bin between the bracket's
+// bounds, and the list words of each chunk (positions above the bin, then the
+// bin's positions and keys)
 constexpr int kCompactTake = 2048;
-constexpr int kCompactBin = 1024;
+constexpr int kCompactBin = 4096;
 constexpr int kCandWords = kCompactTake + 2 * kCompactBin;
-// candidates per row of the collected path (its finishing step keeps a bitmap
-// of them in LDS: 128 KiB at this size)
-constexpr int kCompactMaxCand = 1 << 20;
+// sample of a row for its bracket: every SR-th run of 64 positions, SR at
+// least kBracketStride (rows of more than kBracketRuns runs), at most
+// kBracketRuns runs
+constexpr int kBracketRuns = 256;
+constexpr int kBracketStride = 16;
+// chunks per row the bracketed path's finishing step gathers from
+constexpr int kFinishMaxChunks = 1024;
+__host__ __device__ inline bool sel_bracketed(int units, int nchunks) {
+  return (int64_t)units * nchunks >= kSelMinWorkgroups;
+}
 
 struct CombineParams {
   const float* part_ml;
@@ -151,12 +159,12 @@ struct SelectParams {
   int32_t* count;
   int32_t* state;   // [units][16]
   int32_t* hist;    // [units][3][4096] digit histograms of the three passes
-  int32_t* cnt;     // [units][nchunks][258]: keys above the 24-bit prefix, suffix sums of the last digit
-  int32_t* cand;    // [units][kCandWords]: the collected path's lists
+  int32_t* cnt;     // [units][nchunks][258]: keys above the 24-bit prefix, suffix sums of the last digit;
+                    // bracketed path: [units][nchunks][2] list lengths
+  int32_t* cand;    // bracketed path: [units][nchunks][kCandWords] each chunk's lists
   double* bmass;    // [units][nblocks_max] (block mode)
   int nblocks_max;
   int pre_hist0;    // token mode: state and pass-0 histogram already built (merge + score pass)
-  int collected;    // set by the launcher: the collected path runs (rows may finish there)
 };
 
 // launchers (return hipError_t of the launch)

@@ -14,20 +14,25 @@
 // The emit pass keeps every key above the threshold and the lowest-positioned
 // keys equal to it, compacted in ascending position order.
 //
-// Collected path: the keys that share the 24-bit prefix found by the first two
-// passes are few (a handful on attention scores: the third digit only splits
-// near-equal values).  Where that bin and k are small enough, one pass
-// collects the keys above the prefix (all selected) and the bin's keys, and
-// one workgroup per row finishes the selection on chip: the bin's keys in
-// (score desc, position asc) order, then every taken position sorted
-// ascending.  That replaces the third histogram pass and the emit pass, each a
-// full read of the scores; rows whose bin is too large take those two passes.
+// Bracketed path (grids of many rows, where the passes are throughput-bound):
+// a fixed sample of each row -- every SR-th run of 64 positions, at most
+// 16384 keys -- gives the sample's keys of ranks r -/+ m around the expected
+// rank r of the k-th key (m = 4 sqrt(r) + 8), to 24 bits by a two-digit radix
+// on chip.  One pass over the scores then collects the keys above the upper
+// bound (all taken) and the keys between the bounds, with exact counts, and
+// one workgroup per row finds the k-th key among the latter by a radix select
+// on chip and writes the taken positions in ascending order.  The
+// counts show whether the bracket holds the k-th key; a row where it does not
+// (an unrepresentative sample, heavy ties, k above the lists' size) is done
+// by one workgroup running the plain radix select over that row alone.  Every
+// row's result is the exact selection either way; the sample only decides
+// which of the two exact routes a row takes.
 //
 // Block mode (block_size > 1) is the previous generation's 64-token block
 // selection (zgeo.com.cn comparison table): block mass = fp64 sum of its
 // scores over C in ascending position, heaviest blocks first, ties to the
 // lower block.
-#include <atomic>
+#include <type_traits>
 
 #include "hs2_internal.hpp"
 #include "select_common.hpp"
@@ -214,6 +219,36 @@ __device__ __forceinline__ void load_keys_inline(const float* s, int base, int e
   }
 }
 
+// The chunk's keys in runs of 16 consecutive positions: key 16*r + e at
+// position base + 4096*r + 16*threadIdx.x + e (r < 4), so the thread order is
+// the position order within each quarter of the chunk.
+__device__ __forceinline__ void load_keys_runs(const float* s, int base, int end, bool vec_ok, ChunkKeys& K) {
+  K.valid = 0;
+#pragma unroll
+  for (int rnd = 0; rnd < 4; ++rnd) {
+    const int j0 = base + rnd * 4096 + threadIdx.x * 16;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int j = j0 + 4 * q, i = rnd * 16 + 4 * q;
+      if (vec_ok && j + 3 < end) {
+        const float4 v = *(const float4*)(s + j);
+        K.key[i] = score_key(v.x);
+        K.key[i + 1] = score_key(v.y);
+        K.key[i + 2] = score_key(v.z);
+        K.key[i + 3] = score_key(v.w);
+        K.valid |= (uint64_t)0xF << i;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bool ok = j + e < end;
+          K.key[i + e] = ok ? score_key(s[j + e]) : 0u;
+          K.valid |= (uint64_t)ok << (i + e);
+        }
+      }
+    }
+  }
+}
+
 // LDS histogram of one digit over the keys that match `prefix` (pass 0: all
 // keys, by the windowed register counts of hist_digit0).
 template <int PASS>
@@ -248,7 +283,6 @@ __global__ void __launch_bounds__(256) sel_hist(SelectParams P) {
   const int ncand = sel_ncand(row_pos(P, u), P.cand_window);
   const int take = sel_take(ncand, P.k, 1);
   if (sel_mode(take, ncand, 1) != MODE_RADIX) return;
-  if (PASS == 2 && P.collected && st[ST_COMPACT]) return;  // finished by the collected path
   const int base = chunk * kSelChunk;
   if (base >= ncand) return;
   const int end = min(base + kSelChunk, ncand);
@@ -310,70 +344,257 @@ __device__ __forceinline__ void write_window(const SelectParams& P, int u, int t
   if (threadIdx.x == 0) P.count[u] = take + nw;
 }
 
-// Collected path, first step (after the second histogram pass): settle the
-// second digit, decide whether the row is collected (k <= kCompactTake and at
-// most kCompactBin keys share the 24-bit prefix -- both known exactly from the
-// histograms), and if so append this chunk's keys above the prefix (positions)
-// and in its bin (key, position) to the row's lists.  Offsets come from one
-// atomic per list and workgroup, so list order varies between runs; the
-// finishing kernel sorts, which makes the result deterministic.
-__global__ void __launch_bounds__(256) sel_collect(SelectParams P) {
+// Bracketed path, first step: one workgroup per row sets the row's state up
+// and brackets its k-th key from a sample.  Runs i * SR of 64 positions
+// (i < nsr <= kBracketRuns) of the candidates are read, 32 keys per thread
+// per half of the sample, once per digit; the sample's keys of ranks r_hi = r - m and r_lo =
+// r + m (0 = largest) are found to 24 bits -- the first digit for both from
+// one histogram, the second from one histogram each -- and stored as the
+// prefixes P_hi >= P_lo.  Rows of up to kBracketRuns runs are sampled whole
+// (SR = 1), and then both ranks are the k-th key itself.  A rank below 0
+// leaves nothing above the bracket (P_hi = 2^24 - 1); one past the sample
+// leaves nothing below it (P_lo = 0).
+struct BracketRow {
+  const float* row;
+  int ncand, SR, nsr;
+  bool vec_ok;
+};
+constexpr int kBracketKeys = kKeysPerThread / 2;  // keys per thread per half of the sample
+
+// half h: float4 slot q = tid + 256 * m (m in [8h, 8h + 8)) is the (q & 15)-th
+// of sampled run q >> 4, so a wave reads four whole runs
+__device__ __forceinline__ void bracket_load(const BracketRow& R, int h, uint32_t (&key)[kBracketKeys],
+                                             uint64_t& valid) {
+  valid = 0;
+#pragma unroll
+  for (int mm = 0; mm < kBracketKeys / 4; ++mm) {
+    const int q = threadIdx.x + 256 * (h * (kBracketKeys / 4) + mm), run = q >> 4;
+    const int j = run * R.SR * 64 + (q & 15) * 4;
+    float4 v = {0.f, 0.f, 0.f, 0.f};
+    int nv = 0;
+    if (run < R.nsr) {
+      nv = min(max(R.ncand - j, 0), 4);
+      if (R.vec_ok && nv == 4) {
+        v = *(const float4*)(R.row + j);
+      } else {
+        v.x = nv > 0 ? R.row[j] : 0.f;
+        v.y = nv > 1 ? R.row[j + 1] : 0.f;
+        v.z = nv > 2 ? R.row[j + 2] : 0.f;
+        v.w = nv > 3 ? R.row[j + 3] : 0.f;
+      }
+    }
+    key[4 * mm] = score_key(v.x);
+    key[4 * mm + 1] = score_key(v.y);
+    key[4 * mm + 2] = score_key(v.z);
+    key[4 * mm + 3] = score_key(v.w);
+    valid |= (uint64_t)((1u << nv) - 1) << (4 * mm);
+  }
+}
+
+// The two ranks' 24-bit prefixes from a sample of HALVES halves, read once
+// per digit (64 KiB per row at most, from the caches the second time: keeping
+// the keys in registers instead would take three times the registers).  h0
+// and h1 are cleared on entry.
+template <int HALVES>
+__device__ __forceinline__ void bracket_prefixes(const BracketRow& R, int r_hi, int r_lo, int nsamp, int32_t* h0,
+                                                 int32_t* h1, int32_t* sm, uint32_t& p_hi, uint32_t& p_lo) {
+  uint32_t key[kBracketKeys];
+  uint64_t valid;
+#pragma unroll 1
+  for (int h = 0; h < HALVES; ++h) {
+    bracket_load(R, h, key, valid);
+    hist_digit0<kBracketKeys>(key, valid, h0);
+  }
+  __syncthreads();
+  // first digits of the two ranks (uniform conditions around the block-wide searches)
+  const bool want_hi = r_hi >= 0, want_lo = r_lo < nsamp;
+  int d_hi = 0, a_hi = 0, d_lo = 0, a_lo = 0;
+  if (want_hi) find_digit<0>(h0, r_hi + 1, sm, d_hi, a_hi);
+  if (want_lo) find_digit<0>(h0, r_lo + 1, sm, d_lo, a_lo);
+  // second digits: h1 for the upper rank, h0 (cleared) for the lower one
+  for (int i = threadIdx.x; i < kHistBins; i += 256) h0[i] = 0;
+  __syncthreads();
+#pragma unroll 1
+  for (int h = 0; h < HALVES; ++h) {
+    bracket_load(R, h, key, valid);
+#pragma unroll
+    for (int i = 0; i < kBracketKeys; ++i) {
+      if (!(valid >> i & 1)) continue;
+      const uint32_t d = key[i] >> 20, d2 = (key[i] >> 8) & 0xFFFu;
+      if (want_hi && d == (uint32_t)d_hi) atomicAdd(&h1[d2], 1);
+      if (want_lo && d == (uint32_t)d_lo) atomicAdd(&h0[d2], 1);
+    }
+  }
+  __syncthreads();
+  p_hi = 0xFFFFFFu;
+  p_lo = 0u;
+  if (want_hi) {
+    int d2, a2;
+    find_digit<1>(h1, r_hi + 1 - a_hi, sm, d2, a2);
+    p_hi = ((uint32_t)d_hi << 12) | (uint32_t)d2;
+  }
+  if (want_lo) {
+    int d2, a2;
+    find_digit<1>(h0, r_lo + 1 - a_lo, sm, d2, a2);
+    p_lo = ((uint32_t)d_lo << 12) | (uint32_t)d2;
+  }
+}
+
+__global__ void __launch_bounds__(256) sel_bracket(SelectParams P) {
+  __shared__ int32_t h0[kHistBins], h1[kHistBins];
   __shared__ int32_t sm[264];
-  __shared__ int32_t s_base[2];
-  const int u = blockIdx.y, chunk = blockIdx.x;
+  const int u = blockIdx.x, tid = threadIdx.x;
   int32_t* st = P.state + (int64_t)u * ST_WORDS;
-  if (st[ST_MODE] != MODE_RADIX) return;
-  const int ncand = st[ST_NCAND];
+  const int p = row_pos(P, u);
+  const int ncand = sel_ncand(p, P.cand_window), take = sel_take(ncand, P.k, 1);
+  const int mode = sel_mode(take, ncand, 1);
+  if (tid == 0) {
+    st[ST_MODE] = mode;
+    st[ST_NCAND] = ncand;
+    st[ST_TAKE] = take;
+    st[ST_P] = p;
+    st[ST_DONE] = 0;
+  }
+  if (mode != MODE_RADIX) return;  // (uniform) the per-row kernel writes these rows
+  // the collecting pass adds to its chunks' count words
+  const int nch = (ncand + kSelChunk - 1) / kSelChunk;
+  for (int i = tid; i < 2 * nch; i += 256) P.cnt[(int64_t)u * P.nchunks * 2 + i] = 0;
+  BracketRow R;
+  R.row = P.scores + (int64_t)u * P.N;
+  R.ncand = ncand;
+  R.vec_ok = (P.N & 3) == 0;
+  const int nruns = (ncand + 63) >> 6;
+  R.SR = nruns <= kBracketRuns ? 1 : max(kBracketStride, (nruns + kBracketRuns - 1) / kBracketRuns);
+  R.nsr = (nruns + R.SR - 1) / R.SR;
+  const int last = (R.nsr - 1) * R.SR * 64;  // first position of the last sampled run (< ncand)
+  const int nsamp = (R.nsr - 1) * 64 + min(64, ncand - last);
+  int r_hi, r_lo;
+  if (R.SR == 1) {
+    r_hi = r_lo = take - 1;
+  } else {
+    const float r = (float)take * (float)nsamp / (float)ncand;
+    const float m = 4.f * sqrtf(r) + 8.f;
+    r_hi = (int)floorf(r - m);
+    r_lo = min((int)ceilf(r + m), nsamp);
+  }
+  for (int i = tid; i < kHistBins; i += 256) {
+    h0[i] = 0;
+    h1[i] = 0;
+  }
+  __syncthreads();
+  uint32_t p_hi, p_lo;
+  if (R.nsr > kBracketRuns / 2)
+    bracket_prefixes<2>(R, r_hi, r_lo, nsamp, h0, h1, sm, p_hi, p_lo);
+  else
+    bracket_prefixes<1>(R, r_hi, r_lo, nsamp, h0, h1, sm, p_hi, p_lo);
+  if (tid == 0) {
+    st[ST_PHI] = (int32_t)p_hi;
+    st[ST_PLO] = (int32_t)p_lo;
+  }
+}
+
+// Bracketed path, second step (one workgroup per chunk of a row): the
+// positions of the chunk's keys whose 24-bit prefix lies above P_hi, and the
+// positions and keys of those between P_lo and P_hi, go to the chunk's own
+// lists, their numbers to the chunk's two count words (cleared by the bracket
+// kernel).  Every chunk owns list room for as many entries as the finishing
+// step accepts in all.  The bounds are compared as floats (for non-negative
+// scores and -0 the same order as the keys; the bound of an empty upper side
+// is a NaN, above which nothing lies).  No barrier waits on the scores: each
+// wave compacts its own hits (a prefix sum across the wave) at offsets taken
+// from LDS counters, and adds its counts to the chunk's words.
+__global__ void __launch_bounds__(256) sel_collect(SelectParams P) {
+  constexpr int NV = kKeysPerThread / 4;  // float4 loads per thread
+  __shared__ int32_t s_cnt[2];
+  const int u = blockIdx.y, chunk = blockIdx.x;
+  // the row's mode and candidates follow from its position, so the score
+  // loads go out before the bracket is read
+  const int ncand = sel_ncand(row_pos(P, u), P.cand_window);
+  const int take = sel_take(ncand, P.k, 1);
+  if (sel_mode(take, ncand, 1) != MODE_RADIX) return;
   const int base = chunk * kSelChunk;
   if (base >= ncand) return;
   const int end = min(base + kSelChunk, ncand);
-  ChunkKeys K;
-  load_keys_first(P.scores + (int64_t)u * P.N, base, end, (P.N & 3) == 0, K);
-  const int32_t* hist = P.hist + (int64_t)u * 3 * kHistBins;
-  int need = st[ST_NEED1];
-  int d, above, nbin;
-  find_digit<1>(hist + kHistBins, need, sm, d, above, &nbin);
-  const uint32_t prefix = (uint32_t)st[ST_PREFIX1] | ((uint32_t)d << Digit<1>::SHIFT);
-  need -= above;
-  const bool compact = st[ST_TAKE] <= kCompactTake && nbin <= kCompactBin && ncand <= kCompactMaxCand;
-  if (chunk == 0 && threadIdx.x == 0) {
-    st[ST_PREFIX2] = (int32_t)prefix;
-    st[ST_NEED2] = need;
-    st[ST_COMPACT] = compact;
-  }
-  if (!compact) return;
-  const uint32_t p24 = prefix >> 8;
-  uint64_t hit_a = 0, hit_b = 0;  // keys above the prefix / in its bin
-#pragma unroll
-  for (int i = 0; i < kKeysPerThread; ++i) {
-    const uint32_t hk = K.key[i] >> 8;
-    hit_a |= (uint64_t)(hk > p24) << i;
-    hit_b |= (uint64_t)(hk == p24) << i;
-  }
-  hit_a &= K.valid;
-  hit_b &= K.valid;
-  const int32_t na = __popcll(hit_a), nb = __popcll(hit_b);
-  // both counts in one scan: at most kSelChunk each, so the halves never carry
-  int32_t tot;
-  const int32_t off = block_exclusive_scan<int32_t>((na << 16) | nb, sm, tot);
   if (threadIdx.x == 0) {
-    s_base[0] = atomicAdd(&st[ST_NABOVE], tot >> 16);
-    s_base[1] = atomicAdd(&st[ST_NBIN], tot & 0xffff);
+    s_cnt[0] = 0;
+    s_cnt[1] = 0;
   }
   __syncthreads();
-  int32_t* cand = P.cand + (int64_t)u * kCandWords;
-  int oa = s_base[0] + (off >> 16), ob = s_base[1] + (off & 0xffff);
-  if (hit_a | hit_b) {
+  // element 4 i + e at position base + 4 (tid + 256 i) + e
+  const float* s = P.scores + (int64_t)u * P.N;
+  float4 v[NV];
+  uint64_t valid = ~0ull;
+  if ((P.N & 3) == 0 && end - base == kSelChunk) {  // whole chunk (uniform): 16-byte loads
 #pragma unroll
-    for (int i = 0; i < kKeysPerThread; ++i) {
-      const int pos = base + 4 * (threadIdx.x + 256 * (i >> 2)) + (i & 3);
-      if (hit_a >> i & 1) {
+    for (int i = 0; i < NV; ++i) v[i] = *(const float4*)(s + base + 4 * (threadIdx.x + 256 * i));
+  } else {
+    valid = 0;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int j = base + 4 * (threadIdx.x + 256 * i);
+      v[i].x = j < end ? s[j] : 0.f;
+      v[i].y = j + 1 < end ? s[j + 1] : 0.f;
+      v[i].z = j + 2 < end ? s[j + 2] : 0.f;
+      v[i].w = j + 3 < end ? s[j + 3] : 0.f;
+      const uint64_t nv = (uint64_t)min(max(end - j, 0), 4);
+      valid |= ((1ull << nv) - 1) << (4 * i);
+    }
+  }
+  const int32_t* st = P.state + (int64_t)u * ST_WORDS;
+  const float hi = __uint_as_float(((uint32_t)st[ST_PHI] << 8) | 0xFFu);
+  const float lo = __uint_as_float((uint32_t)st[ST_PLO] << 8);
+  uint32_t a_lo = 0, a_hi = 0, b_lo = 0, b_hi = 0;  // hit masks, elements 0-31 and 32-63
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const float x[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int bit = (4 * i + e) & 31;
+      const bool above = x[e] > hi, in = !above && x[e] >= lo;
+      if (4 * i + e < 32) {
+        a_lo |= above ? 1u << bit : 0u;
+        b_lo |= in ? 1u << bit : 0u;
+      } else {
+        a_hi |= above ? 1u << bit : 0u;
+        b_hi |= in ? 1u << bit : 0u;
+      }
+    }
+  }
+  uint64_t hit_a = ((uint64_t)a_hi << 32 | a_lo) & valid, hit_b = ((uint64_t)b_hi << 32 | b_lo) & valid;
+  // both counts in one wave scan: at most kSelChunk each, so the halves never carry
+  const int32_t mine = (__popcll(hit_a) << 16) | __popcll(hit_b);
+  const int32_t incl = wave_inclusive_scan(mine);
+  const int32_t wtot = __shfl(incl, 63);
+  if (wtot == 0) return;  // (wave-uniform) no hits in this wave
+  int32_t wbase = 0;
+  const int lane = threadIdx.x & 63;
+  if (lane == 63) {
+    const int32_t ba = (wtot >> 16) ? atomicAdd(&s_cnt[0], wtot >> 16) : 0;
+    const int32_t bb = (wtot & 0xffff) ? atomicAdd(&s_cnt[1], wtot & 0xffff) : 0;
+    wbase = (ba << 16) | bb;
+  }
+  wbase = __shfl(wbase, 63);
+  const int64_t cb = (int64_t)u * P.nchunks + chunk;
+  if (lane == 0) {
+    if (wtot >> 16) atomicAdd(&P.cnt[2 * cb], wtot >> 16);
+    if (wtot & 0xffff) atomicAdd(&P.cnt[2 * cb + 1], wtot & 0xffff);
+  }
+  const int32_t off = wbase + incl - mine;
+  int32_t* cand = P.cand + cb * kCandWords;
+  int oa = off >> 16, ob = off & 0xffff;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const float x[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int pos = base + 4 * (threadIdx.x + 256 * i) + e;
+      if (hit_a >> (4 * i + e) & 1) {
         if (oa < kCompactTake) cand[oa] = pos;
         ++oa;
-      } else if (hit_b >> i & 1) {
+      } else if (hit_b >> (4 * i + e) & 1) {
         if (ob < kCompactBin) {
-          cand[kCompactTake + ob] = (int32_t)K.key[i];
-          cand[kCompactTake + kCompactBin + ob] = pos;
+          cand[kCompactTake + ob] = pos;
+          cand[kCompactTake + kCompactBin + ob] = (int32_t)score_key(x[e]);
         }
         ++ob;
       }
@@ -407,92 +628,270 @@ __device__ __forceinline__ int pow2_at_least(int n) {
   return m;
 }
 
-// Collected path, second step: one workgroup per collected row.  The bin's
-// keys sorted by (score desc, position asc) give the need2 highest keys with
-// ties to the lower position.  Those and the keys above the prefix are the
-// row's `take` positions: marked in an LDS bitmap over the candidates, they
-// come out in ascending order from a prefix count of the bitmap, followed by
-// the window.  Each thread counts a run of 16-byte bitmap groups; group q sits
-// at q + q/32, so the runs of 16 consecutive threads start on distinct banks.
+// Output order of the finishing kernel: a bitmap over the row's candidates
+// in LDS (16-byte groups of 128 positions; group q at slot q + q/32, so the
+// runs of 16 consecutive threads start on distinct banks) for rows of up to
+// kBitmapMaxCand candidates, a sort of the taken positions beyond.
 __host__ __device__ __forceinline__ int bm_slot4(int q) { return q + (q >> 5); }
-
-// dynamic LDS of the finishing kernel for rows of up to min(N, kCompactMaxCand) candidates
+constexpr int kBitmapMaxCand = 1 << 18;
 inline size_t finish_lds_bytes(int N) {
-  const int nq = (min(N, kCompactMaxCand) + 127) >> 7;
+  const int nq = (min(N, kBitmapMaxCand) + 127) >> 7;
   return ((size_t)bm_slot4(nq - 1) + 1) * 16;
 }
 
+// Bracketed path, third step: one workgroup per row.  The chunks' list
+// lengths give the row's na keys above the bracket and nb inside it; the
+// bracket holds the k-th key when na < take <= na + nb, and with both within
+// the lists' sizes the row is settled here, else left to the per-row kernel.  The bin's keys (16 per thread in registers) give the need = take -
+// na highest by a radix select on chip (digits of 12, 12 and 8 bits): every
+// key above the threshold tau and, of the keys equal to tau, the lowest
+// positions (found by sorting the tied positions, when not all of them are
+// taken).  Those and the na positions above the bracket are the row's
+// selection, written in ascending order from a prefix count of their bitmap
+// (or a sort of them), then the window.
 __global__ void __launch_bounds__(256) sel_finish(SelectParams P) {
+  constexpr int BPT = kCompactBin / 256, APT = kCompactTake / 256;
   extern __shared__ __align__(16) u32x4_t bm4[];  // finish_lds_bytes(N)
-  __shared__ uint64_t s_bin[kCompactBin];
+  __shared__ int32_t h[kHistBins];               // digit histograms, then tied positions or the taken list
+  __shared__ int32_t s_pa[kFinishMaxChunks], s_pb[kFinishMaxChunks];  // list starts per chunk
   __shared__ int32_t sm[264];
-  const int u = blockIdx.x;
-  const int32_t* st = P.state + (int64_t)u * ST_WORDS;
-  if (st[ST_MODE] != MODE_RADIX || !st[ST_COMPACT]) return;
-  const int take = st[ST_TAKE], p = st[ST_P], ncand = st[ST_NCAND];
-  // the histograms make these exact (na + need = take, need <= nb); the clamps
-  // only keep LDS accesses inside their arrays
-  const int na = min(st[ST_NABOVE], kCompactTake);
-  const int nb = min(st[ST_NBIN], kCompactBin);
-  const int need = min(max(st[ST_NEED2], 0), nb);
-  const int32_t* cand = P.cand + (int64_t)u * kCandWords;
-  // every list load issued at once: positions above the prefix, then the bin
-  constexpr int kAbovePerThread = kCompactTake / 256;
-  int32_t apos[kAbovePerThread];
-#pragma unroll
-  for (int r = 0; r < kAbovePerThread; ++r) {
-    const int i = threadIdx.x + 256 * r;
-    apos[r] = i < na ? cand[i] : -1;
+  __shared__ int32_t s_n;
+  int32_t* st = P.state + (int64_t)blockIdx.x * ST_WORDS;
+  if (st[ST_MODE] != MODE_RADIX) return;
+  const int u = blockIdx.x, take = st[ST_TAKE], p = st[ST_P], ncand = st[ST_NCAND];
+  const int tid = threadIdx.x;
+  // the chunks' list lengths, their exclusive prefix sums and the totals
+  const int nch = (ncand + kSelChunk - 1) / kSelChunk;
+  if (nch > kFinishMaxChunks) return;  // (uniform) left to the per-row kernel
+  const int32_t* cnt = P.cnt + (int64_t)u * P.nchunks * 2;
+  int na = 0, nb = 0;
+  for (int c0 = 0; c0 < nch; c0 += 256) {
+    const int c = c0 + tid;
+    int32_t v[2] = {c < nch ? cnt[2 * c] : 0, c < nch ? cnt[2 * c + 1] : 0}, t[2];
+    block_exclusive_scan_n<2>(v, sm, t);
+    if (c < nch) {
+      s_pa[c] = na + v[0];
+      s_pb[c] = nb + v[1];
+    }
+    na += t[0];
+    nb += t[1];
   }
-  const int nbp = pow2_at_least(nb);
-  for (int i = threadIdx.x; i < nbp; i += 256)
-    s_bin[i] = i < nb ? ((uint64_t)(~(uint32_t)cand[kCompactTake + i]) << 32) |
-                            (uint32_t)cand[kCompactTake + kCompactBin + i]
-                      : ~0ull;
-  const int nq = (ncand + 127) >> 7;  // 128-position groups
-  const int nslots = bm_slot4(nq - 1) + 1;
-  for (int i = threadIdx.x; i < nslots; i += 256) bm4[i] = u32x4_t{0u, 0u, 0u, 0u};
+  if (!(na < take && take <= na + nb && take <= kCompactTake && nb <= kCompactBin)) return;
   __syncthreads();
-  lds_bitonic_sort(s_bin, nbp);
-  uint32_t* bm = (uint32_t*)bm4;
-  auto mark = [&](int pos) {
-    if (pos >= 0 && pos < ncand) atomicOr(&bm[4 * bm_slot4(pos >> 7) + ((pos >> 5) & 3)], 1u << (pos & 31));
+  // entry i of a list lies in the last chunk whose start is <= i
+  auto chunk_of = [&](const int32_t* starts, int i) {
+    int lo = 0, hi = nch - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (starts[mid] <= i) lo = mid;
+      else hi = mid - 1;
+    }
+    return lo;
   };
+  const int32_t* cand = P.cand + (int64_t)u * P.nchunks * kCandWords;
+  uint32_t bk[BPT];
+  int32_t bp[BPT], ap[APT];
+  uint64_t bvalid = 0;
 #pragma unroll
-  for (int r = 0; r < kAbovePerThread; ++r) mark(apos[r]);
-  for (int i = threadIdx.x; i < need; i += 256) mark((int)(uint32_t)s_bin[i]);
-  __syncthreads();
-  // at most 32 groups per thread (kCompactMaxCand / 128 / 256); the mask of
-  // the non-empty ones lets the output loop visit only those
-  const int per = (nq + 255) >> 8;
-  const int q0 = min((int)threadIdx.x * per, nq), q1 = min(q0 + per, nq);
-  int32_t cnt = 0;
-  uint32_t nz = 0;
-#pragma unroll 4
-  for (int q = q0; q < q1; ++q) {
-    const u32x4_t v = bm4[bm_slot4(q)];
-    const int c = __popc(v.x) + __popc(v.y) + __popc(v.z) + __popc(v.w);
-    cnt += c;
-    nz |= (uint32_t)(c != 0) << (q - q0);
+  for (int j = 0; j < BPT; ++j) {
+    const int i = tid + 256 * j;
+    const bool ok = i < nb;
+    bp[j] = -1;
+    bk[j] = 0u;
+    if (ok) {
+      const int c = chunk_of(s_pb, i);
+      const int32_t* cc = cand + (int64_t)c * kCandWords + kCompactTake + (i - s_pb[c]);
+      bp[j] = cc[0];
+      bk[j] = (uint32_t)cc[kCompactBin];
+    }
+    bvalid |= (uint64_t)ok << j;
   }
-  int32_t tot;
-  int32_t o = block_exclusive_scan<int32_t>(cnt, sm, tot);
-  int32_t* out = P.idx + (int64_t)u * P.max_sel;
-  while (nz) {
-    const int q = q0 + __builtin_ctz(nz);
-    nz &= nz - 1;
-    const u32x4_t v = bm4[bm_slot4(q)];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      uint32_t bits = v[c];
-      while (bits) {
-        if (o < take) out[o] = (q << 7) + (c << 5) + __builtin_ctz(bits);
-        ++o;
-        bits &= bits - 1;
-      }
+  for (int r = 0; r < APT; ++r) {
+    const int i = tid + 256 * r;
+    ap[r] = -1;
+    if (i < na) {
+      const int c = chunk_of(s_pa, i);
+      ap[r] = cand[(int64_t)c * kCandWords + i - s_pa[c]];
     }
   }
+  // radix select of the need-th largest bin key
+  int need = take - na, d, above, n_eq = 0;
+  for (int i = tid; i < kHistBins; i += 256) h[i] = 0;
+  __syncthreads();
+  hist_digit0<BPT>(bk, bvalid, h);
+  __syncthreads();
+  find_digit<0>(h, need, sm, d, above);
+  uint32_t tau = (uint32_t)d << 20;
+  need -= above;
+  for (int i = tid; i < kHistBins; i += 256) h[i] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < BPT; ++j)
+    if ((bvalid >> j & 1) && (bk[j] & 0xFFF00000u) == tau) atomicAdd(&h[(bk[j] >> 8) & 0xFFFu], 1);
+  __syncthreads();
+  find_digit<1>(h, need, sm, d, above);
+  tau |= (uint32_t)d << 8;
+  need -= above;
+  for (int i = tid; i < 256; i += 256) h[i] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < BPT; ++j)
+    if ((bvalid >> j & 1) && (bk[j] & 0xFFFFFF00u) == tau) atomicAdd(&h[bk[j] & 0xFFu], 1);
+  __syncthreads();
+  find_digit<2>(h, need, sm, d, above, &n_eq);
+  tau |= (uint32_t)d;
+  need -= above;  // keys equal to tau that are taken: 1 <= need <= n_eq
+  // ties: the need lowest positions among the n_eq keys equal to tau
+  int32_t cut = INT32_MAX;
+  if (need < n_eq) {  // uniform
+    if (tid == 0) s_n = 0;
+    const int np = pow2_at_least(n_eq);
+    for (int i = n_eq + tid; i < np; i += 256) h[i] = INT32_MAX;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < BPT; ++j)
+      if ((bvalid >> j & 1) && bk[j] == tau) h[atomicAdd(&s_n, 1)] = bp[j];
+    __syncthreads();
+    lds_bitonic_sort(h, np);
+    cut = h[need - 1];
+    __syncthreads();
+  }
+  uint32_t bsel = 0;  // bin entries taken
+#pragma unroll
+  for (int j = 0; j < BPT; ++j)
+    bsel |= (uint32_t)((bvalid >> j & 1) && (bk[j] > tau || (bk[j] == tau && bp[j] <= cut))) << j;
+  int32_t* out = P.idx + (int64_t)u * P.max_sel;
+  if (ncand <= kBitmapMaxCand) {  // uniform
+    const int nq = (ncand + 127) >> 7;  // 128-position groups
+    const int nslots = bm_slot4(nq - 1) + 1;
+    for (int i = tid; i < nslots; i += 256) bm4[i] = u32x4_t{0u, 0u, 0u, 0u};
+    __syncthreads();
+    uint32_t* bm = (uint32_t*)bm4;
+    // (positions come from the collecting pass, always in [0, ncand); the test
+    // keeps every LDS access inside the bitmap whatever the lists hold)
+    auto mark = [&](int pos) {
+      if ((unsigned)pos < (unsigned)ncand) atomicOr(&bm[4 * bm_slot4(pos >> 7) + ((pos >> 5) & 3)], 1u << (pos & 31));
+    };
+#pragma unroll
+    for (int r = 0; r < APT; ++r)
+      if (ap[r] >= 0) mark(ap[r]);
+#pragma unroll
+    for (int j = 0; j < BPT; ++j)
+      if (bsel >> j & 1) mark(bp[j]);
+    __syncthreads();
+    // at most 8 groups per thread (kBitmapMaxCand / 128 / 256); the mask of
+    // the non-empty ones lets the output loop visit only those
+    const int per = (nq + 255) >> 8;
+    const int q0 = min(tid * per, nq), q1 = min(q0 + per, nq);
+    int32_t cnt = 0;
+    uint32_t nz = 0;
+    for (int q = q0; q < q1; ++q) {
+      const u32x4_t v = bm4[bm_slot4(q)];
+      const int c = __popc(v.x) + __popc(v.y) + __popc(v.z) + __popc(v.w);
+      cnt += c;
+      nz |= (uint32_t)(c != 0) << (q - q0);
+    }
+    int32_t tot;
+    int32_t o = block_exclusive_scan<int32_t>(cnt, sm, tot);
+    while (nz) {
+      const int q = q0 + __builtin_ctz(nz);
+      nz &= nz - 1;
+      const u32x4_t v = bm4[bm_slot4(q)];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        uint32_t bits = v[c];
+        while (bits) {
+          if (o < take) out[o] = (q << 7) + (c << 5) + __builtin_ctz(bits);
+          ++o;
+          bits &= bits - 1;
+        }
+      }
+    }
+  } else {  // long rows: the taken positions sorted
+    if (tid == 0) s_n = 0;
+    const int ntp = pow2_at_least(take);
+    for (int i = take + tid; i < ntp; i += 256) h[i] = INT32_MAX;
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < APT; ++r)
+      if (ap[r] >= 0) h[atomicAdd(&s_n, 1)] = ap[r];
+#pragma unroll
+    for (int j = 0; j < BPT; ++j)
+      if (bsel >> j & 1) h[atomicAdd(&s_n, 1)] = bp[j];
+    __syncthreads();
+    lds_bitonic_sort(h, ntp);
+    for (int i = tid; i < take; i += 256) out[i] = h[i];
+  }
   write_window(P, u, take, p, out);
+  if (tid == 0) st[ST_DONE] = 1;
+}
+
+// Ordered compaction of one chunk's keys (load_keys_runs layout): every key
+// above tau, and of the keys equal to tau those whose rank among the row's
+// equal keys (eq_before of them in earlier chunks) is below need, into the
+// slots from sel_before on (keys taken in earlier chunks), never past take.
+// The four quarters' counts go through two packed scans (16 bits per quarter;
+// a quarter holds at most 4096 keys): first the keys equal to tau, whose rank
+// decides which of them are taken, then the taken keys, whose prefix is the
+// output slot.  eq_tot / sel_tot: this chunk's equal and taken keys.
+__device__ __forceinline__ void emit_chunk(const ChunkKeys& K, int base, uint32_t tau, int need, int32_t eq_before,
+                                           int32_t sel_before, int take, int32_t* out, int32_t* sm, int32_t& eq_tot,
+                                           int32_t& sel_tot) {
+  int32_t eqc[4];
+#pragma unroll
+  for (int rnd = 0; rnd < 4; ++rnd) {
+    int32_t c = 0;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) c += (K.valid >> (rnd * 16 + e) & 1) && K.key[rnd * 16 + e] == tau;
+    eqc[rnd] = c;
+  }
+  int32_t pe[2] = {eqc[0] | (eqc[1] << 16), eqc[2] | (eqc[3] << 16)}, te[2];
+  block_exclusive_scan_n<2>(pe, sm, te);
+  uint32_t selmask[4];
+  int32_t selc[4];
+  int32_t rbase = eq_before;
+#pragma unroll
+  for (int rnd = 0; rnd < 4; ++rnd) {
+    const int f = (rnd & 1) * 16, w = rnd >> 1;
+    int32_t r_eq = rbase + ((pe[w] >> f) & 0xffff);
+    rbase += (te[w] >> f) & 0xffff;
+    uint32_t m = 0;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const uint32_t key = K.key[rnd * 16 + e];
+      bool take_it = false;
+      if (K.valid >> (rnd * 16 + e) & 1) {
+        if (key > tau) {
+          take_it = true;
+        } else if (key == tau) {
+          take_it = r_eq < need;
+          ++r_eq;
+        }
+      }
+      m |= (uint32_t)take_it << e;
+    }
+    selmask[rnd] = m;
+    selc[rnd] = __builtin_popcount(m);
+  }
+  eq_tot = rbase - eq_before;
+  int32_t ps[2] = {selc[0] | (selc[1] << 16), selc[2] | (selc[3] << 16)}, ts[2];
+  block_exclusive_scan_n<2>(ps, sm, ts);
+  int32_t sbase = sel_before;
+#pragma unroll
+  for (int rnd = 0; rnd < 4; ++rnd) {
+    const int j0 = base + rnd * 4096 + threadIdx.x * 16;
+    const int f = (rnd & 1) * 16, w = rnd >> 1;
+    int32_t sl = sbase + ((ps[w] >> f) & 0xffff);
+    sbase += (ts[w] >> f) & 0xffff;
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+      if (selmask[rnd] >> e & 1u) {
+        if ((uint32_t)sl < (uint32_t)take) out[sl] = j0 + e;  // never past this unit's budget
+        ++sl;
+      }
+  }
+  sel_tot = sbase - sel_before;
 }
 
 // Ascending compaction: every key above tau and the lowest-positioned keys
@@ -508,7 +907,6 @@ __global__ void __launch_bounds__(256) sel_emit(SelectParams P) {
   const int mode = sel_mode(take, ncand, 1);
   int32_t* out = P.idx + (int64_t)u * P.max_sel;
 
-  if (mode == MODE_RADIX && P.collected && st[ST_COMPACT]) return;  // written by the collected path
   if (chunk == 0) write_window(P, u, take, p, out);
   if (mode == MODE_NONE) return;
   const int base = chunk * kSelChunk;
@@ -518,28 +916,8 @@ __global__ void __launch_bounds__(256) sel_emit(SelectParams P) {
     for (int j = base + threadIdx.x; j < end; j += 256) out[j] = j;
     return;
   }
-  // this chunk's keys, 16 consecutive positions per thread per round of 4096
-  const float* s = P.scores + (int64_t)u * P.N;
-  const bool vec_ok = (P.N & 3) == 0;
-  uint32_t keys[kKeysPerThread];
-#pragma unroll
-  for (int rnd = 0; rnd < 4; ++rnd) {
-    const int j0 = base + rnd * 4096 + threadIdx.x * 16;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int j = j0 + 4 * q;
-      if (vec_ok && j + 3 < end) {
-        const float4 v = *(const float4*)(s + j);
-        keys[rnd * 16 + 4 * q] = score_key(v.x);
-        keys[rnd * 16 + 4 * q + 1] = score_key(v.y);
-        keys[rnd * 16 + 4 * q + 2] = score_key(v.z);
-        keys[rnd * 16 + 4 * q + 3] = score_key(v.w);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) keys[rnd * 16 + 4 * q + e] = (j + e < end) ? score_key(s[j + e]) : 0u;
-      }
-    }
-  }
+  ChunkKeys K;
+  load_keys_runs(P.scores + (int64_t)u * P.N, base, end, (P.N & 3) == 0, K);
   // final digit, threshold tau and how many keys equal to it are taken
   int d, above;
   find_digit<2>(P.hist + ((int64_t)u * 3 + 2) * kHistBins, st[ST_NEED2], sm, d, above);
@@ -564,64 +942,64 @@ __global__ void __launch_bounds__(256) sel_emit(SelectParams P) {
     eq_before += eq_tot;
     sel_before += sel_tot;
   }
-  // The four rounds' counts go through two packed scans (16 bits per round;
-  // a round holds at most 4096 keys): first the keys equal to tau, whose rank
-  // decides which of them are taken, then the taken keys, whose prefix is the
-  // output slot.  Positions are ordered by (round, thread, element).
-  int32_t eqc[4];
-#pragma unroll
-  for (int rnd = 0; rnd < 4; ++rnd) {
-    const int j0 = base + rnd * 4096 + threadIdx.x * 16;
-    int32_t c = 0;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) c += (j0 + e < end) && keys[rnd * 16 + e] == tau;
-    eqc[rnd] = c;
-  }
-  int32_t pe[2] = {eqc[0] | (eqc[1] << 16), eqc[2] | (eqc[3] << 16)}, te[2];
-  block_exclusive_scan_n<2>(pe, sm, te);
-  uint32_t selmask[4];
-  int32_t selc[4];
-  int32_t rbase = eq_before;
-#pragma unroll
-  for (int rnd = 0; rnd < 4; ++rnd) {
-    const int j0 = base + rnd * 4096 + threadIdx.x * 16;
-    const int f = (rnd & 1) * 16, w = rnd >> 1;
-    int32_t r_eq = rbase + ((pe[w] >> f) & 0xffff);
-    rbase += (te[w] >> f) & 0xffff;
-    uint32_t m = 0;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const uint32_t key = keys[rnd * 16 + e];
-      bool take_it = false;
-      if (j0 + e < end) {
-        if (key > tau) {
-          take_it = true;
-        } else if (key == tau) {
-          take_it = r_eq < need;
-          ++r_eq;
-        }
+  int32_t eq_c, sel_c;
+  emit_chunk(K, base, tau, need, eq_before, sel_before, take, out, sm, eq_c, sel_c);
+}
+
+// A row the bracketed path did not settle -- and every row that takes all or
+// none of its candidates -- done by one workgroup: the three radix digits
+// over the row's candidates (each pass reads the row once; digits of 12, 12
+// and 8 bits as in the multi-workgroup passes), then the ordered compaction
+// chunk by chunk with running counts, then the window.
+__global__ void __launch_bounds__(256) sel_row_exact(SelectParams P) {
+  __shared__ int32_t h[kHistBins];
+  __shared__ int32_t sm[264];
+  const int u = blockIdx.x;
+  if (P.state[(int64_t)u * ST_WORDS + ST_DONE]) return;
+  const int p = row_pos(P, u);
+  const int ncand = sel_ncand(p, P.cand_window), take = sel_take(ncand, P.k, 1);
+  const int mode = sel_mode(take, ncand, 1);
+  int32_t* out = P.idx + (int64_t)u * P.max_sel;
+  if (mode == MODE_ALL) {
+    for (int j = threadIdx.x; j < ncand; j += 256) out[j] = j;
+  } else if (mode == MODE_RADIX) {
+    const float* row = P.scores + (int64_t)u * P.N;
+    const bool vec_ok = (P.N & 3) == 0;
+    int need = take;
+    uint32_t prefix = 0;
+    // one pass per digit: the LDS histogram of the keys sharing the digits so far
+    auto count = [&](auto pass_tag) {
+      constexpr int PASS = decltype(pass_tag)::value;
+      for (int i = threadIdx.x; i < kHistBins; i += 256) h[i] = 0;
+      __syncthreads();
+#pragma unroll 1
+      for (int base = 0; base < ncand; base += kSelChunk) {
+        ChunkKeys K;
+        load_keys_runs(row, base, min(base + kSelChunk, ncand), vec_ok, K);
+        hist_keys<PASS>(K, prefix, h);
       }
-      m |= (uint32_t)take_it << e;
+      __syncthreads();
+      int d, above;
+      find_digit<PASS>(h, need, sm, d, above);
+      prefix |= (uint32_t)d << Digit<PASS>::SHIFT;
+      need -= above;
+    };
+    count(std::integral_constant<int, 0>());
+    count(std::integral_constant<int, 1>());
+    count(std::integral_constant<int, 2>());
+    // prefix is now the k-th key tau; need of the keys equal to it are taken
+    int32_t eq_before = 0, sel_before = 0;
+#pragma unroll 1
+    for (int base = 0; base < ncand; base += kSelChunk) {
+      ChunkKeys K;
+      load_keys_runs(row, base, min(base + kSelChunk, ncand), vec_ok, K);
+      int32_t eq_c, sel_c;
+      emit_chunk(K, base, prefix, need, eq_before, sel_before, take, out, sm, eq_c, sel_c);
+      eq_before += eq_c;
+      sel_before += sel_c;
     }
-    selmask[rnd] = m;
-    selc[rnd] = __builtin_popcount(m);
   }
-  int32_t ps[2] = {selc[0] | (selc[1] << 16), selc[2] | (selc[3] << 16)}, ts[2];
-  block_exclusive_scan_n<2>(ps, sm, ts);
-  int32_t sbase = sel_before;
-#pragma unroll
-  for (int rnd = 0; rnd < 4; ++rnd) {
-    const int j0 = base + rnd * 4096 + threadIdx.x * 16;
-    const int f = (rnd & 1) * 16, w = rnd >> 1;
-    int32_t sl = sbase + ((ps[w] >> f) & 0xffff);
-    sbase += (ts[w] >> f) & 0xffff;
-#pragma unroll
-    for (int e = 0; e < 16; ++e)
-      if (selmask[rnd] >> e & 1u) {
-        if ((uint32_t)sl < (uint32_t)take) out[sl] = j0 + e;  // never past this unit's budget
-        ++sl;
-      }
-  }
+  write_window(P, u, take, p, out);
 }
 
 // The window competes (candidates [0, p]): the emit wrote the `take`
@@ -948,8 +1326,7 @@ __global__ void __launch_bounds__(256) sel_block_pick(SelectParams P) {
 }  // namespace
 
 hipError_t launch_select(const SelectParams& p_in, hipStream_t s) {
-  SelectParams p = p_in;
-  p.collected = p.block_size == 1 && p.units * p.nchunks >= kSelMinWorkgroups;
+  const SelectParams& p = p_in;
   const dim3 grid_c(p.nchunks, p.units);
   hipError_t e;
 #define HS2_L(name, kern, grid)                                   \
@@ -958,6 +1335,20 @@ hipError_t launch_select(const SelectParams& p_in, hipStream_t s) {
     hipLaunchKernelGGL(kern, grid, dim3(256), 0, s, p);           \
     if ((e = hipGetLastError()) != hipSuccess) return e;          \
   } while (0)
+  if (p.block_size == 1 && sel_bracketed(p.units, p.nchunks)) {
+    // many rows: bracket from a sample, one collecting pass, finish on chip,
+    // unsettled rows by the per-row kernel (the set-up is the bracket's)
+    HS2_L("select_bracket", sel_bracket, dim3(p.units));
+    HS2_L("select_collect", sel_collect, grid_c);
+    {
+      TimedLaunch tl_("select_finish", s);
+      hipLaunchKernelGGL(sel_finish, dim3(p.units), dim3(256), finish_lds_bytes(p.N), s, p);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    HS2_L("select_exact", sel_row_exact, dim3(p.units));
+    if (p.competes) HS2_L("select_window", sel_window_merge, dim3(p.units));
+    return hipSuccess;
+  }
   if (!(p.pre_hist0 && p.block_size == 1)) HS2_L("select_init", sel_init, dim3(p.units));
   if (p.block_size == 1) {
     const bool small = p.units * p.nchunks <= 512;  // up to about two workgroups per CU: latency-bound passes
@@ -967,26 +1358,6 @@ hipError_t launch_select(const SelectParams& p_in, hipStream_t s) {
     }
     if (small) HS2_L("select_hist", (sel_hist<1, true>), grid_c);
     else HS2_L("select_hist", (sel_hist<1, false>), grid_c);
-    // The collected path saves two full reads of the scores but adds two
-    // launches: taken where the passes are throughput-bound.
-    if (p.collected) {
-      HS2_L("select_collect", sel_collect, grid_c);
-      // the LDS attribute is set once per device, for the largest bitmap
-      static std::atomic<uint64_t> attr_done{0};
-      int dev = 0;
-      if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
-      const uint64_t bit = 1ull << (dev & 63);
-      if (!(attr_done.load() & bit)) {
-        if ((e = hipFuncSetAttribute((const void*)sel_finish, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     (int)finish_lds_bytes(kCompactMaxCand))) != hipSuccess)
-          return e;
-        attr_done.fetch_or(bit);
-      }
-      const size_t lds = finish_lds_bytes(p.N);
-      TimedLaunch tl_("select_finish", s);
-      hipLaunchKernelGGL(sel_finish, dim3(p.units), dim3(256), lds, s, p);
-      if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
     if (small) HS2_L("select_hist", (sel_hist<2, true>), grid_c);
     else HS2_L("select_hist", (sel_hist<2, false>), grid_c);
     HS2_L("select_emit", sel_emit, grid_c);
