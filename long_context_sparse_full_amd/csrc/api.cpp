@@ -91,16 +91,11 @@ struct FullPlan {
   size_t off_ml, off_o, off_lse2, off_lg16, off_lgmax, total;
 };
 
-// Position splits: about HS2_SCAN_TARGET_WGS workgroups in total (4 per CU on
-// 256 CUs; 8 for a bf16 cache, whose scan measured 2-3% faster with the finer
+// Position splits: about kScanTargetWgs workgroups in total (4 per CU on 256
+// CUs; 8 for a bf16 cache, whose scan measured 2-3% faster with the finer
 // splits while the FP8 scan measured slower), split lengths a multiple of 256
 // positions (64 on the fp32 path).
-#ifndef HS2_SCAN_TARGET_WGS
-#define HS2_SCAN_TARGET_WGS 1024
-#endif
-#ifndef HS2_SCAN_TARGET_WGS_BF16
-#define HS2_SCAN_TARGET_WGS_BF16 2048
-#endif
+constexpr int64_t kScanTargetWgs = 1024, kScanTargetWgsBf16 = 2048;
 FullPlan plan_full(const hs2_kv_desc* kv, int Tq, int Hq) {
   FullPlan p{};
   const int G = Hq / kv->Hkv;
@@ -111,12 +106,12 @@ FullPlan plan_full(const hs2_kv_desc* kv, int Tq, int Hq) {
   p.units = kv->B * p.n_tpacks * kv->Hkv;
   const bool g_pow2 = G == 4 || G == 8 || G == 16;  // the chunk score pass sums heads in 4-row lane groups
   p.chunk = !f32 && g_pow2 && p.n_tpacks >= hs2::kChunkMinPacks;
-  if (p.chunk) {  // work items (b, block of packs, g) x position splits, HS2_CHUNK_TARGET_WGS in all
+  if (p.chunk) {  // work items (b, block of packs, g) x position splits, kChunkTargetWgs in all
     const int64_t items = (int64_t)kv->B * cdiv(p.n_tpacks, hs2::kChunkPacks) * kv->Hkv;
-    const int64_t per_item = std::max<int64_t>(1, HS2_CHUNK_TARGET_WGS / items);
+    const int64_t per_item = std::max<int64_t>(1, hs2::kChunkTargetWgs / items);
     p.split_len = (int)rup(cdiv(kv->N, per_item), 128);  // whole 32-position tiles
   } else {
-    const int64_t target = kv->dtype == HS2_BF16 ? HS2_SCAN_TARGET_WGS_BF16 : HS2_SCAN_TARGET_WGS;
+    const int64_t target = kv->dtype == HS2_BF16 ? kScanTargetWgsBf16 : kScanTargetWgs;
     const int64_t per_unit = std::max<int64_t>(1, target / p.units);
     const int64_t quantum = f32 ? 64 : 256;
     p.split_len = (int)rup(cdiv(kv->N, per_unit), quantum);

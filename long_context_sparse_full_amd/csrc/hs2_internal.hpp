@@ -72,9 +72,7 @@ constexpr int kFlashRG = 2;
 constexpr int kChunkPacks = 4 * kFlashRG;
 constexpr int kChunkMinPacks = 4;
 // Chunk position splits: about this many full-pass work items in all.
-#ifndef HS2_CHUNK_TARGET_WGS
-#define HS2_CHUNK_TARGET_WGS 1024
-#endif
+constexpr int64_t kChunkTargetWgs = 1024;
 
 constexpr int kSelChunk = 16384;  // candidates per workgroup in the select passes
 constexpr int kHistBins = 4096;  // 12-bit digits
