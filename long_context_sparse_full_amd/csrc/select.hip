@@ -500,9 +500,12 @@ __global__ void __launch_bounds__(256) sel_bracket(SelectParams P) {
 // kernel).  Every chunk owns list room for as many entries as the finishing
 // step accepts in all.  The bounds are compared as floats (for non-negative
 // scores and -0 the same order as the keys; the bound of an empty upper side
-// is a NaN, above which nothing lies).  No barrier waits on the scores: each
-// wave compacts its own hits (a prefix sum across the wave) at offsets taken
-// from LDS counters, and adds its counts to the chunk's words.
+// is a NaN, above which nothing lies).  Hits are rare, so the compaction runs
+// per wave and per key slot: each compare gives the wave's ballot of hits for
+// that slot, empty ballots cost a scalar branch, and a hit lane's slot in the
+// list is the wave's running count plus its rank in the ballot.  A first pass
+// counts (the wave's list offsets then come from LDS counters, no barrier
+// waiting on the scores), a second pass writes.
 __global__ void __launch_bounds__(256) sel_collect(SelectParams P) {
   constexpr int NV = kKeysPerThread / 4;  // float4 loads per thread
   __shared__ int32_t s_cnt[2];
@@ -520,83 +523,81 @@ __global__ void __launch_bounds__(256) sel_collect(SelectParams P) {
     s_cnt[1] = 0;
   }
   __syncthreads();
-  // element 4 i + e at position base + 4 (tid + 256 i) + e
+  // element 4 i + e at position base + 4 (tid + 256 i) + e; positions past the
+  // chunk read as NaN, which no bound test accepts
   const float* s = P.scores + (int64_t)u * P.N;
   float4 v[NV];
-  uint64_t valid = ~0ull;
   if ((P.N & 3) == 0 && end - base == kSelChunk) {  // whole chunk (uniform): 16-byte loads
 #pragma unroll
     for (int i = 0; i < NV; ++i) v[i] = *(const float4*)(s + base + 4 * (threadIdx.x + 256 * i));
   } else {
-    valid = 0;
+    const float nan = __int_as_float(0x7fc00000);
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int j = base + 4 * (threadIdx.x + 256 * i);
-      v[i].x = j < end ? s[j] : 0.f;
-      v[i].y = j + 1 < end ? s[j + 1] : 0.f;
-      v[i].z = j + 2 < end ? s[j + 2] : 0.f;
-      v[i].w = j + 3 < end ? s[j + 3] : 0.f;
-      const uint64_t nv = (uint64_t)min(max(end - j, 0), 4);
-      valid |= ((1ull << nv) - 1) << (4 * i);
+      v[i].x = j < end ? s[j] : nan;
+      v[i].y = j + 1 < end ? s[j + 1] : nan;
+      v[i].z = j + 2 < end ? s[j + 2] : nan;
+      v[i].w = j + 3 < end ? s[j + 3] : nan;
     }
   }
-  const int32_t* st = P.state + (int64_t)u * ST_WORDS;
-  const float hi = __uint_as_float(((uint32_t)st[ST_PHI] << 8) | 0xFFu);
-  const float lo = __uint_as_float((uint32_t)st[ST_PLO] << 8);
-  uint32_t a_lo = 0, a_hi = 0, b_lo = 0, b_hi = 0;  // hit masks, elements 0-31 and 32-63
+  const int32_t* stw = P.state + (int64_t)u * ST_WORDS;
+  const float hi = __uint_as_float(((uint32_t)stw[ST_PHI] << 8) | 0xFFu);
+  const float lo = __uint_as_float((uint32_t)stw[ST_PLO] << 8);
+  // above: x > hi; inside: lo <= x and not above (NaN fails both, -0 >= +0 holds)
+  auto above = [&](float x) { return x > hi; };
+  auto inside = [&](float x) { return x >= lo && !(x > hi); };
+  int na = 0, nb = 0;  // wave-uniform
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const float x[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int bit = (4 * i + e) & 31;
-      const bool above = x[e] > hi, in = !above && x[e] >= lo;
-      if (4 * i + e < 32) {
-        a_lo |= above ? 1u << bit : 0u;
-        b_lo |= in ? 1u << bit : 0u;
-      } else {
-        a_hi |= above ? 1u << bit : 0u;
-        b_hi |= in ? 1u << bit : 0u;
-      }
+      na += __popcll(__ballot(above(x[e])));
+      nb += __popcll(__ballot(inside(x[e])));
     }
   }
-  uint64_t hit_a = ((uint64_t)a_hi << 32 | a_lo) & valid, hit_b = ((uint64_t)b_hi << 32 | b_lo) & valid;
-  // both counts in one wave scan: at most kSelChunk each, so the halves never carry
-  const int32_t mine = (__popcll(hit_a) << 16) | __popcll(hit_b);
-  const int32_t incl = wave_inclusive_scan(mine);
-  const int32_t wtot = __shfl(incl, 63);
-  if (wtot == 0) return;  // (wave-uniform) no hits in this wave
-  int32_t wbase = 0;
+  if ((na | nb) == 0) return;  // (wave-uniform) no hits in this wave
   const int lane = threadIdx.x & 63;
-  if (lane == 63) {
-    const int32_t ba = (wtot >> 16) ? atomicAdd(&s_cnt[0], wtot >> 16) : 0;
-    const int32_t bb = (wtot & 0xffff) ? atomicAdd(&s_cnt[1], wtot & 0xffff) : 0;
-    wbase = (ba << 16) | bb;
-  }
-  wbase = __shfl(wbase, 63);
-  const int64_t cb = (int64_t)u * P.nchunks + chunk;
+  int wa = 0, wb = 0;
   if (lane == 0) {
-    if (wtot >> 16) atomicAdd(&P.cnt[2 * cb], wtot >> 16);
-    if (wtot & 0xffff) atomicAdd(&P.cnt[2 * cb + 1], wtot & 0xffff);
+    const int64_t cb = (int64_t)u * P.nchunks + chunk;
+    if (na) {
+      wa = atomicAdd(&s_cnt[0], na);
+      atomicAdd(&P.cnt[2 * cb], na);
+    }
+    if (nb) {
+      wb = atomicAdd(&s_cnt[1], nb);
+      atomicAdd(&P.cnt[2 * cb + 1], nb);
+    }
   }
-  const int32_t off = wbase + incl - mine;
-  int32_t* cand = P.cand + cb * kCandWords;
-  int oa = off >> 16, ob = off & 0xffff;
+  int oa = __builtin_amdgcn_readfirstlane(wa), ob = __builtin_amdgcn_readfirstlane(wb);
+  int32_t* cand = P.cand + ((int64_t)u * P.nchunks + chunk) * kCandWords;
+  const uint64_t below = (1ull << lane) - 1;  // lanes ranked before this one
+  // the bounds pass through an empty asm statement, so the compares below are
+  // formed again rather than the first pass's 128 results kept in registers
+  float hi2 = hi, lo2 = lo;
+  asm volatile("" : "+v"(hi2), "+v"(lo2));
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const float x[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int pos = base + 4 * (threadIdx.x + 256 * i) + e;
-      if (hit_a >> (4 * i + e) & 1) {
-        if (oa < kCompactTake) cand[oa] = pos;
-        ++oa;
-      } else if (hit_b >> (4 * i + e) & 1) {
-        if (ob < kCompactBin) {
-          cand[kCompactTake + ob] = pos;
-          cand[kCompactTake + kCompactBin + ob] = (int32_t)score_key(x[e]);
+      const bool ha = x[e] > hi2, hb = x[e] >= lo2 && !(x[e] > hi2);
+      const uint64_t ba = __ballot(ha), bb = __ballot(hb);
+      if (ba) {  // uniform
+        const int o = oa + __popcll(ba & below);
+        if (ha && o < kCompactTake) cand[o] = pos;
+        oa += __popcll(ba);
+      }
+      if (bb) {  // uniform
+        const int o = ob + __popcll(bb & below);
+        if (hb && o < kCompactBin) {
+          cand[kCompactTake + o] = pos;
+          cand[kCompactTake + kCompactBin + o] = (int32_t)score_key(x[e]);
         }
-        ++ob;
+        ob += __popcll(bb);
       }
     }
   }
