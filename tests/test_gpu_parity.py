@@ -159,6 +159,10 @@ SEL_CASES = [
     (1, 1024, 2, 12001, 300, 0, 1, "tiny"),     # odd N, no window, every row's bin too large
     (1, 32, 8, 300001, 700, 64, 1, "levels"),   # 19 chunks per row, two per workgroup
     (1, 32, 8, 300001, 700, 64, 1, "mixed"),
+    # odd kv heads: every top score in runs of 64 positions the bracket's
+    # sample skips, so those rows' brackets miss and the per-row kernel
+    # selects them; even heads take the bracketed path in the same grid
+    (1, 512, 4, 65536, 1024, 128, 1, "unsampled"),
     # block baseline: staged block masses (power-of-two sizes), LDS pick
     (1, 64, 4, 131072, 16, 128, 64, "random"),  # the chunk workload's row shape
     (1, 3, 2, 10001, 40, 7, 4, "random"),       # 4-position blocks, odd N
@@ -185,6 +189,10 @@ def test_select_bit_exact_on_identical_scores(hs2, case):
     elif kind == "mixed":  # even rows: a few thousand levels; odd rows: six values
         sc = (rng.integers(0, 20000, (B, Tq, Hkv, N)) / 20000.0 * 1e-3).astype(np.float32)
         sc[:, :, 1::2] = (rng.integers(0, 6, sc[:, :, 1::2].shape) / 64.0).astype(np.float32)
+    elif kind == "unsampled":
+        sc = (rng.random((B, Tq, Hkv, N)) * 1e-3).astype(np.float32)
+        off_sample = (np.arange(N) // 64) % 16 != 0  # the sample reads every 16th run at this row length
+        sc[:, :, 1::2, off_sample] += np.float32(1e-3)
     elif kind == "blockties":
         sc = np.zeros((B, Tq, Hkv, N), np.float32)
         sc[..., ::64] = 0.5  # every block has the same mass
