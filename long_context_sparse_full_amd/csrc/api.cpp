@@ -153,10 +153,10 @@ SelPlan plan_select(int B, int Tq, int Hkv, int N, int block_size) {
     p.off_cnt = off;
     off = a256(off + (size_t)p.units * p.nchunks * 258 * sizeof(int32_t));
     p.off_cand = off;
-  } else if (block_size == 1) {  // bracketed: each chunk's list lengths and lists
+  } else if (block_size == 1) {  // bracketed: each chunk's per-wave list lengths and lists
     p.off_hist = off;
     p.off_cnt = off;
-    off = a256(off + (size_t)p.units * p.nchunks * 2 * sizeof(int32_t));
+    off = a256(off + (size_t)p.units * p.nchunks * 8 * sizeof(int32_t));
     p.off_cand = off;
     off = a256(off + (size_t)p.units * p.nchunks * hs2::kCandWords * sizeof(int32_t));
   } else {

@@ -90,8 +90,9 @@ constexpr int kCandWords = kCompactTake + 2 * kCompactBin;
 // kBracketRuns runs
 constexpr int kBracketRuns = 256;
 constexpr int kBracketStride = 16;
-// chunks per row the bracketed path's finishing step gathers from
-constexpr int kFinishMaxChunks = 1024;
+// chunks per row the bracketed path's finishing step gathers from (rows of
+// up to 4M candidates; longer rows take the per-row kernel)
+constexpr int kFinishMaxChunks = 256;
 __host__ __device__ inline bool sel_bracketed(int units, int nchunks) {
   return (int64_t)units * nchunks >= kSelMinWorkgroups;
 }
@@ -158,8 +159,8 @@ struct SelectParams {
   int32_t* state;   // [units][16]
   int32_t* hist;    // [units][3][4096] digit histograms of the three passes
   int32_t* cnt;     // [units][nchunks][258]: keys above the 24-bit prefix, suffix sums of the last digit;
-                    // bracketed path: [units][nchunks][2] list lengths
-  int32_t* cand;    // bracketed path: [units][nchunks][kCandWords] each chunk's lists
+                    // bracketed path: [units][nchunks][4 waves][2] list lengths
+  int32_t* cand;    // bracketed path: [units][nchunks][kCandWords] each chunk's lists, a quarter per wave
   double* bmass;    // [units][nblocks_max] (block mode)
   int nblocks_max;
   int pre_hist0;    // token mode: state and pass-0 histogram already built (merge + score pass)

@@ -456,9 +456,6 @@ __global__ void __launch_bounds__(256) sel_bracket(SelectParams P) {
     st[ST_DONE] = 0;
   }
   if (mode != MODE_RADIX) return;  // (uniform) the per-row kernel writes these rows
-  // the collecting pass adds to its chunks' count words
-  const int nch = (ncand + kSelChunk - 1) / kSelChunk;
-  for (int i = tid; i < 2 * nch; i += 256) P.cnt[(int64_t)u * P.nchunks * 2 + i] = 0;
   BracketRow R;
   R.row = P.scores + (int64_t)u * P.N;
   R.ncand = ncand;
@@ -495,20 +492,19 @@ __global__ void __launch_bounds__(256) sel_bracket(SelectParams P) {
 
 // Bracketed path, second step (one workgroup per chunk of a row): the
 // positions of the chunk's keys whose 24-bit prefix lies above P_hi, and the
-// positions and keys of those between P_lo and P_hi, go to the chunk's own
-// lists, their numbers to the chunk's two count words (cleared by the bracket
-// kernel).  Every chunk owns list room for as many entries as the finishing
-// step accepts in all.  The bounds are compared as floats (for non-negative
-// scores and -0 the same order as the keys; the bound of an empty upper side
-// is a NaN, above which nothing lies).  Hits are rare, so the compaction runs
-// per wave and per key slot: each compare gives the wave's ballot of hits for
-// that slot, empty ballots cost a scalar branch, and a hit lane's slot in the
-// list is the wave's running count plus its rank in the ballot.  A first pass
-// counts (the wave's list offsets then come from LDS counters, no barrier
-// waiting on the scores), a second pass writes.
+// positions and keys of those between P_lo and P_hi, go to lists the chunk
+// owns, a quarter of them per wave (kWaveTake and kWaveBin entries), and each
+// wave stores its two list lengths.  The bounds are compared as floats (for
+// non-negative scores and -0 the same order as the keys; the bound of an
+// empty upper side is a NaN, above which nothing lies).  Hits are rare, so
+// each key slot's compare gives the wave's ballot of hits, an empty ballot
+// costs a scalar branch, and a hit is written at once at the wave's running
+// count plus its rank in the ballot: one pass, no atomics, no barrier, no LDS.
+// A wave with more hits than its quarter holds (clustered scores) leaves its
+// row to the per-row kernel.
+constexpr int kWaveTake = kCompactTake / 4, kWaveBin = kCompactBin / 4;
 __global__ void __launch_bounds__(256) sel_collect(SelectParams P) {
   constexpr int NV = kKeysPerThread / 4;  // float4 loads per thread
-  __shared__ int32_t s_cnt[2];
   const int u = blockIdx.y, chunk = blockIdx.x;
   // the row's mode and candidates follow from its position, so the score
   // loads go out before the bracket is read
@@ -518,11 +514,6 @@ __global__ void __launch_bounds__(256) sel_collect(SelectParams P) {
   const int base = chunk * kSelChunk;
   if (base >= ncand) return;
   const int end = min(base + kSelChunk, ncand);
-  if (threadIdx.x == 0) {
-    s_cnt[0] = 0;
-    s_cnt[1] = 0;
-  }
-  __syncthreads();
   // element 4 i + e at position base + 4 (tid + 256 i) + e; positions past the
   // chunk read as NaN, which no bound test accepts
   const float* s = P.scores + (int64_t)u * P.N;
@@ -544,62 +535,40 @@ __global__ void __launch_bounds__(256) sel_collect(SelectParams P) {
   const int32_t* stw = P.state + (int64_t)u * ST_WORDS;
   const float hi = __uint_as_float(((uint32_t)stw[ST_PHI] << 8) | 0xFFu);
   const float lo = __uint_as_float((uint32_t)stw[ST_PLO] << 8);
-  // above: x > hi; inside: lo <= x and not above (NaN fails both, -0 >= +0 holds)
-  auto above = [&](float x) { return x > hi; };
-  auto inside = [&](float x) { return x >= lo && !(x > hi); };
-  int na = 0, nb = 0;  // wave-uniform
-#pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const float x[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      na += __popcll(__ballot(above(x[e])));
-      nb += __popcll(__ballot(inside(x[e])));
-    }
-  }
-  if ((na | nb) == 0) return;  // (wave-uniform) no hits in this wave
-  const int lane = threadIdx.x & 63;
-  int wa = 0, wb = 0;
-  if (lane == 0) {
-    const int64_t cb = (int64_t)u * P.nchunks + chunk;
-    if (na) {
-      wa = atomicAdd(&s_cnt[0], na);
-      atomicAdd(&P.cnt[2 * cb], na);
-    }
-    if (nb) {
-      wb = atomicAdd(&s_cnt[1], nb);
-      atomicAdd(&P.cnt[2 * cb + 1], nb);
-    }
-  }
-  int oa = __builtin_amdgcn_readfirstlane(wa), ob = __builtin_amdgcn_readfirstlane(wb);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t cw = ((int64_t)u * P.nchunks + chunk) * 4 + wave;
   int32_t* cand = P.cand + ((int64_t)u * P.nchunks + chunk) * kCandWords;
+  int32_t* la = cand + wave * kWaveTake;                           // above: positions
+  int32_t* lb = cand + kCompactTake + wave * kWaveBin;             // inside: positions
+  int32_t* lk = cand + kCompactTake + kCompactBin + wave * kWaveBin;  // inside: keys
   const uint64_t below = (1ull << lane) - 1;  // lanes ranked before this one
-  // the bounds pass through an empty asm statement, so the compares below are
-  // formed again rather than the first pass's 128 results kept in registers
-  float hi2 = hi, lo2 = lo;
-  asm volatile("" : "+v"(hi2), "+v"(lo2));
+  int oa = 0, ob = 0;  // wave-uniform running counts
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const float x[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int pos = base + 4 * (threadIdx.x + 256 * i) + e;
-      const bool ha = x[e] > hi2, hb = x[e] >= lo2 && !(x[e] > hi2);
+      // above: x > hi; inside: lo <= x and not above (NaN fails both, -0 >= +0 holds)
+      const bool ha = x[e] > hi, hb = x[e] >= lo && !(x[e] > hi);
       const uint64_t ba = __ballot(ha), bb = __ballot(hb);
       if (ba) {  // uniform
         const int o = oa + __popcll(ba & below);
-        if (ha && o < kCompactTake) cand[o] = pos;
+        if (ha && o < kWaveTake) la[o] = base + 4 * (threadIdx.x + 256 * i) + e;
         oa += __popcll(ba);
       }
       if (bb) {  // uniform
         const int o = ob + __popcll(bb & below);
-        if (hb && o < kCompactBin) {
-          cand[kCompactTake + o] = pos;
-          cand[kCompactTake + kCompactBin + o] = (int32_t)score_key(x[e]);
+        if (hb && o < kWaveBin) {
+          lb[o] = base + 4 * (threadIdx.x + 256 * i) + e;
+          lk[o] = (int32_t)score_key(x[e]);
         }
         ob += __popcll(bb);
       }
     }
+  }
+  if (lane == 0) {
+    P.cnt[2 * cw] = oa;
+    P.cnt[2 * cw + 1] = ob;
   }
 }
 
@@ -640,10 +609,10 @@ inline size_t finish_lds_bytes(int N) {
   return ((size_t)bm_slot4(nq - 1) + 1) * 16;
 }
 
-// Bracketed path, third step: one workgroup per row.  The chunks' list
+// Bracketed path, third step: one workgroup per row.  The (chunk, wave) list
 // lengths give the row's na keys above the bracket and nb inside it; the
-// bracket holds the k-th key when na < take <= na + nb, and with both within
-// the lists' sizes the row is settled here, else left to the per-row kernel.  The bin's keys (16 per thread in registers) give the need = take -
+// bracket holds the k-th key when na < take <= na + nb, and with every list
+// within its room the row is settled here, else left to the per-row kernel.  The bin's keys (16 per thread in registers) give the need = take -
 // na highest by a radix select on chip (digits of 12, 12 and 8 bits): every
 // key above the threshold tau and, of the keys equal to tau, the lowest
 // positions (found by sorting the tied positions, when not all of them are
@@ -654,34 +623,39 @@ __global__ void __launch_bounds__(256) sel_finish(SelectParams P) {
   constexpr int BPT = kCompactBin / 256, APT = kCompactTake / 256;
   extern __shared__ __align__(16) u32x4_t bm4[];  // finish_lds_bytes(N)
   __shared__ int32_t h[kHistBins];               // digit histograms, then tied positions or the taken list
-  __shared__ int32_t s_pa[kFinishMaxChunks], s_pb[kFinishMaxChunks];  // list starts per chunk
+  __shared__ int32_t s_pa[4 * kFinishMaxChunks], s_pb[4 * kFinishMaxChunks];  // list starts per (chunk, wave)
   __shared__ int32_t sm[264];
   __shared__ int32_t s_n;
   int32_t* st = P.state + (int64_t)blockIdx.x * ST_WORDS;
   if (st[ST_MODE] != MODE_RADIX) return;
   const int u = blockIdx.x, take = st[ST_TAKE], p = st[ST_P], ncand = st[ST_NCAND];
   const int tid = threadIdx.x;
-  // the chunks' list lengths, their exclusive prefix sums and the totals
+  // the (chunk, wave) regions' list lengths, their exclusive prefix sums and
+  // the totals; a region over its quarter lost entries, and a length outside
+  // [0, room] can only be corrupt: either sends the row to the per-row kernel
   const int nch = (ncand + kSelChunk - 1) / kSelChunk;
   if (nch > kFinishMaxChunks) return;  // (uniform) left to the per-row kernel
-  const int32_t* cnt = P.cnt + (int64_t)u * P.nchunks * 2;
-  int na = 0, nb = 0;
-  for (int c0 = 0; c0 < nch; c0 += 256) {
-    const int c = c0 + tid;
-    int32_t v[2] = {c < nch ? cnt[2 * c] : 0, c < nch ? cnt[2 * c + 1] : 0}, t[2];
-    block_exclusive_scan_n<2>(v, sm, t);
-    if (c < nch) {
-      s_pa[c] = na + v[0];
-      s_pb[c] = nb + v[1];
+  const int nreg = 4 * nch;
+  const int32_t* cnt = P.cnt + (int64_t)u * P.nchunks * 8;
+  int na = 0, nb = 0, over = 0;
+  for (int r0 = 0; r0 < nreg; r0 += 256) {
+    const int r = r0 + tid;
+    const int ca = r < nreg ? cnt[2 * r] : 0, cb = r < nreg ? cnt[2 * r + 1] : 0;
+    int32_t v[3] = {ca, cb, (ca < 0) | (cb < 0) | (ca > kWaveTake) | (cb > kWaveBin)}, t[3];
+    block_exclusive_scan_n<3>(v, sm, t);
+    if (r < nreg) {
+      s_pa[r] = na + v[0];
+      s_pb[r] = nb + v[1];
     }
     na += t[0];
     nb += t[1];
+    over += t[2];
   }
-  if (!(na < take && take <= na + nb && take <= kCompactTake && nb <= kCompactBin)) return;
+  if (over || !(na < take && take <= na + nb && take <= kCompactTake && nb <= kCompactBin)) return;
   __syncthreads();
-  // entry i of a list lies in the last chunk whose start is <= i
-  auto chunk_of = [&](const int32_t* starts, int i) {
-    int lo = 0, hi = nch - 1;
+  // entry i of a list lies in the last region whose start is <= i
+  auto region_of = [&](const int32_t* starts, int i) {
+    int lo = 0, hi = nreg - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
       if (starts[mid] <= i) lo = mid;
@@ -689,6 +663,7 @@ __global__ void __launch_bounds__(256) sel_finish(SelectParams P) {
     }
     return lo;
   };
+  // region r = 4 c + w: chunk c's lists, wave w's quarter
   const int32_t* cand = P.cand + (int64_t)u * P.nchunks * kCandWords;
   uint32_t bk[BPT];
   int32_t bp[BPT], ap[APT];
@@ -700,20 +675,20 @@ __global__ void __launch_bounds__(256) sel_finish(SelectParams P) {
     bp[j] = -1;
     bk[j] = 0u;
     if (ok) {
-      const int c = chunk_of(s_pb, i);
-      const int32_t* cc = cand + (int64_t)c * kCandWords + kCompactTake + (i - s_pb[c]);
+      const int r = region_of(s_pb, i);
+      const int32_t* cc = cand + (int64_t)(r >> 2) * kCandWords + kCompactTake + (r & 3) * kWaveBin + (i - s_pb[r]);
       bp[j] = cc[0];
       bk[j] = (uint32_t)cc[kCompactBin];
     }
     bvalid |= (uint64_t)ok << j;
   }
 #pragma unroll
-  for (int r = 0; r < APT; ++r) {
-    const int i = tid + 256 * r;
-    ap[r] = -1;
+  for (int r_ = 0; r_ < APT; ++r_) {
+    const int i = tid + 256 * r_;
+    ap[r_] = -1;
     if (i < na) {
-      const int c = chunk_of(s_pa, i);
-      ap[r] = cand[(int64_t)c * kCandWords + i - s_pa[c]];
+      const int r = region_of(s_pa, i);
+      ap[r_] = cand[(int64_t)(r >> 2) * kCandWords + (r & 3) * kWaveTake + (i - s_pa[r])];
     }
   }
   // radix select of the need-th largest bin key
