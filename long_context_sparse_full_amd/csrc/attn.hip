@@ -371,7 +371,7 @@ __device__ __forceinline__ void wait_vm() {
 }
 
 // Query fragments (MFMA B operand of QK^T): row r, head-dim slice dmap(c, g4).
-template <bool FP8, int D>
+template <bool FP8, int D, bool WAIT = true>
 __device__ __forceinline__ void load_q(u32x4_t (&qf)[D / 32], const ScanParams& P, int b, int t, int h, bool row_ok,
                                        int g4) {
   const uint16_t* qb = (const uint16_t*)P.q + (((int64_t)b * P.Tq + (row_ok ? t : 0)) * P.Hq + (row_ok ? h : 0)) * D;
@@ -380,7 +380,8 @@ __device__ __forceinline__ void load_q(u32x4_t (&qf)[D / 32], const ScanParams& 
   // The fragments arrive before any tile load is issued: left in flight, the
   // compiler's wait bookkeeping would count them as pending inside the tile
   // loops and drain the prefetched tile (a full vmcnt(0)) on every iteration.
-  wait_vm<0>();
+  // (WAIT = false: the caller waits once for everything in flight.)
+  if constexpr (WAIT) wait_vm<0>();
 }
 
 // Full layer: one workgroup per (position split, unit); waves take interleaved
@@ -843,7 +844,6 @@ __global__ void __launch_bounds__(256, BAND ? 2 : 3) chunk_flash(ScanParams P) {
     const ChunkRows cr = chunk_row<RG>(P, q0, blk_w, rg, r);
     jlim[rg] = cr.jlim;
     jlo[rg] = BAND ? cr.jlim - P.band + 1 : 0;  // sliding window: the row's first position
-    load_q<FP8, D>(qf[rg], P, b, cr.ok ? cr.t : 0, g * P.G + (r % P.G), cr.ok, g4);
   }
   const int t_first = it.blk * 4 * RG * P.tpack;  // first token of the workgroup
   const int t_last = min(t_first + 4 * RG * P.tpack, P.Tq) - 1;
@@ -871,6 +871,16 @@ __global__ void __launch_bounds__(256, BAND ? 2 : 3) chunk_flash(ScanParams P) {
     if (tile < ntile) ld.issue(tiles[tile % NBUF], j_begin + 32 * tile, p_max);
   };
 
+  // the ring's first tiles go out before the query fragments, and one wait
+  // covers both; after it the compiler's own wait bookkeeping has nothing
+  // pending across the loop (the tile loads are invisible to it)
+#pragma unroll
+  for (int t = 0; t < NBUF - 1; ++t) issue(t);
+#pragma unroll
+  for (int rg = 0; rg < RG; ++rg) {
+    const ChunkRows cr = chunk_row<RG>(P, q0, blk_w, rg, r);
+    load_q<FP8, D, false>(qf[rg], P, b, cr.ok ? cr.t : 0, g * P.G + (r % P.G), cr.ok, g4);
+  }
   ChunkState<D, RG> S;
 #pragma unroll
   for (int rg = 0; rg < RG; ++rg) {
@@ -881,11 +891,7 @@ __global__ void __launch_bounds__(256, BAND ? 2 : 3) chunk_flash(ScanParams P) {
 #pragma unroll
     for (int dt = 0; dt < VE; ++dt) S.o[rg][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
-  // the query loads complete here, so the compiler's own wait bookkeeping has
-  // nothing pending across the loop (the tile loads are invisible to it)
   wait_vm<0>();
-#pragma unroll
-  for (int t = 0; t < NBUF - 1; ++t) issue(t);
   // step n (buffer n % NBUF known at compile time in the unrolled body, so
   // every LDS address is a per-lane constant plus an immediate offset)
   auto step = [&](auto buf, int n) {
@@ -926,13 +932,25 @@ __global__ void __launch_bounds__(256, BAND ? 2 : 3) chunk_flash(ScanParams P) {
       const int64_t orow = ((int64_t)b * P.Tq + t) * P.Hq + g * P.G + r % P.G;
       const float inv = l > 0.f ? 1.f / l : 0.f;
       const float vsc = FP8 ? P.v_scale[b * P.Hkv + g] : 1.f;
-#pragma unroll
-      for (int dt = 0; dt < VE; ++dt)
+      const float f = inv * vsc;
+      uint16_t* orow_p = (uint16_t*)P.out + orow * D;
+      if constexpr (FP8) {  // head dims VE (4 g4 + ii) + dt: VE consecutive per ii, one 2*VE-byte store
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
-          const int d = FP8 ? VE * (4 * g4 + ii) + dt : 16 * dt + 4 * g4 + ii;
-          ((__bf16*)P.out)[orow * D + d] = (__bf16)(S.o[rg][dt][ii] * inv * vsc);
+          uint32_t w[VE / 2];
+#pragma unroll
+          for (int dt = 0; dt < VE; dt += 2) w[dt / 2] = pack_bf16(S.o[rg][dt][ii] * f, S.o[rg][dt + 1][ii] * f);
+          if constexpr (VE == 8)
+            *(u32x4_t*)(orow_p + VE * (4 * g4 + ii)) = u32x4_t{w[0], w[1], w[2], w[3]};
+          else
+            *(u32x2_t*)(orow_p + VE * (4 * g4 + ii)) = u32x2_t{w[0], w[1]};
         }
+      } else {  // head dims 16 dt + 4 g4 + ii: four consecutive per dt, one 8-byte store
+#pragma unroll
+        for (int dt = 0; dt < VE; ++dt)
+          *(u32x2_t*)(orow_p + 16 * dt + 4 * g4) =
+              u32x2_t{pack_bf16(S.o[rg][dt][0] * f, S.o[rg][dt][1] * f), pack_bf16(S.o[rg][dt][2] * f, S.o[rg][dt][3] * f)};
+      }
       if (g4 == 0 && P.lse) P.lse[orow] = l > 0.f ? (S.m[rg] + log2f(l)) * kLn2 : kNegInf;
       continue;
     }
@@ -995,20 +1013,7 @@ __global__ void __launch_bounds__(256, 2) chunk_score_flash(ScanParams P) {
   // a log2-sum-exp of +inf turns them into exact zeros with no extra test.
   u32x4_t qf[RG][NC];
   int rl_lim[RG][4];
-  float rl_l2[RG][4];
-#pragma unroll
-  for (int rg = 0; rg < RG; ++rg) {
-    const ChunkRows cr = chunk_row<RG>(P, q0, blk_w, rg, r);
-    load_q<FP8, D>(qf[rg], P, b, cr.ok ? cr.t : 0, g * P.G + (r % P.G), cr.ok, g4);
-    const int tp = blk_w * RG + rg;
-    const int unit = (b * P.n_tpacks + min(tp, P.n_tpacks - 1)) * P.Hkv + g;
-#pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
-      const ChunkRows crr = chunk_row<RG>(P, q0, blk_w, rg, 4 * g4 + ii);
-      rl_lim[rg][ii] = crr.jlim;  // -1 for such rows
-      rl_l2[rg][ii] = crr.ok ? P.lse2_in[(int64_t)unit * P.rows + 4 * g4 + ii] : __builtin_inff();
-    }
-  }
+  float rl_l2[RG][4];  // (loaded after the ring's first tiles are issued, below)
   const int t_first = it.blk * 4 * RG * P.tpack;  // first token of the workgroup
   const int t_last = min(t_first + 4 * RG * P.tpack, P.Tq) - 1;
   const int p_max = q0 + t_last;
@@ -1108,10 +1113,25 @@ __global__ void __launch_bounds__(256, 2) chunk_score_flash(ScanParams P) {
     }
     stage_flush(j0);
   };
-  // query and log-sum-exp loads complete before the tile loads start
-  wait_vm<0>();
+  // the ring's first tiles go out before the query and log-sum-exp loads,
+  // and one wait covers all of them (the compiler's own wait bookkeeping then
+  // has nothing pending across the loop)
 #pragma unroll
   for (int t = 0; t < NBUF - 1; ++t) issue(t);
+#pragma unroll
+  for (int rg = 0; rg < RG; ++rg) {
+    const ChunkRows cr = chunk_row<RG>(P, q0, blk_w, rg, r);
+    load_q<FP8, D, false>(qf[rg], P, b, cr.ok ? cr.t : 0, g * P.G + (r % P.G), cr.ok, g4);
+    const int tp = blk_w * RG + rg;
+    const int unit = (b * P.n_tpacks + min(tp, P.n_tpacks - 1)) * P.Hkv + g;
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      const ChunkRows crr = chunk_row<RG>(P, q0, blk_w, rg, 4 * g4 + ii);
+      rl_lim[rg][ii] = crr.jlim;  // -1 for such rows
+      rl_l2[rg][ii] = crr.ok ? P.lse2_in[(int64_t)unit * P.rows + 4 * g4 + ii] : __builtin_inff();
+    }
+  }
+  wait_vm<0>();
   // unrolled over the ring so each step's buffer is a compile-time constant
   auto step = [&](auto buf, int n) {
     constexpr int B = decltype(buf)::value;
