@@ -158,8 +158,8 @@ struct SelectParams {
   int32_t* count;
   int32_t* state;   // [units][16]
   int32_t* hist;    // [units][3][4096] digit histograms of the three passes
-  int32_t* cnt;     // [units][nchunks][258]: keys above the 24-bit prefix, suffix sums of the last digit;
-                    // bracketed path: [units][nchunks][4 waves][2] list lengths
+  int32_t* cnt;     // radix path: [units][nchunks][258]: keys above the 24-bit prefix, suffix sums of the
+                    // last digit; bracketed path: [units][nchunks][4 waves][2] list lengths
   int32_t* cand;    // bracketed path: [units][nchunks][kCandWords] each chunk's lists, a quarter per wave
   double* bmass;    // [units][nblocks_max] (block mode)
   int nblocks_max;

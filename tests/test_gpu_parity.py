@@ -146,18 +146,19 @@ SEL_CASES = [
     (1, 2, 1, 30000, 3000, 64, 1, "random"),   # k of several thousand
     (2, 2, 2, 40000, 2048, 128, 1, "ties"),    # heavy ties across chunks
     # a few thousand levels: small 24-bit bins with exact ties at the threshold
-    # (collected path; ties resolved by position on chip)
+    # (ties resolved by position)
     (1, 2, 2, 70000, 1024, 128, 1, "levels"),
-    (1, 1, 3, 40000, 2048, 64, 1, "levels"),   # largest k of the collected path
-    (1, 1, 2, 40000, 2049, 64, 1, "levels"),   # one more: the histogram path
+    (1, 1, 3, 40000, 2048, 64, 1, "levels"),   # k = 2048
+    (1, 1, 2, 40000, 2049, 64, 1, "levels"),   # k = 2049
     (3, 1, 1, 20001, 700, 5, 1, "levels"),     # odd N (scalar key loads)
-    # 2048 rows or more: the collected path (passes throughput-bound)
+    # 2048 chunk workgroups or more: the bracketed path (rows of up to 16384
+    # positions are sampled whole, so their bracket is the k-th key's 24-bit bin)
     (1, 512, 4, 16384, 1024, 128, 1, "levels"),
-    (1, 512, 4, 16384, 1024, 128, 1, "mixed"),  # rows alternate small and huge threshold bins
-    (2, 256, 4, 8000, 2048, 16, 1, "levels"),   # largest k of the collected path
-    (1, 256, 8, 20000, 2049, 64, 1, "levels"),  # k above it: every row on the histogram path
+    (1, 512, 4, 16384, 1024, 128, 1, "mixed"),  # rows alternate small and huge threshold bins (huge: per-row kernel)
+    (2, 256, 4, 8000, 2048, 16, 1, "levels"),   # the largest k the bracketed path settles
+    (1, 256, 8, 20000, 2049, 64, 1, "levels"),  # k above it: every row on the per-row kernel
     (1, 1024, 2, 12001, 300, 0, 1, "tiny"),     # odd N, no window, every row's bin too large
-    (1, 32, 8, 300001, 700, 64, 1, "levels"),   # 19 chunks per row, two per workgroup
+    (1, 32, 8, 300001, 700, 64, 1, "levels"),   # 19 chunks per row, over 2^18 candidates (sorted output)
     (1, 32, 8, 300001, 700, 64, 1, "mixed"),
     # odd kv heads: every top score in runs of 64 positions the bracket's
     # sample skips, so those rows' brackets miss and the per-row kernel
@@ -650,8 +651,8 @@ COMPETE_CASES = [
     (1, 1, 1, 3000, 5000, 16, "random"),      # k >= p + 1: every position
     (1, 4, 1, 100, 10, 128, "random"),        # p < window
     (1, 1, 2, 5000, 40, 0, "random"),         # no window
-    (1, 2, 2, 40000, 2049, 64, "recent"),     # k above the collected path's limit
-    (1, 512, 4, 16384, 1024, 128, "levels"),  # 2048 rows: the collected path
+    (1, 2, 2, 40000, 2049, 64, "recent"),     # k = 2049
+    (1, 512, 4, 16384, 1024, 128, "levels"),  # 2048 rows: the bracketed path
     (1, 512, 4, 16384, 1024, 128, "recent"),
 ]
 
