@@ -103,3 +103,28 @@ def test_varlen_swa_and_clamping(hs2):
     torch.cuda.synchronize()
     for x, y in zip(a, c):
         assert np.array_equal(gu.host(x), gu.host(y)), "full layer: clamped positions differ"
+
+
+@pytest.mark.parametrize("competes", [False, True], ids=["window", "competes"])
+def test_varlen_select_large_grid(hs2, competes):
+    """Per-batch query positions on a grid of 2048 rows x 3 chunks (the
+    bracketed selection): long rows whose bracket comes from a sample, rows
+    sampled whole, rows that take every candidate and rows that take none,
+    in one call; bit for bit against the oracle run per batch entry at its
+    position."""
+    B, Tq, Hkv, N, k, W = 4, 128, 4, 40000, 1024, 128
+    pos = [N - Tq, 12000, 100, 1200]
+    gu.log(f"varlen select, 2048 rows, positions {pos}, window competes: {competes}")
+    rng = np.random.default_rng(78 + competes)
+    sc = (rng.integers(0, 20000, (B, Tq, Hkv, N)) / 20000.0 * 1e-3).astype(np.float32)
+    max_sel = min(N, k + W)
+    qb = torch.tensor(pos, dtype=torch.int32, device="cuda")
+    idx, cnt = hs2.select_topk_window(torch.from_numpy(sc).cuda(), N - Tq, k, W, max_sel=max_sel, q_pos0_b=qb,
+                                      window_competes=competes)
+    torch.cuda.synchronize()
+    idx, cnt = gu.host(idx), gu.host(cnt)
+    for b in range(B):
+        i_or, c_or = oracle.select_topk_window(sc[b:b + 1].astype(np.float64), pos[b], k, W, max_sel=max_sel,
+                                               window_competes=competes)
+        assert np.array_equal(cnt[b:b + 1], c_or), f"counts differ at batch entry {b} (position {pos[b]})"
+        assert np.array_equal(idx[b:b + 1], i_or), f"index lists differ at batch entry {b} (position {pos[b]})"
