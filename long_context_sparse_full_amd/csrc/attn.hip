@@ -974,15 +974,9 @@ __global__ void __launch_bounds__(256, BAND ? 2 : 3) chunk_flash(ScanParams P) {
 // 2^(x_hj - lse2_h) for j <= p_t, 0 beyond.  K only; tiles past the
 // workgroup's last query position are zeros without loads.  Logits in the
 // S = Q K^T orientation (G >= 4): lane l holds rows 4*(l/16)+i of position
-// l%16, all of one token, so the head sum is three in-lane adds plus G/8 lane
-// exchanges.
-template <int G>
-__device__ __forceinline__ float head_sum_s(const float (&a)[4]) {
-  float v = (a[0] + a[1]) + (a[2] + a[3]);
-  if constexpr (G >= 8) v = sum_x16(v);
-  if constexpr (G >= 16) v = sum_x32(v);
-  return v;
-}
+// l%16, all of one token, so a token's head sum starts with three in-lane adds;
+// for G >= 8 one permlane16 swap then pairs the row groups (0,1) and (2,3) of
+// both 16-position halves at once (G = 16 adds a permlane32 swap).
 
 // Score pass, LDS-staged form: the workgroup's 4 waves hold kFlashRG row
 // groups each (4 * kFlashRG packs per workgroup) and share every K tile
@@ -1034,9 +1028,6 @@ __global__ void __launch_bounds__(256, 2) chunk_score_flash(ScanParams P) {
     if (tile < ntile) ld.issue(tiles[tile % NBUF], j_begin + 32 * tile, p_max);
   };
 
-  // writers: one lane group per token (G = 4: every group; 8: even groups; 16: group 0)
-  const bool writer = (g4 % (G / 4)) == 0;
-  const int wtok = (4 * g4) / G;
   float* st = stage[wave];
   auto stage_flush = [&](int j0) {
     for (int q = lane; q < RG * TP * 8; q += 64) {  // q: 4-float piece
@@ -1093,6 +1084,7 @@ __global__ void __launch_bounds__(256, 2) chunk_score_flash(ScanParams P) {
         for (int hh = 0; hh < 2; ++hh) sacc[rg][hh] = mfma_bf16(qf[rg][c], kf[hh][c], sacc[rg][hh]);
 #pragma unroll
     for (int rg = 0; rg < RG; ++rg) {
+      float hs[2];  // in-lane head sums of the two 16-position halves
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         const int j = j0 + 16 * hh + r;  // this lane's position
@@ -1107,8 +1099,18 @@ __global__ void __launch_bounds__(256, 2) chunk_score_flash(ScanParams P) {
 #pragma unroll
           for (int ii = 0; ii < 4; ++ii) acc[ii] = exp2_fast(__builtin_fmaf(sacc[rg][hh][ii], cs, -rl_l2[rg][ii]));
         }
-        const float v = head_sum_s<G>(acc);
-        if (writer) st[(rg * TP + wtok) * 32 + 16 * hh + r] = v;
+        hs[hh] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+      }
+      if constexpr (G == 4) {  // one token per row group of lanes: no exchange
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) st[(rg * TP + g4) * 32 + 16 * hh + r] = hs[hh];
+      } else {
+        // the swap leaves rows 0 and 2 holding half 0's pair, rows 1 and 3
+        // half 1's: lane row g4 ends with token g4 / 2 (G = 8), half g4 % 2
+        const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(hs[0]), __float_as_uint(hs[1]), false, false);
+        float v = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+        if constexpr (G == 16) v = sum_x32(v);  // rows 0 + 2 and 1 + 3: the token's 16 heads
+        if (G == 8 || g4 < 2) st[(rg * TP + (G == 8 ? g4 >> 1 : 0)) * 32 + 16 * (g4 & 1) + r] = v;
       }
     }
     stage_flush(j0);
@@ -2100,14 +2102,21 @@ hipError_t launch_chunk_score(const ScanParams& p, int kv_dtype, hipStream_t s) 
   if (p.G != 4 && p.G != 8 && p.G != 16) return hipErrorInvalidValue;
   if (!flash_rows_fit(p, kv_dtype)) return hipErrorInvalidValue;
   const int nblk = (p.n_tpacks + kChunkPacks - 1) / kChunkPacks;
-  const dim3 grid(p.B * nblk * p.Hkv * p.nsplit);
+  // the score pass needs no partials, so its position splits are its own:
+  // whole 128-position pieces, about kChunkScoreTargetWgs work items
+  ScanParams q = p;
+  const int64_t items = (int64_t)p.B * nblk * p.Hkv;
+  const int64_t per_item = std::max<int64_t>(1, kChunkScoreTargetWgs / items);
+  q.split_len = (int)(((p.N + per_item - 1) / per_item + 127) / 128 * 128);
+  q.nsplit = (p.N + q.split_len - 1) / q.split_len;
+  const dim3 grid(p.B * nblk * p.Hkv * q.nsplit);
   TimedLaunch tl("chunk_score", s);
   if (kv_dtype == HS2_FP8_E4M3FN) {
-    if (p.D == 128) go_chunk_score<true, 128>(p, grid, s);
-    else go_chunk_score<true, 64>(p, grid, s);
+    if (p.D == 128) go_chunk_score<true, 128>(q, grid, s);
+    else go_chunk_score<true, 64>(q, grid, s);
   } else {
-    if (p.D == 128) go_chunk_score<false, 128>(p, grid, s);
-    else go_chunk_score<false, 64>(p, grid, s);
+    if (p.D == 128) go_chunk_score<false, 128>(q, grid, s);
+    else go_chunk_score<false, 64>(q, grid, s);
   }
   return hipGetLastError();
 }

@@ -71,8 +71,12 @@ struct ScanParams {
 constexpr int kFlashRG = 2;
 constexpr int kChunkPacks = 4 * kFlashRG;
 constexpr int kChunkMinPacks = 4;
-// Chunk position splits: about this many full-pass work items in all.
-constexpr int64_t kChunkTargetWgs = 1024;
+// Chunk position splits.  The full pass holds three workgroups per CU (48 KiB
+// LDS rings), so about 768 work items fill the 256 CUs in one round (1024
+// left a second round a third full: 5% slower); the score pass holds four per
+// CU and splits the positions on its own, about 1024 work items in all.
+constexpr int64_t kChunkTargetWgs = 768;
+constexpr int64_t kChunkScoreTargetWgs = 1024;
 
 constexpr int kSelChunk = 16384;  // candidates per workgroup in the select passes
 constexpr int kHistBins = 4096;  // 12-bit digits
