@@ -130,43 +130,35 @@ struct RawTile {
   uint32_t v[8][VW];
 };
 
-template <typename T, bool NT>
-__device__ __forceinline__ T ld(const char* p) {
-  if constexpr (NT) {
-    return __builtin_nontemporal_load((const T*)p);
-  } else {
-    return *(const T*)p;
-  }
-}
-
+// One V row slice (T: 16, 8 or 4 bytes) into dwords.
 template <typename T>
-__device__ __forceinline__ void ldv(uint32_t* dst, const char* p, bool nt) {
+__device__ __forceinline__ void ldv(uint32_t* dst, const char* p) {
   if constexpr (sizeof(T) == 16) {
-    const u32x4_t w = nt ? ld<u32x4_t, true>(p) : ld<u32x4_t, false>(p);
+    const u32x4_t w = *(const u32x4_t*)p;
     dst[0] = w.x; dst[1] = w.y; dst[2] = w.z; dst[3] = w.w;
   } else if constexpr (sizeof(T) == 8) {
-    const u32x2_t w = nt ? ld<u32x2_t, true>(p) : ld<u32x2_t, false>(p);
+    const u32x2_t w = *(const u32x2_t*)p;
     dst[0] = w.x; dst[1] = w.y;
   } else {
-    dst[0] = nt ? ld<uint32_t, true>(p) : ld<uint32_t, false>(p);
+    dst[0] = *(const uint32_t*)p;
   }
 }
 
 // Loads of one tile from per-lane row addresses: kptr[hh] / vptr[kk] point at
 // this lane's first byte of the row.
-template <bool FP8, int D, bool NT>
+template <bool FP8, int D>
 __device__ __forceinline__ void load_tile(RawTile<FP8, D>& R, const char* const kptr[2], const char* const vptr[8]) {
   using RT = RawTile<FP8, D>;
   constexpr int VB = RT::VW * 4;  // bytes per V row slice
 #pragma unroll
   for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-    for (int c = 0; c < RT::KW; ++c) R.k[hh][c] = ld<u32x4_t, NT>(kptr[hh] + 64 * c);
+    for (int c = 0; c < RT::KW; ++c) R.k[hh][c] = *(const u32x4_t*)(kptr[hh] + 64 * c);
 #pragma unroll
   for (int kk = 0; kk < 8; ++kk) {
-    if constexpr (VB == 16) ldv<u32x4_t>(R.v[kk], vptr[kk], NT);
-    else if constexpr (VB == 8) ldv<u32x2_t>(R.v[kk], vptr[kk], NT);
-    else ldv<uint32_t>(R.v[kk], vptr[kk], NT);
+    if constexpr (VB == 16) ldv<u32x4_t>(R.v[kk], vptr[kk]);
+    else if constexpr (VB == 8) ldv<u32x2_t>(R.v[kk], vptr[kk]);
+    else ldv<uint32_t>(R.v[kk], vptr[kk]);
   }
 }
 
@@ -460,7 +452,7 @@ __global__ void __launch_bounds__(WAVES * 64) scan_full(ScanParams P) {
     for (int hh = 0; hh < 2; ++hh) kp[hh] = tk + koff[hh];
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) vp[kk] = tv + voff[kk];
-    load_tile<FP8, D, false>(R, kp, vp);
+    load_tile<FP8, D>(R, kp, vp);
   };
   auto load = [&](RawTile<FP8, D>& R, int j0) {
     if (j0 + 31 <= p_max) {
@@ -473,7 +465,7 @@ __global__ void __launch_bounds__(WAVES * 64) scan_full(ScanParams P) {
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk)
         vp[kk] = vb + (int64_t)min(j0 + 16 * (kk >> 2) + 4 * g4 + (kk & 3), p_max) * snb + VE * r * EB;
-      load_tile<FP8, D, false>(R, kp, vp);
+      load_tile<FP8, D>(R, kp, vp);
     }
   };
   auto compute = [&](const RawTile<FP8, D>& R, int j0) {
@@ -1219,7 +1211,7 @@ __global__ void __launch_bounds__(WAVES * 64, (FP8 || D == 64) ? 3 : 2) scan_gat
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk)
         vp[kk] = vb + (int64_t)s_idx[min(j0 - base + 16 * (kk >> 2) + 4 * g4 + (kk & 3), nb - 1)] * snb;
-      load_tile<FP8, D, false>(R, kp, vp);
+      load_tile<FP8, D>(R, kp, vp);
     };
     auto compute = [&](const RawTile<FP8, D>& R, int j0) {
       compute_tile<FP8, D, false>(R, qf, cs, j0, jl, j0 + 31 > jl, g4, nullptr, nullptr, 0, S);
@@ -1315,7 +1307,7 @@ __global__ void __launch_bounds__(WAVES * 64) scan_gather_split(ScanParams P) {
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk)
         vp[kk] = vb + (int64_t)s_idx[min(j0 - lo + 16 * (kk >> 2) + 4 * g4 + (kk & 3), nb - 1)] * snb;
-      load_tile<FP8, D, false>(R, kp, vp);
+      load_tile<FP8, D>(R, kp, vp);
     };
     // this wave's tiles j_first + i * STEP, i < nt; unconditional loads as in
     // the one-workgroup form (tiles past the slice reload its last row, unused)
