@@ -95,6 +95,9 @@ def main():
                     help="full layer + selection through hs2_full_attn_topk (1, default) or two calls (0)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (counter calibration)")
+    ap.add_argument("--read-probe", action="store_true",
+                    help="decode configs: only time the scan's read-pattern probe (with and without its code "
+                         "stores) beside the scan itself")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no multi-GPU path",
@@ -148,6 +151,30 @@ def main():
     scores = torch.empty((B, Tq, Hkv, N), dtype=torch.float32, device="cuda")
     ws_full = torch.empty(hs2.full_attn_scores_workspace(k, v, Tq, Hq), dtype=torch.uint8, device="cuda")
     ws_topk = torch.empty(hs2.full_attn_topk_workspace(k, v, Tq, Hq), dtype=torch.uint8, device="cuda")
+    if args.read_probe:
+        # the scan's loads alone, then with its code stores, then the scan (same plan, grid and tiles)
+        calls = (("scan_read_probe", lambda: hs2.debug_scan_read_probe(k, v, Hq, False, ks, vs, workspace=ws_full)),
+                 ("scan_read_probe_codes", lambda: hs2.debug_scan_read_probe(k, v, Hq, True, ks, vs, workspace=ws_full)),
+                 ("full_scan", lambda: hs2.full_attn_scores(k, v, q, spec.q_pos0, k_scale=ks, v_scale=vs, out=out,
+                                                            lse=lse, scores=scores, workspace=ws_full)))
+        res = {"workload": spec.name, "cache_bytes": int(k.numel() * k.element_size() + v.numel() * v.element_size())}
+        for name, call in calls:
+            for _ in range(3):
+                call()
+            torch.cuda.synchronize()
+            hs2.timing_enable(True)
+            hs2.timing_reset()
+            for _ in range(10):
+                call()
+            torch.cuda.synchronize()
+            ms, n = hs2.timing_collect(name)
+            hs2.timing_enable(False)
+            hs2.timing_reset()
+            res[f"{name}_us"] = round(ms * 1e3 / max(n, 1), 2)
+            res[f"{name}_cache_read_tbps"] = round(res["cache_bytes"] / (ms * 1e-3 / max(n, 1)) / 1e12, 3)
+            log(f"[read-probe] {name}: {res[f'{name}_us']} us")
+        print(json.dumps({"read_probe": res}), flush=True)
+        return
     idx = torch.empty((B, Tq, Hkv, spec.max_sel), dtype=torch.int32, device="cuda")
     cnt = torch.empty((B, Tq, Hkv), dtype=torch.int32, device="cuda")
     ws_sel = torch.empty(hs2.select_workspace(B, Tq, Hkv, N, 1), dtype=torch.uint8, device="cuda")
@@ -517,6 +544,30 @@ def bench_chunk(spec, args):
     scores = torch.empty((B, Tq, Hkv, N), dtype=torch.float32, device="cuda")
     ws_full = torch.empty(hs2.full_attn_scores_workspace(k, v, Tq, Hq), dtype=torch.uint8, device="cuda")
     ws_topk = torch.empty(hs2.full_attn_topk_workspace(k, v, Tq, Hq), dtype=torch.uint8, device="cuda")
+    if args.read_probe:
+        # the scan's loads alone, then with its code stores, then the scan (same plan, grid and tiles)
+        calls = (("scan_read_probe", lambda: hs2.debug_scan_read_probe(k, v, Hq, False, ks, vs, workspace=ws_full)),
+                 ("scan_read_probe_codes", lambda: hs2.debug_scan_read_probe(k, v, Hq, True, ks, vs, workspace=ws_full)),
+                 ("full_scan", lambda: hs2.full_attn_scores(k, v, q, spec.q_pos0, k_scale=ks, v_scale=vs, out=out,
+                                                            lse=lse, scores=scores, workspace=ws_full)))
+        res = {"workload": spec.name, "cache_bytes": int(k.numel() * k.element_size() + v.numel() * v.element_size())}
+        for name, call in calls:
+            for _ in range(3):
+                call()
+            torch.cuda.synchronize()
+            hs2.timing_enable(True)
+            hs2.timing_reset()
+            for _ in range(10):
+                call()
+            torch.cuda.synchronize()
+            ms, n = hs2.timing_collect(name)
+            hs2.timing_enable(False)
+            hs2.timing_reset()
+            res[f"{name}_us"] = round(ms * 1e3 / max(n, 1), 2)
+            res[f"{name}_cache_read_tbps"] = round(res["cache_bytes"] / (ms * 1e-3 / max(n, 1)) / 1e12, 3)
+            log(f"[read-probe] {name}: {res[f'{name}_us']} us")
+        print(json.dumps({"read_probe": res}), flush=True)
+        return
     idx = torch.empty((B, Tq, Hkv, spec.max_sel), dtype=torch.int32, device="cuda")
     cnt = torch.empty((B, Tq, Hkv), dtype=torch.int32, device="cuda")
     bsel = spec.block_k * spec.block_size + spec.window

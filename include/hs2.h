@@ -285,6 +285,22 @@ int hs2_debug_e4m3fn_to_f32(const uint8_t* codes, float* out, int32_t n, hipStre
  * compared with. */
 int hs2_debug_stream_read(const void* buf, size_t bytes, uint32_t* out, int32_t blocks, hipStream_t stream);
 
+/* Diagnostic: read-pattern probe of the decode scan.  Runs the full layer's
+ * decode plan (one query token at position N-1 of every batch row, Hq query
+ * heads) with the scan's grid, position splits, per-lane loads and tile loop
+ * over the cache `kv` (bf16 or FP8_E4M3FN, D = 64 or 128), with the attention
+ * arithmetic replaced by an xor of the loaded words; with_codes != 0 adds the
+ * scan's stores of 16-bit logit codes and tile maxima.  The results are
+ * scratch: the workspace (hs2_full_attn_scores_workspace(kv, 1, Hq) bytes,
+ * 256-byte aligned) receives the codes and one word per thread.  Its duration
+ * (kernels "scan_read_probe" and "scan_read_probe_codes") beside the scan's
+ * ("full_scan") separates the cache read, the code writes and the arithmetic
+ * in the scan's cost.  Errors: HS2_ERR_INVALID_ARG for a bad descriptor, Hq
+ * or alignment, HS2_ERR_UNSUPPORTED for an fp32 cache, HS2_ERR_WORKSPACE when
+ * the workspace is short. */
+int hs2_debug_scan_read_probe(const hs2_kv_desc* kv, int32_t Hq, int32_t with_codes, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream);
+
 /* Full layer and token selection in one call: the results of
  * hs2_full_attn_scores followed by hs2_select_topk_window with block_size 1
  * (same layouts, rules, flags and requirements; both passages above).  With one

@@ -183,7 +183,8 @@ const char* const kKernelNames[] = {"full_scan",      "combine",        "score",
                                     "select_hist",    "select_bracket", "select_collect", "select_finish",
                                     "select_exact",   "select_emit",    "select_window",  "select_block_mass",
                                     "select_block_pick", "sparse_gather", "kv_bridge",    "stream_read",
-                                    "chunk_full",     "chunk_score",    "swa_chunk",      nullptr};
+                                    "chunk_full",     "chunk_score",    "swa_chunk",      "scan_read_probe",
+                                    "scan_read_probe_codes", nullptr};
 
 // Timing state (only while hs2_timing_enable(1) is in force): the event pairs
 // of the launches since the last reset.  Events are created per launch and
@@ -939,6 +940,46 @@ int hs2_debug_stream_read(const void* buf, size_t bytes, uint32_t* out, int32_t 
     return fail(HS2_ERR_INVALID_ARG, "hs2_debug_stream_read: bad arguments");
   const hipError_t e = hs2::launch_stream_read(buf, bytes, out, blocks, stream);
   if (e != hipSuccess) return hip_fail(e, "stream_read launch");
+  return HS2_OK;
+}
+
+int hs2_debug_scan_read_probe(const hs2_kv_desc* kv, int32_t Hq, int32_t with_codes, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream) {
+  const char* name = "hs2_debug_scan_read_probe";
+  int st = check_kv(kv, name);
+  if (st) return st;
+  if (kv->dtype == HS2_F32) return fail(HS2_ERR_UNSUPPORTED, std::string(name) + ": bf16 or FP8_E4M3FN cache only");
+  if (Hq <= 0 || Hq % kv->Hkv || Hq / kv->Hkv > 16)
+    return fail(HS2_ERR_INVALID_ARG, std::string(name) + ": Hq must be a multiple of Hkv with at most 16 heads per group");
+  const FullPlan pl = plan_full(kv, 1, Hq);
+  if (!workspace || workspace_bytes < pl.total)
+    return fail(HS2_ERR_WORKSPACE, std::string(name) + ": workspace needs " + std::to_string(pl.total) + " bytes");
+  if ((uintptr_t)workspace & 255) return fail(HS2_ERR_INVALID_ARG, std::string(name) + ": workspace must be 256-byte aligned");
+  hs2::ScanParams p{};
+  p.k = kv->k;
+  p.v = kv->v;
+  p.sb = kv->stride_b;
+  p.sh = kv->stride_h;
+  p.sn = kv->stride_n;
+  p.B = kv->B;
+  p.Hkv = kv->Hkv;
+  p.N = kv->N;
+  p.D = kv->D;
+  p.G = Hq / kv->Hkv;
+  p.Tq = 1;
+  p.Hq = Hq;
+  p.q_pos0 = kv->N - 1;  // one query token at the last position: the whole cache
+  p.tpack = pl.tpack;
+  p.n_tpacks = pl.n_tpacks;
+  p.rows = pl.rows;
+  p.nsplit = pl.nsplit;
+  p.split_len = pl.split_len;
+  p.part_o = at<float>(workspace, pl.off_o);
+  p.lg16 = at<uint16_t>(workspace, pl.off_lg16);
+  p.lgmax = at<float>(workspace, pl.off_lgmax);
+  p.npad = pl.npad;
+  const hipError_t e = hs2::launch_scan_read_probe(p, kv->dtype, with_codes != 0, stream);
+  if (e != hipSuccess) return hip_fail(e, "scan_read_probe launch");
   return HS2_OK;
 }
 

@@ -1974,6 +1974,118 @@ __global__ void __launch_bounds__(256) stream_read(const u32x4_t* __restrict__ b
   out[(int64_t)blockIdx.x * 256 + threadIdx.x] = acc;
 }
 
+// Read-pattern probe of the decode scan: the launch, split mapping, per-lane
+// row offsets and tile loads of scan_full, two tiles in flight per wave, with
+// the attention arithmetic replaced by an xor of the loaded words.  With CODES
+// every valid row lane also stores what the scan stores per tile (two 8-byte
+// words of 16-bit codes in the row-major code buffer, and the tile maximum from
+// lane group 0).  Its duration with and without CODES, beside the scan's,
+// separates the cache read, the code writes and the arithmetic.  One xor word
+// per thread goes to part_o (as words): units x nsplit x 256 of them.
+template <bool FP8, int D, bool CODES, int WAVES>
+__global__ void __launch_bounds__(WAVES * 64) scan_read_probe(ScanParams P) {
+  constexpr int VE = D / 16, EB = FP8 ? 1 : 2;
+  constexpr int STEP = WAVES * 32;
+  using RT = RawTile<FP8, D>;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane & 15, g4 = lane >> 4;
+  const int unit = blockIdx.y, split = blockIdx.x;
+  const int g = unit % P.Hkv;
+  const int tp = (unit / P.Hkv) % P.n_tpacks;
+  const int b = unit / (P.Hkv * P.n_tpacks);
+  const int t = tp * P.tpack + r / P.G;
+  const bool row_ok = (r < P.rows) && (t < P.Tq);
+  const int q0 = qpos_of(P.qpos_b, P.q_pos0, b, P.N, P.Tq);
+  const int p_max = q0 + min(tp * P.tpack + P.tpack, P.Tq) - 1;
+  const int j_begin = split * STEP;
+  const int j_end = p_max + 1;
+  const int jstride = P.nsplit * STEP;
+  const int64_t kvoff = ((int64_t)b * P.sb + (int64_t)g * P.sh) * EB;
+  const char* kb = (const char*)P.k + kvoff;
+  const char* vb = (const char*)P.v + kvoff;
+  const int64_t snb = P.sn * EB;
+  uint16_t* lg_row = nullptr;
+  float* lgm_row = nullptr;
+  if (CODES && row_ok) {
+    lg_row = P.lg16 + ((int64_t)unit * P.rows + r) * P.npad + 4 * g4;
+    lgm_row = P.lgmax + (int64_t)unit * (P.npad >> 5) * P.rows + r;
+  }
+  uint32_t koff[2], voff[8];
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) koff[hh] = (uint32_t)((16 * hh + r) * snb) + 16u * g4;
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk)
+    voff[kk] = (uint32_t)((16 * (kk >> 2) + 4 * g4 + (kk & 3)) * snb) + (uint32_t)(VE * r * EB);
+  auto load_full = [&](RT& R, int j0) {
+    const char* kp[2];
+    const char* vp[8];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) kp[hh] = kb + (int64_t)j0 * snb + koff[hh];
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) vp[kk] = vb + (int64_t)j0 * snb + voff[kk];
+    load_tile<FP8, D>(R, kp, vp);
+  };
+  auto load = [&](RT& R, int j0) {
+    if (j0 + 31 <= p_max) {
+      load_full(R, j0);
+    } else {  // tail tile: rows past the last position repeat it
+      const char* kp[2];
+      const char* vp[8];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) kp[hh] = kb + (int64_t)min(j0 + 16 * hh + r, p_max) * snb + 16 * g4;
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk)
+        vp[kk] = vb + (int64_t)min(j0 + 16 * (kk >> 2) + 4 * g4 + (kk & 3), p_max) * snb + VE * r * EB;
+      load_tile<FP8, D>(R, kp, vp);
+    }
+  };
+  uint32_t acc = 0;
+  auto consume = [&](const RT& R, int j0) {
+    uint32_t x = 0;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int c = 0; c < RT::KW; ++c) x ^= R.k[hh][c].x ^ R.k[hh][c].y ^ R.k[hh][c].z ^ R.k[hh][c].w;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk)
+#pragma unroll
+      for (int w = 0; w < RT::VW; ++w) x ^= R.v[kk][w];
+    acc = acc * 3u + x;
+    if (CODES && lg_row) {
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) *(u32x2_t*)(lg_row + j0 + 16 * hh) = u32x2_t{x, x + (uint32_t)hh};
+      if (g4 == 0) lgm_row[(j0 >> 5) * P.rows] = __uint_as_float(x & 0x3f7fffffu);
+    }
+  };
+  // the scan's tile loop: unconditional prefetches in the steady state, at
+  // most three tiles in the epilogue
+  const int j_first = j_begin + wave * 32;
+  const int n = j_first < j_end ? (j_end - 1 - j_first) / jstride + 1 : 0;
+  const int n_full = j_first + 31 <= p_max ? min(n, (p_max - 31 - j_first) / jstride + 1) : 0;
+  RT A, B;
+  int i = 0;
+  if (n > 0) load(A, j_first);
+  for (; i + 2 < n_full; i += 2) {
+    const int j0 = j_first + i * jstride;
+    load_full(B, j0 + jstride);
+    consume(A, j0);
+    load_full(A, j0 + 2 * jstride);
+    consume(B, j0 + jstride);
+  }
+  if (i < n) {
+    const int j0 = j_first + i * jstride;
+    if (i + 1 < n) load(B, j0 + jstride);
+    consume(A, j0);
+    if (i + 1 < n) {
+      if (i + 2 < n) load(A, j0 + 2 * jstride);
+      consume(B, j0 + jstride);
+      if (i + 2 < n) consume(A, j0 + 2 * jstride);
+    }
+  }
+  ((uint32_t*)P.part_o)[((int64_t)unit * P.nsplit + split) * (WAVES * 64) + threadIdx.x] = acc;
+}
+
 __global__ void debug_e4m3fn(const uint8_t* codes, float* out, int n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i * 4 >= n) return;
@@ -2142,6 +2254,26 @@ hipError_t launch_score(const ScoreParams& p, int units, hipStream_t s) {
     const int blocks = (p.N + 1023) / 1024;
     hipLaunchKernelGGL(score, dim3(blocks, units), dim3(256), 0, s, p);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_scan_read_probe(const ScanParams& p, int kv_dtype, bool codes, hipStream_t s) {
+  if (kv_dtype == HS2_F32) return hipErrorInvalidValue;
+  const dim3 grid(p.nsplit, p.B * p.n_tpacks * p.Hkv);
+  TimedLaunch tl(codes ? "scan_read_probe_codes" : "scan_read_probe", s);
+#define HS2_PR(F8, DD)                                                                                  \
+  do {                                                                                                  \
+    if (codes) hipLaunchKernelGGL((scan_read_probe<F8, DD, true, kScanWaves>), grid, dim3(kScanWaves * 64), 0, s, p); \
+    else hipLaunchKernelGGL((scan_read_probe<F8, DD, false, kScanWaves>), grid, dim3(kScanWaves * 64), 0, s, p);      \
+  } while (0)
+  if (kv_dtype == HS2_FP8_E4M3FN) {
+    if (p.D == 128) HS2_PR(true, 128);
+    else HS2_PR(true, 64);
+  } else {
+    if (p.D == 128) HS2_PR(false, 128);
+    else HS2_PR(false, 64);
+  }
+#undef HS2_PR
   return hipGetLastError();
 }
 

@@ -205,6 +205,9 @@ hipError_t launch_bridge(const uint16_t* hidden, int T, int dm, const uint16_t* 
                          const BridgeLayers& out, hipStream_t s);
 hipError_t launch_debug_e4m3fn(const uint8_t* codes, float* out, int n, hipStream_t s);
 hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* out, int blocks, hipStream_t s);
+// Read-pattern probe of the decode scan (same plan and grid as launch_scan
+// over the full cache); `codes` adds the scan's code stores.
+hipError_t launch_scan_read_probe(const ScanParams& p, int kv_dtype, bool codes, hipStream_t s);
 
 // timing hooks used by the launchers
 struct TimedLaunch {

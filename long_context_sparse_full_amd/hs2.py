@@ -82,6 +82,7 @@ _swa = _sig("hs2_swa_attn", ctypes.c_int, [_KVP, _vp, _i32, _i32, _i32, _i32, _v
 _bridge = _sig("hs2_kv_bridge", ctypes.c_int, [_vp, _i32, _i32, _vp, ctypes.POINTER(KVOutDesc), _i32, _i32, _vp])
 _dbg_e4m3 = _sig("hs2_debug_e4m3fn_to_f32", ctypes.c_int, [_vp, _vp, _i32, _vp])
 _dbg_stream = _sig("hs2_debug_stream_read", ctypes.c_int, [_vp, _sz, _vp, _i32, _vp])
+_dbg_scanprobe = _sig("hs2_debug_scan_read_probe", ctypes.c_int, [_vp, _i32, _i32, _vp, _sz, _vp])
 _t_enable = _sig("hs2_timing_enable", ctypes.c_int, [ctypes.c_int])
 _t_reset = _sig("hs2_timing_reset", ctypes.c_int, [])
 _t_collect = _sig("hs2_timing_collect", ctypes.c_int,
@@ -94,6 +95,7 @@ EXPORTED = [
     "hs2_sparse_attn_gather", "hs2_sparse_attn_workspace", "hs2_sparse_attn_gather_ws",
     "hs2_sparse_attn_static_limit", "hs2_sparse_attn_gather_static", "hs2_swa_attn", "hs2_kv_bridge",
     "hs2_kv_bridge_layers_workspace", "hs2_kv_bridge_layers", "hs2_debug_e4m3fn_to_f32", "hs2_debug_stream_read",
+    "hs2_debug_scan_read_probe",
     "hs2_timing_enable",
     "hs2_timing_reset", "hs2_timing_collect", "hs2_timing_kernel_name",
 ]
@@ -384,6 +386,19 @@ def debug_stream_read(buf: torch.Tensor, blocks: int = 2048) -> torch.Tensor:
     _check(_dbg_stream(buf.data_ptr(), nbytes - nbytes % 16, out.data_ptr(), blocks, _stream()),
            "hs2_debug_stream_read")
     return out
+
+
+def debug_scan_read_probe(k, v, Hq: int, with_codes: bool, k_scale=None, v_scale=None, workspace=None):
+    """The decode scan's read pattern over the cache with its arithmetic replaced by an xor
+    (with_codes: plus its code stores); returns the scratch workspace."""
+    d = kv_desc(k, v, k_scale, v_scale)
+    need = int(_full_ws(ctypes.byref(d), 1, Hq))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=k.device)
+    _dense(workspace)
+    _check(_dbg_scanprobe(ctypes.byref(d), int(Hq), int(bool(with_codes)), workspace.data_ptr(), workspace.numel(),
+                          _stream()), "hs2_debug_scan_read_probe")
+    return workspace
 
 
 def timing_enable(on: bool = True):

@@ -60,6 +60,7 @@ def test_version_and_status_strings(hs2):
 def test_timing_names(hs2):
     names = hs2.timing_kernel_names()
     assert "full_scan" in names and "sparse_gather" in names and "select_hist" in names
+    assert "scan_read_probe" in names and "scan_read_probe_codes" in names
 
 
 # --- validation, with fake (never dereferenced) device addresses -----------
@@ -127,6 +128,31 @@ def test_full_attn_validation(hs2, case, want):
                          None) == want
         return
     assert full(hs2, d, **kw) == want
+    assert hs2._last_error().decode()
+
+
+@pytest.mark.parametrize("case,want", [
+    ("small_ws", -3), ("null_kv", -1), ("f32_cache", -2), ("hq_not_multiple", -1), ("group_32", -1),
+    ("fp8_without_scales", -2), ("ws_misaligned", -1),
+])
+def test_scan_read_probe_validation(hs2, case, want):
+    d, Hq, ws, wsb = desc(hs2), 16, FAKE, 1 << 40
+    if case == "small_ws":
+        wsb = 16
+    elif case == "null_kv":
+        assert hs2._dbg_scanprobe(None, Hq, 1, ws, wsb, None) == want
+        return
+    elif case == "f32_cache":
+        d = desc(hs2, dtype=0)
+    elif case == "hq_not_multiple":
+        Hq = 15
+    elif case == "group_32":
+        d, Hq = desc(hs2, H=1), 32
+    elif case == "fp8_without_scales":
+        d = desc(hs2, dtype=2)
+    elif case == "ws_misaligned":
+        ws = FAKE + 16
+    assert hs2._dbg_scanprobe(ctypes.byref(d), Hq, 1, ws, wsb, None) == want
     assert hs2._last_error().decode()
 
 
