@@ -973,7 +973,8 @@ __global__ void __launch_bounds__(256, BAND ? 2 : 3) chunk_flash(ScanParams P) {
 // Score pass, LDS-staged form: the workgroup's 4 waves hold kFlashRG row
 // groups each (4 * kFlashRG packs per workgroup) and share every K tile
 // through the LDS ring; each wave stages its tokens' 32-position score rows
-// in LDS and writes them with 16-byte stores.
+// in LDS and writes them with 16-byte stores.  Software-pipelined: a step
+// issues the next tile's QK^T while it forms this tile's terms.
 template <bool FP8, int D, int G>
 __global__ void __launch_bounds__(256, 2) chunk_score_flash(ScanParams P) {
   static_assert(G == 4 || G == 8 || G == 16, "chunk score pass: G in {4, 8, 16}");
@@ -993,12 +994,12 @@ __global__ void __launch_bounds__(256, 2) chunk_score_flash(ScanParams P) {
   const int blk_w = it.blk * 4 + wave;  // this wave's block of RG packs
   const int q0 = qpos_of(P.qpos_b, P.q_pos0, b, P.N, P.Tq);
 
-  // query fragments (row r of each group), and this lane's four S rows
-  // 4*g4 + ii: their token, causal limit and log2-sum-exp
-  // Rows past Tq (or past the pack) have a zero query, so their logits are 0;
-  // a log2-sum-exp of +inf turns them into exact zeros with no extra test.
+  // query fragments (row r of each group), and the log2-sum-exp of this
+  // lane's four S rows 4*g4 + ii.  Rows past Tq (or past the pack) have a zero
+  // query, so their logits are 0; a log2-sum-exp of +inf turns them into
+  // exact zeros with no extra test.  Positions past a token's own are zeroed
+  // when the tile's scores are flushed.
   u32x4_t qf[RG][NC];
-  int rl_lim[RG][4];
   float rl_l2[RG][4];  // (loaded after the ring's first tiles are issued, below)
   const int t_first = it.blk * 4 * RG * P.tpack;  // first token of the workgroup
   const int t_last = min(t_first + 4 * RG * P.tpack, P.Tq) - 1;
@@ -1026,8 +1027,13 @@ __global__ void __launch_bounds__(256, 2) chunk_score_flash(ScanParams P) {
       const int row = q >> 3, pos = (q & 7) * 4;
       const int rg = row / TP, tl = row - rg * TP;
       const int t = (blk_w * RG + rg) * TP + tl;
-      const f32x4_t v = *(const f32x4_t*)(st + row * 32 + pos);
+      f32x4_t v = *(const f32x4_t*)(st + row * 32 + pos);
       if (t >= P.Tq) continue;
+      if (j0 + 31 > j_nomask) {  // positions past the token's own are zero
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (j0 + pos + e > q0 + t) v[e] = 0.f;
+      }
       float* dst = P.scores + (((int64_t)b * P.Tq + t) * P.Hkv + g) * P.N + j0 + pos;
       if ((P.N & 3) == 0 && j0 + pos + 3 < P.N) {
         *(f32x4_t*)dst = v;
@@ -1038,8 +1044,8 @@ __global__ void __launch_bounds__(256, 2) chunk_score_flash(ScanParams P) {
       }
     }
   };
-  auto compute = [&](const char* kl, int n) {
-    const int j0 = j_begin + 32 * n;
+  // QK^T of the tile in LDS buffer kl into s
+  auto qk = [&](const char* kl, f32x4_t (&s)[RG][2]) {
     u32x4_t kf[2][NC];
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
@@ -1061,51 +1067,40 @@ __global__ void __launch_bounds__(256, 2) chunk_score_flash(ScanParams P) {
         }
       }
     }
-    // tiles ending at or before j_nomask lie inside every live row's window
-    const bool need_mask = j0 + 31 > j_nomask;
-    f32x4_t sacc[RG][2];
 #pragma unroll
     for (int rg = 0; rg < RG; ++rg)
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) sacc[rg][hh] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int hh = 0; hh < 2; ++hh) s[rg][hh] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < NC; ++c)
 #pragma unroll
       for (int rg = 0; rg < RG; ++rg)
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) sacc[rg][hh] = mfma_bf16(qf[rg][c], kf[hh][c], sacc[rg][hh]);
+        for (int hh = 0; hh < 2; ++hh) s[rg][hh] = mfma_bf16(qf[rg][c], kf[hh][c], s[rg][hh]);
+  };
+  // exponentials, head sums and LDS staging of one tile's scores (causal
+  // zeros are applied by the flush)
+  auto terms = [&](const f32x4_t (&s)[RG][2]) {
 #pragma unroll
     for (int rg = 0; rg < RG; ++rg) {
       float hs[2];  // in-lane head sums of the two 16-position halves
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
-        const int j = j0 + 16 * hh + r;  // this lane's position
         float acc[4];
-        if (need_mask) {
 #pragma unroll
-          for (int ii = 0; ii < 4; ++ii) {
-            const float x = __builtin_fmaf(sacc[rg][hh][ii], cs, -rl_l2[rg][ii]);
-            acc[ii] = exp2_fast(j <= rl_lim[rg][ii] ? x : kNegInf);
-          }
-        } else {
-#pragma unroll
-          for (int ii = 0; ii < 4; ++ii) acc[ii] = exp2_fast(__builtin_fmaf(sacc[rg][hh][ii], cs, -rl_l2[rg][ii]));
-        }
+        for (int ii = 0; ii < 4; ++ii) acc[ii] = exp2_fast(__builtin_fmaf(s[rg][hh][ii], cs, -rl_l2[rg][ii]));
         hs[hh] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
       }
-      if constexpr (G == 4) {  // one token per row group of lanes: no exchange
+      if constexpr (G == 4) {
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) st[(rg * TP + g4) * 32 + 16 * hh + r] = hs[hh];
       } else {
-        // the swap leaves rows 0 and 2 holding half 0's pair, rows 1 and 3
-        // half 1's: lane row g4 ends with token g4 / 2 (G = 8), half g4 % 2
         const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(hs[0]), __float_as_uint(hs[1]), false, false);
         float v = __uint_as_float(p[0]) + __uint_as_float(p[1]);
-        if constexpr (G == 16) v = sum_x32(v);  // rows 0 + 2 and 1 + 3: the token's 16 heads
+        if constexpr (G == 16) v = sum_x32(v);
         if (G == 8 || g4 < 2) st[(rg * TP + (G == 8 ? g4 >> 1 : 0)) * 32 + 16 * (g4 & 1) + r] = v;
       }
     }
-    stage_flush(j0);
   };
   // the ring's first tiles go out before the query and log-sum-exp loads,
   // and one wait covers all of them (the compiler's own wait bookkeeping then
@@ -1121,29 +1116,47 @@ __global__ void __launch_bounds__(256, 2) chunk_score_flash(ScanParams P) {
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
       const ChunkRows crr = chunk_row<RG>(P, q0, blk_w, rg, 4 * g4 + ii);
-      rl_lim[rg][ii] = crr.jlim;  // -1 for such rows
       rl_l2[rg][ii] = crr.ok ? P.lse2_in[(int64_t)unit * P.rows + 4 * g4 + ii] : __builtin_inff();
     }
   }
   wait_vm<0>();
-  // unrolled over the ring so each step's buffer is a compile-time constant
-  auto step = [&](auto buf, int n) {
-    constexpr int B = decltype(buf)::value;
-    ring_wait<NBUF, TL::PER>(n, ntile);
-    if (n + NBUF - 1 < ntile) ld.issue(tiles[(B + NBUF - 1) % NBUF], j_begin + 32 * (n + NBUF - 1), p_max);
-    compute(tiles[B], n);
-  };
-  static_assert(NBUF == 3 || NBUF == 4, "the unrolled ring below has 3 or 4 buffers");
-  for (int n = 0; n < ntile; n += NBUF) {
-    step(std::integral_constant<int, 0>{}, n);
-    if (n + 1 >= ntile) break;
-    step(std::integral_constant<int, 1>{}, n + 1);
-    if (n + 2 >= ntile) break;
-    step(std::integral_constant<int, 2>{}, n + 2);
-    if constexpr (NBUF == 4) {
-      if (n + 3 >= ntile) break;
-      step(std::integral_constant<int, NBUF - 1>{}, n + 3);
+  // software pipeline: step n issues tile n+1's QK^T (from LDS) and forms
+  // tile n's terms while those MFMAs run; its barrier makes tile n+1 visible
+  // and frees tile n's buffer for tile n+4
+  f32x4_t SA[RG][2], SB[RG][2];
+  if (ntile > 0) {
+    ring_wait<NBUF, TL::PER>(0, ntile);
+    if (NBUF - 1 < ntile) ld.issue(tiles[NBUF - 1], j_begin + 32 * (NBUF - 1), p_max);
+    qk(tiles[0], SA);
+  }
+  auto step = [&](auto buf, int n, const f32x4_t (&cur)[RG][2], f32x4_t (&nxt)[RG][2]) {
+    constexpr int B = decltype(buf)::value;  // tile n's buffer
+    ring_wait<NBUF, TL::PER>(n + 1, ntile);  // (past the last tile: an extra barrier, every wave alike)
+    if (n + NBUF < ntile) ld.issue(tiles[B], j_begin + 32 * (n + NBUF), p_max);
+    {
+      qk(tiles[(B + 1) % NBUF], nxt);  // past the last tile: a stale buffer, result unused
+      terms(cur);
+      // schedule: the K fragment reads first, then each MFMA followed by
+      // three vector instructions of the terms, so the matrix core works
+      // while the wave issues them
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * (FP8 ? RT::KW : NC), 0);  // LDS reads
+#pragma unroll
+      for (int i = 0; i < 2 * RG * NC; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // three VALU
+      }
     }
+    stage_flush(j_begin + 32 * n);
+  };
+  static_assert(NBUF == 4, "the unrolled pipeline below has 4 buffers");
+  for (int n = 0; n < ntile; n += NBUF) {
+    step(std::integral_constant<int, 0>{}, n, SA, SB);
+    if (n + 1 >= ntile) break;
+    step(std::integral_constant<int, 1>{}, n + 1, SB, SA);
+    if (n + 2 >= ntile) break;
+    step(std::integral_constant<int, 2>{}, n + 2, SA, SB);
+    if (n + 3 >= ntile) break;
+    step(std::integral_constant<int, 3>{}, n + 3, SB, SA);
   }
   // remaining tiles lie past every query position of the workgroup: zeros
   if (ntile * 32 + j_begin < j_end) {
