@@ -712,13 +712,15 @@ __device__ __forceinline__ void flash_pv(const char* vl, f32x4_t (&s)[RG][2], fl
 #pragma unroll
   for (int rg = 0; rg < RG; ++rg) {
     if (need_mask) {
+      // position j0 + 4 g4 + o with o = 16 hh + ii: compared through
+      // o > jlim - j0 - 4 g4 (and o < jlo - j0 - 4 g4), constants on one side
+      const int dhi = jlim[rg] - j0 - 4 * g4;
+      const int dlo = BAND ? jlo[rg] - j0 - 4 * g4 : 0;
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-          const int j = j0 + 16 * hh + 4 * g4 + ii;
-          if (j > jlim[rg] || (BAND && j < jlo[rg])) s[rg][hh][ii] = kNegInf;
-        }
+        for (int ii = 0; ii < 4; ++ii)
+          if (16 * hh + ii > dhi || (BAND && 16 * hh + ii < dlo)) s[rg][hh][ii] = kNegInf;
     }
     float x[2][4];
 #pragma unroll
