@@ -727,8 +727,9 @@ __device__ __forceinline__ void flash_pv(const char* vl, f32x4_t (&s)[RG][2], fl
     for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) x[hh][ii] = __builtin_fmaf(s[rg][hh][ii], cs, -S.mu[rg]);
-    const float xm = fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])),
-                           fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])));
+    // chained three-input maxima (four instructions for the eight exponents)
+    const float xm = fmaxf(fmaxf(fmaxf(fmaxf(fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), x[0][2]), x[0][3]), x[1][0]),
+                                       x[1][1]), x[1][2]), x[1][3]);
     if (__any(xm > S.thr[rg])) {
       const float rmax = max_x32(max_x16(xm));  // the row's largest exponent
       const bool move = rmax > S.thr[rg];       // uniform over the row's lanes
@@ -746,15 +747,11 @@ __device__ __forceinline__ void flash_pv(const char* vl, f32x4_t (&s)[RG][2], fl
         for (int ii = 0; ii < 4; ++ii) x[hh][ii] = __builtin_fmaf(s[rg][hh][ii], cs, -S.mu[rg]);
     }
     float pr[2][4];
-    float psum = 0.f;
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        pr[hh][ii] = exp2_fast(x[hh][ii]);
-        psum += pr[hh][ii];
-      }
-    S.l[rg] += psum;
+      for (int ii = 0; ii < 4; ++ii) pr[hh][ii] = exp2_fast(x[hh][ii]);
+    S.l[rg] += ((pr[0][0] + pr[0][1]) + (pr[0][2] + pr[0][3])) + ((pr[1][0] + pr[1][1]) + (pr[1][2] + pr[1][3]));
     pf[rg] = u32x4_t{pack_bf16(pr[0][0], pr[0][1]), pack_bf16(pr[0][2], pr[0][3]), pack_bf16(pr[1][0], pr[1][1]),
                      pack_bf16(pr[1][2], pr[1][3])};
   }
