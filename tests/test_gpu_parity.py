@@ -438,6 +438,46 @@ def test_kv_bridge_fp8_cache(hs2, T, dm, Hkv, D):
 
 # ------------------------------------------------ full layer + selection in one call
 
+CHUNK_SHORT_CASES = [
+    # kv, D, G, Hkv, B, N, Tq: the multi-query chunk path on short caches, so
+    # a workgroup's position split holds 1 to 8 tiles (the score pass's
+    # pipeline prologue, its unrolled steps and the zero tail all meet)
+    ("bf16", 128, 8, 2, 2, 32, 32),     # the cache is the chunk: one tile
+    ("bf16", 128, 8, 2, 1, 33, 32),     # two tiles, the second one position long
+    ("bf16", 64, 4, 2, 1, 100, 32),     # 4 heads per group
+    ("fp8", 128, 8, 2, 1, 129, 32),
+    ("bf16", 128, 16, 1, 2, 200, 32),   # 16 heads per group
+    ("fp8", 64, 8, 2, 1, 640, 48),
+    ("bf16", 128, 8, 1, 1, 20000, 32),  # eight tiles per split
+]
+
+
+@pytest.mark.parametrize("case", CHUNK_SHORT_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_chunk_path_short_caches(hs2, case):
+    kv, D, G, Hkv, B, N, Tq = case
+    spec = small_spec(kv, D=D, G=G, Hkv=Hkv, B=B, N=N, Tq=Tq, needles=min(8, max(0, N - 16)))
+    gu.log(f"chunk path, short cache {case}")
+    inp = synth.make_inputs(spec, seed=2468)
+    blk = gu.DeviceBlock(inp)
+    try:
+        hs2.timing_reset()
+        hs2.timing_enable(True)
+        out, lse, sc = hs2.full_attn_scores(blk.k, blk.v, blk.q, spec.q_pos0, k_scale=blk.ks, v_scale=blk.vs)
+        torch.cuda.synchronize()
+        _, n_full = hs2.timing_collect("chunk_full")
+        _, n_score = hs2.timing_collect("chunk_score")
+    finally:
+        hs2.timing_enable(False)
+        hs2.timing_reset()
+    assert n_full == 1 and n_score == 1, "expected the multi-query chunk kernels"
+    o_or, l_or, s_or = oracle_full(inp, spec)
+    e_o = gu.assert_close(gu.host(out), o_or, gu.O_TOL[kv], "out")
+    r_o = gu.assert_rows_rel(gu.host(out), o_or, kv)
+    e_l = gu.assert_lse(gu.host(lse), l_or, kv, "lse")
+    e_s = gu.assert_scores(gu.host(sc), s_or, G=G)
+    gu.log(f"  max|dO|={e_o:.2e} (row rel {r_o:.2e}) max|dLSE|={e_l:.2e} max rel dS={e_s:.2e}")
+
+
 TOPK_CASES = [
     # kv, D, G, Hkv, B, N, k, window, queries
     ("bf16", 128, 8, 4, 2, 20000, 1024, 128, "rand"),
