@@ -354,6 +354,27 @@ int full_layer(const hs2_kv_desc* kv, const void* q, hs2_dtype q_dtype, int32_t 
     return HS2_OK;
   }
 
+  // one query token per unit: the selection's rows are set up before the
+  // score pass, which counts their first digit -- this saves the selection two
+  // passes (grids of many rows take the bracketed selection, which needs
+  // neither).  bf16/FP8 caches: the scan sets the rows up and the merge runs
+  // inside the score launch; fp32: the merge kernel does both.
+  const bool pre_sel = sel != nullptr && pl.tpack == 1 &&
+                       !hs2::sel_bracketed(pl.units, (int)cdiv(kv->N, hs2::kSelChunk));
+  const bool fused_merge = pre_sel && kv->dtype != HS2_F32;
+  int32_t* sel_hist = nullptr;
+  int32_t* sel_state = nullptr;
+  if (pre_sel) {
+    const SelPlan sp = plan_select(kv->B, Tq, kv->Hkv, kv->N, 1);
+    sel_state = at<int32_t>(sel->ws, sp.off_state);
+    sel_hist = at<int32_t>(sel->ws, sp.off_hist);
+  }
+  if (fused_merge) {
+    p.sel_state = sel_state;
+    p.sel_hist = sel_hist;
+    p.sel_k = sel->k;
+    p.sel_window = sel->cand_window;
+  }
   e = hs2::launch_scan(p, kv->dtype, false, true, stream);
   if (e != hipSuccess) return hip_fail(e, "full_scan launch");
 
@@ -374,23 +395,17 @@ int full_layer(const hs2_kv_desc* kv, const void* q, hs2_dtype q_dtype, int32_t 
   c.out = out;
   c.lse = lse;
   c.lse2 = at<float>(workspace, pl.off_lse2);
-  // one query token per unit: the merge sets the selection's rows up and the
-  // score pass counts their first digit, which saves the selection two passes
-  // (grids of many rows take the bracketed selection, which needs neither)
-  const bool pre_sel = sel != nullptr && pl.tpack == 1 &&
-                       !hs2::sel_bracketed(pl.units, (int)cdiv(kv->N, hs2::kSelChunk));
-  int32_t* sel_hist = nullptr;
-  if (pre_sel) {
-    const SelPlan sp = plan_select(kv->B, Tq, kv->Hkv, kv->N, 1);
-    c.sel_state = at<int32_t>(sel->ws, sp.off_state);
-    c.sel_hist = sel_hist = at<int32_t>(sel->ws, sp.off_hist);
+  if (pre_sel && !fused_merge) {
+    c.sel_state = sel_state;
+    c.sel_hist = sel_hist;
     c.sel_k = sel->k;
     c.sel_window = sel->cand_window;
     c.q_pos0 = q_pos0;
     c.N = kv->N;
     c.qpos_b = q_pos0_b;
   }
-  if ((e = hs2::launch_combine(c, pl.units, stream)) != hipSuccess) return hip_fail(e, "combine launch");
+  if (!fused_merge && (e = hs2::launch_combine(c, pl.units, stream)) != hipSuccess)
+    return hip_fail(e, "combine launch");
 
   hs2::ScoreParams s{};
   s.lg16 = p.lg16;
@@ -420,7 +435,8 @@ int full_layer(const hs2_kv_desc* kv, const void* q, hs2_dtype q_dtype, int32_t 
   s.sn = kv->stride_n;
   s.k_scale = kv->k_scale;
   s.scale_log2 = p.scale_log2;
-  if ((e = hs2::launch_score(s, pl.units, stream)) != hipSuccess) return hip_fail(e, "score launch");
+  if ((e = hs2::launch_score(s, pl.units, stream, fused_merge ? &c : nullptr)) != hipSuccess)
+    return hip_fail(e, "score launch");
   if (pre_sel) sel->hist0_done = true;
   return HS2_OK;
 }

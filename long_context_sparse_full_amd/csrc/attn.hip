@@ -502,6 +502,9 @@ __global__ void __launch_bounds__(WAVES * 64) scan_full(ScanParams P) {
       if (i + 2 < n) compute(A, j0 + 2 * jstride);
     }
   }
+  if (P.sel_state && split == 0)  // tpack = 1: unit = selection row (b, t, g), query position q0 + tp
+    sel_init_row(P.sel_state + (int64_t)unit * ST_WORDS, P.sel_hist + (int64_t)unit * 3 * kHistBins, q0 + tp,
+                 P.sel_k, P.sel_window, 1, threadIdx.x, WAVES * 64);
   merge_and_store<FP8, D, false, WAVES>(P, S, unit, split, b, g, wave, r, g4, sm_m, sm_l, sm_o);
 }
 
@@ -1623,26 +1626,34 @@ __device__ __forceinline__ void sel_init_unit_rows(const CombineParams& P, int b
   }
 }
 
-// grid (unit, row, head-dim chunk of 32): every workgroup recomputes the split
-// weights 2^(m_s - M) into LDS, then 8 groups of 32 threads sum interleaved
-// splits, each thread's loads issued 32 at a time.
-__global__ void __launch_bounds__(256) combine(CombineParams P) {
-  __shared__ float sw[kMaxSplits];
-  __shared__ float sl[kMaxSplits];
-  __shared__ float red[8];
-  __shared__ float part[256];
-  const int unit = blockIdx.x, r = blockIdx.y, tid = threadIdx.x;
+// LDS of one merging workgroup: split weights and sums, reduction slots, the
+// per-thread partial sums
+struct CombineLds {
+  float sw[kMaxSplits];
+  float sl[kMaxSplits];
+  float red[8];
+  float part[256];
+};
+
+// Merge of row r, head dims [32 z, 32 z + 32) of a unit by one workgroup:
+// the split weights 2^(m_s - M) into LDS, then 8 groups of 32 threads sum
+// interleaved splits, each thread's loads issued 32 at a time.
+__device__ __forceinline__ void combine_row(const CombineParams& P, int unit, int r, int z, CombineLds& L_) {
+  float* sw = L_.sw;
+  float* sl = L_.sl;
+  float* red = L_.red;
+  float* part = L_.part;
+  const int tid = threadIdx.x;
   const int g = unit % P.Hkv;
   const int tp = (unit / P.Hkv) % P.n_tpacks;
   const int b = unit / (P.Hkv * P.n_tpacks);
   const int tl = r / P.G, i = r - tl * P.G;
   const int t = tp * P.tpack + tl;
-  if (P.sel_state && r == 0 && blockIdx.z == 0) sel_init_unit_rows(P, b, tp, g, tid);
   if (t >= P.Tq) return;
   const int h = g * P.G + i;
   const float* ml = P.part_ml + ((int64_t)unit * P.nsplit * 16 + r) * 2;
   const int dl = tid & 31, pp = tid >> 5;
-  const int d = blockIdx.z * 32 + dl;
+  const int d = z * 32 + dl;
   const float* po = P.part_o + ((int64_t)unit * P.nsplit * 16 + r) * P.D + d;
   const int64_t sstride = (int64_t)16 * P.D;
   // This thread sums splits pp, pp + 8, ... in batches of CB whose loads are
@@ -1700,6 +1711,19 @@ __global__ void __launch_bounds__(256) combine(CombineParams P) {
     if (P.lse) P.lse[orow] = l2 * kLn2;
     P.lse2[(int64_t)unit * P.rows + r] = l2;
   }
+}
+
+// grid (unit, row, head-dim chunk of 32)
+__global__ void __launch_bounds__(256) combine(CombineParams P) {
+  __shared__ CombineLds L_;
+  const int unit = blockIdx.x, r = blockIdx.y;
+  if (P.sel_state && r == 0 && blockIdx.z == 0) {
+    const int g = unit % P.Hkv;
+    const int tp = (unit / P.Hkv) % P.n_tpacks;
+    const int b = unit / (P.Hkv * P.n_tpacks);
+    sel_init_unit_rows(P, b, tp, g, threadIdx.x);
+  }
+  combine_row(P, unit, r, blockIdx.z, L_);
 }
 
 // The same merge for many units with few splits each (the chunk path: a
@@ -1805,14 +1829,15 @@ __device__ __forceinline__ float recompute_logit(const ScoreParams& P, int b, in
 // The terms of position j (j <= p) whose codes saturated, for row group tl
 // (token t) of a unit: exact where the probability of the code's tile maximum
 // exceeds 2^kExactFloor, zero otherwise -- the terms the code-based sum took
-// as zero.
-__device__ __forceinline__ float saturated_terms(const ScoreParams& P, int unit, int b, int t, int tl, int g, int j) {
+// as zero.  l2u: the unit's rows' log2-domain LSE.
+__device__ __forceinline__ float saturated_terms(const ScoreParams& P, int unit, int b, int t, int tl, int g, int j,
+                                                 const float* l2u) {
   float add = 0.f;
   for (int i = 0; i < P.G; ++i) {
     const int rr = tl * P.G + i;
     const int64_t row = (int64_t)unit * P.rows + rr;
     if (P.lg16[row * P.npad + j] != 65535u) continue;
-    const float l2 = P.lse2[row];
+    const float l2 = l2u[rr];
     const float c = P.lgmax[((int64_t)unit * (P.npad >> 5) + (j >> 5)) * P.rows + rr] - l2;
     if (!(c > kExactFloor)) continue;
     add += exp2_fast(recompute_logit(P, b, t, g * P.G + i, g, j) - l2);
@@ -1852,7 +1877,7 @@ __global__ void __launch_bounds__(256) score(ScoreParams P) {
       }
       if (exact) {  // rare: a tile holding a dominant logit and terms 16+ log2 units below it
         for (int e = 0; e < 4; ++e)
-          if (j4 + e <= p) s[e] += saturated_terms(P, unit, b, t, tl, g, j4 + e);
+          if (j4 + e <= p) s[e] += saturated_terms(P, unit, b, t, tl, g, j4 + e, P.lse2 + (int64_t)unit * P.rows);
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e)
@@ -1867,6 +1892,58 @@ __global__ void __launch_bounds__(256) score(ScoreParams P) {
   }
 }
 
+// The log2-domain LSE of every row of a unit from the scan's split partials
+// (max, sum), the quantity the merge computes (summed in another order): wave
+// w takes rows w, w + 4, w + 8, w + 12, each lane every 64th split with an
+// online (max, sum); the loads of four splits of all four rows are issued
+// together.  Ends with a barrier that publishes s_l2[rows].
+__device__ __forceinline__ void unit_lse2(const float* part_ml, int unit, int nsplit, int rows, float* s_l2) {
+  constexpr int QS = 4;  // splits per lane per batch
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const float* ml0 = part_ml + (int64_t)unit * nsplit * 32;
+  float m[4], l[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    m[k] = kNegInf;
+    l[k] = 0.f;
+  }
+  for (int s0 = 0; s0 < nsplit; s0 += 64 * QS) {
+    float mv[4][QS], lv[4][QS];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+      for (int q = 0; q < QS; ++q) {
+        const int r = wave + 4 * k, sp = s0 + lane + 64 * q;
+        const bool ok = r < rows && sp < nsplit;
+        const float* e = ml0 + ((int64_t)sp * 16 + r) * 2;
+        mv[k][q] = ok ? e[0] : kNegInf;
+        lv[k][q] = ok ? e[1] : 0.f;
+      }
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+      for (int q = 0; q < QS; ++q) {
+        const float mn = fmaxf(m[k], mv[k][q]);
+        if (mn != kNegInf) {
+          l[k] = l[k] * exp2f(m[k] - mn) + lv[k][q] * exp2f(mv[k][q] - mn);
+          m[k] = mn;
+        }
+      }
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    float M = m[k];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+    float L = (M == kNegInf) ? 0.f : l[k] * exp2f(m[k] - M);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) L += __shfl_xor(L, o);
+    const int r = wave + 4 * k;
+    if (lane == 0 && r < rows) s_l2[r] = (L > 0.f) ? M + log2f(L) : kNegInf;
+  }
+  __syncthreads();
+}
+
 // The score pass of a decode step whose selection follows (one query token
 // per unit): the scores as above, R groups of 4 positions per thread (1024 R
 // positions per workgroup), and the first radix digit of every candidate's
@@ -1874,15 +1951,34 @@ __global__ void __launch_bounds__(256) score(ScoreParams P) {
 // workgroup, flushed with one global atomic per non-empty digit).  Counts are
 // integers, so the histogram equals the one the selection's own first pass
 // would build from the stored scores.
-template <int R, int GC>
-__global__ void __launch_bounds__(256) score_hist(ScoreParams P) {
-  __shared__ int32_t h[kHistBins];
+// MERGE: the full layer's merge runs in the same launch.  The first
+// rows * D/32 workgroups of each unit merge one (row, 32 head dims) each
+// (outputs, LSE), and every score workgroup derives its rows' LSE from the
+// split partials itself while its first code loads are in flight; the
+// selection rows were set up by the scan.
+template <int R, int GC, bool MERGE>
+__global__ void __launch_bounds__(256) score_hist(ScoreParams P, CombineParams C) {
+  __shared__ union {
+    int32_t h[kHistBins];
+    CombineLds c;
+  } U;
+  __shared__ float s_l2[16];
+  int32_t* h = U.h;
   const int unit = blockIdx.y;
+  int bx = blockIdx.x;
+  if constexpr (MERGE) {
+    const int ncomb = C.rows * (C.D / 32);
+    if (bx < ncomb) {
+      combine_row(C, unit, bx / (C.D / 32), bx % (C.D / 32), U.c);
+      return;
+    }
+    bx -= ncomb;
+  }
   const int g = unit % P.Hkv;
   const int t = (unit / P.Hkv) % P.n_tpacks;  // tpack = 1
   const int b = unit / (P.Hkv * P.n_tpacks);
   const int p = qpos_of(P.qpos_b, P.q_pos0, b, P.N, P.Tq) + t;
-  const int base = blockIdx.x * 1024 * R;
+  const int base = bx * 1024 * R;
   const int ncand = sel_ncand(p, P.sel_window);
   const int take = sel_take(ncand, P.sel_k, 1);
   float* dst = P.scores + (((int64_t)b * P.Tq + t) * P.Hkv + g) * P.N;
@@ -1902,41 +1998,57 @@ __global__ void __launch_bounds__(256) score_hist(ScoreParams P) {
       for (int e = 0; e < 4; ++e) s[q][e] += code_term(code[e], c, exact);
     }
   };
+  // the unit's rows' LSE: from the merge, or derived here after the first
+  // code loads have been issued
+  auto row_lse = [&]() -> const float* {
+    if constexpr (MERGE) {
+      unit_lse2(C.part_ml, unit, C.nsplit, P.rows, s_l2);
+      return s_l2;
+    } else {
+      return P.lse2 + (int64_t)unit * P.rows;
+    }
+  };
+  const float* l2u;
   if constexpr (GC > 0) {
     // every head's loads issued before any is used: one memory round trip
     u32x2_t w[GC][R];
-    float mx[GC][R], l2[GC];
+    float mx[GC][R];
 #pragma unroll
     for (int i = 0; i < GC; ++i) {
       const int64_t row = (int64_t)unit * P.rows + i;
-      l2[i] = P.lse2[row];
 #pragma unroll
       for (int q = 0; q < R; ++q) {
         w[i][q] = *(const u32x2_t*)(P.lg16 + row * P.npad + (jc[q] & ~3));
         mx[i][q] = P.lgmax[((int64_t)unit * (P.npad >> 5) + (jc[q] >> 5)) * P.rows + i];
       }
     }
+    l2u = row_lse();
 #pragma unroll
-    for (int i = 0; i < GC; ++i) add_head(w[i], mx[i], l2[i]);
+    for (int i = 0; i < GC; ++i) add_head(w[i], mx[i], l2u[i]);
   } else {
     // head-outer, group-inner: each head's loads for all R groups together
-    for (int i = 0; i < P.G; ++i) {
+    u32x2_t w[R];
+    float mx[R];
+    auto load_head = [&](int i) {
       const int64_t row = (int64_t)unit * P.rows + i;
-      u32x2_t w[R];
-      float mx[R];
 #pragma unroll
       for (int q = 0; q < R; ++q) {
         w[q] = *(const u32x2_t*)(P.lg16 + row * P.npad + (jc[q] & ~3));
         mx[q] = P.lgmax[((int64_t)unit * (P.npad >> 5) + (jc[q] >> 5)) * P.rows + i];
       }
-      add_head(w, mx, P.lse2[row]);
+    };
+    load_head(0);
+    l2u = row_lse();
+    for (int i = 0; i < P.G; ++i) {
+      if (i > 0) load_head(i);
+      add_head(w, mx, l2u[i]);
     }
   }
   if (exact) {  // rare: a tile holding a dominant logit and terms 16+ log2 units below it
     for (int q = 0; q < R; ++q) {
       const int j4 = base + 4 * (threadIdx.x + 256 * q);
       for (int e = 0; e < 4; ++e)
-        if (j4 + e <= p) s[q][e] += saturated_terms(P, unit, b, t, 0, g, j4 + e);
+        if (j4 + e <= p) s[q][e] += saturated_terms(P, unit, b, t, 0, g, j4 + e, l2u);
     }
   }
   uint32_t key[4 * R];
@@ -2246,7 +2358,7 @@ hipError_t launch_combine(const CombineParams& p, int units, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_score(const ScoreParams& p, int units, hipStream_t s) {
+hipError_t launch_score(const ScoreParams& p, int units, hipStream_t s, const CombineParams* merge) {
   TimedLaunch tl("score", s);
   if (p.sel_hist) {
     if (p.tpack != 1) return hipErrorInvalidValue;
@@ -2254,13 +2366,19 @@ hipError_t launch_score(const ScoreParams& p, int units, hipStream_t s) {
     // thread and one head's loads at a time.  Small grids (latency-bound,
     // fewer workgroups than CUs): 2 groups per thread and, for 8 heads per
     // group, every head's loads at once (measured at 1M: 24.0 against 25.6 us;
-    // at 32K: 11.2 against 14.5 us).
+    // at 32K: 11.2 against 14.5 us).  With the merge folded in, its
+    // rows * D/32 workgroups per unit come first.
+    const CombineParams c = merge ? *merge : CombineParams{};
+    const int ncomb = merge ? c.rows * (c.D / 32) : 0;
+    if (merge && (c.D % 32 || c.nsplit > kMaxSplits)) return hipErrorInvalidValue;
     const int blocks4 = (p.N + 4095) / 4096;
     if ((int64_t)blocks4 * units >= 512 || p.G != 8) {
-      hipLaunchKernelGGL((score_hist<4, 0>), dim3(blocks4, units), dim3(256), 0, s, p);
+      if (merge) hipLaunchKernelGGL((score_hist<4, 0, true>), dim3(ncomb + blocks4, units), dim3(256), 0, s, p, c);
+      else hipLaunchKernelGGL((score_hist<4, 0, false>), dim3(blocks4, units), dim3(256), 0, s, p, c);
     } else {
       const int blocks2 = (p.N + 2047) / 2048;
-      hipLaunchKernelGGL((score_hist<2, 8>), dim3(blocks2, units), dim3(256), 0, s, p);
+      if (merge) hipLaunchKernelGGL((score_hist<2, 8, true>), dim3(ncomb + blocks2, units), dim3(256), 0, s, p, c);
+      else hipLaunchKernelGGL((score_hist<2, 8, false>), dim3(blocks2, units), dim3(256), 0, s, p, c);
     }
   } else {
     const int blocks = (p.N + 1023) / 1024;

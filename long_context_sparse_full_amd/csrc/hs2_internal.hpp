@@ -62,6 +62,13 @@ struct ScanParams {
   // multi-query chunk path: log2-domain LSE per (unit, row) from the merge,
   // read by the score pass
   const float* lse2_in;
+  // full layer with the token selection after it, one query token per unit
+  // (tpack = 1): the scan's first split of each unit sets the unit's
+  // selection row up (state words, digit histograms cleared) as the
+  // selection's own set-up would; sel_state nullptr = none
+  int32_t* sel_state;
+  int32_t* sel_hist;
+  int sel_k, sel_window;
 };
 
 // Multi-query chunk path: a workgroup of 4 waves, each holding kFlashRG
@@ -190,7 +197,9 @@ hipError_t launch_gather_split(const ScanParams& p, int kv_dtype, hipStream_t s)
 hipError_t launch_chunk_full(const ScanParams& p, int kv_dtype, hipStream_t s);
 hipError_t launch_chunk_score(const ScanParams& p, int kv_dtype, hipStream_t s);
 hipError_t launch_combine(const CombineParams& p, int units, hipStream_t s);
-hipError_t launch_score(const ScoreParams& p, int units, hipStream_t s);
+// merge != nullptr (selection with one query token per unit, bf16/FP8): the
+// full layer's merge runs inside the score launch.
+hipError_t launch_score(const ScoreParams& p, int units, hipStream_t s, const CombineParams* merge = nullptr);
 hipError_t launch_select(const SelectParams& p, hipStream_t s);
 // K/V bridge outputs: per layer, the cache of one batch entry (row n of head
 // h at k/v + h*sh + n*sn), new rows from pos0 on; FP8 caches pass that batch
