@@ -152,8 +152,7 @@ SelPlan plan_select(int B, int Tq, int Hkv, int N, int block_size) {
     off = a256(off + (size_t)p.units * 3 * hs2::kHistBins * sizeof(int32_t));
     p.off_cnt = off;
     off = a256(off + (size_t)p.units * p.nchunks * 258 * sizeof(int32_t));
-    p.off_cand = off;  // the fused emit's per-chunk lists (k <= kC24Take)
-    if (p.nchunks <= hs2::kC24MaxChunks) off = a256(off + (size_t)p.units * p.nchunks * hs2::kC24Words * sizeof(int32_t));
+    p.off_cand = off;
   } else if (block_size == 1) {  // bracketed: each chunk's per-wave list lengths and lists
     p.off_hist = off;
     p.off_cnt = off;

@@ -104,17 +104,6 @@ constexpr int kBracketStride = 16;
 // chunks per row the bracketed path's finishing step gathers from (rows of
 // up to 4M candidates; longer rows take the per-row kernel)
 constexpr int kFinishMaxChunks = 256;
-// radix path, last step (k up to kC24Take): per chunk, the positions of its
-// keys above the 24-bit prefix of the k-th key (fewer than k in the whole row)
-// and up to kC24Eq positions and keys sharing that prefix, after two list
-// lengths; the row's last workgroup takes up to kC24EqTotal shared-prefix keys
-// on chip, from rows of up to kC24MaxChunks chunks
-constexpr int kC24Take = 2048;
-constexpr int kC24Eq = 512;
-constexpr int kC24EqTotal = 2048;
-constexpr int kC24MaxChunks = 256;
-constexpr int kC24Words = 2 + kC24Take + 2 * kC24Eq;
-__host__ __device__ inline bool sel_fused_emit(int k, int nchunks) { return k <= kC24Take && nchunks <= kC24MaxChunks; }
 __host__ __device__ inline bool sel_bracketed(int units, int nchunks) {
   return (int64_t)units * nchunks >= kSelMinWorkgroups;
 }
@@ -182,8 +171,7 @@ struct SelectParams {
   int32_t* hist;    // [units][3][4096] digit histograms of the three passes
   int32_t* cnt;     // radix path: [units][nchunks][258]: keys above the 24-bit prefix, suffix sums of the
                     // last digit; bracketed path: [units][nchunks][4 waves][2] list lengths
-  int32_t* cand;    // bracketed path: [units][nchunks][kCandWords] each chunk's lists, a quarter per wave;
-                    // radix path: [units][nchunks][kC24Words] each chunk's lists for the fused emit
+  int32_t* cand;    // bracketed path: [units][nchunks][kCandWords] each chunk's lists, a quarter per wave
   double* bmass;    // [units][nblocks_max] (block mode)
   int nblocks_max;
   int pre_hist0;    // token mode: state and pass-0 histogram already built (merge + score pass)

@@ -12,10 +12,7 @@
 // keys that share the digits found so far.  Histograms use integer atomics
 // only, so every count -- and therefore the selection -- is deterministic.
 // The emit pass keeps every key above the threshold and the lowest-positioned
-// keys equal to it, compacted in ascending position order.  For k up to
-// kC24Take the third digit's pass and the emit are one pass: each chunk lists
-// its keys above the 24-bit prefix and those sharing it, and the row's last
-// workgroup settles the last 8 bits on chip and writes the list.
+// keys equal to it, compacted in ascending position order.
 //
 // Bracketed path (grids of many rows, where the passes are throughput-bound):
 // a fixed sample of each row -- every SR-th run of 64 positions, at most
@@ -925,52 +922,11 @@ __global__ void __launch_bounds__(256) sel_emit(SelectParams P) {
   emit_chunk(K, base, tau, need, eq_before, sel_before, take, out, sm, eq_c, sel_c);
 }
 
-// The `take` highest of row u's ncand candidate keys by one workgroup, in
-// ascending position order at out[0, take): three radix digits over the row
-// (each pass reads it once; digits of 12, 12 and 8 bits as in the
-// multi-workgroup passes), then the ordered compaction chunk by chunk with
-// running counts.  h: kHistBins ints of LDS.
-__device__ void row_exact_radix(const SelectParams& P, int u, int ncand, int take, int32_t* out, int32_t* h,
-                                int32_t* sm) {
-  const float* row = P.scores + (int64_t)u * P.N;
-  const bool vec_ok = (P.N & 3) == 0;
-  int need = take;
-  uint32_t prefix = 0;
-  // one pass per digit: the LDS histogram of the keys sharing the digits so far
-  auto count = [&](auto pass_tag) {
-    constexpr int PASS = decltype(pass_tag)::value;
-    for (int i = threadIdx.x; i < kHistBins; i += 256) h[i] = 0;
-    __syncthreads();
-#pragma unroll 1
-    for (int base = 0; base < ncand; base += kSelChunk) {
-      ChunkKeys K;
-      load_keys_runs(row, base, min(base + kSelChunk, ncand), vec_ok, K);
-      hist_keys<PASS>(K, prefix, h);
-    }
-    __syncthreads();
-    int d, above;
-    find_digit<PASS>(h, need, sm, d, above);
-    prefix |= (uint32_t)d << Digit<PASS>::SHIFT;
-    need -= above;
-  };
-  count(std::integral_constant<int, 0>());
-  count(std::integral_constant<int, 1>());
-  count(std::integral_constant<int, 2>());
-  // prefix is now the k-th key tau; need of the keys equal to it are taken
-  int32_t eq_before = 0, sel_before = 0;
-#pragma unroll 1
-  for (int base = 0; base < ncand; base += kSelChunk) {
-    ChunkKeys K;
-    load_keys_runs(row, base, min(base + kSelChunk, ncand), vec_ok, K);
-    int32_t eq_c, sel_c;
-    emit_chunk(K, base, prefix, need, eq_before, sel_before, take, out, sm, eq_c, sel_c);
-    eq_before += eq_c;
-    sel_before += sel_c;
-  }
-}
-
 // A row the bracketed path did not settle -- and every row that takes all or
-// none of its candidates -- done by one workgroup, then the window.
+// none of its candidates -- done by one workgroup: the three radix digits
+// over the row's candidates (each pass reads the row once; digits of 12, 12
+// and 8 bits as in the multi-workgroup passes), then the ordered compaction
+// chunk by chunk with running counts, then the window.
 __global__ void __launch_bounds__(256) sel_row_exact(SelectParams P) {
   __shared__ int32_t h[kHistBins];
   __shared__ int32_t sm[264];
@@ -983,256 +939,41 @@ __global__ void __launch_bounds__(256) sel_row_exact(SelectParams P) {
   if (mode == MODE_ALL) {
     for (int j = threadIdx.x; j < ncand; j += 256) out[j] = j;
   } else if (mode == MODE_RADIX) {
-    row_exact_radix(P, u, ncand, take, out, h, sm);
-  }
-  write_window(P, u, take, p, out);
-}
-
-// Device-coherent accesses for the fused emit's lists, which the row's last
-// workgroup reads (another workgroup of the same launch, possibly on another
-// XCD with its own L2).
-__device__ __forceinline__ void st_dev(int32_t* p, int32_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ int32_t ld_dev(const int32_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Radix path, last step for k <= kC24Take (fuses the third digit's histogram
-// with the emit).  One workgroup per chunk of a row settles the second digit
-// -- the 24-bit prefix P24 of the k-th key -- and writes, each in ascending
-// position order, the positions of its keys above P24 (all taken) and the
-// positions and keys of those sharing P24 to lists it owns.  The workgroup
-// that finishes last for the row (a device-scope count of finished chunks,
-// cleared by the set-up; fenced on both sides) takes the shared-prefix keys
-// on chip, finds the k-th key tau among them by its last 8 bits, keeps those
-// above tau and the lowest-positioned of those equal to it, and writes the
-// row's list: both parts merged in position order, then the window.  A row
-// whose shared-prefix keys overflow their lists is finished by that
-// workgroup running the radix select over the row alone.
-__global__ void __launch_bounds__(256) sel_collect24(SelectParams P) {
-  constexpr int EPT = kC24EqTotal / 256;  // shared-prefix keys per thread on chip
-  // shared-prefix positions, keys, taken positions, then the positions above
-  // P24 (or the fallback's histogram)
-  __shared__ int32_t lds[3 * kC24EqTotal + kC24Take];
-  __shared__ int32_t s_sa[kC24MaxChunks], s_sb[kC24MaxChunks];
-  __shared__ int32_t h8[256];
-  __shared__ int32_t sm[272];
-  __shared__ int32_t s_last;
-  static_assert(3 * kC24EqTotal >= kHistBins, "fallback histogram");
-  const int u = blockIdx.y, chunk = blockIdx.x, tid = threadIdx.x;
-  int32_t* st = P.state + (int64_t)u * ST_WORDS;
-  const int p = row_pos(P, u);
-  const int ncand = sel_ncand(p, P.cand_window), take = sel_take(ncand, P.k, 1);
-  const int mode = sel_mode(take, ncand, 1);
-  int32_t* out = P.idx + (int64_t)u * P.max_sel;
-  const int base = chunk * kSelChunk;
-  if (mode != MODE_RADIX) {  // all or none of the candidates
-    if (chunk == 0) write_window(P, u, take, p, out);
-    if (mode == MODE_ALL)
-      for (int j = base + tid; j < min(base + kSelChunk, ncand); j += 256) out[j] = j;
-    return;
-  }
-  if (base >= ncand) return;
-  const int nch = (ncand + kSelChunk - 1) / kSelChunk;
-  const int end = min(base + kSelChunk, ncand);
-  ChunkKeys K;
-  load_keys_runs(P.scores + (int64_t)u * P.N, base, end, (P.N & 3) == 0, K);
-  int d, above;
-  find_digit<1>(P.hist + ((int64_t)u * 3 + 1) * kHistBins, st[ST_NEED1], sm, d, above);
-  const uint32_t pre = ((uint32_t)st[ST_PREFIX1] >> 8) | (uint32_t)d;  // key >> 8 of the k-th key
-
-  // hit masks of the two lists per round of 16 consecutive positions, their
-  // counts packed two rounds to a word, exclusive prefix sums over the threads
-  uint32_t ma[4], mb[4];
-#pragma unroll
-  for (int rnd = 0; rnd < 4; ++rnd) {
-    ma[rnd] = mb[rnd] = 0u;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int i = rnd * 16 + e;
-      const bool ok = K.valid >> i & 1;
-      const uint32_t k8 = K.key[i] >> 8;
-      ma[rnd] |= (uint32_t)(ok && k8 > pre) << e;
-      mb[rnd] |= (uint32_t)(ok && k8 == pre) << e;
-    }
-  }
-  int32_t v[4] = {__builtin_popcount(ma[0]) | (__builtin_popcount(ma[1]) << 16),
-                  __builtin_popcount(ma[2]) | (__builtin_popcount(ma[3]) << 16),
-                  __builtin_popcount(mb[0]) | (__builtin_popcount(mb[1]) << 16),
-                  __builtin_popcount(mb[2]) | (__builtin_popcount(mb[3]) << 16)},
-          t[4];
-  block_exclusive_scan_n<4>(v, sm, t);
-  int32_t* lists = P.cand + ((int64_t)u * P.nchunks + chunk) * kC24Words;
-  int32_t* la = lists + 2;
-  int32_t* lbp = la + kC24Take;
-  int32_t* lbk = lbp + kC24Eq;
-  int32_t oa = 0, ob = 0;
-#pragma unroll
-  for (int rnd = 0; rnd < 4; ++rnd) {
-    const int f = (rnd & 1) * 16, w = rnd >> 1;
-    int32_t sa = oa + ((v[w] >> f) & 0xffff), sb = ob + ((v[2 + w] >> f) & 0xffff);
-    oa += (t[w] >> f) & 0xffff;
-    ob += (t[2 + w] >> f) & 0xffff;
-    if (ma[rnd] | mb[rnd]) {
-      const int j0 = base + rnd * 4096 + tid * 16;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        if (ma[rnd] >> e & 1) {
-          if (sa < kC24Take) st_dev(la + sa, j0 + e);
-          ++sa;
-        }
-        if (mb[rnd] >> e & 1) {
-          if (sb < kC24Eq) {
-            st_dev(lbp + sb, j0 + e);
-            st_dev(lbk + sb, (int32_t)K.key[rnd * 16 + e]);
-          }
-          ++sb;
-        }
+    const float* row = P.scores + (int64_t)u * P.N;
+    const bool vec_ok = (P.N & 3) == 0;
+    int need = take;
+    uint32_t prefix = 0;
+    // one pass per digit: the LDS histogram of the keys sharing the digits so far
+    auto count = [&](auto pass_tag) {
+      constexpr int PASS = decltype(pass_tag)::value;
+      for (int i = threadIdx.x; i < kHistBins; i += 256) h[i] = 0;
+      __syncthreads();
+#pragma unroll 1
+      for (int base = 0; base < ncand; base += kSelChunk) {
+        ChunkKeys K;
+        load_keys_runs(row, base, min(base + kSelChunk, ncand), vec_ok, K);
+        hist_keys<PASS>(K, prefix, h);
       }
+      __syncthreads();
+      int d, above;
+      find_digit<PASS>(h, need, sm, d, above);
+      prefix |= (uint32_t)d << Digit<PASS>::SHIFT;
+      need -= above;
+    };
+    count(std::integral_constant<int, 0>());
+    count(std::integral_constant<int, 1>());
+    count(std::integral_constant<int, 2>());
+    // prefix is now the k-th key tau; need of the keys equal to it are taken
+    int32_t eq_before = 0, sel_before = 0;
+#pragma unroll 1
+    for (int base = 0; base < ncand; base += kSelChunk) {
+      ChunkKeys K;
+      load_keys_runs(row, base, min(base + kSelChunk, ncand), vec_ok, K);
+      int32_t eq_c, sel_c;
+      emit_chunk(K, base, prefix, need, eq_before, sel_before, take, out, sm, eq_c, sel_c);
+      eq_before += eq_c;
+      sel_before += sel_c;
     }
-  }
-  if (tid == 0) {
-    st_dev(lists, oa);
-    st_dev(lists + 1, ob);
-  }
-  // arrival: every wave's list stores complete, then one release fence
-  // before the count of finished chunks
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (tid == 0) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    s_last = atomicAdd(&st[ST_ARRIVE], 1) == nch - 1;
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-
-  // the row's last workgroup: list lengths, their exclusive prefix sums, totals
-  const int32_t* l0 = P.cand + (int64_t)u * P.nchunks * kC24Words;
-  int32_t na = 0, nb = 0, over = 0;
-  for (int c0 = 0; c0 < nch; c0 += 256) {
-    const int c = c0 + tid;
-    const int32_t ca = c < nch ? ld_dev(l0 + (int64_t)c * kC24Words) : 0;
-    const int32_t cb = c < nch ? ld_dev(l0 + (int64_t)c * kC24Words + 1) : 0;
-    int32_t w3[3] = {ca, cb, (ca < 0) | (cb < 0) | (ca > kC24Take) | (cb > kC24Eq)}, t3[3];
-    block_exclusive_scan_n<3>(w3, sm, t3);
-    if (c < nch) {
-      s_sa[c] = na + w3[0];
-      s_sb[c] = nb + w3[1];
-    }
-    na += t3[0];
-    nb += t3[1];
-    over += t3[2];
-  }
-  __syncthreads();
-  const int need = take - na;  // keys taken from the shared-prefix list
-  if (over || nb > kC24EqTotal || need < 1 || need > nb) {
-    row_exact_radix(P, u, ncand, take, out, lds, sm);
-    write_window(P, u, take, p, out);
-    return;
-  }
-  // entry i of a list lies in the last chunk whose start is <= i
-  auto chunk_of = [&](const int32_t* starts, int i) {
-    int lo = 0, hi = nch - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (starts[mid] <= i) lo = mid;
-      else hi = mid - 1;
-    }
-    return lo;
-  };
-  // both lists on chip, every load issued before any is used (one memory
-  // round trip): entries tid + 256 q
-  int32_t* bpos = lds;
-  int32_t* bkey = lds + kC24EqTotal;
-  int32_t* tsel = lds + 2 * kC24EqTotal;
-  int32_t* apos = lds + 3 * kC24EqTotal;
-  constexpr int QA = kC24Take / 256, QB = kC24EqTotal / 256;
-  int32_t av[QA], bv[QB], bw[QB];
-#pragma unroll
-  for (int q = 0; q < QA; ++q) {
-    const int i = tid + 256 * q;
-    av[q] = 0;
-    if (i < na) {
-      const int c = chunk_of(s_sa, i);
-      av[q] = ld_dev(l0 + (int64_t)c * kC24Words + 2 + (i - s_sa[c]));
-    }
-  }
-#pragma unroll
-  for (int q = 0; q < QB; ++q) {
-    const int i = tid + 256 * q;
-    bv[q] = bw[q] = 0;
-    if (i < nb) {
-      const int c = chunk_of(s_sb, i);
-      const int32_t* lc = l0 + (int64_t)c * kC24Words + 2 + kC24Take + (i - s_sb[c]);
-      bv[q] = ld_dev(lc);
-      bw[q] = ld_dev(lc + kC24Eq);
-    }
-  }
-#pragma unroll
-  for (int q = 0; q < QA; ++q)
-    if (tid + 256 * q < na) apos[tid + 256 * q] = av[q];
-#pragma unroll
-  for (int q = 0; q < QB; ++q)
-    if (tid + 256 * q < nb) {
-      bpos[tid + 256 * q] = bv[q];
-      bkey[tid + 256 * q] = bw[q];
-    }
-  h8[tid] = 0;
-  __syncthreads();
-  for (int i = tid; i < nb; i += 256) atomicAdd(&h8[(uint32_t)bkey[i] & 0xFFu], 1);
-  __syncthreads();
-  int d2, above2;
-  find_digit<2>(h8, need, sm, d2, above2);
-  const uint32_t tau = (pre << 8) | (uint32_t)d2;
-  const int need_eq = need - above2;  // keys equal to tau taken, lowest positions first
-  // thread T holds shared-prefix entries [EPT T, EPT T + EPT) (position order)
-  int32_t neq = 0;
-#pragma unroll
-  for (int e = 0; e < EPT; ++e) {
-    const int i = tid * EPT + e;
-    neq += i < nb && (uint32_t)bkey[i] == tau;
-  }
-  int32_t tot;
-  int32_t r_eq = block_exclusive_scan<int32_t>(neq, sm, tot);
-  uint32_t msel = 0;
-#pragma unroll
-  for (int e = 0; e < EPT; ++e) {
-    const int i = tid * EPT + e;
-    if (i < nb) {
-      const uint32_t key = (uint32_t)bkey[i];
-      bool tk = key > tau;
-      if (key == tau) tk = r_eq++ < need_eq;
-      msel |= (uint32_t)tk << e;
-    }
-  }
-  int32_t s0 = block_exclusive_scan<int32_t>(__builtin_popcount(msel), sm, tot);
-#pragma unroll
-  for (int e = 0; e < EPT; ++e)
-    if (msel >> e & 1) tsel[s0++] = bpos[tid * EPT + e];
-  __syncthreads();
-  // out[0, take): the na positions above P24 and the need taken shared-prefix
-  // positions, each ascending, merged by their ranks in the other list
-  for (int i = tid; i < na; i += 256) {
-    const int32_t a = apos[i];
-    int lo = 0, hi = need;
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (tsel[mid] < a) lo = mid + 1;
-      else hi = mid;
-    }
-    out[i + lo] = a;
-  }
-  for (int s = tid; s < need; s += 256) {
-    const int32_t b = tsel[s];
-    int lo = 0, hi = na;
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (apos[mid] < b) lo = mid + 1;
-      else hi = mid;
-    }
-    out[lo + s] = b;
   }
   write_window(P, u, take, p, out);
 }
@@ -1593,13 +1334,9 @@ hipError_t launch_select(const SelectParams& p_in, hipStream_t s) {
     }
     if (small) HS2_L("select_hist", (sel_hist<1, true>), grid_c);
     else HS2_L("select_hist", (sel_hist<1, false>), grid_c);
-    if (sel_fused_emit(p.k, p.nchunks)) {  // third digit and emit in one pass, finished on chip
-      HS2_L("select_emit", sel_collect24, grid_c);
-    } else {
-      if (small) HS2_L("select_hist", (sel_hist<2, true>), grid_c);
-      else HS2_L("select_hist", (sel_hist<2, false>), grid_c);
-      HS2_L("select_emit", sel_emit, grid_c);
-    }
+    if (small) HS2_L("select_hist", (sel_hist<2, true>), grid_c);
+    else HS2_L("select_hist", (sel_hist<2, false>), grid_c);
+    HS2_L("select_emit", sel_emit, grid_c);
     if (p.competes) HS2_L("select_window", sel_window_merge, dim3(p.units));
   } else {
     const dim3 grid_t((p.N + kMassTile - 1) / kMassTile, p.units);

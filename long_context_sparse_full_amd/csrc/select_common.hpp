@@ -13,10 +13,9 @@ namespace hs2 {
 
 // per-row state words; each selection kernel reads the slots written by the
 // kernels before it and writes its own
-// (ST_DONE, ST_PLO, ST_PHI: the bracketed path's settled flag and bracket;
-// ST_ARRIVE: the fused emit's count of finished chunks)
+// (ST_DONE, ST_PLO, ST_PHI: the bracketed path's settled flag and bracket)
 enum { ST_MODE = 0, ST_NCAND = 1, ST_TAKE = 2, ST_P = 3, ST_PREFIX1 = 4, ST_NEED1 = 5,
-       ST_PREFIX2 = 6, ST_NEED2 = 7, ST_DONE = 8, ST_PLO = 9, ST_PHI = 10, ST_ARRIVE = 11, ST_WORDS = 16 };
+       ST_PREFIX2 = 6, ST_NEED2 = 7, ST_DONE = 8, ST_PLO = 9, ST_PHI = 10, ST_WORDS = 16 };
 enum { MODE_RADIX = 0, MODE_ALL = 1, MODE_NONE = 2 };
 
 // Candidates of a query at position p: [0, p - window], so ncand of them; the
@@ -43,7 +42,6 @@ __device__ __forceinline__ void sel_init_row(int32_t* st, int32_t* hist3, int p,
     st[ST_TAKE] = take;
     st[ST_P] = p;
     st[ST_DONE] = 0;
-    st[ST_ARRIVE] = 0;
   }
   if (block_size == 1)
     for (int i = tid; i < 3 * kHistBins; i += nthreads) hist3[i] = 0;

@@ -504,8 +504,7 @@ def test_full_attn_topk(hs2, case):
     bit for bit equal to the oracle's selection on the returned scores.  With
     one bf16/FP8 query token per unit the merge sets the selection up and the
     score pass counts the first digit, so only the last two histogram passes
-    of the select kernels run (one, when k is small enough for the pass that
-    fuses the third digit with the emit)."""
+    of the select kernels run."""
     kv, D, G, Hkv, B, N, k, window, qk = case[:9]
     Tq = case[9] if len(case) > 9 else 1
     spec = small_spec(kv, D=D, G=G, Hkv=Hkv, B=B, N=N, Tq=Tq, k=k, window=window,
@@ -526,13 +525,11 @@ def test_full_attn_topk(hs2, case):
     finally:
         hs2.timing_enable(False)
         hs2.timing_reset()
-    fused = k <= 2048  # the third digit is counted by the emitting pass (rows of up to 256 chunks)
     if n_chunk == 0 and Tq == 1:
         # the merge sets the rows up and the score pass counts the first digit
-        want = 1 if fused else 2
-        assert n_hist == want, f"expected {want} histogram pass(es) of the select kernels"
+        assert n_hist == 2, "expected the last two histogram passes of the select kernels"
     else:
-        assert n_hist in ((1, 2) if fused else (2, 3)), "expected the select kernels"
+        assert n_hist in (2, 3), "expected the select kernels"
     o_or, l_or, s_or = oracle_full(inp, spec)
     gu.assert_close(gu.host(out), o_or, gu.O_TOL[kv], "out")
     gu.assert_lse(gu.host(lse), l_or, kv, "lse")
