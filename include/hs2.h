@@ -304,10 +304,11 @@ int hs2_debug_scan_read_probe(const hs2_kv_desc* kv, int32_t Hq, int32_t with_co
 /* Full layer and token selection in one call: the results of
  * hs2_full_attn_scores followed by hs2_select_topk_window with block_size 1
  * (same layouts, rules, flags and requirements; both passages above).  With one
- * query token per (b, kv head) unit, the full layer's merge kernel sets the
- * selection's rows up and its score kernel counts the selection's first radix
- * digit while writing the scores, which saves the selection two passes over
- * them.  Workspace: at least hs2_full_attn_topk_workspace() bytes, 256-byte
+ * query token per (b, kv head) unit, the full layer sets the selection's rows
+ * up (a bf16/FP8 scan itself, an fp32 cache in its merge kernel) and its score
+ * kernel counts the selection's first radix digit while writing the scores,
+ * which saves the selection two passes over them; with a bf16/FP8 cache the
+ * split merge runs in the same launch as the scores.  Workspace: at least hs2_full_attn_topk_workspace() bytes, 256-byte
  * aligned. */
 size_t hs2_full_attn_topk_workspace(const hs2_kv_desc* kv, int32_t Tq, int32_t Hq);
 int hs2_full_attn_topk(const hs2_kv_desc* kv, const void* q, hs2_dtype q_dtype, int32_t Tq, int32_t Hq,
