@@ -448,10 +448,14 @@ def bench_extras(hs2, synth, k, v, ks, vs, q, spec, args):
     op = torch.empty_like(qp)
     us = timed_us(lambda: hs2.swa_attn(kp, vp, qp, 0, W, out=op, want_lse=False), reps)
     flops = 4 * Hq * D * sum(min(W, t + 1) for t in range(Tp))
+    # its HBM floor: the queries and the cache read once, the outputs written once
+    sbytes = 2 * qp.numel() * qp.element_size() + kp.numel() * kp.element_size() + vp.numel() * vp.element_size()
     ex["swa128_prefill_32k"] = {"avg_us": round(us, 2), "tokens_per_s": round(Tp / (us * 1e-6), 1),
                                 "TFLOPs": round(flops / (us * 1e-6) / 1e12, 1),
                                 "mfma_frac": round(flops / (us * 1e-6) / 1e12 / MFMA_BF16_TFLOPS, 4),
-                                "algorithmic_flops": flops}
+                                "algorithmic_flops": flops, "algorithmic_bytes": sbytes,
+                                "GBps": round(sbytes / (us * 1e-6) / 1e9, 1),
+                                "hbm_frac": round(sbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
     del kp, vp, qp, op
     # K/V bridge of 4 layers from one hidden state
     L, dm = 4, 4096

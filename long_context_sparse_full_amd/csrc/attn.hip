@@ -6,7 +6,8 @@
 //                   over bf16 or E4M3FN caches.  QK^T and PV run on
 //                   v_mfma_f32_16x16x32_bf16 with positions on the MFMA M side
 //                   and up to 16 query rows (the heads of one GQA group) on N.
-//  * scan_f32    -- the same two roles for fp32 caches on the VALU (exact fp32).
+//  * scan_f32    -- the same two roles for fp32 caches on the VALU (fp32 products
+//                   and sums; its scores come from the same 16-bit logit codes).
 //  * combine     -- merges the per-split (max, sum, output) partials.
 //  * score       -- importance scores: per position, sum over the group's query
 //                   heads of the softmax probability, from the stored logits.
