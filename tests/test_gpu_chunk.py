@@ -98,8 +98,22 @@ def test_chunk512_end_to_end(hs2):
         gu.check_selection_vs_oracle(idx[:, sl], cnt[:, sl], i_or, c_or, s_or, qp, spec.k, spec.window)
     gu.log(f"[chunk512] sampled units: worst row rel dO {worst_rel:.2e}, max rel dS {worst_s:.2e}")
 
-    gu.log("[chunk512] selections vs the oracle's on the GPU scores (all units)")
+    # every unit at full size: a score row is the sum over the group's G heads
+    # of probability rows that each sum to one, so it sums to G, is
+    # non-negative and is zero past the row's query position.  The chunk's
+    # score pass forms each term in fp32 from a recomputed logit (relative
+    # error near 2^-20), so the sum stays far inside 1e-4 G.
+    gu.log("[chunk512] score rows of all units: sum to G, zero past the query position")
     s64 = sc.astype(np.float64)
+    assert (sc >= 0).all(), "negative score"
+    tot = s64.sum(axis=-1)  # [B, Tq, Hkv]
+    worst_sum = float(np.abs(tot - G).max())
+    assert worst_sum <= 1e-4 * G, f"a score row sums to G {G} only within {worst_sum:.3e}"
+    for t in range(Tq):
+        assert not sc[:, t, :, spec.q_pos0 + t + 1:].any(), f"nonzero score past the query position of token {t}"
+    gu.log(f"[chunk512] score rows: worst |sum - G| {worst_sum:.2e}")
+
+    gu.log("[chunk512] selections vs the oracle's on the GPU scores (all units)")
     i_g, c_g = oracle.select_topk_window(s64, spec.q_pos0, spec.k, spec.window, max_sel=spec.max_sel)
     assert np.array_equal(cnt, c_g) and np.array_equal(idx, i_g), "token selection differs"
     gu.check_structure(idx, cnt, spec.q_pos0, spec.k, spec.window, N)
