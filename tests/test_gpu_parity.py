@@ -812,3 +812,55 @@ def test_swa_attn_parity(hs2, case):
         vv = gu.host(blk.v)[:, :, qp:qp + Tq]  # [B, Hkv, Tq, D]
         want = np.repeat(np.transpose(vv, (0, 2, 1, 3)), G, axis=2)
         gu.assert_close(gu.host(out), want, 0.0, "window of one")
+
+
+# ------------------------------- merge inside the score launch (one-call path)
+
+MERGE_CASES = [
+    # kv, D, G, Hkv, B, N, Tq
+    ("fp8", 128, 8, 4, 1, 300000, 1),    # several hundred splits per unit, as at long context
+    ("bf16", 128, 8, 4, 2, 40000, 1),
+    ("bf16", 64, 16, 2, 1, 9001, 2),     # 16 rows per unit (four per wave in the LSE prologue), two tokens
+    ("fp8", 64, 4, 2, 3, 5003, 1),       # 4 rows per unit, ragged length
+]
+
+
+@pytest.mark.parametrize("case", MERGE_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_merge_in_score_launch_matches_merge_kernel(hs2, case):
+    """With a bf16/FP8 cache and one query token per unit, hs2_full_attn_topk
+    runs the split merge as part of the score launch (its score workgroups
+    derive the rows' LSE themselves) and the scan sets the selection rows up;
+    hs2_full_attn_scores runs the merge kernel.  Both merge the same split
+    partials with the same code, so outputs and LSE agree bit for bit; the
+    scores differ only by the order in which the LSE was summed (fp32
+    rounding)."""
+    kv, D, G, Hkv, B, N, Tq = case
+    spec = small_spec(kv, D=D, G=G, Hkv=Hkv, B=B, N=N, Tq=Tq, k=256, window=32)
+    inp = synth.make_inputs(spec, seed=515 + N)
+    blk = gu.DeviceBlock(inp)
+    gu.log(f"merge in score launch {case}")
+    o1, l1, s1 = hs2.full_attn_scores(blk.k, blk.v, blk.q, spec.q_pos0, k_scale=blk.ks, v_scale=blk.vs)
+    hs2.timing_reset()
+    hs2.timing_enable(True)
+    try:
+        o2, l2, s2, idx, cnt = hs2.full_attn_topk(blk.k, blk.v, blk.q, spec.q_pos0, spec.k, spec.window,
+                                                  max_sel=spec.max_sel, k_scale=blk.ks, v_scale=blk.vs)
+        torch.cuda.synchronize()
+        _, n_comb = hs2.timing_collect("combine")
+        _, n_score = hs2.timing_collect("score")
+    finally:
+        hs2.timing_enable(False)
+        hs2.timing_reset()
+    assert n_comb == 0 and n_score == 1, "expected the merge inside the score launch"
+    o1, o2 = gu.host(o1), gu.host(o2)
+    assert np.array_equal(o1.view(np.uint32), o2.view(np.uint32)), "outputs differ between the two merge paths"
+    assert np.array_equal(gu.host(l1).view(np.uint32), gu.host(l2).view(np.uint32)), "LSE differs between the paths"
+    s1, s2 = gu.host(s1).astype(np.float64), gu.host(s2).astype(np.float64)
+    rel = float((np.abs(s1 - s2) / np.maximum(s1, 1e-30)).max())
+    assert rel <= 1e-5, f"scores of the two paths differ by {rel:.2e} (relative)"
+    # and the one-call path against the oracle
+    o_or, l_or, s_or = oracle_full(inp, spec)
+    gu.assert_rows_rel(o2, o_or, kv)
+    gu.assert_scores(s2, s_or, G=G)
+    i_g, c_g = oracle.select_topk_window(s2, spec.q_pos0, spec.k, spec.window, max_sel=spec.max_sel)
+    assert np.array_equal(gu.host(cnt), c_g) and np.array_equal(gu.host(idx), i_g)
