@@ -57,7 +57,7 @@ extern "C" {
 struct ihipStream_t;
 typedef struct ihipStream_t* hipStream_t;
 
-#define HS2_ABI_VERSION 2
+#define HS2_ABI_VERSION 3
 
 typedef enum { HS2_F32 = 0, HS2_BF16 = 1, HS2_FP8_E4M3FN = 2 } hs2_dtype;
 
@@ -316,6 +316,40 @@ int hs2_full_attn_topk(const hs2_kv_desc* kv, const void* q, hs2_dtype q_dtype, 
                        float* scores, int32_t k, int32_t window, int32_t flags, int32_t* idx,
                        int32_t* count, int32_t max_sel, void* workspace, size_t workspace_bytes,
                        hipStream_t stream);
+
+/* Paged cache (decode path): the rows of all sequences live in a shared pool
+ * of fixed-size pages, and a table maps each sequence's logical pages to pool
+ * pages, as a serving layer that owns the cache memory hands them out (the
+ * pages treat the cache as one array per layer; paging is a layout of that
+ * array, not part of the method).  The descriptor's k/v point at the pool:
+ * row r of kv head h at k + h*stride_h + r*stride_n, stride_b = 0, N the
+ * logical length of every sequence; logical row j of sequence b is pool row
+ * table[b*pages_per_seq + j/page_rows]*page_rows + j%page_rows.  Results are
+ * those of the contiguous cache holding the same rows, bit for bit. */
+typedef struct {
+  const int32_t* table;  /* device [B][pages_per_seq]; entries are clamped to [0, pool_pages) */
+  int32_t page_rows;     /* rows per page: a power of two, at least 32 */
+  int32_t pages_per_seq; /* table entries per sequence; pages_per_seq * page_rows >= N */
+  int32_t pool_pages;    /* pages in the pool; pool_pages * page_rows < 2^31 */
+} hs2_page_table;
+
+/* hs2_full_attn_topk over a paged cache: same arguments, rules, results and
+ * workspace (hs2_full_attn_topk_workspace with the logical N) plus `pages`.
+ * bf16/FP8 caches; calls that take the multi-query chunk path (many query
+ * tokens per kv head) return HS2_ERR_UNSUPPORTED, as does an fp32 cache;
+ * HS2_ERR_INVALID_ARG for a page table outside the rules above. */
+int hs2_full_attn_topk_paged(const hs2_kv_desc* kv, const hs2_page_table* pages, const void* q, hs2_dtype q_dtype,
+                             int32_t Tq, int32_t Hq, int32_t q_pos0, const int32_t* q_pos0_b, float softmax_scale,
+                             void* out, float* lse, float* scores, int32_t k, int32_t window, int32_t flags,
+                             int32_t* idx, int32_t* count, int32_t max_sel, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream);
+/* hs2_sparse_attn_gather_ws over a paged cache (the index lists hold logical
+ * positions): same arguments, rules, results and workspace plus `pages`;
+ * bf16/FP8 caches. */
+int hs2_sparse_attn_gather_paged(const hs2_kv_desc* kv, const hs2_page_table* pages, const void* q,
+                                 hs2_dtype q_dtype, int32_t Tq, int32_t Hq, float softmax_scale, const int32_t* idx,
+                                 const int32_t* count, int32_t max_sel, void* out, float* lse, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream);
 
 /* Per-kernel timing with HIP events on the launch stream (off by default; a
  * measurement aid, process-wide).  While enabled, every kernel launch of the

@@ -66,6 +66,34 @@ int check_q(const hs2_kv_desc* kv, const void* q, int q_dtype, int Tq, int Hq, c
   return HS2_OK;
 }
 
+// A paged cache's table against the rules in hs2.h (bf16/FP8 only; the pool
+// is shared, so stride_b is 0).
+int check_pages(const hs2_kv_desc* kv, const hs2_page_table* pt, const char* what) {
+  const std::string w(what);
+  if (kv->dtype == HS2_F32) return fail(HS2_ERR_UNSUPPORTED, w + ": paged caches are bf16 or FP8_E4M3FN");
+  if (!pt || !pt->table) return fail(HS2_ERR_INVALID_ARG, w + ": page table is NULL");
+  if ((uintptr_t)pt->table & 3) return fail(HS2_ERR_INVALID_ARG, w + ": page table must be 4-byte aligned");
+  const int32_t pr = pt->page_rows;
+  if (pr < 32 || pr > (1 << 24) || (pr & (pr - 1)))
+    return fail(HS2_ERR_INVALID_ARG, w + ": page_rows must be a power of two from 32 to 2^24");
+  if (pt->pages_per_seq <= 0 || (int64_t)pt->pages_per_seq * pr < kv->N)
+    return fail(HS2_ERR_INVALID_ARG, w + ": pages_per_seq * page_rows must cover N");
+  if (pt->pool_pages <= 0 || (int64_t)pt->pool_pages * pr > INT32_MAX)
+    return fail(HS2_ERR_INVALID_ARG, w + ": need 0 < pool_pages and pool_pages * page_rows < 2^31");
+  if (kv->stride_b != 0) return fail(HS2_ERR_INVALID_ARG, w + ": a paged pool is shared by the sequences (stride_b = 0)");
+  return HS2_OK;
+}
+
+hs2::PageMap page_map(const hs2_page_table* pt) {
+  hs2::PageMap m{};
+  if (!pt) return m;
+  m.table = pt->table;
+  while ((1 << m.shift) < pt->page_rows) ++m.shift;
+  m.per_seq = pt->pages_per_seq;
+  m.pool = pt->pool_pages;
+  return m;
+}
+
 // The read-only view of a writable cache descriptor (for validation).
 hs2_kv_desc as_read_desc(const hs2_kv_out_desc& o) {
   hs2_kv_desc d{};
@@ -257,7 +285,17 @@ struct SelPrep {
 
 int full_layer(const hs2_kv_desc* kv, const void* q, hs2_dtype q_dtype, int32_t Tq, int32_t Hq, int32_t q_pos0,
                const int32_t* q_pos0_b, float softmax_scale, void* out, float* lse, float* scores, void* workspace,
-               size_t workspace_bytes, hipStream_t stream, SelPrep* sel);
+               size_t workspace_bytes, hipStream_t stream, SelPrep* sel, const hs2_page_table* pages = nullptr);
+// the one-workgroup gather on checked arguments (pages nullptr: contiguous)
+int gather_single(const hs2_kv_desc* kv, const hs2_page_table* pages, const void* q, int32_t Tq, int32_t Hq,
+                  float softmax_scale, const int32_t* idx, const int32_t* count, int32_t max_sel, void* out,
+                  float* lse, hipStream_t stream);
+// hs2_full_attn_topk, on a contiguous (pages nullptr) or paged cache
+int full_attn_topk_impl(const char* name, const hs2_kv_desc* kv, const hs2_page_table* pages, const void* q,
+                        hs2_dtype q_dtype, int32_t Tq, int32_t Hq, int32_t q_pos0, const int32_t* q_pos0_b,
+                        float softmax_scale, void* out, float* lse, float* scores, int32_t k, int32_t window,
+                        int32_t flags, int32_t* idx, int32_t* count, int32_t max_sel, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream);
 // hs2_select_topk_window; pre_hist0: the row state and first histogram are
 // already built (full layer's merge and score pass)
 int select_impl(const float* scores, int32_t B, int32_t Tq, int32_t Hkv, int32_t N, int32_t q_pos0,
@@ -280,7 +318,7 @@ int hs2_full_attn_scores(const hs2_kv_desc* kv, const void* q, hs2_dtype q_dtype
 namespace {
 int full_layer(const hs2_kv_desc* kv, const void* q, hs2_dtype q_dtype, int32_t Tq, int32_t Hq, int32_t q_pos0,
                const int32_t* q_pos0_b, float softmax_scale, void* out, float* lse, float* scores, void* workspace,
-               size_t workspace_bytes, hipStream_t stream, SelPrep* sel) {
+               size_t workspace_bytes, hipStream_t stream, SelPrep* sel, const hs2_page_table* pages) {
   int st = check_kv(kv, "hs2_full_attn_scores");
   if (st) return st;
   if ((st = check_q(kv, q, q_dtype, Tq, Hq, "hs2_full_attn_scores"))) return st;
@@ -295,8 +333,12 @@ int full_layer(const hs2_kv_desc* kv, const void* q, hs2_dtype q_dtype, int32_t 
     return fail(HS2_ERR_WORKSPACE, "hs2_full_attn_scores: workspace needs " + std::to_string(pl.total) + " bytes");
   if ((uintptr_t)workspace & 255) return fail(HS2_ERR_INVALID_ARG, "hs2_full_attn_scores: workspace must be 256-byte aligned");
   if ((uintptr_t)q_pos0_b & 3) return fail(HS2_ERR_INVALID_ARG, "hs2_full_attn_scores: q_pos0_b must be 4-byte aligned");
+  if (pages && pl.chunk)
+    return fail(HS2_ERR_UNSUPPORTED, "hs2_full_attn_topk_paged: many query tokens per kv head (the chunk path) "
+                                     "on a paged cache");
 
   hs2::ScanParams p{};
+  p.pages = page_map(pages);
   p.k = kv->k;
   p.v = kv->v;
   p.sb = kv->stride_b;
@@ -434,6 +476,7 @@ int full_layer(const hs2_kv_desc* kv, const void* q, hs2_dtype q_dtype, int32_t 
   s.sn = kv->stride_n;
   s.k_scale = kv->k_scale;
   s.scale_log2 = p.scale_log2;
+  s.pages = p.pages;
   if ((e = hs2::launch_score(s, pl.units, stream, fused_merge ? &c : nullptr)) != hipSuccess)
     return hip_fail(e, "score launch");
   if (pre_sel) sel->hist0_done = true;
@@ -452,33 +495,24 @@ size_t hs2_full_attn_topk_workspace(const hs2_kv_desc* kv, int32_t Tq, int32_t H
 
 int hs2_full_attn_topk(const hs2_kv_desc* kv, const void* q, hs2_dtype q_dtype, int32_t Tq, int32_t Hq,
                        int32_t q_pos0, const int32_t* q_pos0_b, float softmax_scale, void* out, float* lse,
-                       float* scores, int32_t k,
-                       int32_t window, int32_t flags, int32_t* idx, int32_t* count, int32_t max_sel, void* workspace,
-                       size_t workspace_bytes, hipStream_t stream) {
-  int st = check_kv(kv, "hs2_full_attn_topk");
+                       float* scores, int32_t k, int32_t window, int32_t flags, int32_t* idx, int32_t* count,
+                       int32_t max_sel, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return full_attn_topk_impl("hs2_full_attn_topk", kv, nullptr, q, q_dtype, Tq, Hq, q_pos0, q_pos0_b, softmax_scale,
+                             out, lse, scores, k, window, flags, idx, count, max_sel, workspace, workspace_bytes,
+                             stream);
+}
+
+int hs2_full_attn_topk_paged(const hs2_kv_desc* kv, const hs2_page_table* pages, const void* q, hs2_dtype q_dtype,
+                             int32_t Tq, int32_t Hq, int32_t q_pos0, const int32_t* q_pos0_b, float softmax_scale,
+                             void* out, float* lse, float* scores, int32_t k, int32_t window, int32_t flags,
+                             int32_t* idx, int32_t* count, int32_t max_sel, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream) {
+  const char* name = "hs2_full_attn_topk_paged";
+  int st = check_kv(kv, name);
   if (st) return st;
-  if (!idx || !count) return fail(HS2_ERR_INVALID_ARG, "hs2_full_attn_topk: NULL idx/count");
-  if (k < 0 || window < 0) return fail(HS2_ERR_INVALID_ARG, "hs2_full_attn_topk: need k >= 0 and window >= 0");
-  if (flags & ~HS2_SEL_WINDOW_COMPETES) return fail(HS2_ERR_INVALID_ARG, "hs2_full_attn_topk: unknown flags");
-  const int64_t need_sel = std::min<int64_t>((int64_t)k + window, kv->N);
-  if (max_sel < need_sel)
-    return fail(HS2_ERR_INVALID_ARG, "hs2_full_attn_topk: max_sel must be >= min(k + window, N) = " +
-                                         std::to_string(need_sel));
-  if (((uintptr_t)idx & 3) || ((uintptr_t)count & 3))
-    return fail(HS2_ERR_INVALID_ARG, "hs2_full_attn_topk: idx/count must be 4-byte aligned");
-  if (Tq <= 0 || Hq <= 0 || Hq % kv->Hkv) return check_q(kv, q, q_dtype, Tq, Hq, "hs2_full_attn_topk");
-  const size_t need_ws = hs2_full_attn_topk_workspace(kv, Tq, Hq);
-  if (!workspace || workspace_bytes < need_ws)
-    return fail(HS2_ERR_WORKSPACE, "hs2_full_attn_topk: workspace needs " + std::to_string(need_ws) + " bytes");
-  const size_t full_bytes = plan_full(kv, Tq, Hq).total;
-  void* rest = static_cast<char*>(workspace) + full_bytes;
-  const int32_t cand_window = (flags & HS2_SEL_WINDOW_COMPETES) ? 0 : window;
-  SelPrep sel{k, window, cand_window, rest};
-  st = full_layer(kv, q, q_dtype, Tq, Hq, q_pos0, q_pos0_b, softmax_scale, out, lse, scores, workspace, full_bytes,
-                  stream, &sel);
-  if (st) return st;
-  return select_impl(scores, kv->B, Tq, kv->Hkv, kv->N, q_pos0, q_pos0_b, k, window, 1, flags, idx, count, max_sel,
-                     rest, workspace_bytes - full_bytes, stream, sel.hist0_done);
+  if ((st = check_pages(kv, pages, name))) return st;
+  return full_attn_topk_impl(name, kv, pages, q, q_dtype, Tq, Hq, q_pos0, q_pos0_b, softmax_scale, out, lse, scores,
+                             k, window, flags, idx, count, max_sel, workspace, workspace_bytes, stream);
 }
 
 size_t hs2_select_workspace(int32_t B, int32_t Tq, int32_t Hkv, int32_t N) {
@@ -502,6 +536,37 @@ int hs2_select_topk_window(const float* scores, int32_t B, int32_t Tq, int32_t H
 }  // extern "C"
 
 namespace {
+int full_attn_topk_impl(const char* name, const hs2_kv_desc* kv, const hs2_page_table* pages, const void* q,
+                        hs2_dtype q_dtype, int32_t Tq, int32_t Hq, int32_t q_pos0, const int32_t* q_pos0_b,
+                        float softmax_scale, void* out, float* lse, float* scores, int32_t k, int32_t window,
+                        int32_t flags, int32_t* idx, int32_t* count, int32_t max_sel, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream) {
+  int st = check_kv(kv, "hs2_full_attn_topk");
+  if (st) return st;
+  if (!idx || !count) return fail(HS2_ERR_INVALID_ARG, std::string(name) + ": NULL idx/count");
+  if (k < 0 || window < 0) return fail(HS2_ERR_INVALID_ARG, std::string(name) + ": need k >= 0 and window >= 0");
+  if (flags & ~HS2_SEL_WINDOW_COMPETES) return fail(HS2_ERR_INVALID_ARG, std::string(name) + ": unknown flags");
+  const int64_t need_sel = std::min<int64_t>((int64_t)k + window, kv->N);
+  if (max_sel < need_sel)
+    return fail(HS2_ERR_INVALID_ARG, std::string(name) + ": max_sel must be >= min(k + window, N) = " +
+                                         std::to_string(need_sel));
+  if (((uintptr_t)idx & 3) || ((uintptr_t)count & 3))
+    return fail(HS2_ERR_INVALID_ARG, std::string(name) + ": idx/count must be 4-byte aligned");
+  if (Tq <= 0 || Hq <= 0 || Hq % kv->Hkv) return check_q(kv, q, q_dtype, Tq, Hq, "hs2_full_attn_topk");
+  const size_t need_ws = hs2_full_attn_topk_workspace(kv, Tq, Hq);
+  if (!workspace || workspace_bytes < need_ws)
+    return fail(HS2_ERR_WORKSPACE, std::string(name) + ": workspace needs " + std::to_string(need_ws) + " bytes");
+  const size_t full_bytes = plan_full(kv, Tq, Hq).total;
+  void* rest = static_cast<char*>(workspace) + full_bytes;
+  const int32_t cand_window = (flags & HS2_SEL_WINDOW_COMPETES) ? 0 : window;
+  SelPrep sel{k, window, cand_window, rest};
+  st = full_layer(kv, q, q_dtype, Tq, Hq, q_pos0, q_pos0_b, softmax_scale, out, lse, scores, workspace, full_bytes,
+                  stream, &sel, pages);
+  if (st) return st;
+  return select_impl(scores, kv->B, Tq, kv->Hkv, kv->N, q_pos0, q_pos0_b, k, window, 1, flags, idx, count, max_sel,
+                     rest, workspace_bytes - full_bytes, stream, sel.hist0_done);
+}
+
 int select_impl(const float* scores, int32_t B, int32_t Tq, int32_t Hkv, int32_t N, int32_t q_pos0,
                 const int32_t* q_pos0_b, int32_t k, int32_t window, int32_t block_size, int32_t flags, int32_t* idx,
                 int32_t* count, int32_t max_sel, void* workspace, size_t workspace_bytes, hipStream_t stream,
@@ -571,36 +636,7 @@ int hs2_sparse_attn_gather(const hs2_kv_desc* kv, const void* q, hs2_dtype q_dty
   if (!al16(out) || ((uintptr_t)idx & 3) || ((uintptr_t)count & 3) || (lse && ((uintptr_t)lse & 3)))
     return fail(HS2_ERR_INVALID_ARG, "hs2_sparse_attn_gather: out must be 16-byte aligned, idx/count/lse 4-byte");
   if (!std::isfinite(softmax_scale)) return fail(HS2_ERR_INVALID_ARG, "hs2_sparse_attn_gather: softmax_scale not finite");
-  hs2::ScanParams p{};
-  p.k = kv->k;
-  p.v = kv->v;
-  p.sb = kv->stride_b;
-  p.sh = kv->stride_h;
-  p.sn = kv->stride_n;
-  p.k_scale = kv->k_scale;
-  p.v_scale = kv->v_scale;
-  p.B = kv->B;
-  p.Hkv = kv->Hkv;
-  p.N = kv->N;
-  p.D = kv->D;
-  p.G = Hq / kv->Hkv;
-  p.q = q;
-  p.Tq = Tq;
-  p.Hq = Hq;
-  p.q_pos0 = 0;
-  p.scale_log2 = softmax_scale * 1.44269504088896340736f;
-  p.tpack = 1;
-  p.n_tpacks = Tq;
-  p.rows = p.G;
-  p.nsplit = 1;
-  p.idx = idx;
-  p.count = count;
-  p.max_sel = max_sel;
-  p.out = out;
-  p.lse = lse;
-  const hipError_t e = hs2::launch_scan(p, kv->dtype, true, false, stream);
-  if (e != hipSuccess) return hip_fail(e, "sparse_gather launch");
-  return HS2_OK;
+  return gather_single(kv, nullptr, q, Tq, Hq, softmax_scale, idx, count, max_sel, out, lse, stream);
 }
 
 namespace {
@@ -639,6 +675,43 @@ size_t hs2_sparse_attn_workspace(int32_t B, int32_t Tq, int32_t Hkv, int32_t D, 
 }  // extern "C"
 
 namespace {
+// The one-workgroup gather on checked arguments (pages nullptr: contiguous cache).
+int gather_single(const hs2_kv_desc* kv, const hs2_page_table* pages, const void* q, int32_t Tq, int32_t Hq,
+                  float softmax_scale, const int32_t* idx, const int32_t* count, int32_t max_sel, void* out,
+                  float* lse, hipStream_t stream) {
+  hs2::ScanParams p{};
+  p.pages = page_map(pages);
+  p.k = kv->k;
+  p.v = kv->v;
+  p.sb = kv->stride_b;
+  p.sh = kv->stride_h;
+  p.sn = kv->stride_n;
+  p.k_scale = kv->k_scale;
+  p.v_scale = kv->v_scale;
+  p.B = kv->B;
+  p.Hkv = kv->Hkv;
+  p.N = kv->N;
+  p.D = kv->D;
+  p.G = Hq / kv->Hkv;
+  p.q = q;
+  p.Tq = Tq;
+  p.Hq = Hq;
+  p.q_pos0 = 0;
+  p.scale_log2 = softmax_scale * 1.44269504088896340736f;
+  p.tpack = 1;
+  p.n_tpacks = Tq;
+  p.rows = p.G;
+  p.nsplit = 1;
+  p.idx = idx;
+  p.count = count;
+  p.max_sel = max_sel;
+  p.out = out;
+  p.lse = lse;
+  const hipError_t e = hs2::launch_scan(p, kv->dtype, true, false, stream);
+  if (e != hipSuccess) return hip_fail(e, "sparse_gather launch");
+  return HS2_OK;
+}
+
 // Checks shared by the split gather's entry points.
 int check_gather_args(const char* name, const hs2_kv_desc* kv, const void* q, hs2_dtype q_dtype, int32_t Tq,
                       int32_t Hq, float softmax_scale, const int32_t* idx, const int32_t* count, int32_t max_sel,
@@ -669,8 +742,10 @@ bool use_split_gather(const hs2_kv_desc* kv, int units, const GatherPlan& gp) {
 // alignment (arrival counters zero on entry; zero again on exit).
 int launch_split_gather(const char* name, const hs2_kv_desc* kv, const void* q, int32_t Tq, int32_t Hq,
                         float softmax_scale, const int32_t* idx, const int32_t* count, int32_t max_sel, void* out,
-                        float* lse, const GatherPlan& gp, void* workspace, hipStream_t stream) {
+                        float* lse, const GatherPlan& gp, void* workspace, hipStream_t stream,
+                        const hs2_page_table* pages = nullptr) {
   hs2::ScanParams p{};
+  p.pages = page_map(pages);
   p.k = kv->k;
   p.v = kv->v;
   p.sb = kv->stride_b;
@@ -703,6 +778,26 @@ int launch_split_gather(const char* name, const hs2_kv_desc* kv, const void* q, 
   const hipError_t e = hs2::launch_gather_split(p, kv->dtype, stream);
   if (e != hipSuccess) return hip_fail(e, (std::string(name) + ": sparse_gather launch").c_str());
   return HS2_OK;
+}
+
+// hs2_sparse_attn_gather_ws on a contiguous (pages nullptr) or paged cache.
+int gather_ws_impl(const char* name, const hs2_kv_desc* kv, const hs2_page_table* pages, const void* q,
+                   hs2_dtype q_dtype, int32_t Tq, int32_t Hq, float softmax_scale, const int32_t* idx,
+                   const int32_t* count, int32_t max_sel, void* out, float* lse, void* workspace,
+                   size_t workspace_bytes, hipStream_t stream) {
+  int st = check_gather_args(name, kv, q, q_dtype, Tq, Hq, softmax_scale, idx, count, max_sel, out, lse);
+  if (st) return st;
+  if (kv->dtype == HS2_F32)  // the fp32 path has no split form; it needs no workspace
+    return gather_single(kv, nullptr, q, Tq, Hq, softmax_scale, idx, count, max_sel, out, lse, stream);
+  const int units = kv->B * Tq * kv->Hkv;
+  const GatherPlan gp = plan_gather(units, max_sel, kv->D);
+  if (!workspace || workspace_bytes < gp.total)
+    return fail(HS2_ERR_WORKSPACE, std::string(name) + ": workspace needs " + std::to_string(gp.total) + " bytes");
+  if (!use_split_gather(kv, units, gp))
+    return gather_single(kv, pages, q, Tq, Hq, softmax_scale, idx, count, max_sel, out, lse, stream);
+  if ((uintptr_t)workspace & 255) return fail(HS2_ERR_INVALID_ARG, std::string(name) + ": workspace must be 256-byte aligned");
+  return launch_split_gather(name, kv, q, Tq, Hq, softmax_scale, idx, count, max_sel, out, lse, gp, workspace, stream,
+                             pages);
 }
 
 // ---- the no-allocation variant's scratch --------------------------------
@@ -756,19 +851,20 @@ extern "C" {
 int hs2_sparse_attn_gather_ws(const hs2_kv_desc* kv, const void* q, hs2_dtype q_dtype, int32_t Tq, int32_t Hq,
                               float softmax_scale, const int32_t* idx, const int32_t* count, int32_t max_sel,
                               void* out, float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  const char* name = "hs2_sparse_attn_gather_ws";
-  int st = check_gather_args(name, kv, q, q_dtype, Tq, Hq, softmax_scale, idx, count, max_sel, out, lse);
+  return gather_ws_impl("hs2_sparse_attn_gather_ws", kv, nullptr, q, q_dtype, Tq, Hq, softmax_scale, idx, count,
+                        max_sel, out, lse, workspace, workspace_bytes, stream);
+}
+
+int hs2_sparse_attn_gather_paged(const hs2_kv_desc* kv, const hs2_page_table* pages, const void* q,
+                                 hs2_dtype q_dtype, int32_t Tq, int32_t Hq, float softmax_scale, const int32_t* idx,
+                                 const int32_t* count, int32_t max_sel, void* out, float* lse, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream) {
+  const char* name = "hs2_sparse_attn_gather_paged";
+  int st = check_kv(kv, name);
   if (st) return st;
-  if (kv->dtype == HS2_F32)  // the fp32 path has no split form; it needs no workspace
-    return hs2_sparse_attn_gather(kv, q, q_dtype, Tq, Hq, softmax_scale, idx, count, max_sel, out, lse, stream);
-  const int units = kv->B * Tq * kv->Hkv;
-  const GatherPlan gp = plan_gather(units, max_sel, kv->D);
-  if (!workspace || workspace_bytes < gp.total)
-    return fail(HS2_ERR_WORKSPACE, std::string(name) + ": workspace needs " + std::to_string(gp.total) + " bytes");
-  if (!use_split_gather(kv, units, gp))
-    return hs2_sparse_attn_gather(kv, q, q_dtype, Tq, Hq, softmax_scale, idx, count, max_sel, out, lse, stream);
-  if ((uintptr_t)workspace & 255) return fail(HS2_ERR_INVALID_ARG, std::string(name) + ": workspace must be 256-byte aligned");
-  return launch_split_gather(name, kv, q, Tq, Hq, softmax_scale, idx, count, max_sel, out, lse, gp, workspace, stream);
+  if ((st = check_pages(kv, pages, name))) return st;
+  return gather_ws_impl(name, kv, pages, q, q_dtype, Tq, Hq, softmax_scale, idx, count, max_sel, out, lse, workspace,
+                        workspace_bytes, stream);
 }
 
 size_t hs2_sparse_attn_static_limit(void) { return kStaticScratchBytes; }

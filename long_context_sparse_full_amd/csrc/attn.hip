@@ -381,7 +381,9 @@ __device__ __forceinline__ void load_q(u32x4_t (&qf)[D / 32], const ScanParams& 
 // 32-position tiles and prefetch the next tile while computing this one.
 // Tile bases are wave-uniform (scalar registers); each lane adds a fixed
 // 32-bit offset, so interior tiles need no per-lane address arithmetic.
-template <bool FP8, int D, bool WRITE_LOGITS, int WAVES>
+// PAGED: the cache is a paged pool (P.pages); a 32-aligned tile lies in one
+// page, so a full tile's base is its first row's physical row.
+template <bool FP8, int D, bool WRITE_LOGITS, int WAVES, bool PAGED = false>
 __global__ void __launch_bounds__(WAVES * 64) scan_full(ScanParams P) {
   constexpr int VE = D / 16, NC = D / 32, EB = FP8 ? 1 : 2;
   constexpr int STEP = WAVES * 32;
@@ -447,8 +449,9 @@ __global__ void __launch_bounds__(WAVES * 64) scan_full(ScanParams P) {
   auto load_full = [&](RawTile<FP8, D>& R, int j0) {
     const char* kp[2];
     const char* vp[8];
-    const char* tk = kb + (int64_t)j0 * snb;
-    const char* tv = vb + (int64_t)j0 * snb;
+    const int64_t row0 = PAGED ? phys_row(P.pages, b, j0) : j0;
+    const char* tk = kb + row0 * snb;
+    const char* tv = vb + row0 * snb;
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) kp[hh] = tk + koff[hh];
 #pragma unroll
@@ -461,11 +464,12 @@ __global__ void __launch_bounds__(WAVES * 64) scan_full(ScanParams P) {
     } else {  // tail tile: rows past the last position repeat it
       const char* kp[2];
       const char* vp[8];
+      auto row = [&](int j) -> int64_t { return PAGED ? phys_row(P.pages, b, j) : j; };
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) kp[hh] = kb + (int64_t)min(j0 + 16 * hh + r, p_max) * snb + 16 * g4;
+      for (int hh = 0; hh < 2; ++hh) kp[hh] = kb + row(min(j0 + 16 * hh + r, p_max)) * snb + 16 * g4;
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk)
-        vp[kk] = vb + (int64_t)min(j0 + 16 * (kk >> 2) + 4 * g4 + (kk & 3), p_max) * snb + VE * r * EB;
+        vp[kk] = vb + row(min(j0 + 16 * (kk >> 2) + 4 * g4 + (kk & 3), p_max)) * snb + VE * r * EB;
       load_tile<FP8, D>(R, kp, vp);
     }
   };
@@ -1215,8 +1219,10 @@ __global__ void __launch_bounds__(WAVES * 64, (FP8 || D == 64) ? 3 : 2) scan_gat
   for (int base = 0; base < n; base += kGatherIdxCap) {
     const int nb = min(kGatherIdxCap, n - base);
     __syncthreads();
-    for (int i = threadIdx.x; i < nb; i += WAVES * 64)
-      s_idx[i] = P.band > 0 ? lo + base + i : min(max(list[base + i], 0), P.N - 1);
+    for (int i = threadIdx.x; i < nb; i += WAVES * 64) {
+      const int j = P.band > 0 ? lo + base + i : min(max(list[base + i], 0), P.N - 1);
+      s_idx[i] = P.pages.table ? phys_row(P.pages, b, j) : j;  // the row's place in the cache
+    }
     __syncthreads();
     const int jl = base + nb - 1;
     auto load = [&](RawTile<FP8, D>& R, int j0) {
@@ -1310,8 +1316,13 @@ __global__ void __launch_bounds__(WAVES * 64) scan_gather_split(ScanParams P) {
   for (int dt = 0; dt < VE; ++dt) S.o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   const int nb = max(0, hi - lo);  // <= gslice <= kGatherIdxCap
-  if ((int)threadIdx.x < nb) s_idx[threadIdx.x] = min(max(e0, 0), P.N - 1);
-  for (int i = threadIdx.x + WAVES * 64; i < nb; i += WAVES * 64) s_idx[i] = min(max(list[lo + i], 0), P.N - 1);
+  // each entry's place in the cache (its physical row in a paged pool)
+  auto place = [&](int e) {
+    const int j = min(max(e, 0), P.N - 1);
+    return P.pages.table ? phys_row(P.pages, b, j) : j;
+  };
+  if ((int)threadIdx.x < nb) s_idx[threadIdx.x] = place(e0);
+  for (int i = threadIdx.x + WAVES * 64; i < nb; i += WAVES * 64) s_idx[i] = place(list[lo + i]);
   __syncthreads();
   if (nb > 0) {
     const int jl = lo + nb - 1;
@@ -1790,7 +1801,8 @@ __global__ void __launch_bounds__(256) combine_few(CombineParams P) {
 // g, recomputed in fp32 from the stored elements: the scan's expression, summed
 // in another order.
 __device__ __forceinline__ float recompute_logit(const ScoreParams& P, int b, int t, int h, int g, int j) {
-  const int64_t krow = (int64_t)b * P.sb + (int64_t)g * P.sh + (int64_t)j * P.sn;
+  const int64_t jr = P.pages.table ? phys_row(P.pages, b, j) : j;  // the row's place in the cache
+  const int64_t krow = (int64_t)b * P.sb + (int64_t)g * P.sh + jr * P.sn;
   const int64_t qrow = (((int64_t)b * P.Tq + t) * P.Hq + h) * P.D;
   float acc = 0.f;
   if (P.kv_dtype == HS2_F32) {
@@ -2226,7 +2238,10 @@ __global__ void debug_e4m3fn(const uint8_t* codes, float* out, int n) {
 template <bool FP8, int D, bool WL, int WAVES>
 hipError_t go_full(const ScanParams& p, dim3 grid, hipStream_t s) {
   TimedLaunch tl("full_scan", s);
-  hipLaunchKernelGGL((scan_full<FP8, D, WL, WAVES>), grid, dim3(WAVES * 64), 0, s, p);
+  if (WL && p.pages.table)  // a paged pool (the host admits it only with the logits written)
+    hipLaunchKernelGGL((scan_full<FP8, D, WL, WAVES, true>), grid, dim3(WAVES * 64), 0, s, p);
+  else
+    hipLaunchKernelGGL((scan_full<FP8, D, WL, WAVES>), grid, dim3(WAVES * 64), 0, s, p);
   return hipGetLastError();
 }
 

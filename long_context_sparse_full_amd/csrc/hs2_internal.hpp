@@ -23,6 +23,19 @@ __host__ __device__ inline int qpos_of(const int32_t* qpos_b, int q_pos0, int b,
 // A unit is (b, token-pack, kv group g).  Its rows are the query heads of the
 // group for `tpack` consecutive tokens: row r = tl*G + i <-> token
 // t = tp*tpack + tl, head h = g*G + i.  Rows never exceed 16 (one MFMA tile).
+// A paged cache's row map: logical row j of sequence b is physical row
+// (page << shift) | (j & (2^shift - 1)) of the pool, page = the table entry
+// [b * per_seq + (j >> shift)] clamped to [0, pool).  Pages hold 2^shift >= 32
+// rows, so an aligned 32-row tile never straddles two pages.
+struct PageMap {
+  const int32_t* table;  // nullptr = contiguous cache
+  int shift, per_seq, pool;
+};
+__device__ __forceinline__ int phys_row(const PageMap& M, int b, int j) {
+  const int pg = min(max(M.table[(int64_t)b * M.per_seq + (j >> M.shift)], 0), M.pool - 1);
+  return (pg << M.shift) | (j & ((1 << M.shift) - 1));
+}
+
 struct ScanParams {
   const void* k;
   const void* v;
@@ -69,6 +82,10 @@ struct ScanParams {
   int32_t* sel_state;
   int32_t* sel_hist;
   int sel_k, sel_window;
+  // paged cache (full layer with one query token per unit, and the gathers):
+  // row j of sequence b lies at physical row phys_row(b, j) of a pool shared
+  // by the sequences (stride_b 0); ptab nullptr = contiguous rows
+  PageMap pages;
 };
 
 // Multi-query chunk path: a workgroup of 4 waves, each holding kFlashRG
@@ -151,6 +168,7 @@ struct ScoreParams {
   int64_t sb, sh, sn;     // cache strides, elements
   const float* k_scale;   // FP8 only
   float scale_log2;       // softmax_scale * log2(e)
+  PageMap pages;          // paged cache (see ScanParams)
 };
 
 // ---------------------------------------------------------------------------

@@ -42,6 +42,12 @@ class KVOutDesc(KVDesc):
     """hs2_kv_out_desc: the writable view the bridge takes (same fields)."""
 
 
+class PageTable(ctypes.Structure):
+    """hs2_page_table: a paged cache's map from logical to pool pages."""
+    _fields_ = [("table", ctypes.c_void_p), ("page_rows", ctypes.c_int32), ("pages_per_seq", ctypes.c_int32),
+                ("pool_pages", ctypes.c_int32)]
+
+
 _vp, _i32, _f32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
 _KVP = ctypes.POINTER(KVDesc)
 
@@ -72,6 +78,12 @@ _sparse = _sig("hs2_sparse_attn_gather", ctypes.c_int,
 _sparse_ws_size = _sig("hs2_sparse_attn_workspace", _sz, [_i32, _i32, _i32, _i32, _i32])
 _sparse_ws = _sig("hs2_sparse_attn_gather_ws", ctypes.c_int,
                   [_KVP, _vp, _i32, _i32, _i32, _f32, _vp, _vp, _i32, _vp, _vp, _vp, _sz, _vp])
+_PTP = ctypes.POINTER(PageTable)
+_topk_paged = _sig("hs2_full_attn_topk_paged", ctypes.c_int,
+                   [_KVP, _PTP, _vp, _i32, _i32, _i32, _i32, _vp, _f32, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp,
+                    _i32, _vp, _sz, _vp])
+_sparse_paged = _sig("hs2_sparse_attn_gather_paged", ctypes.c_int,
+                     [_KVP, _PTP, _vp, _i32, _i32, _i32, _f32, _vp, _vp, _i32, _vp, _vp, _vp, _sz, _vp])
 _sparse_static_limit = _sig("hs2_sparse_attn_static_limit", _sz, [])
 _sparse_static = _sig("hs2_sparse_attn_gather_static", ctypes.c_int,
                       [_KVP, _vp, _i32, _i32, _i32, _f32, _vp, _vp, _i32, _vp, _vp, _vp])
@@ -93,7 +105,8 @@ EXPORTED = [
     "hs2_abi_version", "hs2_status_string", "hs2_last_error", "hs2_full_attn_scores_workspace",
     "hs2_full_attn_scores", "hs2_full_attn_topk_workspace", "hs2_full_attn_topk", "hs2_select_workspace", "hs2_select_workspace_for", "hs2_select_topk_window",
     "hs2_sparse_attn_gather", "hs2_sparse_attn_workspace", "hs2_sparse_attn_gather_ws",
-    "hs2_sparse_attn_static_limit", "hs2_sparse_attn_gather_static", "hs2_swa_attn", "hs2_kv_bridge",
+    "hs2_sparse_attn_static_limit", "hs2_sparse_attn_gather_static", "hs2_full_attn_topk_paged",
+    "hs2_sparse_attn_gather_paged", "hs2_swa_attn", "hs2_kv_bridge",
     "hs2_kv_bridge_layers_workspace", "hs2_kv_bridge_layers", "hs2_debug_e4m3fn_to_f32", "hs2_debug_stream_read",
     "hs2_debug_scan_read_probe",
     "hs2_timing_enable",
@@ -155,6 +168,89 @@ def kv_desc(k: torch.Tensor, v: torch.Tensor, k_scale=None, v_scale=None, cls=KV
             ks = k_scale.data_ptr()
             vs = v_scale.data_ptr()
     return cls(k.data_ptr(), v.data_ptr(), code, k.stride(0), k.stride(1), k.stride(2), ks, vs, B, H, N, D)
+
+
+def pool_desc(k_pool: torch.Tensor, v_pool: torch.Tensor, B: int, N: int, k_scale=None, v_scale=None) -> KVDesc:
+    """Descriptor of a paged pool [Hkv, pool_rows, D] shared by B sequences of
+    logical length N (stride_b 0; FP8 pools need per-(sequence, head) scales)."""
+    if k_pool.shape != v_pool.shape or k_pool.dim() != 3 or k_pool.stride() != v_pool.stride() \
+            or k_pool.dtype != v_pool.dtype:
+        raise ValueError("k and v pools must be [Hkv, pool_rows, D] tensors of one dtype and layout")
+    if k_pool.stride(2) != 1:
+        raise ValueError("head_dim must be contiguous")
+    H, _, D = k_pool.shape
+    code = _dtype_code(k_pool)
+    ks = vs = None
+    if code == FP8_E4M3FN and k_scale is not None and v_scale is not None:
+        _dense(k_scale, v_scale)
+        ks, vs = k_scale.data_ptr(), v_scale.data_ptr()
+    return KVDesc(k_pool.data_ptr(), v_pool.data_ptr(), code, 0, k_pool.stride(0), k_pool.stride(1), ks, vs, B, H,
+                  N, D)
+
+
+def page_table(table: torch.Tensor, page_rows: int, pool_pages: int) -> PageTable:
+    """hs2_page_table over an int32 [B, pages_per_seq] device tensor."""
+    if table.dtype != torch.int32 or table.dim() != 2 or not table.is_contiguous():
+        raise ValueError("the page table must be a contiguous int32 [B, pages_per_seq] tensor")
+    return PageTable(table.data_ptr(), int(page_rows), table.shape[1], int(pool_pages))
+
+
+def full_attn_topk_paged(k_pool, v_pool, table, page_rows: int, N: int, q, q_pos0: int, topk: int, window: int,
+                         max_sel: int | None = None, softmax_scale: float | None = None, k_scale=None, v_scale=None,
+                         out=None, lse=None, scores=None, idx=None, count=None, workspace=None, want_lse: bool = True,
+                         window_competes: bool = False, q_pos0_b=None):
+    """full_attn_topk over a paged pool [Hkv, pool_rows, D]: `table` [B, pages_per_seq] int32 maps each
+    sequence's pages of `page_rows` rows to pool pages.  Returns (out, lse, scores, idx, count)."""
+    B, Tq, Hq, D = q.shape
+    d = pool_desc(k_pool, v_pool, B, N, k_scale, v_scale)
+    pt = page_table(table, page_rows, k_pool.shape[1] // page_rows)
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(D)
+    if max_sel is None:
+        max_sel = min(N, topk + window)
+    dev = q.device
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Tq, Hq), dtype=torch.float32, device=dev)
+    if scores is None:
+        scores = torch.empty((B, Tq, d.Hkv, N), dtype=torch.float32, device=dev)
+    if idx is None:
+        idx = torch.empty((B, Tq, d.Hkv, max_sel), dtype=torch.int32, device=dev)
+    if count is None:
+        count = torch.empty((B, Tq, d.Hkv), dtype=torch.int32, device=dev)
+    need = int(_topk_ws(ctypes.byref(d), Tq, Hq))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    _dense(q, out, lse, scores, idx, count, workspace)
+    st = _topk_paged(ctypes.byref(d), ctypes.byref(pt), q.data_ptr(), _dtype_code(q), Tq, Hq, int(q_pos0),
+                     _qpos(q_pos0_b), float(softmax_scale), out.data_ptr(), None if lse is None else lse.data_ptr(),
+                     scores.data_ptr(), int(topk), int(window), SEL_WINDOW_COMPETES if window_competes else 0,
+                     idx.data_ptr(), count.data_ptr(), int(max_sel), workspace.data_ptr(), workspace.numel(),
+                     _stream())
+    _check(st, "hs2_full_attn_topk_paged")
+    return out, lse, scores, idx, count
+
+
+def sparse_attn_gather_paged(k_pool, v_pool, table, page_rows: int, N: int, q, idx, count, workspace,
+                             softmax_scale: float | None = None, k_scale=None, v_scale=None, out=None, lse=None,
+                             want_lse: bool = True):
+    """sparse_attn_gather_ws over a paged pool (idx holds logical positions); `workspace` as there."""
+    B, Tq, Hq, D = q.shape
+    d = pool_desc(k_pool, v_pool, B, N, k_scale, v_scale)
+    pt = page_table(table, page_rows, k_pool.shape[1] // page_rows)
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Tq, Hq), dtype=torch.float32, device=q.device)
+    _dense(q, idx, count, out, lse, workspace)
+    st = _sparse_paged(ctypes.byref(d), ctypes.byref(pt), q.data_ptr(), _dtype_code(q), Tq, Hq, float(softmax_scale),
+                       idx.data_ptr(), count.data_ptr(), idx.shape[-1], out.data_ptr(),
+                       None if lse is None else lse.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream())
+    _check(st, "hs2_sparse_attn_gather_paged")
+    return out, lse
 
 
 def full_attn_scores_workspace(k, v, Tq: int, Hq: int) -> int:

@@ -52,7 +52,7 @@ def test_every_declared_symbol_is_exported(hs2):
 
 
 def test_version_and_status_strings(hs2):
-    assert hs2.abi_version() == 2
+    assert hs2.abi_version() == 3
     for st in (0, -1, -2, -3, -4):
         assert hs2._status_string(st).decode()
 
@@ -266,3 +266,42 @@ def test_bridge_layers_validation(hs2):
     ws = hs2._bridge_layers_ws(2, 4, d8.Hkv, d8.D)
     assert ws > 2 * 4 * 2 * d8.Hkv * d8.D * 4
     assert f(FAKE, 4, 4096, FAKE, 2, (out * 2)(d8, d8), 0, 0, 1, FAKE, ws - 1, None) == -3  # grow: workspace
+
+
+def test_paged_validation(hs2):
+    """The paged entry points check the page table and the pool descriptor
+    before any launch: page rows a power of two of at least 32, the table
+    covering N, a pool shared by the sequences (stride_b 0), bf16/FP8 only, and
+    no multi-query chunk on a paged cache."""
+    d = desc(hs2, B=2, H=2, N=256)
+    d.stride_b = 0
+    ws = int(hs2._topk_ws(ctypes.byref(d), 1, 16))
+
+    def topk(pt, dd=d, Tq=1, wsb=ws):
+        return hs2._topk_paged(ctypes.byref(dd), None if pt is None else ctypes.byref(pt), FAKE, 1, Tq, 16,
+                               dd.N - Tq, None, 0.1, FAKE, None, FAKE, 8, 4, 0, FAKE, FAKE, 12, FAKE, wsb, None)
+
+    def gather(pt, dd=d):
+        return hs2._sparse_paged(ctypes.byref(dd), None if pt is None else ctypes.byref(pt), FAKE, 1, 1, 16, 0.1,
+                                 FAKE, FAKE, 12, FAKE, None, FAKE, 1 << 30, None)
+
+    P = hs2.PageTable
+    assert topk(None) == -1                              # no table
+    assert topk(P(None, 64, 4, 8)) == -1                 # NULL table pointer
+    assert topk(P(FAKE, 48, 6, 8)) == -1                 # page rows not a power of two
+    assert topk(P(FAKE, 16, 16, 32)) == -1               # pages below 32 rows
+    assert topk(P(FAKE, 64, 3, 8)) == -1                 # 3 pages of 64 rows do not cover N = 256
+    assert topk(P(FAKE, 64, 4, 0)) == -1                 # empty pool
+    assert topk(P(FAKE, 1 << 20, 1, 4096)) == -1         # pool rows beyond 2^31
+    assert topk(P(FAKE + 2, 64, 4, 8)) == -1             # misaligned table
+    d_b = desc(hs2, B=2, H=2, N=256)
+    assert topk(P(FAKE, 64, 4, 8), dd=d_b) == -1         # stride_b of a per-sequence cache
+    d32 = desc(hs2, dtype=0, B=2, H=2, N=256)
+    d32.stride_b = 0
+    assert topk(P(FAKE, 64, 4, 8), dd=d32) == -2         # fp32 cache
+    wsc = int(hs2._topk_ws(ctypes.byref(d), 64, 16))
+    assert topk(P(FAKE, 64, 4, 8), Tq=64, wsb=wsc) == -2  # 64 query tokens: the chunk path
+    assert topk(P(FAKE, 64, 4, 8), wsb=ws - 1) == -3     # workspace
+    assert gather(None) == -1
+    assert gather(P(FAKE, 64, 3, 8)) == -1
+    assert gather(P(FAKE, 64, 4, 8), dd=d32) == -2

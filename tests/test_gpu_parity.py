@@ -864,3 +864,74 @@ def test_merge_in_score_launch_matches_merge_kernel(hs2, case):
     gu.assert_scores(s2, s_or, G=G)
     i_g, c_g = oracle.select_topk_window(s2, spec.q_pos0, spec.k, spec.window, max_sel=spec.max_sel)
     assert np.array_equal(gu.host(cnt), c_g) and np.array_equal(gu.host(idx), i_g)
+
+
+# ------------------------------------------------- paged cache (decode path)
+
+PAGED_CASES = [
+    # kv, D, G, Hkv, B, N, page_rows
+    ("bf16", 128, 8, 4, 2, 20000, 256),   # last page partly used
+    ("fp8", 128, 8, 4, 2, 20000, 32),     # one scan tile per page
+    ("fp8", 128, 8, 4, 1, 70001, 1024),   # several score workgroups per row
+    ("bf16", 64, 4, 2, 3, 5003, 64),
+    ("bf16", 128, 8, 4, 16, 3000, 64),    # 64 lists: the one-workgroup gather
+]
+
+
+def paged_pool(x: np.ndarray, page_rows: int, rng, poison) -> tuple[np.ndarray, np.ndarray, int]:
+    """The [B, Hkv, N, D] cache x as a pool [Hkv, pool_pages * page_rows, D]
+    whose pages are shuffled (three spare pages, every unused row `poison`),
+    and the table [B, pages_per_seq] mapping each sequence's pages to it."""
+    B, H, N, D = x.shape
+    pps = -(-N // page_rows)
+    pool_pages = B * pps + 3
+    table = rng.permutation(pool_pages)[: B * pps].astype(np.int32).reshape(B, pps)
+    pool = np.full((H, pool_pages * page_rows, D), poison, dtype=x.dtype)
+    for b in range(B):
+        for i in range(pps):
+            lo, hi = i * page_rows, min(N, (i + 1) * page_rows)
+            dst = table[b, i] * page_rows
+            pool[:, dst:dst + hi - lo] = x[b, :, lo:hi]
+    return pool, table, pool_pages
+
+
+@pytest.mark.parametrize("case", PAGED_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_paged_cache_matches_contiguous(hs2, case):
+    """The decode path on a paged cache (full layer with the top-k, and the
+    split gather) gives the contiguous cache's results bit for bit: it visits
+    the same logical tiles and rows in the same order.  Unused pool rows hold
+    a large value, so a read of a row outside the table's pages would show."""
+    kv, D, G, Hkv, B, N, P = case
+    spec = small_spec(kv, D=D, G=G, Hkv=Hkv, B=B, N=N, k=256, window=32)
+    inp = synth.make_inputs(spec, seed=909 + N + P)
+    gu.log(f"paged {case}")
+    blk = gu.DeviceBlock(inp)
+    rng = np.random.default_rng(N + P)
+    poison = 0x7E if kv == "fp8" else 0x4700  # E4M3FN 448 / bf16 32768
+    kp, table, pool_pages = paged_pool(inp.k, P, rng, poison)
+    vp, _, _ = paged_pool(inp.v, P, np.random.default_rng(N + P), poison)  # the same page map
+    kpool, vpool, tab = gu.dev(kp), gu.dev(vp), torch.from_numpy(table).cuda()
+    assert kpool.shape[1] == pool_pages * P
+    o1, l1, s1, i1, c1 = hs2.full_attn_topk(blk.k, blk.v, blk.q, spec.q_pos0, spec.k, spec.window,
+                                            max_sel=spec.max_sel, k_scale=blk.ks, v_scale=blk.vs)
+    o2, l2, s2, i2, c2 = hs2.full_attn_topk_paged(kpool, vpool, tab, P, N, blk.q, spec.q_pos0, spec.k, spec.window,
+                                                  max_sel=spec.max_sel, k_scale=blk.ks, v_scale=blk.vs)
+    nws = hs2.sparse_attn_workspace(B, spec.Tq, Hkv, D, spec.max_sel)
+    ws1 = torch.zeros(nws, dtype=torch.uint8, device="cuda")
+    ws2 = torch.zeros(nws, dtype=torch.uint8, device="cuda")
+    g1 = [hs2.sparse_attn_gather_ws(blk.k, blk.v, q, i1, c1, ws1, k_scale=blk.ks, v_scale=blk.vs) for q in blk.qs]
+    g2 = [hs2.sparse_attn_gather_paged(kpool, vpool, tab, P, N, q, i2, c2, ws2, k_scale=blk.ks, v_scale=blk.vs)
+          for q in blk.qs]
+    torch.cuda.synchronize()
+    bits = lambda t: gu.host(t).view(np.uint32)
+    assert np.array_equal(bits(o1), bits(o2)), "full-layer outputs differ"
+    assert np.array_equal(bits(l1), bits(l2)), "full-layer LSE differs"
+    assert np.array_equal(bits(s1), bits(s2)), "scores differ"
+    assert np.array_equal(gu.host(i1), gu.host(i2)) and np.array_equal(gu.host(c1), gu.host(c2)), "selection differs"
+    for layer, ((a, la), (b_, lb)) in enumerate(zip(g1, g2)):
+        assert np.array_equal(bits(a), bits(b_)), f"sparse layer {layer} outputs differ"
+        assert np.array_equal(bits(la), bits(lb)), f"sparse layer {layer} LSE differs"
+    # and the contiguous run against the oracle (so the paged one is too)
+    o_or, _, s_or = oracle_full(inp, spec)
+    gu.assert_rows_rel(gu.host(o2), o_or, kv)
+    gu.assert_scores(gu.host(s2), s_or, G=G)
