@@ -394,7 +394,8 @@ def timed_us(call, reps, warm=2):
 
 def bench_extras(hs2, synth, k, v, ks, vs, q, spec, args):
     """The other paths of the library at the decode workload's shapes:
-    the competing-window selection, 64-token block lists against token lists
+    the competing-window selection, the decode step on a paged pool, 64-token
+    block lists against token lists
     in the gather (throughput regime), sliding-window attention (decode at 1M
     FP8 and a 32K-token bf16 prefill on the banded matrix-core pass), and the
     K/V bridge of 4 layers (512-token block, and decoding's one-token append
@@ -414,7 +415,42 @@ def bench_extras(hs2, synth, k, v, ks, vs, q, spec, args):
         ex[label] = round(timed_us(lambda: hs2.full_attn_topk(
             k, v, q, spec.q_pos0, spec.k, spec.window, max_sel=spec.max_sel, k_scale=ks, v_scale=vs, out=o[0],
             lse=o[1], scores=o[2], idx=o[3], count=o[4], workspace=ws, window_competes=comp), reps), 2)
-    del ws, o
+    # the decode step (full layer + top-k, three sparse layers) on a paged
+    # pool of 256-row pages in shuffled order, beside the same step on the
+    # contiguous cache (the sparse layers take q as their query here)
+    P = 256
+    pps = -(-N // P)
+    table = torch.from_numpy(np.random.default_rng(0xBA6E).permutation(pps).astype(np.int32)).view(1, pps).cuda()
+    pools = []
+    for src in (k, v):
+        pool = torch.zeros((Hkv, pps * P, D), dtype=src.dtype, device="cuda")
+        full_pages = N // P
+        pool.view(Hkv, pps, P, D)[:, table[0, :full_pages].long()] = src[0, :, : full_pages * P].reshape(
+            Hkv, full_pages, P, D)
+        if N % P:
+            t = int(table[0, full_pages])
+            pool[:, t * P: t * P + N % P] = src[0, :, full_pages * P:]
+        pools.append(pool)
+    wsg = torch.zeros(hs2.sparse_attn_workspace(1, 1, Hkv, D, spec.max_sel), dtype=torch.uint8, device="cuda")
+    go, gl = torch.empty_like(q), torch.empty((1, 1, Hq), dtype=torch.float32, device="cuda")
+
+    def contiguous_step():
+        hs2.full_attn_topk(k, v, q, spec.q_pos0, spec.k, spec.window, max_sel=spec.max_sel, k_scale=ks, v_scale=vs,
+                           out=o[0], lse=o[1], scores=o[2], idx=o[3], count=o[4], workspace=ws)
+        for _ in range(3):
+            hs2.sparse_attn_gather_ws(k, v, q, o[3], o[4], wsg, k_scale=ks, v_scale=vs, out=go, lse=gl)
+
+    def paged_step():
+        hs2.full_attn_topk_paged(pools[0], pools[1], table, P, N, q, spec.q_pos0, spec.k, spec.window,
+                                 max_sel=spec.max_sel, k_scale=ks, v_scale=vs, out=o[0], lse=o[1], scores=o[2],
+                                 idx=o[3], count=o[4], workspace=ws)
+        for _ in range(3):
+            hs2.sparse_attn_gather_paged(pools[0], pools[1], table, P, N, q, o[3], o[4], wsg, k_scale=ks,
+                                         v_scale=vs, out=go, lse=gl)
+
+    ex["paged_step"] = {"page_rows": P, "us": round(timed_us(paged_step, reps), 2),
+                        "contiguous_us": round(timed_us(contiguous_step, reps), 2)}
+    del ws, o, pools, wsg
     # gathers over token lists and over 64-token block lists (16 blocks + the 128-row window), 256 lists
     bq, rows = 256, spec.max_sel
     rng = np.random.default_rng(0xB10C)

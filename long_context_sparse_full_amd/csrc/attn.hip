@@ -414,6 +414,14 @@ __global__ void __launch_bounds__(WAVES * 64) scan_full(ScanParams P) {
   // tiles ending at or before j_nomask need no masking for any valid row
   const int j_nomask = min(q0 + tp * P.tpack, j_end - 1);
 
+  // PAGED: lane i holds the page of this wave's tile i (i < 64), loaded
+  // with the query fragments; a tile reads its page back with one readlane
+  int pg_lane = 0;
+  if constexpr (PAGED) {
+    const int jt = j_begin + wave * 32 + lane * jstride;
+    if (jt <= p_max)
+      pg_lane = min(max(P.pages.table[(int64_t)b * P.pages.per_seq + (jt >> P.pages.shift)], 0), P.pages.pool - 1);
+  }
   u32x4_t qf[NC];
   load_q<FP8, D>(qf, P, b, t, h, row_ok, g4);
   const int64_t kvoff = ((int64_t)b * P.sb + (int64_t)g * P.sh) * EB;
@@ -445,11 +453,20 @@ __global__ void __launch_bounds__(WAVES * 64) scan_full(ScanParams P) {
 #pragma unroll
   for (int dt = 0; dt < VE; ++dt) S.o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
+  // first cache row of this wave's tile ti (at position j0)
+  auto tile_row0 = [&](int j0, int ti) -> int64_t {
+    if constexpr (PAGED) {
+      const int pg = ti < 64 ? __builtin_amdgcn_readlane(pg_lane, ti) : (phys_row(P.pages, b, j0) >> P.pages.shift);
+      return ((int64_t)pg << P.pages.shift) | (j0 & ((1 << P.pages.shift) - 1));
+    } else {
+      return j0;
+    }
+  };
   // full tile (j0 + 31 <= p_max): scalar tile base plus the fixed lane offsets
-  auto load_full = [&](RawTile<FP8, D>& R, int j0) {
+  auto load_full = [&](RawTile<FP8, D>& R, int j0, int ti) {
     const char* kp[2];
     const char* vp[8];
-    const int64_t row0 = PAGED ? phys_row(P.pages, b, j0) : j0;
+    const int64_t row0 = tile_row0(j0, ti);
     const char* tk = kb + row0 * snb;
     const char* tv = vb + row0 * snb;
 #pragma unroll
@@ -458,9 +475,9 @@ __global__ void __launch_bounds__(WAVES * 64) scan_full(ScanParams P) {
     for (int kk = 0; kk < 8; ++kk) vp[kk] = tv + voff[kk];
     load_tile<FP8, D>(R, kp, vp);
   };
-  auto load = [&](RawTile<FP8, D>& R, int j0) {
+  auto load = [&](RawTile<FP8, D>& R, int j0, int ti) {
     if (j0 + 31 <= p_max) {
-      load_full(R, j0);
+      load_full(R, j0, ti);
     } else {  // tail tile: rows past the last position repeat it
       const char* kp[2];
       const char* vp[8];
@@ -488,21 +505,21 @@ __global__ void __launch_bounds__(WAVES * 64) scan_full(ScanParams P) {
   const int n_full = j_first + 31 <= p_max ? min(n, (p_max - 31 - j_first) / jstride + 1) : 0;
   RawTile<FP8, D> A, B;
   int i = 0;
-  if (n > 0) load(A, j_first);
+  if (n > 0) load(A, j_first, 0);
   for (; i + 2 < n_full; i += 2) {
     const int j0 = j_first + i * jstride;
-    load_full(B, j0 + jstride);
+    load_full(B, j0 + jstride, i + 1);
     compute(A, j0);
-    load_full(A, j0 + 2 * jstride);
+    load_full(A, j0 + 2 * jstride, i + 2);
     compute(B, j0 + jstride);
   }
   // tail: A holds tile i; at most three tiles remain
   if (i < n) {
     const int j0 = j_first + i * jstride;
-    if (i + 1 < n) load(B, j0 + jstride);
+    if (i + 1 < n) load(B, j0 + jstride, i + 1);
     compute(A, j0);
     if (i + 1 < n) {
-      if (i + 2 < n) load(A, j0 + 2 * jstride);
+      if (i + 2 < n) load(A, j0 + 2 * jstride, i + 2);
       compute(B, j0 + jstride);
       if (i + 2 < n) compute(A, j0 + 2 * jstride);
     }
