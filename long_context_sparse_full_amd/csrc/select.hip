@@ -496,36 +496,35 @@ __global__ void __launch_bounds__(256) sel_bracket(SelectParams P) {
 // owns, a quarter of them per wave (kWaveTake and kWaveBin entries), and each
 // wave stores its two list lengths.  The bounds are compared as floats (for
 // non-negative scores and -0 the same order as the keys; the bound of an
-// empty upper side is a NaN, above which nothing lies).  Hits are rare, so
-// each key slot's compare gives the wave's ballot of hits, an empty ballot
-// costs a scalar branch, and a hit is written at once at the wave's running
-// count plus its rank in the ballot: one pass, no atomics, no barrier, no LDS.
-// A wave with more hits than its quarter holds (clustered scores) leaves its
-// row to the per-row kernel.
+// empty upper side is a NaN, above which nothing lies).  Each key slot's
+// compare gives the wave's ballot of hits, an empty ballot costs a scalar
+// branch, and a hit goes at the wave's running count plus its rank in the
+// ballot into the wave's own lists in LDS; the wave then copies its lists out
+// with whole-row stores (hits are spread thinly over the row, so writing them
+// at once would cost one narrow global store per ballot).  One pass, no
+// atomics, no barrier.  A wave with more hits than its quarter holds
+// (clustered scores) leaves its row to the per-row kernel.
 constexpr int kWaveTake = kCompactTake / 4, kWaveBin = kCompactBin / 4;
-__global__ void __launch_bounds__(256) sel_collect(SelectParams P) {
+struct CollectLds {
+  int32_t la[4][kWaveTake], lb[4][kWaveBin], lk[4][kWaveBin];
+};
+template <bool VEC>
+__device__ __forceinline__ void collect_chunk(const SelectParams& P, int u, int chunk, int base, int end,
+                                              CollectLds& L) {
   constexpr int NV = kKeysPerThread / 4;  // float4 loads per thread
-  const int u = blockIdx.y, chunk = blockIdx.x;
-  // the row's mode and candidates follow from its position, so the score
-  // loads go out before the bracket is read
-  const int ncand = sel_ncand(row_pos(P, u), P.cand_window);
-  const int take = sel_take(ncand, P.k, 1);
-  if (sel_mode(take, ncand, 1) != MODE_RADIX) return;
-  const int base = chunk * kSelChunk;
-  if (base >= ncand) return;
-  const int end = min(base + kSelChunk, ncand);
   // element 4 i + e at position base + 4 (tid + 256 i) + e; positions past the
   // chunk read as NaN, which no bound test accepts
   const float* s = P.scores + (int64_t)u * P.N;
+  const float nan = __int_as_float(0x7fc00000);
   float4 v[NV];
-  if ((P.N & 3) == 0 && end - base == kSelChunk) {  // whole chunk (uniform): 16-byte loads
 #pragma unroll
-    for (int i = 0; i < NV; ++i) v[i] = *(const float4*)(s + base + 4 * (threadIdx.x + 256 * i));
-  } else {
-    const float nan = __int_as_float(0x7fc00000);
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int j = base + 4 * (threadIdx.x + 256 * i);
+  for (int i = 0; i < NV; ++i) {
+    const int j = base + 4 * (threadIdx.x + 256 * i);
+    if constexpr (VEC) {
+      // N a multiple of 4: a group that starts before the chunk's end lies in
+      // the row; one past it loads the chunk's first group and is masked
+      v[i] = *(const float4*)(s + (j < end ? j : base));
+    } else {
       v[i].x = j < end ? s[j] : nan;
       v[i].y = j + 1 < end ? s[j + 1] : nan;
       v[i].z = j + 2 < end ? s[j + 2] : nan;
@@ -536,16 +535,16 @@ __global__ void __launch_bounds__(256) sel_collect(SelectParams P) {
   const float hi = __uint_as_float(((uint32_t)stw[ST_PHI] << 8) | 0xFFu);
   const float lo = __uint_as_float((uint32_t)stw[ST_PLO] << 8);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t cw = ((int64_t)u * P.nchunks + chunk) * 4 + wave;
-  int32_t* cand = P.cand + ((int64_t)u * P.nchunks + chunk) * kCandWords;
-  int32_t* la = cand + wave * kWaveTake;                           // above: positions
-  int32_t* lb = cand + kCompactTake + wave * kWaveBin;             // inside: positions
-  int32_t* lk = cand + kCompactTake + kCompactBin + wave * kWaveBin;  // inside: keys
   const uint64_t below = (1ull << lane) - 1;  // lanes ranked before this one
   int oa = 0, ob = 0;  // wave-uniform running counts
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
-    const float x[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+    const int j = base + 4 * (threadIdx.x + 256 * i);
+    float x[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+    if constexpr (VEC) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = j + e < end ? x[e] : nan;
+    }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       // above: x > hi; inside: lo <= x and not above (NaN fails both, -0 >= +0 holds)
@@ -553,23 +552,50 @@ __global__ void __launch_bounds__(256) sel_collect(SelectParams P) {
       const uint64_t ba = __ballot(ha), bb = __ballot(hb);
       if (ba) {  // uniform
         const int o = oa + __popcll(ba & below);
-        if (ha && o < kWaveTake) la[o] = base + 4 * (threadIdx.x + 256 * i) + e;
+        if (ha && o < kWaveTake) L.la[wave][o] = j + e;
         oa += __popcll(ba);
       }
       if (bb) {  // uniform
         const int o = ob + __popcll(bb & below);
         if (hb && o < kWaveBin) {
-          lb[o] = base + 4 * (threadIdx.x + 256 * i) + e;
-          lk[o] = (int32_t)score_key(x[e]);
+          L.lb[wave][o] = j + e;
+          L.lk[wave][o] = (int32_t)score_key(x[e]);
         }
         ob += __popcll(bb);
       }
     }
   }
+  const int64_t cw = ((int64_t)u * P.nchunks + chunk) * 4 + wave;
+  int32_t* cand = P.cand + ((int64_t)u * P.nchunks + chunk) * kCandWords;
+  int32_t* la = cand + wave * kWaveTake;                              // above: positions
+  int32_t* lb = cand + kCompactTake + wave * kWaveBin;                // inside: positions
+  int32_t* lk = cand + kCompactTake + kCompactBin + wave * kWaveBin;  // inside: keys
+  const int na = min(oa, kWaveTake), nb = min(ob, kWaveBin);
+  for (int i = lane; i < na; i += 64) la[i] = L.la[wave][i];
+  for (int i = lane; i < nb; i += 64) {
+    lb[i] = L.lb[wave][i];
+    lk[i] = L.lk[wave][i];
+  }
   if (lane == 0) {
     P.cnt[2 * cw] = oa;
     P.cnt[2 * cw + 1] = ob;
   }
+}
+
+// VEC: rows of a multiple of 4 scores (16-byte loads); else scalar loads
+template <bool VEC>
+__global__ void __launch_bounds__(256) sel_collect(SelectParams P) {
+  const int u = blockIdx.y, chunk = blockIdx.x;
+  // the row's mode and candidates follow from its position, so the score
+  // loads go out before the bracket is read
+  const int ncand = sel_ncand(row_pos(P, u), P.cand_window);
+  const int take = sel_take(ncand, P.k, 1);
+  if (sel_mode(take, ncand, 1) != MODE_RADIX) return;
+  const int base = chunk * kSelChunk;
+  if (base >= ncand) return;
+  const int end = min(base + kSelChunk, ncand);
+  __shared__ CollectLds L;
+  collect_chunk<VEC>(P, u, chunk, base, end, L);
 }
 
 // Ascending bitonic sort of n (a power of two) LDS elements by the workgroup.
@@ -1315,7 +1341,10 @@ hipError_t launch_select(const SelectParams& p_in, hipStream_t s) {
     // many rows: bracket from a sample, one collecting pass, finish on chip,
     // unsettled rows by the per-row kernel (the set-up is the bracket's)
     HS2_L("select_bracket", sel_bracket, dim3(p.units));
-    HS2_L("select_collect", sel_collect, grid_c);
+    if ((p.N & 3) == 0)
+      HS2_L("select_collect", sel_collect<true>, grid_c);
+    else
+      HS2_L("select_collect", sel_collect<false>, grid_c);
     {
       TimedLaunch tl_("select_finish", s);
       hipLaunchKernelGGL(sel_finish, dim3(p.units), dim3(256), finish_lds_bytes(p.N), s, p);
