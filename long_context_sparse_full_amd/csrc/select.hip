@@ -1059,12 +1059,13 @@ __global__ void __launch_bounds__(256) sel_block_mass(SelectParams P) {
 // Block masses with coalesced loads: a workgroup stages 4096 consecutive
 // scores (64 threads x 16 floats per wave row) in LDS, then one thread per
 // block adds its block's scores in ascending position, as the plain kernel
-// does.  Power-of-two block sizes up to 256; LDS slot i + i / BS keeps the
-// threads' sequential reads on distinct banks.
+// does.  Power-of-two block sizes up to 256; a block's BS scores sit at LDS
+// slot t (BS + 4): 16-byte writes and reads, and the 16 lanes of a 16-byte
+// read phase start 4 banks apart, so neither side conflicts.
 constexpr int kMassTile = 4096;
 template <int BS>
 __global__ void __launch_bounds__(256) sel_block_mass_tiled(SelectParams P) {
-  __shared__ float sv[kMassTile + kMassTile / BS];
+  __shared__ __align__(16) float sv[kMassTile + 4 * (kMassTile / BS)];
   const int u = blockIdx.y;
   const int ncand = sel_ncand(row_pos(P, u), P.window);  // as stored by the set-up
   const int lo = blockIdx.x * kMassTile;
@@ -1084,11 +1085,7 @@ __global__ void __launch_bounds__(256) sel_block_mass_tiled(SelectParams P) {
       v.z = j + 2 < ncand ? s[j + 2] : 0.f;
       v.w = j + 3 < ncand ? s[j + 3] : 0.f;
     }
-    const int base = i + i / BS;  // 4 | BS, so the float4 stays inside one block
-    sv[base] = v.x;
-    sv[base + 1] = v.y;
-    sv[base + 2] = v.z;
-    sv[base + 3] = v.w;
+    *(float4*)(sv + i + 4 * (i / BS)) = v;  // 4 | BS, so the float4 stays inside one block
   }
   __syncthreads();
   constexpr int NB = kMassTile / BS;
@@ -1096,9 +1093,17 @@ __global__ void __launch_bounds__(256) sel_block_mass_tiled(SelectParams P) {
     const int beta = blockIdx.x * NB + t;
     if (beta * BS >= ncand) break;
     const int n = min(BS, ncand - beta * BS);
-    const float* b = sv + t * (BS + 1);
+    const float* b = sv + t * (BS + 4);
     double m = 0.0;
-    for (int e = 0; e < n; ++e) m += (double)b[e];
+    int e = 0;
+    for (; e + 4 <= n; e += 4) {
+      const float4 x = *(const float4*)(b + e);
+      m += (double)x.x;
+      m += (double)x.y;
+      m += (double)x.z;
+      m += (double)x.w;
+    }
+    for (; e < n; ++e) m += (double)b[e];
     P.bmass[(int64_t)u * P.nblocks_max + beta] = m;
   }
 }
